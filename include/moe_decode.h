@@ -1,0 +1,244 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) batch-1 decode MoE FFN stage.
+ *
+ * One MoE layer of a Qwen3.6-35B-A3B-shaped decoder, per token:
+ *   a1  residual add folded into RMSNorm, Q8_1 of the normed vector
+ *   a2  fp32 router GEMV over the experts (+ the shared-expert gate row)
+ *   a3  top-k by (value descending, index ascending) + softmax over the selected logits
+ *   a4  routed gate/up GEMVs (Q4_K x Q8_1) + SwiGLU + Q8_1 of the product
+ *   a5  routed down GEMV (Q4_K or Q5_K x Q8_1) + weighted combine
+ *   a6  sigmoid-gated shared expert (Q4_K or Q8_0 x Q8_1)
+ * and the 40-layer stack of such layers without launch gaps (a7).
+ *
+ * Source pages (cited by short name in the comments below):
+ *   [P273] "perf(qwen3.6): fused router GEMV+top-k + folded residual-norm (decode)"
+ *   [P239] "perf(qwen3.6): fuse decode kernel launches -- shared-expert + GDN conv/L2-norm"
+ *   [P359] "perf(qwen36): Q4_K shared-expert FFN kernels + Q8_0/Q5_K->Q4_K requant of the MoE FFN stage"
+ *
+ * Conventions (every entry point):
+ *  - Pointers named "device" are HIP device pointers; descriptor structs and
+ *    the layer-weights array of moe_stack_bind live in host memory and are
+ *    read only during the call.
+ *  - The caller allocates and owns every buffer, the workspace included.  The
+ *    library keeps no mutable state between calls apart from what the caller's
+ *    workspace holds; it never allocates device memory.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream).  No call synchronises the host, reads device data back or
+ *    issues a memset, so every call can be captured in a HIP graph.
+ *  - Every argument is validated on the host before anything is enqueued.  An
+ *    invalid argument returns a negative MOE_ERR_* code and enqueues nothing.
+ *    A launch failure returns MOE_ERR_HIP.  There is no fallback path: an
+ *    unsupported shape or type is an error.
+ *  - bf16 values are passed as uint16_t bit patterns.  Quantised blocks are
+ *    bytes in the GGUF layouts (see MOE_TYPE_*), rows of a matrix back to
+ *    back, experts of a stacked matrix back to back; every weight pointer must
+ *    be 16-byte aligned and every row a whole number of blocks.
+ *  - Calls that share one workspace must not overlap in time (they are
+ *    ordered when issued on one stream).
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)          /* a required pointer is NULL */
+#define MOE_ERR_SHAPE (-2)         /* a size is out of range or not a whole number of blocks */
+#define MOE_ERR_TYPE (-3)          /* unsupported block type for that operand */
+#define MOE_ERR_ALIGN (-4)         /* a pointer is not aligned as required */
+#define MOE_ERR_WORKSPACE (-5)     /* workspace NULL or smaller than moe_workspace_size() */
+#define MOE_ERR_HIP (-6)           /* a HIP launch or runtime call failed */
+#define MOE_ERR_UNSUPPORTED (-7)   /* valid arguments, combination not implemented */
+#define MOE_ERR_NOT_BOUND (-8)     /* moe_decode_stack before moe_stack_bind */
+
+/* ---- block types: GGUF type ids ([P359] Summary: type id 12 is Q4_K) ----
+ *  Q4_K 144 B / 256 elements: d f16 | dmin f16 | scales[12] (6-bit scale and min of
+ *       8 sub-blocks of 32) | qs[128] (4-bit codes); element = d*sc*q - dmin*m.
+ *  Q5_K 176 B / 256 elements: as Q4_K with qh[32] (fifth code bit) before qs[128].
+ *  Q8_0  34 B / 32 elements: d f16 | q int8[32]  ([P359] Summary: 34 bytes per block).
+ *  Q8_1  36 B / 32 elements: d f16 | s f16 | q int8[32], s = d * sum(q) (activations). */
+#define MOE_TYPE_F32 0
+#define MOE_TYPE_Q8_0 8
+#define MOE_TYPE_Q8_1 9
+#define MOE_TYPE_Q4_K 12
+#define MOE_TYPE_Q5_K 13
+
+/* ---- limits ---- */
+#define MOE_MAX_HIDDEN 8192
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_FFN 4096
+#define MOE_MAX_LAYERS 256
+
+typedef struct moe_layer_desc {
+    int hidden;        /* H: multiple of 256, <= MOE_MAX_HIDDEN */
+    int n_experts;     /* E: 1..MOE_MAX_EXPERTS */
+    int top_k;         /* k: 1..min(E, MOE_MAX_TOPK) */
+    int ffn;           /* F: routed intermediate size, multiple of 32, <= MOE_MAX_FFN */
+    int shared_ffn;    /* Fs: 0 = no shared expert, else multiple of 32, <= MOE_MAX_FFN */
+    int gate_up_type;  /* MOE_TYPE_Q4_K */
+    int down_type;     /* MOE_TYPE_Q4_K or MOE_TYPE_Q5_K */
+    int shared_type;   /* MOE_TYPE_Q4_K or MOE_TYPE_Q8_0 (all three shared matrices) */
+    int norm;          /* 1: the layer input is folded and RMS-normed (a1);
+                          0: the layer input is an fp32 vector used as the normed vector */
+    float eps;         /* RMSNorm epsilon */
+} moe_layer_desc;
+
+/* Device pointers of one layer's weights.  Down rows have K = F rounded up to a
+ * whole block of down_type (the padding is part of every row). */
+typedef struct moe_layer_weights {
+    const float* norm_w;        /* [H] fp32 (norm = 1) */
+    const float* router_w;      /* [E][H] fp32 */
+    const float* shared_gate_w; /* [H] fp32 (Fs > 0) */
+    const void* gate;           /* [E][F] rows of H, gate_up_type */
+    const void* up;             /* [E][F] rows of H, gate_up_type */
+    const void* down;           /* [E][H] rows of pad(F), down_type */
+    const void* shared_gate;    /* [Fs] rows of H, shared_type (Fs > 0) */
+    const void* shared_up;      /* [Fs] rows of H, shared_type (Fs > 0) */
+    const void* shared_down;    /* [H] rows of pad(Fs), shared_type (Fs > 0) */
+} moe_layer_weights;
+
+/* Per-call device buffers of moe_decode_layer (one token). */
+typedef struct moe_layer_io {
+    const uint16_t* residual;   /* [H] bf16 residual stream (norm = 1) */
+    const uint16_t* routed_in;  /* [H] bf16 previous layer's routed output, or NULL (= 0) */
+    const uint16_t* shared_in;  /* [H] bf16 previous layer's shared output, or NULL (2-input form) */
+    const float* x;             /* [H] fp32 input (norm = 0) */
+    uint16_t* out_sum;          /* [H] bf16 new residual = bf16(residual + bf16(routed_in + shared_in)) (norm = 1) */
+    uint16_t* routed_out;       /* [H] bf16 */
+    uint16_t* shared_out;       /* [H] bf16 (Fs > 0) */
+    /* optional intermediates, NULL = not written */
+    float* xn;                  /* [H] fp32 normed vector */
+    void* xq;                   /* [H/32] Q8_1 blocks */
+    float* logits;              /* [E] fp32 */
+    int32_t* ids;               /* [k] selected experts, slot order */
+    float* weights;             /* [k] routing weights */
+    float* shared_gate;         /* [1] sigmoid of the shared-gate logit */
+    float* h;                   /* [k][F] SwiGLU outputs */
+    float* hs;                  /* [Fs] shared SwiGLU output */
+} moe_layer_io;
+
+/* ------------------------------------------------------------------------
+ * Workspace.  moe_workspace_size gives the bytes one token of `desc` needs
+ * (n_layers >= 1: the bound stack of moe_stack_bind included).  The
+ * workspace must be 256-byte aligned and initialised once by
+ * moe_workspace_init before its first use; the library returns every
+ * counter in it to its initial value, so graph replays need no reset.
+ * ---------------------------------------------------------------------- */
+size_t moe_workspace_size(const moe_layer_desc* desc, int n_layers);
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* moe_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * a1: residual add folded into RMSNorm ([P273] Summary item 2: the
+ * routed+shared residual add is folded into a 3-input add_rmsnorm3 that is
+ * bit-identical to the add followed by the 2-input norm; [P273] Relation to
+ * open PRs: add_rmsnorm3_q8 keeps the reload of the stored sum).
+ *   t = shared ? bf16(routed + shared) : (routed ? routed : 0)
+ *   u = bf16(residual + t)              -> out_sum (bf16), the new residual
+ *   xn = u * (1/sqrt(mean(u^2) + eps)) * norm_w   (fp32; mean over H)
+ *   xq = Q8_1(xn): per 32 values d = amax/127, codes rounded half away from
+ *        zero, d and s = d*sum(q) stored as fp16; an all-zero block is zero.
+ * residual: [n_tok][H] bf16; routed, shared: [n_tok][H] bf16 or NULL;
+ * norm_w [H] fp32; out_sum [n_tok][H] bf16; xn [n_tok][H] fp32 or NULL;
+ * xq [n_tok][H/32] Q8_1 or NULL.  All device.  n_tok 1..4096.
+ * ---------------------------------------------------------------------- */
+int add_rmsnorm3(const uint16_t* residual, const uint16_t* routed, const uint16_t* shared,
+                 const float* norm_w, int hidden, int n_tok, float eps,
+                 uint16_t* out_sum, float* xn, void* xq, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a2 + a3: router GEMV + in-kernel top-k + routing weights ([P273] Summary
+ * item 1: the split-K fp32 GEMV's logits and the top-k select in one kernel,
+ * selection by value descending with ties to the lower expert index, the
+ * last workgroup selecting after a grid-completion handshake that returns to
+ * zero by itself).  Routing weights: softmax over the k selected logits.
+ *   logits[e] = sum_i W[e][i] * xn[i]           (fp32 result)
+ *   ids       = top-k of logits                 (slot order = rank order)
+ *   weights   = softmax(logits[ids])
+ *   shared_gate_out = sigmoid(sum_i g[i] * xn[i]) if w_shared_gate != NULL
+ * xn [n_tok][H] fp32; w_router [E][H] fp32; w_shared_gate [H] fp32 or NULL;
+ * logits [n_tok][E] or NULL; ids [n_tok][k] int32; weights [n_tok][k] fp32;
+ * shared_gate_out [n_tok] or NULL.  All device.  Needs the workspace for the
+ * handshake counter and, when logits == NULL, the logit buffer.
+ * ---------------------------------------------------------------------- */
+int router_topk(const float* xn, const float* w_router, const float* w_shared_gate,
+                int n_tok, int hidden, int n_experts, int top_k,
+                float* logits, int32_t* ids, float* weights, float* shared_gate_out,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a4 + a5 (+ a6): expert FFN for one token ([P359] Summary: Q8_1 activations
+ * -> gate/up with SiLU -> Q8_1 of the product -> down, with an int8 dot of the
+ * weight codes against the Q8_1 codes; [P239] Summary item 1: gate and up of
+ * the shared expert in one pass over the activations).
+ *   for slot s (expert e = ids[s]): g = G_e xq, u = U_e xq (fp32 rows),
+ *     h = silu(g) * u (fp32), y_e = D_e Q8_1(h) (fp32 rows; Q8_1 padding blocks
+ *     of zeros up to the down row length)
+ *   routed_out = bf16(sum_s weights[s] * y_e)       (slot order)
+ *   shared (desc->shared_ffn > 0): same FFN with the shared matrices,
+ *     shared_out = bf16(shared_gate[0] * ys)
+ * xq [H/32] Q8_1; ids [k]; weights [k]; shared_gate [1] fp32 (device, read
+ * when Fs > 0); routed_out, shared_out [H] bf16; h [k][F], hs [Fs] fp32 or
+ * NULL.  All device.  n_tok must be 1.  An id outside [0, E) is not read
+ * through: its slot's h and the routed/shared outputs become NaN.
+ * ---------------------------------------------------------------------- */
+int expert_ffn_q4k(const moe_layer_desc* desc, const moe_layer_weights* w,
+                   const void* xq, const int32_t* ids, const float* weights, const float* shared_gate,
+                   int n_tok, uint16_t* routed_out, uint16_t* shared_out, float* h, float* hs,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a1..a6: one MoE layer for one token, composed on the device (no host
+ * synchronisation, ids never leave the device).
+ * ---------------------------------------------------------------------- */
+int moe_decode_layer(const moe_layer_desc* desc, const moe_layer_weights* w,
+                     const moe_layer_io* io, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a7: the L-layer stack for one token ([P239] Summary: decode is graph- and
+ * launch-bound; [P273] Summary item 2: one graph node per layer matters).
+ *   res_0 = input, previous outputs 0; layer l folds the previous layer's
+ *   routed/shared outputs into its norm; output = bf16(res_L + t_L) with
+ *   t_L = bf16(routed_{L-1} + shared_{L-1}) (the fold the next norm would do).
+ * layers: host array of n_layers structs of device pointers.
+ * mode MOE_STACK_KERNELS enqueues 4 kernels per layer plus the final fold on
+ * `stream` (capture them in a HIP graph to remove launch overhead);
+ * MOE_STACK_PERSISTENT runs every layer in one cooperative launch and needs a
+ * prior moe_stack_bind of the same layers into the same workspace (it copies
+ * the pointer table to the device and synchronises `stream` once; do not call
+ * it during graph capture).  MOE_STACK_AUTO picks the fastest bound mode.
+ * ids_per_layer [L][k] int32 and resid_per_layer [L][H] bf16 (each layer's
+ * out_sum) are optional device outputs.  desc->norm must be 1.
+ * ---------------------------------------------------------------------- */
+#define MOE_STACK_AUTO 0
+#define MOE_STACK_KERNELS 1
+#define MOE_STACK_PERSISTENT 2
+int moe_stack_bind(const moe_layer_desc* desc, const moe_layer_weights* layers, int n_layers,
+                   void* ws, size_t ws_bytes, void* stream);
+int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers, int n_layers,
+                     const uint16_t* input, uint16_t* output, int32_t* ids_per_layer, uint16_t* resid_per_layer,
+                     int mode, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Test export: the integer sub-block dots of weight rows against Q8_1
+ * activations, the bit-exact quantity of the int8 dot path ([P359] Summary).
+ * rows: [n_rows] rows of K elements of `type` (Q4_K, Q5_K or Q8_0); xq [K/32]
+ * Q8_1; out [n_rows][K/32] int32: out[r][j] = sum over the 32 elements of
+ * sub-block j of weight code * activation code.  All device.
+ * ---------------------------------------------------------------------- */
+int moe_test_subblock_dots(const void* rows, int type, int K, int n_rows, const void* xq,
+                           int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

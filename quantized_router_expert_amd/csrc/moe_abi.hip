@@ -1,0 +1,239 @@
+// moe_abi.hip -- extern "C" entry points: host-side validation, workspace
+// carving and kernel enqueue.  Nothing is enqueued unless every argument
+// passes validation.
+#include <string.h>
+
+#include "../../include/moe_decode.h"
+#include "moe_device.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+template <class T>
+inline T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off); }
+
+// router_topk's own workspace use: counters, then logits [n_tok][E+1]
+constexpr size_t kRouterLogitsOff = ((sizeof(unsigned) * kCounterSlots) + 255) & ~(size_t)255;
+inline size_t router_ws_bytes(int n_tok, int E) {
+  return kRouterLogitsOff + ((sizeof(float) * (size_t)n_tok * (E + 1) + 255) & ~(size_t)255);
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGN;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or not a whole number of blocks";
+    case MOE_ERR_TYPE: return "unsupported block type";
+    case MOE_ERR_ALIGN: return "pointer not aligned as required";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+    case MOE_ERR_UNSUPPORTED: return "combination not implemented";
+    case MOE_ERR_NOT_BOUND: return "layer stack not bound to this workspace";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_size(const moe_layer_desc* desc, int n_layers) {
+  if (check_desc(desc) != MOE_OK || n_layers < 0 || n_layers > MOE_MAX_LAYERS) return 0;
+  return ws_layout(desc, n_layers).total;
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGN;
+  if (ws_bytes < 256) return MOE_ERR_WORKSPACE;
+  return launch_fill(ws, ws_bytes / 4, 0u, as_stream(stream));
+}
+
+int add_rmsnorm3(const uint16_t* residual, const uint16_t* routed, const uint16_t* shared, const float* norm_w,
+                 int hidden, int n_tok, float eps, uint16_t* out_sum, float* xn, void* xq, void* stream) {
+  if (!residual || !norm_w || !out_sum) return MOE_ERR_NULL;
+  if (shared && !routed) return MOE_ERR_NULL;
+  if (hidden <= 0 || hidden % 256 || hidden > MOE_MAX_HIDDEN || n_tok <= 0 || n_tok > 65535) return MOE_ERR_SHAPE;
+  if (!(eps >= 0.0f)) return MOE_ERR_SHAPE;
+  if (!aligned(residual, 2) || (routed && !aligned(routed, 2)) || (shared && !aligned(shared, 2)) ||
+      !aligned(out_sum, 2) || !aligned(norm_w, 4) || (xn && !aligned(xn, 4)) || (xq && !aligned(xq, 4)))
+    return MOE_ERR_ALIGN;
+  return launch_norm(residual, routed, shared, norm_w, hidden, n_tok, eps, out_sum, xn, xq, 1, as_stream(stream));
+}
+
+int router_topk(const float* xn, const float* w_router, const float* w_shared_gate, int n_tok, int hidden,
+                int n_experts, int top_k, float* logits, int32_t* ids, float* weights, float* shared_gate_out,
+                void* ws, size_t ws_bytes, void* stream) {
+  if (!xn || !w_router || !ids || !weights) return MOE_ERR_NULL;
+  if (n_tok <= 0 || n_tok > kCounterSlots || hidden <= 0 || hidden % 256 || hidden > MOE_MAX_HIDDEN) return MOE_ERR_SHAPE;
+  if (n_experts <= 0 || n_experts > MOE_MAX_EXPERTS || top_k <= 0 || top_k > n_experts || top_k > MOE_MAX_TOPK)
+    return MOE_ERR_SHAPE;
+  if (!aligned(xn, 16) || !aligned(w_router, 16) || (w_shared_gate && !aligned(w_shared_gate, 16)) ||
+      !aligned(ids, 4) || !aligned(weights, 4) || (logits && !aligned(logits, 4)) ||
+      (shared_gate_out && !aligned(shared_gate_out, 4)))
+    return MOE_ERR_ALIGN;
+  int rc = check_ws(ws, ws_bytes, router_ws_bytes(n_tok, n_experts));
+  if (rc) return rc;
+  return launch_router(xn, w_router, w_shared_gate, n_tok, hidden, n_experts, top_k, at<float>(ws, kRouterLogitsOff),
+                       logits, ids, weights, shared_gate_out, at<unsigned>(ws, 0), as_stream(stream));
+}
+
+int expert_ffn_q4k(const moe_layer_desc* desc, const moe_layer_weights* w, const void* xq, const int32_t* ids,
+                   const float* weights, const float* shared_gate, int n_tok, uint16_t* routed_out,
+                   uint16_t* shared_out, float* h, float* hs, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  rc = check_weights(desc, w);
+  if (rc) return rc;
+  if (!xq || !ids || !weights || !routed_out) return MOE_ERR_NULL;
+  if (desc->shared_ffn > 0 && (!shared_gate || !shared_out)) return MOE_ERR_NULL;
+  if (n_tok != 1) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(xq, 4) || !aligned(ids, 4) || !aligned(weights, 4) || !aligned(routed_out, 2) ||
+      (shared_out && !aligned(shared_out, 2)) || (h && !aligned(h, 4)) || (hs && !aligned(hs, 4)))
+    return MOE_ERR_ALIGN;
+  const WsLayout L = ws_layout(desc, 0);
+  rc = check_ws(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  float* hb = h ? h : at<float>(ws, L.h);
+  float* hsb = hs ? hs : at<float>(ws, L.hs);
+  hipStream_t st = as_stream(stream);
+  rc = launch_gate_up(desc, w, xq, ids, hb, hsb, st);
+  if (rc) return rc;
+  return launch_down(desc, w, hb, hsb, ids, weights, shared_gate, routed_out, shared_out, st);
+}
+
+int moe_decode_layer(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_layer_io* io, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  rc = check_weights(desc, w);
+  if (rc) return rc;
+  if (!io || !io->routed_out) return MOE_ERR_NULL;
+  if (desc->norm ? (!io->residual || !io->out_sum) : !io->x) return MOE_ERR_NULL;
+  if (desc->shared_ffn > 0 && !io->shared_out) return MOE_ERR_NULL;
+  if (io->shared_in && !io->routed_in) return MOE_ERR_NULL;
+  if ((io->x && !aligned(io->x, 16)) || (io->xn && !aligned(io->xn, 16)) || (io->xq && !aligned(io->xq, 4)) ||
+      (io->residual && !aligned(io->residual, 2)) || (io->out_sum && !aligned(io->out_sum, 2)) ||
+      !aligned(io->routed_out, 2) || (io->shared_out && !aligned(io->shared_out, 2)) ||
+      (io->logits && !aligned(io->logits, 4)) || (io->ids && !aligned(io->ids, 4)) ||
+      (io->weights && !aligned(io->weights, 4)) || (io->h && !aligned(io->h, 4)) || (io->hs && !aligned(io->hs, 4)))
+    return MOE_ERR_ALIGN;
+  const WsLayout L = ws_layout(desc, 0);
+  rc = check_ws(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  hipStream_t st = as_stream(stream);
+  const int H = desc->hidden, E = desc->n_experts, k = desc->top_k;
+  float* xn = io->xn ? io->xn : at<float>(ws, L.xn);
+  void* xq = io->xq ? io->xq : at<void>(ws, L.xq);
+  int32_t* ids = io->ids ? io->ids : at<int32_t>(ws, L.ids);
+  float* wts = io->weights ? io->weights : at<float>(ws, L.wts);
+  float* sg = io->shared_gate ? io->shared_gate : at<float>(ws, L.sg);
+  float* h = io->h ? io->h : at<float>(ws, L.h);
+  float* hs = io->hs ? io->hs : at<float>(ws, L.hs);
+  if (desc->norm) {
+    rc = launch_norm(io->residual, io->routed_in, io->shared_in, w->norm_w, H, 1, desc->eps, io->out_sum, xn, xq, 1, st);
+  } else {
+    if (io->xn) {
+      if (hipMemcpyAsync(xn, io->x, sizeof(float) * H, hipMemcpyDeviceToDevice, st) != hipSuccess) return MOE_ERR_HIP;
+    }
+    xn = io->xn ? io->xn : const_cast<float*>(io->x);
+    rc = launch_quantize(io->x, H, xq, st);
+  }
+  if (rc) return rc;
+  rc = launch_router(xn, w->router_w, desc->shared_ffn > 0 ? w->shared_gate_w : nullptr, 1, H, E, k,
+                     at<float>(ws, L.logits), io->logits, ids, wts, sg, at<unsigned>(ws, L.counters), st);
+  if (rc) return rc;
+  rc = launch_gate_up(desc, w, xq, ids, h, hs, st);
+  if (rc) return rc;
+  return launch_down(desc, w, h, hs, ids, wts, sg, io->routed_out, io->shared_out, st);
+}
+
+int moe_stack_bind(const moe_layer_desc* desc, const moe_layer_weights* layers, int n_layers, void* ws,
+                   size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!desc->norm) return MOE_ERR_UNSUPPORTED;
+  if (!layers) return MOE_ERR_NULL;
+  if (n_layers <= 0 || n_layers > MOE_MAX_LAYERS) return MOE_ERR_SHAPE;
+  for (int l = 0; l < n_layers; ++l)
+    if ((rc = check_weights(desc, &layers[l]))) return rc;
+  const WsLayout L = ws_layout(desc, n_layers);
+  rc = check_ws(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  hipStream_t st = as_stream(stream);
+  if (hipMemcpyAsync(at<void>(ws, L.table), layers, sizeof(moe_layer_weights) * n_layers, hipMemcpyHostToDevice, st) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  int bound[4] = {n_layers, 0, 0, 0};
+  if (hipMemcpyAsync(at<void>(ws, L.bound), bound, sizeof(bound), hipMemcpyHostToDevice, st) != hipSuccess)
+    return MOE_ERR_HIP;
+  return hipStreamSynchronize(st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers, int n_layers, const uint16_t* input,
+                     uint16_t* output, int32_t* ids_per_layer, uint16_t* resid_per_layer, int mode, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!desc->norm) return MOE_ERR_UNSUPPORTED;
+  if (!layers || !input || !output) return MOE_ERR_NULL;
+  if (n_layers <= 0 || n_layers > MOE_MAX_LAYERS) return MOE_ERR_SHAPE;
+  if (mode != MOE_STACK_AUTO && mode != MOE_STACK_KERNELS && mode != MOE_STACK_PERSISTENT) return MOE_ERR_SHAPE;
+  for (int l = 0; l < n_layers; ++l)
+    if ((rc = check_weights(desc, &layers[l]))) return rc;
+  if (!aligned(input, 2) || !aligned(output, 2) || (ids_per_layer && !aligned(ids_per_layer, 4)) ||
+      (resid_per_layer && !aligned(resid_per_layer, 2)))
+    return MOE_ERR_ALIGN;
+  const WsLayout L = ws_layout(desc, n_layers);
+  rc = check_ws(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  if (mode == MOE_STACK_PERSISTENT) return MOE_ERR_UNSUPPORTED;
+  hipStream_t st = as_stream(stream);
+  const int H = desc->hidden, E = desc->n_experts, k = desc->top_k;
+  const bool has_shared = desc->shared_ffn > 0;
+  uint16_t* routed = at<uint16_t>(ws, L.routed);
+  uint16_t* shared = at<uint16_t>(ws, L.shared);
+  const uint16_t* res_in = input;
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer_weights* w = &layers[l];
+    uint16_t* res_out = resid_per_layer ? resid_per_layer + (size_t)l * H : at<uint16_t>(ws, L.res);
+    int32_t* ids = ids_per_layer ? ids_per_layer + (size_t)l * k : at<int32_t>(ws, L.ids);
+    rc = launch_norm(res_in, l ? routed : nullptr, (l && has_shared) ? shared : nullptr, w->norm_w, H, 1, desc->eps,
+                     res_out, at<float>(ws, L.xn), at<void>(ws, L.xq), 1, st);
+    if (rc) return rc;
+    rc = launch_router(at<float>(ws, L.xn), w->router_w, has_shared ? w->shared_gate_w : nullptr, 1, H, E, k,
+                       at<float>(ws, L.logits), nullptr, ids, at<float>(ws, L.wts), at<float>(ws, L.sg),
+                       at<unsigned>(ws, L.counters), st);
+    if (rc) return rc;
+    rc = launch_gate_up(desc, w, at<void>(ws, L.xq), ids, at<float>(ws, L.h), at<float>(ws, L.hs), st);
+    if (rc) return rc;
+    rc = launch_down(desc, w, at<float>(ws, L.h), at<float>(ws, L.hs), ids, at<float>(ws, L.wts), at<float>(ws, L.sg),
+                     routed, has_shared ? shared : nullptr, st);
+    if (rc) return rc;
+    res_in = res_out;
+  }
+  // the fold the next layer's norm would do: output = bf16(res_L + bf16(routed + shared))
+  return launch_norm(res_in, routed, has_shared ? shared : nullptr, nullptr, H, 1, desc->eps, output, nullptr, nullptr, 0,
+                     st);
+}
+
+int moe_test_subblock_dots(const void* rows, int type, int K, int n_rows, const void* xq, int32_t* out, void* stream) {
+  if (!rows || !xq || !out) return MOE_ERR_NULL;
+  if (type != MOE_TYPE_Q4_K && type != MOE_TYPE_Q5_K && type != MOE_TYPE_Q8_0) return MOE_ERR_TYPE;
+  if (K <= 0 || K % 256 || K > MOE_MAX_HIDDEN || n_rows <= 0 || n_rows > 65535) return MOE_ERR_SHAPE;
+  if (!aligned(rows, 16) || !aligned(xq, 4) || !aligned(out, 4)) return MOE_ERR_ALIGN;
+  return launch_subblock_dots(rows, type, K, n_rows, xq, out, as_stream(stream));
+}
+
+}  // extern "C"

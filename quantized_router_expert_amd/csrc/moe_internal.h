@@ -1,0 +1,42 @@
+// moe_internal.h -- host/device declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_decode.h"
+
+namespace moe {
+
+constexpr int kNormThreads = 256;
+constexpr int kRouterThreads = 256;
+constexpr int kFfnThreads = 256;
+constexpr int kTopkPerLane = MOE_MAX_EXPERTS / 64;
+constexpr int kCounterSlots = 4096;
+constexpr int kGateUpRows = 16;
+constexpr int kDownRows = 8;
+constexpr size_t kLdsBudget = 64 * 1024;
+
+// Byte offsets of the workspace regions (all 256-byte aligned).
+struct WsLayout {
+  size_t counters, xn, xq, logits, ids, wts, sg, h, hs, res, routed, shared, table, bound, total;
+};
+WsLayout ws_layout(const moe_layer_desc* d, int n_layers);
+
+int check_desc(const moe_layer_desc* d);
+int check_weights(const moe_layer_desc* d, const moe_layer_weights* w);
+
+int launch_norm(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, const float* w, int H, int n_tok,
+                float eps, uint16_t* out_sum, float* xn, void* xq, int do_norm, hipStream_t st);
+int launch_quantize(const float* x, int n, void* xq, hipStream_t st);
+int launch_router(const float* xn, const float* W, const float* wsg, int n_tok, int H, int E, int k, float* logits,
+                  float* user_logits, int32_t* ids, float* wts, float* sg, unsigned* counters, hipStream_t st);
+int launch_gate_up(const moe_layer_desc* d, const moe_layer_weights* w, const void* xq, const int32_t* ids, float* h,
+                   float* hs, hipStream_t st);
+int launch_down(const moe_layer_desc* d, const moe_layer_weights* w, const float* h, const float* hs, const int32_t* ids,
+                const float* wts, const float* sg, uint16_t* routed, uint16_t* shared, hipStream_t st);
+int launch_fill(void* p, size_t n_u32, uint32_t v, hipStream_t st);
+int launch_subblock_dots(const void* rows, int type, int K, int n_rows, const void* xq, int32_t* out, hipStream_t st);
+
+}  // namespace moe

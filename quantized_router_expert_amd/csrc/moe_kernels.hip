@@ -1,0 +1,671 @@
+// moe_kernels.hip -- gfx950 kernels and the C ABI of the batch-1 decode MoE stage.
+//
+// Per-layer kernels (one launch each, used by the separate entry points, by
+// moe_decode_layer and by the per-layer stack mode):
+//   k_add_rmsnorm   a1: fold + RMSNorm + Q8_1, one workgroup per token
+//   k_router_topk   a2+a3: fp32 GEMV rows (fp64 accumulate) + last-workgroup top-k/softmax
+//   k_gate_up       a4 (+a6 gate/up): Q4_K/Q8_0 rows x Q8_1 + SwiGLU, rows staged in LDS
+//   k_down_combine  a5 (+a6 down): Q8_1 of h in LDS, down rows x Q8_1, weighted combine
+// Source pages: [P273] fused router GEMV+top-k + folded residual-norm;
+// [P239] fused shared-expert launches; [P359] Q4_K shared-expert FFN kernels.
+#include "../../include/moe_decode.h"
+#include "moe_device.h"
+#include "moe_internal.h"
+
+#include <string.h>
+
+namespace moe {
+
+// =====================================================================
+// a1: residual add folded into RMSNorm, Q8_1 of the normed vector
+// =====================================================================
+// t = shared ? bf16(routed + shared) : routed ; u = bf16(residual + t) -> out_sum.
+// sum(u^2) is reduced in fp64; r = 1/sqrt(mean + eps) in fp64; xn = f32((u*r)*w).
+// Thread i handles elements i, i+256, ...: each 32-element Q8_1 block is held by
+// 32 consecutive lanes.
+__device__ void norm_token_block(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, const float* w,
+                                 int H, float eps, uint16_t* out_sum, float* xn_out, uint8_t* xq_out,
+                                 float* u_lds, double* red_lds, int do_norm) {
+  const int tid = threadIdx.x;
+  double ss = 0.0;
+  for (int i = tid; i < H; i += kNormThreads) {
+    float t = 0.0f;
+    if (rt && sh) t = bf16_to_f32(f32_to_bf16(bf16_to_f32(rt[i]) + bf16_to_f32(sh[i])));
+    else if (rt) t = bf16_to_f32(rt[i]);
+    const uint16_t ub = f32_to_bf16(bf16_to_f32(res[i]) + t);
+    if (out_sum) out_sum[i] = ub;
+    const float u = bf16_to_f32(ub);
+    u_lds[i] = u;
+    ss += (double)u * (double)u;
+  }
+  if (!do_norm) return;
+  ss = wave_sum_f64(ss);
+  if ((tid & 63) == 0) red_lds[tid >> 6] = ss;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int wv = 0; wv < kNormThreads / 64; ++wv) tot += red_lds[wv];
+  const double r = 1.0 / sqrt(tot / (double)H + (double)eps);
+  for (int i = tid; i < H; i += kNormThreads) {
+    const float x = (float)(((double)u_lds[i] * r) * (double)w[i]);
+    if (xn_out) xn_out[i] = x;
+    if (xq_out) {
+      Q81Lane q = quantize_q81_lane(x);
+      const int blk = i >> 5, l = i & 31;
+      uint8_t* ob = xq_out + (long)blk * kQ81Bytes;
+      if (l == 0) *reinterpret_cast<uint32_t*>(ob) = q.ds;
+      ob[4 + l] = (uint8_t)(int8_t)q.q;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kNormThreads) void k_add_rmsnorm(const uint16_t* res, const uint16_t* rt, const uint16_t* sh,
+                                                               const float* w, int H, float eps, uint16_t* out_sum,
+                                                               float* xn, uint8_t* xq, int do_norm) {
+  __shared__ float u_lds[MOE_MAX_HIDDEN];
+  __shared__ double red_lds[kNormThreads / 64];
+  const long tok = blockIdx.x;
+  norm_token_block(res + tok * H, rt ? rt + tok * H : nullptr, sh ? sh + tok * H : nullptr, w, H, eps,
+                   out_sum ? out_sum + tok * H : nullptr, xn ? xn + tok * H : nullptr,
+                   xq ? xq + tok * (H / 32) * kQ81Bytes : nullptr, u_lds, red_lds, do_norm);
+}
+
+// Plain Q8_1 of an fp32 vector (the layer input when the layer has no norm).
+__global__ __launch_bounds__(kNormThreads) void k_quantize_q81(const float* x, int n, uint8_t* xq) {
+  for (int i = blockIdx.x * kNormThreads + threadIdx.x; i < n; i += gridDim.x * kNormThreads) {
+    Q81Lane q = quantize_q81_lane(x[i]);
+    uint8_t* ob = xq + (long)(i >> 5) * kQ81Bytes;
+    if ((i & 31) == 0) *reinterpret_cast<uint32_t*>(ob) = q.ds;
+    ob[4 + (i & 31)] = (uint8_t)(int8_t)q.q;
+  }
+}
+
+// =====================================================================
+// a2 + a3: router GEMV + last-workgroup top-k + routing weights
+// =====================================================================
+// Orderable 64-bit key: larger key = larger logit, ties broken toward the lower
+// index.  -0 is canonicalised to +0 (IEEE equality ties them) and NaN to -inf.
+__device__ __forceinline__ unsigned long long topk_key(float v, int e) {
+  if (v != v) v = -__builtin_inff();
+  if (v == 0.0f) v = 0.0f;
+  uint32_t b = __float_as_uint(v);
+  uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)o << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
+}
+
+// Wave-level top-k over E <= 64*kTopkPerLane logits held in memory.  Each lane
+// keeps its keys; k rounds of a wave-wide 64-bit max pick the slots in rank order.
+__device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* ids_out, float* w_out) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long key[kTopkPerLane];
+#pragma unroll
+  for (int j = 0; j < kTopkPerLane; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = (e < E) ? topk_key(logits[e], e) : 0ull;
+  }
+  int sel[MOE_MAX_TOPK];
+  for (int s = 0; s < k; ++s) {
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int j = 0; j < kTopkPerLane; ++j) best = key[j] > best ? key[j] : best;
+    unsigned long long wbest = best;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      unsigned long long other = __shfl_xor(wbest, o, 64);
+      wbest = other > wbest ? other : wbest;
+    }
+#pragma unroll
+    for (int j = 0; j < kTopkPerLane; ++j)
+      if (key[j] == wbest) key[j] = 0ull;
+    sel[s] = (int)(0xffffffffu - (uint32_t)(wbest & 0xffffffffull));
+  }
+  if (lane == 0) {
+    // softmax over the selected logits, shifted by the largest (slot 0), fp64
+    const double m = (double)logits[sel[0]];
+    double p[MOE_MAX_TOPK];
+    double sum = 0.0;
+    for (int s = 0; s < k; ++s) {
+      p[s] = exp((double)logits[sel[s]] - m);
+      sum += p[s];
+    }
+    for (int s = 0; s < k; ++s) {
+      ids_out[s] = sel[s];
+      w_out[s] = (float)(p[s] / sum);
+    }
+  }
+}
+
+// grid (nblk, n_tok): each wave computes one row (router row e < E, or the
+// shared-gate row e == E).  The last workgroup to finish (a wrapping atomic
+// increment returns nblk-1 to it and leaves 0 behind) selects.
+__global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn, const float* W, const float* wsg,
+                                                                 int H, int E, int k, float* logits, float* user_logits,
+                                                                 int32_t* ids, float* wts, float* sg_out,
+                                                                 unsigned* counters) {
+  const int logits_stride = E + 1;
+  const int tok = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nrows = E + (wsg ? 1 : 0);
+  const int row = blockIdx.x * (kRouterThreads / 64) + wave;
+  const float* x = xn + (long)tok * H;
+  float* lg = logits + (long)tok * logits_stride;
+  if (row < nrows) {
+    const float* wr = (row < E) ? W + (long)row * H : wsg;
+    double acc = 0.0;
+    for (int i = lane * 4; i < H; i += 256) {
+      const float4 a = *reinterpret_cast<const float4*>(wr + i);
+      const float4 b = *reinterpret_cast<const float4*>(x + i);
+      acc += (double)a.x * (double)b.x;
+      acc += (double)a.y * (double)b.y;
+      acc += (double)a.z * (double)b.z;
+      acc += (double)a.w * (double)b.w;
+    }
+    acc = wave_sum_f64(acc);
+    if (lane == 0) lg[row] = (float)acc;
+  }
+  __shared__ int is_last;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __builtin_amdgcn_atomic_inc32(counters + tok, gridDim.x - 1, __ATOMIC_ACQ_REL, "agent");
+    is_last = (old == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  if (wave == 0) {
+    wave_topk_softmax(lg, E, k, ids + (long)tok * k, wts + (long)tok * k);
+    if (lane == 0 && sg_out) sg_out[tok] = wsg ? (float)sigmoid_f64((double)lg[E]) : 0.0f;
+  } else if (user_logits) {
+    for (int e = threadIdx.x - 64; e < E; e += kRouterThreads - 64) user_logits[(long)tok * E + e] = lg[e];
+  }
+}
+
+// =====================================================================
+// Row staging and row dots from LDS
+// =====================================================================
+// Copy `bytes` (multiple of 16) from global to LDS with 16-byte loads by all threads.
+__device__ __forceinline__ void stage_to_lds(uint8_t* dst, const uint8_t* src, long bytes, int nthreads) {
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  const int n16 = (int)(bytes >> 4);
+  for (int i = threadIdx.x; i < n16; i += nthreads) d[i] = s[i];
+}
+
+// Q8_1 activations (global, 36-byte blocks) -> LDS codes/d/s.
+__device__ void load_act_lds(const uint8_t* xq, int K, uint8_t* codes, float* d, float* s, int nthreads) {
+  const int nb = K / 32;
+  for (int i = threadIdx.x; i < nb * 8; i += nthreads) {
+    const int b = i >> 3, t = i & 7;
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(xq + (long)b * kQ81Bytes + 4 + 4 * t);
+    reinterpret_cast<uint32_t*>(codes)[i] = v;
+  }
+  for (int b = threadIdx.x; b < nb; b += nthreads) {
+    const uint32_t ds = *reinterpret_cast<const uint32_t*>(xq + (long)b * kQ81Bytes);
+    d[b] = f16_to_f32(ds);
+    s[b] = f16_to_f32(ds >> 16);
+  }
+}
+
+// All tasks of `nrows` rows of K elements staged back to back at `rows`:
+// partial[r*T + t] = fp64 contribution of task t of row r.
+template <int TYPE>
+__device__ void rows_partials(const uint8_t* rows, long rbytes, int nrows, int K, const ActLds& act, double* partial,
+                              int nthreads) {
+  const int T = tasks_per_row(TYPE, K);
+  const int total = nrows * T;
+  for (int i = threadIdx.x; i < total; i += nthreads) {
+    const int r = i / T, t = i - r * T;
+    partial[i] = row_task<TYPE>(rows + (long)r * rbytes, t, act);
+  }
+}
+
+__device__ __forceinline__ double sum_partials(const double* p, int T) {
+  double a = 0.0;
+  for (int t = 0; t < T; ++t) a += p[t];
+  return a;
+}
+
+// =====================================================================
+// a4 (+ a6 gate/up): gate/up rows + SwiGLU
+// =====================================================================
+// Block b < k*cpe handles routed slot b/cpe, rows [(b%cpe)*R, +R); the rest
+// handle the shared expert's rows.  Gate and up rows of a chunk are contiguous
+// in memory and staged into LDS with 16-byte loads.
+struct GateUpArgs {
+  const uint8_t* xq;
+  const int32_t* ids;
+  const uint8_t* gate;
+  const uint8_t* up;
+  const uint8_t* sgate;
+  const uint8_t* sup;
+  float* h;
+  float* hs;
+  int H, F, Fs, k, E, R, cpe, cps;
+  int type, stype;
+};
+
+template <int TYPE>
+__device__ void gate_up_chunk(const uint8_t* gate_rows, const uint8_t* up_rows, int nr, int H, const ActLds& act,
+                              uint8_t* stage, double* partial, float* h_out) {
+  const long rb = row_bytes(TYPE, H);
+  stage_to_lds(stage, gate_rows, nr * rb, blockDim.x);
+  stage_to_lds(stage + nr * rb, up_rows, nr * rb, blockDim.x);
+  __syncthreads();
+  rows_partials<TYPE>(stage, rb, 2 * nr, H, act, partial, blockDim.x);
+  __syncthreads();
+  const int T = tasks_per_row(TYPE, H);
+  for (int f = threadIdx.x; f < nr; f += blockDim.x) {
+    const float g = (float)sum_partials(partial + (long)f * T, T);
+    const float u = (float)sum_partials(partial + (long)(nr + f) * T, T);
+    h_out[f] = (float)(silu_f64((double)g) * (double)u);
+  }
+}
+
+__global__ __launch_bounds__(kFfnThreads) void k_gate_up(GateUpArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int H = a.H;
+  uint8_t* codes = smem;
+  float* dact = reinterpret_cast<float*>(smem + H);
+  float* sact = dact + H / 32;
+  uint8_t* stage = reinterpret_cast<uint8_t*>(sact + H / 32);
+  stage = reinterpret_cast<uint8_t*>(((uintptr_t)stage + 15) & ~(uintptr_t)15);
+  load_act_lds(a.xq, H, codes, dact, sact, blockDim.x);
+  __syncthreads();
+  ActLds act{codes, dact, sact};
+  const int b = blockIdx.x;
+  if (b < a.k * a.cpe) {
+    const int slot = b / a.cpe;
+    const int f0 = (b % a.cpe) * a.R;
+    const int nr = min(a.R, a.F - f0);
+    const long e = a.ids[slot];
+    if (e < 0 || e >= a.E) {  // an id outside the experts reads nothing and yields NaN
+      for (int f = threadIdx.x; f < nr; f += blockDim.x) a.h[(long)slot * a.F + f0 + f] = __builtin_nanf("");
+      return;
+    }
+    const long rb = row_bytes(MOE_TYPE_Q4_K, H);
+    const uint8_t* g = a.gate + (e * a.F + f0) * rb;
+    const uint8_t* u = a.up + (e * a.F + f0) * rb;
+    double* partial = reinterpret_cast<double*>(stage + 2 * (long)a.R * rb + 16);
+    gate_up_chunk<MOE_TYPE_Q4_K>(g, u, nr, H, act, stage, partial, a.h + (long)slot * a.F + f0);
+  } else {
+    const int f0 = (b - a.k * a.cpe) * a.R;
+    const int nr = min(a.R, a.Fs - f0);
+    const long rb = row_bytes(a.stype, H);
+    double* partial = reinterpret_cast<double*>(stage + 2 * (long)a.R * rb + 16);
+    if (a.stype == MOE_TYPE_Q8_0)
+      gate_up_chunk<MOE_TYPE_Q8_0>(a.sgate + f0 * rb, a.sup + f0 * rb, nr, H, act, stage, partial, a.hs + f0);
+    else
+      gate_up_chunk<MOE_TYPE_Q4_K>(a.sgate + f0 * rb, a.sup + f0 * rb, nr, H, act, stage, partial, a.hs + f0);
+  }
+}
+
+// =====================================================================
+// a5 (+ a6 down): Q8_1 of h, down rows, weighted combine
+// =====================================================================
+struct DownArgs {
+  const float* h;         // [k][F]
+  const float* hs;        // [Fs]
+  const int32_t* ids;
+  const float* wts;
+  const float* sg;        // [1]
+  const uint8_t* down;    // [E][H] rows of Kp
+  const uint8_t* sdown;   // [H] rows of Kps
+  uint16_t* routed;
+  uint16_t* shared;
+  int H, F, Fs, k, E, Ro;
+  int dtype, stype;
+  int Kp, Kps;
+};
+
+// Q8_1 of n values (n multiple of 32) into LDS codes/d/s, zero blocks up to np.
+__device__ void quantize_to_lds(const float* x, int n, int np, uint8_t* codes, float* d, float* s) {
+  const int nthreads = blockDim.x;
+  for (int i0 = 0; i0 < np; i0 += nthreads) {
+    const int i = i0 + threadIdx.x;
+    // whole 32-blocks per half wave: np is a multiple of 32 and nthreads of 64
+    const float v = (i < n) ? x[i] : 0.0f;
+    Q81Lane q = quantize_q81_lane(v);
+    if (i < np) {
+      codes[i] = (uint8_t)(int8_t)q.q;
+      if ((i & 31) == 0) {
+        d[i >> 5] = f16_to_f32(q.ds);
+        s[i >> 5] = f16_to_f32(q.ds >> 16);
+      }
+    }
+  }
+}
+
+template <int DT, int ST>
+__device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
+  const int nm = a.k + (a.Fs > 0 ? 1 : 0);
+  const int Kp = a.Kp, Kps = a.Kps;
+  // layout: codes [k][Kp] | codes_s [Kps] | d,s [k][Kp/32] | d,s [Kps/32] | stage | partials | y
+  uint8_t* codes = smem;
+  uint8_t* codes_s = codes + (long)a.k * Kp;
+  float* dact = reinterpret_cast<float*>(codes_s + Kps);
+  float* sact = dact + a.k * (Kp / 32);
+  float* dsh = sact + a.k * (Kp / 32);
+  float* ssh = dsh + Kps / 32;
+  uint8_t* stage = reinterpret_cast<uint8_t*>((((uintptr_t)(ssh + Kps / 32)) + 15) & ~(uintptr_t)15);
+  const long rb = row_bytes(DT, Kp);
+  const long rbs = a.Fs > 0 ? row_bytes(ST, Kps) : 0;
+  const int i0 = blockIdx.x * a.Ro;
+  const int nr = min(a.Ro, a.H - i0);
+  uint8_t* stage_s = stage + (long)a.k * a.Ro * rb;
+  double* partial = reinterpret_cast<double*>(stage_s + (long)a.Ro * rbs + 16);
+  const int T = tasks_per_row(DT, Kp);
+  const int Ts = a.Fs > 0 ? tasks_per_row(ST, Kps) : 0;
+  double* partial_s = partial + (long)a.k * a.Ro * T;
+  float* y = reinterpret_cast<float*>(partial_s + (long)a.Ro * Ts);
+
+  bool bad_id = false;
+  for (int s = 0; s < a.k; ++s) bad_id |= (a.ids[s] < 0 || a.ids[s] >= a.E);
+  if (bad_id) {  // an id outside the experts reads nothing and yields NaN outputs
+    for (int r = threadIdx.x; r < nr; r += blockDim.x) {
+      a.routed[i0 + r] = 0x7fc0u;
+      if (a.Fs > 0 && a.shared) a.shared[i0 + r] = 0x7fc0u;
+    }
+    return;
+  }
+
+  // stage the weight rows first so their loads are in flight during the quantisation
+  for (int s = 0; s < a.k; ++s) {
+    const long e = a.ids[s];
+    stage_to_lds(stage + (long)s * a.Ro * rb, a.down + (e * a.H + i0) * rb, nr * rb, blockDim.x);
+  }
+  if (a.Fs > 0) stage_to_lds(stage_s, a.sdown + (long)i0 * rbs, nr * rbs, blockDim.x);
+  for (int s = 0; s < a.k; ++s)
+    quantize_to_lds(a.h + (long)s * a.F, a.F, Kp, codes + (long)s * Kp, dact + s * (Kp / 32), sact + s * (Kp / 32));
+  if (a.Fs > 0) quantize_to_lds(a.hs, a.Fs, Kps, codes_s, dsh, ssh);
+  __syncthreads();
+  // tasks of all routed rows
+  const int total = a.k * nr * T;
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int s = i / (nr * T);
+    const int rem = i - s * nr * T;
+    const int r = rem / T, t = rem - r * T;
+    ActLds act{codes + (long)s * Kp, dact + s * (Kp / 32), sact + s * (Kp / 32)};
+    partial[((long)s * a.Ro + r) * T + t] = row_task<DT>(stage + ((long)s * a.Ro + r) * rb, t, act);
+  }
+  if (a.Fs > 0) {
+    ActLds acts{codes_s, dsh, ssh};
+    for (int i = threadIdx.x; i < nr * Ts; i += blockDim.x) {
+      const int r = i / Ts, t = i - r * Ts;
+      partial_s[(long)r * Ts + t] = row_task<ST>(stage_s + (long)r * rbs, t, acts);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nm * nr; i += blockDim.x) {
+    const int m = i / nr, r = i - m * nr;
+    const double v = (m < a.k) ? sum_partials(partial + ((long)m * a.Ro + r) * T, T) : sum_partials(partial_s + (long)r * Ts, Ts);
+    y[m * a.Ro + r] = (float)v;
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < nr; r += blockDim.x) {
+    double acc = 0.0;
+    for (int s = 0; s < a.k; ++s) acc += (double)a.wts[s] * (double)y[s * a.Ro + r];
+    a.routed[i0 + r] = f32_to_bf16((float)acc);
+    if (a.Fs > 0 && a.shared) a.shared[i0 + r] = f32_to_bf16((float)((double)a.sg[0] * (double)y[a.k * a.Ro + r]));
+  }
+}
+
+__global__ __launch_bounds__(kFfnThreads) void k_down_combine(DownArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  if (a.dtype == MOE_TYPE_Q5_K) {
+    if (a.stype == MOE_TYPE_Q8_0) down_combine_body<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0>(a, smem);
+    else down_combine_body<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K>(a, smem);
+  } else {
+    if (a.stype == MOE_TYPE_Q8_0) down_combine_body<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0>(a, smem);
+    else down_combine_body<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K>(a, smem);
+  }
+}
+
+// =====================================================================
+// Test export: integer sub-block dots, through the same integer path
+// =====================================================================
+template <int TYPE>
+__device__ void subblock_dots_row(const uint8_t* row, int K, const ActLds& act, int32_t* out) {
+  const int T = tasks_per_row(TYPE, K);
+  for (int t = threadIdx.x; t < T; t += blockDim.x) {
+    if (TYPE == MOE_TYPE_Q8_0) {
+      float d;
+      uint32_t w[8], av[8];
+      q80_load(row, t, d, w);
+      lds_load8(act.codes + 32 * t, av);
+      out[t] = q8_block_dot(w, av);
+    } else {
+      const int b = t >> 2, g = t & 3;
+      const uint8_t* blk = row + (long)b * block_bytes(TYPE);
+      uint32_t qs[8], qh[8], alo[8], ahi[8];
+      if (TYPE == MOE_TYPE_Q5_K) {
+        lds_load8(blk + 16, qh);
+        lds_load8(blk + 48 + 32 * g, qs);
+      } else {
+        lds_load8(blk + 16 + 32 * g, qs);
+      }
+      lds_load8(act.codes + 32 * (8 * b + 2 * g), alo);
+      lds_load8(act.codes + 32 * (8 * b + 2 * g + 1), ahi);
+      int lo, hi;
+      kquant_group_dots<TYPE == MOE_TYPE_Q5_K>(qs, qh, g, alo, ahi, lo, hi);
+      out[8 * b + 2 * g] = lo;
+      out[8 * b + 2 * g + 1] = hi;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kFfnThreads) void k_subblock_dots(const uint8_t* rows, int type, int K, const uint8_t* xq,
+                                                                int32_t* out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* codes = smem;
+  float* d = reinterpret_cast<float*>(smem + K);
+  float* s = d + K / 32;
+  uint8_t* stage = reinterpret_cast<uint8_t*>((((uintptr_t)(s + K / 32)) + 15) & ~(uintptr_t)15);
+  load_act_lds(xq, K, codes, d, s, blockDim.x);
+  const long rb = row_bytes(type, K);
+  stage_to_lds(stage, rows + blockIdx.x * rb, rb, blockDim.x);
+  __syncthreads();
+  ActLds act{codes, d, s};
+  int32_t* o = out + (long)blockIdx.x * (K / 32);
+  if (type == MOE_TYPE_Q4_K) subblock_dots_row<MOE_TYPE_Q4_K>(stage, K, act, o);
+  else if (type == MOE_TYPE_Q5_K) subblock_dots_row<MOE_TYPE_Q5_K>(stage, K, act, o);
+  else subblock_dots_row<MOE_TYPE_Q8_0>(stage, K, act, o);
+}
+
+__global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// =====================================================================
+// Host side
+// =====================================================================
+static inline int launch_ok() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_desc(const moe_layer_desc* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->hidden <= 0 || d->hidden % 256 || d->hidden > MOE_MAX_HIDDEN) return MOE_ERR_SHAPE;
+  if (d->n_experts <= 0 || d->n_experts > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (d->top_k <= 0 || d->top_k > d->n_experts || d->top_k > MOE_MAX_TOPK) return MOE_ERR_SHAPE;
+  if (d->ffn <= 0 || d->ffn % 32 || d->ffn > MOE_MAX_FFN) return MOE_ERR_SHAPE;
+  if (d->shared_ffn < 0 || d->shared_ffn % 32 || d->shared_ffn > MOE_MAX_FFN) return MOE_ERR_SHAPE;
+  if (d->gate_up_type != MOE_TYPE_Q4_K) return MOE_ERR_TYPE;
+  if (d->down_type != MOE_TYPE_Q4_K && d->down_type != MOE_TYPE_Q5_K) return MOE_ERR_TYPE;
+  if (d->shared_ffn > 0 && d->shared_type != MOE_TYPE_Q4_K && d->shared_type != MOE_TYPE_Q8_0) return MOE_ERR_TYPE;
+  // Q8_0 rows are staged with 16-byte loads: a row must be a multiple of 16 bytes (K % 256 == 0)
+  if (d->shared_ffn > 0 && d->shared_type == MOE_TYPE_Q8_0 && (d->shared_ffn % 256)) return MOE_ERR_SHAPE;
+  if (d->norm != 0 && d->norm != 1) return MOE_ERR_SHAPE;
+  if (!(d->eps >= 0.0f)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int check_weights(const moe_layer_desc* d, const moe_layer_weights* w) {
+  if (!w) return MOE_ERR_NULL;
+  if (!w->router_w || !w->gate || !w->up || !w->down) return MOE_ERR_NULL;
+  if (d->norm && !w->norm_w) return MOE_ERR_NULL;
+  if (d->shared_ffn > 0 && (!w->shared_gate_w || !w->shared_gate || !w->shared_up || !w->shared_down)) return MOE_ERR_NULL;
+  const void* p16[] = {w->router_w, w->gate, w->up, w->down, w->shared_gate, w->shared_up, w->shared_down, w->shared_gate_w};
+  for (const void* p : p16)
+    if (p && !aligned(p, 16)) return MOE_ERR_ALIGN;
+  if (w->norm_w && !aligned(w->norm_w, 4)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- workspace layout
+static inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const moe_layer_desc* d, int n_layers) {
+  WsLayout L;
+  size_t o = 0;
+  L.counters = o; o += up256(sizeof(unsigned) * kCounterSlots);
+  L.xn = o; o += up256(sizeof(float) * d->hidden);
+  L.xq = o; o += up256((size_t)(d->hidden / 32) * kQ81Bytes);
+  L.logits = o; o += up256(sizeof(float) * (d->n_experts + 1));
+  L.ids = o; o += up256(sizeof(int32_t) * d->top_k);
+  L.wts = o; o += up256(sizeof(float) * d->top_k);
+  L.sg = o; o += up256(sizeof(float));
+  L.h = o; o += up256(sizeof(float) * (size_t)d->top_k * d->ffn);
+  L.hs = o; o += up256(sizeof(float) * (size_t)(d->shared_ffn > 0 ? d->shared_ffn : 1));
+  L.res = o; o += up256(sizeof(uint16_t) * d->hidden);
+  L.routed = o; o += up256(sizeof(uint16_t) * d->hidden);
+  L.shared = o; o += up256(sizeof(uint16_t) * d->hidden);
+  L.table = o; o += up256(sizeof(moe_layer_weights) * (size_t)(n_layers > 0 ? n_layers : 1));
+  L.bound = o; o += up256(sizeof(int) * 4);
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------------- launch helpers
+int launch_norm(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, const float* w, int H, int n_tok,
+                float eps, uint16_t* out_sum, float* xn, void* xq, int do_norm, hipStream_t st) {
+  hipLaunchKernelGGL(k_add_rmsnorm, dim3(n_tok), dim3(kNormThreads), 0, st, res, rt, sh, w, H, eps, out_sum, xn,
+                     (uint8_t*)xq, do_norm);
+  return launch_ok();
+}
+
+int launch_quantize(const float* x, int n, void* xq, hipStream_t st) {
+  int blocks = (n + kNormThreads - 1) / kNormThreads;
+  hipLaunchKernelGGL(k_quantize_q81, dim3(blocks), dim3(kNormThreads), 0, st, x, n, (uint8_t*)xq);
+  return launch_ok();
+}
+
+int launch_router(const float* xn, const float* W, const float* wsg, int n_tok, int H, int E, int k, float* logits,
+                  float* user_logits, int32_t* ids, float* wts, float* sg, unsigned* counters, hipStream_t st) {
+  const int nrows = E + (wsg ? 1 : 0);
+  const int rpb = kRouterThreads / 64;
+  const int nblk = (nrows + rpb - 1) / rpb;
+  hipLaunchKernelGGL(k_router_topk, dim3(nblk, n_tok), dim3(kRouterThreads), 0, st, xn, W, wsg, H, E, k, logits,
+                     user_logits, ids, wts, sg, counters);
+  return launch_ok();
+}
+
+size_t gate_up_lds(int H, int R, int rtype) {
+  const long rb = row_bytes(rtype, H);
+  size_t act = (size_t)H + 2 * sizeof(float) * (H / 32) + 16;
+  size_t stage = 2 * (size_t)R * rb + 16;
+  size_t part = sizeof(double) * 2 * (size_t)R * tasks_per_row(rtype, H);
+  return act + stage + part + 16;
+}
+
+int pick_gate_up_rows(int H, int rtype) {
+  int R = kGateUpRows;
+  while (R > 1 && gate_up_lds(H, R, rtype) > kLdsBudget) R >>= 1;
+  return R;
+}
+
+int launch_gate_up(const moe_layer_desc* d, const moe_layer_weights* w, const void* xq, const int32_t* ids, float* h,
+                   float* hs, hipStream_t st) {
+  GateUpArgs a;
+  a.xq = (const uint8_t*)xq;
+  a.ids = ids;
+  a.gate = (const uint8_t*)w->gate;
+  a.up = (const uint8_t*)w->up;
+  a.sgate = (const uint8_t*)w->shared_gate;
+  a.sup = (const uint8_t*)w->shared_up;
+  a.h = h;
+  a.hs = hs;
+  a.H = d->hidden;
+  a.F = d->ffn;
+  a.Fs = d->shared_ffn;
+  a.k = d->top_k;
+  a.E = d->n_experts;
+  a.type = d->gate_up_type;
+  a.stype = d->shared_type;
+  const int Rr = pick_gate_up_rows(d->hidden, MOE_TYPE_Q4_K);
+  const int Rs = d->shared_ffn > 0 ? pick_gate_up_rows(d->hidden, d->shared_type) : Rr;
+  a.R = Rr < Rs ? Rr : Rs;
+  a.cpe = (a.F + a.R - 1) / a.R;
+  a.cps = a.Fs > 0 ? (a.Fs + a.R - 1) / a.R : 0;
+  size_t lds = gate_up_lds(a.H, a.R, MOE_TYPE_Q4_K);
+  if (a.Fs > 0) {
+    size_t l2 = gate_up_lds(a.H, a.R, a.stype);
+    lds = l2 > lds ? l2 : lds;
+  }
+  const int nblk = a.k * a.cpe + a.cps;
+  hipLaunchKernelGGL(k_gate_up, dim3(nblk), dim3(kFfnThreads), lds, st, a);
+  return launch_ok();
+}
+
+size_t down_lds(const moe_layer_desc* d, int Ro) {
+  const int Kp = pad_k(d->down_type, d->ffn);
+  const int Kps = d->shared_ffn > 0 ? pad_k(d->shared_type, d->shared_ffn) : 0;
+  const int k = d->top_k;
+  size_t acts = (size_t)k * Kp + Kps + 2 * sizeof(float) * ((size_t)k * (Kp / 32) + Kps / 32) + 16;
+  const long rb = row_bytes(d->down_type, Kp);
+  const long rbs = d->shared_ffn > 0 ? row_bytes(d->shared_type, Kps) : 0;
+  size_t stage = (size_t)k * Ro * rb + (size_t)Ro * rbs + 16;
+  size_t part = sizeof(double) * ((size_t)k * Ro * tasks_per_row(d->down_type, Kp) +
+                                  (size_t)Ro * (d->shared_ffn > 0 ? tasks_per_row(d->shared_type, Kps) : 0));
+  size_t y = sizeof(float) * (size_t)(k + 1) * Ro;
+  return acts + stage + part + y + 32;
+}
+
+int pick_down_rows(const moe_layer_desc* d) {
+  int Ro = kDownRows;
+  while (Ro > 1 && down_lds(d, Ro) > kLdsBudget) Ro >>= 1;
+  return Ro;
+}
+
+int launch_down(const moe_layer_desc* d, const moe_layer_weights* w, const float* h, const float* hs, const int32_t* ids,
+                const float* wts, const float* sg, uint16_t* routed, uint16_t* shared, hipStream_t st) {
+  DownArgs a;
+  a.h = h;
+  a.hs = hs;
+  a.ids = ids;
+  a.wts = wts;
+  a.sg = sg;
+  a.down = (const uint8_t*)w->down;
+  a.sdown = (const uint8_t*)w->shared_down;
+  a.routed = routed;
+  a.shared = shared;
+  a.H = d->hidden;
+  a.F = d->ffn;
+  a.Fs = d->shared_ffn;
+  a.k = d->top_k;
+  a.E = d->n_experts;
+  a.dtype = d->down_type;
+  a.stype = d->shared_ffn > 0 ? d->shared_type : MOE_TYPE_Q4_K;
+  a.Kp = pad_k(d->down_type, d->ffn);
+  a.Kps = d->shared_ffn > 0 ? pad_k(d->shared_type, d->shared_ffn) : 0;
+  a.Ro = pick_down_rows(d);
+  if (down_lds(d, a.Ro) > kLdsBudget) return MOE_ERR_UNSUPPORTED;
+  const int nblk = (a.H + a.Ro - 1) / a.Ro;
+  hipLaunchKernelGGL(k_down_combine, dim3(nblk), dim3(kFfnThreads), down_lds(d, a.Ro), st, a);
+  return launch_ok();
+}
+
+int launch_fill(void* p, size_t n_u32, uint32_t v, hipStream_t st) {
+  if (n_u32 == 0) return MOE_OK;
+  int blocks = (int)((n_u32 + 255) / 256);
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(256), 0, st, (uint32_t*)p, n_u32, v);
+  return launch_ok();
+}
+
+int launch_subblock_dots(const void* rows, int type, int K, int n_rows, const void* xq, int32_t* out, hipStream_t st) {
+  size_t lds = (size_t)K + 2 * sizeof(float) * (K / 32) + 16 + row_bytes(type, K) + 16;
+  hipLaunchKernelGGL(k_subblock_dots, dim3(n_rows), dim3(kFfnThreads), lds, st, (const uint8_t*)rows, type, K,
+                     (const uint8_t*)xq, out);
+  return launch_ok();
+}
+
+}  // namespace moe

@@ -1,0 +1,154 @@
+"""The C-ABI library loads, exports every function include/moe_decode.h
+declares, and rejects invalid arguments with the documented codes on the
+host, before anything is enqueued (these calls need no GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_decode.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\*?([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", "moe_decode_stack",
+              "moe_stack_bind", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
+              "moe_test_subblock_dots"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    import quantized_router_expert_amd as q
+    lib = C.CDLL(q.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in moe_decode.h but not exported"
+    assert set(q.EXPORTS) <= set(declared_functions())
+
+
+@pytest.fixture(scope="module")
+def q():
+    import quantized_router_expert_amd as q
+    return q
+
+
+def _desc(q, **kw):
+    d = dict(hidden=2048, n_experts=256, top_k=8, ffn=512, shared_ffn=512)
+    d.update(kw)
+    return q.make_desc(**d)
+
+
+def test_status_strings(q):
+    assert q.moe_status_string(0) == "ok"
+    for s in range(-1, -9, -1):
+        assert q.moe_status_string(s) != "unknown status"
+
+
+def test_workspace_size(q):
+    assert q.moe_workspace_size(_desc(q)) > 0
+    assert q.moe_workspace_size(_desc(q), 40) > q.moe_workspace_size(_desc(q), 0)
+    assert q.moe_workspace_size(_desc(q, hidden=100)) == 0          # invalid desc -> 0
+    assert q.moe_workspace_size(_desc(q, top_k=300)) == 0
+
+
+FAKE = 0x10000       # 256-aligned fake device address: never dereferenced on these paths
+ODD = 0x10001
+
+
+def test_add_rmsnorm3_validation(q):
+    f = q._add_rmsnorm3
+    ok = dict(res=FAKE, rt=None, sh=None, w=FAKE, H=2048, n=1, eps=1e-6, out=FAKE, xn=None, xq=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["res"], a["rt"], a["sh"], a["w"], a["H"], a["n"], a["eps"], a["out"], a["xn"], a["xq"], None)
+
+    assert call(res=None) == -1
+    assert call(w=None) == -1
+    assert call(out=None) == -1
+    assert call(sh=FAKE, rt=None) == -1          # shared without routed
+    assert call(H=100) == -2
+    assert call(H=0) == -2
+    assert call(H=16384) == -2
+    assert call(n=0) == -2
+    assert call(eps=-1.0) == -2
+    assert call(eps=float("nan")) == -2
+    assert call(res=ODD) == -4
+    assert call(xq=FAKE + 2) == -4
+
+
+def test_router_topk_validation(q):
+    f = q._router_topk
+
+    def call(xn=FAKE, W=FAKE, g=None, n=1, H=2048, E=256, k=8, lg=None, ids=FAKE, w=FAKE, sg=None, ws=FAKE,
+             wsb=1 << 20):
+        return f(xn, W, g, n, H, E, k, lg, ids, w, sg, ws, wsb, None)
+
+    assert call(xn=None) == -1
+    assert call(ids=None) == -1
+    assert call(k=0) == -2
+    assert call(k=9, E=8) == -2
+    assert call(k=17, E=256) == -2
+    assert call(E=2000) == -2
+    assert call(H=1000) == -2
+    assert call(n=5000) == -2
+    assert call(xn=FAKE + 4) == -4               # float4 loads need 16-byte alignment
+    assert call(ws=None) == -5
+    assert call(wsb=1024) == -5
+    assert call(ws=FAKE + 16) == -4
+
+
+def test_expert_ffn_validation(q):
+    d = _desc(q)
+    good = q.LayerWeights(norm_w=FAKE, router_w=FAKE, shared_gate_w=FAKE, gate=FAKE, up=FAKE, down=FAKE,
+                          shared_gate=FAKE, shared_up=FAKE, shared_down=FAKE)
+    f = q._expert_ffn_q4k
+
+    def call(desc=d, w=good, xq=FAKE, ids=FAKE, wts=FAKE, sg=FAKE, n=1, ro=FAKE, so=FAKE, ws=FAKE, wsb=1 << 24):
+        return f(C.byref(desc), C.byref(w), xq, ids, wts, sg, n, ro, so, None, None, ws, wsb, None)
+
+    assert call(xq=None) == -1
+    assert call(sg=None) == -1                                    # shared expert needs the gate value
+    assert call(n=2) == -7
+    assert call(desc=_desc(q, gate_up_type=13)) == -3
+    assert call(desc=_desc(q, down_type=8)) == -3
+    assert call(desc=_desc(q, shared_type=13)) == -3
+    assert call(desc=_desc(q, ffn=100)) == -2
+    assert call(desc=_desc(q, shared_type=8, shared_ffn=128)) == -2  # Q8_0 rows must be whole 16-byte multiples
+    bad = q.LayerWeights(**{n: FAKE for n, _ in q.LayerWeights._fields_})
+    bad.gate = FAKE + 8
+    assert call(w=bad) == -4
+    nul = q.LayerWeights(**{n: FAKE for n, _ in q.LayerWeights._fields_})
+    nul.down = None
+    assert call(w=nul) == -1
+    assert call(wsb=100) == -5
+
+
+def test_layer_and_stack_validation(q):
+    d = _desc(q)
+    w = q.LayerWeights(**{n: FAKE for n, _ in q.LayerWeights._fields_})
+    io = q.LayerIO(residual=FAKE, out_sum=FAKE, routed_out=FAKE, shared_out=FAKE)
+    assert q._moe_decode_layer(C.byref(d), C.byref(w), None, FAKE, 1 << 24, None) == -1
+    io2 = q.LayerIO(residual=None, out_sum=FAKE, routed_out=FAKE, shared_out=FAKE)
+    assert q._moe_decode_layer(C.byref(d), C.byref(w), C.byref(io2), FAKE, 1 << 24, None) == -1
+    assert q._moe_decode_layer(C.byref(d), C.byref(w), C.byref(io), FAKE, 16, None) == -5
+    arr = (q.LayerWeights * 2)(w, w)
+    assert q._moe_decode_stack(C.byref(d), arr, 0, FAKE, FAKE, None, None, 0, FAKE, 1 << 24, None) == -2
+    assert q._moe_decode_stack(C.byref(d), arr, 2, FAKE, FAKE, None, None, 9, FAKE, 1 << 24, None) == -2
+    assert q._moe_decode_stack(C.byref(d), arr, 2, None, FAKE, None, None, 0, FAKE, 1 << 24, None) == -1
+    d0 = _desc(q, norm=0)
+    assert q._moe_decode_stack(C.byref(d0), arr, 2, FAKE, FAKE, None, None, 0, FAKE, 1 << 24, None) == -7
+    assert q._moe_stack_bind(C.byref(d), arr, 2, FAKE, 1024, None) == -5
+    assert q._moe_test_subblock_dots(FAKE, 9, 256, 1, FAKE, FAKE, None) == -3
+    assert q._moe_test_subblock_dots(FAKE, 12, 100, 1, FAKE, FAKE, None) == -2
+    assert q._moe_workspace_init(None, 1024, None) == -5
+    assert q._moe_workspace_init(FAKE + 8, 1024, None) == -4
