@@ -1,0 +1,254 @@
+"""Benchmark: batch-1 decode MoE stage of a Qwen3.6-35B-A3B-shaped model on one MI355X.
+
+One step = one decode token through the 40-layer MoE stack (residual-add +
+RMSNorm, fp32 router over 256 experts, top-8 + softmax, Q4_K x Q8_1 routed
+gate/up + SwiGLU + down, sigmoid-gated shared expert), tokens strictly in
+sequence on one stream.  Weights (18 GB of Q4_K routed experts + router +
+shared) and the 128 token inputs are generated from seeds and resident in HBM
+before timing.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps 128] [--warmup 8] [--mode auto|kernels|persistent]
+                  [--variant after|before|both] [--no-cpu] [--calib-copy]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=128)
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--mode", default="auto", choices=["auto", "kernels", "persistent"])
+    p.add_argument("--variant", default="both", choices=["after", "before", "both"])
+    p.add_argument("--layers", type=int, default=40)
+    p.add_argument("--tokens", type=int, default=128)
+    p.add_argument("--repeats", type=int, default=5)
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--calib-copy", action="store_true", help="only run a 1 GiB device copy (counter calibration)")
+    p.add_argument("--trace", action="store_true", help="print the persistent kernel's per-phase times to stderr")
+    return p.parse_args()
+
+
+def algorithmic_bytes(cfg, shared_type, down_type):
+    """Bytes the method must read per token: router, shared-gate row, norm weight,
+    the k selected experts' gate/up/down rows and the shared expert, per layer."""
+    H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+    per = 4 * E * H + 4 * H + 4 * H
+    per += k * 2 * F * wl.row_bytes(wl.Q4_K, H)
+    per += k * H * wl.row_bytes(down_type, wl.pad_k(down_type, F))
+    if Fs:
+        per += 2 * Fs * wl.row_bytes(shared_type, H) + H * wl.row_bytes(shared_type, wl.pad_k(shared_type, Fs))
+    return per * cfg.layers
+
+
+class Stack:
+    """40 layers of weights on the GPU plus everything one token needs."""
+
+    def __init__(self, q, cfg, shared_type, down_type, mode):
+        self.q, self.cfg = q, cfg
+        self.shared_type, self.down_type = shared_type, down_type
+        t0 = time.time()
+        self.layers = [wl.layer_weights(cfg, l, "cuda", shared_type=shared_type, down_type=down_type)
+                       for l in range(cfg.layers)]
+        torch.cuda.synchronize()
+        self.gen_s = time.time() - t0
+        self.desc = q.make_desc(cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs, down_type=down_type, shared_type=shared_type,
+                                eps=cfg.eps)
+        self.arr = q.layer_array(self.layers)
+        self.ws = q.alloc_workspace(self.desc, cfg.layers)
+        self.inputs = torch.stack([wl.token_inputs(cfg, t, "cuda")["residual"] for t in range(cfg.tokens)])
+        self.out = torch.zeros(cfg.tokens, cfg.H, dtype=torch.bfloat16, device="cuda")
+        self.ids = torch.zeros(cfg.layers, cfg.k, dtype=torch.int32, device="cuda")
+        self.mode = self._pick_mode(mode)
+        self.graphs = None
+        if self.mode == q.MOE_STACK_KERNELS:
+            self._capture()
+
+    def _pick_mode(self, mode):
+        q = self.q
+        if mode in ("auto", "persistent"):
+            try:
+                q.moe_stack_bind(self.desc, self.layers, self.ws)
+                self.run_eager(0, q.MOE_STACK_PERSISTENT)
+                torch.cuda.synchronize()
+                return q.MOE_STACK_PERSISTENT
+            except q.MoeError as e:
+                if mode == "persistent":
+                    raise
+                print(f"# persistent mode unavailable ({e}); using per-layer kernels in HIP graphs", file=sys.stderr)
+        return q.MOE_STACK_KERNELS
+
+    def run_eager(self, t, mode, ids=None):
+        self.q.moe_decode_stack(self.desc, None, self.inputs[t], self.out[t], ids, None, mode, self.ws,
+                                layer_array=self.arr)
+
+    def _capture(self):
+        """One HIP graph per token input (4 kernels per layer + the final fold)."""
+        s = torch.cuda.Stream()
+        self.stream = s
+        with torch.cuda.stream(s):
+            self.run_eager(0, self.q.MOE_STACK_KERNELS)
+        s.synchronize()
+        self.graphs = []
+        for t in range(self.cfg.tokens):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                self.run_eager(t, self.q.MOE_STACK_KERNELS)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step(self, t):
+        t %= self.cfg.tokens
+        if self.graphs is not None:
+            self.graphs[t].replay()
+        else:
+            self.run_eager(t, self.mode)
+
+
+def time_steps(stack, steps, warmup, repeats):
+    for i in range(warmup):
+        stack.step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    per_token_us = []
+    for r in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            stack.step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_token_us.append(e0.elapsed_time(e1) * 1e3 / steps)
+    return per_token_us
+
+
+def cpu_baseline(stack, seconds):
+    """The oracle, as it stands, on the host cores: whole tokens through the
+    40-layer stack, same weights and inputs, until `seconds` have passed."""
+    import oracle as orc
+    cfg = stack.cfg
+    t0 = time.time()
+    Wn = [wl.to_numpy_weights(w) for w in stack.layers]
+    copy_s = time.time() - t0
+    d = orc.make_desc(cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs, down_type=stack.down_type,
+                      shared_type=stack.shared_type, eps=cfg.eps)
+    inputs = [wl.u16(stack.inputs[t]) for t in range(cfg.tokens)]
+    n = 0
+    t0 = time.time()
+    while True:
+        orc.moe_stack(d, Wn, inputs[n % cfg.tokens])
+        n += 1
+        if time.time() - t0 >= seconds or n >= cfg.tokens:
+            break
+    el = time.time() - t0
+    return {"us_per_token": el / n * 1e6, "tokens": n, "threads": orc.num_threads(), "copy_s": copy_s}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": f"--gpus {a.gpus}: this benchmark runs on one GPU only; the stage is a batch-1 "
+                                   "decode step whose multi-GPU sharding is not built"}))
+        sys.exit(2)
+    if a.calib_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+        return
+    import quantized_router_expert_amd as q
+    torch.cuda.set_device(0)
+    cfg = wl.variant(wl.CONFIGS["stack"], layers=a.layers, tokens=a.tokens)
+    variants = {"after": (wl.Q4_K, wl.Q4_K), "before": (wl.Q8_0, wl.Q5_K)}
+    order = ["after", "before"] if a.variant == "both" else [a.variant]
+    results = {}
+    primary = None
+    for name in order:
+        st, dt = variants[name]
+        stack = Stack(q, cfg, st, dt, a.mode)
+        print(f"# {name}: generated {cfg.layers} layers in {stack.gen_s:.1f}s; mode "
+              f"{'persistent' if stack.mode == q.MOE_STACK_PERSISTENT else 'kernels+graphs'}", file=sys.stderr, flush=True)
+        us = time_steps(stack, a.steps, a.warmup, a.repeats)
+        med = float(np.median(us))
+        alg = algorithmic_bytes(cfg, st, dt)
+        res = {"us_per_token": med, "us_p10": float(np.percentile(us, 10)), "us_p90": float(np.percentile(us, 90)),
+               "tokens_per_s": 1e6 / med, "alg_bytes_per_token": alg, "achieved_GBs": alg / (med * 1e-6) / 1e9,
+               "us_per_layer": med / cfg.layers, "mode": "persistent" if stack.mode == q.MOE_STACK_PERSISTENT else "kernels"}
+        res["frac_of_peak"] = res["achieved_GBs"] / HBM_PEAK_GBS
+        if name == "after":
+            primary = (stack, res)
+        else:
+            del stack
+            torch.cuda.empty_cache()
+        if a.trace and stack.mode == q.MOE_STACK_PERSISTENT:
+            stack.step(0)
+            torch.cuda.synchronize()
+            tr, mhz = q.stack_trace(stack.desc, cfg.layers, stack.ws)
+            d = (tr[:, 1:] - tr[:, :-1]).mean(0).tolist()
+            names = ["prev outputs in", "fixed weights landed", "norm+router+shared gate/up", "experts selected",
+                     "routed gate/up landed", "gate/up compute", "h quantised (exchange)", "down rows landed",
+                     "down+combine"]
+            print(f"# {name} per-layer phases (us, mean over layers): " +
+                  ", ".join(f"{n} {v:.2f}" for n, v in zip(names, d)) + f"; layer {tr[:, -1].mean():.2f}"
+                  + f"; shader clock {mhz:.0f} MHz",
+                  file=sys.stderr, flush=True)
+        results[name] = res
+        print(f"# {name}: {med:.1f} us/token ({res['achieved_GBs']:.0f} GB/s)", file=sys.stderr, flush=True)
+    stack, res = primary if primary else (None, results[order[0]])
+    cpu = None
+    if not a.no_cpu and stack is not None:
+        c = cpu_baseline(stack, a.cpu_seconds)
+        cpu = {"value": c["us_per_token"], "unit": "us/token", "cores": c["threads"], "kind": "oracle",
+               "sample": f"{c['tokens']} whole tokens through the {cfg.layers}-layer stack (same weights and inputs)",
+               "cpu_model": cpu_model()}
+    kernel = "moe_stack_persistent" if res["mode"] == "persistent" else "per-token graph of per-layer kernels"
+    line = {
+        "metric": "MoE decode stage latency (us/token, 40 layers) + achieved HBM GB/s vs peak",
+        "value": res["us_per_token"], "unit": "us/token", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": res["us_per_token"] / 1e3, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "q4_k x q8_1 (int8 dot), fp64 accumulate, bf16 out", "data": "synthetic",
+        "config": {"workload": f"Qwen3.6-35B-A3B-shaped MoE stack: {cfg.layers} layers, H 2048, 256 experts top-8, "
+                               f"F 512, shared 512, batch 1, {cfg.tokens} sequential tokens",
+                   "variant": "shared Q4_K + routed down Q4_K", "parallelism": "none (1 GPU)"},
+        "tokens_per_s": res["tokens_per_s"], "achieved_GBs": res["achieved_GBs"],
+        "us_per_layer": res["us_per_layer"], "us_p10": res["us_p10"], "us_p90": res["us_p90"],
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": res["achieved_GBs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": res["frac_of_peak"], "traffic": None,
+                     "alg_bytes_per_launch": res["alg_bytes_per_token"]},
+        "cpu_baseline": cpu,
+        "variants": results,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

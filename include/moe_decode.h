@@ -212,10 +212,14 @@ int moe_decode_layer(const moe_layer_desc* desc, const moe_layer_weights* w,
  * layers: host array of n_layers structs of device pointers.
  * mode MOE_STACK_KERNELS enqueues 4 kernels per layer plus the final fold on
  * `stream` (capture them in a HIP graph to remove launch overhead);
- * MOE_STACK_PERSISTENT runs every layer in one cooperative launch and needs a
- * prior moe_stack_bind of the same layers into the same workspace (it copies
- * the pointer table to the device and synchronises `stream` once; do not call
- * it during graph capture).  MOE_STACK_AUTO picks the fastest bound mode.
+ * MOE_STACK_PERSISTENT runs every layer in one cooperative launch (one
+ * workgroup per CU) and needs a prior moe_stack_bind of the same layers into
+ * the same workspace (it copies the pointer table to the device, clears the
+ * stack's exchange buffers and synchronises `stream` once; do not call it
+ * during graph capture).  A launch checks on the device that the bound table
+ * is the caller's; see moe_stack_status_offset for its status word.
+ * MOE_STACK_AUTO uses the persistent kernel when the shape fits in LDS, else
+ * the per-layer kernels.
  * ids_per_layer [L][k] int32 and resid_per_layer [L][H] bf16 (each layer's
  * out_sum) are optional device outputs.  desc->norm must be 1.
  * ---------------------------------------------------------------------- */
@@ -227,6 +231,24 @@ int moe_stack_bind(const moe_layer_desc* desc, const moe_layer_weights* layers, 
 int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers, int n_layers,
                      const uint16_t* input, uint16_t* output, int32_t* ids_per_layer, uint16_t* resid_per_layer,
                      int mode, void* ws, size_t ws_bytes, void* stream);
+
+/* Byte offset, in a workspace sized for (desc, n_layers), of a uint32 status
+ * word of the persistent stack: 0 while every launch completed, 1 after a
+ * launch stopped at a bounded wait (its outputs are invalid), 2 after a launch
+ * found no binding of the caller's layers (its output is set to NaN).  A
+ * nonzero word stays until moe_stack_bind or moe_workspace_init clears the
+ * workspace.  Returns 0 if the shape has no persistent stack. */
+size_t moe_stack_status_offset(const moe_layer_desc* desc, int n_layers);
+
+/* Byte offset, in the same workspace, of the persistent stack's phase
+ * timestamps: uint64 [64 layers][12 slots]: slots 0..9 the 100 MHz device wall clock,
+ * written by workgroup 0 of the last launch at the phase boundaries of each of
+ * its first 64 layers (slot 0 layer start, 1 previous outputs received,
+ * 2 fixed weights landed, 3 router rows done, 4 experts selected, 5 routed
+ * gate/up rows landed, 6 gate/up done, 7 every h quantised, 8 down rows
+ * landed, 9 layer done), slots 10/11 the shader cycle counter at the layer's
+ * start and end.  Returns 0 if the shape has no persistent stack. */
+size_t moe_stack_trace_offset(const moe_layer_desc* desc, int n_layers);
 
 /* ------------------------------------------------------------------------
  * Test export: the integer sub-block dots of weight rows against Q8_1

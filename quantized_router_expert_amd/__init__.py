@@ -72,11 +72,13 @@ _moe_stack_bind = _sig("moe_stack_bind", C.c_int, C.POINTER(LayerDesc), C.POINTE
                        C.c_size_t, P)
 _moe_decode_stack = _sig("moe_decode_stack", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights), C.c_int, P, P, P,
                          P, C.c_int, P, C.c_size_t, P)
+_moe_stack_status_offset = _sig("moe_stack_status_offset", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
+_moe_stack_trace_offset = _sig("moe_stack_trace_offset", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
 _moe_test_subblock_dots = _sig("moe_test_subblock_dots", C.c_int, P, C.c_int, C.c_int, C.c_int, P, P, P)
 
 EXPORTS = ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", "moe_stack_bind",
            "moe_decode_stack", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
-           "moe_test_subblock_dots")
+           "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots")
 
 
 # ---------------------------------------------------------------- marshalling helpers
@@ -197,6 +199,36 @@ def moe_decode_stack(desc, layers, inp, out, ids_per_layer=None, resid_per_layer
     return _check("moe_decode_stack", _moe_decode_stack(C.byref(desc), arr, n, ptr(inp), ptr(out), ptr(ids_per_layer),
                                                         ptr(resid_per_layer), mode, ptr(ws),
                                                         ws.numel() * ws.element_size(), stream_handle(stream)))
+
+
+def moe_stack_status_offset(desc, n_layers):
+    return _moe_stack_status_offset(C.byref(desc), n_layers)
+
+
+def stack_status(desc, n_layers, ws):
+    """The persistent stack's status word (reads the device workspace; synchronises)."""
+    off = moe_stack_status_offset(desc, n_layers)
+    if off == 0:
+        raise MoeError("moe_stack_status_offset", -7)
+    return int(ws[off:off + 4].view(torch.int32).item())
+
+
+def moe_stack_trace_offset(desc, n_layers):
+    return _moe_stack_trace_offset(C.byref(desc), n_layers)
+
+
+def stack_trace(desc, n_layers, ws):
+    """Per-layer phase timestamps (microseconds from the layer start) of the last
+    persistent launch, as a [min(L, 64), 10] float tensor, and the shader clock
+    in MHz over those layers (reads the workspace)."""
+    off = moe_stack_trace_offset(desc, n_layers)
+    if off == 0:
+        raise MoeError("moe_stack_trace_offset", -7)
+    n = min(n_layers, 64)
+    t = ws[off:off + 8 * 64 * 12].view(torch.int64).view(64, 12)[:n].double().cpu()
+    wall = t[:, :10]
+    mhz = float(((t[:, 11] - t[:, 10]).sum() / ((wall[:, 9] - wall[:, 0]).sum() / 100.0)))
+    return (wall - wall[:, :1]) / 100.0, mhz
 
 
 def layer_array(layers):

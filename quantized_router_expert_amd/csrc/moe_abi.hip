@@ -6,6 +6,7 @@
 #include "../../include/moe_decode.h"
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_stack.h"
 
 using namespace moe;
 
@@ -172,12 +173,16 @@ int moe_stack_bind(const moe_layer_desc* desc, const moe_layer_weights* layers, 
   rc = check_ws(ws, ws_bytes, L.total);
   if (rc) return rc;
   hipStream_t st = as_stream(stream);
+  if (L.stack == 0) return MOE_ERR_UNSUPPORTED;
   if (hipMemcpyAsync(at<void>(ws, L.table), layers, sizeof(moe_layer_weights) * n_layers, hipMemcpyHostToDevice, st) !=
       hipSuccess)
     return MOE_ERR_HIP;
-  int bound[4] = {n_layers, 0, 0, 0};
+  const int bound[4] = {(int)kBoundMagic, n_layers, 0, 0};
   if (hipMemcpyAsync(at<void>(ws, L.bound), bound, sizeof(bound), hipMemcpyHostToDevice, st) != hipSuccess)
     return MOE_ERR_HIP;
+  // a fresh generation: control block and exchange words start from zero
+  rc = launch_fill(at<void>(ws, L.stack), (L.total - L.stack) / 4, 0u, st);
+  if (rc) return rc;
   return hipStreamSynchronize(st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -198,8 +203,21 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
   const WsLayout L = ws_layout(desc, n_layers);
   rc = check_ws(ws, ws_bytes, L.total);
   if (rc) return rc;
-  if (mode == MOE_STACK_PERSISTENT) return MOE_ERR_UNSUPPORTED;
   hipStream_t st = as_stream(stream);
+  if (mode == MOE_STACK_PERSISTENT || mode == MOE_STACK_AUTO) {
+    int G = 0;
+    if ((rc = device_cu_count(&G))) return rc;
+    StackGeom g;
+    rc = (G >= 8 && G % 8 == 0 && L.stack) ? stack_geometry(desc, G, &g) : MOE_ERR_UNSUPPORTED;
+    if (rc == MOE_OK && g.lds > kStackMaxLds) rc = MOE_ERR_UNSUPPORTED;
+    if (rc == MOE_OK) {
+      stack_ws_layout(&g, L.stack);
+      return launch_stack(desc, n_layers, at<moe_layer_weights>(ws, L.table), at<int>(ws, L.bound), layers[0],
+                          layers[n_layers - 1], input, output, ids_per_layer, resid_per_layer,
+                          static_cast<uint8_t*>(ws), g, st);
+    }
+    if (mode == MOE_STACK_PERSISTENT) return rc;
+  }
   const int H = desc->hidden, E = desc->n_experts, k = desc->top_k;
   const bool has_shared = desc->shared_ffn > 0;
   uint16_t* routed = at<uint16_t>(ws, L.routed);
@@ -226,6 +244,26 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
   // the fold the next layer's norm would do: output = bf16(res_L + bf16(routed + shared))
   return launch_norm(res_in, routed, has_shared ? shared : nullptr, nullptr, H, 1, desc->eps, output, nullptr, nullptr, 0,
                      st);
+}
+
+size_t moe_stack_status_offset(const moe_layer_desc* desc, int n_layers) {
+  if (check_desc(desc) != MOE_OK || n_layers <= 0 || n_layers > MOE_MAX_LAYERS) return 0;
+  const WsLayout L = ws_layout(desc, n_layers);
+  if (!L.stack) return 0;
+  StackGeom g;
+  if (stack_geometry(desc, 256, &g) != MOE_OK) return 0;
+  stack_ws_layout(&g, L.stack);
+  return g.w_ctrl + 4 * kErrWord;
+}
+
+size_t moe_stack_trace_offset(const moe_layer_desc* desc, int n_layers) {
+  if (check_desc(desc) != MOE_OK || n_layers <= 0 || n_layers > MOE_MAX_LAYERS) return 0;
+  const WsLayout L = ws_layout(desc, n_layers);
+  if (!L.stack) return 0;
+  StackGeom g;
+  if (stack_geometry(desc, 256, &g) != MOE_OK) return 0;
+  stack_ws_layout(&g, L.stack);
+  return g.w_trace;
 }
 
 int moe_test_subblock_dots(const void* rows, int type, int K, int n_rows, const void* xq, int32_t* out, void* stream) {

@@ -68,21 +68,102 @@ __device__ __forceinline__ uint32_t f32_to_f16(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// ---------------------------------------------------------------- wave reductions (wave64)
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+// ---------------------------------------------------------------- lane exchange (wave64)
+// Butterfly steps over groups of 2, 4, 8, 16, 32, 64 lanes, all on the VALU:
+// DPP quad_perm [1,0,3,2] and [2,3,0,1] (xor 1, xor 2), row_half_mirror and
+// row_mirror (partner 7-i / 15-i: equivalent to xor 4 / xor 8 once the smaller
+// groups agree), and gfx950's permlane16/permlane32 swaps, whose two results
+// are the values of lanes l & ~16 and l | 16 (resp. 32) in every lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+enum { kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
+
+struct Pair32 { uint32_t a, b; };  // values of the two lanes of a pair, same in both lanes
+__device__ __forceinline__ Pair32 swap16(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return {(uint32_t)r[0], (uint32_t)r[1]};
+}
+__device__ __forceinline__ Pair32 swap32(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return {(uint32_t)r[0], (uint32_t)r[1]};
+}
+
+// partner value of a 32-bit lane value at butterfly level `lvl` (0..3: DPP)
+template <int LVL>
+__device__ __forceinline__ uint32_t partner_dpp(uint32_t v) {
+  if (LVL == 0) return dpp_u32<kDppXor1>(v);
+  if (LVL == 1) return dpp_u32<kDppXor2>(v);
+  if (LVL == 2) return dpp_u32<kDppHalfMirror>(v);
+  return dpp_u32<kDppMirror>(v);
+}
+
+__device__ __forceinline__ double dbl(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ uint32_t lo32(double d) { return (uint32_t)__builtin_bit_cast(unsigned long long, d); }
+__device__ __forceinline__ uint32_t hi32(double d) { return (uint32_t)(__builtin_bit_cast(unsigned long long, d) >> 32); }
+
+template <int LVL>
+__device__ __forceinline__ double sum_step_f64(double v) {
+  if (LVL < 4) return v + dbl(partner_dpp<LVL>(lo32(v)), partner_dpp<LVL>(hi32(v)));
+  const Pair32 l = (LVL == 4) ? swap16(lo32(v)) : swap32(lo32(v));
+  const Pair32 h = (LVL == 4) ? swap16(hi32(v)) : swap32(hi32(v));
+  return dbl(l.a, h.a) + dbl(l.b, h.b);   // same operand order in both lanes: identical results
+}
+
+// sum over aligned groups of `n` lanes (n a power of two, 1..64); every lane of a group gets the sum
+__device__ __forceinline__ double group_sum_f64(double v, int n) {
+  if (n >= 2) v = sum_step_f64<0>(v);
+  if (n >= 4) v = sum_step_f64<1>(v);
+  if (n >= 8) v = sum_step_f64<2>(v);
+  if (n >= 16) v = sum_step_f64<3>(v);
+  if (n >= 32) v = sum_step_f64<4>(v);
+  if (n >= 64) v = sum_step_f64<5>(v);
   return v;
 }
+__device__ __forceinline__ double wave_sum_f64(double v) { return group_sum_f64(v, 64); }
+
 __device__ __forceinline__ float half_wave_max_f32(float v) {  // within aligned groups of 32 lanes
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 32));
-  return v;
+  v = fmaxf(v, __uint_as_float(partner_dpp<0>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(partner_dpp<1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(partner_dpp<2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(partner_dpp<3>(__float_as_uint(v))));
+  const Pair32 p = swap16(__float_as_uint(v));
+  return fmaxf(__uint_as_float(p.a), __uint_as_float(p.b));
 }
 __device__ __forceinline__ int half_wave_sum_i32(int v) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 32);
-  return v;
+  v += (int)partner_dpp<0>((uint32_t)v);
+  v += (int)partner_dpp<1>((uint32_t)v);
+  v += (int)partner_dpp<2>((uint32_t)v);
+  v += (int)partner_dpp<3>((uint32_t)v);
+  const Pair32 p = swap16((uint32_t)v);
+  return (int)p.a + (int)p.b;
+}
+
+// wave-wide max of 64-bit unsigned keys; every lane gets it
+template <int LVL>
+__device__ __forceinline__ unsigned long long max_step_u64(unsigned long long v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  unsigned long long o;
+  if (LVL < 4) {
+    o = ((unsigned long long)partner_dpp<LVL>(hi) << 32) | partner_dpp<LVL>(lo);
+    return o > v ? o : v;
+  }
+  const Pair32 l = (LVL == 4) ? swap16(lo) : swap32(lo);
+  const Pair32 h = (LVL == 4) ? swap16(hi) : swap32(hi);
+  const unsigned long long a = ((unsigned long long)h.a << 32) | l.a;
+  const unsigned long long c = ((unsigned long long)h.b << 32) | l.b;
+  return a > c ? a : c;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  v = max_step_u64<0>(v);
+  v = max_step_u64<1>(v);
+  v = max_step_u64<2>(v);
+  v = max_step_u64<3>(v);
+  v = max_step_u64<4>(v);
+  return max_step_u64<5>(v);
 }
 
 // ---------------------------------------------------------------- Q8_1 quantiser
@@ -108,6 +189,49 @@ __device__ __forceinline__ Q81Lane quantize_q81_lane(float x) {
   float s = __fmul_rn(f16_to_f32(d16), (float)qsum);  // exact: 11-bit d16 times |qsum| <= 4064
   r.ds = d16 | (f32_to_f16(s) << 16);
   return r;
+}
+
+// The same quantiser with one lane per 32-element block: the lane reads the
+// block's 32 fp32 values from LDS (16-byte aligned), writes its 32 codes to
+// dst (16-byte aligned) and returns d16 | s16 << 16.  Same fp32 operations,
+// so the same bytes as quantize_q81_lane.
+__device__ __forceinline__ uint32_t quantize_q81_block(const float* src, uint8_t* dst) {
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = reinterpret_cast<const float4*>(src)[i];
+    x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  if (amax == 0.0f) {
+    d4[0] = make_uint4(0, 0, 0, 0);
+    d4[1] = make_uint4(0, 0, 0, 0);
+    return 0u;
+  }
+  const float d32 = amax / 127.0f;
+  const float id = 1.0f / d32;
+  uint32_t w[8];
+  int qsum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t pk = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float qf = fminf(fmaxf(roundf(__fmul_rn(x[4 * j + i], id)), -127.0f), 127.0f);
+      const int q = (int)qf;
+      qsum += q;
+      pk |= ((uint32_t)q & 0xffu) << (8 * i);
+    }
+    w[j] = pk;
+  }
+  d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  const uint32_t d16 = f32_to_f16(d32);
+  const float sv = __fmul_rn(f16_to_f32(d16), (float)qsum);
+  return d16 | (f32_to_f16(sv) << 16);
 }
 
 // ---------------------------------------------------------------- K-quant scales
@@ -233,6 +357,36 @@ __device__ __forceinline__ double row_task(const uint8_t* row, int t, const ActL
   if (TYPE == MOE_TYPE_Q8_0) return q80_task(row, t, act);
   const int b = t >> 2, g = t & 3;
   return kquant_task<TYPE>(row + (long)b * block_bytes(TYPE), b, g, act);
+}
+
+// A weight row and the activations it is dotted with.
+struct RowRef {
+  const uint8_t* row;
+  ActLds act;
+};
+
+// Row values of nrows rows computed by lane groups: the T tasks of a row sit in
+// TP = the next power of two >= min(T, 64) consecutive lanes (lanes past T add
+// 0; with T > 64 a lane takes tasks t, t+64, ...), and a DPP/permlane sum over
+// the group gives the row's fp64 value.  Waves [0, nw) split the rows (wave
+// index `wave`); out[r] receives row r.  rowfn(r) returns the RowRef of row r.
+template <int TYPE, class RowFn>
+__device__ __forceinline__ void rows_dot(int nrows, int T, RowFn rowfn, double* out, int wave, int nw) {
+  int TP = 1;
+  while (TP < T && TP < 64) TP <<= 1;
+  const int rpi = 64 / TP;
+  const int lane = threadIdx.x & 63;
+  const int rl = lane / TP, t0 = lane - rl * TP;
+  for (int r0 = wave * rpi; r0 < nrows; r0 += nw * rpi) {
+    const int r = r0 + rl;
+    double v = 0.0;
+    if (r < nrows) {
+      const RowRef rr = rowfn(r);
+      for (int t = t0; t < T; t += 64) v += row_task<TYPE>(rr.row, t, rr.act);
+    }
+    v = group_sum_f64(v, TP);
+    if (t0 == 0 && r < nrows) out[r] = v;
+  }
 }
 
 __device__ __forceinline__ double silu_f64(double x) { return x / (1.0 + exp(-x)); }

@@ -11,6 +11,7 @@
 #include "../../include/moe_decode.h"
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_stack.h"
 
 #include <string.h>
 
@@ -103,35 +104,22 @@ __device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* id
     const int e = lane + 64 * j;
     key[j] = (e < E) ? topk_key(logits[e], e) : 0ull;
   }
-  int sel[MOE_MAX_TOPK];
   for (int s = 0; s < k; ++s) {
     unsigned long long best = 0ull;
 #pragma unroll
     for (int j = 0; j < kTopkPerLane; ++j) best = key[j] > best ? key[j] : best;
-    unsigned long long wbest = best;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      unsigned long long other = __shfl_xor(wbest, o, 64);
-      wbest = other > wbest ? other : wbest;
-    }
+    const unsigned long long wbest = wave_max_u64(best);
 #pragma unroll
     for (int j = 0; j < kTopkPerLane; ++j)
       if (key[j] == wbest) key[j] = 0ull;
-    sel[s] = (int)(0xffffffffu - (uint32_t)(wbest & 0xffffffffull));
+    if (lane == 0) ids_out[s] = (int32_t)(0xffffffffu - (uint32_t)(wbest & 0xffffffffull));
   }
   if (lane == 0) {
     // softmax over the selected logits, shifted by the largest (slot 0), fp64
-    const double m = (double)logits[sel[0]];
-    double p[MOE_MAX_TOPK];
+    const double m = (double)logits[ids_out[0]];
     double sum = 0.0;
-    for (int s = 0; s < k; ++s) {
-      p[s] = exp((double)logits[sel[s]] - m);
-      sum += p[s];
-    }
-    for (int s = 0; s < k; ++s) {
-      ids_out[s] = sel[s];
-      w_out[s] = (float)(p[s] / sum);
-    }
+    for (int s = 0; s < k; ++s) sum += exp((double)logits[ids_out[s]] - m);
+    for (int s = 0; s < k; ++s) w_out[s] = (float)(exp((double)logits[ids_out[s]] - m) / sum);
   }
 }
 
@@ -530,6 +518,15 @@ WsLayout ws_layout(const moe_layer_desc* d, int n_layers) {
   L.shared = o; o += up256(sizeof(uint16_t) * d->hidden);
   L.table = o; o += up256(sizeof(moe_layer_weights) * (size_t)(n_layers > 0 ? n_layers : 1));
   L.bound = o; o += up256(sizeof(int) * 4);
+  // exchange buffers of the persistent stack (their sizes do not depend on the grid)
+  StackGeom g;
+  if (stack_geometry(d, 256, &g) == MOE_OK) {
+    stack_ws_layout(&g, o);
+    L.stack = o;
+    o = g.w_end;
+  } else {
+    L.stack = 0;
+  }
   L.total = o;
   return L;
 }

@@ -1,0 +1,62 @@
+// moe_stack.h -- geometry and arguments of the persistent L-layer stack kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_decode.h"
+
+namespace moe {
+
+constexpr int kStackThreads = 512;
+constexpr int kStackWaves = kStackThreads / 64;
+constexpr int kStackMinLds = 84 * 1024;     // above half of a CU's LDS: one workgroup per CU
+constexpr int kStackMaxLds = 160 * 1024;
+// control block: word 0 = generation, word kErrWord = error, census words (64 B apart) per XCC
+constexpr uint32_t kErrWord = 16;
+constexpr uint32_t kCensusWord = 64;
+constexpr uint32_t kStackCtrlBytes = 4 * (64 + 16 * 16);
+// phase timestamps of workgroup 0: [layer][slot], 100 MHz wall clock
+constexpr int kTraceLayers = 64;
+constexpr int kTraceSlots = 12;   // 0..9 wall clock at phase boundaries, 10/11 shader cycles at layer start/end
+
+struct StackGeom {
+  int G, per_xcc;
+  int RR, SR, RD, RP;                 // per-workgroup rows: router, shared gate/up, down outputs, routed gate/up pairs
+  int Kp, Kps;
+  int n_t, n_lg, n_h, n_sel, n_hq;    // exchange sizes in 8-byte words
+  // LDS byte offsets
+  int o_res, o_xn, o_xqc, o_xqd, o_xqs, o_nw, o_rrow, o_sgu, o_sdn, o_rgu, o_rdn, o_hqc, o_hqd, o_hqs, o_part, o_xbuf,
+      o_sel, o_red, o_y, o_smx;
+  int sgu_half, rgu_half, rdn_slot;
+  int lds;
+  // workspace byte offsets
+  size_t w_ctrl, w_t, w_lg, w_h, w_loc, loc_stride, l_t, l_sel, l_hq, w_trace, w_end;
+};
+
+constexpr uint32_t kBoundMagic = 0x4d6f4553u;
+
+struct StackArgs {
+  StackGeom g;
+  const moe_layer_weights* layers;   // device copy of the per-layer pointer table
+  const int* bound;                  // {magic, n_layers} written by moe_stack_bind
+  moe_layer_weights first, last;     // the caller's first and last layer, checked against the table
+  const uint16_t* input;
+  uint16_t* output;
+  int32_t* ids_out;
+  uint16_t* resid_out;
+  uint8_t* ws;
+  int L, H, E, k, F, Fs;
+  float eps;
+};
+
+int stack_geometry(const moe_layer_desc* d, int G, StackGeom* out);
+void stack_ws_layout(StackGeom* g, size_t base);
+int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_dev, const int* bound,
+                 const moe_layer_weights& first, const moe_layer_weights& last, const uint16_t* input,
+                 uint16_t* output, int32_t* ids_out, uint16_t* resid_out, uint8_t* ws, const StackGeom& g,
+                 hipStream_t st);
+int device_cu_count(int* n);
+
+}  // namespace moe
