@@ -172,6 +172,8 @@ def cpu_model():
 
 def main():
     a = parse()
+    if a.trace:
+        os.environ["MOE_STACK_TRACE"] = "1"
     if a.gpus != 1:
         print(json.dumps({"error": f"--gpus {a.gpus}: this benchmark runs on one GPU only; the stage is a batch-1 "
                                    "decode step whose multi-GPU sharding is not built"}))
@@ -204,23 +206,34 @@ def main():
                "tokens_per_s": 1e6 / med, "alg_bytes_per_token": alg, "achieved_GBs": alg / (med * 1e-6) / 1e9,
                "us_per_layer": med / cfg.layers, "mode": "persistent" if stack.mode == q.MOE_STACK_PERSISTENT else "kernels"}
         res["frac_of_peak"] = res["achieved_GBs"] / HBM_PEAK_GBS
+        if a.trace and stack.mode == q.MOE_STACK_PERSISTENT:
+            stack.step(0)
+            torch.cuda.synchronize()
+            tr, mhz = q.stack_trace(stack.desc, cfg.layers, stack.ws)
+            tr = tr[1:]   # layer 0 has no previous outputs to wait for
+            d = (tr[:, 1:10] - tr[:, :9]).mean(0).tolist()
+            names = ["prev outputs in", "fixed weights landed", "norm+router+shared gate/up", "experts selected",
+                     "routed gate/up landed", "gate/up compute", "h quantised (exchange)", "down rows landed",
+                     "down+combine"]
+            print(f"# {name} per-layer phases (us, mean over layers 1..): " +
+                  ", ".join(f"{n} {v:.2f}" for n, v in zip(names, d)) + f"; layer {tr[:, 9].mean():.2f}"
+                  + f"; shader clock {mhz:.0f} MHz", file=sys.stderr, flush=True)
+            bt = q.stack_block_trace(stack.desc, cfg.layers, stack.ws)
+            # layer l's events against the moment the last workgroup stored layer l-1's outputs
+            ref = bt[:-1, :, 10].max(1).values
+            order = [0, 1, 2, 11, 12, 3, 4, 13, 5, 6, 15, 7, 14, 8, 9, 10]
+            rel = bt[1:, :, order] - ref[:, None, None]
+            ev = ["start", "t in", "fixed", "normed", "xq", "logits out", "hs out", "lg in", "sel", "gu landed",
+                  "dn queued", "h out", "h in", "hq", "dn landed", "t out"]
+            print("#   all workgroups, from the last t of the previous layer: " +
+                  ", ".join(f"{n} {m:.2f}/{x:.2f}" for n, m, x in
+                            zip(ev, rel.median(1).values.mean(0).tolist(), rel.max(1).values.mean(0).tolist())) +
+                  "  (median/max over workgroups)", file=sys.stderr, flush=True)
         if name == "after":
             primary = (stack, res)
         else:
             del stack
             torch.cuda.empty_cache()
-        if a.trace and stack.mode == q.MOE_STACK_PERSISTENT:
-            stack.step(0)
-            torch.cuda.synchronize()
-            tr, mhz = q.stack_trace(stack.desc, cfg.layers, stack.ws)
-            d = (tr[:, 1:] - tr[:, :-1]).mean(0).tolist()
-            names = ["prev outputs in", "fixed weights landed", "norm+router+shared gate/up", "experts selected",
-                     "routed gate/up landed", "gate/up compute", "h quantised (exchange)", "down rows landed",
-                     "down+combine"]
-            print(f"# {name} per-layer phases (us, mean over layers): " +
-                  ", ".join(f"{n} {v:.2f}" for n, v in zip(names, d)) + f"; layer {tr[:, -1].mean():.2f}"
-                  + f"; shader clock {mhz:.0f} MHz",
-                  file=sys.stderr, flush=True)
         results[name] = res
         print(f"# {name}: {med:.1f} us/token ({res['achieved_GBs']:.0f} GB/s)", file=sys.stderr, flush=True)
     stack, res = primary if primary else (None, results[order[0]])

@@ -241,13 +241,22 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
 size_t moe_stack_status_offset(const moe_layer_desc* desc, int n_layers);
 
 /* Byte offset, in the same workspace, of the persistent stack's phase
- * timestamps: uint64 [64 layers][12 slots]: slots 0..9 the 100 MHz device wall clock,
- * written by workgroup 0 of the last launch at the phase boundaries of each of
- * its first 64 layers (slot 0 layer start, 1 previous outputs received,
- * 2 fixed weights landed, 3 router rows done, 4 experts selected, 5 routed
- * gate/up rows landed, 6 gate/up done, 7 every h quantised, 8 down rows
- * landed, 9 layer done), slots 10/11 the shader cycle counter at the layer's
- * start and end.  Returns 0 if the shape has no persistent stack. */
+ * timestamps: uint64 [64 layers][12 slots], written by the last launch for each
+ * of its first 64 layers.  Slots 0..9: the 100 MHz device wall clock seen by
+ * workgroup 0 at its phase boundaries (0 layer start, 1 previous outputs
+ * received, 2 fixed weights landed, 3 router rows done, 4 experts selected,
+ * 5 routed gate/up rows landed, 6 gate/up done, 7 every h quantised, 8 down rows
+ * landed, 9 layer done); slots 10/11: its shader cycle counter at the layer's
+ * start and end.  Right after them, uint64 [64 layers][256 workgroups][16
+ * events]: the wall clock of every workgroup at its own events (0 layer start,
+ * 1 previous outputs received, 2 fixed weights landed, 3 router rows stored,
+ * 4 shared h stored, 5 experts known, 6 routed gate/up rows landed, 7 routed h
+ * stored, 8 down inputs quantised, 9 down rows landed, 10 layer outputs stored,
+ * 11 input normalised, 12 input quantised, 13 logits received, 14 every h
+ * received),
+ * written only when the environment variable MOE_STACK_TRACE is "1" at the
+ * library's first persistent launch.  Returns 0 if the shape has no
+ * persistent stack. */
 size_t moe_stack_trace_offset(const moe_layer_desc* desc, int n_layers);
 
 /* ------------------------------------------------------------------------

@@ -217,18 +217,42 @@ def moe_stack_trace_offset(desc, n_layers):
     return _moe_stack_trace_offset(C.byref(desc), n_layers)
 
 
+TRACE_SLOTS = 12
+
+
 def stack_trace(desc, n_layers, ws):
-    """Per-layer phase timestamps (microseconds from the layer start) of the last
-    persistent launch, as a [min(L, 64), 10] float tensor, and the shader clock
-    in MHz over those layers (reads the workspace)."""
+    """Per-layer phase timestamps (microseconds from workgroup 0's layer start)
+    of the last persistent launch, as a [min(L, 64), 10] float tensor, and the
+    shader clock in MHz over those layers (reads the workspace)."""
     off = moe_stack_trace_offset(desc, n_layers)
     if off == 0:
         raise MoeError("moe_stack_trace_offset", -7)
     n = min(n_layers, 64)
-    t = ws[off:off + 8 * 64 * 12].view(torch.int64).view(64, 12)[:n].double().cpu()
-    wall = t[:, :10]
-    mhz = float(((t[:, 11] - t[:, 10]).sum() / ((wall[:, 9] - wall[:, 0]).sum() / 100.0)))
-    return (wall - wall[:, :1]) / 100.0, mhz
+    t = ws[off:off + 8 * 64 * TRACE_SLOTS].view(torch.int64).view(64, TRACE_SLOTS)[:n].double().cpu()
+    mhz = float(((t[:, 11] - t[:, 10]).sum() / ((t[:, 9] - t[:, 0]).sum() / 100.0)))
+    return (t[:, :10] - t[:, :1]) / 100.0, mhz
+
+
+BLOCK_EVENTS = 16
+TRACE_MAX_G = 256
+
+
+def stack_block_trace(desc, n_layers, ws):
+    """Per-workgroup event times of the last persistent launch, in microseconds
+    of the device wall clock, as a [min(L, 64), 256, 16] float tensor (recorded
+    only when MOE_STACK_TRACE=1 was set before the library's first launch):
+    0 layer start, 1 previous outputs received, 2 fixed weights landed,
+    3 router rows stored, 4 shared h stored, 5 experts known, 6 routed gate/up
+    rows landed, 7 routed h stored, 8 down inputs quantised, 9 down rows landed,
+    10 layer outputs stored, 11 input normalised, 12 input quantised, 13 logits
+    received, 14 every h received."""
+    off = moe_stack_trace_offset(desc, n_layers)
+    if off == 0:
+        raise MoeError("moe_stack_trace_offset", -7)
+    off += 8 * 64 * TRACE_SLOTS
+    n = min(n_layers, 64)
+    t = ws[off:off + 8 * 64 * TRACE_MAX_G * BLOCK_EVENTS].view(torch.int64).view(64, TRACE_MAX_G, BLOCK_EVENTS)
+    return t[:n].double().cpu() / 100.0
 
 
 def layer_array(layers):

@@ -166,6 +166,28 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return max_step_u64<5>(v);
 }
 
+// wave-wide max / min of 32-bit unsigned values; every lane gets the result
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, partner_dpp<0>(v));
+  v = max(v, partner_dpp<1>(v));
+  v = max(v, partner_dpp<2>(v));
+  v = max(v, partner_dpp<3>(v));
+  Pair32 p = swap16(v);
+  v = max(p.a, p.b);
+  p = swap32(v);
+  return max(p.a, p.b);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, partner_dpp<0>(v));
+  v = min(v, partner_dpp<1>(v));
+  v = min(v, partner_dpp<2>(v));
+  v = min(v, partner_dpp<3>(v));
+  Pair32 p = swap16(v);
+  v = min(p.a, p.b);
+  p = swap32(v);
+  return min(p.a, p.b);
+}
+
 // ---------------------------------------------------------------- Q8_1 quantiser
 // One 32-element block held by 32 consecutive lanes (one value per lane).
 // d32 = amax/127 and the codes x*(1/d32) are fp32 and correctly rounded (a
@@ -232,6 +254,78 @@ __device__ __forceinline__ uint32_t quantize_q81_block(const float* src, uint8_t
   const uint32_t d16 = f32_to_f16(d32);
   const float sv = __fmul_rn(f16_to_f32(d16), (float)qsum);
   return d16 | (f32_to_f16(sv) << 16);
+}
+
+// The same quantiser spread over 8 consecutive lanes per block, 4 values per
+// lane (lanes 8j..8j+7 of a wave share block j).  x4 = the lane's 4 values
+// (elements 4p..4p+3 of the block, p = lane & 7).  Returns the lane's 4 codes
+// packed little-endian; every lane of the group gets ds = d16 | s16 << 16.
+// Same fp32 operations as quantize_q81_lane, so the same bytes.  All 8 lanes
+// of a group must be active together.
+__device__ __forceinline__ uint32_t quantize_q81_oct(float4 x4, uint32_t& ds) {
+  float amax = fmaxf(fmaxf(fabsf(x4.x), fabsf(x4.y)), fmaxf(fabsf(x4.z), fabsf(x4.w)));
+  amax = fmaxf(amax, __uint_as_float(partner_dpp<0>(__float_as_uint(amax))));
+  amax = fmaxf(amax, __uint_as_float(partner_dpp<1>(__float_as_uint(amax))));
+  amax = fmaxf(amax, __uint_as_float(partner_dpp<2>(__float_as_uint(amax))));
+  // branch-free, so several blocks can be in flight in one lane: an all-zero
+  // block computes with a stand-in scale and is replaced by zeros at the end
+  const bool zero = (amax == 0.0f);
+  const float d32 = (zero ? 1.0f : amax) / 127.0f;
+  const float id = 1.0f / d32;
+  const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+  uint32_t pk = 0;
+  int qsum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float qf = fminf(fmaxf(roundf(__fmul_rn(xs[i], id)), -127.0f), 127.0f);
+    const int q = (int)qf;
+    qsum += q;
+    pk |= ((uint32_t)q & 0xffu) << (8 * i);
+  }
+  qsum += (int)partner_dpp<0>((uint32_t)qsum);
+  qsum += (int)partner_dpp<1>((uint32_t)qsum);
+  qsum += (int)partner_dpp<2>((uint32_t)qsum);
+  const uint32_t d16 = f32_to_f16(d32);
+  const float sv = __fmul_rn(f16_to_f32(d16), (float)qsum);
+  ds = zero ? 0u : (d16 | (f32_to_f16(sv) << 16));
+  return zero ? 0u : pk;
+}
+
+// Quantise nblk blocks with threads [tid0, tid0 + nthr) of the workgroup
+// (nthr a multiple of 64): block j reads 32 fp32 values from src(j) (LDS,
+// 16-byte aligned; nullptr = a zero block) and writes its codes to codes(j)
+// (16-byte aligned), d and s to dq[j] and sq[j].  Each lane keeps up to U
+// blocks in flight (independent dependency chains).
+template <int U, class Src, class Dst>
+__device__ __forceinline__ void quantize_q81_blocks(int nblk, Src src, Dst codes, float* dq, float* sq, int tid,
+                                                    int nthr) {
+  const int n = 8 * nblk;
+  for (int i0 = tid; i0 < n; i0 += U * nthr) {
+    float4 x4[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * nthr;
+      ok[u] = i < n;   // the same for the 8 lanes of a block
+      const float* sp = ok[u] ? src(i >> 3) : nullptr;
+      x4[u] = sp ? reinterpret_cast<const float4*>(sp)[i & 7] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    uint32_t pk[U], ds[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) pk[u] = quantize_q81_oct(x4[u], ds[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * nthr;
+      if (ok[u]) {
+        const int j = i >> 3, p = i & 7;
+        reinterpret_cast<uint32_t*>(codes(j))[p] = pk[u];
+        if (p == 0) {
+          dq[j] = f16_to_f32(ds[u]);
+          sq[j] = f16_to_f32(ds[u] >> 16);
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- K-quant scales

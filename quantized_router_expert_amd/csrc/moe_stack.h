@@ -13,26 +13,28 @@ constexpr int kStackThreads = 512;
 constexpr int kStackWaves = kStackThreads / 64;
 constexpr int kStackMinLds = 84 * 1024;     // above half of a CU's LDS: one workgroup per CU
 constexpr int kStackMaxLds = 160 * 1024;
-// control block: word 0 = generation, word kErrWord = error, census words (64 B apart) per XCC
+// control block: word 0 = generation, word kErrWord = error
 constexpr uint32_t kErrWord = 16;
-constexpr uint32_t kCensusWord = 64;
-constexpr uint32_t kStackCtrlBytes = 4 * (64 + 16 * 16);
+constexpr uint32_t kStackCtrlBytes = 256;
 // phase timestamps of workgroup 0: [layer][slot], 100 MHz wall clock
 constexpr int kTraceLayers = 64;
 constexpr int kTraceSlots = 12;   // 0..9 wall clock at phase boundaries, 10/11 shader cycles at layer start/end
+// per-workgroup event times [layer][workgroup][event], written only when asked for
+constexpr int kBlockEvents = 16;
+constexpr int kTraceMaxG = 256;
 
 struct StackGeom {
-  int G, per_xcc;
+  int G;
   int RR, SR, RD, RP;                 // per-workgroup rows: router, shared gate/up, down outputs, routed gate/up pairs
   int Kp, Kps;
-  int n_t, n_lg, n_h, n_sel, n_hq;    // exchange sizes in 8-byte words
+  int n_t, n_lg, n_h, n_sel;          // exchange sizes in 8-byte words (n_sel: selection words in LDS)
   // LDS byte offsets
   int o_res, o_xn, o_xqc, o_xqd, o_xqs, o_nw, o_rrow, o_sgu, o_sdn, o_rgu, o_rdn, o_hqc, o_hqd, o_hqs, o_part, o_xbuf,
-      o_sel, o_red, o_y, o_smx;
+      o_sel, o_red, o_y, o_cand, o_lgsel;
   int sgu_half, rgu_half, rdn_slot;
   int lds;
   // workspace byte offsets
-  size_t w_ctrl, w_t, w_lg, w_h, w_loc, loc_stride, l_t, l_sel, l_hq, w_trace, w_end;
+  size_t w_ctrl, w_t, w_lg, w_h, w_trace, w_end;
 };
 
 constexpr uint32_t kBoundMagic = 0x4d6f4553u;
@@ -49,6 +51,7 @@ struct StackArgs {
   uint8_t* ws;
   int L, H, E, k, F, Fs;
   float eps;
+  int trace_blocks;                  // nonzero: every workgroup stamps its events
 };
 
 int stack_geometry(const moe_layer_desc* d, int G, StackGeom* out);

@@ -18,11 +18,11 @@
 //      combine -> t = bf16(routed + shared) for those rows
 // Exchanges: every produced value travels as an 8-byte word (32-bit payload,
 // 32-bit epoch) written with one agent-coherent store, so a reader knows a
-// word is current without a separate flag.  Only one workgroup per XCD (the
-// leader, elected from the hardware XCC id) reads produced data from memory;
-// it republishes into its XCD's L2 with plain stores, where the XCD's other
-// workgroups read it with non-temporal loads.  Every wait is bounded: a spin
-// limit sets an error word and the grid exits.
+// word is current without a separate flag.  Every workgroup reads the words it
+// needs straight from memory with agent-coherent loads (a per-XCD gatherer
+// that republished into its L2 measured slower: the extra hop costs more than
+// the contention it saves).  Every wait is bounded: a spin limit sets an
+// error word and the grid exits.
 #include "../../include/moe_decode.h"
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -33,10 +33,7 @@ namespace moe {
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kPollWaves = 4;   // waves 0..3 poll and load the routed gate/up rows
 constexpr int kAuxSC1 = 16;     // agent-coherent (bypasses the XCD L2)
-constexpr int kAuxNT = 2;       // non-temporal (bypasses L1, served by the XCD L2)
 constexpr uint32_t kSpinLimit = 1u << 22;
-
-__device__ __forceinline__ unsigned xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xfu; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
@@ -46,17 +43,57 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
+// outstanding global load of the wave (its workgroup-scope fence covers global
+// memory), which would stall a wave at the first barrier after it has queued
+// weight rows for a later phase.  Nothing in this kernel passes data between
+// the waves of a workgroup through global memory; the rows streamed into LDS
+// are waited for explicitly by the waves that queued them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// 16 bytes per lane from global memory straight into LDS (buffer_load ... lds):
+// the wave's 64 lanes fill the 1 KiB at LDS address `lds` (M0) from byte
+// offset `off` + 16 * lane of the buffer described by `rsrc`.  Issued from
+// inline asm so the compiler does not track it: it would otherwise wait for
+// every such load before any LDS read it cannot prove disjoint, which stalls
+// the waves that compute while their next rows stream in.  The consumer waits
+// explicitly (s_waitcnt vmcnt(0) in the issuing waves, then a barrier).
+__device__ __forceinline__ void lds_dma_1k(v4u rsrc, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(off), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Buffer descriptor with hardware range checking: loads past `bytes` read 0.
+__device__ __forceinline__ v4u raw_rsrc(const void* p, uint32_t bytes) {
+  const unsigned long long a = (unsigned long long)p;
+  v4u r;
+  r.x = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r.z = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000u;
+  return r;
+}
+
 // Stream `bytes` from src into LDS dst (1 KiB per wave instruction); waves
 // [w0, w0+nw) take chunks round-robin.  dst must have room for the byte count
-// rounded up to 1 KiB: lanes past the source end read 0 (bounds-checked
-// buffer) and write that 0 into the padding.
+// rounded up to 1 KiB: lanes past the source end read 0 (range-checked
+// descriptor) and write that 0 into the padding.
 __device__ __forceinline__ void stage_async(uint8_t* dst, const void* src, uint32_t bytes, int wave, int w0, int nw) {
   if (wave < w0 || wave >= w0 + nw || bytes == 0) return;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, bytes);
+  const v4u r = raw_rsrc(src, bytes);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)dst;
   const int lane = threadIdx.x & 63;
   const uint32_t nchunks = (bytes + 1023) >> 10;
   for (uint32_t c = wave - w0; c < nchunks; c += nw)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (c << 10)), 16, (c << 10) + lane * 16, 0, 0, 0);
+    lds_dma_1k(r, (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (c << 10))), (c << 10) + lane * 16);
 }
 
 __device__ __forceinline__ void ll_store(const __amdgpu_buffer_rsrc_t& r, uint32_t word, uint32_t payload, uint32_t epoch,
@@ -73,7 +110,7 @@ __device__ __forceinline__ void ll_store(const __amdgpu_buffer_rsrc_t& r, uint32
 // spin limit.
 constexpr int kPollMax = 6;
 template <int AUX>
-__device__ __noinline__ bool poll_ll(const __amdgpu_buffer_rsrc_t& r, uint32_t n, uint32_t epoch, uint32_t* dst, int nw) {
+__device__ __forceinline__ bool poll_ll(const __amdgpu_buffer_rsrc_t& r, uint32_t n, uint32_t epoch, uint32_t* dst, int nw) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (wave >= nw) return true;
   const uint32_t npairs = (n + 1) >> 1;
@@ -132,65 +169,158 @@ __device__ __forceinline__ double sum_row(const double* p, int T) {
 __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   v = wave_sum_f64(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
+  lds_barrier();
   double t = 0.0;
 #pragma unroll
   for (int w = 0; w < kStackThreads / 64; ++w) t += red[w];
-  __syncthreads();
+  lds_barrier();
   return t;
 }
 
-__device__ __forceinline__ unsigned long long key_of(float v, int e) {
+// Order-preserving 32-bit key of a logit (a larger float gives a larger key);
+// NaN counts as -inf and -0 as +0.  Never 0, which marks an empty or taken slot.
+__device__ __forceinline__ uint32_t logit_key(float v) {
   if (v != v) v = -__builtin_inff();
   if (v == 0.0f) v = 0.0f;
   const uint32_t b = __float_as_uint(v);
-  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((unsigned long long)o << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// wave 0: top-k of lg[0..E), softmax over the selected logits, sigmoid of lg[E] -> sel[] (ids, weights bits, gate bits)
-__device__ __noinline__ void select_experts(const float* lg, int E, int k, bool has_sg, uint32_t* sel, double* scratch) {
+// Expert selection ([P273] Summary item 1: the top-k runs inside the router's
+// kernel), larger logit first and the lower expert id first among equal
+// logits, in three steps:
+//  1. waves 0..3 each take the experts e = 64w + lane + 256j and find their own
+//     k best by k wave-wide picks, as 64-bit candidates key << 32 | ~id
+//     (0 where a wave has fewer than k experts);
+//  2. wave 0 ranks the 4k candidates against each other (all distinct), and
+//     the candidate of rank r < k is slot r; the selected logits (and the
+//     shared-gate logit) are copied out, as the logits' landing area is reused
+//     for the routed rows right after;
+//  3. later, off the critical path, wave 0 turns the copied logits into the
+//     softmax weights (fp64, shifted by the largest, summed in slot order) and
+//     the shared expert's sigmoid gate.
+template <int NPL>
+__device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int w, unsigned long long* cand) {
   const int lane = threadIdx.x & 63;
-  unsigned long long key[kTopkPerLane];
+  uint32_t key[NPL];
 #pragma unroll
-  for (int j = 0; j < kTopkPerLane; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = (e < E) ? key_of(lg[e], e) : 0ull;
+  for (int j = 0; j < NPL; ++j) {
+    const int e = 64 * w + lane + 256 * j;
+    key[j] = (e < E) ? logit_key(lg[e]) : 0u;
   }
   for (int s = 0; s < k; ++s) {
-    unsigned long long best = 0ull;
+    uint32_t hv = key[0], hid = (uint32_t)(64 * w + lane);
 #pragma unroll
-    for (int j = 0; j < kTopkPerLane; ++j) best = key[j] > best ? key[j] : best;
-    best = wave_max_u64(best);
+    for (int j = 1; j < NPL; ++j)
+      if (key[j] > hv) { hv = key[j]; hid = (uint32_t)(64 * w + lane + 256 * j); }
+    const uint32_t m = wave_max_u32(hv);
+    const unsigned long long tied = __ballot(hv == m);
+    // usually one lane holds the maximum: it takes its own key out and writes
+    // the candidate; on a tie the lowest id among the tied lanes goes first
+    uint32_t id = hid;
+    bool win = (hv == m);
+    if (__popcll(tied) != 1) {
+      id = wave_min_u32(hv == m ? hid : 0xffffffffu);
+      win = (hid == id);
+    }
+    if (win) {
 #pragma unroll
-    for (int j = 0; j < kTopkPerLane; ++j)
-      if (key[j] == best) key[j] = 0ull;
-    if (lane == 0) sel[s] = 0xffffffffu - (uint32_t)(best & 0xffffffffull);
+      for (int j = 0; j < NPL; ++j)
+        if ((uint32_t)(64 * w + lane + 256 * j) == id) key[j] = 0u;
+      cand[16 * w + s] = m ? (((unsigned long long)m << 32) | (uint32_t)~id) : 0ull;
+    }
   }
-  // softmax over the selected logits, shifted by the largest (slot 0), fp64:
-  // lane s computes slot s's exponential, lane 0 sums them in slot order
-  __builtin_amdgcn_wave_barrier();
-  const double m = (double)lg[sel[0]];
-  double p = 0.0;
-  if (lane < k) p = exp((double)lg[sel[lane]] - m);
-  if (lane < k) scratch[lane] = p;
-  __builtin_amdgcn_wave_barrier();
-  if (lane == 0) {
-    double sum = 0.0;
-    for (int s = 0; s < k; ++s) sum += scratch[s];
-    scratch[MOE_MAX_TOPK] = sum;
+}
+
+__device__ __forceinline__ void topk_candidates(const float* lg, int E, int k, int wave, unsigned long long* cand) {
+  if (wave >= 4) return;
+  if (E <= 256) wave_topk<1>(lg, E, k, wave, cand);
+  else if (E <= 512) wave_topk<2>(lg, E, k, wave, cand);
+  else wave_topk<4>(lg, E, k, wave, cand);
+}
+
+// wave 0, after a barrier: slot ids -> sel[0..k), their logits -> lgsel[0..k),
+// the shared-gate logit -> lgsel[k]
+__device__ __forceinline__ void rank_candidates(const float* lg, int E, int k, bool has_sg,
+                                                const unsigned long long* cand, uint32_t* sel, float* lgsel) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long c = 0ull;
+  if (lane < 4 * k) {
+    const int wq = lane / k;
+    c = cand[16 * wq + (lane - wq * k)];
   }
-  __builtin_amdgcn_wave_barrier();
-  if (lane < k) sel[k + lane] = __float_as_uint((float)(p / scratch[MOE_MAX_TOPK]));
-  if (lane == k) {
-    sel[2 * k] = __float_as_uint(has_sg ? (float)sigmoid_f64((double)lg[E]) : 0.0f);
+  int rank = 0;
+  for (int w = 0; w < 4; ++w)
+    for (int s = 0; s < k; ++s) rank += (cand[16 * w + s] > c) ? 1 : 0;
+  if (c != 0ull && rank < k) {
+    const uint32_t id = ~(uint32_t)c;
+    sel[rank] = id;
+    lgsel[rank] = lg[id];
   }
+  if (lane == 0) lgsel[k] = has_sg ? lg[E] : 0.0f;
+}
+
+// wave 0: routing weights sel[k..2k) and the shared gate sel[2k] from lgsel;
+// scr: k doubles of LDS
+__device__ __forceinline__ void routing_weights(int k, bool has_sg, const float* lgsel, uint32_t* sel, double* scr) {
+  const int lane = threadIdx.x & 63;
+  const double lmax = (double)lgsel[0];
+  double arg = 0.0;
+  if (lane < k) arg = (double)lgsel[lane] - lmax;
+  else if (lane == k && has_sg) arg = -(double)lgsel[k];
+  const double ex = exp(arg);
+  if (lane < k) scr[lane] = ex;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  double sum = 0.0;
+  for (int s = 0; s < k; ++s) sum += scr[s];   // slot order
+  if (lane < k) sel[k + lane] = __float_as_uint((float)(ex / sum));
+  else if (lane == k) sel[2 * k] = __float_as_uint(has_sg ? (float)(1.0 / (1.0 + ex)) : 0.0f);
 }
 
 __device__ __forceinline__ bool same_layer(const moe_layer_weights& p, const moe_layer_weights& q) {
   return p.norm_w == q.norm_w && p.router_w == q.router_w && p.shared_gate_w == q.shared_gate_w && p.gate == q.gate &&
          p.up == q.up && p.down == q.down && p.shared_gate == q.shared_gate && p.shared_up == q.shared_up &&
          p.shared_down == q.shared_down;
+}
+
+// A layer's weight pointers, wave-uniform.  Read once per layer at a moment
+// when this wave has no row transfer in flight: a later read of the table
+// would make the wave wait (in order) for every transfer queued before it.
+struct LayerPtrs {
+  const float* norm_w;
+  const float* router_w;
+  const float* shared_gate_w;
+  const uint8_t* gate;
+  const uint8_t* up;
+  const uint8_t* down;
+  const uint8_t* shared_gate;
+  const uint8_t* shared_up;
+  const uint8_t* shared_down;
+};
+
+template <class T>
+__device__ __forceinline__ const T* uniform_ptr(const void* p) {
+  const unsigned long long a = (unsigned long long)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return reinterpret_cast<const T*>(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ LayerPtrs load_layer(const moe_layer_weights* table, int l) {
+  const moe_layer_weights w = table[l];
+  LayerPtrs p;
+  p.norm_w = uniform_ptr<float>(w.norm_w);
+  p.router_w = uniform_ptr<float>(w.router_w);
+  p.shared_gate_w = uniform_ptr<float>(w.shared_gate_w);
+  p.gate = uniform_ptr<uint8_t>(w.gate);
+  p.up = uniform_ptr<uint8_t>(w.up);
+  p.down = uniform_ptr<uint8_t>(w.down);
+  p.shared_gate = uniform_ptr<uint8_t>(w.shared_gate);
+  p.shared_up = uniform_ptr<uint8_t>(w.shared_up);
+  p.shared_down = uniform_ptr<uint8_t>(w.shared_down);
+  return p;
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -221,9 +351,10 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   uint32_t* sel = reinterpret_cast<uint32_t*>(smem + g.o_sel);
   double* red = reinterpret_cast<double*>(smem + g.o_red);
   float* yv = reinterpret_cast<float*>(smem + g.o_y);
-  double* smx = reinterpret_cast<double*>(smem + g.o_smx);
+  unsigned long long* cand = reinterpret_cast<unsigned long long*>(smem + g.o_cand);
+  float* lgsel = reinterpret_cast<float*>(smem + g.o_lgsel);
 
-  __shared__ uint32_t s_gen, s_x, s_leader;
+  __shared__ uint32_t s_gen;
   __shared__ int s_fail;
   {
     // the bound pointer table must be the caller's stack
@@ -244,23 +375,13 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     s_fail = 0;
     v2u gv = __builtin_amdgcn_raw_buffer_load_b64(r_ctrl, 0, 0, kAuxSC1);
     s_gen = gv.x;
-    const unsigned x = xcc_id();
-    const unsigned old = __hip_atomic_fetch_add(ctrl + kCensusWord + 16 * x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_x = x;
-    s_leader = (old % (unsigned)g.per_xcc) == 0u;
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t base = s_gen * (uint32_t)(3 * a.L + 2) + 1u;
-  const unsigned x = s_x & 7u;
-  const bool leader = s_leader != 0;
 
   const __amdgpu_buffer_rsrc_t r_t = make_rsrc(a.ws + g.w_t, (uint32_t)g.n_t * 8);
   const __amdgpu_buffer_rsrc_t r_lg = make_rsrc(a.ws + g.w_lg, (uint32_t)g.n_lg * 8);
   const __amdgpu_buffer_rsrc_t r_h = make_rsrc(a.ws + g.w_h, (uint32_t)g.n_h * 8);
-  uint8_t* loc = a.ws + g.w_loc + (size_t)x * g.loc_stride;
-  const __amdgpu_buffer_rsrc_t r_lt = make_rsrc(loc + g.l_t, (uint32_t)g.n_t * 8);
-  const __amdgpu_buffer_rsrc_t r_ls = make_rsrc(loc + g.l_sel, (uint32_t)g.n_sel * 8);
-  const __amdgpu_buffer_rsrc_t r_lh = make_rsrc(loc + g.l_hq, (uint32_t)g.n_hq * 8);
 
   const long rb_gu = row_bytes(MOE_TYPE_Q4_K, H);
   const long rb_sgu = has_sg ? row_bytes(ST, H) : 0;
@@ -271,9 +392,8 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   const int sf0 = b * g.SR;
   const int nsr = has_sg ? max(0, min(g.SR, Fs - sf0)) : 0;
 
-  // weights that do not depend on the routing decision, for layer l
-  auto prefetch_fixed = [&](int l) {
-    const moe_layer_weights& w = a.layers[l];
+  // weights that do not depend on the routing decision, for layer `w`
+  auto prefetch_fixed = [&](const LayerPtrs& w) {
     stage_async(smem + g.o_nw, w.norm_w, (uint32_t)(H * 4), wave, kPollWaves, kStackWaves - kPollWaves);
     for (int j = 0; j < g.RR; ++j) {
       const int r = b + j * g.G;
@@ -281,13 +401,13 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       if (src) stage_async(rrow + (long)j * H * 4, src, (uint32_t)(H * 4), wave, kPollWaves, kStackWaves - kPollWaves);
     }
     if (nsr > 0) {
-      stage_async(sgu, (const uint8_t*)w.shared_gate + sf0 * rb_sgu, (uint32_t)(nsr * rb_sgu), wave, kPollWaves,
+      stage_async(sgu, w.shared_gate + sf0 * rb_sgu, (uint32_t)(nsr * rb_sgu), wave, kPollWaves,
                   kStackWaves - kPollWaves);
-      stage_async(sgu + g.sgu_half, (const uint8_t*)w.shared_up + sf0 * rb_sgu, (uint32_t)(nsr * rb_sgu), wave,
+      stage_async(sgu + g.sgu_half, w.shared_up + sf0 * rb_sgu, (uint32_t)(nsr * rb_sgu), wave,
                   kPollWaves, kStackWaves - kPollWaves);
     }
     if (has_sg && nrd > 0)
-      stage_async(sdn, (const uint8_t*)w.shared_down + row0 * rb_sdn, (uint32_t)(nrd * rb_sdn), wave, kPollWaves,
+      stage_async(sdn, w.shared_down + row0 * rb_sdn, (uint32_t)(nrd * rb_sdn), wave, kPollWaves,
                   kStackWaves - kPollWaves);
   };
 
@@ -299,28 +419,31 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       if (i == 9) trace[l * kTraceSlots + 11] = clock64();
     }
   };
+  uint64_t* btrace = trace + kTraceLayers * kTraceSlots;
+  auto bstamp = [&](int l, int i) {
+    if (a.trace_blocks && tid == 0 && l < kTraceLayers && b < kTraceMaxG)
+      btrace[((long)l * kTraceMaxG + b) * kBlockEvents + i] = wall_clock64();
+  };
 
   auto fail_out = [&]() {
     if (tid == 0) __builtin_amdgcn_raw_buffer_store_b32(1u, r_ctrl, kErrWord * 4, 0, kAuxSC1);
   };
 
   // ---- layer-0 inputs: the token's residual, no previous outputs
-  prefetch_fixed(0);
   for (int i = tid; i < H; i += kStackThreads) res[i] = bf16_to_f32(a.input[i]);
+  LayerPtrs w = load_layer(a.layers, 0);
+  prefetch_fixed(w);
 
   for (int l = 0; l < a.L; ++l) {
     const uint32_t ep0 = base + 3u * l, ep1 = ep0 + 1u, ep2 = ep0 + 2u;
-    const moe_layer_weights& w = a.layers[l];
     stamp(l, 0);
-    // ================= R1: t of the previous layer
+    bstamp(l, 0);
+    // ================= R1: t of the previous layer, read by every workgroup
     if (l > 0) {
-      const bool ok = leader ? poll_ll<kAuxSC1>(r_t, g.n_t, ep2 - 3u, xbuf, kPollWaves)
-                             : poll_ll<kAuxNT>(r_lt, g.n_t, ep2 - 3u, xbuf, kPollWaves);
+      const bool ok = poll_ll<kAuxSC1>(r_t, g.n_t, ep2 - 3u, xbuf, kPollWaves);
       if (!ok) s_fail = 1;
-      __syncthreads();
+      lds_barrier();
       if (s_fail) { fail_out(); return; }
-      if (leader)
-        for (int i = tid; i < g.n_t; i += kStackThreads) ll_store(r_lt, i, xbuf[i], ep2 - 3u, 0);
       for (int i = tid; i < H; i += kStackThreads) {
         const uint32_t pr = xbuf[i >> 1];
         const float t = bf16_to_f32((uint16_t)((i & 1) ? (pr >> 16) : (pr & 0xffffu)));
@@ -329,9 +452,11 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     }
     // ================= phase A: norm, router rows, shared gate/up rows
     stamp(l, 1);
+    bstamp(l, 1);
     if (wave >= kPollWaves) wait_vmem();
-    __syncthreads();
+    lds_barrier();
     stamp(l, 2);
+    bstamp(l, 2);
     if (b == 0 && a.resid_out)
       for (int i = tid; i < H; i += kStackThreads) a.resid_out[(long)l * H + i] = f32_to_bf16(res[i]);
     double ss = 0.0;
@@ -339,38 +464,40 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     ss = block_sum_f64(ss, red);
     const double rinv = 1.0 / sqrt(ss / (double)H + (double)a.eps);
     for (int i = tid; i < H; i += kStackThreads) xn[i] = (float)(((double)res[i] * rinv) * (double)nw[i]);
-    __syncthreads();
-    for (int j = tid; j < H / 32; j += kStackThreads) {
-      const uint32_t ds = quantize_q81_block(xn + 32 * j, xqc + 32 * j);
-      xqd[j] = f16_to_f32(ds);
-      xqs[j] = f16_to_f32(ds >> 16);
-    }
-    __syncthreads();
+    lds_barrier();
+    bstamp(l, 11);
+    quantize_q81_blocks<1>(H / 32, [&](int j) { return (const float*)(xn + 32 * j); },
+                           [&](int j) { return xqc + 32 * j; }, xqd, xqs, tid, kStackThreads);
+    lds_barrier();
+    bstamp(l, 12);
     // router rows (fp64 dot of fp32 products), one wave per row
     for (int j = wave; j < g.RR; j += kStackWaves) {
       const int r = b + j * g.G;
       const bool real = (r < E) || (r == E && has_sg);
       if (!real) break;
       const float* wr = reinterpret_cast<const float*>(rrow + (long)j * H * 4);
-      double acc = 0.0;
+      // four independent fp64 partial sums per lane (fp64 keeps the fp32 result
+      // of the sum independent of its order but for rare last-bit cases)
+      double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
       for (int i = (tid & 63) * 4; i < H; i += 256) {
         const float4 wv = *reinterpret_cast<const float4*>(wr + i);
         const float4 xv = *reinterpret_cast<const float4*>(xn + i);
-        acc += (double)wv.x * (double)xv.x;
-        acc += (double)wv.y * (double)xv.y;
-        acc += (double)wv.z * (double)xv.z;
-        acc += (double)wv.w * (double)xv.w;
+        a0 += (double)wv.x * (double)xv.x;
+        a1 += (double)wv.y * (double)xv.y;
+        a2 += (double)wv.z * (double)xv.z;
+        a3 += (double)wv.w * (double)xv.w;
       }
-      acc = wave_sum_f64(acc);
+      const double acc = wave_sum_f64((a0 + a1) + (a2 + a3));
       if ((tid & 63) == 0) ll_store(r_lg, r, __float_as_uint((float)acc), ep0, kAuxSC1);
     }
+    bstamp(l, 3);
     // shared gate/up rows -> hs (word k*F + f of the h exchange)
     if (nsr > 0) {
       const ActLds act{xqc, xqd, xqs};
       rows_dot<ST>(2 * nsr, tasks_per_row(ST, H), [&](int r) {
         return RowRef{(r < nsr) ? sgu + (long)r * rb_sgu : sgu + g.sgu_half + (long)(r - nsr) * rb_sgu, act};
       }, part, wave, kStackWaves);
-      __syncthreads();
+      lds_barrier();
       if (tid < nsr) {
         const float gg = (float)part[tid];
         const float uu = (float)part[nsr + tid];
@@ -378,23 +505,24 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         ll_store(r_h, k * F + sf0 + tid, __float_as_uint(hv), ep1, kAuxSC1);
       }
     }
-    // ================= R2: logits -> selection
+    // ================= R2: logits -> selection, in every workgroup
     stamp(l, 3);
+    bstamp(l, 4);
     {
-      const bool ok = leader ? poll_ll<kAuxSC1>(r_lg, g.n_lg, ep0, xbuf, kPollWaves)
-                             : poll_ll<kAuxNT>(r_ls, g.n_sel, ep0, sel, kPollWaves);
+      const bool ok = poll_ll<kAuxSC1>(r_lg, g.n_lg, ep0, xbuf, kPollWaves);
       if (!ok) s_fail = 1;
-      __syncthreads();
+      lds_barrier();
       if (s_fail) { fail_out(); return; }
-      if (leader) {
-        if (wave == 0) select_experts(reinterpret_cast<const float*>(xbuf), E, k, has_sg, sel, smx);
-        __syncthreads();
-        for (int i = tid; i < g.n_sel; i += kStackThreads) ll_store(r_ls, i, sel[i], ep0, 0);
-        if (a.ids_out && x == 0)
-          for (int s = tid; s < k; s += kStackThreads) a.ids_out[(long)l * k + s] = (int32_t)sel[s];
-      }
+      bstamp(l, 13);
+      topk_candidates(reinterpret_cast<const float*>(xbuf), E, k, wave, cand);
+      lds_barrier();
+      if (wave == 0) rank_candidates(reinterpret_cast<const float*>(xbuf), E, k, has_sg, cand, sel, lgsel);
+      lds_barrier();
+      if (b == 0 && a.ids_out)
+        for (int s = tid; s < k; s += kStackThreads) a.ids_out[(long)l * k + s] = (int32_t)sel[s];
     }
     stamp(l, 4);
+    bstamp(l, 5);
     // ================= phase B: routed gate/up rows (this workgroup's slot and rows)
     const int p0 = b * g.RP;
     const int slot = p0 / F;
@@ -405,26 +533,45 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     if (bad_id) { fail_out(); return; }
     if (nrp > 0 && wave < kPollWaves) {
       const long e = sel[slot];
-      stage_async(rgu, (const uint8_t*)w.gate + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0, kPollWaves);
-      stage_async(rgu + g.rgu_half, (const uint8_t*)w.up + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0,
+      stage_async(rgu, w.gate + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0, kPollWaves);
+      stage_async(rgu + g.rgu_half, w.up + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0,
                   kPollWaves);
     }
+    // the routing weights are first needed by the combine: computed while the rows land
+    if (wave == 0) routing_weights(k, has_sg, lgsel, sel, reinterpret_cast<double*>(cand));
+    if (wave < kPollWaves) wait_vmem();
+    lds_barrier();
+    stamp(l, 5);
+    bstamp(l, 6);
+    // the down rows are needed only after the h exchange: requested once the
+    // gate/up rows have landed, so they do not share the memory system with them
     if (nrd > 0 && wave >= kPollWaves) {
-      for (int s = 0; s < k; ++s) {
-        const long e = sel[s];
-        stage_async(rdn + (long)s * g.rdn_slot, (const uint8_t*)w.down + (e * H + row0) * rb_dn, (uint32_t)(nrd * rb_dn),
-                    wave, kPollWaves, kStackWaves - kPollWaves);
+      // wave 4+j queues slots j, j+4, j+8, j+12: their ids are read first, so
+      // the requests go out back to back instead of each after an LDS round trip
+      const int j = wave - kPollWaves;
+      constexpr int kSlotsPerWave = (MOE_MAX_TOPK + kStackWaves - kPollWaves - 1) / (kStackWaves - kPollWaves);
+      uint32_t ex[kSlotsPerWave];
+#pragma unroll
+      for (int i = 0; i < kSlotsPerWave; ++i) {
+        const int s = j + (kStackWaves - kPollWaves) * i;
+        ex[i] = (s < k) ? sel[s] : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < kSlotsPerWave; ++i) {
+        const int s = j + (kStackWaves - kPollWaves) * i;
+        if (s < k)
+          stage_async(rdn + (long)s * g.rdn_slot, w.down + ((long)ex[i] * H + row0) * rb_dn, (uint32_t)(nrd * rb_dn),
+                      0, 0, 1);
       }
     }
-    if (wave < kPollWaves) wait_vmem();
-    __syncthreads();
-    stamp(l, 5);
+    if (a.trace_blocks && tid == 256 && l < kTraceLayers && b < kTraceMaxG)
+      btrace[((long)l * kTraceMaxG + b) * kBlockEvents + 15] = wall_clock64();
     if (nrp > 0) {
       const ActLds act{xqc, xqd, xqs};
       rows_dot<MOE_TYPE_Q4_K>(2 * nrp, tasks_per_row(MOE_TYPE_Q4_K, H), [&](int r) {
         return RowRef{(r < nrp) ? rgu + (long)r * rb_gu : rgu + g.rgu_half + (long)(r - nrp) * rb_gu, act};
       }, part, wave, kStackWaves);
-      __syncthreads();
+      lds_barrier();
       if (tid < nrp) {
         const float gg = (float)part[tid];
         const float uu = (float)part[nrp + tid];
@@ -432,61 +579,38 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         ll_store(r_h, slot * F + f0 + tid, __float_as_uint(hv), ep1, kAuxSC1);
       }
     }
-    // ================= R3: h -> Q8_1 codes of every slot (+ shared)
+    // ================= R3: every h, read and quantised to Q8_1 by every workgroup
     stamp(l, 6);
+    bstamp(l, 7);
     {
       const int nb_r = g.Kp / 32, nb_s = g.Kps / 32;
-      const int nblk = k * nb_r + nb_s;           // Q8_1 blocks of all down inputs
-      const int ncode_words = (k * g.Kp + g.Kps) / 4;
-      // the leader polls the largest exchange with every wave (the down rows that
-      // waves 4..7 requested in phase B have had the whole of phase B to land)
-      const bool ok = leader ? poll_ll<kAuxSC1>(r_h, g.n_h, ep1, xbuf, kStackWaves)
-                             : poll_ll<kAuxNT>(r_lh, g.n_hq, ep1, xbuf, kPollWaves);
+      // the down rows waves 4..7 requested in phase B have had the whole of
+      // phase B to land, so every wave polls
+      const bool ok = poll_ll<kAuxSC1>(r_h, g.n_h, ep1, xbuf, kStackWaves);
       if (!ok) s_fail = 1;
-      __syncthreads();
+      lds_barrier();
       if (s_fail) { fail_out(); return; }
-      if (leader) {
-        {
-          // quantise, one lane per Q8_1 block: block j of slot s covers
-          // h[s*F + 32j ..]; blocks past F (or Fs) are the zero padding
-          for (int blk = tid; blk < nblk; blk += kStackThreads) {
-            uint32_t ds = 0;
-            uint8_t* codes;
-            if (blk < k * nb_r) {
-              const int s = blk / nb_r, jb = blk - s * nb_r;
-              codes = hqc + (long)s * g.Kp + 32 * jb;
-              if (jb * 32 < F) ds = quantize_q81_block(reinterpret_cast<const float*>(xbuf) + s * F + 32 * jb, codes);
-              else *reinterpret_cast<uint4*>(codes) = make_uint4(0, 0, 0, 0), *reinterpret_cast<uint4*>(codes + 16) = make_uint4(0, 0, 0, 0);
-            } else {
-              const int jb = blk - k * nb_r;
-              codes = hqc + (long)k * g.Kp + 32 * jb;
-              if (jb * 32 < Fs) ds = quantize_q81_block(reinterpret_cast<const float*>(xbuf) + k * F + 32 * jb, codes);
-              else *reinterpret_cast<uint4*>(codes) = make_uint4(0, 0, 0, 0), *reinterpret_cast<uint4*>(codes + 16) = make_uint4(0, 0, 0, 0);
-            }
-            hqd[blk] = f16_to_f32(ds);
-            hqs[blk] = f16_to_f32(ds >> 16);
-            xbuf[g.n_h + blk] = ds;     // the raw fp16 pair, for republishing
-          }
-          __syncthreads();
-          const uint32_t* cw = reinterpret_cast<const uint32_t*>(hqc);
-          for (int i = tid; i < ncode_words; i += kStackThreads) ll_store(r_lh, i, cw[i], ep1, 0);
-          for (int i = tid; i < nblk; i += kStackThreads) ll_store(r_lh, ncode_words + i, xbuf[g.n_h + i], ep1, 0);
-        }
-      } else {
-        uint32_t* cw = reinterpret_cast<uint32_t*>(hqc);
-        for (int i = tid; i < ncode_words; i += kStackThreads) cw[i] = xbuf[i];
-        for (int i = tid; i < nblk; i += kStackThreads) {
-          const uint32_t ds = xbuf[ncode_words + i];
-          hqd[i] = f16_to_f32(ds);
-          hqs[i] = f16_to_f32(ds >> 16);
-        }
-      }
+      bstamp(l, 14);
+      // block jb of slot s covers h[s*F + 32jb ..]; blocks past F (or Fs) are the zero padding
+      const float* hf = reinterpret_cast<const float*>(xbuf);
+      quantize_q81_blocks<3>(k * nb_r + nb_s,
+                          [&](int j) -> const float* {
+                            if (j < k * nb_r) {
+                              const int s = j / nb_r, jb = j - s * nb_r;
+                              return (jb * 32 < F) ? hf + s * F + 32 * jb : nullptr;
+                            }
+                            const int jb = j - k * nb_r;
+                            return (jb * 32 < Fs) ? hf + k * F + 32 * jb : nullptr;
+                          },
+                          [&](int j) { return hqc + 32 * j; }, hqd, hqs, tid, kStackThreads);
     }
     // ================= phase C: down rows of all slots + shared, combine
     stamp(l, 7);
+    bstamp(l, 8);
     if (wave >= kPollWaves) wait_vmem();
-    __syncthreads();
+    lds_barrier();
     stamp(l, 8);
+    bstamp(l, 9);
     if (nrd > 0) {
       rows_dot<DT>(k * nrd, tasks_per_row(DT, g.Kp), [&](int r) {
         const int s = r / nrd, rr = r - s * nrd;
@@ -498,12 +622,12 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         rows_dot<ST>(nrd, tasks_per_row(ST, g.Kps), [&](int r) { return RowRef{sdn + (long)r * rb_sdn, acts}; },
                      part + k * nrd, wave, kStackWaves);
       }
-      __syncthreads();
+      lds_barrier();
       for (int i = tid; i < (k + 1) * nrd; i += kStackThreads) {
         const int m = i / nrd, r = i - m * nrd;
         yv[m * g.RD + r] = (m < k || has_sg) ? (float)part[m * nrd + r] : 0.0f;
       }
-      __syncthreads();
+      lds_barrier();
       const float sgv = __uint_as_float(sel[2 * k]);
       for (int r2 = tid; 2 * r2 < nrd; r2 += kStackThreads) {
         uint32_t pr = 0;
@@ -522,23 +646,27 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         ll_store(r_t, (row0 >> 1) + r2, pr, ep2, kAuxSC1);
       }
     }
-    __syncthreads();
+    lds_barrier();
     stamp(l, 9);
-    if (l + 1 < a.L) prefetch_fixed(l + 1);
+    bstamp(l, 10);
+    if (l + 1 < a.L) {
+      w = load_layer(a.layers, l + 1);
+      prefetch_fixed(w);
+    }
   }
   // ================= the fold a next layer would do: output = bf16(res + t)
   if (b == 0) {
     const uint32_t epl = base + 3u * (a.L - 1) + 2u;
     const bool ok = poll_ll<kAuxSC1>(r_t, g.n_t, epl, xbuf, kPollWaves);
     if (!ok) s_fail = 1;
-    __syncthreads();
+    lds_barrier();
     if (s_fail) { fail_out(); return; }
     for (int i = tid; i < H; i += kStackThreads) {
       const uint32_t pr = xbuf[i >> 1];
       const float t = bf16_to_f32((uint16_t)((i & 1) ? (pr >> 16) : (pr & 0xffffu)));
       a.output[i] = f32_to_bf16(res[i] + t);
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
       v2u nv = {s_gen + 1u, 0u};
       __builtin_amdgcn_raw_buffer_store_b64(nv, r_ctrl, 0, 0, kAuxSC1);
@@ -556,7 +684,6 @@ int stack_geometry(const moe_layer_desc* d, int G, StackGeom* out) {
   const bool has_sg = Fs > 0;
   const int st = has_sg ? d->shared_type : MOE_TYPE_Q4_K;
   g.G = G;
-  g.per_xcc = G / 8;
   g.Kp = pad_k(d->down_type, F);
   g.Kps = has_sg ? pad_k(st, Fs) : 0;
   g.RR = (E + (has_sg ? 1 : 0) + G - 1) / G;
@@ -575,7 +702,6 @@ int stack_geometry(const moe_layer_desc* d, int G, StackGeom* out) {
   g.n_h = k * F + Fs;
   g.n_sel = 2 * k + 1;
   const int nblk = k * (g.Kp / 32) + g.Kps / 32;
-  g.n_hq = (k * g.Kp + g.Kps) / 4 + nblk;
   // LDS
   long o = 0;
   auto take = [&](long bytes) { long r = o; o += up16(bytes); return (int)r; };
@@ -600,10 +726,9 @@ int stack_geometry(const moe_layer_desc* d, int G, StackGeom* out) {
   np = np > 2L * g.SR ? np : 2L * g.SR;
   np = np > (long)(k + 1) * g.RD ? np : (long)(k + 1) * g.RD;
   g.o_part = take(8L * np);
-  long xb = g.n_h + nblk;                            // words landing from an exchange (h + fp16 pairs)
+  long xb = g.n_h;                                   // words landing from an exchange
   xb = xb > g.n_t ? xb : g.n_t;
   xb = xb > g.n_lg ? xb : g.n_lg;
-  xb = xb > g.n_hq ? xb : g.n_hq;
   // the exchange landing area is only written while the routed gate/up rows are
   // not in use (before they are staged, after they are consumed): share it
   if (4L * (xb + 2) <= 2L * g.rgu_half) g.o_xbuf = g.o_rgu;
@@ -611,7 +736,8 @@ int stack_geometry(const moe_layer_desc* d, int G, StackGeom* out) {
   g.o_sel = take(4L * (g.n_sel + 1));
   g.o_red = take(8L * (kStackThreads / 64));
   g.o_y = take(4L * (k + 1) * g.RD);
-  g.o_smx = take(8L * (MOE_MAX_TOPK + 1));
+  g.o_cand = take(8L * 64);
+  g.o_lgsel = take(4L * (MOE_MAX_TOPK + 1));
   g.lds = (int)o;
   if (g.lds < kStackMinLds) g.lds = kStackMinLds;   // keeps one workgroup per CU
   // workspace (exchange buffers after the per-layer region)
@@ -626,12 +752,7 @@ void stack_ws_layout(StackGeom* g, size_t base) {
   g->w_t = take(8u * g->n_t);
   g->w_lg = take(8u * g->n_lg);
   g->w_h = take(8u * g->n_h);
-  g->l_t = 0;
-  g->l_sel = ((8u * g->n_t + 255) & ~(size_t)255);
-  g->l_hq = g->l_sel + ((8u * g->n_sel + 255) & ~(size_t)255);
-  g->loc_stride = g->l_hq + ((8u * g->n_hq + 255) & ~(size_t)255);
-  g->w_loc = take(8 * g->loc_stride);
-  g->w_trace = take(8u * kTraceLayers * kTraceSlots);
+  g->w_trace = take(8u * kTraceLayers * kTraceSlots + 8u * kTraceLayers * kTraceMaxG * kBlockEvents);
   g->w_end = o;
 }
 
@@ -664,6 +785,11 @@ int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_
   a.F = d->ffn;
   a.Fs = d->shared_ffn;
   a.eps = d->eps;
+  static const int trace_blocks = [] {
+    const char* e = getenv("MOE_STACK_TRACE");
+    return (e && e[0] == '1') ? 1 : 0;
+  }();
+  a.trace_blocks = trace_blocks;
   const void* fn;
   const int dt = d->down_type;
   const int stt = d->shared_ffn > 0 ? d->shared_type : MOE_TYPE_Q4_K;
