@@ -39,7 +39,8 @@ def parse():
     p.add_argument("--repeats", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--calib-copy", action="store_true", help="only run a 1 GiB device copy (counter calibration)")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="only run a kernel that reads and writes 1 GiB each (HBM counter calibration)")
     p.add_argument("--trace", action="store_true", help="print the persistent kernel's per-phase times to stderr")
     return p.parse_args()
 
@@ -138,6 +139,55 @@ def time_steps(stack, steps, warmup, repeats):
     return per_token_us
 
 
+def launch_durations(stack, n):
+    """Average duration of one launch of the step's kernel (one token), from
+    events recorded around each launch on the stream the kernel runs on."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i][0].record(stream)
+        stack.step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev]))
+
+
+KERNEL_SOURCES = ["quantized_router_expert_amd/csrc/moe_stack.hip", "quantized_router_expert_amd/csrc/moe_stack.h",
+                  "quantized_router_expert_amd/csrc/moe_device.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(variant):
+    """HBM bytes per launch of the persistent kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or
+    None when that summary was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"moe_stack_40L_{variant}_traffic.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel source sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(stack, seconds):
     """The oracle, as it stands, on the host cores: whole tokens through the
     40-layer stack, same weights and inputs, until `seconds` have passed."""
@@ -179,13 +229,16 @@ def main():
                                    "decode step whose multi-GPU sharding is not built"}))
         sys.exit(2)
     if a.calib_copy:
-        n = 1 << 30
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        # a plain streaming kernel of known traffic for scaling the HBM byte
+        # counters: reads 1 GiB and writes 1 GiB (an elementwise kernel, not a
+        # copy-engine transfer, so the counters see it)
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+        print(json.dumps({"calib_read_bytes": 4 * n, "calib_write_bytes": 4 * n, "launches": 5}))
         return
     import quantized_router_expert_amd as q
     torch.cuda.set_device(0)
@@ -206,6 +259,9 @@ def main():
                "tokens_per_s": 1e6 / med, "alg_bytes_per_token": alg, "achieved_GBs": alg / (med * 1e-6) / 1e9,
                "us_per_layer": med / cfg.layers, "mode": "persistent" if stack.mode == q.MOE_STACK_PERSISTENT else "kernels"}
         res["frac_of_peak"] = res["achieved_GBs"] / HBM_PEAK_GBS
+        res["launch_us"] = launch_durations(stack, min(64, a.steps))
+        res["kernel_GBs"] = alg / (res["launch_us"] * 1e-6) / 1e9
+        res["traffic_bytes_per_launch"] = measured_traffic(name) if res["mode"] == "persistent" else None
         if a.trace and stack.mode == q.MOE_STACK_PERSISTENT:
             stack.step(0)
             torch.cuda.synchronize()
@@ -254,9 +310,10 @@ def main():
                    "variant": "shared Q4_K + routed down Q4_K", "parallelism": "none (1 GPU)"},
         "tokens_per_s": res["tokens_per_s"], "achieved_GBs": res["achieved_GBs"],
         "us_per_layer": res["us_per_layer"], "us_p10": res["us_p10"], "us_p90": res["us_p90"],
-        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": res["achieved_GBs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": res["frac_of_peak"], "traffic": None,
-                     "alg_bytes_per_launch": res["alg_bytes_per_token"]},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": res["kernel_GBs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": res["kernel_GBs"] / HBM_PEAK_GBS,
+                     "traffic": res["traffic_bytes_per_launch"],
+                     "alg_bytes_per_launch": res["alg_bytes_per_token"], "launch_us": res["launch_us"]},
         "cpu_baseline": cpu,
         "variants": results,
     }
