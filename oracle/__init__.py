@@ -75,6 +75,9 @@ def _declare(L):
     L.orc_moe_layer.argtypes = [P, P, P, P, P, P, P]; L.orc_moe_layer.restype = C.c_int
     L.orc_moe_stack.argtypes = [P, P, C.c_int, P, P, P, P, P, P]; L.orc_moe_stack.restype = C.c_int
     L.orc_num_threads.argtypes = []; L.orc_num_threads.restype = C.c_int
+    L.orc_moe_layer_batch.argtypes = [P, P, C.c_int, C.c_int, P, P, P, P, P]
+    L.orc_moe_layer_batch.restype = C.c_int
+    L.orc_row_dot_bf16.argtypes = [P, C.c_int, C.c_int, P, C.c_int]; L.orc_row_dot_bf16.restype = C.c_float
 
 
 def _p(a):
@@ -320,6 +323,50 @@ def expert_ffn(desc, weights, xq, ids, wts, shared_gate):
     out["y"] = out["y"].reshape(desc.k, desc.H)
     out["hs"] = out["hs"][:desc.Fs]
     return out
+
+
+_BATCH_FIELDS = ("out_sum", "xn", "xq", "ids", "weights", "shared_gate", "group_size", "h", "hs", "y", "ys",
+                 "routed", "shared", "routed_exact", "shared_exact")
+
+
+class BatchOut(C.Structure):
+    _fields_ = [(n, P) for n in _BATCH_FIELDS]
+
+
+def moe_layer_batch(desc, weights, n_tok, threshold=4, residual=None, routed_prev=None, shared_prev=None, x=None):
+    """One layer for n_tok tokens at once, experts grouped (groups of at least
+    `threshold` tokens on the bf16 path).  Inputs are [n_tok][H] arrays;
+    returns a dict of [n_tok][...] arrays."""
+    L = lib()
+    held = _Held()
+    wst = make_weights(weights, held)
+    H, k, F, Fs = desc.H, desc.k, desc.F, desc.Fs
+    n = n_tok
+    out = {
+        "out_sum": np.zeros((n, H), np.uint16), "xn": np.zeros((n, H), np.float32),
+        "xq": np.zeros((n, H // 32 * 36), np.uint8), "ids": np.zeros((n, k), np.int32),
+        "weights": np.zeros((n, k), np.float32), "shared_gate": np.zeros(n, np.float32),
+        "group_size": np.zeros((n, k), np.int32), "h": np.zeros((n, k, F), np.float32),
+        "hs": np.zeros((n, max(Fs, 1)), np.float32), "y": np.zeros((n, k, H), np.float32),
+        "ys": np.zeros((n, H), np.float32), "routed": np.zeros((n, H), np.uint16),
+        "shared": np.zeros((n, H), np.uint16), "routed_exact": np.zeros((n, H), np.float64),
+        "shared_exact": np.zeros((n, H), np.float64),
+    }
+    bo = BatchOut(**{f: out[f].ctypes.data for f in _BATCH_FIELDS})
+    rc = L.orc_moe_layer_batch(C.byref(desc), C.byref(wst), n, threshold,
+                               held.hold(residual, np.uint16), held.hold(routed_prev, np.uint16),
+                               held.hold(shared_prev, np.uint16), held.hold(x, np.float32), C.byref(bo))
+    if rc != 0:
+        raise ValueError("oracle rejected the batch description")
+    out["hs"] = out["hs"][:, :Fs]
+    return out
+
+
+def row_dot_bf16(row, typ, K, x, n=None):
+    """One weight row on the bf16 path: f32(sum bf16(f32(w_i)) * bf16(x_i)), i < n."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    row = _u8(row)
+    return float(lib().orc_row_dot_bf16(_p(row), typ, K, _p(x), len(x) if n is None else n))
 
 
 def moe_stack(desc, layers, inp, per_layer=False):

@@ -606,6 +606,229 @@ int orc_moe_layer(const orc_desc* d, const orc_weights* w,
     return 0;
 }
 
+
+/* ------------------------------------------------------------------ */
+/* a8: several tokens at once, grouped by expert.  The pages cover batch 1 */
+/* only; reading: the tokens whose top-k contains expert e form its group; */
+/* a group of at least `threshold` tokens runs on bf16 inputs -- weights   */
+/* f32(w_deq) then bf16, activations bf16(xn) and bf16(h), exact products, */
+/* the sum rounded once to fp32 -- and a smaller group runs the Q8_1       */
+/* integer path of a4/a5 for each of its tokens.  The shared expert is one */
+/* group of all tokens.  Norm, router, top-k, weights and the combine are  */
+/* the single-token steps applied to each token.                          */
+/* ------------------------------------------------------------------ */
+
+/* bf16 of a value: first to fp32, then to bf16, both to nearest even. */
+static double bf16_of(double v) { return orc_bf16_to_f64(st_bf16(v)); }
+
+/* n_rows rows of K elements of `type`, decoded exactly and rounded as the
+ * bf16 path feeds them: out[r*K + i] = bf16(f32(w)). */
+static void decode_rows_bf16(const uint8_t* rows, int type, int K, int n_rows, double* out)
+{
+    long rb = orc_row_bytes(type, K);
+    int per = (type == ORC_Q8_0) ? 32 : 256;
+    int r;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (r = 0; r < n_rows; ++r) {
+        double blk[256];
+        for (int b = 0; b < K / per; ++b) {
+            const uint8_t* p = rows + rb * r + (long)b * (type == ORC_Q8_0 ? ORC_Q80_BYTES
+                                                       : (type == ORC_Q5_K ? ORC_Q5K_BYTES : ORC_Q4K_BYTES));
+            if (type == ORC_Q4_K) orc_decode_q4k(p, blk);
+            else if (type == ORC_Q5_K) orc_decode_q5k(p, blk);
+            else orc_decode_q8_0(p, blk);
+            for (int i = 0; i < per; ++i)
+                out[(long)r * K + (long)b * per + i] = bf16_of(blk[i]);
+        }
+    }
+}
+
+/* f32 of sum_{i<n} wb[i] * bf16(x[i]); wb already bf16 values, x fp32 */
+static float dot_bf16(const double* wb, const float* x, int n)
+{
+    double acc = 0.0;
+    for (int i = 0; i < n; ++i)
+        acc += wb[i] * bf16_of((double)x[i]);
+    return st_f32(acc);
+}
+
+/* Gate/up + SwiGLU and down of one expert on the bf16 path for the tokens
+ * toks[0..nt): xn [n_tok][H] fp32; h_out [nt][F]; y_out [nt][H]. */
+static void expert_bf16(const uint8_t* gate, const uint8_t* up, int gu_type, const uint8_t* down, int dn_type,
+                        int H, int F, int Kp, const float* xn, const int* toks, int nt, float* h_out, float* y_out)
+{
+    double* G = (double*)malloc(sizeof(double) * (size_t)F * H);
+    double* U = (double*)malloc(sizeof(double) * (size_t)F * H);
+    double* D = (double*)malloc(sizeof(double) * (size_t)H * Kp);
+    decode_rows_bf16(gate, gu_type, H, F, G);
+    decode_rows_bf16(up, gu_type, H, F, U);
+    decode_rows_bf16(down, dn_type, Kp, H, D);
+    for (int j = 0; j < nt; ++j) {
+        const float* x = xn + (long)toks[j] * H;
+        float* h = h_out + (long)j * F;
+        float* y = y_out + (long)j * H;
+        int f, i;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+        for (f = 0; f < F; ++f) {
+            float g = dot_bf16(G + (long)f * H, x, H);
+            float u = dot_bf16(U + (long)f * H, x, H);
+            h[f] = st_f32(silu((double)g) * (double)u);
+        }
+        /* the padding past F holds zero activations (reading S14) */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+        for (i = 0; i < H; ++i)
+            y[i] = dot_bf16(D + (long)i * Kp, h, F);
+    }
+    free(D);
+    free(U);
+    free(G);
+}
+
+/* Q8_1 integer path of one expert for one token (a4/a5). */
+static void expert_int(const uint8_t* gate, const uint8_t* up, int gu_type, const uint8_t* down, int dn_type,
+                       int H, int F, int Kp, const uint8_t* xq, float* h, float* y)
+{
+    uint8_t* hq = (uint8_t*)malloc((size_t)(Kp / 32) * ORC_Q81_BYTES);
+    ffn_gate_up(gate, up, gu_type, H, F, xq, h);
+    quantize_h_padded(h, F, Kp, hq);
+    ffn_down(down, dn_type, H, Kp, hq, y);
+    free(hq);
+}
+
+int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok, int threshold,
+                        const uint16_t* residual, const uint16_t* routed_prev, const uint16_t* shared_prev,
+                        const float* x, orc_batch_out* o)
+{
+    if (!desc_ok(d) || n_tok <= 0 || threshold < 1)
+        return -1;
+    int H = d->H, E = d->E, k = d->k, F = d->F, Fs = d->Fs;
+    int Kp = orc_pad_k(d->down_type, F);
+    int Kps = Fs > 0 ? orc_pad_k(d->shared_type, Fs) : 0;
+    long gu_rb = orc_row_bytes(d->gate_up_type, H);
+    long dn_rb = orc_row_bytes(d->down_type, Kp);
+    float* xn = (float*)malloc(sizeof(float) * (size_t)n_tok * H);
+    uint8_t* xq = (uint8_t*)malloc((size_t)n_tok * (H / 32) * ORC_Q81_BYTES);
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_tok * k);
+    float* wts = (float*)malloc(sizeof(float) * (size_t)n_tok * k);
+    float* sg = (float*)malloc(sizeof(float) * (size_t)n_tok);
+    float* logits = (float*)malloc(sizeof(float) * (size_t)E);
+    float* y = (float*)malloc(sizeof(float) * (size_t)n_tok * k * H);
+    float* ys = (float*)malloc(sizeof(float) * (size_t)n_tok * H);
+    int* cnt = (int*)calloc((size_t)E, sizeof(int));
+    int* toks = (int*)malloc(sizeof(int) * (size_t)n_tok);
+    int* slot_of = (int*)malloc(sizeof(int) * (size_t)n_tok);
+
+    /* a1..a3 per token */
+    for (int t = 0; t < n_tok; ++t) {
+        float* xt = xn + (long)t * H;
+        uint8_t* qt = xq + (long)t * (H / 32) * ORC_Q81_BYTES;
+        if (d->norm) {
+            orc_add_rmsnorm(residual + (long)t * H, routed_prev ? routed_prev + (long)t * H : NULL,
+                            shared_prev ? shared_prev + (long)t * H : NULL, w->norm_w, H, d->eps,
+                            o->out_sum ? o->out_sum + (long)t * H : NULL, xt, qt);
+        } else {
+            memcpy(xt, x + (long)t * H, sizeof(float) * (size_t)H);
+            orc_quantize_q8_1(xt, H, qt);
+        }
+        float z;
+        orc_router_topk(d, w, xt, logits, &z, ids + (long)t * k, wts + (long)t * k, &sg[t]);
+    }
+    /* group sizes */
+    for (int t = 0; t < n_tok; ++t)
+        for (int s = 0; s < k; ++s)
+            cnt[ids[(long)t * k + s]] += 1;
+    /* routed experts, one group at a time, in expert order */
+    for (int e = 0; e < E; ++e) {
+        if (cnt[e] == 0) continue;
+        int nt = 0;
+        for (int t = 0; t < n_tok; ++t)
+            for (int s = 0; s < k; ++s)
+                if (ids[(long)t * k + s] == e) { toks[nt] = t; slot_of[nt] = s; ++nt; }
+        const uint8_t* G = w->gate + (long)e * F * gu_rb;
+        const uint8_t* U = w->up + (long)e * F * gu_rb;
+        const uint8_t* D = w->down + (long)e * H * dn_rb;
+        float* h = (float*)malloc(sizeof(float) * (size_t)nt * F);
+        float* ye = (float*)malloc(sizeof(float) * (size_t)nt * H);
+        if (cnt[e] >= threshold) {
+            expert_bf16(G, U, d->gate_up_type, D, d->down_type, H, F, Kp, xn, toks, nt, h, ye);
+        } else {
+            for (int j = 0; j < nt; ++j)
+                expert_int(G, U, d->gate_up_type, D, d->down_type, H, F, Kp,
+                           xq + (long)toks[j] * (H / 32) * ORC_Q81_BYTES, h + (long)j * F, ye + (long)j * H);
+        }
+        for (int j = 0; j < nt; ++j) {
+            memcpy(y + ((long)toks[j] * k + slot_of[j]) * H, ye + (long)j * H, sizeof(float) * (size_t)H);
+            if (o->h) memcpy(o->h + ((long)toks[j] * k + slot_of[j]) * F, h + (long)j * F, sizeof(float) * (size_t)F);
+        }
+        free(ye);
+        free(h);
+    }
+    /* shared expert: one group of all tokens */
+    if (Fs > 0) {
+        float* hs = (float*)malloc(sizeof(float) * (size_t)n_tok * Fs);
+        for (int t = 0; t < n_tok; ++t) toks[t] = t;
+        if (n_tok >= threshold) {
+            expert_bf16(w->sgate, w->sup, d->shared_type, w->sdown, d->shared_type, H, Fs, Kps, xn, toks, n_tok, hs, ys);
+        } else {
+            for (int t = 0; t < n_tok; ++t)
+                expert_int(w->sgate, w->sup, d->shared_type, w->sdown, d->shared_type, H, Fs, Kps,
+                           xq + (long)t * (H / 32) * ORC_Q81_BYTES, hs + (long)t * Fs, ys + (long)t * H);
+        }
+        if (o->hs) memcpy(o->hs, hs, sizeof(float) * (size_t)n_tok * Fs);
+        free(hs);
+    }
+    /* combine per token, slot order */
+    for (int t = 0; t < n_tok; ++t) {
+        for (int i = 0; i < H; ++i) {
+            double acc = 0.0;
+            for (int s = 0; s < k; ++s)
+                acc += (double)wts[(long)t * k + s] * (double)y[((long)t * k + s) * H + i];
+            if (o->routed_exact) o->routed_exact[(long)t * H + i] = acc;
+            if (o->routed) o->routed[(long)t * H + i] = st_bf16(acc);
+            double v = Fs > 0 ? (double)sg[t] * (double)ys[(long)t * H + i] : 0.0;
+            if (o->shared_exact) o->shared_exact[(long)t * H + i] = v;
+            if (o->shared) o->shared[(long)t * H + i] = Fs > 0 ? st_bf16(v) : 0;
+        }
+        for (int s = 0; s < k; ++s)
+            if (o->group_size) o->group_size[(long)t * k + s] = cnt[ids[(long)t * k + s]];
+    }
+    if (o->xn) memcpy(o->xn, xn, sizeof(float) * (size_t)n_tok * H);
+    if (o->xq) memcpy(o->xq, xq, (size_t)n_tok * (H / 32) * ORC_Q81_BYTES);
+    if (o->ids) memcpy(o->ids, ids, sizeof(int32_t) * (size_t)n_tok * k);
+    if (o->weights) memcpy(o->weights, wts, sizeof(float) * (size_t)n_tok * k);
+    if (o->shared_gate) memcpy(o->shared_gate, sg, sizeof(float) * (size_t)n_tok);
+    if (o->y) memcpy(o->y, y, sizeof(float) * (size_t)n_tok * k * H);
+    if (o->ys) memcpy(o->ys, ys, sizeof(float) * (size_t)n_tok * H);
+    free(slot_of);
+    free(toks);
+    free(cnt);
+    free(ys);
+    free(y);
+    free(logits);
+    free(sg);
+    free(wts);
+    free(ids);
+    free(xq);
+    free(xn);
+    return 0;
+}
+
+/* One row on the bf16 path (test export): f32(sum_{i<n} bf16(f32(w_i)) * bf16(x_i)). */
+float orc_row_dot_bf16(const uint8_t* row, int type, int K, const float* x, int n)
+{
+    double* wb = (double*)malloc(sizeof(double) * (size_t)K);
+    decode_rows_bf16(row, type, K, 1, wb);
+    float r = dot_bf16(wb, x, n);
+    free(wb);
+    return r;
+}
+
 /* Stack of L layers for one token.  Layer l reads the residual stream and
  * the previous layer's routed/shared outputs (zero before layer 0, so the
  * first norm sees the input itself); the stack output is the residual plus

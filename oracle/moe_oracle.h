@@ -160,6 +160,39 @@ int orc_moe_stack(const orc_desc* d, const orc_weights* layers, int L,
                   uint16_t* shared_per_layer /* [L][H] or NULL */,
                   uint16_t* resid_per_layer /* [L][H] or NULL: out_sum of each layer */);
 
+/* ---- several tokens at once, grouped by expert ----
+ * Per token: a1..a3.  The tokens whose ids contain expert e form its group;
+ * a group of >= threshold tokens runs on bf16 inputs (weights f32(w_deq) then
+ * bf16, activations bf16(xn) and bf16(h), exact products, one fp32 rounding
+ * of the sum), a smaller group runs the Q8_1 integer path per token.  The
+ * shared expert is one group of all n_tok tokens.  Arrays are [n_tok][...]
+ * versions of the single-token ones; every output pointer may be NULL. */
+typedef struct {
+    uint16_t* out_sum;       /* [n][H] */
+    float* xn;               /* [n][H] */
+    uint8_t* xq;             /* [n][H/32] Q8_1 */
+    int32_t* ids;            /* [n][k] */
+    float* weights;          /* [n][k] */
+    float* shared_gate;      /* [n] */
+    int32_t* group_size;     /* [n][k]: tokens in the group of that slot's expert */
+    float* h;                /* [n][k][F] */
+    float* hs;               /* [n][Fs] */
+    float* y;                /* [n][k][H] */
+    float* ys;               /* [n][H] */
+    uint16_t* routed;        /* [n][H] */
+    uint16_t* shared;        /* [n][H] */
+    double* routed_exact;    /* [n][H] */
+    double* shared_exact;    /* [n][H] */
+} orc_batch_out;
+
+int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok, int threshold,
+                        const uint16_t* residual, const uint16_t* routed_prev, const uint16_t* shared_prev,
+                        const float* x, orc_batch_out* o);
+
+/* One weight row on the bf16 path: f32(sum_{i<n} bf16(f32(w_i)) * bf16(x_i));
+ * elements past n count as zero activations. */
+float orc_row_dot_bf16(const uint8_t* row, int type, int K, const float* x, int n);
+
 /* Threads the OpenMP loops use (1 when built without OpenMP). */
 int orc_num_threads(void);
 

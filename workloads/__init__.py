@@ -80,7 +80,7 @@ def row_bytes(typ, K):
 
 # ------------------------------------------------------------------ seeds
 # Tensor ids for the seed spawn key.
-T_NORM, T_ROUTER, T_SGATE, T_GATE, T_UP, T_DOWN, T_SG, T_SU, T_SD, T_INPUT, T_RPREV, T_SPREV, T_ZERO = range(13)
+T_NORM, T_ROUTER, T_SGATE, T_GATE, T_UP, T_DOWN, T_SG, T_SU, T_SD, T_INPUT, T_RPREV, T_SPREV, T_ZERO, T_PAIR, T_STEER = range(15)
 
 
 def seed_for(cfg_index, layer, tensor, expert=0, base=0):
@@ -285,6 +285,50 @@ def prev_outputs(cfg, token, device="cpu", layer=0):
     if cfg.three_input and cfg.Fs > 0:
         out["shared_prev"] = randn((cfg.H,), seed_for(cfg.config_index, layer, T_SPREV, token), device).to(torch.bfloat16)
     return out
+
+
+def batch_pair(cfg, layer=0):
+    """The two experts A < B that a quarter of a batch is steered to (seeded)."""
+    rng = np.random.default_rng(seed_for(cfg.config_index, layer, T_PAIR))
+    a, b = sorted(int(e) for e in rng.choice(cfg.E, size=2, replace=False))
+    return a, b
+
+
+def steered_tokens(cfg, n_tok, layer=0, frac=0.25):
+    """Seeded choice of round(frac * n_tok) token indices of a batch."""
+    rng = np.random.default_rng(seed_for(cfg.config_index, layer, T_STEER, n_tok))
+    n = int(round(frac * n_tok))
+    return sorted(int(t) for t in rng.choice(n_tok, size=n, replace=False))
+
+
+def batch_inputs(cfg, n_tok, device="cpu", layer=0, lam=1.0):
+    """Inputs of a batch of n_tok tokens (3-input norm form, bf16 [n_tok][H]).
+    Every token draws residual, routed_prev and shared_prev ~N(0,1); the
+    steered quarter instead gets residual = z + lam*sqrt(H)*unit(w * (R_A + R_B))
+    (w the norm weight, R_A, R_B the two chosen router rows, z its own draw)
+    and zero previous outputs, which pushes experts A and B to the top of its
+    ranking.  Returns (inputs dict, steered token list, (A, B))."""
+    res, rp, sp = [], [], []
+    for t in range(n_tok):
+        r = randn((cfg.H,), seed_for(cfg.config_index, layer, T_INPUT, t), device)
+        res.append(r)
+        rp.append(randn((cfg.H,), seed_for(cfg.config_index, layer, T_RPREV, t), device))
+        sp.append(randn((cfg.H,), seed_for(cfg.config_index, layer, T_SPREV, t), device))
+    a, b = batch_pair(cfg, layer)
+    steer = steered_tokens(cfg, n_tok, layer)
+    if steer:
+        w = rand_uniform((cfg.H,), seed_for(cfg.config_index, layer, T_NORM), 0.5, 1.5, device)
+        rows = _router_rows(cfg, layer, device)
+        v = w * (rows[a] + rows[b])
+        v = v / torch.linalg.vector_norm(v)
+        for t in steer:
+            res[t] = res[t] + lam * (cfg.H ** 0.5) * v
+            rp[t] = torch.zeros_like(rp[t])
+            sp[t] = torch.zeros_like(sp[t])
+    out = {"residual": torch.stack(res).to(torch.bfloat16),
+           "routed_prev": torch.stack(rp).to(torch.bfloat16),
+           "shared_prev": torch.stack(sp).to(torch.bfloat16)}
+    return out, steer, (a, b)
 
 
 def zero_tokens(cfg, n_tokens):
