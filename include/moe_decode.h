@@ -75,6 +75,8 @@ extern "C" {
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_FFN 4096
 #define MOE_MAX_LAYERS 256
+#define MOE_MAX_BATCH 64      /* tokens of one grouped (batch > 1) call */
+#define MOE_MAX_GROUP_MIN 16  /* largest group size threshold */
 
 typedef struct moe_layer_desc {
     int hidden;        /* H: multiple of 256, <= MOE_MAX_HIDDEN */
@@ -202,6 +204,42 @@ int expert_ffn_q4k(const moe_layer_desc* desc, const moe_layer_weights* w,
  * ---------------------------------------------------------------------- */
 int moe_decode_layer(const moe_layer_desc* desc, const moe_layer_weights* w,
                      const moe_layer_io* io, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a8: several tokens at once, experts grouped by the tokens that selected
+ * them (the pages describe batch 1 only; this is the batch > 1 reading).
+ * Per token the norm, router, top-k and weights are the batch-1 steps.  The
+ * group of expert e is the set of tokens whose ids contain e (token order).
+ * A group of >= group_min tokens reads the expert's rows once and runs on the
+ * matrix cores with bf16 inputs: weights decoded to fp32 then rounded to bf16,
+ * activations bf16(xn) for gate/up and bf16(h) for down, fp32 accumulation;
+ * h = silu(g) * u in fp32.  A smaller group runs the batch-1 integer path
+ * (Q8_1 activations, int8 dots) for each of its tokens.  The shared expert is
+ * one group of all n_tok tokens.  routed_out[t] = bf16(sum_s weights[t][s] *
+ * y[t][s]) in slot order; shared_out[t] = bf16(shared_gate[t] * ys[t]).
+ *
+ * moe_batch_workspace_size: bytes of workspace for n_tok tokens (0 on a bad
+ * description or n_tok outside 1..MOE_MAX_BATCH).
+ *
+ * expert_ffn_grouped (a4..a6 + a8): xn [n_tok][H] fp32 (16-byte aligned);
+ * xq [n_tok][H/32] Q8_1; ids, weights [n_tok][k]; shared_gate [n_tok] (read
+ * when Fs > 0); routed_out, shared_out [n_tok][H] bf16; h [n_tok][k][F] and
+ * hs [n_tok][Fs] fp32 or NULL (then kept in the workspace).  group_min in
+ * 1..MOE_MAX_GROUP_MIN.  All device.  An id outside [0, E) is never read
+ * through: every output of the call becomes NaN.
+ *
+ * moe_decode_layer_batch (a1..a6 + a8): io fields hold [n_tok][...] arrays
+ * (residual, routed_in, shared_in, x, out_sum, routed_out, shared_out, xn,
+ * xq, logits, ids, weights, shared_gate); optional ones may be NULL; io->h and
+ * io->hs, when given, are [n_tok][k][F] and [n_tok][Fs].
+ * ---------------------------------------------------------------------- */
+size_t moe_batch_workspace_size(const moe_layer_desc* desc, int n_tok);
+int expert_ffn_grouped(const moe_layer_desc* desc, const moe_layer_weights* w, const float* xn, const void* xq,
+                       const int32_t* ids, const float* weights, const float* shared_gate, int n_tok,
+                       int group_min, uint16_t* routed_out, uint16_t* shared_out, float* h, float* hs,
+                       void* ws, size_t ws_bytes, void* stream);
+int moe_decode_layer_batch(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_layer_io* io,
+                           int n_tok, int group_min, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * a7: the L-layer stack for one token ([P239] Summary: decode is graph- and

@@ -78,6 +78,8 @@ def _declare(L):
     L.orc_moe_layer_batch.argtypes = [P, P, C.c_int, C.c_int, P, P, P, P, P]
     L.orc_moe_layer_batch.restype = C.c_int
     L.orc_row_dot_bf16.argtypes = [P, C.c_int, C.c_int, P, C.c_int]; L.orc_row_dot_bf16.restype = C.c_float
+    L.orc_rows_dot_bf16.argtypes = [P, C.c_int, C.c_int, C.c_int, P, C.c_int, C.c_int, P]
+    L.orc_rows_dot_bf16.restype = None
 
 
 def _p(a):
@@ -367,6 +369,16 @@ def row_dot_bf16(row, typ, K, x, n=None):
     x = np.ascontiguousarray(x, dtype=np.float32)
     row = _u8(row)
     return float(lib().orc_row_dot_bf16(_p(row), typ, K, _p(x), len(x) if n is None else n))
+
+
+def rows_dot_bf16(rows, typ, K, n_rows, x):
+    """n_rows weight rows on the bf16 path against the vectors x [m][n] (n <= K;
+    elements past n are zero activations): returns fp32 [m][n_rows]."""
+    x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+    rows = _u8(rows)
+    out = np.zeros((x.shape[0], n_rows), np.float32)
+    lib().orc_rows_dot_bf16(_p(rows), typ, K, n_rows, _p(x), x.shape[1], x.shape[0], _p(out))
+    return out
 
 
 def moe_stack(desc, layers, inp, per_layer=False):

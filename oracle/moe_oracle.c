@@ -819,6 +819,23 @@ int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok, int 
     return 0;
 }
 
+/* Rows on the bf16 path against m vectors (test export):
+ * out[j][r] = f32(sum_{i<n} bf16(f32(w_ri)) * bf16(x_j[i])), x [m][n]. */
+void orc_rows_dot_bf16(const uint8_t* rows, int type, int K, int n_rows, const float* x, int n, int m, float* out)
+{
+    double* wb = (double*)malloc(sizeof(double) * (size_t)K * n_rows);
+    decode_rows_bf16(rows, type, K, n_rows, wb);
+    for (int j = 0; j < m; ++j) {
+        int r;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+        for (r = 0; r < n_rows; ++r)
+            out[(long)j * n_rows + r] = dot_bf16(wb + (long)r * K, x + (long)j * n, n);
+    }
+    free(wb);
+}
+
 /* One row on the bf16 path (test export): f32(sum_{i<n} bf16(f32(w_i)) * bf16(x_i)). */
 float orc_row_dot_bf16(const uint8_t* row, int type, int K, const float* x, int n)
 {

@@ -193,6 +193,9 @@ int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok, int 
  * elements past n count as zero activations. */
 float orc_row_dot_bf16(const uint8_t* row, int type, int K, const float* x, int n);
 
+/* n_rows rows on the bf16 path against m vectors x [m][n]: out [m][n_rows]. */
+void orc_rows_dot_bf16(const uint8_t* rows, int type, int K, int n_rows, const float* x, int n, int m, float* out);
+
 /* Threads the OpenMP loops use (1 when built without OpenMP). */
 int orc_num_threads(void);
 

@@ -72,13 +72,21 @@ _moe_stack_bind = _sig("moe_stack_bind", C.c_int, C.POINTER(LayerDesc), C.POINTE
                        C.c_size_t, P)
 _moe_decode_stack = _sig("moe_decode_stack", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights), C.c_int, P, P, P,
                          P, C.c_int, P, C.c_size_t, P)
+_moe_batch_workspace_size = _sig("moe_batch_workspace_size", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
+_expert_ffn_grouped = _sig("expert_ffn_grouped", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights), P, P, P, P, P,
+                           C.c_int, C.c_int, P, P, P, P, P, C.c_size_t, P)
+_moe_decode_layer_batch = _sig("moe_decode_layer_batch", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights),
+                               C.POINTER(LayerIO), C.c_int, C.c_int, P, C.c_size_t, P)
 _moe_stack_status_offset = _sig("moe_stack_status_offset", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
 _moe_stack_trace_offset = _sig("moe_stack_trace_offset", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
 _moe_test_subblock_dots = _sig("moe_test_subblock_dots", C.c_int, P, C.c_int, C.c_int, C.c_int, P, P, P)
 
 EXPORTS = ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", "moe_stack_bind",
            "moe_decode_stack", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
-           "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots")
+           "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots",
+           "moe_batch_workspace_size", "expert_ffn_grouped", "moe_decode_layer_batch")
+MAX_BATCH = 64
+MAX_GROUP_MIN = 16
 
 
 # ---------------------------------------------------------------- marshalling helpers
@@ -177,6 +185,41 @@ def moe_decode_layer(desc, weights, io, ws, stream=None):
     lio = LayerIO(**{n: ptr(io.get(n)) for n, _ in LayerIO._fields_})
     return _check("moe_decode_layer", _moe_decode_layer(C.byref(desc), C.byref(lw), C.byref(lio), ptr(ws),
                                                         ws.numel() * ws.element_size(), stream_handle(stream)))
+
+
+def moe_batch_workspace_size(desc, n_tok):
+    return _moe_batch_workspace_size(C.byref(desc), n_tok)
+
+
+def alloc_batch_workspace(desc, n_tok, device="cuda"):
+    """A zero-initialised, 256-byte aligned workspace for the grouped path."""
+    n = moe_batch_workspace_size(desc, n_tok)
+    if n == 0:
+        raise MoeError("moe_batch_workspace_size", -2)
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + n]
+    moe_workspace_init(ws)
+    return ws
+
+
+def expert_ffn_grouped(desc, weights, xn, xq, ids, wts, shared_gate, n_tok, group_min, routed_out, shared_out,
+                       h, hs, ws, stream=None):
+    lw = weights if isinstance(weights, LayerWeights) else make_weights(weights)
+    return _check("expert_ffn_grouped", _expert_ffn_grouped(C.byref(desc), C.byref(lw), ptr(xn), ptr(xq), ptr(ids),
+                                                            ptr(wts), ptr(shared_gate), n_tok, group_min,
+                                                            ptr(routed_out), ptr(shared_out), ptr(h), ptr(hs),
+                                                            ptr(ws), ws.numel() * ws.element_size(),
+                                                            stream_handle(stream)))
+
+
+def moe_decode_layer_batch(desc, weights, io, n_tok, group_min, ws, stream=None):
+    """io: dict of CUDA tensors ([n_tok][...]) keyed by the moe_layer_io field names."""
+    lw = weights if isinstance(weights, LayerWeights) else make_weights(weights)
+    lio = LayerIO(**{n: ptr(io.get(n)) for n, _ in LayerIO._fields_})
+    return _check("moe_decode_layer_batch", _moe_decode_layer_batch(C.byref(desc), C.byref(lw), C.byref(lio), n_tok,
+                                                                    group_min, ptr(ws), ws.numel() * ws.element_size(),
+                                                                    stream_handle(stream)))
 
 
 def _layer_array(layers):

@@ -160,6 +160,80 @@ int moe_decode_layer(const moe_layer_desc* desc, const moe_layer_weights* w, con
   return launch_down(desc, w, h, hs, ids, wts, sg, io->routed_out, io->shared_out, st);
 }
 
+size_t moe_batch_workspace_size(const moe_layer_desc* desc, int n_tok) {
+  if (check_desc(desc) != MOE_OK || n_tok <= 0 || n_tok > MOE_MAX_BATCH) return 0;
+  return batch_ws_layout(desc, n_tok).total;
+}
+
+int expert_ffn_grouped(const moe_layer_desc* desc, const moe_layer_weights* w, const float* xn, const void* xq,
+                       const int32_t* ids, const float* weights, const float* shared_gate, int n_tok, int group_min,
+                       uint16_t* routed_out, uint16_t* shared_out, float* h, float* hs, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  rc = check_weights(desc, w);
+  if (rc) return rc;
+  if (!xn || !xq || !ids || !weights || !routed_out) return MOE_ERR_NULL;
+  if (desc->shared_ffn > 0 && (!shared_gate || !shared_out)) return MOE_ERR_NULL;
+  if (n_tok <= 0 || n_tok > MOE_MAX_BATCH || group_min < 1 || group_min > MOE_MAX_GROUP_MIN) return MOE_ERR_SHAPE;
+  if (!aligned(xn, 16) || !aligned(xq, 4) || !aligned(ids, 4) || !aligned(weights, 4) || !aligned(routed_out, 2) ||
+      (shared_out && !aligned(shared_out, 2)) || (shared_gate && !aligned(shared_gate, 4)) || (h && !aligned(h, 16)) ||
+      (hs && !aligned(hs, 16)))
+    return MOE_ERR_ALIGN;
+  const BatchWs L = batch_ws_layout(desc, n_tok);
+  rc = check_ws(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  return launch_grouped_ffn(desc, w, xn, xq, ids, weights, shared_gate, n_tok, group_min, routed_out, shared_out,
+                            h ? h : at<float>(ws, L.h), hs ? hs : at<float>(ws, L.hs), wsb, L, as_stream(stream));
+}
+
+int moe_decode_layer_batch(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_layer_io* io, int n_tok,
+                           int group_min, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  rc = check_weights(desc, w);
+  if (rc) return rc;
+  if (!io || !io->routed_out) return MOE_ERR_NULL;
+  if (desc->norm ? (!io->residual || !io->out_sum) : !io->x) return MOE_ERR_NULL;
+  if (desc->shared_ffn > 0 && !io->shared_out) return MOE_ERR_NULL;
+  if (io->shared_in && !io->routed_in) return MOE_ERR_NULL;
+  if (n_tok <= 0 || n_tok > MOE_MAX_BATCH || group_min < 1 || group_min > MOE_MAX_GROUP_MIN) return MOE_ERR_SHAPE;
+  if ((io->x && !aligned(io->x, 16)) || (io->xn && !aligned(io->xn, 16)) || (io->xq && !aligned(io->xq, 4)) ||
+      (io->residual && !aligned(io->residual, 2)) || (io->out_sum && !aligned(io->out_sum, 2)) ||
+      !aligned(io->routed_out, 2) || (io->shared_out && !aligned(io->shared_out, 2)) ||
+      (io->logits && !aligned(io->logits, 4)) || (io->ids && !aligned(io->ids, 4)) ||
+      (io->weights && !aligned(io->weights, 4)) || (io->shared_gate && !aligned(io->shared_gate, 4)) ||
+      (io->h && !aligned(io->h, 16)) || (io->hs && !aligned(io->hs, 16)))
+    return MOE_ERR_ALIGN;
+  const BatchWs L = batch_ws_layout(desc, n_tok);
+  rc = check_ws(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  hipStream_t st = as_stream(stream);
+  const int H = desc->hidden, E = desc->n_experts, k = desc->top_k;
+  float* xn = io->xn ? io->xn : at<float>(ws, L.xn);
+  void* xq = io->xq ? io->xq : at<void>(ws, L.xq);
+  int32_t* ids = io->ids ? io->ids : at<int32_t>(ws, L.ids);
+  float* wts = io->weights ? io->weights : at<float>(ws, L.wts);
+  float* sg = io->shared_gate ? io->shared_gate : at<float>(ws, L.sg);
+  if (desc->norm) {
+    rc = launch_norm(io->residual, io->routed_in, io->shared_in, w->norm_w, H, n_tok, desc->eps, io->out_sum, xn, xq, 1,
+                     st);
+  } else {
+    if (hipMemcpyAsync(xn, io->x, sizeof(float) * (size_t)n_tok * H, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return MOE_ERR_HIP;
+    rc = launch_quantize(io->x, n_tok * H, xq, st);
+  }
+  if (rc) return rc;
+  rc = launch_router(xn, w->router_w, desc->shared_ffn > 0 ? w->shared_gate_w : nullptr, n_tok, H, E, k,
+                     at<float>(ws, L.router + kRouterLogitsOff), io->logits, ids, wts, sg,
+                     at<unsigned>(ws, L.router), st);
+  if (rc) return rc;
+  return launch_grouped_ffn(desc, w, xn, xq, ids, wts, sg, n_tok, group_min, io->routed_out, io->shared_out,
+                            io->h ? io->h : at<float>(ws, L.h), io->hs ? io->hs : at<float>(ws, L.hs),
+                            static_cast<uint8_t*>(ws), L, st);
+}
+
 int moe_stack_bind(const moe_layer_desc* desc, const moe_layer_weights* layers, int n_layers, void* ws,
                    size_t ws_bytes, void* stream) {
   int rc = check_desc(desc);

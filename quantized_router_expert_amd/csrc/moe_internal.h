@@ -37,6 +37,15 @@ int launch_gate_up(const moe_layer_desc* d, const moe_layer_weights* w, const vo
 int launch_down(const moe_layer_desc* d, const moe_layer_weights* w, const float* h, const float* hs, const int32_t* ids,
                 const float* wts, const float* sg, uint16_t* routed, uint16_t* shared, hipStream_t st);
 int launch_fill(void* p, size_t n_u32, uint32_t v, hipStream_t st);
+
+// workspace of the grouped (batch > 1) path
+struct BatchWs {
+  size_t router, cnt, moff, members, dlist, nd, err, xn, xq, ids, wts, sg, h, hs, y, ys, total;
+};
+BatchWs batch_ws_layout(const moe_layer_desc* d, int n_tok);
+int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const float* xn, const void* xq,
+                       const int32_t* ids, const float* wts, const float* sg, int n, int gmin, uint16_t* routed,
+                       uint16_t* shared, float* h, float* hs, uint8_t* ws, const BatchWs& L, hipStream_t st);
 int launch_subblock_dots(const void* rows, int type, int K, int n_rows, const void* xq, int32_t* out, hipStream_t st);
 
 }  // namespace moe

@@ -42,9 +42,11 @@ def assert_bf16_within(gpu_u16, exact, what="", rel=REL, floor=FLOOR):
     ok, tol = bf16_within(gpu_u16, exact, rel, floor)
     if not ok.all():
         i = np.flatnonzero(~ok)[:5]
-        g = bf16_bits_to_f64(gpu_u16)
+        g = bf16_bits_to_f64(gpu_u16).ravel()
+        r = np.asarray(exact, np.float64).ravel()
         raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} bf16 outputs outside the bound; "
-                             f"idx {i.tolist()} gpu {g[i].tolist()} exact {np.asarray(exact)[i].tolist()}")
+                             f"flat idx {i.tolist()} gpu {g[i].tolist()} exact {r[i].tolist()} "
+                             f"allowed {np.asarray(tol).ravel()[i].tolist()}")
 
 
 def assert_f32_within(gpu, ref, what="", rel=REL, floor=FLOOR):
@@ -56,7 +58,7 @@ def assert_f32_within(gpu, ref, what="", rel=REL, floor=FLOOR):
     if bad.any():
         i = np.flatnonzero(bad)[:5]
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} fp32 values outside the bound; "
-                             f"idx {i.tolist()} gpu {g[i].tolist()} ref {r[i].tolist()}")
+                             f"flat idx {i.tolist()} gpu {g.ravel()[i].tolist()} ref {r.ravel()[i].tolist()}")
 
 
 def ulp_diff_f32(a, b):

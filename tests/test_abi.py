@@ -152,3 +152,34 @@ def test_layer_and_stack_validation(q):
     assert q._moe_test_subblock_dots(FAKE, 12, 100, 1, FAKE, FAKE, None) == -2
     assert q._moe_workspace_init(None, 1024, None) == -5
     assert q._moe_workspace_init(FAKE + 8, 1024, None) == -4
+
+
+def test_grouped_path_validation(q):
+    d = _desc(q)
+    w = q.LayerWeights(**{n: FAKE for n, _ in q.LayerWeights._fields_})
+    f = q._expert_ffn_grouped
+    need = q.moe_batch_workspace_size(d, 8)
+    assert need > 0
+    assert q.moe_batch_workspace_size(d, 0) == 0 and q.moe_batch_workspace_size(d, 65) == 0
+
+    def call(xn=FAKE, xq=FAKE, ids=FAKE, wts=FAKE, sg=FAKE, n=8, gmin=4, ro=FAKE, so=FAKE, h=None, hs=None, ws=FAKE,
+             wsb=need):
+        return f(C.byref(d), C.byref(w), xn, xq, ids, wts, sg, n, gmin, ro, so, h, hs, ws, wsb, None)
+
+    assert call(xn=None) == -1
+    assert call(sg=None) == -1                   # the shared expert needs its gate values
+    assert call(so=None) == -1
+    assert call(n=0) == -2
+    assert call(n=65) == -2
+    assert call(gmin=0) == -2
+    assert call(gmin=17) == -2
+    assert call(xn=FAKE + 4) == -4               # the bf16 path reads xn 16 bytes at a time
+    assert call(h=FAKE + 8) == -4
+    assert call(wsb=need - 1) == -5
+    io = q.LayerIO(residual=FAKE, out_sum=FAKE, routed_out=FAKE, shared_out=FAKE)
+    g = q._moe_decode_layer_batch
+    assert g(C.byref(d), C.byref(w), C.byref(io), 8, 4, FAKE, need - 1, None) == -5
+    assert g(C.byref(d), C.byref(w), C.byref(io), 0, 4, FAKE, need, None) == -2
+    assert g(C.byref(d), C.byref(w), C.byref(io), 8, 99, FAKE, need, None) == -2
+    io2 = q.LayerIO(residual=FAKE, out_sum=FAKE, routed_out=FAKE, shared_out=None)
+    assert g(C.byref(d), C.byref(w), C.byref(io2), 8, 4, FAKE, need, None) == -1

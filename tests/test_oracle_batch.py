@@ -53,6 +53,17 @@ def test_row_dot_bf16_matches_numpy(orc, typ, n_active):
         assert abs(float(got) - float(ref)) <= float(np.spacing(abs(ref))), (seed, got, ref)
 
 
+def test_rows_dot_bf16_is_the_single_row_dot(orc):
+    K, n_rows = 512, 7
+    rows = wl.quantize(wl.randn((n_rows, K), 77) * 0.02, wl.Q5_K).numpy()
+    x = np.random.default_rng(3).standard_normal((4, 300)).astype(np.float32)
+    rb = wl.row_bytes(wl.Q5_K, K)
+    got = orc.rows_dot_bf16(rows, wl.Q5_K, K, n_rows, x)
+    for j in range(4):
+        for r in range(n_rows):
+            assert got[j, r] == np.float32(orc.row_dot_bf16(rows.reshape(n_rows, rb)[r], wl.Q5_K, K, x[j], 300))
+
+
 def test_row_dot_bf16_exact_on_small_integers(orc):
     """d = 1, dmin = 0, scales 1..3, codes 0..15: every weight and activation is a
     small integer, so no rounding happens anywhere and the result is the integer dot."""
