@@ -38,6 +38,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=128)
     p.add_argument("--repeats", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--no-batch", action="store_true", help="skip the grouped batch-path leg")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a kernel that reads and writes 1 GiB each (HBM counter calibration)")
@@ -137,6 +138,49 @@ def time_steps(stack, steps, warmup, repeats):
         torch.cuda.synchronize()
         per_token_us.append(e0.elapsed_time(e1) * 1e3 / steps)
     return per_token_us
+
+
+def batch_leg(q, sizes=(8, 32), group_min=4, iters=30):
+    """The grouped batch path on one layer of the 40-layer shape: per batch
+    size, microseconds per layer step (norm, router, grouped experts, combine)
+    over `iters` steps on fresh seeded inputs, tokens/s, and GB/s over the
+    bytes the step must read (router, shared expert, each distinct selected
+    expert once)."""
+    cfg = wl.CONFIGS["batch"]
+    W = wl.layer_weights(cfg, 0, "cuda")
+    H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+    desc = q.make_desc(H, E, k, F, Fs, eps=cfg.eps)
+    per_expert = 2 * F * wl.row_bytes(wl.Q4_K, H) + H * wl.row_bytes(wl.Q4_K, wl.pad_k(wl.Q4_K, F))
+    fixed = 4 * E * H + 4 * H + 4 * H + 2 * Fs * wl.row_bytes(wl.Q4_K, H) + H * wl.row_bytes(wl.Q4_K, Fs)
+    out = {}
+    for n in sizes:
+        ws = q.alloc_batch_workspace(desc, n)
+        inp, _, _ = wl.batch_inputs(cfg, n, "cuda")
+        res = inp["residual"].contiguous()
+        io = {"residual": res, "routed_in": inp["routed_prev"].contiguous(),
+              "shared_in": inp["shared_prev"].contiguous(),
+              "out_sum": torch.empty(n, H, dtype=torch.bfloat16, device="cuda"),
+              "routed_out": torch.empty(n, H, dtype=torch.bfloat16, device="cuda"),
+              "shared_out": torch.empty(n, H, dtype=torch.bfloat16, device="cuda"),
+              "ids": torch.empty(n, k, dtype=torch.int32, device="cuda")}
+        q.moe_decode_layer_batch(desc, W, io, n, group_min, ws)
+        torch.cuda.synchronize()
+        distinct = len(set(io["ids"].flatten().tolist()))
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            q.moe_decode_layer_batch(desc, W, io, n, group_min, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        nbytes = fixed + distinct * per_expert
+        out[f"batch{n}"] = {"us_per_layer_step": us, "tokens_per_s_per_layer": n * 1e6 / us,
+                            "distinct_experts": distinct, "bytes_per_step": nbytes,
+                            "achieved_GBs": nbytes / (us * 1e-6) / 1e9, "group_min": group_min}
+        print(f"# batch {n}: {us:.1f} us per layer step, {distinct} distinct experts, "
+              f"{out[f'batch{n}']['achieved_GBs']:.0f} GB/s", file=sys.stderr, flush=True)
+    return out
 
 
 def launch_durations(stack, n):
@@ -293,6 +337,7 @@ def main():
         results[name] = res
         print(f"# {name}: {med:.1f} us/token ({res['achieved_GBs']:.0f} GB/s)", file=sys.stderr, flush=True)
     stack, res = primary if primary else (None, results[order[0]])
+    batch = None if a.no_batch else batch_leg(q)
     cpu = None
     if not a.no_cpu and stack is not None:
         c = cpu_baseline(stack, a.cpu_seconds)
@@ -316,6 +361,7 @@ def main():
                      "alg_bytes_per_launch": res["alg_bytes_per_token"], "launch_us": res["launch_us"]},
         "cpu_baseline": cpu,
         "variants": results,
+        "batch": batch,
     }
     print(json.dumps(line))
 
