@@ -13,7 +13,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_decode.so")
+# MOE_DECODE_LIB names another build of the same library (e.g. to compare two builds)
+LIB_PATH = os.environ.get("MOE_DECODE_LIB") or os.path.join(HERE, "libmoe_decode.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run quantized_router_expert_amd/build.py (or __graft_entry__.build())")

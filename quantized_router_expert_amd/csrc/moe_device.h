@@ -333,14 +333,12 @@ __device__ __forceinline__ void quantize_q81_blocks(int nblk, Src src, Dst codes
 // dwords s0 (bytes 0..3), s1 (4..7), s2 (8..11).
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xffu; }
 __device__ __forceinline__ void kquant_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int j, int& sc, int& m) {
-  if (j < 4) {
-    sc = (int)(byte_of(s0, j) & 63u);
-    m = (int)(byte_of(s1, j) & 63u);
-  } else {
-    int i = j - 4;
-    sc = (int)((byte_of(s2, i) & 0xfu) | ((byte_of(s0, i) >> 6) << 4));
-    m = (int)((byte_of(s2, i) >> 4) | ((byte_of(s1, i) >> 6) << 4));
-  }
+  // branch-free (lanes of a wave decode different sub-blocks)
+  const int i = j & 3;
+  const uint32_t b0 = byte_of(s0, i), b1 = byte_of(s1, i), b2 = byte_of(s2, i);
+  const bool hi = j >= 4;
+  sc = (int)(hi ? ((b2 & 0xfu) | ((b0 >> 6) << 4)) : (b0 & 63u));
+  m = (int)(hi ? ((b2 >> 4) | ((b1 >> 6) << 4)) : (b1 & 63u));
 }
 
 // ---------------------------------------------------------------- integer dots
@@ -350,7 +348,7 @@ __device__ __forceinline__ void kquant_scale_min(uint32_t s0, uint32_t s1, uint3
 template <bool Q5>
 __device__ __forceinline__ void kquant_group_dots(const uint32_t qs[8], const uint32_t* qh, int g,
                                                   const uint32_t alo[8], const uint32_t ahi[8], int& Dlo, int& Dhi) {
-  int lo = 0, hi = 0;
+  int lo[2] = {0, 0}, hi[2] = {0, 0};   // two independent chains each (exact integer sums)
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     uint32_t wl = qs[t] & 0x0f0f0f0fu;
@@ -359,18 +357,18 @@ __device__ __forceinline__ void kquant_group_dots(const uint32_t qs[8], const ui
       wl |= ((qh[t] >> (2 * g)) & 0x01010101u) << 4;
       wh |= ((qh[t] >> (2 * g + 1)) & 0x01010101u) << 4;
     }
-    lo = __builtin_amdgcn_sdot4((int)wl, (int)alo[t], lo, false);
-    hi = __builtin_amdgcn_sdot4((int)wh, (int)ahi[t], hi, false);
+    lo[t & 1] = __builtin_amdgcn_sdot4((int)wl, (int)alo[t], lo[t & 1], false);
+    hi[t & 1] = __builtin_amdgcn_sdot4((int)wh, (int)ahi[t], hi[t & 1], false);
   }
-  Dlo = lo;
-  Dhi = hi;
+  Dlo = lo[0] + lo[1];
+  Dhi = hi[0] + hi[1];
 }
 
 __device__ __forceinline__ int q8_block_dot(const uint32_t w[8], const uint32_t a[8]) {
-  int acc = 0;
+  int acc[2] = {0, 0};
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_sdot4((int)w[t], (int)a[t], acc, false);
-  return acc;
+  for (int t = 0; t < 8; ++t) acc[t & 1] = __builtin_amdgcn_sdot4((int)w[t], (int)a[t], acc[t & 1], false);
+  return acc[0] + acc[1];
 }
 
 // Activations staged in LDS: int8 codes [K] (16-byte aligned), per-block d and s as float.
@@ -464,6 +462,9 @@ struct RowRef {
 // 0; with T > 64 a lane takes tasks t, t+64, ...), and a DPP/permlane sum over
 // the group gives the row's fp64 value.  Waves [0, nw) split the rows (wave
 // index `wave`); out[r] receives row r.  rowfn(r) returns the RowRef of row r.
+// Each lane works on two rows at once (this round's and the next round's), so
+// two independent dependency chains are in flight; the second is skipped when
+// the wave has no row there.
 template <int TYPE, class RowFn>
 __device__ __forceinline__ void rows_dot(int nrows, int T, RowFn rowfn, double* out, int wave, int nw) {
   int TP = 1;
@@ -471,15 +472,30 @@ __device__ __forceinline__ void rows_dot(int nrows, int T, RowFn rowfn, double* 
   const int rpi = 64 / TP;
   const int lane = threadIdx.x & 63;
   const int rl = lane / TP, t0 = lane - rl * TP;
-  for (int r0 = wave * rpi; r0 < nrows; r0 += nw * rpi) {
-    const int r = r0 + rl;
-    double v = 0.0;
-    if (r < nrows) {
-      const RowRef rr = rowfn(r);
-      for (int t = t0; t < T; t += 64) v += row_task<TYPE>(rr.row, t, rr.act);
+  const int step = nw * rpi;
+  const int tt = (t0 < T) ? t0 : 0;
+  for (int r0 = wave * rpi; r0 < nrows; r0 += 2 * step) {
+    const int ra = r0 + rl, rb = r0 + step + rl;
+    const bool two = (r0 + step) < nrows;   // wave-uniform
+    const RowRef A = rowfn(ra < nrows ? ra : nrows - 1);
+    double va = row_task<TYPE>(A.row, tt, A.act);
+    double vb = 0.0;
+    RowRef B = A;
+    if (two) {
+      B = rowfn(rb < nrows ? rb : nrows - 1);
+      vb = row_task<TYPE>(B.row, tt, B.act);
     }
-    v = group_sum_f64(v, TP);
-    if (t0 == 0 && r < nrows) out[r] = v;
+    if (t0 >= T) { va = 0.0; vb = 0.0; }
+    for (int t = t0 + 64; t < T; t += 64) {
+      va += row_task<TYPE>(A.row, t, A.act);
+      if (two) vb += row_task<TYPE>(B.row, t, B.act);
+    }
+    va = group_sum_f64(va, TP);
+    if (two) vb = group_sum_f64(vb, TP);
+    if (t0 == 0) {
+      if (ra < nrows) out[ra] = va;
+      if (two && rb < nrows) out[rb] = vb;
+    }
   }
 }
 

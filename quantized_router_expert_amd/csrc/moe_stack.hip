@@ -208,6 +208,7 @@ __device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int w, 
     const int e = 64 * w + lane + 256 * j;
     key[j] = (e < E) ? logit_key(lg[e]) : 0u;
   }
+  if (lane >= k && lane < 16) cand[16 * w + lane] = 0ull;   // slots past k never rank
   for (int s = 0; s < k; ++s) {
     uint32_t hv = key[0], hid = (uint32_t)(64 * w + lane);
 #pragma unroll
@@ -232,32 +233,60 @@ __device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int w, 
   }
 }
 
-__device__ __forceinline__ void topk_candidates(const float* lg, int E, int k, int wave, unsigned long long* cand) {
+// Count of the 64 keys at `k2` (32 pairs) that are above c.
+__device__ __forceinline__ int count_above(const ulonglong2* k2, unsigned long long c) {
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const ulonglong2 v = k2[j];
+    rank += (v.x > c ? 1 : 0) + (v.y > c ? 1 : 0);
+  }
+  return rank;
+}
+
+// E <= 256: wave w ranks its 64 experts against each other in parallel
+// (one key per lane; 32 broadcast 16-byte LDS loads and 64 independent
+// compares per lane, no dependent chain); the lanes ranked below k are the
+// wave's candidates, already in order.  keys: 256 u64 of LDS.
+__device__ __forceinline__ void wave_rank_topk(const float* lg, int E, int k, int w, unsigned long long* keys,
+                                               unsigned long long* cand) {
+  const int lane = threadIdx.x & 63;
+  const int e = 64 * w + lane;
+  const unsigned long long c = (e < E) ? (((unsigned long long)logit_key(lg[e]) << 32) | (uint32_t)~e) : 0ull;
+  keys[e] = c;
+  if (lane < 16) cand[16 * w + lane] = 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const int rank = count_above(reinterpret_cast<const ulonglong2*>(keys + 64 * w), c);
+  if (rank < k && c != 0ull) cand[16 * w + rank] = c;
+}
+
+__device__ __forceinline__ void topk_candidates(const float* lg, int E, int k, int wave, unsigned long long* keys,
+                                                unsigned long long* cand) {
   if (wave >= 4) return;
-  if (E <= 256) wave_topk<1>(lg, E, k, wave, cand);
+  if (E <= 256) wave_rank_topk(lg, E, k, wave, keys, cand);
   else if (E <= 512) wave_topk<2>(lg, E, k, wave, cand);
   else wave_topk<4>(lg, E, k, wave, cand);
 }
 
 // wave 0, after a barrier: slot ids -> sel[0..k), their logits -> lgsel[0..k),
-// the shared-gate logit -> lgsel[k]
-__device__ __forceinline__ void rank_candidates(const float* lg, int E, int k, bool has_sg,
+// the shared-gate logit -> lgsel[k].  Lane 16w + s holds candidate s of wave w
+// and counts the candidates above it; all 64 slots are read with unrolled
+// 16-byte loads (unused slots hold 0).  Returns true if an id is out of range.
+__device__ __forceinline__ bool rank_candidates(const float* lg, int E, int k, bool has_sg,
                                                 const unsigned long long* cand, uint32_t* sel, float* lgsel) {
   const int lane = threadIdx.x & 63;
-  unsigned long long c = 0ull;
-  if (lane < 4 * k) {
-    const int wq = lane / k;
-    c = cand[16 * wq + (lane - wq * k)];
-  }
-  int rank = 0;
-  for (int w = 0; w < 4; ++w)
-    for (int s = 0; s < k; ++s) rank += (cand[16 * w + s] > c) ? 1 : 0;
+  const unsigned long long c = ((lane & 15) < k) ? cand[lane] : 0ull;
+  const int rank = count_above(reinterpret_cast<const ulonglong2*>(cand), c);
   if (c != 0ull && rank < k) {
     const uint32_t id = ~(uint32_t)c;
     sel[rank] = id;
     lgsel[rank] = lg[id];
   }
   if (lane == 0) lgsel[k] = has_sg ? lg[E] : 0.0f;
+  const bool bad = (lane < k) && (sel[lane] >= (uint32_t)E);
+  return __any(bad);
 }
 
 // wave 0: routing weights sel[k..2k) and the shared gate sel[2k] from lgsel;
@@ -352,6 +381,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   double* red = reinterpret_cast<double*>(smem + g.o_red);
   float* yv = reinterpret_cast<float*>(smem + g.o_y);
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(smem + g.o_cand);
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(smem + g.o_keys);
   float* lgsel = reinterpret_cast<float*>(smem + g.o_lgsel);
 
   __shared__ uint32_t s_gen;
@@ -479,6 +509,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       // four independent fp64 partial sums per lane (fp64 keeps the fp32 result
       // of the sum independent of its order but for rare last-bit cases)
       double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+#pragma unroll 4
       for (int i = (tid & 63) * 4; i < H; i += 256) {
         const float4 wv = *reinterpret_cast<const float4*>(wr + i);
         const float4 xv = *reinterpret_cast<const float4*>(xn + i);
@@ -514,10 +545,12 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       lds_barrier();
       if (s_fail) { fail_out(); return; }
       bstamp(l, 13);
-      topk_candidates(reinterpret_cast<const float*>(xbuf), E, k, wave, cand);
+      topk_candidates(reinterpret_cast<const float*>(xbuf), E, k, wave, keys, cand);
       lds_barrier();
-      if (wave == 0) rank_candidates(reinterpret_cast<const float*>(xbuf), E, k, has_sg, cand, sel, lgsel);
+      if (wave == 0 && rank_candidates(reinterpret_cast<const float*>(xbuf), E, k, has_sg, cand, sel, lgsel))
+        s_fail = 1;
       lds_barrier();
+      if (s_fail) { fail_out(); return; }
       if (b == 0 && a.ids_out)
         for (int s = tid; s < k; s += kStackThreads) a.ids_out[(long)l * k + s] = (int32_t)sel[s];
     }
@@ -528,9 +561,6 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     const int slot = p0 / F;
     const int f0 = p0 - slot * F;
     const int nrp = (slot < k) ? min(g.RP, F - f0) : 0;
-    bool bad_id = false;
-    for (int s = 0; s < k; ++s) bad_id |= (sel[s] >= (uint32_t)E);
-    if (bad_id) { fail_out(); return; }
     if (nrp > 0 && wave < kPollWaves) {
       const long e = sel[slot];
       stage_async(rgu, w.gate + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0, kPollWaves);
@@ -544,7 +574,9 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     stamp(l, 5);
     bstamp(l, 6);
     // the down rows are needed only after the h exchange: requested once the
-    // gate/up rows have landed, so they do not share the memory system with them
+    // gate/up rows have landed, so they do not share the memory system with
+    // them (requested together, the gate/up rows land later by more than the
+    // request time saved)
     if (nrd > 0 && wave >= kPollWaves) {
       // wave 4+j queues slots j, j+4, j+8, j+12: their ids are read first, so
       // the requests go out back to back instead of each after an LDS round trip
@@ -623,28 +655,29 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
                      part + k * nrd, wave, kStackWaves);
       }
       lds_barrier();
-      for (int i = tid; i < (k + 1) * nrd; i += kStackThreads) {
-        const int m = i / nrd, r = i - m * nrd;
-        yv[m * g.RD + r] = (m < k || has_sg) ? (float)part[m * nrd + r] : 0.0f;
-      }
-      lds_barrier();
+      // combine: one lane per (row, slot), the slots of a row in GS adjacent
+      // lanes summed by a DPP tree (fp64; y_s is the fp32 row value)
       const float sgv = __uint_as_float(sel[2 * k]);
-      for (int r2 = tid; 2 * r2 < nrd; r2 += kStackThreads) {
-        uint32_t pr = 0;
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int r = 2 * r2 + h2;
-          double acc = 0.0;
-          for (int s = 0; s < k; ++s) acc += (double)__uint_as_float(sel[k + s]) * (double)yv[s * g.RD + r];
-          const uint16_t routed = f32_to_bf16((float)acc);
+      const int GS = (k <= 8) ? 8 : 16;
+      uint16_t* tb = reinterpret_cast<uint16_t*>(yv);
+      for (int i = tid; i < nrd * GS; i += kStackThreads) {
+        const int r = i / GS, sl = i - r * GS;
+        double v = 0.0;
+        if (sl < k) v = (double)__uint_as_float(sel[k + sl]) * (double)(float)part[sl * nrd + r];
+        v = group_sum_f64(v, GS);
+        if (sl == 0) {
+          const uint16_t routed = f32_to_bf16((float)v);
           float t = bf16_to_f32(routed);
           if (has_sg) {
-            const uint16_t shared = f32_to_bf16((float)((double)sgv * (double)yv[k * g.RD + r]));
+            const uint16_t shared = f32_to_bf16((float)((double)sgv * (double)(float)part[k * nrd + r]));
             t = bf16_to_f32(f32_to_bf16(bf16_to_f32(routed) + bf16_to_f32(shared)));
           }
-          pr |= (uint32_t)f32_to_bf16(t) << (16 * h2);
+          tb[r] = f32_to_bf16(t);
         }
-        ll_store(r_t, (row0 >> 1) + r2, pr, ep2, kAuxSC1);
       }
+      lds_barrier();
+      for (int r2 = tid; 2 * r2 < nrd; r2 += kStackThreads)
+        ll_store(r_t, (row0 >> 1) + r2, (uint32_t)tb[2 * r2] | ((uint32_t)tb[2 * r2 + 1] << 16), ep2, kAuxSC1);
     }
     lds_barrier();
     stamp(l, 9);
@@ -737,6 +770,7 @@ int stack_geometry(const moe_layer_desc* d, int G, StackGeom* out) {
   g.o_red = take(8L * (kStackThreads / 64));
   g.o_y = take(4L * (k + 1) * g.RD);
   g.o_cand = take(8L * 64);
+  g.o_keys = take(8L * 256);
   g.o_lgsel = take(4L * (MOE_MAX_TOPK + 1));
   g.lds = (int)o;
   if (g.lds < kStackMinLds) g.lds = kStackMinLds;   // keeps one workgroup per CU

@@ -28,6 +28,7 @@ STACK_CASES = [
     ("e128", dict(layers=3), wl.Q4_K, wl.Q4_K, 3),
     ("tiny", dict(layers=2, norm=True), wl.Q4_K, wl.Q4_K, 4),
     ("stack", dict(layers=2, E=16), wl.Q4_K, wl.Q4_K, 2),
+    ("tiny", dict(layers=2, norm=True, E=320, router_dup=1), wl.Q4_K, wl.Q4_K, 3),   # E > 256: per-wave picks
 ]
 
 
