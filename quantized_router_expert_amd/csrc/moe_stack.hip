@@ -190,8 +190,9 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
 // kernel), larger logit first and the lower expert id first among equal
 // logits, in three steps:
 //  1. waves 0..3 each take the experts e = 64w + lane + 256j and find their own
-//     k best by k wave-wide picks, as 64-bit candidates key << 32 | ~id
-//     (0 where a wave has fewer than k experts);
+//     k best (by ranking within the wave for E <= 256, else by k wave-wide
+//     picks), as 64-bit candidates key << 32 | ~id (0 where a wave has fewer
+//     than k experts);
 //  2. wave 0 ranks the 4k candidates against each other (all distinct), and
 //     the candidate of rank r < k is slot r; the selected logits (and the
 //     shared-gate logit) are copied out, as the logits' landing area is reused
@@ -199,8 +200,12 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
 //  3. later, off the critical path, wave 0 turns the copied logits into the
 //     softmax weights (fp64, shifted by the largest, summed in slot order) and
 //     the shared expert's sigmoid gate.
+// Candidate slots per wave: wave w's candidates sit at kc*w + 0..k-1 (the rest
+// of its kc slots hold 0), so 4*kc slots in all.
+__device__ __forceinline__ int cand_stride(int k) { return k <= 8 ? 8 : 16; }
+
 template <int NPL>
-__device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int w, unsigned long long* cand) {
+__device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int kc, int w, unsigned long long* cand) {
   const int lane = threadIdx.x & 63;
   uint32_t key[NPL];
 #pragma unroll
@@ -208,7 +213,7 @@ __device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int w, 
     const int e = 64 * w + lane + 256 * j;
     key[j] = (e < E) ? logit_key(lg[e]) : 0u;
   }
-  if (lane >= k && lane < 16) cand[16 * w + lane] = 0ull;   // slots past k never rank
+  if (lane >= k && lane < kc) cand[kc * w + lane] = 0ull;   // slots past k never rank
   for (int s = 0; s < k; ++s) {
     uint32_t hv = key[0], hid = (uint32_t)(64 * w + lane);
 #pragma unroll
@@ -228,57 +233,82 @@ __device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int w, 
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
         if ((uint32_t)(64 * w + lane + 256 * j) == id) key[j] = 0u;
-      cand[16 * w + s] = m ? (((unsigned long long)m << 32) | (uint32_t)~id) : 0ull;
+      cand[kc * w + s] = m ? (((unsigned long long)m << 32) | (uint32_t)~id) : 0ull;
     }
   }
 }
 
-// Count of the 64 keys at `k2` (32 pairs) that are above c.
+// Count of the 2*NP keys at `k2` (NP pairs) that are above c.  The loads go
+// out in batches of 8 pairs, each batch before the compares of the previous
+// one, and the count is kept in four separate sums (the empty asm stops the
+// compiler from folding them back into one chain of dependent adds, which
+// would cost a full VALU latency per key).
+template <int NP>
 __device__ __forceinline__ int count_above(const ulonglong2* k2, unsigned long long c) {
-  int rank = 0;
+  static_assert(NP % 8 == 0, "whole batches");
+  int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+  ulonglong2 v[8], nv[8];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const ulonglong2 v = k2[j];
-    rank += (v.x > c ? 1 : 0) + (v.y > c ? 1 : 0);
+  for (int j = 0; j < 8; ++j) v[j] = k2[j];
+#pragma unroll
+  for (int b = 0; b < NP; b += 8) {
+    if (b + 8 < NP) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) nv[j] = k2[b + 8 + j];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      a0 += (v[j].x > c) ? 1 : 0;
+      a1 += (v[j].y > c) ? 1 : 0;
+      a2 += (v[j + 1].x > c) ? 1 : 0;
+      a3 += (v[j + 1].y > c) ? 1 : 0;
+      asm("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = nv[j];
   }
-  return rank;
+  return (a0 + a1) + (a2 + a3);
 }
 
 // E <= 256: wave w ranks its 64 experts against each other in parallel
 // (one key per lane; 32 broadcast 16-byte LDS loads and 64 independent
 // compares per lane, no dependent chain); the lanes ranked below k are the
 // wave's candidates, already in order.  keys: 256 u64 of LDS.
-__device__ __forceinline__ void wave_rank_topk(const float* lg, int E, int k, int w, unsigned long long* keys,
-                                               unsigned long long* cand) {
+__device__ __forceinline__ void wave_rank_topk(const float* lg, int E, int k, int kc, int w,
+                                               unsigned long long* keys, unsigned long long* cand) {
   const int lane = threadIdx.x & 63;
   const int e = 64 * w + lane;
   const unsigned long long c = (e < E) ? (((unsigned long long)logit_key(lg[e]) << 32) | (uint32_t)~e) : 0ull;
   keys[e] = c;
-  if (lane < 16) cand[16 * w + lane] = 0ull;
+  if (lane < kc) cand[kc * w + lane] = 0ull;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  const int rank = count_above(reinterpret_cast<const ulonglong2*>(keys + 64 * w), c);
-  if (rank < k && c != 0ull) cand[16 * w + rank] = c;
+  const int rank = count_above<32>(reinterpret_cast<const ulonglong2*>(keys + 64 * w), c);
+  if (rank < k && c != 0ull) cand[kc * w + rank] = c;
 }
 
 __device__ __forceinline__ void topk_candidates(const float* lg, int E, int k, int wave, unsigned long long* keys,
                                                 unsigned long long* cand) {
   if (wave >= 4) return;
-  if (E <= 256) wave_rank_topk(lg, E, k, wave, keys, cand);
-  else if (E <= 512) wave_topk<2>(lg, E, k, wave, cand);
-  else wave_topk<4>(lg, E, k, wave, cand);
+  const int kc = cand_stride(k);
+  if (E <= 256) wave_rank_topk(lg, E, k, kc, wave, keys, cand);
+  else if (E <= 512) wave_topk<2>(lg, E, k, kc, wave, cand);
+  else wave_topk<4>(lg, E, k, kc, wave, cand);
 }
 
 // wave 0, after a barrier: slot ids -> sel[0..k), their logits -> lgsel[0..k),
-// the shared-gate logit -> lgsel[k].  Lane 16w + s holds candidate s of wave w
-// and counts the candidates above it; all 64 slots are read with unrolled
+// the shared-gate logit -> lgsel[k].  Lane kc*w + s holds candidate s of wave w
+// and counts the candidates above it over all 4*kc slots, read with unrolled
 // 16-byte loads (unused slots hold 0).  Returns true if an id is out of range.
 __device__ __forceinline__ bool rank_candidates(const float* lg, int E, int k, bool has_sg,
                                                 const unsigned long long* cand, uint32_t* sel, float* lgsel) {
   const int lane = threadIdx.x & 63;
-  const unsigned long long c = ((lane & 15) < k) ? cand[lane] : 0ull;
-  const int rank = count_above(reinterpret_cast<const ulonglong2*>(cand), c);
+  const int kc = cand_stride(k);
+  const unsigned long long c = (lane < 4 * kc && (lane & (kc - 1)) < k) ? cand[lane] : 0ull;
+  const int rank = (kc == 8) ? count_above<16>(reinterpret_cast<const ulonglong2*>(cand), c)
+                             : count_above<32>(reinterpret_cast<const ulonglong2*>(cand), c);
   if (c != 0ull && rank < k) {
     const uint32_t id = ~(uint32_t)c;
     sel[rank] = id;

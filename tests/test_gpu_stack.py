@@ -29,6 +29,8 @@ STACK_CASES = [
     ("tiny", dict(layers=2, norm=True), wl.Q4_K, wl.Q4_K, 4),
     ("stack", dict(layers=2, E=16), wl.Q4_K, wl.Q4_K, 2),
     ("tiny", dict(layers=2, norm=True, E=320, router_dup=1), wl.Q4_K, wl.Q4_K, 3),   # E > 256: per-wave picks
+    ("tiny", dict(layers=2, norm=True, k=12), wl.Q4_K, wl.Q4_K, 3),                   # k > 8: 16 slots per wave
+    ("tiny", dict(layers=2, norm=True, E=320, k=16, router_dup=1), wl.Q4_K, wl.Q4_K, 2),
 ]
 
 
