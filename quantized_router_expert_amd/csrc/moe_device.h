@@ -328,6 +328,136 @@ __device__ __forceinline__ void quantize_q81_blocks(int nblk, Src src, Dst codes
   }
 }
 
+// ---------------------------------------------------------------- Q8_1, four lanes per block
+// Fast forms of the quantiser's fp32 operations that give the same values as
+// the IEEE operations they replace, for the inputs they are used on:
+//  * amax/127 as q = RN(amax * RN(1/127)) corrected once with the exact
+//    remainder fma(-q, 127, amax): Markstein's correction step (P. Markstein,
+//    IBM J. Res. Dev. 34(1), 1990), correctly rounded because RN(1/127) is the
+//    correctly rounded reciprocal and q is within an ulp of the quotient;
+//  * 1/d as one Newton step y + y*(1 - d*y) from the hardware reciprocal y;
+//  * round-half-away-from-zero as an fp64 add of +-1/2 (exact: a 24-bit value
+//    plus 1/2 needs at most 26 bits) followed by truncation.
+// All three were compared with the IEEE operations over every fp32
+// significand (exponents -120..120 for the first two, every |v| <= 128 for the
+// rounding) with no difference.  Blocks whose maximum lies outside
+// [2^-100, 2^100] (so that no intermediate leaves the normal range) or that
+// hold a NaN take the IEEE operations instead; the choice is made per wave.
+__device__ __forceinline__ float div127_rn(float a) {
+  constexpr float y = 1.0f / 127.0f;
+  const float q = a * y;
+  const float r = __builtin_fmaf(-q, 127.0f, a);
+  return __builtin_fmaf(r, y, q);
+}
+__device__ __forceinline__ float recip_rn(float d) {
+  const float y = __builtin_amdgcn_rcpf(d);
+  return __builtin_fmaf(__builtin_fmaf(-d, y, 1.0f), y, y);
+}
+__device__ __forceinline__ int round_away_i32(float v) {
+  const double w = (double)v;
+  return (int)(w + __builtin_copysign(0.5, w));
+}
+__device__ __forceinline__ uint32_t pack_i8x4(int q0, int q1, int q2, int q3) {
+  return ((uint32_t)q0 & 0xffu) | (((uint32_t)q1 & 0xffu) << 8) | (((uint32_t)q2 & 0xffu) << 16) |
+         ((uint32_t)q3 << 24);
+}
+
+// One block spread over LPB consecutive lanes (2 or 4), V = 32/LPB values
+// each (x = elements V*p .. V*p+V-1 of the block, p = lane % LPB); amax = the
+// block's max |x| (already reduced over the LPB lanes).  IEEE selects the
+// plain IEEE operations.  Same bytes as quantize_q81_lane either way.  w gets
+// the lane's V codes (little-endian, V/4 dwords); returns d16 | s16 << 16
+// (same in the LPB lanes of the block).
+template <int LPB, bool IEEE>
+__device__ __forceinline__ uint32_t q81_group(const float* x, float amax, uint32_t* w) {
+  constexpr int V = 32 / LPB;
+  const bool zero = (amax == 0.0f);
+  const float a = zero ? 1.0f : amax;   // stand-in scale for an all-zero block
+  const float d32 = IEEE ? a / 127.0f : div127_rn(a);
+  const float id = IEEE ? 1.0f / d32 : recip_rn(d32);
+  int qsum = 0;
+#pragma unroll
+  for (int c = 0; c < V / 4; ++c) {
+    int q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float t = __fmul_rn(x[4 * c + i], id);
+      // |t| <= 127(1 + 2^-22) when the fast operations apply: no clamp needed
+      q[i] = IEEE ? (int)fminf(fmaxf(roundf(t), -127.0f), 127.0f) : round_away_i32(t);
+    }
+    w[c] = zero ? 0u : pack_i8x4(q[0], q[1], q[2], q[3]);
+    qsum = __builtin_amdgcn_sdot4((int)w[c], 0x01010101, qsum, false);
+  }
+  qsum += (int)partner_dpp<0>((uint32_t)qsum);
+  if (LPB >= 4) qsum += (int)partner_dpp<1>((uint32_t)qsum);
+  const uint32_t d16 = f32_to_f16(d32);
+  const float sv = __fmul_rn(f16_to_f32(d16), (float)qsum);
+  return zero ? 0u : (d16 | (f32_to_f16(sv) << 16));
+}
+
+// Quantise nblk blocks with threads [tid, ...) stepping by nthr (a multiple of
+// 64), LPB lanes per block (2 or 4) and up to U blocks in flight per lane.
+// Block j's 32 fp32 values are at base + off(j) (LDS, 16-byte aligned;
+// off(j) < 0 = a zero block); its codes go to codes(j) (16-byte aligned), d
+// and s to dq[j] and sq[j].
+template <int LPB, int U, class Off, class Dst>
+__device__ __forceinline__ void quantize_q81_groups(int nblk, const float* base, Off off, Dst codes, float* dq,
+                                                    float* sq, int tid, int nthr) {
+  constexpr int V = 32 / LPB;
+  const int n = LPB * nblk;
+  for (int i0 = tid; i0 < n; i0 += U * nthr) {
+    float x[U][V], amax[U];
+    bool live[U];
+    bool slow = false;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * nthr;
+      live[u] = i < n;   // the same for the LPB lanes of a block
+      const int o = live[u] ? off(i / LPB) : -1;
+      const float4* p = reinterpret_cast<const float4*>(base + (o < 0 ? 0 : o) + V * (i % LPB));
+      float m = 0.0f;
+      bool nan = false;
+#pragma unroll
+      for (int c = 0; c < V / 4; ++c) {
+        const float4 v = p[c];
+        const float xs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[u][4 * c + e] = (o < 0) ? 0.0f : xs[e];
+          m = fmaxf(m, fabsf(x[u][4 * c + e]));
+          nan |= (x[u][4 * c + e] != x[u][4 * c + e]);
+        }
+      }
+      m = fmaxf(m, __uint_as_float(partner_dpp<0>(__float_as_uint(m))));
+      if (LPB >= 4) m = fmaxf(m, __uint_as_float(partner_dpp<1>(__float_as_uint(m))));
+      amax[u] = m;
+      slow |= nan || !(m == 0.0f || (m >= 0x1p-100f && m <= 0x1p100f));
+    }
+    uint32_t w[U][V / 4], ds[U];
+    if (__builtin_expect(__any(slow), 0)) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) ds[u] = q81_group<LPB, true>(x[u], amax[u], w[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) ds[u] = q81_group<LPB, false>(x[u], amax[u], w[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * nthr;
+      if (live[u]) {
+        const int j = i / LPB, p = i % LPB;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(codes(j)) + (V / 4) * p;
+        if (V == 16) *reinterpret_cast<uint4*>(dst) = make_uint4(w[u][0], w[u][1], w[u][2], w[u][3]);
+        else *reinterpret_cast<uint2*>(dst) = make_uint2(w[u][0], w[u][1]);
+        if (p == 0) {
+          dq[j] = f16_to_f32(ds[u]);
+          sq[j] = f16_to_f32(ds[u] >> 16);
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- K-quant scales
 // 6-bit scale and min of sub-block j from the 12 scale bytes held as three
 // dwords s0 (bytes 0..3), s1 (4..7), s2 (8..11).

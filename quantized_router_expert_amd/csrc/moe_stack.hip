@@ -526,8 +526,8 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     for (int i = tid; i < H; i += kStackThreads) xn[i] = (float)(((double)res[i] * rinv) * (double)nw[i]);
     lds_barrier();
     bstamp(l, 11);
-    quantize_q81_blocks<1>(H / 32, [&](int j) { return (const float*)(xn + 32 * j); },
-                           [&](int j) { return xqc + 32 * j; }, xqd, xqs, tid, kStackThreads);
+    quantize_q81_groups<4, 1>(H / 32, xn, [](int j) { return 32 * j; }, [&](int j) { return xqc + 32 * j; }, xqd,
+                              xqs, tid, kStackThreads);
     lds_barrier();
     bstamp(l, 12);
     // router rows (fp64 dot of fp32 products), one wave per row
@@ -646,6 +646,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     bstamp(l, 7);
     {
       const int nb_r = g.Kp / 32, nb_s = g.Kps / 32;
+      const float inv_nbr = 1.0f / (float)nb_r;
       // the down rows waves 4..7 requested in phase B have had the whole of
       // phase B to land, so every wave polls
       const bool ok = poll_ll<kAuxSC1>(r_h, g.n_h, ep1, xbuf, kStackWaves);
@@ -653,18 +654,22 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       lds_barrier();
       if (s_fail) { fail_out(); return; }
       bstamp(l, 14);
-      // block jb of slot s covers h[s*F + 32jb ..]; blocks past F (or Fs) are the zero padding
+      // block j < k*nb_r is block jb = j % nb_r of slot s = j / nb_r and covers
+      // h[s*F + 32jb ..]; block k*nb_r + jb covers the shared h[k*F + 32jb ..];
+      // blocks past F (or Fs) are the zero padding.  s comes from a float
+      // product: (j + 1/2)/nb_r lies at least 1/(2 nb_r) from an integer and
+      // the product is within 2^-23 relative of it, so truncation is exact
+      // for j < 2^22.
       const float* hf = reinterpret_cast<const float*>(xbuf);
-      quantize_q81_blocks<3>(k * nb_r + nb_s,
-                          [&](int j) -> const float* {
-                            if (j < k * nb_r) {
-                              const int s = j / nb_r, jb = j - s * nb_r;
-                              return (jb * 32 < F) ? hf + s * F + 32 * jb : nullptr;
-                            }
-                            const int jb = j - k * nb_r;
-                            return (jb * 32 < Fs) ? hf + k * F + 32 * jb : nullptr;
-                          },
-                          [&](int j) { return hqc + 32 * j; }, hqd, hqs, tid, kStackThreads);
+      quantize_q81_groups<4, 1>(k * nb_r + nb_s, hf,
+                                [&](int j) -> int {
+                                  const int s = (int)(((float)j + 0.5f) * inv_nbr);
+                                  const int jb = j - s * nb_r, jr = j - k * nb_r;
+                                  const int o_r = (32 * jb < F) ? s * F + 32 * jb : -1;
+                                  const int o_s = (32 * jr < Fs) ? k * F + 32 * jr : -1;
+                                  return (s < k) ? o_r : o_s;
+                                },
+                                [&](int j) { return hqc + 32 * j; }, hqd, hqs, tid, kStackThreads);
     }
     // ================= phase C: down rows of all slots + shared, combine
     stamp(l, 7);
