@@ -307,6 +307,19 @@ size_t moe_stack_trace_offset(const moe_layer_desc* desc, int n_layers);
 int moe_test_subblock_dots(const void* rows, int type, int K, int n_rows, const void* xq,
                            int32_t* out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Test export: the persistent kernel's Q8_1 quantiser ([P359] Summary: the
+ * activations and the gate/up product are quantised to Q8_1 blocks of 32
+ * before the int8 dots), run over n/32 independent blocks.  Same definition
+ * as in add_rmsnorm3: d = amax/127, codes rounded half away from zero, d and
+ * s = d*sum(q) as fp16, an all-zero block all zero.  The codes of a block
+ * holding a NaN or an infinity, or whose d or 1/d leaves the fp32 range,
+ * are unspecified.
+ * x [n] fp32 (16-byte aligned), n a multiple of 32 up to 2^26; xq [n/32]
+ * Q8_1 blocks of 36 bytes (d, s, 32 codes).  All device.
+ * ---------------------------------------------------------------------- */
+int moe_test_quantize_q81(const float* x, int n, void* xq, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -81,10 +81,11 @@ _moe_decode_layer_batch = _sig("moe_decode_layer_batch", C.c_int, C.POINTER(Laye
 _moe_stack_status_offset = _sig("moe_stack_status_offset", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
 _moe_stack_trace_offset = _sig("moe_stack_trace_offset", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
 _moe_test_subblock_dots = _sig("moe_test_subblock_dots", C.c_int, P, C.c_int, C.c_int, C.c_int, P, P, P)
+_moe_test_quantize_q81 = _sig("moe_test_quantize_q81", C.c_int, P, C.c_int, P, P)
 
 EXPORTS = ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", "moe_stack_bind",
            "moe_decode_stack", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
-           "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots",
+           "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots", "moe_test_quantize_q81",
            "moe_batch_workspace_size", "expert_ffn_grouped", "moe_decode_layer_batch")
 MAX_BATCH = 64
 MAX_GROUP_MIN = 16
@@ -302,6 +303,10 @@ def stack_block_trace(desc, n_layers, ws):
 def layer_array(layers):
     """Pre-marshalled host array of layer weight pointers (reuse across calls)."""
     return _layer_array(layers)
+
+
+def moe_test_quantize_q81(x, n, xq, stream=None):
+    return _check("moe_test_quantize_q81", _moe_test_quantize_q81(ptr(x), n, ptr(xq), stream_handle(stream)))
 
 
 def moe_test_subblock_dots(rows, typ, K, n_rows, xq, out, stream=None):

@@ -348,4 +348,11 @@ int moe_test_subblock_dots(const void* rows, int type, int K, int n_rows, const 
   return launch_subblock_dots(rows, type, K, n_rows, xq, out, as_stream(stream));
 }
 
+int moe_test_quantize_q81(const float* x, int n, void* xq, void* stream) {
+  if (!x || !xq) return MOE_ERR_NULL;
+  if (n <= 0 || n % 32 || n > (1 << 26)) return MOE_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(xq, 2)) return MOE_ERR_ALIGN;
+  return launch_test_q81_groups(x, n, xq, as_stream(stream));
+}
+
 }  // extern "C"

@@ -192,6 +192,15 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 // One 32-element block held by 32 consecutive lanes (one value per lane).
 // d32 = amax/127 and the codes x*(1/d32) are fp32 and correctly rounded (a
 // float decides an integer here, so the precision is fixed, not widened);
+// s = d16 * qsum in fp32 (exact: 11-bit d16 times |qsum| <= 4064), then fp16.
+// The empty asm keeps the product a separate fp32 multiply: fused with the
+// conversion into one mixed-precision fma with a +0 addend, a -0 product
+// (d16 = 0, qsum < 0) would come out +0.
+__device__ __forceinline__ uint32_t q81_s16(uint32_t d16, int qsum) {
+  float sv = __fmul_rn(f16_to_f32(d16), (float)qsum);
+  asm("" : "+v"(sv));
+  return f32_to_f16(sv);
+}
 // codes round half away from zero; d and s = d16*sum(q) are stored as fp16.
 struct Q81Lane {
   int q;            // this lane's code
@@ -208,8 +217,7 @@ __device__ __forceinline__ Q81Lane quantize_q81_lane(float x) {
   r.q = (int)qf;
   int qsum = half_wave_sum_i32(r.q);
   uint32_t d16 = f32_to_f16(d32);
-  float s = __fmul_rn(f16_to_f32(d16), (float)qsum);  // exact: 11-bit d16 times |qsum| <= 4064
-  r.ds = d16 | (f32_to_f16(s) << 16);
+  r.ds = d16 | (q81_s16(d16, qsum) << 16);
   return r;
 }
 
@@ -252,8 +260,7 @@ __device__ __forceinline__ uint32_t quantize_q81_block(const float* src, uint8_t
   d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
   d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
   const uint32_t d16 = f32_to_f16(d32);
-  const float sv = __fmul_rn(f16_to_f32(d16), (float)qsum);
-  return d16 | (f32_to_f16(sv) << 16);
+  return d16 | (q81_s16(d16, qsum) << 16);
 }
 
 // The same quantiser spread over 8 consecutive lanes per block, 4 values per
@@ -286,8 +293,7 @@ __device__ __forceinline__ uint32_t quantize_q81_oct(float4 x4, uint32_t& ds) {
   qsum += (int)partner_dpp<1>((uint32_t)qsum);
   qsum += (int)partner_dpp<2>((uint32_t)qsum);
   const uint32_t d16 = f32_to_f16(d32);
-  const float sv = __fmul_rn(f16_to_f32(d16), (float)qsum);
-  ds = zero ? 0u : (d16 | (f32_to_f16(sv) << 16));
+  ds = zero ? 0u : (d16 | (q81_s16(d16, qsum) << 16));
   return zero ? 0u : pk;
 }
 
@@ -391,8 +397,7 @@ __device__ __forceinline__ uint32_t q81_group(const float* x, float amax, uint32
   qsum += (int)partner_dpp<0>((uint32_t)qsum);
   if (LPB >= 4) qsum += (int)partner_dpp<1>((uint32_t)qsum);
   const uint32_t d16 = f32_to_f16(d32);
-  const float sv = __fmul_rn(f16_to_f32(d16), (float)qsum);
-  return zero ? 0u : (d16 | (f32_to_f16(sv) << 16));
+  return zero ? 0u : (d16 | (q81_s16(d16, qsum) << 16));
 }
 
 // Quantise nblk blocks with threads [tid, ...) stepping by nthr (a multiple of

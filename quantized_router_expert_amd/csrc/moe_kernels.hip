@@ -458,6 +458,30 @@ __global__ __launch_bounds__(kFfnThreads) void k_subblock_dots(const uint8_t* ro
   else subblock_dots_row<MOE_TYPE_Q8_0>(stage, K, act, o);
 }
 
+// The persistent kernel's Q8_1 quantiser (four lanes per block, exact fast
+// operations with a per-wave IEEE fallback) over n/32 blocks: 128 blocks per
+// workgroup of 512 threads, staged through LDS as in the persistent kernel.
+constexpr int kQ81TestThreads = 512, kQ81TestBlocks = 128;
+__global__ __launch_bounds__(kQ81TestThreads) void k_test_q81_groups(const float* x, int nblk, uint8_t* xq) {
+  __shared__ __attribute__((aligned(16))) float vals[32 * kQ81TestBlocks];
+  __shared__ __attribute__((aligned(16))) uint8_t codes[32 * kQ81TestBlocks];
+  __shared__ float dq[kQ81TestBlocks], sq[kQ81TestBlocks];
+  const int b0 = blockIdx.x * kQ81TestBlocks;
+  const int nb = min(kQ81TestBlocks, nblk - b0);
+  for (int i = threadIdx.x; i < 32 * nb; i += kQ81TestThreads) vals[i] = x[(long)32 * b0 + i];
+  __syncthreads();
+  quantize_q81_groups<4, 1>(nb, vals, [](int j) { return 32 * j; }, [&](int j) { return codes + 32 * j; }, dq, sq,
+                            (int)threadIdx.x, kQ81TestThreads);
+  __syncthreads();
+  for (int j = threadIdx.x; j < nb; j += kQ81TestThreads) {
+    uint8_t* o = xq + (long)(b0 + j) * 36;
+    const uint32_t ds = f32_to_f16(dq[j]) | (f32_to_f16(sq[j]) << 16);
+    reinterpret_cast<uint16_t*>(o)[0] = (uint16_t)ds;
+    reinterpret_cast<uint16_t*>(o)[1] = (uint16_t)(ds >> 16);
+    for (int i = 0; i < 32; i += 2) reinterpret_cast<uint16_t*>(o + 4)[i / 2] = reinterpret_cast<const uint16_t*>(codes + 32 * j)[i / 2];
+  }
+}
+
 __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -655,6 +679,13 @@ int launch_fill(void* p, size_t n_u32, uint32_t v, hipStream_t st) {
   int blocks = (int)((n_u32 + 255) / 256);
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(256), 0, st, (uint32_t*)p, n_u32, v);
+  return launch_ok();
+}
+
+int launch_test_q81_groups(const float* x, int n, void* xq, hipStream_t st) {
+  const int nblk = n / 32;
+  hipLaunchKernelGGL(k_test_q81_groups, dim3((nblk + kQ81TestBlocks - 1) / kQ81TestBlocks), dim3(kQ81TestThreads), 0,
+                     st, x, nblk, (uint8_t*)xq);
   return launch_ok();
 }
 

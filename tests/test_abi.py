@@ -22,7 +22,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", "moe_decode_stack",
               "moe_stack_bind", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
-              "moe_test_subblock_dots"):
+              "moe_test_subblock_dots", "moe_test_quantize_q81"):
         assert n in names, n
 
 
@@ -150,6 +150,9 @@ def test_layer_and_stack_validation(q):
     assert q._moe_stack_bind(C.byref(d), arr, 2, FAKE, 1024, None) == -5
     assert q._moe_test_subblock_dots(FAKE, 9, 256, 1, FAKE, FAKE, None) == -3
     assert q._moe_test_subblock_dots(FAKE, 12, 100, 1, FAKE, FAKE, None) == -2
+    assert q._moe_test_quantize_q81(None, 32, FAKE, None) == -1
+    assert q._moe_test_quantize_q81(FAKE, 48, FAKE, None) == -2
+    assert q._moe_test_quantize_q81(FAKE + 4, 32, FAKE, None) == -4
     assert q._moe_workspace_init(None, 1024, None) == -5
     assert q._moe_workspace_init(FAKE + 8, 1024, None) == -4
 

@@ -47,11 +47,47 @@ def test_subblock_dots_bit_exact(q, orc, typ, K):
         assert np.array_equal(got[r], orc.subblock_dots(rows[r], typ, K, xq)), r
 
 
+# ------------------------------------------------------------------ Q8_1 quantiser of the persistent kernel
+@pytest.mark.parametrize("nblk,mix", [(1000, "normal"), (1000, "mixed"), (131, "mixed"), (4096, "wide")])
+def test_quantize_q81_four_lane_bit_exact(q, orc, nblk, mix):
+    """The four-lane quantiser's fast operations (and its per-wave IEEE fallback
+    for out-of-range maxima) give the oracle's bytes: block scales from 2^-112
+    to 2^124, all-zero and one-value blocks, signed zeros."""
+    gu.banner(f"four-lane Q8_1 quantiser {nblk} blocks, {mix}")
+    rng = np.random.default_rng(nblk * 7 + len(mix))
+    x = rng.standard_normal((nblk, 32)).astype(np.float64)
+    if mix == "normal":
+        e = rng.integers(-20, 21, nblk)
+    elif mix == "mixed":
+        e = rng.integers(-20, 21, nblk)
+        far = rng.random(nblk) < 0.02            # a few blocks per wave force the fallback
+        e[far] = rng.choice(np.r_[np.arange(-112, -100), np.arange(101, 125)], far.sum())
+    else:
+        e = rng.integers(-112, 125, nblk)
+    x *= np.exp2(e)[:, None]
+    kind = rng.integers(0, 12, nblk)
+    x[kind == 0] = 0.0
+    x[kind == 1] = -0.0
+    x[kind == 2, 1:] = 0.0                       # a single nonzero value
+    x = x.astype(np.float32).ravel()
+    ref = orc.quantize_q8_1(x)
+    out = torch.zeros(nblk * 36, dtype=torch.uint8, device="cuda")
+    q.moe_test_quantize_q81(gu.dev(x), x.size, out)
+    _sync()
+    got = gu.host(out)
+    bad = np.nonzero((got.reshape(nblk, 36) != ref.reshape(nblk, 36)).any(1))[0]
+    assert bad.size == 0, f"{bad.size} blocks differ, first {bad[:5]}"
+
+
 # ------------------------------------------------------------------ a1: add_rmsnorm3
 @pytest.mark.parametrize("H,n_tok,form", [(2048, 1, 3), (2048, 5, 3), (2048, 3, 2), (2048, 2, 1), (512, 7, 3),
-                                          (8192, 2, 3), (256, 3, 2)])
+                                          (8192, 2, 3), (256, 3, 2), (2048, 4, 4)])
 def test_add_rmsnorm3(q, orc, H, n_tok, form):
+    """form 4 = form 3 with norm weights near 1e-6: Q8_1 scales below the fp16
+    range (d = 0, and s = -0 for a negative code sum)."""
     gu.banner(f"add_rmsnorm3 H {H} n_tok {n_tok} form {form}")
+    tiny = form == 4
+    form = 3 if tiny else form
     rng = np.random.default_rng(H * 10 + n_tok + form)
     bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
     res = bf(rng.standard_normal((n_tok, H)))
@@ -63,7 +99,7 @@ def test_add_rmsnorm3(q, orc, H, n_tok, form):
             rt[1] = 0.0
         if sh is not None:
             sh[1] = 0.0
-    w = torch.from_numpy(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    w = torch.from_numpy(rng.uniform(0.5, 1.5, H).astype(np.float32) * (1e-6 if tiny else 1.0))
     out = torch.zeros(n_tok, H, dtype=torch.bfloat16, device="cuda")
     xn = torch.zeros(n_tok, H, dtype=torch.float32, device="cuda")
     xq = torch.zeros(n_tok, H // 32 * 36, dtype=torch.uint8, device="cuda")
