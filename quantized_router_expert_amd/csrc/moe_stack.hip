@@ -165,7 +165,9 @@ __device__ __forceinline__ double sum_row(const double* p, int T) {
   return a;
 }
 
-// block-wide fp64 sum (all threads get the result); red needs kStackThreads/64 doubles
+// block-wide fp64 sum (all threads get the result); red needs kStackThreads/64
+// doubles.  The caller keeps red unwritten until a later barrier (every wave
+// reads it after this returns).
 __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   v = wave_sum_f64(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
@@ -173,8 +175,11 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   double t = 0.0;
 #pragma unroll
   for (int w = 0; w < kStackThreads / 64; ++w) t += red[w];
-  lds_barrier();
   return t;
+}
+
+__device__ __forceinline__ double sq4_f64(float4 r) {
+  return ((double)r.x * (double)r.x + (double)r.y * (double)r.y) + ((double)r.z * (double)r.z + (double)r.w * (double)r.w);
 }
 
 // Order-preserving 32-bit key of a logit (a larger float gives a larger key);
@@ -499,16 +504,27 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     stamp(l, 0);
     bstamp(l, 0);
     // ================= R1: t of the previous layer, read by every workgroup
+    // (four elements per thread: t as two words of bf16 pairs); the sum of
+    // squares of the new residual is taken on the way
+    double ss = 0.0;
+    float4* res4 = reinterpret_cast<float4*>(res);
     if (l > 0) {
       const bool ok = poll_ll<kAuxSC1>(r_t, g.n_t, ep2 - 3u, xbuf, kPollWaves);
       if (!ok) s_fail = 1;
       lds_barrier();
       if (s_fail) { fail_out(); return; }
-      for (int i = tid; i < H; i += kStackThreads) {
-        const uint32_t pr = xbuf[i >> 1];
-        const float t = bf16_to_f32((uint16_t)((i & 1) ? (pr >> 16) : (pr & 0xffffu)));
-        res[i] = bf16_to_f32(f32_to_bf16(res[i] + t));
+      for (int c = tid; c < H / 4; c += kStackThreads) {
+        const uint2 pr = reinterpret_cast<const uint2*>(xbuf)[c];
+        float4 r = res4[c];
+        r.x = bf16_to_f32(f32_to_bf16(r.x + bf16_to_f32((uint16_t)(pr.x & 0xffffu))));
+        r.y = bf16_to_f32(f32_to_bf16(r.y + bf16_to_f32((uint16_t)(pr.x >> 16))));
+        r.z = bf16_to_f32(f32_to_bf16(r.z + bf16_to_f32((uint16_t)(pr.y & 0xffffu))));
+        r.w = bf16_to_f32(f32_to_bf16(r.w + bf16_to_f32((uint16_t)(pr.y >> 16))));
+        res4[c] = r;
+        ss += sq4_f64(r);
       }
+    } else {
+      for (int c = tid; c < H / 4; c += kStackThreads) ss += sq4_f64(res4[c]);
     }
     // ================= phase A: norm, router rows, shared gate/up rows
     stamp(l, 1);
@@ -519,11 +535,18 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     bstamp(l, 2);
     if (b == 0 && a.resid_out)
       for (int i = tid; i < H; i += kStackThreads) a.resid_out[(long)l * H + i] = f32_to_bf16(res[i]);
-    double ss = 0.0;
-    for (int i = tid; i < H; i += kStackThreads) ss += (double)res[i] * (double)res[i];
     ss = block_sum_f64(ss, red);
     const double rinv = 1.0 / sqrt(ss / (double)H + (double)a.eps);
-    for (int i = tid; i < H; i += kStackThreads) xn[i] = (float)(((double)res[i] * rinv) * (double)nw[i]);
+    for (int c = tid; c < H / 4; c += kStackThreads) {
+      const float4 r = res4[c];
+      const float4 wv = reinterpret_cast<const float4*>(nw)[c];
+      float4 o;
+      o.x = (float)(((double)r.x * rinv) * (double)wv.x);
+      o.y = (float)(((double)r.y * rinv) * (double)wv.y);
+      o.z = (float)(((double)r.z * rinv) * (double)wv.z);
+      o.w = (float)(((double)r.w * rinv) * (double)wv.w);
+      reinterpret_cast<float4*>(xn)[c] = o;
+    }
     lds_barrier();
     bstamp(l, 11);
     quantize_q81_groups<4, 1>(H / 32, xn, [](int j) { return 32 * j; }, [&](int j) { return xqc + 32 * j; }, xqd,
