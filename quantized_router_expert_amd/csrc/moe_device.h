@@ -33,20 +33,19 @@ constexpr int kQ5KBytes = 176;
 constexpr int kQ80Bytes = 34;
 constexpr int kQ81Bytes = 36;
 
-__host__ __device__ inline int block_bytes(int type) {
+__host__ __device__ constexpr inline int block_bytes(int type) {
   return type == MOE_TYPE_Q4_K ? kQ4KBytes : type == MOE_TYPE_Q5_K ? kQ5KBytes : type == MOE_TYPE_Q8_0 ? kQ80Bytes : kQ81Bytes;
 }
-__host__ __device__ inline int block_elems(int type) {
+__host__ __device__ constexpr inline int block_elems(int type) {
   return (type == MOE_TYPE_Q4_K || type == MOE_TYPE_Q5_K) ? 256 : 32;
 }
-__host__ __device__ inline int pad_k(int type, int K) {
-  int b = block_elems(type);
-  return (K + b - 1) / b * b;
+__host__ __device__ constexpr inline int pad_k(int type, int K) {
+  return (K + block_elems(type) - 1) / block_elems(type) * block_elems(type);
 }
-__host__ __device__ inline long row_bytes(int type, int K) { return (long)(K / block_elems(type)) * block_bytes(type); }
+__host__ __device__ constexpr inline long row_bytes(int type, int K) { return (long)(K / block_elems(type)) * block_bytes(type); }
 // Independent work items ("tasks") per row: one per 64 elements for K-quants
 // (a 32-byte group of qs = two sub-blocks), one per 32-element block for Q8_0.
-__host__ __device__ inline int tasks_per_row(int type, int K) {
+__host__ __device__ constexpr inline int tasks_per_row(int type, int K) {
   return (type == MOE_TYPE_Q8_0) ? K / 32 : K / 64;
 }
 

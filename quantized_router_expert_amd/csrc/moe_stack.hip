@@ -23,6 +23,9 @@
 // that republished into its L2 measured slower: the extra hop costs more than
 // the contention it saves).  Every wait is bounded: a spin limit sets an
 // error word and the grid exits.
+#include <cstddef>
+#include <cstring>
+
 #include "../../include/moe_decode.h"
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -387,13 +390,102 @@ __device__ __forceinline__ LayerPtrs load_layer(const moe_layer_weights* table, 
   return p;
 }
 
+// Per-workgroup shares, LDS layout and exchange sizes of the persistent
+// kernel for G workgroups (constexpr: also evaluated at compile time for the
+// shape the kernel is specialised for).  The workspace offsets w_* are set by
+// stack_ws_layout.
+constexpr int up1k(long x) { return (int)((x + 1023) & ~1023L); }
+constexpr int up16(long x) { return (int)((x + 15) & ~15L); }
+
+constexpr int stack_geometry_core(int H, int E, int k, int F, int Fs, int down_type, int st, int G, StackGeom* out) {
+  StackGeom g = {};
+  const bool has_sg = Fs > 0;
+  g.G = G;
+  g.Kp = pad_k(down_type, F);
+  g.Kps = has_sg ? pad_k(st, Fs) : 0;
+  g.RR = (E + (has_sg ? 1 : 0) + G - 1) / G;
+  g.SR = has_sg ? (Fs + G - 1) / G : 0;
+  g.RD = (H + G - 1) / G;
+  if (g.RD & 1) g.RD += 1;                    // t travels in bf16 pairs
+  g.RP = (k * F + G - 1) / G;
+  while (F % g.RP) g.RP++;
+  if ((long)g.RP * G < (long)k * F) return MOE_ERR_UNSUPPORTED;
+  const long rb_gu = row_bytes(MOE_TYPE_Q4_K, H);
+  const long rb_sgu = has_sg ? row_bytes(st, H) : 0;
+  const long rb_dn = row_bytes(down_type, g.Kp);
+  const long rb_sdn = has_sg ? row_bytes(st, g.Kps) : 0;
+  g.n_t = H / 2;
+  g.n_lg = E + (has_sg ? 1 : 0);
+  g.n_h = k * F + Fs;
+  g.n_sel = 2 * k + 1;
+  const int nblk = k * (g.Kp / 32) + g.Kps / 32;
+  // LDS
+  long o = 0;
+  auto take = [&](long bytes) { long r = o; o += up16(bytes); return (int)r; };
+  g.o_res = take(4L * H);
+  g.o_xn = take(4L * H);
+  g.o_xqc = take(H);
+  g.o_xqd = take(4L * (H / 32));
+  g.o_xqs = take(4L * (H / 32));
+  g.o_nw = take(up1k(4L * H));
+  g.o_rrow = take((long)g.RR * up1k(4L * H));
+  g.sgu_half = up1k(g.SR * rb_sgu);
+  g.o_sgu = take(2L * g.sgu_half);
+  g.o_sdn = take(up1k(g.RD * rb_sdn));
+  g.rgu_half = up1k(g.RP * rb_gu);
+  g.o_rgu = take(2L * g.rgu_half);
+  g.rdn_slot = up1k(g.RD * rb_dn);
+  g.o_rdn = take((long)k * g.rdn_slot);
+  g.o_hqc = take((long)k * g.Kp + g.Kps);
+  g.o_hqd = take(4L * nblk);
+  g.o_hqs = take(4L * nblk);
+  long np = 2L * g.RP;                               // fp64 row values of one phase
+  np = np > 2L * g.SR ? np : 2L * g.SR;
+  np = np > (long)(k + 1) * g.RD ? np : (long)(k + 1) * g.RD;
+  g.o_part = take(8L * np);
+  long xb = g.n_h;                                   // words landing from an exchange
+  xb = xb > g.n_t ? xb : g.n_t;
+  xb = xb > g.n_lg ? xb : g.n_lg;
+  // the exchange landing area is only written while the routed gate/up rows are
+  // not in use (before they are staged, after they are consumed): share it
+  if (4L * (xb + 2) <= 2L * g.rgu_half) g.o_xbuf = g.o_rgu;
+  else g.o_xbuf = take(4L * (xb + 2));
+  g.o_sel = take(4L * (g.n_sel + 1));
+  g.o_red = take(8L * (kStackThreads / 64));
+  g.o_y = take(4L * (k + 1) * g.RD);
+  g.o_cand = take(8L * 64);
+  g.o_keys = take(8L * 256);
+  g.o_lgsel = take(4L * (MOE_MAX_TOPK + 1));
+  g.lds = (int)o;
+  if (g.lds < kStackMinLds) g.lds = kStackMinLds;   // keeps one workgroup per CU
+  // workspace (exchange buffers after the per-layer region)
+  out[0] = g;
+  return MOE_OK;
+}
+
+// The shape the kernel is also compiled for with every size a constant
+// (hidden 2048, 256 experts, top-8, expert and shared FFN 512, Q4_K
+// throughout, 256 workgroups): loop bounds, LDS offsets and quotients fold
+// into the code, and the scalar registers that would hold them stay free.
+constexpr int kFixH = 2048, kFixE = 256, kFixK = 8, kFixF = 512, kFixFs = 512, kFixG = 256;
+constexpr StackGeom fixed_geom() {
+  StackGeom g = {};
+  stack_geometry_core(kFixH, kFixE, kFixK, kFixF, kFixFs, MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, kFixG, &g);
+  return g;
+}
+constexpr StackGeom kFixGeom = fixed_geom();
+
 // ---------------------------------------------------------------- the kernel
-template <int DT, int ST>
+template <int DT, int ST, bool FIX>
 __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const StackGeom& g = a.g;
+  // FIX: the geometry and sizes are the compile-time ones (the launch checks
+  // that they equal the runtime ones); the workspace offsets always come from
+  // the arguments
+  const StackGeom g = FIX ? kFixGeom : a.g;
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
-  const int H = a.H, E = a.E, k = a.k, F = a.F, Fs = a.Fs;
+  const int H = FIX ? kFixH : a.H, E = FIX ? kFixE : a.E, k = FIX ? kFixK : a.k, F = FIX ? kFixF : a.F,
+            Fs = FIX ? kFixFs : a.Fs;
   const bool has_sg = Fs > 0;
 
   float* res = reinterpret_cast<float*>(smem + g.o_res);
@@ -428,13 +520,13 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     if (!ok) {
       if (b == 0) {
         for (int i = tid; i < H; i += kStackThreads) a.output[i] = 0x7fc0u;
-        if (tid == 0) __hip_atomic_store(reinterpret_cast<uint32_t*>(a.ws + g.w_ctrl) + kErrWord, 2u, __ATOMIC_RELAXED,
+        if (tid == 0) __hip_atomic_store(reinterpret_cast<uint32_t*>(a.ws + a.g.w_ctrl) + kErrWord, 2u, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
       }
       return;
     }
   }
-  uint32_t* ctrl = reinterpret_cast<uint32_t*>(a.ws + g.w_ctrl);
+  uint32_t* ctrl = reinterpret_cast<uint32_t*>(a.ws + a.g.w_ctrl);
   const __amdgpu_buffer_rsrc_t r_ctrl = make_rsrc(ctrl, kStackCtrlBytes);
   if (tid == 0) {
     s_fail = 0;
@@ -444,9 +536,9 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   lds_barrier();
   const uint32_t base = s_gen * (uint32_t)(3 * a.L + 2) + 1u;
 
-  const __amdgpu_buffer_rsrc_t r_t = make_rsrc(a.ws + g.w_t, (uint32_t)g.n_t * 8);
-  const __amdgpu_buffer_rsrc_t r_lg = make_rsrc(a.ws + g.w_lg, (uint32_t)g.n_lg * 8);
-  const __amdgpu_buffer_rsrc_t r_h = make_rsrc(a.ws + g.w_h, (uint32_t)g.n_h * 8);
+  const __amdgpu_buffer_rsrc_t r_t = make_rsrc(a.ws + a.g.w_t, (uint32_t)g.n_t * 8);
+  const __amdgpu_buffer_rsrc_t r_lg = make_rsrc(a.ws + a.g.w_lg, (uint32_t)g.n_lg * 8);
+  const __amdgpu_buffer_rsrc_t r_h = make_rsrc(a.ws + a.g.w_h, (uint32_t)g.n_h * 8);
 
   const long rb_gu = row_bytes(MOE_TYPE_Q4_K, H);
   const long rb_sgu = has_sg ? row_bytes(ST, H) : 0;
@@ -454,6 +546,9 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   const long rb_sdn = has_sg ? row_bytes(ST, g.Kps) : 0;
   const int row0 = b * g.RD;
   const int nrd = max(0, min(g.RD, H - row0));
+  // reciprocals for quotients taken as float products (see their uses)
+  const float inv_nrd = 1.0f / (float)max(nrd, 1);
+  const float inv_nbr = 1.0f / (float)(g.Kp / 32);
   const int sf0 = b * g.SR;
   const int nsr = has_sg ? max(0, min(g.SR, Fs - sf0)) : 0;
 
@@ -476,7 +571,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
                   kStackWaves - kPollWaves);
   };
 
-  uint64_t* trace = reinterpret_cast<uint64_t*>(a.ws + g.w_trace);
+  uint64_t* trace = reinterpret_cast<uint64_t*>(a.ws + a.g.w_trace);
   auto stamp = [&](int l, int i) {
     if (b == 0 && tid == 0 && l < kTraceLayers) {
       trace[l * kTraceSlots + i] = wall_clock64();
@@ -669,7 +764,6 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     bstamp(l, 7);
     {
       const int nb_r = g.Kp / 32, nb_s = g.Kps / 32;
-      const float inv_nbr = 1.0f / (float)nb_r;
       // the down rows waves 4..7 requested in phase B have had the whole of
       // phase B to land, so every wave polls
       const bool ok = poll_ll<kAuxSC1>(r_h, g.n_h, ep1, xbuf, kStackWaves);
@@ -702,16 +796,21 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     stamp(l, 8);
     bstamp(l, 9);
     if (nrd > 0) {
-      rows_dot<DT>(k * nrd, tasks_per_row(DT, g.Kp), [&](int r) {
-        const int s = r / nrd, rr = r - s * nrd;
+      // row r < k*nrd is row r % nrd of slot r / nrd (the quotient from a
+      // float product, exact as for the h blocks above); with the shared
+      // expert's rows of the same type, its nrd rows follow as one more slot
+      // in the same pass (they then run alongside the slot rows of one wave)
+      const ActLds acts{hqc + (long)k * g.Kp, hqd + k * (g.Kp / 32), hqs + k * (g.Kp / 32)};
+      const bool one_pass = has_sg && DT == ST && g.Kps == g.Kp;
+      rows_dot<DT>((k + (one_pass ? 1 : 0)) * nrd, tasks_per_row(DT, g.Kp), [&](int r) {
+        const int s = (int)(((float)r + 0.5f) * inv_nrd), rr = r - s * nrd;
+        if (s == k) return RowRef{sdn + (long)rr * rb_sdn, acts};
         return RowRef{rdn + (long)s * g.rdn_slot + (long)rr * rb_dn,
                       ActLds{hqc + (long)s * g.Kp, hqd + s * (g.Kp / 32), hqs + s * (g.Kp / 32)}};
       }, part, wave, kStackWaves);
-      if (has_sg) {
-        const ActLds acts{hqc + (long)k * g.Kp, hqd + k * (g.Kp / 32), hqs + k * (g.Kp / 32)};
+      if (has_sg && !one_pass)
         rows_dot<ST>(nrd, tasks_per_row(ST, g.Kps), [&](int r) { return RowRef{sdn + (long)r * rb_sdn, acts}; },
                      part + k * nrd, wave, kStackWaves);
-      }
       lds_barrier();
       // combine: one lane per (row, slot), the slots of a row in GS adjacent
       // lanes summed by a DPP tree (fp64; y_s is the fp32 row value)
@@ -766,75 +865,9 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
 }
 
 // ---------------------------------------------------------------- host side
-static inline int up1k(long x) { return (int)((x + 1023) & ~1023L); }
-static inline int up16(long x) { return (int)((x + 15) & ~15L); }
-
 int stack_geometry(const moe_layer_desc* d, int G, StackGeom* out) {
-  StackGeom g = {};
-  const int H = d->hidden, E = d->n_experts, k = d->top_k, F = d->ffn, Fs = d->shared_ffn;
-  const bool has_sg = Fs > 0;
-  const int st = has_sg ? d->shared_type : MOE_TYPE_Q4_K;
-  g.G = G;
-  g.Kp = pad_k(d->down_type, F);
-  g.Kps = has_sg ? pad_k(st, Fs) : 0;
-  g.RR = (E + (has_sg ? 1 : 0) + G - 1) / G;
-  g.SR = has_sg ? (Fs + G - 1) / G : 0;
-  g.RD = (H + G - 1) / G;
-  if (g.RD & 1) g.RD += 1;                    // t travels in bf16 pairs
-  g.RP = (k * F + G - 1) / G;
-  while (F % g.RP) g.RP++;
-  if ((long)g.RP * G < (long)k * F) return MOE_ERR_UNSUPPORTED;
-  const long rb_gu = row_bytes(MOE_TYPE_Q4_K, H);
-  const long rb_sgu = has_sg ? row_bytes(st, H) : 0;
-  const long rb_dn = row_bytes(d->down_type, g.Kp);
-  const long rb_sdn = has_sg ? row_bytes(st, g.Kps) : 0;
-  g.n_t = H / 2;
-  g.n_lg = E + (has_sg ? 1 : 0);
-  g.n_h = k * F + Fs;
-  g.n_sel = 2 * k + 1;
-  const int nblk = k * (g.Kp / 32) + g.Kps / 32;
-  // LDS
-  long o = 0;
-  auto take = [&](long bytes) { long r = o; o += up16(bytes); return (int)r; };
-  g.o_res = take(4L * H);
-  g.o_xn = take(4L * H);
-  g.o_xqc = take(H);
-  g.o_xqd = take(4L * (H / 32));
-  g.o_xqs = take(4L * (H / 32));
-  g.o_nw = take(up1k(4L * H));
-  g.o_rrow = take((long)g.RR * up1k(4L * H));
-  g.sgu_half = up1k(g.SR * rb_sgu);
-  g.o_sgu = take(2L * g.sgu_half);
-  g.o_sdn = take(up1k(g.RD * rb_sdn));
-  g.rgu_half = up1k(g.RP * rb_gu);
-  g.o_rgu = take(2L * g.rgu_half);
-  g.rdn_slot = up1k(g.RD * rb_dn);
-  g.o_rdn = take((long)k * g.rdn_slot);
-  g.o_hqc = take((long)k * g.Kp + g.Kps);
-  g.o_hqd = take(4L * nblk);
-  g.o_hqs = take(4L * nblk);
-  long np = 2L * g.RP;                               // fp64 row values of one phase
-  np = np > 2L * g.SR ? np : 2L * g.SR;
-  np = np > (long)(k + 1) * g.RD ? np : (long)(k + 1) * g.RD;
-  g.o_part = take(8L * np);
-  long xb = g.n_h;                                   // words landing from an exchange
-  xb = xb > g.n_t ? xb : g.n_t;
-  xb = xb > g.n_lg ? xb : g.n_lg;
-  // the exchange landing area is only written while the routed gate/up rows are
-  // not in use (before they are staged, after they are consumed): share it
-  if (4L * (xb + 2) <= 2L * g.rgu_half) g.o_xbuf = g.o_rgu;
-  else g.o_xbuf = take(4L * (xb + 2));
-  g.o_sel = take(4L * (g.n_sel + 1));
-  g.o_red = take(8L * (kStackThreads / 64));
-  g.o_y = take(4L * (k + 1) * g.RD);
-  g.o_cand = take(8L * 64);
-  g.o_keys = take(8L * 256);
-  g.o_lgsel = take(4L * (MOE_MAX_TOPK + 1));
-  g.lds = (int)o;
-  if (g.lds < kStackMinLds) g.lds = kStackMinLds;   // keeps one workgroup per CU
-  // workspace (exchange buffers after the per-layer region)
-  out[0] = g;
-  return MOE_OK;
+  const int st = d->shared_ffn > 0 ? d->shared_type : MOE_TYPE_Q4_K;
+  return stack_geometry_core(d->hidden, d->n_experts, d->top_k, d->ffn, d->shared_ffn, d->down_type, st, G, out);
 }
 
 void stack_ws_layout(StackGeom* g, size_t base) {
@@ -885,10 +918,17 @@ int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_
   const void* fn;
   const int dt = d->down_type;
   const int stt = d->shared_ffn > 0 ? d->shared_type : MOE_TYPE_Q4_K;
+  // the compile-time shape when every size and the whole geometry match it
+  const bool fix = dt == MOE_TYPE_Q4_K && stt == MOE_TYPE_Q4_K && d->hidden == kFixH && d->n_experts == kFixE &&
+                   d->top_k == kFixK && d->ffn == kFixF && d->shared_ffn == kFixFs &&
+                   memcmp(&g, &kFixGeom, offsetof(StackGeom, w_ctrl)) == 0;
   if (dt == MOE_TYPE_Q5_K)
-    fn = (stt == MOE_TYPE_Q8_0) ? (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0> : (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K>;
+    fn = (stt == MOE_TYPE_Q8_0) ? (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, false>
+                                : (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K, false>;
+  else if (stt == MOE_TYPE_Q8_0)
+    fn = (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0, false>;
   else
-    fn = (stt == MOE_TYPE_Q8_0) ? (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0> : (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K>;
+    fn = fix ? (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, true> : (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, false>;
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds) != hipSuccess) return MOE_ERR_HIP;
   void* args[] = {&a};
   if (hipLaunchCooperativeKernel(fn, dim3(g.G), dim3(kStackThreads), args, g.lds, st) != hipSuccess) {
