@@ -709,15 +709,15 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     const int slot = p0 / F;
     const int f0 = p0 - slot * F;
     const int nrp = (slot < k) ? min(g.RP, F - f0) : 0;
-    if (nrp > 0 && wave < kPollWaves) {
+    if (nrp > 0) {
       const long e = sel[slot];
-      stage_async(rgu, w.gate + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0, kPollWaves);
+      stage_async(rgu, w.gate + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0, kStackWaves);
       stage_async(rgu + g.rgu_half, w.up + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0,
-                  kPollWaves);
+                  kStackWaves);
     }
     // the routing weights are first needed by the combine: computed while the rows land
     if (wave == 0) routing_weights(k, has_sg, lgsel, sel, reinterpret_cast<double*>(cand));
-    if (wave < kPollWaves) wait_vmem();
+    wait_vmem();
     lds_barrier();
     stamp(l, 5);
     bstamp(l, 6);
