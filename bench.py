@@ -40,6 +40,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-batch", action="store_true", help="skip the grouped batch-path leg")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-seconds-1t", type=float, default=6.0, help="single-thread oracle time")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a kernel that reads and writes 1 GiB each (HBM counter calibration)")
     p.add_argument("--trace", action="store_true", help="print the persistent kernel's per-phase times to stderr")
@@ -232,9 +233,10 @@ def measured_traffic(variant):
         return None
 
 
-def cpu_baseline(stack, seconds):
+def cpu_baseline(stack, seconds, seconds_1t):
     """The oracle, as it stands, on the host cores: whole tokens through the
-    40-layer stack, same weights and inputs, until `seconds` have passed."""
+    40-layer stack, same weights and inputs, until `seconds` have passed; then
+    the same on one thread for `seconds_1t`."""
     import oracle as orc
     cfg = stack.cfg
     t0 = time.time()
@@ -243,15 +245,61 @@ def cpu_baseline(stack, seconds):
     d = orc.make_desc(cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs, down_type=stack.down_type,
                       shared_type=stack.shared_type, eps=cfg.eps)
     inputs = [wl.u16(stack.inputs[t]) for t in range(cfg.tokens)]
-    n = 0
-    t0 = time.time()
-    while True:
-        orc.moe_stack(d, Wn, inputs[n % cfg.tokens])
-        n += 1
-        if time.time() - t0 >= seconds or n >= cfg.tokens:
-            break
-    el = time.time() - t0
-    return {"us_per_token": el / n * 1e6, "tokens": n, "threads": orc.num_threads(), "copy_s": copy_s}
+
+    def run(limit):
+        n = 0
+        t0 = time.time()
+        while True:
+            orc.moe_stack(d, Wn, inputs[n % cfg.tokens])
+            n += 1
+            if time.time() - t0 >= limit or n >= cfg.tokens:
+                break
+        return (time.time() - t0) / n * 1e6, n
+
+    threads = orc.num_threads()
+    us, n = run(seconds)
+    orc.set_threads(1)
+    us1, n1 = run(seconds_1t)
+    orc.set_threads(threads)
+    return {"us_per_token": us, "tokens": n, "threads": threads, "copy_s": copy_s,
+            "us_per_token_1t": us1, "tokens_1t": n1}
+
+
+def stream_read_gbs(q, n_bytes=4 << 30, reps=10, blocks=512):
+    """Achievable HBM read bandwidth from a plain read kernel (the library's
+    moe_stream_read: every 16-byte word of a 4 GiB buffer read once)."""
+    x = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    q.moe_stream_read(x, n_bytes, out, blocks)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        q.moe_stream_read(x, n_bytes, out, blocks)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / reps
+    del x, out
+    torch.cuda.empty_cache()
+    return n_bytes / s / 1e9
+
+
+def cold_tokens(stack, n, evict_bytes=1 << 30):
+    """Per-token latency with the caches flushed: a 1 GiB buffer is streamed
+    (read and written) before every token, outside the per-token events."""
+    buf = torch.ones(evict_bytes // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for t in range(n):
+        buf.mul_(1.0)
+        ev[t][0].record(stream)
+        stack.step(t % stack.cfg.tokens)
+        ev[t][1].record(stream)
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    del buf
+    torch.cuda.empty_cache()
+    return float(np.median(us))
 
 
 def cpu_model():
@@ -306,6 +354,7 @@ def main():
         res["launch_us"] = launch_durations(stack, min(64, a.steps))
         res["kernel_GBs"] = alg / (res["launch_us"] * 1e-6) / 1e9
         res["traffic_bytes_per_launch"] = measured_traffic(name) if res["mode"] == "persistent" else None
+        res["cold_us_per_token"] = cold_tokens(stack, 32)
         if a.trace and stack.mode == q.MOE_STACK_PERSISTENT:
             stack.step(0)
             torch.cuda.synchronize()
@@ -340,9 +389,11 @@ def main():
     batch = None if a.no_batch else batch_leg(q)
     cpu = None
     if not a.no_cpu and stack is not None:
-        c = cpu_baseline(stack, a.cpu_seconds)
+        c = cpu_baseline(stack, a.cpu_seconds, a.cpu_seconds_1t)
         cpu = {"value": c["us_per_token"], "unit": "us/token", "cores": c["threads"], "kind": "oracle",
                "sample": f"{c['tokens']} whole tokens through the {cfg.layers}-layer stack (same weights and inputs)",
+               "single_thread": {"value": c["us_per_token_1t"], "unit": "us/token", "cores": 1,
+                                 "sample": f"{c['tokens_1t']} whole tokens"},
                "cpu_model": cpu_model()}
     kernel = "moe_stack_persistent" if res["mode"] == "persistent" else "per-token graph of per-layer kernels"
     line = {
@@ -358,7 +409,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": res["kernel_GBs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": res["kernel_GBs"] / HBM_PEAK_GBS,
                      "traffic": res["traffic_bytes_per_launch"],
-                     "alg_bytes_per_launch": res["alg_bytes_per_token"], "launch_us": res["launch_us"]},
+                     "alg_bytes_per_launch": res["alg_bytes_per_token"], "launch_us": res["launch_us"],
+                     "stream_read_GBs": stream_read_gbs(q)},
         "cpu_baseline": cpu,
         "variants": results,
         "batch": batch,

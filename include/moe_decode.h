@@ -308,6 +308,15 @@ int moe_test_subblock_dots(const void* rows, int type, int K, int n_rows, const 
                            int32_t* out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Measurement helper: a plain streaming read of `bytes` (a multiple of 16)
+ * from device memory p (16-byte aligned) by `blocks` workgroups of 256
+ * threads, each lane folding its 16-byte words; out [blocks] uint32 (device)
+ * receives one fold per workgroup.  It gives the achievable HBM read rate the
+ * stage's weight streaming is compared with (not a step of the method).
+ * ---------------------------------------------------------------------- */
+int moe_stream_read(const void* p, size_t bytes, uint32_t* out, int blocks, void* stream);
+
+/* ------------------------------------------------------------------------
  * Test export: the persistent kernel's Q8_1 quantiser ([P359] Summary: the
  * activations and the gate/up product are quantised to Q8_1 blocks of 32
  * before the int8 dots), run over n/32 independent blocks.  Same definition

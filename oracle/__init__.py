@@ -75,6 +75,7 @@ def _declare(L):
     L.orc_moe_layer.argtypes = [P, P, P, P, P, P, P]; L.orc_moe_layer.restype = C.c_int
     L.orc_moe_stack.argtypes = [P, P, C.c_int, P, P, P, P, P, P]; L.orc_moe_stack.restype = C.c_int
     L.orc_num_threads.argtypes = []; L.orc_num_threads.restype = C.c_int
+    L.orc_set_threads.argtypes = [C.c_int]; L.orc_set_threads.restype = None
     L.orc_moe_layer_batch.argtypes = [P, P, C.c_int, C.c_int, P, P, P, P, P]
     L.orc_moe_layer_batch.restype = C.c_int
     L.orc_row_dot_bf16.argtypes = [P, C.c_int, C.c_int, P, C.c_int]; L.orc_row_dot_bf16.restype = C.c_float
@@ -234,6 +235,10 @@ def softmax_selected(logits, ids):
 
 def num_threads():
     return lib().orc_num_threads()
+
+
+def set_threads(n):
+    lib().orc_set_threads(int(n))
 
 
 # ---------------------------------------------------------------- layer

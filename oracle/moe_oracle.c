@@ -901,6 +901,16 @@ int orc_moe_stack(const orc_desc* d, const orc_weights* layers, int L,
     return rc;
 }
 
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

@@ -198,6 +198,8 @@ void orc_rows_dot_bf16(const uint8_t* rows, int type, int K, int n_rows, const f
 
 /* Threads the OpenMP loops use (1 when built without OpenMP). */
 int orc_num_threads(void);
+/* OpenMP threads for the calls that follow (n > 0) */
+void orc_set_threads(int n);
 
 #ifdef __cplusplus
 }

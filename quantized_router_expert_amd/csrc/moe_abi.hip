@@ -348,6 +348,13 @@ int moe_test_subblock_dots(const void* rows, int type, int K, int n_rows, const 
   return launch_subblock_dots(rows, type, K, n_rows, xq, out, as_stream(stream));
 }
 
+int moe_stream_read(const void* p, size_t bytes, uint32_t* out, int blocks, void* stream) {
+  if (!p || !out) return MOE_ERR_NULL;
+  if (bytes == 0 || bytes % 16 || blocks <= 0 || blocks > 65535) return MOE_ERR_SHAPE;
+  if (!aligned(p, 16) || !aligned(out, 4)) return MOE_ERR_ALIGN;
+  return launch_stream_read(p, bytes, out, blocks, as_stream(stream));
+}
+
 int moe_test_quantize_q81(const float* x, int n, void* xq, void* stream) {
   if (!x || !xq) return MOE_ERR_NULL;
   if (n <= 0 || n % 32 || n > (1 << 26)) return MOE_ERR_SHAPE;

@@ -451,7 +451,7 @@ __device__ __forceinline__ void quantize_q81_groups(int nblk, const float* base,
       if (live[u]) {
         const int j = i / LPB, p = i % LPB;
         uint32_t* dst = reinterpret_cast<uint32_t*>(codes(j)) + (V / 4) * p;
-        if (V == 16) *reinterpret_cast<uint4*>(dst) = make_uint4(w[u][0], w[u][1], w[u][2], w[u][3]);
+        if constexpr (V == 16) *reinterpret_cast<uint4*>(dst) = make_uint4(w[u][0], w[u][1], w[u][2], w[u][3]);
         else *reinterpret_cast<uint2*>(dst) = make_uint2(w[u][0], w[u][1]);
         if (p == 0) {
           dq[j] = f16_to_f32(ds[u]);

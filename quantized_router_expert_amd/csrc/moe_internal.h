@@ -48,5 +48,6 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
                        uint16_t* shared, float* h, float* hs, uint8_t* ws, const BatchWs& L, hipStream_t st);
 int launch_subblock_dots(const void* rows, int type, int K, int n_rows, const void* xq, int32_t* out, hipStream_t st);
 int launch_test_q81_groups(const float* x, int n, void* xq, hipStream_t st);
+int launch_stream_read(const void* p, size_t bytes, uint32_t* out, int blocks, hipStream_t st);
 
 }  // namespace moe
