@@ -153,6 +153,10 @@ def test_layer_and_stack_validation(q):
     assert q._moe_test_quantize_q81(None, 32, FAKE, None) == -1
     assert q._moe_test_quantize_q81(FAKE, 48, FAKE, None) == -2
     assert q._moe_test_quantize_q81(FAKE + 4, 32, FAKE, None) == -4
+    assert q._moe_stream_read(None, 1024, FAKE, 8, None) == -1
+    assert q._moe_stream_read(FAKE, 1000, FAKE, 8, None) == -2
+    assert q._moe_stream_read(FAKE, 1024, FAKE, 0, None) == -2
+    assert q._moe_stream_read(FAKE + 8, 1024, FAKE, 8, None) == -4
     assert q._moe_workspace_init(None, 1024, None) == -5
     assert q._moe_workspace_init(FAKE + 8, 1024, None) == -4
 
