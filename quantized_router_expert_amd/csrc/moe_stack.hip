@@ -35,6 +35,13 @@ namespace moe {
 
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kPollWaves = 4;   // waves 0..3 poll and load the routed gate/up rows
+// Copies of each exchange area: the producer of a word writes it into every
+// copy and workgroup b reads copy b % R, so the 256 readers of one word are
+// spread over R areas (4-KiB-aligned regions) instead of all polling the same
+// few cache lines.  Eight copies of the 257 logits shorten that exchange; for
+// t and h the extra stores cost more than they save.
+constexpr int kRepT = 1, kRepLg = 8, kRepH = 1;   // measured: copies help the logits only
+constexpr uint32_t rep_bytes(int n_words) { return (8u * (uint32_t)n_words + 4095u) & ~4095u; }
 constexpr int kAuxSC1 = 16;     // agent-coherent (bypasses the XCD L2)
 constexpr uint32_t kSpinLimit = 1u << 22;
 
@@ -104,6 +111,14 @@ __device__ __forceinline__ void ll_store(const __amdgpu_buffer_rsrc_t& r, uint32
   v2u v = {payload, epoch};
   if (aux == kAuxSC1) __builtin_amdgcn_raw_buffer_store_b64(v, r, word * 8, 0, kAuxSC1);
   else __builtin_amdgcn_raw_buffer_store_b64(v, r, word * 8, 0, 0);
+}
+// the same word into each of R copies spaced rep bytes apart
+template <int R>
+__device__ __forceinline__ void ll_store_rep(const __amdgpu_buffer_rsrc_t& r, uint32_t rep, uint32_t word,
+                                             uint32_t payload, uint32_t epoch) {
+  v2u v = {payload, epoch};
+#pragma unroll
+  for (int c = 0; c < R; ++c) __builtin_amdgcn_raw_buffer_store_b64(v, r, c * rep + word * 8, 0, kAuxSC1);
 }
 
 // Poll n LL words until every epoch equals `epoch`, copying payloads to dst[].
@@ -536,9 +551,14 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   lds_barrier();
   const uint32_t base = s_gen * (uint32_t)(3 * a.L + 2) + 1u;
 
-  const __amdgpu_buffer_rsrc_t r_t = make_rsrc(a.ws + a.g.w_t, (uint32_t)g.n_t * 8);
-  const __amdgpu_buffer_rsrc_t r_lg = make_rsrc(a.ws + a.g.w_lg, (uint32_t)g.n_lg * 8);
-  const __amdgpu_buffer_rsrc_t r_h = make_rsrc(a.ws + a.g.w_h, (uint32_t)g.n_h * 8);
+  // writers see every copy; this workgroup reads copy b % R
+  const uint32_t rb_t = rep_bytes(g.n_t), rb_lg = rep_bytes(g.n_lg), rb_h = rep_bytes(g.n_h);
+  const __amdgpu_buffer_rsrc_t w_t = make_rsrc(a.ws + a.g.w_t, kRepT * rb_t);
+  const __amdgpu_buffer_rsrc_t w_lg = make_rsrc(a.ws + a.g.w_lg, kRepLg * rb_lg);
+  const __amdgpu_buffer_rsrc_t w_h = make_rsrc(a.ws + a.g.w_h, kRepH * rb_h);
+  const __amdgpu_buffer_rsrc_t r_t = make_rsrc(a.ws + a.g.w_t + (b % kRepT) * rb_t, (uint32_t)g.n_t * 8);
+  const __amdgpu_buffer_rsrc_t r_lg = make_rsrc(a.ws + a.g.w_lg + (b % kRepLg) * rb_lg, (uint32_t)g.n_lg * 8);
+  const __amdgpu_buffer_rsrc_t r_h = make_rsrc(a.ws + a.g.w_h + (b % kRepH) * rb_h, (uint32_t)g.n_h * 8);
 
   const long rb_gu = row_bytes(MOE_TYPE_Q4_K, H);
   const long rb_sgu = has_sg ? row_bytes(ST, H) : 0;
@@ -667,7 +687,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         a3 += (double)wv.w * (double)xv.w;
       }
       const double acc = wave_sum_f64((a0 + a1) + (a2 + a3));
-      if ((tid & 63) == 0) ll_store(r_lg, r, __float_as_uint((float)acc), ep0, kAuxSC1);
+      if ((tid & 63) == 0) ll_store_rep<kRepLg>(w_lg, rb_lg, r, __float_as_uint((float)acc), ep0);
     }
     bstamp(l, 3);
     // shared gate/up rows -> hs (word k*F + f of the h exchange)
@@ -681,7 +701,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         const float gg = (float)part[tid];
         const float uu = (float)part[nsr + tid];
         const float hv = (float)(silu_f64((double)gg) * (double)uu);
-        ll_store(r_h, k * F + sf0 + tid, __float_as_uint(hv), ep1, kAuxSC1);
+        ll_store_rep<kRepH>(w_h, rb_h, k * F + sf0 + tid, __float_as_uint(hv), ep1);
       }
     }
     // ================= R2: logits -> selection, in every workgroup
@@ -756,7 +776,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         const float gg = (float)part[tid];
         const float uu = (float)part[nrp + tid];
         const float hv = (float)(silu_f64((double)gg) * (double)uu);
-        ll_store(r_h, slot * F + f0 + tid, __float_as_uint(hv), ep1, kAuxSC1);
+        ll_store_rep<kRepH>(w_h, rb_h, slot * F + f0 + tid, __float_as_uint(hv), ep1);
       }
     }
     // ================= R3: every h, read and quantised to Q8_1 by every workgroup
@@ -834,7 +854,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       }
       lds_barrier();
       for (int r2 = tid; 2 * r2 < nrd; r2 += kStackThreads)
-        ll_store(r_t, (row0 >> 1) + r2, (uint32_t)tb[2 * r2] | ((uint32_t)tb[2 * r2 + 1] << 16), ep2, kAuxSC1);
+        ll_store_rep<kRepT>(w_t, rb_t, (row0 >> 1) + r2, (uint32_t)tb[2 * r2] | ((uint32_t)tb[2 * r2 + 1] << 16), ep2);
     }
     lds_barrier();
     stamp(l, 9);
@@ -874,9 +894,9 @@ void stack_ws_layout(StackGeom* g, size_t base) {
   size_t o = base;
   auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~(size_t)255; return r; };
   g->w_ctrl = take(kStackCtrlBytes);
-  g->w_t = take(8u * g->n_t);
-  g->w_lg = take(8u * g->n_lg);
-  g->w_h = take(8u * g->n_h);
+  g->w_t = take((size_t)kRepT * rep_bytes(g->n_t));
+  g->w_lg = take((size_t)kRepLg * rep_bytes(g->n_lg));
+  g->w_h = take((size_t)kRepH * rep_bytes(g->n_h));
   g->w_trace = take(8u * kTraceLayers * kTraceSlots + 8u * kTraceLayers * kTraceMaxG * kBlockEvents);
   g->w_end = o;
 }
