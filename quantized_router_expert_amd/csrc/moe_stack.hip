@@ -128,9 +128,10 @@ __device__ __forceinline__ void ll_store_rep(const __amdgpu_buffer_rsrc_t& r, ui
 // spin limit.
 constexpr int kPollMax = 6;
 template <int AUX>
-__device__ __forceinline__ bool poll_ll(const __amdgpu_buffer_rsrc_t& r, uint32_t n, uint32_t epoch, uint32_t* dst, int nw) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave >= nw) return true;
+__device__ __forceinline__ bool poll_ll(const __amdgpu_buffer_rsrc_t& r, uint32_t n, uint32_t epoch, uint32_t* dst, int nw,
+                                        int w0 = 0) {
+  const int wave = (threadIdx.x >> 6) - w0, lane = threadIdx.x & 63;
+  if (wave < 0 || wave >= nw) return true;
   const uint32_t npairs = (n + 1) >> 1;
   const uint32_t stride = 64u * nw;
   for (uint32_t base = 0; base < npairs; base += stride * kPollMax) {
@@ -471,6 +472,7 @@ constexpr int stack_geometry_core(int H, int E, int k, int F, int Fs, int down_t
   g.o_cand = take(8L * 64);
   g.o_keys = take(8L * 256);
   g.o_lgsel = take(4L * (MOE_MAX_TOPK + 1));
+  g.o_hs = take(4L * (g.Kps > 0 ? g.Kps : 1));
   g.lds = (int)o;
   if (g.lds < kStackMinLds) g.lds = kStackMinLds;   // keeps one workgroup per CU
   // workspace (exchange buffers after the per-layer region)
@@ -525,6 +527,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(smem + g.o_cand);
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(smem + g.o_keys);
   float* lgsel = reinterpret_cast<float*>(smem + g.o_lgsel);
+  float* hsf = reinterpret_cast<float*>(smem + g.o_hs);   // the shared h, landed in phase B
 
   __shared__ uint32_t s_gen;
   __shared__ int s_fail;
@@ -559,6 +562,9 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   const __amdgpu_buffer_rsrc_t r_t = make_rsrc(a.ws + a.g.w_t + (b % kRepT) * rb_t, (uint32_t)g.n_t * 8);
   const __amdgpu_buffer_rsrc_t r_lg = make_rsrc(a.ws + a.g.w_lg + (b % kRepLg) * rb_lg, (uint32_t)g.n_lg * 8);
   const __amdgpu_buffer_rsrc_t r_h = make_rsrc(a.ws + a.g.w_h + (b % kRepH) * rb_h, (uint32_t)g.n_h * 8);
+  // the shared h words alone (they follow the k*F routed words)
+  const __amdgpu_buffer_rsrc_t r_hs =
+      make_rsrc(a.ws + a.g.w_h + (b % kRepH) * rb_h + 8L * k * F, (uint32_t)(Fs > 0 ? Fs : 1) * 8);
 
   const long rb_gu = row_bytes(MOE_TYPE_Q4_K, H);
   const long rb_sgu = has_sg ? row_bytes(ST, H) : 0;
@@ -729,16 +735,29 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     const int slot = p0 / F;
     const int f0 = p0 - slot * F;
     const int nrp = (slot < k) ? min(g.RP, F - f0) : 0;
-    if (nrp > 0) {
+    if (nrp > 0 && wave < kPollWaves) {
       const long e = sel[slot];
-      stage_async(rgu, w.gate + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0, kStackWaves);
+      stage_async(rgu, w.gate + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0, kPollWaves);
       stage_async(rgu + g.rgu_half, w.up + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0,
-                  kStackWaves);
+                  kPollWaves);
     }
     // the routing weights are first needed by the combine: computed while the rows land
     if (wave == 0) routing_weights(k, has_sg, lgsel, sel, reinterpret_cast<double*>(cand));
-    wait_vmem();
+    // meanwhile wave 4 reads the shared h (sent in phase A, so long arrived)
+    // and quantises it: h blocks k*nb_r .. k*nb_r + nb_s - 1
+    if (has_sg && wave == kPollWaves) {
+      if (!poll_ll<kAuxSC1>(r_hs, Fs, ep1, reinterpret_cast<uint32_t*>(hsf), 1, kPollWaves)) s_fail = 1;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      const int nb_r = g.Kp / 32;
+      quantize_q81_groups<4, 1>(g.Kps / 32, hsf, [&](int j) { return (32 * j < Fs) ? 32 * j : -1; },
+                                [&](int j) { return hqc + (long)k * g.Kp + 32 * j; }, hqd + k * nb_r, hqs + k * nb_r,
+                                tid & 63, 64);
+    }
+    if (wave < kPollWaves) wait_vmem();
     lds_barrier();
+    if (s_fail) { fail_out(); return; }
     stamp(l, 5);
     bstamp(l, 6);
     // the down rows are needed only after the h exchange: requested once the
@@ -779,32 +798,30 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         ll_store_rep<kRepH>(w_h, rb_h, slot * F + f0 + tid, __float_as_uint(hv), ep1);
       }
     }
-    // ================= R3: every h, read and quantised to Q8_1 by every workgroup
+    // ================= R3: every routed h, read and quantised to Q8_1 by every workgroup
+    // (the shared h was done in phase B)
     stamp(l, 6);
     bstamp(l, 7);
     {
-      const int nb_r = g.Kp / 32, nb_s = g.Kps / 32;
+      const int nb_r = g.Kp / 32;
       // the down rows waves 4..7 requested in phase B have had the whole of
       // phase B to land, so every wave polls
-      const bool ok = poll_ll<kAuxSC1>(r_h, g.n_h, ep1, xbuf, kStackWaves);
+      const bool ok = poll_ll<kAuxSC1>(r_h, (uint32_t)(k * F), ep1, xbuf, kStackWaves);
       if (!ok) s_fail = 1;
       lds_barrier();
       if (s_fail) { fail_out(); return; }
       bstamp(l, 14);
-      // block j < k*nb_r is block jb = j % nb_r of slot s = j / nb_r and covers
-      // h[s*F + 32jb ..]; block k*nb_r + jb covers the shared h[k*F + 32jb ..];
-      // blocks past F (or Fs) are the zero padding.  s comes from a float
-      // product: (j + 1/2)/nb_r lies at least 1/(2 nb_r) from an integer and
-      // the product is within 2^-23 relative of it, so truncation is exact
+      // block j is block jb = j % nb_r of slot s = j / nb_r and covers
+      // h[s*F + 32jb ..]; blocks past F are the zero padding.  s comes from a
+      // float product: (j + 1/2)/nb_r lies at least 1/(2 nb_r) from an integer
+      // and the product is within 2^-23 relative of it, so truncation is exact
       // for j < 2^22.
       const float* hf = reinterpret_cast<const float*>(xbuf);
-      quantize_q81_groups<4, 1>(k * nb_r + nb_s, hf,
+      quantize_q81_groups<4, 1>(k * nb_r, hf,
                                 [&](int j) -> int {
                                   const int s = (int)(((float)j + 0.5f) * inv_nbr);
-                                  const int jb = j - s * nb_r, jr = j - k * nb_r;
-                                  const int o_r = (32 * jb < F) ? s * F + 32 * jb : -1;
-                                  const int o_s = (32 * jr < Fs) ? k * F + 32 * jr : -1;
-                                  return (s < k) ? o_r : o_s;
+                                  const int jb = j - s * nb_r;
+                                  return (32 * jb < F) ? s * F + 32 * jb : -1;
                                 },
                                 [&](int j) { return hqc + 32 * j; }, hqd, hqs, tid, kStackThreads);
     }
