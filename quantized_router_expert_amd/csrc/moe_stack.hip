@@ -38,9 +38,10 @@ constexpr int kPollWaves = 4;   // waves 0..3 poll and load the routed gate/up r
 // Copies of each exchange area: the producer of a word writes it into every
 // copy and workgroup b reads copy b % R, so the 256 readers of one word are
 // spread over R areas (4-KiB-aligned regions) instead of all polling the same
-// few cache lines.  Eight copies of the 257 logits shorten that exchange; for
-// t and h the extra stores cost more than they save.
-constexpr int kRepT = 1, kRepLg = 8, kRepH = 1;   // measured: copies help the logits only
+// few cache lines.  Eight copies shorten the logits and h exchanges (2 and 4
+// copies of h helped less, 16 did worse); for t the extra stores cost more
+// than they save.
+constexpr int kRepT = 1, kRepLg = 8, kRepH = 8;   // measured: t copies cost more than they save
 constexpr uint32_t rep_bytes(int n_words) { return (8u * (uint32_t)n_words + 4095u) & ~4095u; }
 constexpr int kAuxSC1 = 16;     // agent-coherent (bypasses the XCD L2)
 constexpr uint32_t kSpinLimit = 1u << 22;
