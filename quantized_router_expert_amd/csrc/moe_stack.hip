@@ -113,13 +113,14 @@ __device__ __forceinline__ void ll_store(const __amdgpu_buffer_rsrc_t& r, uint32
   if (aux == kAuxSC1) __builtin_amdgcn_raw_buffer_store_b64(v, r, word * 8, 0, kAuxSC1);
   else __builtin_amdgcn_raw_buffer_store_b64(v, r, word * 8, 0, 0);
 }
-// the same word into each of R copies spaced rep bytes apart
+// the same word into each of R copies spaced rep bytes apart, the first at
+// byte soff of the resource
 template <int R>
-__device__ __forceinline__ void ll_store_rep(const __amdgpu_buffer_rsrc_t& r, uint32_t rep, uint32_t word,
+__device__ __forceinline__ void ll_store_rep(const __amdgpu_buffer_rsrc_t& r, uint32_t soff, uint32_t rep, uint32_t word,
                                              uint32_t payload, uint32_t epoch) {
   v2u v = {payload, epoch};
 #pragma unroll
-  for (int c = 0; c < R; ++c) __builtin_amdgcn_raw_buffer_store_b64(v, r, c * rep + word * 8, 0, kAuxSC1);
+  for (int c = 0; c < R; ++c) __builtin_amdgcn_raw_buffer_store_b64(v, r, c * rep + word * 8, soff, kAuxSC1);
 }
 
 // Poll n LL words until every epoch equals `epoch`, copying payloads to dst[].
@@ -129,8 +130,8 @@ __device__ __forceinline__ void ll_store_rep(const __amdgpu_buffer_rsrc_t& r, ui
 // spin limit.
 constexpr int kPollMax = 6;
 template <int AUX>
-__device__ __forceinline__ bool poll_ll(const __amdgpu_buffer_rsrc_t& r, uint32_t n, uint32_t epoch, uint32_t* dst, int nw,
-                                        int w0 = 0) {
+__device__ __forceinline__ bool poll_ll(const __amdgpu_buffer_rsrc_t& r, uint32_t soff, uint32_t n, uint32_t epoch,
+                                        uint32_t* dst, int nw, int w0 = 0) {
   const int wave = (threadIdx.x >> 6) - w0, lane = threadIdx.x & 63;
   if (wave < 0 || wave >= nw) return true;
   const uint32_t npairs = (n + 1) >> 1;
@@ -147,7 +148,7 @@ __device__ __forceinline__ bool poll_ll(const __amdgpu_buffer_rsrc_t& r, uint32_
 #pragma unroll
       for (int m = 0; m < kPollMax; ++m)
         if ((want & ~done) & (1u << m))
-          v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (first + m * stride) * 16, 0, AUX));
+          v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (first + m * stride) * 16, soff, AUX));
 #pragma unroll
       for (int m = 0; m < kPollMax; ++m) {
         if ((want & ~done) & (1u << m)) {
@@ -482,16 +483,19 @@ constexpr int stack_geometry_core(int H, int E, int k, int F, int Fs, int down_t
 }
 
 // The shape the kernel is also compiled for with every size a constant
-// (hidden 2048, 256 experts, top-8, expert and shared FFN 512, Q4_K
-// throughout, 256 workgroups): loop bounds, LDS offsets and quotients fold
-// into the code, and the scalar registers that would hold them stay free.
+// (hidden 2048, 256 experts, top-8, expert and shared FFN 512, 256
+// workgroups; down/shared types Q4_K/Q4_K and Q5_K/Q8_0): loop bounds, LDS
+// offsets and quotients fold into the code, and the scalar registers that
+// would hold them stay free.
 constexpr int kFixH = 2048, kFixE = 256, kFixK = 8, kFixF = 512, kFixFs = 512, kFixG = 256;
+template <int DT, int ST>
 constexpr StackGeom fixed_geom() {
   StackGeom g = {};
-  stack_geometry_core(kFixH, kFixE, kFixK, kFixF, kFixFs, MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, kFixG, &g);
+  stack_geometry_core(kFixH, kFixE, kFixK, kFixF, kFixFs, DT, ST, kFixG, &g);
   return g;
 }
-constexpr StackGeom kFixGeom = fixed_geom();
+template <int DT, int ST>
+constexpr StackGeom kFixGeom = fixed_geom<DT, ST>();
 
 // ---------------------------------------------------------------- the kernel
 template <int DT, int ST, bool FIX>
@@ -500,7 +504,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   // FIX: the geometry and sizes are the compile-time ones (the launch checks
   // that they equal the runtime ones); the workspace offsets always come from
   // the arguments
-  const StackGeom g = FIX ? kFixGeom : a.g;
+  const StackGeom g = FIX ? kFixGeom<DT, ST> : a.g;
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   const int H = FIX ? kFixH : a.H, E = FIX ? kFixE : a.E, k = FIX ? kFixK : a.k, F = FIX ? kFixF : a.F,
             Fs = FIX ? kFixFs : a.Fs;
@@ -557,15 +561,13 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
 
   // writers see every copy; this workgroup reads copy b % R
   const uint32_t rb_t = rep_bytes(g.n_t), rb_lg = rep_bytes(g.n_lg), rb_h = rep_bytes(g.n_h);
-  const __amdgpu_buffer_rsrc_t w_t = make_rsrc(a.ws + a.g.w_t, kRepT * rb_t);
-  const __amdgpu_buffer_rsrc_t w_lg = make_rsrc(a.ws + a.g.w_lg, kRepLg * rb_lg);
-  const __amdgpu_buffer_rsrc_t w_h = make_rsrc(a.ws + a.g.w_h, kRepH * rb_h);
-  const __amdgpu_buffer_rsrc_t r_t = make_rsrc(a.ws + a.g.w_t + (b % kRepT) * rb_t, (uint32_t)g.n_t * 8);
-  const __amdgpu_buffer_rsrc_t r_lg = make_rsrc(a.ws + a.g.w_lg + (b % kRepLg) * rb_lg, (uint32_t)g.n_lg * 8);
-  const __amdgpu_buffer_rsrc_t r_h = make_rsrc(a.ws + a.g.w_h + (b % kRepH) * rb_h, (uint32_t)g.n_h * 8);
-  // the shared h words alone (they follow the k*F routed words)
-  const __amdgpu_buffer_rsrc_t r_hs =
-      make_rsrc(a.ws + a.g.w_h + (b % kRepH) * rb_h + 8L * k * F, (uint32_t)(Fs > 0 ? Fs : 1) * 8);
+  // one resource over the three exchange areas (t, logits, h: consecutive in
+  // the workspace); an area and a copy are picked by the instruction's
+  // scalar offset, which keeps one descriptor in scalar registers instead of
+  // one per area and copy
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.ws + a.g.w_t, (uint32_t)(a.g.w_trace - a.g.w_t));
+  const uint32_t x_lg = (uint32_t)(a.g.w_lg - a.g.w_t), x_h = (uint32_t)(a.g.w_h - a.g.w_t);
+  const uint32_t rd_t = (b % kRepT) * rb_t, rd_lg = x_lg + (b % kRepLg) * rb_lg, rd_h = x_h + (b % kRepH) * rb_h;
 
   const long rb_gu = row_bytes(MOE_TYPE_Q4_K, H);
   const long rb_sgu = has_sg ? row_bytes(ST, H) : 0;
@@ -631,7 +633,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     double ss = 0.0;
     float4* res4 = reinterpret_cast<float4*>(res);
     if (l > 0) {
-      const bool ok = poll_ll<kAuxSC1>(r_t, g.n_t, ep2 - 3u, xbuf, kPollWaves);
+      const bool ok = poll_ll<kAuxSC1>(rx, rd_t, g.n_t, ep2 - 3u, xbuf, kPollWaves);
       if (!ok) s_fail = 1;
       lds_barrier();
       if (s_fail) { fail_out(); return; }
@@ -694,7 +696,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         a3 += (double)wv.w * (double)xv.w;
       }
       const double acc = wave_sum_f64((a0 + a1) + (a2 + a3));
-      if ((tid & 63) == 0) ll_store_rep<kRepLg>(w_lg, rb_lg, r, __float_as_uint((float)acc), ep0);
+      if ((tid & 63) == 0) ll_store_rep<kRepLg>(rx, x_lg, rb_lg, r, __float_as_uint((float)acc), ep0);
     }
     bstamp(l, 3);
     // shared gate/up rows -> hs (word k*F + f of the h exchange)
@@ -708,14 +710,14 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         const float gg = (float)part[tid];
         const float uu = (float)part[nsr + tid];
         const float hv = (float)(silu_f64((double)gg) * (double)uu);
-        ll_store_rep<kRepH>(w_h, rb_h, k * F + sf0 + tid, __float_as_uint(hv), ep1);
+        ll_store_rep<kRepH>(rx, x_h, rb_h, k * F + sf0 + tid, __float_as_uint(hv), ep1);
       }
     }
     // ================= R2: logits -> selection, in every workgroup
     stamp(l, 3);
     bstamp(l, 4);
     {
-      const bool ok = poll_ll<kAuxSC1>(r_lg, g.n_lg, ep0, xbuf, kPollWaves);
+      const bool ok = poll_ll<kAuxSC1>(rx, rd_lg, g.n_lg, ep0, xbuf, kPollWaves);
       if (!ok) s_fail = 1;
       lds_barrier();
       if (s_fail) { fail_out(); return; }
@@ -747,7 +749,8 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     // meanwhile wave 4 reads the shared h (sent in phase A, so long arrived)
     // and quantises it: h blocks k*nb_r .. k*nb_r + nb_s - 1
     if (has_sg && wave == kPollWaves) {
-      if (!poll_ll<kAuxSC1>(r_hs, Fs, ep1, reinterpret_cast<uint32_t*>(hsf), 1, kPollWaves)) s_fail = 1;
+      // the shared h words follow the k*F routed words
+      if (!poll_ll<kAuxSC1>(rx, rd_h + 8u * k * F, Fs, ep1, reinterpret_cast<uint32_t*>(hsf), 1, kPollWaves)) s_fail = 1;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
@@ -796,7 +799,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         const float gg = (float)part[tid];
         const float uu = (float)part[nrp + tid];
         const float hv = (float)(silu_f64((double)gg) * (double)uu);
-        ll_store_rep<kRepH>(w_h, rb_h, slot * F + f0 + tid, __float_as_uint(hv), ep1);
+        ll_store_rep<kRepH>(rx, x_h, rb_h, slot * F + f0 + tid, __float_as_uint(hv), ep1);
       }
     }
     // ================= R3: every routed h, read and quantised to Q8_1 by every workgroup
@@ -807,7 +810,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       const int nb_r = g.Kp / 32;
       // the down rows waves 4..7 requested in phase B have had the whole of
       // phase B to land, so every wave polls
-      const bool ok = poll_ll<kAuxSC1>(r_h, (uint32_t)(k * F), ep1, xbuf, kStackWaves);
+      const bool ok = poll_ll<kAuxSC1>(rx, rd_h, (uint32_t)(k * F), ep1, xbuf, kStackWaves);
       if (!ok) s_fail = 1;
       lds_barrier();
       if (s_fail) { fail_out(); return; }
@@ -872,7 +875,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       }
       lds_barrier();
       for (int r2 = tid; 2 * r2 < nrd; r2 += kStackThreads)
-        ll_store_rep<kRepT>(w_t, rb_t, (row0 >> 1) + r2, (uint32_t)tb[2 * r2] | ((uint32_t)tb[2 * r2 + 1] << 16), ep2);
+        ll_store_rep<kRepT>(rx, 0u, rb_t, (row0 >> 1) + r2, (uint32_t)tb[2 * r2] | ((uint32_t)tb[2 * r2 + 1] << 16), ep2);
     }
     lds_barrier();
     stamp(l, 9);
@@ -885,7 +888,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   // ================= the fold a next layer would do: output = bf16(res + t)
   if (b == 0) {
     const uint32_t epl = base + 3u * (a.L - 1) + 2u;
-    const bool ok = poll_ll<kAuxSC1>(r_t, g.n_t, epl, xbuf, kPollWaves);
+    const bool ok = poll_ll<kAuxSC1>(rx, rd_t, g.n_t, epl, xbuf, kPollWaves);
     if (!ok) s_fail = 1;
     lds_barrier();
     if (s_fail) { fail_out(); return; }
@@ -957,16 +960,21 @@ int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_
   const int dt = d->down_type;
   const int stt = d->shared_ffn > 0 ? d->shared_type : MOE_TYPE_Q4_K;
   // the compile-time shape when every size and the whole geometry match it
-  const bool fix = dt == MOE_TYPE_Q4_K && stt == MOE_TYPE_Q4_K && d->hidden == kFixH && d->n_experts == kFixE &&
-                   d->top_k == kFixK && d->ffn == kFixF && d->shared_ffn == kFixFs &&
-                   memcmp(&g, &kFixGeom, offsetof(StackGeom, w_ctrl)) == 0;
+  const bool fix_shape = d->hidden == kFixH && d->n_experts == kFixE && d->top_k == kFixK && d->ffn == kFixF &&
+                         d->shared_ffn == kFixFs;
+  const bool fix44 = fix_shape && dt == MOE_TYPE_Q4_K && stt == MOE_TYPE_Q4_K &&
+                     memcmp(&g, &kFixGeom<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K>, offsetof(StackGeom, w_ctrl)) == 0;
+  const bool fix58 = fix_shape && dt == MOE_TYPE_Q5_K && stt == MOE_TYPE_Q8_0 &&
+                     memcmp(&g, &kFixGeom<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0>, offsetof(StackGeom, w_ctrl)) == 0;
   if (dt == MOE_TYPE_Q5_K)
-    fn = (stt == MOE_TYPE_Q8_0) ? (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, false>
+    fn = (stt == MOE_TYPE_Q8_0) ? (fix58 ? (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, true>
+                                         : (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, false>)
                                 : (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K, false>;
   else if (stt == MOE_TYPE_Q8_0)
     fn = (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0, false>;
   else
-    fn = fix ? (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, true> : (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, false>;
+    fn = fix44 ? (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, true>
+               : (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, false>;
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds) != hipSuccess) return MOE_ERR_HIP;
   void* args[] = {&a};
   if (hipLaunchCooperativeKernel(fn, dim3(g.G), dim3(kStackThreads), args, g.lds, st) != hipSuccess) {
