@@ -75,6 +75,8 @@ def _declare(L):
     L.orc_moe_layer.argtypes = [P, P, P, P, P, P, P]; L.orc_moe_layer.restype = C.c_int
     L.orc_moe_stack.argtypes = [P, P, C.c_int, P, P, P, P, P, P]; L.orc_moe_stack.restype = C.c_int
     L.orc_num_threads.argtypes = []; L.orc_num_threads.restype = C.c_int
+    L.orc_quantize_q4k.argtypes = [P, P]; L.orc_quantize_q4k.restype = None
+    L.orc_requant_q4k.argtypes = [P, C.c_int, C.c_int, C.c_int, P]; L.orc_requant_q4k.restype = C.c_int
     L.orc_set_threads.argtypes = [C.c_int]; L.orc_set_threads.restype = None
     L.orc_moe_layer_batch.argtypes = [P, P, C.c_int, C.c_int, P, P, P, P, P]
     L.orc_moe_layer_batch.restype = C.c_int
@@ -168,6 +170,26 @@ def quantize_q8_1(x):
     assert x.size % 32 == 0
     out = np.zeros(x.size // 32 * 36, dtype=np.uint8)
     L.orc_quantize_q8_1(_p(x), x.size, _p(out))
+    return out
+
+
+def quantize_q4k(x):
+    """fp32 [..., K] (K % 256 == 0) -> Q4_K bytes, one call per superblock."""
+    L = lib()
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, 256)
+    out = np.zeros(x.shape[0] * 144, dtype=np.uint8)
+    for i in range(x.shape[0]):
+        L.orc_quantize_q4k(_p(x[i]), _p(out[144 * i:]))
+    return out
+
+
+def requant_q4k(src, src_type, n_rows, K):
+    """rows of K elements of src_type (Q8_0 / Q5_K / Q4_K) -> Q4_K rows (bytes)."""
+    L = lib()
+    src = _u8(src)
+    out = np.zeros(n_rows * (K // 256) * 144, dtype=np.uint8)
+    rc = L.orc_requant_q4k(_p(src), int(src_type), int(n_rows), int(K), _p(out))
+    assert rc == 0, rc
     return out
 
 

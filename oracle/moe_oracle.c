@@ -191,6 +191,113 @@ void orc_decode_q8_1(const uint8_t* blk, double out[32], double* sum_out)
 }
 
 /* ------------------------------------------------------------------ */
+/* Load-time requantisation to Q4_K ([P359] Summary: the shared expert */
+/* stored as Q8_0 and the routed down projection stored as Q5_K are     */
+/* re-quantised to Q4_K once, when the model is loaded).  The pages     */
+/* name the step, not the quantiser.  Reading: the source values are    */
+/* decoded exactly and rounded once to fp32; each 256-value superblock  */
+/* is then quantised by a min/max rule with every step an fp32          */
+/* operation rounded to nearest (ties to even):                         */
+/*   per 32-value sub-block j: lo = min(0, min x), hi = max x,          */
+/*     step_j = (hi - lo) / 15, off_j = -lo;                            */
+/*   d = f16(max_j step_j / 63), dmin = f16(max_j off_j / 63);          */
+/*   sc_j = clamp(rint(step_j / d), 0, 63) (0 when d = 0), and m_j the  */
+/*     same from off_j and dmin;                                        */
+/*   q = clamp(rint((x + dmin*m_j) / (d*sc_j)), 0, 15) (0 when d*sc_j   */
+/*     = 0);                                                            */
+/* then the GGUF Q4_K byte layout (6-bit scale/min packing, nibble      */
+/* order of the decoder above).                                         */
+/* ------------------------------------------------------------------ */
+static float f16_f32(uint16_t h) { return (float)orc_f16_to_f64(h); }
+
+void orc_quantize_q4k(const float x[256], uint8_t blk[144])
+{
+    float step[8], off[8], maxstep = 0.0f, maxoff = 0.0f;
+    for (int j = 0; j < 8; ++j) {
+        float mn = x[32 * j], mx = x[32 * j];
+        for (int i = 1; i < 32; ++i) {
+            if (x[32 * j + i] < mn) mn = x[32 * j + i];
+            if (x[32 * j + i] > mx) mx = x[32 * j + i];
+        }
+        const float lo = mn < 0.0f ? mn : 0.0f;
+        volatile float st = (mx - lo) / 15.0f;
+        step[j] = st;
+        off[j] = -lo;
+        if (step[j] > maxstep) maxstep = step[j];
+        if (off[j] > maxoff) maxoff = off[j];
+    }
+    volatile float dq = maxstep / 63.0f, mq = maxoff / 63.0f;
+    const uint16_t d16 = orc_f32_to_f16(dq), m16 = orc_f32_to_f16(mq);
+    const float d = f16_f32(d16), dmin = f16_f32(m16);
+    int sc[8], m[8];
+    for (int j = 0; j < 8; ++j) {
+        volatile float a = d > 0.0f ? step[j] / d : 0.0f;
+        volatile float b = dmin > 0.0f ? off[j] / dmin : 0.0f;
+        float ra = rintf(a), rb = rintf(b);
+        sc[j] = ra < 0.0f ? 0 : (ra > 63.0f ? 63 : (int)ra);
+        m[j] = rb < 0.0f ? 0 : (rb > 63.0f ? 63 : (int)rb);
+    }
+    int q[256];
+    for (int j = 0; j < 8; ++j) {
+        volatile float es = d * (float)sc[j];
+        volatile float eo = dmin * (float)m[j];
+        for (int i = 0; i < 32; ++i) {
+            int v = 0;
+            if (es > 0.0f) {
+                volatile float num = x[32 * j + i] + eo;
+                volatile float t = num / es;
+                const float r = rintf(t);
+                v = r < 0.0f ? 0 : (r > 15.0f ? 15 : (int)r);
+            }
+            q[32 * j + i] = v;
+        }
+    }
+    blk[0] = (uint8_t)(d16 & 0xFF);
+    blk[1] = (uint8_t)(d16 >> 8);
+    blk[2] = (uint8_t)(m16 & 0xFF);
+    blk[3] = (uint8_t)(m16 >> 8);
+    uint8_t* sb = blk + 4;
+    for (int j = 0; j < 4; ++j) {
+        sb[j] = (uint8_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
+        sb[j + 4] = (uint8_t)((m[j] & 63) | ((m[j + 4] >> 4) << 6));
+        sb[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((m[j + 4] & 15) << 4));
+    }
+    for (int p = 0; p < 4; ++p)
+        for (int l = 0; l < 32; ++l)
+            blk[16 + 32 * p + l] = (uint8_t)(q[64 * p + l] | (q[64 * p + 32 + l] << 4));
+}
+
+/* rows of K source elements (Q8_0, Q5_K or Q4_K) -> rows of Q4_K       */
+int orc_requant_q4k(const uint8_t* src, int src_type, int n_rows, int K, uint8_t* dst)
+{
+    if (K % 256)
+        return -1;
+    const long sb_src = (src_type == ORC_Q8_0) ? 8L * ORC_Q80_BYTES
+                      : (src_type == ORC_Q5_K) ? ORC_Q5K_BYTES
+                      : (src_type == ORC_Q4_K) ? ORC_Q4K_BYTES : -1;
+    if (sb_src < 0)
+        return -1;
+    const int nsb = K / 256;
+#pragma omp parallel for schedule(static)
+    for (long t = 0; t < (long)n_rows * nsb; ++t) {
+        const uint8_t* s = src + t * sb_src;
+        double v[256];
+        if (src_type == ORC_Q8_0)
+            for (int b = 0; b < 8; ++b)
+                orc_decode_q8_0(s + b * ORC_Q80_BYTES, v + 32 * b);
+        else if (src_type == ORC_Q5_K)
+            orc_decode_q5k(s, v);
+        else
+            orc_decode_q4k(s, v);
+        float x[256];
+        for (int i = 0; i < 256; ++i)
+            x[i] = (float)v[i];
+        orc_quantize_q4k(x, dst + t * ORC_Q4K_BYTES);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Q8_1 activation quantiser ([P359] Summary: the shared-expert path    */
 /* quantises the normed activations and the SwiGLU output to Q8_1).    */
 /* Reading: per 32 values, d = amax/127 in fp32, codes are the fp32     */

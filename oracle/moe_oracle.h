@@ -56,6 +56,14 @@ void orc_kquant_scales(const uint8_t* blk, int sc[8], int m[8]);
 /* ---- Q8_1 activation quantiser, n a multiple of 32 ---- */
 void orc_quantize_q8_1(const float* x, int n, uint8_t* out);
 
+/* Load-time requantisation to Q4_K ([P359] Summary), quantiser reading in
+ * moe_oracle.c.  orc_quantize_q4k: 256 fp32 values -> one 144-byte block.
+ * orc_requant_q4k: n_rows rows of K elements (K % 256 == 0) of src_type
+ * (ORC_Q8_0, ORC_Q5_K or ORC_Q4_K) -> n_rows rows of K/256 Q4_K blocks.
+ * Returns 0, or -1 for an unsupported type or K. */
+void orc_quantize_q4k(const float x[256], uint8_t blk[144]);
+int orc_requant_q4k(const uint8_t* src, int src_type, int n_rows, int K, uint8_t* dst);
+
 /* ---- integer sub-block dots: out[j] = sum_{32} qw*qa for each 32-element
  *      sub-block j of one weight row against Q8_1 activations ----
  * type: ORC_Q4_K, ORC_Q5_K or ORC_Q8_0; K multiple of 256 (K-quants) or 32 (Q8_0).
