@@ -308,6 +308,27 @@ int moe_test_subblock_dots(const void* rows, int type, int K, int n_rows, const 
                            int32_t* out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Load-time requantisation to Q4_K ([P359] Summary: the shared expert's
+ * Q8_0 matrices and the routed down projection's Q5_K matrices are
+ * re-quantised to Q4_K once at model load, so the per-token reads shrink).
+ * The pages do not give the quantiser; this one, per 256-value superblock,
+ * decodes the source values exactly and rounds them once to fp32, then:
+ *   per 32-value sub-block lo = min(0, min x), hi = max x,
+ *     step = (hi - lo)/15, off = -lo;
+ *   d = f16(max step / 63), dmin = f16(max off / 63);
+ *   sc, m = nearest integer (ties to even) to step/d, off/dmin, in 0..63
+ *     (0 when d, dmin = 0);
+ *   q = nearest integer to (x + dmin*m)/(d*sc) in 0..15 (0 when d*sc = 0);
+ * each step one fp32 operation rounded to nearest, written in the GGUF Q4_K
+ * layout.  src: n_rows rows of K elements (K % 256 == 0) of src_type
+ * (MOE_TYPE_Q8_0, MOE_TYPE_Q5_K or MOE_TYPE_Q4_K), 16-byte aligned; dst:
+ * n_rows rows of K/256 Q4_K blocks (144 B), 2-byte aligned; the two must not
+ * overlap.  All device, asynchronous on stream.  Source values that are not
+ * finite give unspecified blocks.
+ * ---------------------------------------------------------------------- */
+int moe_requant_q4k(const void* src, int src_type, int n_rows, int K, void* dst, void* stream);
+
+/* ------------------------------------------------------------------------
  * Measurement helper: a plain streaming read of `bytes` (a multiple of 16)
  * from device memory p (16-byte aligned) by `blocks` workgroups of 256
  * threads, each lane folding its 16-byte words; out [blocks] uint32 (device)

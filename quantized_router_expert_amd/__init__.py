@@ -83,10 +83,11 @@ _moe_stack_trace_offset = _sig("moe_stack_trace_offset", C.c_size_t, C.POINTER(L
 _moe_test_subblock_dots = _sig("moe_test_subblock_dots", C.c_int, P, C.c_int, C.c_int, C.c_int, P, P, P)
 _moe_test_quantize_q81 = _sig("moe_test_quantize_q81", C.c_int, P, C.c_int, P, P)
 _moe_stream_read = _sig("moe_stream_read", C.c_int, P, C.c_size_t, P, C.c_int, P)
+_moe_requant_q4k = _sig("moe_requant_q4k", C.c_int, P, C.c_int, C.c_int, C.c_int, P, P)
 
 EXPORTS = ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", "moe_stack_bind",
            "moe_decode_stack", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
-           "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots", "moe_test_quantize_q81", "moe_stream_read",
+           "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots", "moe_test_quantize_q81", "moe_stream_read", "moe_requant_q4k",
            "moe_batch_workspace_size", "expert_ffn_grouped", "moe_decode_layer_batch")
 MAX_BATCH = 64
 MAX_GROUP_MIN = 16
@@ -304,6 +305,10 @@ def stack_block_trace(desc, n_layers, ws):
 def layer_array(layers):
     """Pre-marshalled host array of layer weight pointers (reuse across calls)."""
     return _layer_array(layers)
+
+
+def moe_requant_q4k(src, src_type, n_rows, K, dst, stream=None):
+    return _check("moe_requant_q4k", _moe_requant_q4k(ptr(src), src_type, n_rows, K, ptr(dst), stream_handle(stream)))
 
 
 def moe_stream_read(p, n_bytes, out, blocks, stream=None):

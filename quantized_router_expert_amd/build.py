@@ -11,7 +11,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_decode.so")
-SOURCES = ["moe_kernels.hip", "moe_stack.hip", "moe_batch.hip", "moe_abi.hip"]
+SOURCES = ["moe_kernels.hip", "moe_stack.hip", "moe_batch.hip", "moe_requant.hip", "moe_abi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",

@@ -348,6 +348,14 @@ int moe_test_subblock_dots(const void* rows, int type, int K, int n_rows, const 
   return launch_subblock_dots(rows, type, K, n_rows, xq, out, as_stream(stream));
 }
 
+int moe_requant_q4k(const void* src, int src_type, int n_rows, int K, void* dst, void* stream) {
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (src_type != MOE_TYPE_Q8_0 && src_type != MOE_TYPE_Q5_K && src_type != MOE_TYPE_Q4_K) return MOE_ERR_TYPE;
+  if (n_rows <= 0 || K <= 0 || K % 256 || (long)n_rows * (K / 256) > (1L << 30)) return MOE_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(dst, 2)) return MOE_ERR_ALIGN;
+  return launch_requant_q4k(src, src_type, n_rows, K, dst, as_stream(stream));
+}
+
 int moe_stream_read(const void* p, size_t bytes, uint32_t* out, int blocks, void* stream) {
   if (!p || !out) return MOE_ERR_NULL;
   if (bytes == 0 || bytes % 16 || blocks <= 0 || blocks > 65535) return MOE_ERR_SHAPE;

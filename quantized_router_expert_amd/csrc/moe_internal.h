@@ -49,5 +49,6 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
 int launch_subblock_dots(const void* rows, int type, int K, int n_rows, const void* xq, int32_t* out, hipStream_t st);
 int launch_test_q81_groups(const float* x, int n, void* xq, hipStream_t st);
 int launch_stream_read(const void* p, size_t bytes, uint32_t* out, int blocks, hipStream_t st);
+int launch_requant_q4k(const void* src, int src_type, int n_rows, int K, void* dst, hipStream_t st);
 
 }  // namespace moe

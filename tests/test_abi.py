@@ -153,6 +153,12 @@ def test_layer_and_stack_validation(q):
     assert q._moe_test_quantize_q81(None, 32, FAKE, None) == -1
     assert q._moe_test_quantize_q81(FAKE, 48, FAKE, None) == -2
     assert q._moe_test_quantize_q81(FAKE + 4, 32, FAKE, None) == -4
+    assert q._moe_requant_q4k(None, 13, 1, 256, FAKE, None) == -1
+    assert q._moe_requant_q4k(FAKE, 9, 1, 256, FAKE, None) == -3
+    assert q._moe_requant_q4k(FAKE, 13, 1, 300, FAKE, None) == -2
+    assert q._moe_requant_q4k(FAKE, 13, 0, 256, FAKE, None) == -2
+    assert q._moe_requant_q4k(FAKE + 8, 13, 1, 256, FAKE, None) == -4
+    assert q._moe_requant_q4k(FAKE, 13, 1, 256, FAKE + 1, None) == -4
     assert q._moe_stream_read(None, 1024, FAKE, 8, None) == -1
     assert q._moe_stream_read(FAKE, 1000, FAKE, 8, None) == -2
     assert q._moe_stream_read(FAKE, 1024, FAKE, 0, None) == -2
