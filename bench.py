@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--repeats", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-batch", action="store_true", help="skip the grouped batch-path leg")
+    p.add_argument("--no-requant", action="store_true", help="skip the load-time requantisation leg")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--cpu-seconds-1t", type=float, default=6.0, help="single-thread oracle time")
     p.add_argument("--calib-copy", action="store_true",
@@ -302,6 +303,43 @@ def cold_tokens(stack, n, evict_bytes=1 << 30):
     return float(np.median(us))
 
 
+def requant_leg(q, reps=20):
+    """Load-time requantisation to Q4_K of one layer of the 40-layer shape:
+    the 256 routed down matrices from Q5_K and the shared expert's three
+    matrices from Q8_0.  Reports time and HBM rate (source read + Q4_K
+    written) per call, and the time for all 40 layers."""
+    cfg = wl.CONFIGS["stack"]
+    W = wl.layer_weights(cfg, 0, "cuda", shared_type=wl.Q8_0, down_type=wl.Q5_K)
+    jobs = [("down", wl.Q5_K, cfg.E * cfg.H, cfg.F), ("sgate", wl.Q8_0, cfg.Fs, cfg.H),
+            ("sup", wl.Q8_0, cfg.Fs, cfg.H), ("sdown", wl.Q8_0, cfg.H, cfg.Fs)]
+    out = {}
+    total_us = 0.0
+    for name, st, rows, K in jobs:
+        src = W[name]
+        dst = torch.empty(rows * (K // 256) * 144, dtype=torch.uint8, device="cuda")
+        q.moe_requant_q4k(src, st, rows, K, dst)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            q.moe_requant_q4k(src, st, rows, K, dst)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = src.numel() + dst.numel()
+        out[name] = {"src_type": st, "rows": rows, "K": K, "us": us, "GBs": nbytes / (us * 1e-6) / 1e9,
+                     "src_bytes": src.numel(), "dst_bytes": dst.numel()}
+        total_us += us
+        del dst
+    del W
+    torch.cuda.empty_cache()
+    out["layer_us"] = total_us
+    out["model_40_layers_ms"] = total_us * cfg.layers / 1e3
+    print(f"# requant to Q4_K, one layer: {total_us:.0f} us (routed down {out['down']['GBs']:.0f} GB/s); "
+          f"40 layers {out['model_40_layers_ms']:.1f} ms", file=sys.stderr, flush=True)
+    return out
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -387,6 +425,7 @@ def main():
         print(f"# {name}: {med:.1f} us/token ({res['achieved_GBs']:.0f} GB/s)", file=sys.stderr, flush=True)
     stack, res = primary if primary else (None, results[order[0]])
     batch = None if a.no_batch else batch_leg(q)
+    requant = None if a.no_requant else requant_leg(q)
     cpu = None
     if not a.no_cpu and stack is not None:
         c = cpu_baseline(stack, a.cpu_seconds, a.cpu_seconds_1t)
@@ -414,6 +453,7 @@ def main():
         "cpu_baseline": cpu,
         "variants": results,
         "batch": batch,
+        "requant": requant,
     }
     print(json.dumps(line))
 
