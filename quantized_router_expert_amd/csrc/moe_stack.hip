@@ -123,15 +123,15 @@ __device__ __forceinline__ void ll_store_rep(const __amdgpu_buffer_rsrc_t& r, ui
   for (int c = 0; c < R; ++c) __builtin_amdgcn_raw_buffer_store_b64(v, r, c * rep + word * 8, soff, kAuxSC1);
 }
 
-// Poll n LL words until every epoch equals `epoch`, copying payloads to dst[].
-// Waves [0, nw) split the words; every lane issues all of its loads of a
-// round (up to kPollMax 16-byte word pairs) before checking any, so one
-// memory round trip covers up to 64*nw*kPollMax pairs.  Returns false on the
-// spin limit.
+// Poll n LL words until every epoch equals `epoch`, handing each current pair
+// of words (2p, 2p+1) to sink(p, payload 2p, payload 2p+1) once.  Waves
+// [w0, w0+nw) split the words; every lane issues all of its loads of a round
+// (up to kPollMax 16-byte word pairs) before checking any, so one memory round
+// trip covers up to 64*nw*kPollMax pairs.  Returns false on the spin limit.
 constexpr int kPollMax = 6;
-template <int AUX>
-__device__ __forceinline__ bool poll_ll(const __amdgpu_buffer_rsrc_t& r, uint32_t soff, uint32_t n, uint32_t epoch,
-                                        uint32_t* dst, int nw, int w0 = 0) {
+template <int AUX, class Sink>
+__device__ __forceinline__ bool poll_ll_sink(const __amdgpu_buffer_rsrc_t& r, uint32_t soff, uint32_t n, uint32_t epoch,
+                                             int nw, int w0, Sink sink) {
   const int wave = (threadIdx.x >> 6) - w0, lane = threadIdx.x & 63;
   if (wave < 0 || wave >= nw) return true;
   const uint32_t npairs = (n + 1) >> 1;
@@ -155,8 +155,7 @@ __device__ __forceinline__ bool poll_ll(const __amdgpu_buffer_rsrc_t& r, uint32_
           const uint32_t p = first + m * stride;
           const bool second = (2 * p + 1 < n);
           if (v[m].y == epoch && (!second || v[m].w == epoch)) {
-            dst[2 * p] = v[m].x;
-            if (second) dst[2 * p + 1] = v[m].z;
+            sink(p, v[m].x, v[m].z);
             done |= 1u << m;
           }
         }
@@ -166,6 +165,95 @@ __device__ __forceinline__ bool poll_ll(const __amdgpu_buffer_rsrc_t& r, uint32_
     }
   }
   return true;
+}
+
+// the same, copying the payloads to dst[0..n)
+template <int AUX>
+__device__ __forceinline__ bool poll_ll(const __amdgpu_buffer_rsrc_t& r, uint32_t soff, uint32_t n, uint32_t epoch,
+                                        uint32_t* dst, int nw, int w0 = 0) {
+  return poll_ll_sink<AUX>(r, soff, n, epoch, nw, w0, [&](uint32_t p, uint32_t x, uint32_t z) {
+    dst[2 * p] = x;
+    if (2 * p + 1 < n) dst[2 * p + 1] = z;
+  });
+}
+
+// Poll the M word pairs of this lane, pair[m] (< 0: none), until each is
+// current (one epoch per pair: the words 2p and 2p+1 < n), leaving their
+// payloads in lo[m], hi[m].  All loads of a round go out before any check.
+// Returns false on the spin limit.
+template <int AUX, int M>
+__device__ __forceinline__ bool poll_lane_pairs(const __amdgpu_buffer_rsrc_t& r, uint32_t soff, const int (&pair)[M],
+                                                uint32_t n, uint32_t epoch, uint32_t (&lo)[M], uint32_t (&hi)[M]) {
+  uint32_t want = 0, done = 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    if (pair[m] >= 0) want |= 1u << m;
+  uint32_t spins = 0;
+  for (;;) {
+    uint4 v[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if ((want & ~done) & (1u << m))
+        v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)pair[m] * 16u, soff, AUX));
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      if ((want & ~done) & (1u << m)) {
+        const bool second = (2u * (uint32_t)pair[m] + 1u < n);
+        if (v[m].y == epoch && (!second || v[m].w == epoch)) {
+          lo[m] = v[m].x;
+          hi[m] = v[m].z;
+          done |= 1u << m;
+        }
+      }
+    }
+    if (__all(done == want)) return true;
+    if (++spins > kSpinLimit) return false;
+  }
+}
+
+// R3: the Q8_1 blocks of the routed h, 16 blocks per wave per round.  Block
+// j is block jb = j % nb_r of slot s = j / nb_r and covers words
+// s*F + 32jb .. +31 (F % 32 == 0); blocks past F are the zero padding.  s
+// comes from a float product: (j + 1/2)/nb_r lies at least 1/(2 nb_r) from an
+// integer and the product is within 2^-23 relative of it, so truncation is
+// exact for j < 2^22.  The wave polls its 16 blocks' words (load m of lane L
+// is word pair (64m + L) % 16 of block 4m + L/16: 1 KiB of consecutive words
+// per load where the blocks are), lands them in `land` at their word index
+// and quantises its blocks from there without waiting for the other waves.
+// Codes go to hqc + 32j, d and s to hqd[j], hqs[j].  Returns false on the
+// spin limit.
+__device__ __forceinline__ int h_block_word(int j, int nb_r, float inv_nbr, int F) {
+  const int s = (int)(((float)j + 0.5f) * inv_nbr);
+  const int jb = j - s * nb_r;
+  return (32 * jb < F) ? s * F + 32 * jb : -1;
+}
+__device__ __forceinline__ bool poll_quantize_h(const __amdgpu_buffer_rsrc_t& r, uint32_t soff, int nblk, int nb_r,
+                                                float inv_nbr, int F, uint32_t n, uint32_t epoch, uint32_t* land,
+                                                uint8_t* hqc, float* hqd, float* hqs, int wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  bool ok = true;
+  for (int j0 = wave * 16; j0 < nblk; j0 += nw * 16) {
+    int pair[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int j = j0 + 4 * m + (lane >> 4);
+      const int w0 = (j < nblk) ? h_block_word(j, nb_r, inv_nbr, F) : -1;
+      pair[m] = (w0 >= 0) ? (w0 >> 1) + (lane & 15) : -1;
+    }
+    uint32_t lo[4] = {0u, 0u, 0u, 0u}, hi[4] = {0u, 0u, 0u, 0u};
+    if (!poll_lane_pairs<kAuxSC1, 4>(r, soff, pair, n, epoch, lo, hi)) ok = false;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (pair[m] >= 0) *reinterpret_cast<uint2*>(land + 2 * pair[m]) = make_uint2(lo[m], hi[m]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    const int nb = min(16, nblk - j0);
+    quantize_q81_groups<4, 1>(nb, reinterpret_cast<const float*>(land),
+                              [&](int j) { return h_block_word(j0 + j, nb_r, inv_nbr, F); },
+                              [&](int j) { return hqc + 32L * (j0 + j); }, hqd + j0, hqs + j0, lane, 64);
+  }
+  return ok;
 }
 
 // ---------------------------------------------------------------- row-dot helpers over LDS-staged rows
@@ -627,26 +715,24 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     const uint32_t ep0 = base + 3u * l, ep1 = ep0 + 1u, ep2 = ep0 + 2u;
     stamp(l, 0);
     bstamp(l, 0);
-    // ================= R1: t of the previous layer, read by every workgroup
-    // (four elements per thread: t as two words of bf16 pairs); the sum of
-    // squares of the new residual is taken on the way
+    // ================= R1: t of the previous layer, read by every workgroup.
+    // Word pair p holds t rows 4p..4p+3 (bf16 pairs); the polling lane adds
+    // them to its residual float4 as soon as they are current and takes the
+    // sum of squares of the new residual on the way
     double ss = 0.0;
     float4* res4 = reinterpret_cast<float4*>(res);
     if (l > 0) {
-      const bool ok = poll_ll<kAuxSC1>(rx, rd_t, g.n_t, ep2 - 3u, xbuf, kPollWaves);
-      if (!ok) s_fail = 1;
-      lds_barrier();
-      if (s_fail) { fail_out(); return; }
-      for (int c = tid; c < H / 4; c += kStackThreads) {
-        const uint2 pr = reinterpret_cast<const uint2*>(xbuf)[c];
-        float4 r = res4[c];
-        r.x = bf16_to_f32(f32_to_bf16(r.x + bf16_to_f32((uint16_t)(pr.x & 0xffffu))));
-        r.y = bf16_to_f32(f32_to_bf16(r.y + bf16_to_f32((uint16_t)(pr.x >> 16))));
-        r.z = bf16_to_f32(f32_to_bf16(r.z + bf16_to_f32((uint16_t)(pr.y & 0xffffu))));
-        r.w = bf16_to_f32(f32_to_bf16(r.w + bf16_to_f32((uint16_t)(pr.y >> 16))));
-        res4[c] = r;
+      const bool ok = poll_ll_sink<kAuxSC1>(rx, rd_t, g.n_t, ep2 - 3u, kPollWaves, 0,
+                                            [&](uint32_t p, uint32_t x, uint32_t z) {
+        float4 r = res4[p];
+        r.x = bf16_to_f32(f32_to_bf16(r.x + bf16_to_f32((uint16_t)(x & 0xffffu))));
+        r.y = bf16_to_f32(f32_to_bf16(r.y + bf16_to_f32((uint16_t)(x >> 16))));
+        r.z = bf16_to_f32(f32_to_bf16(r.z + bf16_to_f32((uint16_t)(z & 0xffffu))));
+        r.w = bf16_to_f32(f32_to_bf16(r.w + bf16_to_f32((uint16_t)(z >> 16))));
+        res4[p] = r;
         ss += sq4_f64(r);
-      }
+      });
+      if (!ok) s_fail = 1;
     } else {
       for (int c = tid; c < H / 4; c += kStackThreads) ss += sq4_f64(res4[c]);
     }
@@ -654,12 +740,13 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     stamp(l, 1);
     bstamp(l, 1);
     if (wave >= kPollWaves) wait_vmem();
-    lds_barrier();
+    // the barrier inside also publishes s_fail and the new residual
+    ss = block_sum_f64(ss, red);
+    if (s_fail) { fail_out(); return; }
     stamp(l, 2);
     bstamp(l, 2);
     if (b == 0 && a.resid_out)
       for (int i = tid; i < H; i += kStackThreads) a.resid_out[(long)l * H + i] = f32_to_bf16(res[i]);
-    ss = block_sum_f64(ss, red);
     const double rinv = 1.0 / sqrt(ss / (double)H + (double)a.eps);
     for (int c = tid; c < H / 4; c += kStackThreads) {
       const float4 r = res4[c];
@@ -673,12 +760,13 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     }
     lds_barrier();
     bstamp(l, 11);
-    quantize_q81_groups<4, 1>(H / 32, xn, [](int j) { return 32 * j; }, [&](int j) { return xqc + 32 * j; }, xqd,
-                              xqs, tid, kStackThreads);
-    lds_barrier();
+    // xq on waves 0..3 while waves 4.. take the router rows, which need xn only
+    if (wave < kPollWaves)
+      quantize_q81_groups<4, 1>(H / 32, xn, [](int j) { return 32 * j; }, [&](int j) { return xqc + 32 * j; }, xqd,
+                                xqs, tid, 64 * kPollWaves);
     bstamp(l, 12);
     // router rows (fp64 dot of fp32 products), one wave per row
-    for (int j = wave; j < g.RR; j += kStackWaves) {
+    for (int j = wave - kPollWaves; j >= 0 && j < g.RR; j += kStackWaves - kPollWaves) {
       const int r = b + j * g.G;
       const bool real = (r < E) || (r == E && has_sg);
       if (!real) break;
@@ -699,6 +787,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       if ((tid & 63) == 0) ll_store_rep<kRepLg>(rx, x_lg, rb_lg, r, __float_as_uint((float)acc), ep0);
     }
     bstamp(l, 3);
+    lds_barrier();
     // shared gate/up rows -> hs (word k*F + f of the h exchange)
     if (nsr > 0) {
       const ActLds act{xqc, xqd, xqs};
@@ -717,13 +806,37 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     stamp(l, 3);
     bstamp(l, 4);
     {
-      const bool ok = poll_ll<kAuxSC1>(rx, rd_lg, g.n_lg, ep0, xbuf, kPollWaves);
-      if (!ok) s_fail = 1;
-      lds_barrier();
-      if (s_fail) { fail_out(); return; }
-      bstamp(l, 13);
-      topk_candidates(reinterpret_cast<const float*>(xbuf), E, k, wave, keys, cand);
-      lds_barrier();
+      if (E <= 256) {
+        // wave w < 4 polls the logits of its own 64 experts (word pairs
+        // 32w .. 32w+31; pair 128, the shared-gate logit after 256 experts,
+        // on lane 32 of wave 0), lands them and ranks them right away
+        if (wave < kPollWaves) {
+          const int lane = tid & 63;
+          const int p = 32 * wave + (lane & 31) + 128 * (lane >> 5);
+          const int pair[1] = {(uint32_t)p < ((g.n_lg + 1u) >> 1) ? p : -1};
+          uint32_t lo[1] = {0u}, hi[1] = {0u};
+          if (!poll_lane_pairs<kAuxSC1, 1>(rx, rd_lg, pair, g.n_lg, ep0, lo, hi)) s_fail = 1;
+          if (pair[0] >= 0) {
+            xbuf[2 * p] = lo[0];
+            if (2 * p + 1 < g.n_lg) xbuf[2 * p + 1] = hi[0];
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+          bstamp(l, 13);
+          topk_candidates(reinterpret_cast<const float*>(xbuf), E, k, wave, keys, cand);
+        }
+        lds_barrier();
+        if (s_fail) { fail_out(); return; }
+      } else {
+        const bool ok = poll_ll<kAuxSC1>(rx, rd_lg, g.n_lg, ep0, xbuf, kPollWaves);
+        if (!ok) s_fail = 1;
+        lds_barrier();
+        if (s_fail) { fail_out(); return; }
+        bstamp(l, 13);
+        topk_candidates(reinterpret_cast<const float*>(xbuf), E, k, wave, keys, cand);
+        lds_barrier();
+      }
       if (wave == 0 && rank_candidates(reinterpret_cast<const float*>(xbuf), E, k, has_sg, cand, sel, lgsel))
         s_fail = 1;
       lds_barrier();
@@ -807,33 +920,20 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     stamp(l, 6);
     bstamp(l, 7);
     {
-      const int nb_r = g.Kp / 32;
       // the down rows waves 4..7 requested in phase B have had the whole of
-      // phase B to land, so every wave polls
-      const bool ok = poll_ll<kAuxSC1>(rx, rd_h, (uint32_t)(k * F), ep1, xbuf, kStackWaves);
-      if (!ok) s_fail = 1;
-      lds_barrier();
-      if (s_fail) { fail_out(); return; }
+      // phase B to land, so every wave polls; each wave quantises its own
+      // blocks as soon as they are current
+      if (!poll_quantize_h(rx, rd_h, k * (g.Kp / 32), g.Kp / 32, inv_nbr, F, (uint32_t)(k * F), ep1, xbuf, hqc, hqd,
+                           hqs, wave, kStackWaves))
+        s_fail = 1;
       bstamp(l, 14);
-      // block j is block jb = j % nb_r of slot s = j / nb_r and covers
-      // h[s*F + 32jb ..]; blocks past F are the zero padding.  s comes from a
-      // float product: (j + 1/2)/nb_r lies at least 1/(2 nb_r) from an integer
-      // and the product is within 2^-23 relative of it, so truncation is exact
-      // for j < 2^22.
-      const float* hf = reinterpret_cast<const float*>(xbuf);
-      quantize_q81_groups<4, 1>(k * nb_r, hf,
-                                [&](int j) -> int {
-                                  const int s = (int)(((float)j + 0.5f) * inv_nbr);
-                                  const int jb = j - s * nb_r;
-                                  return (32 * jb < F) ? s * F + 32 * jb : -1;
-                                },
-                                [&](int j) { return hqc + 32 * j; }, hqd, hqs, tid, kStackThreads);
     }
     // ================= phase C: down rows of all slots + shared, combine
     stamp(l, 7);
     bstamp(l, 8);
     if (wave >= kPollWaves) wait_vmem();
     lds_barrier();
+    if (s_fail) { fail_out(); return; }
     stamp(l, 8);
     bstamp(l, 9);
     if (nrd > 0) {
