@@ -19,6 +19,8 @@
 // -- in one step and of its second half, the high nibbles, in the next), which
 // leaves the dot product unchanged and lets each lane decode 8 contiguous
 // bytes.
+#include <algorithm>
+
 #include "../../include/moe_decode.h"
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -60,14 +62,16 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* ids, int n, int k
   __shared__ int s_cnt[MOE_MAX_EXPERTS];
   __shared__ int s_off[MOE_MAX_EXPERTS];
   __shared__ int tmp[1024];
+  __shared__ int s_ids[MOE_MAX_BATCH * MOE_MAX_TOPK];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
+  const int P = n * k;
   for (int e = tid; e < E; e += 1024) s_cnt[e] = 0;
+  for (int p = tid; p < P; p += 1024) s_ids[p] = ids[p];
   if (tid == 0) s_bad = 0;
   __syncthreads();
-  const int P = n * k;
   for (int p = tid; p < P; p += 1024) {
-    const int e = ids[p];
+    const int e = s_ids[p];
     if (e < 0 || e >= E) s_bad = 1;
     else atomicAdd(&s_cnt[e], 1);
   }
@@ -84,11 +88,11 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* ids, int n, int k
   if (tid == 1023) nd[0] = pos + (c > 0 ? 1 : 0);
   __syncthreads();
   for (int p = tid; p < P; p += 1024) {
-    const int e = ids[p];
+    const int e = s_ids[p];
     if (e < 0 || e >= E) continue;
     const int t = p / k;
     int rank = 0;
-    for (int q = 0; q < t * k; ++q) rank += (ids[q] == e) ? 1 : 0;
+    for (int q = 0; q < t * k; ++q) rank += (s_ids[q] == e) ? 1 : 0;
     members[s_off[e] + rank] = p;
   }
   if (tid == 0) err[0] = s_bad;
@@ -167,10 +171,11 @@ __device__ __forceinline__ v4f mfma_bf16(v8s a, v8s b, v4f c) {
 // One wave: rows r0.. (nr <= 16 valid) of one or two matrices (rowsA, rowsB
 // may be null) of TYPE with K elements, against the activations of up to
 // MOE_MAX_BATCH members (act(m) -> fp32 pointer of K_act values, K_act <= K;
-// elements past K_act are zero).  accA/accB [kMaxTiles] receive D tiles.
+// elements past K_act are zero), over the 64-element groups gg0, gg0 + ggs,
+// ... of K.  accA/accB [kMaxTiles] receive D tiles.
 template <int TYPE, class Act>
 __device__ __forceinline__ void wave_mfma(const uint8_t* rowsA, const uint8_t* rowsB, long rb, int nr, int K, int ne,
-                                          int K_act, Act act, v4f* accA, v4f* accB) {
+                                          int K_act, Act act, v4f* accA, v4f* accB, int gg0, int ggs) {
   const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
   const int ntiles = (ne + 15) >> 4;
 #pragma unroll
@@ -181,7 +186,7 @@ __device__ __forceinline__ void wave_mfma(const uint8_t* rowsA, const uint8_t* r
   const bool rv = r < nr;
   const uint8_t* ra = rowsA + (long)(rv ? r : 0) * rb;
   const uint8_t* rbp = rowsB ? rowsB + (long)(rv ? r : 0) * rb : nullptr;
-  for (int gg = 0; gg < K / 64; ++gg) {   // K-quant rows: 4 groups per superblock
+  for (int gg = gg0; gg < K / 64; gg += ggs) {   // K-quant rows: 4 groups per superblock
     v8s alo, ahi, blo, bhi;
     weights_bf16<TYPE>(ra, gg, q, alo, ahi);
     if (!rv) alo = ahi = v8s{0, 0, 0, 0, 0, 0, 0, 0};
@@ -202,6 +207,36 @@ __device__ __forceinline__ void wave_mfma(const uint8_t* rowsA, const uint8_t* r
         accB[j] = mfma_bf16(blo, xlo, accB[j]);
         accB[j] = mfma_bf16(bhi, xhi, accB[j]);
       }
+    }
+  }
+}
+
+// The kBWaves waves of a block hold partial tiles over disjoint K groups:
+// wave 0 ends with their sums, added in wave order (buf: kBWaves * kMaxTiles
+// * 2 * 64 v4f of LDS).  Every wave of the block must call it.
+constexpr size_t kBigLds = sizeof(v4f) * kBWaves * kMaxTiles * 2 * 64;
+__device__ __forceinline__ void reduce_waves(v4f* accA, v4f* accB, int ntiles, bool two, v4f* buf) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < kMaxTiles; ++j) {
+    if (j < ntiles) {
+      buf[((wave * kMaxTiles + j) * 2 + 0) * 64 + lane] = accA[j];
+      if (two) buf[((wave * kMaxTiles + j) * 2 + 1) * 64 + lane] = accB[j];
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int j = 0; j < kMaxTiles; ++j) {
+    if (j < ntiles) {
+      v4f sa = buf[(j * 2 + 0) * 64 + lane], sb = v4f{0.f, 0.f, 0.f, 0.f};
+      if (two) sb = buf[(j * 2 + 1) * 64 + lane];
+      for (int w = 1; w < kBWaves; ++w) {
+        sa += buf[((w * kMaxTiles + j) * 2 + 0) * 64 + lane];
+        if (two) sb += buf[((w * kMaxTiles + j) * 2 + 1) * 64 + lane];
+      }
+      accA[j] = sa;
+      accB[j] = sb;
     }
   }
 }
@@ -256,6 +291,107 @@ __device__ __forceinline__ void member(const BGroupArgs& a, const Group& gp, int
   s = p - t * a.k;
 }
 
+// ---------------------------------------------------------------- integer rows for several tokens
+// A small group's members share the expert's rows: each task's weights are
+// read once and dotted with up to kMulti members' Q8_1 activations.  Each
+// member's value is the single-token row_task value, summed in the same
+// order (task t, t+64, ..., then the lane-group tree), so it is bit-identical
+// to running the rows once per member.
+constexpr int kMulti = 4;
+constexpr int kBSmallPerWave = 4;                       // rows per wave, small groups
+constexpr int kBSmallRows = kBSmallPerWave * kBWaves;   // rows per block, small groups (gate/up)
+static_assert(kBRowsPerBlock % kBSmallRows == 0, "a big group's block spans whole small-group blocks");
+constexpr int kBSmallPerBig = kBRowsPerBlock / kBSmallRows;
+
+template <int TYPE>
+__device__ __forceinline__ void row_task_multi(const uint8_t* row, int t, const ActLds* acts, int ne, double v[kMulti]) {
+  if (TYPE == MOE_TYPE_Q8_0) {
+    float d;
+    uint32_t w[8];
+    q80_load(row, t, d, w);
+#pragma unroll
+    for (int m = 0; m < kMulti; ++m) {
+      v[m] = 0.0;
+      if (m < ne) {
+        uint32_t av[8];
+        lds_load8(acts[m].codes + 32 * t, av);
+        v[m] = (double)d * (double)acts[m].d[t] * (double)q8_block_dot(w, av);
+      }
+    }
+    return;
+  }
+  const int b = t >> 2, g = t & 3;
+  const uint8_t* blk = row + (long)b * block_bytes(TYPE);
+  const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+  uint32_t qs[8], qh[8];
+  if (TYPE == MOE_TYPE_Q5_K) {
+    lds_load8(blk + 16, qh);
+    lds_load8(blk + 48 + 32 * g, qs);
+  } else {
+    lds_load8(blk + 16 + 32 * g, qs);
+  }
+  int sclo, mlo, schi, mhi;
+  kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g, sclo, mlo);
+  kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g + 1, schi, mhi);
+  const double d = (double)f16_to_f32(hdr.x);
+  const double dmin = (double)f16_to_f32(hdr.x >> 16);
+  const int jlo = 8 * b + 2 * g;
+#pragma unroll
+  for (int m = 0; m < kMulti; ++m) {
+    v[m] = 0.0;
+    if (m < ne) {
+      uint32_t alo[8], ahi[8];
+      lds_load8(acts[m].codes + 32 * jlo, alo);
+      lds_load8(acts[m].codes + 32 * (jlo + 1), ahi);
+      int Dlo, Dhi;
+      kquant_group_dots<TYPE == MOE_TYPE_Q5_K>(qs, qh, g, alo, ahi, Dlo, Dhi);
+      const double t1 = d * (double)sclo * (double)acts[m].d[jlo] * (double)Dlo;
+      const double t2 = dmin * (double)mlo * (double)acts[m].s[jlo];
+      const double t3 = d * (double)schi * (double)acts[m].d[jlo + 1] * (double)Dhi;
+      const double t4 = dmin * (double)mhi * (double)acts[m].s[jlo + 1];
+      v[m] = ((t1 - t2) + t3) - t4;
+    }
+  }
+}
+
+// rows_dot for ne <= kMulti activation sets (ne wave-uniform): rowfn(r) gives
+// row r's bytes; out[r * kMulti + m] receives row r against set m.
+template <int TYPE, class RowFn>
+__device__ __forceinline__ void rows_dot_multi(int nrows, int T, RowFn rowfn, const ActLds* acts, int ne, double* out,
+                                               int wave, int nw) {
+  int TP = 1;
+  while (TP < T && TP < 64) TP <<= 1;
+  const int rpi = 64 / TP;
+  const int lane = threadIdx.x & 63;
+  const int rl = lane / TP, t0 = lane - rl * TP;
+  const int step = nw * rpi;
+  const int tt = (t0 < T) ? t0 : 0;
+  for (int r0 = wave * rpi; r0 < nrows; r0 += step) {
+    const int ra = r0 + rl;
+    const uint8_t* row = rowfn(ra < nrows ? ra : nrows - 1);
+    double v[kMulti];
+    row_task_multi<TYPE>(row, tt, acts, ne, v);
+    if (t0 >= T) {
+#pragma unroll
+      for (int m = 0; m < kMulti; ++m) v[m] = 0.0;
+    }
+    for (int t = t0 + 64; t < T; t += 64) {
+      double w[kMulti];
+      row_task_multi<TYPE>(row, t, acts, ne, w);
+#pragma unroll
+      for (int m = 0; m < kMulti; ++m) v[m] += w[m];
+    }
+#pragma unroll
+    for (int m = 0; m < kMulti; ++m)
+      if (m < ne) v[m] = group_sum_f64(v[m], TP);
+    if (t0 == 0 && ra < nrows) {
+#pragma unroll
+      for (int m = 0; m < kMulti; ++m)
+        if (m < ne) out[ra * kMulti + m] = v[m];
+    }
+  }
+}
+
 // Q8_1 activations of `nt` tokens unpacked into LDS (codes [nt][K], d/s [nt][K/32])
 __device__ __forceinline__ void stage_xq(const uint8_t* xq_all, const int* toks, int nt, int K, uint8_t* codes,
                                          float* dq, float* sq) {
@@ -282,16 +418,18 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
   Group gp;
   if (!block_group(a, gp)) return;
   const int Fx = gp.shared ? a.Fs : a.F;
-  const int fb = blockIdx.y * kBRowsPerBlock;
+  const bool big = gp.ne >= a.gmin;
+  // kBSmallRows rows per block: a small group's waves take kBSmallPerWave of
+  // them each; a big group's waves split K over the block's 16 rows
+  const int fb = blockIdx.y * kBSmallRows;
   if (fb >= Fx) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int f0 = fb + wave * kBRows;
-  const int nr = max(0, min(kBRows, Fx - f0));
   const int H = a.H;
-  const bool big = gp.ne >= a.gmin;
   if (big) {
     v4f ag[kMaxTiles], au[kMaxTiles];
-    if (nr > 0) {
+    const int f0 = fb;
+    const int nr = min(kBRows, Fx - f0);
+    {
       auto act = [&](int m) {
         int t, s;
         member(a, gp, m, t, s);
@@ -299,13 +437,15 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
       };
       if (gp.shared) {
         const long rb = row_bytes(ST, H);
-        wave_mfma<ST>(a.sgate + f0 * rb, a.sup + f0 * rb, rb, nr, H, gp.ne, H, act, ag, au);
+        wave_mfma<ST>(a.sgate + f0 * rb, a.sup + f0 * rb, rb, nr, H, gp.ne, H, act, ag, au, wave, kBWaves);
       } else {
         const long rb = row_bytes(MOE_TYPE_Q4_K, H);
         const long base = ((long)gp.e * a.F + f0) * rb;
-        wave_mfma<MOE_TYPE_Q4_K>(a.gate + base, a.up + base, rb, nr, H, gp.ne, H, act, ag, au);
+        wave_mfma<MOE_TYPE_Q4_K>(a.gate + base, a.up + base, rb, nr, H, gp.ne, H, act, ag, au, wave, kBWaves);
       }
       const int ntiles = (gp.ne + 15) >> 4;
+      reduce_waves(ag, au, ntiles, true, reinterpret_cast<v4f*>(smem));
+      if (wave != 0) return;
 #pragma unroll
       for (int j = 0; j < kMaxTiles; ++j) {
         if (j >= ntiles) break;
@@ -326,7 +466,8 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
     }
     return;
   }
-  // a small group: the integer path, token by token
+  // a small group: the integer path, kBSmallPerWave rows of gate and up per
+  // wave, all members at once
   int* toks = reinterpret_cast<int*>(smem);
   int* slots = toks + MOE_MAX_BATCH;
   uint8_t* codes = smem + 2 * sizeof(int) * MOE_MAX_BATCH;
@@ -343,32 +484,46 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
   __syncthreads();
   stage_xq(a.xq, toks, gp.ne, H, codes, dq, sq);
   __syncthreads();
-  if (nr > 0) {
-    double* pw = part + wave * 2 * kBRows;
-    for (int m = 0; m < gp.ne; ++m) {
-      const ActLds act{codes + (long)m * H, dq + m * (H / 32), sq + m * (H / 32)};
+  const int fs = fb + wave * kBSmallPerWave;
+  const int ns = max(0, min(kBSmallPerWave, Fx - fs));
+  if (ns > 0) {
+    double* pw = part + wave * 2 * kBSmallPerWave * kMulti;
+    for (int m0 = 0; m0 < gp.ne; m0 += kMulti) {
+      const int nm = min(kMulti, gp.ne - m0);
+      ActLds acts[kMulti];
+#pragma unroll
+      for (int i = 0; i < kMulti; ++i) {
+        const int m = m0 + min(i, nm - 1);
+        acts[i] = ActLds{codes + (long)m * H, dq + m * (H / 32), sq + m * (H / 32)};
+      }
       if (gp.shared) {
         const long rb = row_bytes(ST, H);
-        rows_dot<ST>(2 * nr, tasks_per_row(ST, H), [&](int r) {
-          return RowRef{(r < nr) ? a.sgate + (f0 + r) * rb : a.sup + (f0 + r - nr) * rb, act};
-        }, pw, 0, 1);
+        rows_dot_multi<ST>(2 * ns, tasks_per_row(ST, H), [&](int r) {
+          return (r < ns) ? a.sgate + (fs + r) * rb : a.sup + (fs + r - ns) * rb;
+        }, acts, nm, pw, 0, 1);
       } else {
         const long rb = row_bytes(MOE_TYPE_Q4_K, H);
-        const long base = ((long)gp.e * a.F + f0) * rb;
-        rows_dot<MOE_TYPE_Q4_K>(2 * nr, tasks_per_row(MOE_TYPE_Q4_K, H), [&](int r) {
-          return RowRef{(r < nr) ? a.gate + base + r * rb : a.up + base + (r - nr) * rb, act};
-        }, pw, 0, 1);
+        const long base = ((long)gp.e * a.F + fs) * rb;
+        rows_dot_multi<MOE_TYPE_Q4_K>(2 * ns, tasks_per_row(MOE_TYPE_Q4_K, H), [&](int r) {
+          return (r < ns) ? a.gate + base + r * rb : a.up + base + (r - ns) * rb;
+        }, acts, nm, pw, 0, 1);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-      if (lane < nr) {
-        const float g = (float)pw[lane], u = (float)pw[nr + lane];
-        const float hv = (float)(silu_f64((double)g) * (double)u);
-        if (gp.shared) a.hs[(long)toks[m] * a.Fs + f0 + lane] = hv;
-        else a.h[((long)toks[m] * a.k + slots[m]) * a.F + f0 + lane] = hv;
+      if (lane < ns * kMulti) {
+        const int r = lane / kMulti, i = lane - r * kMulti;
+        if (i < nm) {
+          const float g = (float)pw[r * kMulti + i], u = (float)pw[(ns + r) * kMulti + i];
+          const float hv = (float)(silu_f64((double)g) * (double)u);
+          const int m = m0 + i;
+          if (gp.shared) a.hs[(long)toks[m] * a.Fs + fs + r] = hv;
+          else a.h[((long)toks[m] * a.k + slots[m]) * a.F + fs + r] = hv;
+        }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     }
   }
 }
@@ -381,7 +536,13 @@ __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
   if (!block_group(a, gp)) return;
   const int H = a.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int i0 = blockIdx.y * kBRowsPerBlock + wave * kBRows;
+  const bool big = gp.ne >= a.gmin;
+  // blockIdx.y counts kBSmallRows-row chunks: a big group's block takes one
+  // (its waves split K), a small group's block kBSmallPerBig of them (the
+  // other blocks of its span leave at once), kBRows rows per wave
+  if (!big && (blockIdx.y % kBSmallPerBig)) return;
+  const int i0 = big ? blockIdx.y * kBSmallRows : (blockIdx.y / kBSmallPerBig) * kBRowsPerBlock + wave * kBRows;
+  if (big && i0 >= H) return;
   const int nr = max(0, min(kBRows, H - i0));
   const int Fx = gp.shared ? a.Fs : a.F;
   const int Kx = gp.shared ? a.Kps : a.Kp;
@@ -390,18 +551,20 @@ __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
     member(a, gp, m, t, s);
     return gp.shared ? a.hs + (long)t * a.Fs : a.h + ((long)t * a.k + s) * a.F;
   };
-  const bool big = gp.ne >= a.gmin;
   if (big) {
     v4f ay[kMaxTiles], dummy[kMaxTiles];
-    if (nr > 0) {
+    {
       if (gp.shared) {
         const long rb = row_bytes(ST, Kx);
-        wave_mfma<ST>(a.sdown + i0 * rb, nullptr, rb, nr, Kx, gp.ne, Fx, hsrc, ay, dummy);
+        wave_mfma<ST>(a.sdown + i0 * rb, nullptr, rb, nr, Kx, gp.ne, Fx, hsrc, ay, dummy, wave, kBWaves);
       } else {
         const long rb = row_bytes(DT, Kx);
-        wave_mfma<DT>(a.down + ((long)gp.e * H + i0) * rb, nullptr, rb, nr, Kx, gp.ne, Fx, hsrc, ay, dummy);
+        wave_mfma<DT>(a.down + ((long)gp.e * H + i0) * rb, nullptr, rb, nr, Kx, gp.ne, Fx, hsrc, ay, dummy, wave,
+                      kBWaves);
       }
       const int ntiles = (gp.ne + 15) >> 4;
+      reduce_waves(ay, dummy, ntiles, false, reinterpret_cast<v4f*>(smem));
+      if (wave != 0) return;
 #pragma unroll
       for (int j = 0; j < kMaxTiles; ++j) {
         if (j >= ntiles) break;
@@ -442,26 +605,37 @@ __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
   }, [&](int j) { return codes + 32L * j; }, dq, sq, threadIdx.x, kBThreads);
   __syncthreads();
   if (nr > 0) {
-    double* pw = part + wave * kBRows;
-    for (int m = 0; m < gp.ne; ++m) {
-      const ActLds act{codes + (long)m * Kx, dq + m * nb, sq + m * nb};
+    double* pw = part + wave * kBRows * kMulti;
+    for (int m0 = 0; m0 < gp.ne; m0 += kMulti) {
+      const int nm = min(kMulti, gp.ne - m0);
+      ActLds acts[kMulti];
+#pragma unroll
+      for (int i = 0; i < kMulti; ++i) {
+        const int m = m0 + min(i, nm - 1);
+        acts[i] = ActLds{codes + (long)m * Kx, dq + m * nb, sq + m * nb};
+      }
       if (gp.shared) {
         const long rb = row_bytes(ST, Kx);
-        rows_dot<ST>(nr, tasks_per_row(ST, Kx), [&](int r) { return RowRef{a.sdown + (i0 + r) * rb, act}; }, pw, 0, 1);
+        rows_dot_multi<ST>(nr, tasks_per_row(ST, Kx), [&](int r) { return a.sdown + (i0 + r) * rb; }, acts, nm, pw, 0,
+                           1);
       } else {
         const long rb = row_bytes(DT, Kx);
         const uint8_t* base = a.down + ((long)gp.e * H + i0) * rb;
-        rows_dot<DT>(nr, tasks_per_row(DT, Kx), [&](int r) { return RowRef{base + r * rb, act}; }, pw, 0, 1);
+        rows_dot_multi<DT>(nr, tasks_per_row(DT, Kx), [&](int r) { return base + r * rb; }, acts, nm, pw, 0, 1);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-      if (lane < nr) {
-        const float yv = (float)pw[lane];
-        if (gp.shared) a.ys[(long)toks[m] * H + i0 + lane] = yv;
-        else a.y[((long)toks[m] * a.k + slots[m]) * H + i0 + lane] = yv;
+      for (int o = lane; o < nr * nm; o += 64) {
+        const int r = o / nm, i = o - r * nm;
+        const float yv = (float)pw[r * kMulti + i];
+        const int m = m0 + i;
+        if (gp.shared) a.ys[(long)toks[m] * H + i0 + r] = yv;
+        else a.y[((long)toks[m] * a.k + slots[m]) * H + i0 + r] = yv;
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     }
   }
 }
@@ -513,7 +687,7 @@ BatchWs batch_ws_layout(const moe_layer_desc* d, int n) {
 
 static size_t int_path_lds(int ne_max, int K) {
   return 2 * sizeof(int) * MOE_MAX_BATCH + (size_t)ne_max * K + 8 * (size_t)ne_max * (K / 32) + 16 +
-         sizeof(double) * 2 * kBRows * kBWaves;
+         sizeof(double) * kMulti * 2 * kBRows * kBWaves;
 }
 
 int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const float* xn, const void* xq,
@@ -559,15 +733,15 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   const int ngroups = min(E, n * k) + has_sg;
   const int small = gmin - 1;   // largest group on the integer path
   const int fmax = max(F, Fs);
-  const dim3 ggu(ngroups, (fmax + kBRowsPerBlock - 1) / kBRowsPerBlock);
-  const size_t lds_gu = small > 0 ? int_path_lds(small > n ? n : small, H) : 0;
+  const dim3 ggu(ngroups, (fmax + kBSmallRows - 1) / kBSmallRows);
+  const size_t lds_gu = std::max(small > 0 ? int_path_lds(small > n ? n : small, H) : (size_t)0, kBigLds);
   const void* fgu = (st_type == MOE_TYPE_Q8_0) ? (const void*)k_bgu<MOE_TYPE_Q8_0> : (const void*)k_bgu<MOE_TYPE_Q4_K>;
   if (hipFuncSetAttribute(fgu, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu) != hipSuccess) return MOE_ERR_HIP;
   void* args[] = {&a};
   if (hipLaunchKernel(fgu, ggu, dim3(kBThreads), args, lds_gu, st) != hipSuccess) return MOE_ERR_HIP;
   const int kmax = max(a.Kp, a.Kps);
-  const dim3 gdn(ngroups, (H + kBRowsPerBlock - 1) / kBRowsPerBlock);
-  const size_t lds_dn = small > 0 ? int_path_lds(small > n ? n : small, kmax) : 0;
+  const dim3 gdn(ngroups, (H + kBSmallRows - 1) / kBSmallRows);
+  const size_t lds_dn = std::max(small > 0 ? int_path_lds(small > n ? n : small, kmax) : (size_t)0, kBigLds);
   const void* fdn;
   if (d->down_type == MOE_TYPE_Q5_K)
     fdn = (st_type == MOE_TYPE_Q8_0) ? (const void*)k_bdn<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0>

@@ -104,6 +104,7 @@ __device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* id
     const int e = lane + 64 * j;
     key[j] = (e < E) ? topk_key(logits[e], e) : 0ull;
   }
+  int my_id = 0;   // lane s < k: the id of slot s
   for (int s = 0; s < k; ++s) {
     unsigned long long best = 0ull;
 #pragma unroll
@@ -112,59 +113,90 @@ __device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* id
 #pragma unroll
     for (int j = 0; j < kTopkPerLane; ++j)
       if (key[j] == wbest) key[j] = 0ull;
-    if (lane == 0) ids_out[s] = (int32_t)(0xffffffffu - (uint32_t)(wbest & 0xffffffffull));
+    if (lane == s) my_id = (int32_t)(0xffffffffu - (uint32_t)(wbest & 0xffffffffull));
   }
-  if (lane == 0) {
-    // softmax over the selected logits, shifted by the largest (slot 0), fp64
-    const double m = (double)logits[ids_out[0]];
-    double sum = 0.0;
-    for (int s = 0; s < k; ++s) sum += exp((double)logits[ids_out[s]] - m);
-    for (int s = 0; s < k; ++s) w_out[s] = (float)(exp((double)logits[ids_out[s]] - m) / sum);
+  // softmax over the selected logits, shifted by the largest (slot 0), fp64:
+  // lane s takes slot s's exponential, every lane sums them in slot order
+  const double m = (double)logits[__shfl(my_id, 0)];
+  const double ex = (lane < k) ? exp((double)logits[my_id] - m) : 0.0;
+  double sum = 0.0;
+  for (int s = 0; s < k; ++s) sum += __shfl(ex, s);
+  if (lane < k) {
+    ids_out[lane] = my_id;
+    w_out[lane] = (float)(ex / sum);
   }
 }
 
-// grid (nblk, n_tok): each wave computes one row (router row e < E, or the
-// shared-gate row e == E).  The last workgroup to finish (a wrapping atomic
-// increment returns nblk-1 to it and leaves 0 behind) selects.
+// grid (nrows, ceil(n_tok / kRouterTok)): workgroup x computes row x (router
+// row e < E, or the shared-gate row e == E) for up to kRouterTok tokens, so a
+// row is read once per token group; its waves take interleaved quarters of
+// the row and their fp64 partial sums are added in wave order.  The last
+// workgroup of a token group to finish (a wrapping atomic increment returns
+// nrows-1 to it and leaves 0 behind) selects for the group's tokens, one
+// token per wave at a time.
 __global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn, const float* W, const float* wsg,
-                                                                 int H, int E, int k, float* logits, float* user_logits,
-                                                                 int32_t* ids, float* wts, float* sg_out,
-                                                                 unsigned* counters) {
+                                                                 int n_tok, int H, int E, int k, float* logits,
+                                                                 float* user_logits, int32_t* ids, float* wts,
+                                                                 float* sg_out, unsigned* counters) {
+  constexpr int kW = kRouterThreads / 64;
+  __shared__ double part[kW][kRouterTok];
   const int logits_stride = E + 1;
-  const int tok = blockIdx.y;
+  const int tg = blockIdx.y;
+  const int t0 = tg * kRouterTok;
+  const int nt = min(kRouterTok, n_tok - t0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nrows = E + (wsg ? 1 : 0);
-  const int row = blockIdx.x * (kRouterThreads / 64) + wave;
-  const float* x = xn + (long)tok * H;
-  float* lg = logits + (long)tok * logits_stride;
-  if (row < nrows) {
+  const int row = blockIdx.x;
+  {
     const float* wr = (row < E) ? W + (long)row * H : wsg;
-    double acc = 0.0;
-    for (int i = lane * 4; i < H; i += 256) {
+    double acc[kRouterTok];
+#pragma unroll
+    for (int t = 0; t < kRouterTok; ++t) acc[t] = 0.0;
+    for (int i = (wave * 64 + lane) * 4; i < H; i += 256 * kW) {
       const float4 a = *reinterpret_cast<const float4*>(wr + i);
-      const float4 b = *reinterpret_cast<const float4*>(x + i);
-      acc += (double)a.x * (double)b.x;
-      acc += (double)a.y * (double)b.y;
-      acc += (double)a.z * (double)b.z;
-      acc += (double)a.w * (double)b.w;
+#pragma unroll
+      for (int t = 0; t < kRouterTok; ++t) {
+        if (t < nt) {
+          const float4 b = *reinterpret_cast<const float4*>(xn + (long)(t0 + t) * H + i);
+          acc[t] += (double)a.x * (double)b.x;
+          acc[t] += (double)a.y * (double)b.y;
+          acc[t] += (double)a.z * (double)b.z;
+          acc[t] += (double)a.w * (double)b.w;
+        }
+      }
     }
-    acc = wave_sum_f64(acc);
-    if (lane == 0) lg[row] = (float)acc;
+#pragma unroll
+    for (int t = 0; t < kRouterTok; ++t) {
+      if (t < nt) {
+        const double v = wave_sum_f64(acc[t]);
+        if (lane == 0) part[wave][t] = v;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < nt) {
+      const int t = threadIdx.x;
+      double v = part[0][t];
+      for (int w = 1; w < kW; ++w) v += part[w][t];
+      logits[(long)(t0 + t) * logits_stride + row] = (float)v;
+    }
   }
   __shared__ int is_last;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = __builtin_amdgcn_atomic_inc32(counters + tok, gridDim.x - 1, __ATOMIC_ACQ_REL, "agent");
+    const unsigned old = __builtin_amdgcn_atomic_inc32(counters + tg, gridDim.x - 1, __ATOMIC_ACQ_REL, "agent");
     is_last = (old == gridDim.x - 1);
   }
   __syncthreads();
   if (!is_last) return;
-  if (wave == 0) {
-    wave_topk_softmax(lg, E, k, ids + (long)tok * k, wts + (long)tok * k);
-    if (lane == 0 && sg_out) sg_out[tok] = wsg ? (float)sigmoid_f64((double)lg[E]) : 0.0f;
-  } else if (user_logits) {
-    for (int e = threadIdx.x - 64; e < E; e += kRouterThreads - 64) user_logits[(long)tok * E + e] = lg[e];
+  for (int t = wave; t < nt; t += kRouterThreads / 64) {
+    const float* lg = logits + (long)(t0 + t) * logits_stride;
+    wave_topk_softmax(lg, E, k, ids + (long)(t0 + t) * k, wts + (long)(t0 + t) * k);
+    if (lane == 0 && sg_out) sg_out[t0 + t] = wsg ? (float)sigmoid_f64((double)lg[E]) : 0.0f;
   }
+  if (user_logits)
+    for (int i = threadIdx.x; i < nt * E; i += kRouterThreads) {
+      const int t = i / E, e = i - t * E;
+      user_logits[(long)(t0 + t) * E + e] = logits[(long)(t0 + t) * logits_stride + e];
+    }
 }
 
 // =====================================================================
@@ -572,10 +604,8 @@ int launch_quantize(const float* x, int n, void* xq, hipStream_t st) {
 int launch_router(const float* xn, const float* W, const float* wsg, int n_tok, int H, int E, int k, float* logits,
                   float* user_logits, int32_t* ids, float* wts, float* sg, unsigned* counters, hipStream_t st) {
   const int nrows = E + (wsg ? 1 : 0);
-  const int rpb = kRouterThreads / 64;
-  const int nblk = (nrows + rpb - 1) / rpb;
-  hipLaunchKernelGGL(k_router_topk, dim3(nblk, n_tok), dim3(kRouterThreads), 0, st, xn, W, wsg, H, E, k, logits,
-                     user_logits, ids, wts, sg, counters);
+  hipLaunchKernelGGL(k_router_topk, dim3(nrows, (n_tok + kRouterTok - 1) / kRouterTok), dim3(kRouterThreads), 0, st, xn,
+                     W, wsg, n_tok, H, E, k, logits, user_logits, ids, wts, sg, counters);
   return launch_ok();
 }
 
