@@ -300,8 +300,9 @@ __device__ __forceinline__ void member(const BGroupArgs& a, const Group& gp, int
 constexpr int kMulti = 4;
 constexpr int kBSmallPerWave = 4;                       // rows per wave, small groups
 constexpr int kBSmallRows = kBSmallPerWave * kBWaves;   // rows per block, small groups (gate/up)
-static_assert(kBRowsPerBlock % kBSmallRows == 0, "a big group's block spans whole small-group blocks");
-constexpr int kBSmallPerBig = kBRowsPerBlock / kBSmallRows;
+static_assert(kBRows % kBSmallRows == 0, "a big group's block spans whole small-group blocks");
+constexpr int kBigSpan = kBRows / kBSmallRows;              // gate/up: small-group blocks per big-group block
+constexpr int kDnSpan = kBRowsPerBlock / kBRows;            // down: 16-row units per small-group block
 
 template <int TYPE>
 __device__ __forceinline__ void row_task_multi(const uint8_t* row, int t, const ActLds* acts, int ne, double v[kMulti]) {
@@ -419,8 +420,11 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
   if (!block_group(a, gp)) return;
   const int Fx = gp.shared ? a.Fs : a.F;
   const bool big = gp.ne >= a.gmin;
-  // kBSmallRows rows per block: a small group's waves take kBSmallPerWave of
-  // them each; a big group's waves split K over the block's 16 rows
+  // blockIdx.y counts kBSmallRows-row chunks: a small group's block takes
+  // one (kBSmallPerWave rows per wave); a big group's block takes kBigSpan
+  // of them, kBRows rows whose K its waves split (the other blocks of its
+  // span leave at once)
+  if (big && (blockIdx.y % kBigSpan)) return;
   const int fb = blockIdx.y * kBSmallRows;
   if (fb >= Fx) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -537,11 +541,11 @@ __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
   const int H = a.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool big = gp.ne >= a.gmin;
-  // blockIdx.y counts kBSmallRows-row chunks: a big group's block takes one
-  // (its waves split K), a small group's block kBSmallPerBig of them (the
-  // other blocks of its span leave at once), kBRows rows per wave
-  if (!big && (blockIdx.y % kBSmallPerBig)) return;
-  const int i0 = big ? blockIdx.y * kBSmallRows : (blockIdx.y / kBSmallPerBig) * kBRowsPerBlock + wave * kBRows;
+  // blockIdx.y counts kBRows-row chunks: a big group's block takes one (its
+  // waves split K), a small group's block kDnSpan of them, kBRows rows per
+  // wave (the other blocks of its span leave at once)
+  if (!big && (blockIdx.y % kDnSpan)) return;
+  const int i0 = big ? blockIdx.y * kBRows : (blockIdx.y / kDnSpan) * kBRowsPerBlock + wave * kBRows;
   if (big && i0 >= H) return;
   const int nr = max(0, min(kBRows, H - i0));
   const int Fx = gp.shared ? a.Fs : a.F;
@@ -740,7 +744,7 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   void* args[] = {&a};
   if (hipLaunchKernel(fgu, ggu, dim3(kBThreads), args, lds_gu, st) != hipSuccess) return MOE_ERR_HIP;
   const int kmax = max(a.Kp, a.Kps);
-  const dim3 gdn(ngroups, (H + kBSmallRows - 1) / kBSmallRows);
+  const dim3 gdn(ngroups, (H + kBRows - 1) / kBRows);
   const size_t lds_dn = std::max(small > 0 ? int_path_lds(small > n ? n : small, kmax) : (size_t)0, kBigLds);
   const void* fdn;
   if (d->down_type == MOE_TYPE_Q5_K)
