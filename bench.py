@@ -8,7 +8,8 @@ shared) and the 128 token inputs are generated from seeds and resident in HBM
 before timing.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 128] [--warmup 8] [--mode auto|kernels|persistent]
-                  [--variant after|before|both] [--no-cpu] [--calib-copy]
+                  [--variant after|before|both] [--no-cpu] [--no-batch] [--no-requant]
+                  [--no-e128] [--calib-copy] [--trace]
 """
 import argparse
 import json
@@ -40,6 +41,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-batch", action="store_true", help="skip the grouped batch-path leg")
     p.add_argument("--no-requant", action="store_true", help="skip the load-time requantisation leg")
+    p.add_argument("--no-e128", action="store_true", help="skip the 128-expert 48-layer stack leg")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--cpu-seconds-1t", type=float, default=6.0, help="single-thread oracle time")
     p.add_argument("--calib-copy", action="store_true",
@@ -49,10 +51,11 @@ def parse():
 
 
 def algorithmic_bytes(cfg, shared_type, down_type):
-    """Bytes the method must read per token: router, shared-gate row, norm weight,
-    the k selected experts' gate/up/down rows and the shared expert, per layer."""
+    """Bytes the method must read per token: router, norm weight, shared-gate row
+    (with a shared expert), the k selected experts' gate/up/down rows and the
+    shared expert, per layer."""
     H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
-    per = 4 * E * H + 4 * H + 4 * H
+    per = 4 * E * H + 4 * H + (4 * H if Fs else 0)   # router, norm weight, shared-gate row
     per += k * 2 * F * wl.row_bytes(wl.Q4_K, H)
     per += k * H * wl.row_bytes(down_type, wl.pad_k(down_type, F))
     if Fs:
@@ -183,6 +186,30 @@ def batch_leg(q, sizes=(8, 32), group_min=4, iters=30):
         print(f"# batch {n}: {us:.1f} us per layer step, {distinct} distinct experts, "
               f"{out[f'batch{n}']['achieved_GBs']:.0f} GB/s", file=sys.stderr, flush=True)
     return out
+
+
+def e128_leg(q, steps, warmup, repeats):
+    """The 128-expert variant with no shared expert: 48 layers, H 2048, top-8,
+    F 768 (Q4_K gate/up/down), 2-input fold, router rows duplicated in groups of
+    4, a tenth of the 128 tokens all zero.  Timed like the primary stack."""
+    cfg3 = wl.CONFIGS["e128"]
+    stack = Stack(q, cfg3, wl.Q4_K, wl.Q4_K, "auto")
+    us = time_steps(stack, steps, warmup, repeats)
+    med = float(np.median(us))
+    alg = algorithmic_bytes(cfg3, wl.Q4_K, wl.Q4_K)
+    launch = launch_durations(stack, min(64, steps))
+    res = {"workload": f"128-expert variant: {cfg3.layers} layers, H 2048, 128 experts top-8, F 768, no shared "
+                       f"expert, batch 1, {cfg3.tokens} sequential tokens",
+           "us_per_token": med, "us_p10": float(np.percentile(us, 10)), "us_p90": float(np.percentile(us, 90)),
+           "tokens_per_s": 1e6 / med, "alg_bytes_per_token": alg, "achieved_GBs": alg / (med * 1e-6) / 1e9,
+           "us_per_layer": med / cfg3.layers, "launch_us": launch, "kernel_GBs": alg / (launch * 1e-6) / 1e9,
+           "mode": "persistent" if stack.mode == q.MOE_STACK_PERSISTENT else "kernels"}
+    res["frac_of_peak"] = res["kernel_GBs"] / HBM_PEAK_GBS
+    print(f"# e128: generated {cfg3.layers} layers in {stack.gen_s:.1f}s; {med:.1f} us/token "
+          f"({res['achieved_GBs']:.0f} GB/s)", file=sys.stderr, flush=True)
+    del stack
+    torch.cuda.empty_cache()
+    return res
 
 
 def launch_durations(stack, n):
@@ -424,6 +451,7 @@ def main():
         results[name] = res
         print(f"# {name}: {med:.1f} us/token ({res['achieved_GBs']:.0f} GB/s)", file=sys.stderr, flush=True)
     stack, res = primary if primary else (None, results[order[0]])
+    e128 = None if a.no_e128 else e128_leg(q, a.steps, a.warmup, a.repeats)
     batch = None if a.no_batch else batch_leg(q)
     requant = None if a.no_requant else requant_leg(q)
     cpu = None
@@ -452,6 +480,7 @@ def main():
                      "stream_read_GBs": stream_read_gbs(q)},
         "cpu_baseline": cpu,
         "variants": results,
+        "e128": e128,
         "batch": batch,
         "requant": requant,
     }
