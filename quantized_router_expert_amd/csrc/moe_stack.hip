@@ -570,32 +570,42 @@ constexpr int stack_geometry_core(int H, int E, int k, int F, int Fs, int down_t
   return MOE_OK;
 }
 
-// The shape the kernel is also compiled for with every size a constant
-// (hidden 2048, 256 experts, top-8, expert and shared FFN 512, 256
-// workgroups; down/shared types Q4_K/Q4_K and Q5_K/Q8_0): loop bounds, LDS
-// offsets and quotients fold into the code, and the scalar registers that
-// would hold them stay free.
-constexpr int kFixH = 2048, kFixE = 256, kFixK = 8, kFixF = 512, kFixFs = 512, kFixG = 256;
-template <int DT, int ST>
+// The shapes the kernel is also compiled for with every size a constant, on
+// 256 workgroups: shape 1 = hidden 2048, 256 experts, top-8, expert and
+// shared FFN 512 (down/shared types Q4_K/Q4_K and Q5_K/Q8_0); shape 2 =
+// hidden 2048, 128 experts, top-8, expert FFN 768, no shared expert (Q4_K).
+// Loop bounds, LDS offsets and quotients fold into the code, and the scalar
+// registers that would hold them stay free.  Shape 0 takes every size from
+// the arguments.
+struct FixShape {
+  int H, E, k, F, Fs, G;
+};
+constexpr FixShape kFixShapes[3] = {{0, 0, 0, 0, 0, 0}, {2048, 256, 8, 512, 512, 256}, {2048, 128, 8, 768, 0, 256}};
+template <int DT, int ST, int S>
 constexpr StackGeom fixed_geom() {
   StackGeom g = {};
-  stack_geometry_core(kFixH, kFixE, kFixK, kFixF, kFixFs, DT, ST, kFixG, &g);
+  if (S != 0) {
+    constexpr FixShape f = kFixShapes[S];
+    stack_geometry_core(f.H, f.E, f.k, f.F, f.Fs, DT, ST, f.G, &g);
+  }
   return g;
 }
-template <int DT, int ST>
-constexpr StackGeom kFixGeom = fixed_geom<DT, ST>();
+template <int DT, int ST, int S>
+constexpr StackGeom kFixGeom = fixed_geom<DT, ST, S>();
 
 // ---------------------------------------------------------------- the kernel
-template <int DT, int ST, bool FIX>
+template <int DT, int ST, int S>
 __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  // FIX: the geometry and sizes are the compile-time ones (the launch checks
-  // that they equal the runtime ones); the workspace offsets always come from
-  // the arguments
-  const StackGeom g = FIX ? kFixGeom<DT, ST> : a.g;
+  // S != 0: the geometry and sizes are the compile-time ones of shape S (the
+  // launch checks that they equal the runtime ones); the workspace offsets
+  // always come from the arguments
+  constexpr bool FIX = S != 0;
+  constexpr FixShape fs = kFixShapes[S];
+  const StackGeom g = FIX ? kFixGeom<DT, ST, S> : a.g;
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
-  const int H = FIX ? kFixH : a.H, E = FIX ? kFixE : a.E, k = FIX ? kFixK : a.k, F = FIX ? kFixF : a.F,
-            Fs = FIX ? kFixFs : a.Fs;
+  const int H = FIX ? fs.H : a.H, E = FIX ? fs.E : a.E, k = FIX ? fs.k : a.k, F = FIX ? fs.F : a.F,
+            Fs = FIX ? fs.Fs : a.Fs;
   const bool has_sg = Fs > 0;
 
   float* res = reinterpret_cast<float*>(smem + g.o_res);
@@ -1059,22 +1069,27 @@ int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_
   const void* fn;
   const int dt = d->down_type;
   const int stt = d->shared_ffn > 0 ? d->shared_type : MOE_TYPE_Q4_K;
-  // the compile-time shape when every size and the whole geometry match it
-  const bool fix_shape = d->hidden == kFixH && d->n_experts == kFixE && d->top_k == kFixK && d->ffn == kFixF &&
-                         d->shared_ffn == kFixFs;
-  const bool fix44 = fix_shape && dt == MOE_TYPE_Q4_K && stt == MOE_TYPE_Q4_K &&
-                     memcmp(&g, &kFixGeom<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K>, offsetof(StackGeom, w_ctrl)) == 0;
-  const bool fix58 = fix_shape && dt == MOE_TYPE_Q5_K && stt == MOE_TYPE_Q8_0 &&
-                     memcmp(&g, &kFixGeom<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0>, offsetof(StackGeom, w_ctrl)) == 0;
+  // a compile-time shape when every size and the whole geometry match it
+  auto is_shape = [&](int S) {
+    const FixShape& f = kFixShapes[S];
+    return d->hidden == f.H && d->n_experts == f.E && d->top_k == f.k && d->ffn == f.F && d->shared_ffn == f.Fs;
+  };
+  const bool fix44 = is_shape(1) && dt == MOE_TYPE_Q4_K && stt == MOE_TYPE_Q4_K &&
+                     memcmp(&g, &kFixGeom<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, 1>, offsetof(StackGeom, w_ctrl)) == 0;
+  const bool fix58 = is_shape(1) && dt == MOE_TYPE_Q5_K && stt == MOE_TYPE_Q8_0 &&
+                     memcmp(&g, &kFixGeom<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, 1>, offsetof(StackGeom, w_ctrl)) == 0;
+  const bool fix2 = is_shape(2) && dt == MOE_TYPE_Q4_K && stt == MOE_TYPE_Q4_K &&
+                    memcmp(&g, &kFixGeom<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, 2>, offsetof(StackGeom, w_ctrl)) == 0;
   if (dt == MOE_TYPE_Q5_K)
-    fn = (stt == MOE_TYPE_Q8_0) ? (fix58 ? (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, true>
-                                         : (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, false>)
-                                : (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K, false>;
+    fn = (stt == MOE_TYPE_Q8_0) ? (fix58 ? (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, 1>
+                                         : (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, 0>)
+                                : (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K, 0>;
   else if (stt == MOE_TYPE_Q8_0)
-    fn = (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0, false>;
+    fn = (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0, 0>;
   else
-    fn = fix44 ? (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, true>
-               : (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, false>;
+    fn = fix44 ? (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, 1>
+               : fix2 ? (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, 2>
+                      : (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, 0>;
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds) != hipSuccess) return MOE_ERR_HIP;
   void* args[] = {&a};
   if (hipLaunchCooperativeKernel(fn, dim3(g.G), dim3(kStackThreads), args, g.lds, st) != hipSuccess) {
