@@ -205,6 +205,8 @@ def e128_leg(q, steps, warmup, repeats):
            "us_per_layer": med / cfg3.layers, "launch_us": launch, "kernel_GBs": alg / (launch * 1e-6) / 1e9,
            "mode": "persistent" if stack.mode == q.MOE_STACK_PERSISTENT else "kernels"}
     res["frac_of_peak"] = res["kernel_GBs"] / HBM_PEAK_GBS
+    res["traffic_bytes_per_launch"] = (measured_traffic("moe_stack_48L_e128_traffic")
+                                       if res["mode"] == "persistent" else None)
     print(f"# e128: generated {cfg3.layers} layers in {stack.gen_s:.1f}s; {med:.1f} us/token "
           f"({res['achieved_GBs']:.0f} GB/s)", file=sys.stderr, flush=True)
     del stack
@@ -239,11 +241,12 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(variant):
+def measured_traffic(summary):
     """HBM bytes per launch of the persistent kernel from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or
-    None when that summary was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"moe_stack_40L_{variant}_traffic.md")
+    summary profiles/<summary>.md (FETCH_SIZE + WRITE_SIZE, scaled by a
+    copy-kernel calibration), or None when that summary was taken on other
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{summary}.md")
     try:
         text = open(path).read()
     except OSError:
@@ -418,7 +421,8 @@ def main():
         res["frac_of_peak"] = res["achieved_GBs"] / HBM_PEAK_GBS
         res["launch_us"] = launch_durations(stack, min(64, a.steps))
         res["kernel_GBs"] = alg / (res["launch_us"] * 1e-6) / 1e9
-        res["traffic_bytes_per_launch"] = measured_traffic(name) if res["mode"] == "persistent" else None
+        res["traffic_bytes_per_launch"] = (measured_traffic(f"moe_stack_40L_{name}_traffic")
+                                           if res["mode"] == "persistent" else None)
         res["cold_us_per_token"] = cold_tokens(stack, 32)
         if a.trace and stack.mode == q.MOE_STACK_PERSISTENT:
             stack.step(0)
