@@ -211,12 +211,15 @@ int moe_decode_layer(const moe_layer_desc* desc, const moe_layer_weights* w,
  * Per token the norm, router, top-k and weights are the batch-1 steps.  The
  * group of expert e is the set of tokens whose ids contain e (token order).
  * A group of >= group_min tokens reads the expert's rows once and runs on the
- * matrix cores with bf16 inputs: weights decoded to fp32 then rounded to bf16,
- * activations bf16(xn) for gate/up and bf16(h) for down, fp32 accumulation;
- * h = silu(g) * u in fp32.  A smaller group runs the batch-1 integer path
- * (Q8_1 activations, int8 dots) for each of its tokens.  The shared expert is
- * one group of all n_tok tokens.  routed_out[t] = bf16(sum_s weights[t][s] *
- * y[t][s]) in slot order; shared_out[t] = bf16(shared_gate[t] * ys[t]).
+ * int8 matrix cores: the weight codes against the tokens' Q8_1 codes (xq for
+ * gate/up, Q8_1 of h for down), each 32-element block's exact integer dot
+ * scaled and summed in fp64 as the batch-1 integer path does.  A smaller
+ * group runs that integer path for all its tokens at once.  Either way each
+ * token's h, y, routed_out and shared_out are bit-identical to what the
+ * batch-1 calls give it (the grouped path is batch-invariant; group_min only
+ * moves work between the two code paths).  The shared expert is one group of
+ * all n_tok tokens.  routed_out[t] = bf16(sum_s weights[t][s] * y[t][s]) in
+ * slot order; shared_out[t] = bf16(shared_gate[t] * ys[t]).
  *
  * moe_batch_workspace_size: bytes of workspace for n_tok tokens (0 on a bad
  * description or n_tok outside 1..MOE_MAX_BATCH).

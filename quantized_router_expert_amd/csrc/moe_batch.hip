@@ -2,23 +2,20 @@
 // selected them.
 //
 // A group (the tokens whose top-k contains expert e) with at least group_min
-// tokens reads its expert's rows once and multiplies them on the matrix cores:
-// weights decoded to f32 then rounded to bf16, activations bf16(xn) and
-// bf16(h), fp32 accumulation (v_mfma_f32_16x16x32_bf16).  A smaller group
-// takes the integer Q8_1 x v_dot4 path of the single-token stage for each of
-// its tokens.  The shared expert is one group of all the tokens.  Norm, router
-// and top-k run per token as at batch 1; the combine is per token in slot
-// order.  The pages cover batch 1 only ([P359] Summary: the Q8_1 integer dot
-// path); the grouping reading is stated with the oracle's grouped path.
+// tokens reads its expert's rows once and multiplies them on the int8 matrix
+// cores against the members' Q8_1 codes (v_mfma_i32_16x16x32_i8, one
+// 32-element block per step), then scales and sums exactly as the
+// single-token integer path does.  A smaller group takes that integer path
+// (Q8_1 x v_dot4) for all its members at once, reading each weight task once.
+// Either way every token gets the bit-identical value the batch-1 stage gives
+// it: the grouped path is batch-invariant.  The shared expert is one group of
+// all the tokens.  Norm, router and top-k run per token as at batch 1; the
+// combine is per token in slot order.  The pages cover batch 1 only ([P359]
+// Summary: the Q8_1 integer dot path); the grouping is this library's.
 //
-// MFMA operand layout (16x16x32 bf16, checked on gfx950): lane l holds row
-// l%16 of A and column l%16 of B at k = 8*(l/16) .. +7, and rows 4*(l/16) .. +3
-// of column l%16 of D.  The k order inside a 64-element group is permuted the
-// same way for both operands (lane group q takes elements 8q..8q+7 of the
-// group's first half -- the low nibbles of bytes 8q..8q+7 of a K-quant group
-// -- in one step and of its second half, the high nibbles, in the next), which
-// leaves the dot product unchanged and lets each lane decode 8 contiguous
-// bytes.
+// MFMA operand layout (16x16x32, 8 elements per lane): lane l holds row l%16
+// of A and column l%16 of B at k = 8*(l/16) .. +7, and rows 4*(l/16) .. +3 of
+// column l%16 of D.
 #include <algorithm>
 
 #include "../../include/moe_decode.h"
@@ -27,15 +24,10 @@
 
 namespace moe {
 
-typedef short v8s __attribute__((ext_vector_type(8)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
 constexpr int kBThreads = 256;
 constexpr int kBWaves = kBThreads / 64;
 constexpr int kBRows = 16;                   // rows per wave
 constexpr int kBRowsPerBlock = kBRows * kBWaves;
-constexpr int kMaxTiles = MOE_MAX_BATCH / 16;
 
 // ---------------------------------------------------------------- grouping
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp) {
@@ -98,147 +90,190 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* ids, int n, int k
   if (tid == 0) err[0] = s_bad;
 }
 
-// ---------------------------------------------------------------- bf16 operands
-// 8 weights of one 64-element group gg of a row (lane group q): lo = elements
-// 64gg + 8q .. +7, hi = 64gg + 32 + 8q .. +7, each f32(w) rounded to bf16.
+// ---------------------------------------------------------------- int8 matrix-core rows
+// A group of group_min or more tokens multiplies its expert's rows on the
+// int8 matrix cores (v_mfma_i32_16x16x32_i8: 16 rows x 16 tokens x one
+// 32-element block).  The weight codes (Q4_K nibbles, Q5_K 5-bit codes, Q8_0
+// bytes) and the tokens' Q8_1 codes go in as int8, so each sub-block's dot
+// is the exact integer of the single-token path; each task (a 64-element
+// K-quant group, or one Q8_0 block) is then scaled in fp64 by the same
+// expression as the single-token row task, and the tasks of a row are summed
+// in the same order: lane position p of a TP-lane group holds tasks p, p+64,
+// ..., and the positions meet in a balanced binary tree (the lane-group
+// reduction).  Every token of the group therefore gets the bit-identical
+// value the batch-1 path gives it.  Wave w of the block takes positions
+// [w TP/4, (w+1) TP/4) as a subtree; the four subtrees meet as
+// (q0 + q1) + (q2 + q3).
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i mfma_i8(uint2 a, uint2 b) {
+  const long la = (long)(((unsigned long long)a.y << 32) | a.x);
+  const long lb = (long)(((unsigned long long)b.y << 32) | b.x);
+  return __builtin_amdgcn_mfma_i32_16x16x32_i8(la, lb, v4i{0, 0, 0, 0}, 0, 0, 0);
+}
+
+// codes of elements 8q .. 8q+7 of sub-block 2g + hi of a K-quant superblock, as int8
 template <int TYPE>
-__device__ __forceinline__ void weights_bf16(const uint8_t* row, int gg, int q, v8s& lo, v8s& hi) {
+__device__ __forceinline__ uint2 kq_codes8(const uint8_t* blk, int g, int q, int hi) {
+  const int qs_off = (TYPE == MOE_TYPE_Q5_K) ? 48 : 16;
+  const uint2 b = *reinterpret_cast<const uint2*>(blk + qs_off + 32 * g + 8 * q);
+  uint2 r = make_uint2((b.x >> (4 * hi)) & 0x0f0f0f0fu, (b.y >> (4 * hi)) & 0x0f0f0f0fu);
+  if (TYPE == MOE_TYPE_Q5_K) {
+    const uint2 h = *reinterpret_cast<const uint2*>(blk + 16 + 8 * q);
+    r.x |= ((h.x >> (2 * g + hi)) & 0x01010101u) << 4;
+    r.y |= ((h.y >> (2 * g + hi)) & 0x01010101u) << 4;
+  }
+  return r;
+}
+// Q8_0 block t of a row: codes 8q .. 8q+7 (34-byte blocks: 2-byte aligned)
+__device__ __forceinline__ uint2 q80_codes8(const uint8_t* row, int t, int q) {
+  const uint16_t* c = reinterpret_cast<const uint16_t*>(row + 34L * t) + 1 + 4 * q;
+  return make_uint2((uint32_t)c[0] | ((uint32_t)c[1] << 16), (uint32_t)c[2] | ((uint32_t)c[3] << 16));
+}
+
+// The fp64 value of task t of this lane's rows (4 rows: 4*(lane/16) + i of the
+// 16; rows past nr and tokens past the tile give unused values) against the
+// lane's token (column lane % 16), for NM matrices of TYPE.  codes8(blk, q)
+// -> the token's 8 codes 8q..8q+7 of its Q8_1 block blk (zero for a missing
+// token); ds(blk) -> its d and s.
+template <int TYPE, int NM, class Codes, class DS>
+__device__ __forceinline__ void i8_task(const uint8_t* const (&mats)[NM], long rb, int nr, int t, Codes codes8, DS ds,
+                                        double (&v)[NM][4]) {
+  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const bool rv = r < nr;
   if (TYPE == MOE_TYPE_Q8_0) {
-    // blocks 2gg and 2gg+1, elements 8q..8q+7 of each (34-byte blocks: 2-byte aligned)
-    const uint8_t* b0 = row + 34L * (2 * gg);
-    const uint8_t* b1 = b0 + 34;
-    const uint16_t* p0 = reinterpret_cast<const uint16_t*>(b0);
-    const uint16_t* p1 = reinterpret_cast<const uint16_t*>(b1);
-    const float d0 = f16_to_f32(p0[0]), d1 = f16_to_f32(p1[0]);
+    const uint2 bq = codes8(t, q);
+    const float2 a = ds(t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t c0 = p0[1 + 4 * q + i], c1 = p1[1 + 4 * q + i];
-      lo[2 * i] = (short)f32_to_bf16(d0 * (float)(int8_t)(c0 & 0xff));
-      lo[2 * i + 1] = (short)f32_to_bf16(d0 * (float)(int8_t)(c0 >> 8));
-      hi[2 * i] = (short)f32_to_bf16(d1 * (float)(int8_t)(c1 & 0xff));
-      hi[2 * i + 1] = (short)f32_to_bf16(d1 * (float)(int8_t)(c1 >> 8));
+    for (int mi = 0; mi < NM; ++mi) {
+      uint2 aq = q80_codes8(mats[mi] + (long)(rv ? r : 0) * rb, t, q);
+      if (!rv) aq = make_uint2(0u, 0u);
+      const v4i D = mfma_i8(aq, bq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ri = 4 * q + i;
+        const float di = f16_to_f32(*reinterpret_cast<const uint16_t*>(mats[mi] + (long)(ri < nr ? ri : 0) * rb + 34L * t));
+        v[mi][i] = (double)di * (double)a.x * (double)D[i];
+      }
     }
     return;
   }
-  const int b = gg >> 2, g = gg & 3;
-  const uint8_t* blk = row + (long)b * block_bytes(TYPE);
-  const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
-  const int qs_off = (TYPE == MOE_TYPE_Q5_K) ? 48 : 16;
-  const uint2 qs = *reinterpret_cast<const uint2*>(blk + qs_off + 32 * g + 8 * q);
-  uint2 qh = make_uint2(0, 0);
-  if (TYPE == MOE_TYPE_Q5_K) qh = *reinterpret_cast<const uint2*>(blk + 16 + 8 * q);
-  int sclo, mlo, schi, mhi;
-  kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g, sclo, mlo);
-  kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g + 1, schi, mhi);
-  const float d = f16_to_f32(hdr.x), dmin = f16_to_f32(hdr.x >> 16);
-  // each product below is exact in fp32; the subtraction rounds once: f32(w)
-  const float alo = d * (float)sclo, ahi = d * (float)schi;
-  const float mlo_f = dmin * (float)mlo, mhi_f = dmin * (float)mhi;
+  const int b = t >> 2, g = t & 3;
+  const int jlo = 8 * b + 2 * g;
+  const uint2 blo = codes8(jlo, q), bhi = codes8(jlo + 1, q);
+  const float2 alo = ds(jlo), ahi = ds(jlo + 1);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t byte = ((i < 4 ? qs.x : qs.y) >> (8 * (i & 3))) & 0xffu;
-    int ql = (int)(byte & 15u), qhv = (int)(byte >> 4);
-    if (TYPE == MOE_TYPE_Q5_K) {
-      const uint32_t hb = ((i < 4 ? qh.x : qh.y) >> (8 * (i & 3))) & 0xffu;
-      ql |= (int)((hb >> (2 * g)) & 1u) << 4;
-      qhv |= (int)((hb >> (2 * g + 1)) & 1u) << 4;
+  for (int mi = 0; mi < NM; ++mi) {
+    const uint8_t* blkA = mats[mi] + (long)(rv ? r : 0) * rb + (long)b * block_bytes(TYPE);
+    uint2 wlo = kq_codes8<TYPE>(blkA, g, q, 0), whi = kq_codes8<TYPE>(blkA, g, q, 1);
+    if (!rv) wlo = whi = make_uint2(0u, 0u);
+    const v4i Dlo = mfma_i8(wlo, blo), Dhi = mfma_i8(whi, bhi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ri = 4 * q + i;
+      const uint8_t* blk = mats[mi] + (long)(ri < nr ? ri : 0) * rb + (long)b * block_bytes(TYPE);
+      const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+      int sclo, mlo, schi, mhi;
+      kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g, sclo, mlo);
+      kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g + 1, schi, mhi);
+      const double d = (double)f16_to_f32(hdr.x);
+      const double dmin = (double)f16_to_f32(hdr.x >> 16);
+      const double t1 = d * (double)sclo * (double)alo.x * (double)Dlo[i];
+      const double t2 = dmin * (double)mlo * (double)alo.y;
+      const double t3 = d * (double)schi * (double)ahi.x * (double)Dhi[i];
+      const double t4 = dmin * (double)mhi * (double)ahi.y;
+      v[mi][i] = ((t1 - t2) + t3) - t4;
     }
-    lo[i] = (short)f32_to_bf16(alo * (float)ql - mlo_f);
-    hi[i] = (short)f32_to_bf16(ahi * (float)qhv - mhi_f);
   }
 }
 
-// 8 activations bf16(x[base .. base+8)) (zero past n, or for a missing token)
-__device__ __forceinline__ v8s acts_bf16(const float* x, int base, int n) {
-  v8s r;
-  if (!x || base >= n) {
+// This wave's subtree: positions p0 .. p0+N-1 (N a power of two), each the sum
+// of tasks p, p+64, ... < T in order (0 past T), met pairwise in a balanced
+// tree.  out[mi][i] = the subtree's value for the lane's row i and token.
+template <int TYPE, int NM, int N, class Codes, class DS>
+__device__ __forceinline__ void i8_subtree(const uint8_t* const (&mats)[NM], long rb, int nr, int T, int p0, Codes codes8,
+                                           DS ds, double (&out)[NM][4]) {
+  constexpr int L = (N == 1) ? 1 : (N == 2) ? 2 : (N == 4) ? 3 : (N == 8) ? 4 : 5;
+  double stk[L][NM][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = 0;
-    return r;
-  }
-  const float4 a = *reinterpret_cast<const float4*>(x + base);
-  const float4 b = *reinterpret_cast<const float4*>(x + base + 4);
-  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  for (int n = 0; n < N; ++n) {
+    const int p = p0 + n;
+    double v[NM][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (base + i < n) ? (short)f32_to_bf16(v[i]) : (short)0;
-  return r;
-}
-
-__device__ __forceinline__ v4f mfma_bf16(v8s a, v8s b, v4f c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
-}
-
-// One wave: rows r0.. (nr <= 16 valid) of one or two matrices (rowsA, rowsB
-// may be null) of TYPE with K elements, against the activations of up to
-// MOE_MAX_BATCH members (act(m) -> fp32 pointer of K_act values, K_act <= K;
-// elements past K_act are zero), over the 64-element groups gg0, gg0 + ggs,
-// ... of K.  accA/accB [kMaxTiles] receive D tiles.
-template <int TYPE, class Act>
-__device__ __forceinline__ void wave_mfma(const uint8_t* rowsA, const uint8_t* rowsB, long rb, int nr, int K, int ne,
-                                          int K_act, Act act, v4f* accA, v4f* accB, int gg0, int ggs) {
-  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
-  const int ntiles = (ne + 15) >> 4;
+    for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-  for (int j = 0; j < kMaxTiles; ++j) {
-    accA[j] = v4f{0.f, 0.f, 0.f, 0.f};
-    accB[j] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
-  const bool rv = r < nr;
-  const uint8_t* ra = rowsA + (long)(rv ? r : 0) * rb;
-  const uint8_t* rbp = rowsB ? rowsB + (long)(rv ? r : 0) * rb : nullptr;
-  for (int gg = gg0; gg < K / 64; gg += ggs) {   // K-quant rows: 4 groups per superblock
-    v8s alo, ahi, blo, bhi;
-    weights_bf16<TYPE>(ra, gg, q, alo, ahi);
-    if (!rv) alo = ahi = v8s{0, 0, 0, 0, 0, 0, 0, 0};
-    if (rbp) {
-      weights_bf16<TYPE>(rbp, gg, q, blo, bhi);
-      if (!rv) blo = bhi = v8s{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+      for (int i = 0; i < 4; ++i) v[mi][i] = 0.0;
+    if (p < T) {
+      i8_task<TYPE, NM>(mats, rb, nr, p, codes8, ds, v);
+      for (int t = p + 64; t < T; t += 64) {
+        double w[NM][4];
+        i8_task<TYPE, NM>(mats, rb, nr, t, codes8, ds, w);
 #pragma unroll
-    for (int j = 0; j < kMaxTiles; ++j) {
-      if (j >= ntiles) break;
-      const int m = 16 * j + r;   // this lane's column: member m
-      const float* x = (m < ne) ? act(m) : nullptr;
-      const v8s xlo = acts_bf16(x, 64 * gg + 8 * q, K_act);
-      const v8s xhi = acts_bf16(x, 64 * gg + 32 + 8 * q, K_act);
-      accA[j] = mfma_bf16(alo, xlo, accA[j]);
-      accA[j] = mfma_bf16(ahi, xhi, accA[j]);
-      if (rbp) {
-        accB[j] = mfma_bf16(blo, xlo, accB[j]);
-        accB[j] = mfma_bf16(bhi, xhi, accB[j]);
+        for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[mi][i] += w[mi][i];
       }
     }
+    // merge with the completed left siblings (n's trailing one bits), then park
+    int lvl = 0;
+#pragma unroll
+    for (int k = 0; k < L - 1; ++k) {
+      if (((n >> k) & 1) == 0) break;
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[mi][i] = stk[k][mi][i] + v[mi][i];
+      lvl = k + 1;
+    }
+#pragma unroll
+    for (int k = 0; k < L; ++k)
+      if (k == lvl) {
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) stk[k][mi][i] = v[mi][i];
+      }
   }
+#pragma unroll
+  for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[mi][i] = stk[L - 1][mi][i];
 }
 
-// The kBWaves waves of a block hold partial tiles over disjoint K groups:
-// wave 0 ends with their sums, added in wave order (buf: kBWaves * kMaxTiles
-// * 2 * 64 v4f of LDS).  Every wave of the block must call it.
-constexpr size_t kBigLds = sizeof(v4f) * kBWaves * kMaxTiles * 2 * 64;
-__device__ __forceinline__ void reduce_waves(v4f* accA, v4f* accB, int ntiles, bool two, v4f* buf) {
+// The block's rows (nr <= 16) of NM matrices against one tile of tokens:
+// every wave computes its subtree, the four meet in LDS (buf: kBWaves * NM * 4
+// * 64 doubles) and wave 0 returns true with the row values in out.
+constexpr size_t kI8Lds = sizeof(double) * kBWaves * 2 * 4 * 64;
+constexpr size_t kStageLdsMax = 160 * 1024;   // a CU's LDS
+template <int TYPE, int NM, class Codes, class DS>
+__device__ __forceinline__ bool i8_rows(const uint8_t* const (&mats)[NM], long rb, int nr, int T, Codes codes8, DS ds,
+                                        double* buf, double (&out)[NM][4]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < kMaxTiles; ++j) {
-    if (j < ntiles) {
-      buf[((wave * kMaxTiles + j) * 2 + 0) * 64 + lane] = accA[j];
-      if (two) buf[((wave * kMaxTiles + j) * 2 + 1) * 64 + lane] = accB[j];
-    }
+  int TP = 4;
+  while (TP < T && TP < 64) TP <<= 1;
+  const int N = TP / kBWaves, p0 = wave * N;
+  double c[NM][4];
+  switch (N) {
+    case 1: i8_subtree<TYPE, NM, 1>(mats, rb, nr, T, p0, codes8, ds, c); break;
+    case 2: i8_subtree<TYPE, NM, 2>(mats, rb, nr, T, p0, codes8, ds, c); break;
+    case 4: i8_subtree<TYPE, NM, 4>(mats, rb, nr, T, p0, codes8, ds, c); break;
+    case 8: i8_subtree<TYPE, NM, 8>(mats, rb, nr, T, p0, codes8, ds, c); break;
+    default: i8_subtree<TYPE, NM, 16>(mats, rb, nr, T, p0, codes8, ds, c); break;
   }
+#pragma unroll
+  for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf[((wave * NM + mi) * 4 + i) * 64 + lane] = c[mi][i];
   __syncthreads();
-  if (wave != 0) return;
+  if (wave != 0) return false;
 #pragma unroll
-  for (int j = 0; j < kMaxTiles; ++j) {
-    if (j < ntiles) {
-      v4f sa = buf[(j * 2 + 0) * 64 + lane], sb = v4f{0.f, 0.f, 0.f, 0.f};
-      if (two) sb = buf[(j * 2 + 1) * 64 + lane];
-      for (int w = 1; w < kBWaves; ++w) {
-        sa += buf[((w * kMaxTiles + j) * 2 + 0) * 64 + lane];
-        if (two) sb += buf[((w * kMaxTiles + j) * 2 + 1) * 64 + lane];
-      }
-      accA[j] = sa;
-      accB[j] = sb;
+  for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double q0 = buf[((0 * NM + mi) * 4 + i) * 64 + lane], q1 = buf[((1 * NM + mi) * 4 + i) * 64 + lane];
+      const double q2 = buf[((2 * NM + mi) * 4 + i) * 64 + lane], q3 = buf[((3 * NM + mi) * 4 + i) * 64 + lane];
+      out[mi][i] = (q0 + q1) + (q2 + q3);
     }
-  }
+  return true;
 }
 
 // ---------------------------------------------------------------- group kernels
@@ -261,6 +296,7 @@ struct BGroupArgs {
   float* y;                 // [n][k][H]
   float* ys;                // [n][H]
   int n, k, H, E, F, Fs, Kp, Kps, gmin, has_sg;
+  int stage_gu, stage_dn;   // matrix-core groups: rows (and gate/up activations) staged in LDS
 };
 
 // the group of blockIdx.x: returns false if this block has no group
@@ -393,6 +429,13 @@ __device__ __forceinline__ void rows_dot_multi(int nrows, int T, RowFn rowfn, co
   }
 }
 
+// bytes (a multiple of 16, 16-byte aligned both sides) from global to LDS by the block
+__device__ __forceinline__ void copy_to_lds(uint8_t* dst, const uint8_t* src, long bytes) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  for (long i = threadIdx.x; i < (bytes >> 4); i += kBThreads) d4[i] = s4[i];
+}
+
 // Q8_1 activations of `nt` tokens unpacked into LDS (codes [nt][K], d/s [nt][K/32])
 __device__ __forceinline__ void stage_xq(const uint8_t* xq_all, const int* toks, int nt, int K, uint8_t* codes,
                                          float* dq, float* sq) {
@@ -413,13 +456,16 @@ __device__ __forceinline__ void stage_xq(const uint8_t* xq_all, const int* toks,
 }
 
 // gate/up + SwiGLU of one group, 64 rows per block
-template <int ST>
+// (BIG: the instance for groups of group_min or more tokens; the other
+// instance takes the smaller groups, so each keeps its own register budget)
+template <int ST, bool BIG>
 __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Group gp;
   if (!block_group(a, gp)) return;
   const int Fx = gp.shared ? a.Fs : a.F;
   const bool big = gp.ne >= a.gmin;
+  if (big != BIG) return;
   // blockIdx.y counts kBSmallRows-row chunks: a small group's block takes
   // one (kBSmallPerWave rows per wave); a big group's block takes kBigSpan
   // of them, kBRows rows whose K its waves split (the other blocks of its
@@ -429,39 +475,67 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
   if (fb >= Fx) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H = a.H;
-  if (big) {
-    v4f ag[kMaxTiles], au[kMaxTiles];
+  if constexpr (BIG) {
+    // int8 matrix cores; blockIdx.z picks the tile of 16 tokens
     const int f0 = fb;
     const int nr = min(kBRows, Fx - f0);
+    const int nb = H / 32;
+    double* buf = reinterpret_cast<double*>(smem);
+    const int j = blockIdx.z;
+    if (16 * j >= gp.ne) return;
     {
-      auto act = [&](int m) {
-        int t, s;
-        member(a, gp, m, t, s);
-        return a.xn + (long)t * H;
-      };
-      if (gp.shared) {
-        const long rb = row_bytes(ST, H);
-        wave_mfma<ST>(a.sgate + f0 * rb, a.sup + f0 * rb, rb, nr, H, gp.ne, H, act, ag, au, wave, kBWaves);
-      } else {
-        const long rb = row_bytes(MOE_TYPE_Q4_K, H);
-        const long base = ((long)gp.e * a.F + f0) * rb;
-        wave_mfma<MOE_TYPE_Q4_K>(a.gate + base, a.up + base, rb, nr, H, gp.ne, H, act, ag, au, wave, kBWaves);
+      const long rbw = gp.shared ? row_bytes(ST, H) : row_bytes(MOE_TYPE_Q4_K, H);
+      const uint8_t* src0 = gp.shared ? a.sgate + f0 * rbw : a.gate + ((long)gp.e * a.F + f0) * rbw;
+      const uint8_t* src1 = gp.shared ? a.sup + f0 * rbw : a.up + ((long)gp.e * a.F + f0) * rbw;
+      const uint8_t* w0 = src0;
+      const uint8_t* w1 = src1;
+      const uint8_t* xq0 = a.xq;   // token t's blocks at xq0 + t * nb * 36
+      const int m = 16 * j + (lane & 15);
+      const bool mv = m < gp.ne;
+      int t = 0, s = 0;
+      if (mv) member(a, gp, m, t, s);
+      long xq_stride = (long)t * nb * kQ81Bytes;
+      if (a.stage_gu) {
+        // one bulk load of the block's rows and the tile's activations, so
+        // the task loop reads LDS instead of waiting on memory per task
+        uint8_t* wst = smem + kI8Lds;
+        uint8_t* xst = wst + 2L * kBRows * rbw;
+        copy_to_lds(wst, src0, nr * rbw);
+        copy_to_lds(wst + kBRows * rbw, src1, nr * rbw);
+        const int nm = min(16, gp.ne - 16 * j);
+        for (int c = 0; c < nm; ++c) {
+          int tc, sc_;
+          member(a, gp, 16 * j + c, tc, sc_);
+          copy_to_lds(xst + (long)c * nb * kQ81Bytes, a.xq + (long)tc * nb * kQ81Bytes, (long)nb * kQ81Bytes);
+        }
+        __syncthreads();
+        w0 = wst;
+        w1 = wst + kBRows * rbw;
+        xq0 = xst;
+        xq_stride = (long)(lane & 15) * nb * kQ81Bytes;
       }
-      const int ntiles = (gp.ne + 15) >> 4;
-      reduce_waves(ag, au, ntiles, true, reinterpret_cast<v4f*>(smem));
-      if (wave != 0) return;
-#pragma unroll
-      for (int j = 0; j < kMaxTiles; ++j) {
-        if (j >= ntiles) break;
-        const int m = 16 * j + (lane & 15);
-        if (m >= gp.ne) continue;
-        int t, s;
-        member(a, gp, m, t, s);
+      const uint8_t* xqt = xq0 + (mv ? xq_stride : 0);
+      auto codes8 = [&](int blk, int q) -> uint2 {
+        if (!mv) return make_uint2(0u, 0u);
+        const uint32_t* c = reinterpret_cast<const uint32_t*>(xqt + (long)blk * kQ81Bytes + 4 + 8 * q);
+        return make_uint2(c[0], c[1]);
+      };
+      auto ds = [&](int blk) -> float2 {
+        if (!mv) return make_float2(0.f, 0.f);
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(xqt + (long)blk * kQ81Bytes);
+        return make_float2(f16_to_f32(w), f16_to_f32(w >> 16));
+      };
+      double gu[2][4];
+      bool first;
+      const uint8_t* const mats[2] = {w0, w1};
+      if (gp.shared) first = i8_rows<ST, 2>(mats, rbw, nr, tasks_per_row(ST, H), codes8, ds, buf, gu);
+      else first = i8_rows<MOE_TYPE_Q4_K, 2>(mats, rbw, nr, tasks_per_row(MOE_TYPE_Q4_K, H), codes8, ds, buf, gu);
+      if (first && mv) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = 4 * (lane >> 4) + i;
           if (rr >= nr) continue;
-          const float g = ag[j][i], u = au[j][i];
+          const float g = (float)gu[0][i], u = (float)gu[1][i];
           const float hv = (float)(silu_f64((double)g) * (double)u);
           if (gp.shared) a.hs[(long)t * a.Fs + f0 + rr] = hv;
           else a.h[((long)t * a.k + s) * a.F + f0 + rr] = hv;
@@ -533,7 +607,7 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
 }
 
 // down rows of one group, 64 output rows per block
-template <int DT, int ST>
+template <int DT, int ST, bool BIG>
 __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Group gp;
@@ -541,6 +615,7 @@ __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
   const int H = a.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool big = gp.ne >= a.gmin;
+  if (big != BIG) return;
   // blockIdx.y counts kBRows-row chunks: a big group's block takes one (its
   // waves split K), a small group's block kDnSpan of them, kBRows rows per
   // wave (the other blocks of its span leave at once)
@@ -555,33 +630,56 @@ __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
     member(a, gp, m, t, s);
     return gp.shared ? a.hs + (long)t * a.Fs : a.h + ((long)t * a.k + s) * a.F;
   };
-  if (big) {
-    v4f ay[kMaxTiles], dummy[kMaxTiles];
+  if constexpr (BIG) {
+    // int8 matrix cores; blockIdx.z picks the tile of 16 tokens, whose h is
+    // quantised to Q8_1 in LDS (as for a small group), then the rows
+    const int nb = Kx / 32;
+    double* buf = reinterpret_cast<double*>(smem);
+    uint8_t* codes = smem + kI8Lds;
+    float* dq = reinterpret_cast<float*>(codes + 16L * Kx);
+    float* sq = dq + 16 * nb;
+    const int j = blockIdx.z;
+    if (16 * j >= gp.ne) return;
     {
-      if (gp.shared) {
-        const long rb = row_bytes(ST, Kx);
-        wave_mfma<ST>(a.sdown + i0 * rb, nullptr, rb, nr, Kx, gp.ne, Fx, hsrc, ay, dummy, wave, kBWaves);
-      } else {
-        const long rb = row_bytes(DT, Kx);
-        wave_mfma<DT>(a.down + ((long)gp.e * H + i0) * rb, nullptr, rb, nr, Kx, gp.ne, Fx, hsrc, ay, dummy, wave,
-                      kBWaves);
+      const int nm = min(16, gp.ne - 16 * j);
+      quantize_q81_blocks<1>(nm * nb, [&](int jj) -> const float* {
+        const int mm = jj / nb, blk = jj - mm * nb;
+        return (blk * 32 < Fx) ? hsrc(16 * j + mm) + 32 * blk : nullptr;
+      }, [&](int jj) { return codes + 32L * jj; }, dq, sq, threadIdx.x, kBThreads);
+      __syncthreads();
+      const int c = lane & 15;
+      const bool mv = c < nm;
+      auto codes8 = [&](int blk, int q) -> uint2 {
+        if (!mv) return make_uint2(0u, 0u);
+        return *reinterpret_cast<const uint2*>(codes + (long)c * Kx + 32 * blk + 8 * q);
+      };
+      auto ds = [&](int blk) -> float2 {
+        if (!mv) return make_float2(0.f, 0.f);
+        return make_float2(dq[c * nb + blk], sq[c * nb + blk]);
+      };
+      double yv[1][4];
+      bool first;
+      const long rb = gp.shared ? row_bytes(ST, Kx) : row_bytes(DT, Kx);
+      const uint8_t* src = gp.shared ? a.sdown + i0 * rb : a.down + ((long)gp.e * H + i0) * rb;
+      const uint8_t* w0 = src;
+      if (a.stage_dn) {   // the rows staged after the tile's codes (already behind a barrier)
+        uint8_t* wst = reinterpret_cast<uint8_t*>(sq + 16 * nb);
+        copy_to_lds(wst, src, nr * rb);
+        __syncthreads();
+        w0 = wst;
       }
-      const int ntiles = (gp.ne + 15) >> 4;
-      reduce_waves(ay, dummy, ntiles, false, reinterpret_cast<v4f*>(smem));
-      if (wave != 0) return;
-#pragma unroll
-      for (int j = 0; j < kMaxTiles; ++j) {
-        if (j >= ntiles) break;
-        const int m = 16 * j + (lane & 15);
-        if (m >= gp.ne) continue;
+      const uint8_t* const mats[1] = {w0};
+      if (gp.shared) first = i8_rows<ST, 1>(mats, rb, nr, tasks_per_row(ST, Kx), codes8, ds, buf, yv);
+      else first = i8_rows<DT, 1>(mats, rb, nr, tasks_per_row(DT, Kx), codes8, ds, buf, yv);
+      if (first && mv) {
         int t, s;
-        member(a, gp, m, t, s);
+        member(a, gp, 16 * j + c, t, s);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = 4 * (lane >> 4) + i;
           if (rr >= nr) continue;
-          if (gp.shared) a.ys[(long)t * H + i0 + rr] = ay[j][i];
-          else a.y[((long)t * a.k + s) * H + i0 + rr] = ay[j][i];
+          if (gp.shared) a.ys[(long)t * H + i0 + rr] = (float)yv[0][i];
+          else a.y[((long)t * a.k + s) * H + i0 + rr] = (float)yv[0][i];
         }
       }
     }
@@ -728,6 +826,7 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   a.Kps = has_sg ? pad_k(st_type, Fs) : 0;
   a.gmin = gmin;
   a.has_sg = has_sg;
+  a.stage_gu = a.stage_dn = 0;
   hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, st, ids, n, k, E, reinterpret_cast<int*>(ws + L.cnt),
                      reinterpret_cast<int*>(ws + L.moff), reinterpret_cast<int*>(ws + L.members),
                      reinterpret_cast<int*>(ws + L.dlist), reinterpret_cast<int*>(ws + L.nd),
@@ -738,23 +837,59 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   const int small = gmin - 1;   // largest group on the integer path
   const int fmax = max(F, Fs);
   const dim3 ggu(ngroups, (fmax + kBSmallRows - 1) / kBSmallRows);
-  const size_t lds_gu = std::max(small > 0 ? int_path_lds(small > n ? n : small, H) : (size_t)0, kBigLds);
-  const void* fgu = (st_type == MOE_TYPE_Q8_0) ? (const void*)k_bgu<MOE_TYPE_Q8_0> : (const void*)k_bgu<MOE_TYPE_Q4_K>;
-  if (hipFuncSetAttribute(fgu, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu) != hipSuccess) return MOE_ERR_HIP;
+  const bool any_big = gmin <= n;   // a group (at least the shared one when n >= gmin) can reach group_min
+  const size_t lds_gu = small > 0 ? int_path_lds(small > n ? n : small, H) : 0;
+  // matrix-core groups stage their rows (and gate/up activations) in LDS when they fit
+  const long rbw_max = std::max(row_bytes(MOE_TYPE_Q4_K, H), has_sg ? row_bytes(st_type, H) : 0L);
+  const size_t gu_stage = 2 * kBRows * (size_t)rbw_max + 16 * (size_t)(H / 32) * kQ81Bytes;
+  a.stage_gu = kI8Lds + gu_stage <= kStageLdsMax && (reinterpret_cast<uintptr_t>(xq) & 15) == 0;
+  const size_t lds_gu_big = kI8Lds + (a.stage_gu ? gu_stage : 0);
   void* args[] = {&a};
-  if (hipLaunchKernel(fgu, ggu, dim3(kBThreads), args, lds_gu, st) != hipSuccess) return MOE_ERR_HIP;
+  {
+    const bool q80 = st_type == MOE_TYPE_Q8_0;
+    const void* fs_ = q80 ? (const void*)k_bgu<MOE_TYPE_Q8_0, false> : (const void*)k_bgu<MOE_TYPE_Q4_K, false>;
+    const void* fb_ = q80 ? (const void*)k_bgu<MOE_TYPE_Q8_0, true> : (const void*)k_bgu<MOE_TYPE_Q4_K, true>;
+    if (small > 0) {
+      if (hipFuncSetAttribute(fs_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu) != hipSuccess) return MOE_ERR_HIP;
+      if (hipLaunchKernel(fs_, ggu, dim3(kBThreads), args, lds_gu, st) != hipSuccess) return MOE_ERR_HIP;
+    }
+    const dim3 ggu_big(ngroups, ggu.y, (n + 15) / 16);   // z: tiles of 16 tokens
+    if (any_big) {
+      if (hipFuncSetAttribute(fb_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu_big) != hipSuccess)
+        return MOE_ERR_HIP;
+      if (hipLaunchKernel(fb_, ggu_big, dim3(kBThreads), args, lds_gu_big, st) != hipSuccess) return MOE_ERR_HIP;
+    }
+  }
   const int kmax = max(a.Kp, a.Kps);
   const dim3 gdn(ngroups, (H + kBRows - 1) / kBRows);
-  const size_t lds_dn = std::max(small > 0 ? int_path_lds(small > n ? n : small, kmax) : (size_t)0, kBigLds);
-  const void* fdn;
-  if (d->down_type == MOE_TYPE_Q5_K)
-    fdn = (st_type == MOE_TYPE_Q8_0) ? (const void*)k_bdn<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0>
-                                     : (const void*)k_bdn<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K>;
-  else
-    fdn = (st_type == MOE_TYPE_Q8_0) ? (const void*)k_bdn<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0>
-                                     : (const void*)k_bdn<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K>;
-  if (hipFuncSetAttribute(fdn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn) != hipSuccess) return MOE_ERR_HIP;
-  if (hipLaunchKernel(fdn, gdn, dim3(kBThreads), args, lds_dn, st) != hipSuccess) return MOE_ERR_HIP;
+  const size_t lds_dn = small > 0 ? int_path_lds(small > n ? n : small, kmax) : 0;
+  size_t lds_dn_big = kI8Lds + 16 * (size_t)kmax + 2 * sizeof(float) * 16 * (size_t)(kmax / 32);
+  const long rbd_max = std::max(row_bytes(d->down_type, a.Kp), has_sg ? row_bytes(st_type, a.Kps) : 0L);
+  a.stage_dn = lds_dn_big + kBRows * (size_t)rbd_max <= kStageLdsMax;
+  if (a.stage_dn) lds_dn_big += kBRows * (size_t)rbd_max;
+  const void* fds;
+  const void* fdb;
+  if (d->down_type == MOE_TYPE_Q5_K) {
+    fds = (st_type == MOE_TYPE_Q8_0) ? (const void*)k_bdn<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, false>
+                                     : (const void*)k_bdn<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K, false>;
+    fdb = (st_type == MOE_TYPE_Q8_0) ? (const void*)k_bdn<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, true>
+                                     : (const void*)k_bdn<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K, true>;
+  } else {
+    fds = (st_type == MOE_TYPE_Q8_0) ? (const void*)k_bdn<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0, false>
+                                     : (const void*)k_bdn<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, false>;
+    fdb = (st_type == MOE_TYPE_Q8_0) ? (const void*)k_bdn<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0, true>
+                                     : (const void*)k_bdn<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, true>;
+  }
+  if (small > 0) {
+    if (hipFuncSetAttribute(fds, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn) != hipSuccess) return MOE_ERR_HIP;
+    if (hipLaunchKernel(fds, gdn, dim3(kBThreads), args, lds_dn, st) != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (any_big) {
+    if (hipFuncSetAttribute(fdb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn_big) != hipSuccess)
+      return MOE_ERR_HIP;
+    const dim3 gdn_big(ngroups, gdn.y, (n + 15) / 16);   // z: tiles of 16 tokens
+    if (hipLaunchKernel(fdb, gdn_big, dim3(kBThreads), args, lds_dn_big, st) != hipSuccess) return MOE_ERR_HIP;
+  }
   hipLaunchKernelGGL(k_bcombine, dim3(n, (H + 255) / 256), dim3(256), 0, st, a.y, a.ys, wts, sg,
                      reinterpret_cast<const int*>(ws + L.err), k, H, has_sg, routed, shared);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
