@@ -30,20 +30,22 @@ constexpr int kBRows = 16;                   // rows per wave
 constexpr int kBRowsPerBlock = kBRows * kBWaves;
 
 // ---------------------------------------------------------------- grouping
-__device__ __forceinline__ int block_excl_scan(int v, int* tmp) {
-  // Hillis-Steele over blockDim.x (a power of two) values in LDS
-  const int tid = threadIdx.x, n = blockDim.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < n; o <<= 1) {
-    const int add = (tid >= o) ? tmp[tid - o] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+// Exclusive prefix sum over the block (blockDim.x a multiple of 64): a
+// shuffle scan in each wave, then the wave totals; wsum holds one int per wave.
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  const int incl = tmp[tid];
+  if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  return incl - v;
+  int pre = 0;
+  for (int w = 0; w < wave; ++w) pre += wsum[w];
+  __syncthreads();
+  return pre + x - v;
 }
 
 // ids [n][k] -> cnt[e] tokens per expert, moff[e] first member, members (p = t*k + s,
@@ -69,8 +71,11 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* ids, int n, int k
   }
   __syncthreads();
   const int c = (tid < E) ? s_cnt[tid] : 0;
-  const int off = block_excl_scan(c, tmp);
-  const int pos = block_excl_scan(c > 0 ? 1 : 0, tmp);
+  // one scan of (count, count > 0) packed in 16-bit halves: each total is at
+  // most n*k <= MOE_MAX_BATCH * MOE_MAX_TOPK = 1024 and E <= 1024
+  static_assert(MOE_MAX_BATCH * MOE_MAX_TOPK < 65536 && MOE_MAX_EXPERTS <= 1024, "packed scan");
+  const int sc = block_excl_scan(c | ((c > 0 ? 1 : 0) << 16), tmp);
+  const int off = sc & 0xffff, pos = sc >> 16;
   if (tid < E) {
     s_off[tid] = off;
     cnt[tid] = c;

@@ -22,22 +22,63 @@ namespace moe {
 // =====================================================================
 // t = shared ? bf16(routed + shared) : routed ; u = bf16(residual + t) -> out_sum.
 // sum(u^2) is reduced in fp64; r = 1/sqrt(mean + eps) in fp64; xn = f32((u*r)*w).
-// Thread i handles elements i, i+256, ...: each 32-element Q8_1 block is held by
-// 32 consecutive lanes.
+// With every vector 16-byte aligned, thread i handles elements 8i .. 8i+7,
+// 8(i+256) .. with 16-byte accesses; otherwise element i, i+256, ...  The
+// Q8_1 blocks are then quantised from LDS with four lanes per block (the same
+// fp32 operations, so the same bytes, as the one-lane-per-element form).
+__device__ __forceinline__ void unpack_bf16x8(uint4 v, float f[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xffffu));
+    f[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+  }
+}
 __device__ void norm_token_block(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, const float* w,
                                  int H, float eps, uint16_t* out_sum, float* xn_out, uint8_t* xq_out,
                                  float* u_lds, double* red_lds, int do_norm) {
   const int tid = threadIdx.x;
+  const bool vec = ((reinterpret_cast<uintptr_t>(res) | reinterpret_cast<uintptr_t>(rt) |
+                     reinterpret_cast<uintptr_t>(sh) | reinterpret_cast<uintptr_t>(out_sum) |
+                     reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(xn_out)) & 15) == 0;
   double ss = 0.0;
-  for (int i = tid; i < H; i += kNormThreads) {
-    float t = 0.0f;
-    if (rt && sh) t = bf16_to_f32(f32_to_bf16(bf16_to_f32(rt[i]) + bf16_to_f32(sh[i])));
-    else if (rt) t = bf16_to_f32(rt[i]);
-    const uint16_t ub = f32_to_bf16(bf16_to_f32(res[i]) + t);
-    if (out_sum) out_sum[i] = ub;
-    const float u = bf16_to_f32(ub);
-    u_lds[i] = u;
-    ss += (double)u * (double)u;
+  if (!vec) {
+    for (int i = tid; i < H; i += kNormThreads) {
+      float t = 0.0f;
+      if (rt && sh) t = bf16_to_f32(f32_to_bf16(bf16_to_f32(rt[i]) + bf16_to_f32(sh[i])));
+      else if (rt) t = bf16_to_f32(rt[i]);
+      const uint16_t ub = f32_to_bf16(bf16_to_f32(res[i]) + t);
+      if (out_sum) out_sum[i] = ub;
+      const float u = bf16_to_f32(ub);
+      u_lds[i] = u;
+      ss += (double)u * (double)u;
+    }
+  }
+  for (int c = tid; vec && c < H / 8; c += kNormThreads) {
+    float r8[8], t8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    unpack_bf16x8(reinterpret_cast<const uint4*>(res)[c], r8);
+    if (rt) {
+      unpack_bf16x8(reinterpret_cast<const uint4*>(rt)[c], t8);
+      if (sh) {
+        float s8[8];
+        unpack_bf16x8(reinterpret_cast<const uint4*>(sh)[c], s8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t8[i] = bf16_to_f32(f32_to_bf16(t8[i] + s8[i]));
+      }
+    }
+    uint32_t ob[4];
+    float u8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t ub = f32_to_bf16(r8[i] + t8[i]);
+      u8[i] = bf16_to_f32(ub);
+      ss += (double)u8[i] * (double)u8[i];
+      if (i & 1) ob[i >> 1] |= (uint32_t)ub << 16;
+      else ob[i >> 1] = ub;
+    }
+    if (out_sum) reinterpret_cast<uint4*>(out_sum)[c] = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+    reinterpret_cast<float4*>(u_lds)[2 * c] = make_float4(u8[0], u8[1], u8[2], u8[3]);
+    reinterpret_cast<float4*>(u_lds)[2 * c + 1] = make_float4(u8[4], u8[5], u8[6], u8[7]);
   }
   if (!do_norm) return;
   ss = wave_sum_f64(ss);
@@ -47,16 +88,50 @@ __device__ void norm_token_block(const uint16_t* res, const uint16_t* rt, const 
 #pragma unroll
   for (int wv = 0; wv < kNormThreads / 64; ++wv) tot += red_lds[wv];
   const double r = 1.0 / sqrt(tot / (double)H + (double)eps);
-  for (int i = tid; i < H; i += kNormThreads) {
-    const float x = (float)(((double)u_lds[i] * r) * (double)w[i]);
-    if (xn_out) xn_out[i] = x;
-    if (xq_out) {
-      Q81Lane q = quantize_q81_lane(x);
-      const int blk = i >> 5, l = i & 31;
-      uint8_t* ob = xq_out + (long)blk * kQ81Bytes;
-      if (l == 0) *reinterpret_cast<uint32_t*>(ob) = q.ds;
-      ob[4 + l] = (uint8_t)(int8_t)q.q;
+  if (!vec) {
+    for (int i = tid; i < H; i += kNormThreads) {
+      const float x = (float)(((double)u_lds[i] * r) * (double)w[i]);
+      if (xn_out) xn_out[i] = x;
+      u_lds[i] = x;
     }
+  }
+  for (int c = tid; vec && c < H / 4; c += kNormThreads) {
+    const float4 u = reinterpret_cast<const float4*>(u_lds)[c];
+    const float4 wv = reinterpret_cast<const float4*>(w)[c];
+    float4 x;
+    x.x = (float)(((double)u.x * r) * (double)wv.x);
+    x.y = (float)(((double)u.y * r) * (double)wv.y);
+    x.z = (float)(((double)u.z * r) * (double)wv.z);
+    x.w = (float)(((double)u.w * r) * (double)wv.w);
+    if (xn_out) reinterpret_cast<float4*>(xn_out)[c] = x;
+    reinterpret_cast<float4*>(u_lds)[c] = x;   // xn replaces u (each float4 is read and written by one thread)
+  }
+  if (!xq_out) return;
+  __syncthreads();
+  // block j: lanes 4j .. 4j+3, values 8p .. 8p+7 each
+  for (int i0 = tid; i0 < H / 8; i0 += kNormThreads) {
+    const int j = i0 >> 2, p = i0 & 3;
+    const float4 a = reinterpret_cast<const float4*>(u_lds + 32 * j + 8 * p)[0];
+    const float4 b = reinterpret_cast<const float4*>(u_lds + 32 * j + 8 * p)[1];
+    float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float amax = 0.0f;
+    bool nan = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      amax = fmaxf(amax, fabsf(x[i]));
+      nan |= (x[i] != x[i]);
+    }
+    amax = fmaxf(amax, __uint_as_float(partner_dpp<0>(__float_as_uint(amax))));
+    amax = fmaxf(amax, __uint_as_float(partner_dpp<1>(__float_as_uint(amax))));
+    const bool slow = nan || !(amax == 0.0f || (amax >= 0x1p-100f && amax <= 0x1p100f));
+    uint32_t q[2];
+    uint32_t ds;
+    if (__builtin_expect(__any(slow), 0)) ds = q81_group<4, true>(x, amax, q);
+    else ds = q81_group<4, false>(x, amax, q);
+    uint8_t* ob = xq_out + (long)j * kQ81Bytes;
+    reinterpret_cast<uint32_t*>(ob + 4 + 8 * p)[0] = q[0];
+    reinterpret_cast<uint32_t*>(ob + 4 + 8 * p)[1] = q[1];
+    if (p == 0) *reinterpret_cast<uint32_t*>(ob) = ds;
   }
 }
 

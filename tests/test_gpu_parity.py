@@ -81,13 +81,16 @@ def test_quantize_q81_four_lane_bit_exact(q, orc, nblk, mix):
 
 # ------------------------------------------------------------------ a1: add_rmsnorm3
 @pytest.mark.parametrize("H,n_tok,form", [(2048, 1, 3), (2048, 5, 3), (2048, 3, 2), (2048, 2, 1), (512, 7, 3),
-                                          (8192, 2, 3), (256, 3, 2), (2048, 4, 4)])
+                                          (8192, 2, 3), (256, 3, 2), (2048, 4, 4), (2048, 3, 5), (512, 2, 6)])
 def test_add_rmsnorm3(q, orc, H, n_tok, form):
     """form 4 = form 3 with norm weights near 1e-6: Q8_1 scales below the fp16
-    range (d = 0, and s = -0 for a negative code sum)."""
+    range (d = 0, and s = -0 for a negative code sum).  Forms 5 and 6 = forms 3
+    and 2 with every vector and the norm weight at an address that is not
+    16-byte aligned (the kernel's element-wise path)."""
     gu.banner(f"add_rmsnorm3 H {H} n_tok {n_tok} form {form}")
     tiny = form == 4
-    form = 3 if tiny else form
+    skew = form in (5, 6)
+    form = 3 if form in (4, 5) else 2 if form == 6 else form
     rng = np.random.default_rng(H * 10 + n_tok + form)
     bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
     res = bf(rng.standard_normal((n_tok, H)))
@@ -103,8 +106,25 @@ def test_add_rmsnorm3(q, orc, H, n_tok, form):
     out = torch.zeros(n_tok, H, dtype=torch.bfloat16, device="cuda")
     xn = torch.zeros(n_tok, H, dtype=torch.float32, device="cuda")
     xq = torch.zeros(n_tok, H // 32 * 36, dtype=torch.uint8, device="cuda")
-    q.add_rmsnorm3(res.cuda(), rt.cuda() if rt is not None else None, sh.cuda() if sh is not None else None,
-                   w.cuda(), H, n_tok, 1e-6, out, xn, xq)
+
+    def put(t):
+        # a device copy, at an address 2 (bf16) or 4 (fp32) bytes past a 16-byte boundary when skewed
+        if t is None:
+            return None
+        if not skew:
+            return t.cuda()
+        flat = torch.zeros(t.numel() + 8, dtype=t.dtype, device="cuda")
+        flat[1:1 + t.numel()] = t.reshape(-1).cuda()
+        return flat[1:1 + t.numel()].view(t.shape)
+
+    if skew:
+        out_s, xn_s = put(out), put(xn)
+        q.add_rmsnorm3(put(res), put(rt), put(sh), put(w), H, n_tok, 1e-6, out_s, xn_s, xq)
+        _sync()
+        out.copy_(out_s)
+        xn.copy_(xn_s)
+    else:
+        q.add_rmsnorm3(put(res), put(rt), put(sh), put(w), H, n_tok, 1e-6, out, xn, xq)
     _sync()
     g_out, g_xn, g_xq = gu.u16_host(out), gu.host(xn), gu.host(xq)
     for t in range(n_tok):
