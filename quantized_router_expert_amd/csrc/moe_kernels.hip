@@ -169,13 +169,14 @@ __device__ __forceinline__ unsigned long long topk_key(float v, int e) {
   return ((unsigned long long)o << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
 }
 
-// Wave-level top-k over E <= 64*kTopkPerLane logits held in memory.  Each lane
-// keeps its keys; k rounds of a wave-wide 64-bit max pick the slots in rank order.
-__device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* ids_out, float* w_out) {
+// Wave-level top-k over E <= 64*NPL logits held in memory.  Each lane keeps
+// its NPL keys; k rounds of a wave-wide 64-bit max pick the slots in rank order.
+template <int NPL>
+__device__ void wave_topk_softmax_n(const float* logits, int E, int k, int32_t* ids_out, float* w_out) {
   const int lane = threadIdx.x & 63;
-  unsigned long long key[kTopkPerLane];
+  unsigned long long key[NPL];
 #pragma unroll
-  for (int j = 0; j < kTopkPerLane; ++j) {
+  for (int j = 0; j < NPL; ++j) {
     const int e = lane + 64 * j;
     key[j] = (e < E) ? topk_key(logits[e], e) : 0ull;
   }
@@ -183,10 +184,10 @@ __device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* id
   for (int s = 0; s < k; ++s) {
     unsigned long long best = 0ull;
 #pragma unroll
-    for (int j = 0; j < kTopkPerLane; ++j) best = key[j] > best ? key[j] : best;
+    for (int j = 0; j < NPL; ++j) best = key[j] > best ? key[j] : best;
     const unsigned long long wbest = wave_max_u64(best);
 #pragma unroll
-    for (int j = 0; j < kTopkPerLane; ++j)
+    for (int j = 0; j < NPL; ++j)
       if (key[j] == wbest) key[j] = 0ull;
     if (lane == s) my_id = (int32_t)(0xffffffffu - (uint32_t)(wbest & 0xffffffffull));
   }
@@ -201,41 +202,60 @@ __device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* id
     w_out[lane] = (float)(ex / sum);
   }
 }
+// keys per lane from the expert count (the scan is the same, over fewer keys)
+__device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* ids_out, float* w_out) {
+  static_assert(kTopkPerLane == 16, "dispatch below covers up to 16 keys per lane");
+  if (E <= 64) wave_topk_softmax_n<1>(logits, E, k, ids_out, w_out);
+  else if (E <= 128) wave_topk_softmax_n<2>(logits, E, k, ids_out, w_out);
+  else if (E <= 256) wave_topk_softmax_n<4>(logits, E, k, ids_out, w_out);
+  else if (E <= 512) wave_topk_softmax_n<8>(logits, E, k, ids_out, w_out);
+  else wave_topk_softmax_n<16>(logits, E, k, ids_out, w_out);
+}
 
-// grid (nrows, ceil(n_tok / kRouterTok)): workgroup x computes row x (router
-// row e < E, or the shared-gate row e == E) for up to kRouterTok tokens, so a
-// row is read once per token group; its waves take interleaved quarters of
-// the row and their fp64 partial sums are added in wave order.  The last
-// workgroup of a token group to finish (a wrapping atomic increment returns
-// nrows-1 to it and leaves 0 behind) selects for the group's tokens, one
-// token per wave at a time.
+// grid (ceil(nrows / kRouterRpb), ceil(n_tok / kRouterTok)): workgroup x
+// computes rows kRouterRpb*x .. (router row e < E, or the shared-gate row
+// e == E) for up to kRouterTok tokens, so a row is read once per token group;
+// the waves of a row take interleaved parts of it and their fp64 partial
+// sums are added in wave order.  The last workgroup of a token group to
+// finish (a wrapping atomic increment on the group's counter, one counter per
+// 128-byte line when the workspace has room, returns gridDim.x-1 to it and
+// leaves 0 behind) selects for the group's tokens, one token per wave at a
+// time.
+#ifndef MOE_ROUTER_RPB
+#define MOE_ROUTER_RPB 1
+#endif
+constexpr int kRouterRpb = MOE_ROUTER_RPB;
 __global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn, const float* W, const float* wsg,
                                                                  int n_tok, int H, int E, int k, float* logits,
                                                                  float* user_logits, int32_t* ids, float* wts,
-                                                                 float* sg_out, unsigned* counters) {
+                                                                 float* sg_out, unsigned* counters, int cstride) {
   constexpr int kW = kRouterThreads / 64;
+  constexpr int kWpr = kW / kRouterRpb;   // waves per row
   __shared__ double part[kW][kRouterTok];
   const int logits_stride = E + 1;
   const int tg = blockIdx.y;
   const int t0 = tg * kRouterTok;
   const int nt = min(kRouterTok, n_tok - t0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x;
+  const int nrows = E + (wsg ? 1 : 0);
+  const int row = blockIdx.x * kRouterRpb + wave / kWpr, qw = wave % kWpr;
   {
-    const float* wr = (row < E) ? W + (long)row * H : wsg;
     double acc[kRouterTok];
 #pragma unroll
     for (int t = 0; t < kRouterTok; ++t) acc[t] = 0.0;
-    for (int i = (wave * 64 + lane) * 4; i < H; i += 256 * kW) {
-      const float4 a = *reinterpret_cast<const float4*>(wr + i);
+    if (row < nrows) {
+      const float* wr = (row < E) ? W + (long)row * H : wsg;
+      for (int i = (qw * 64 + lane) * 4; i < H; i += 256 * kWpr) {
+        const float4 a = *reinterpret_cast<const float4*>(wr + i);
 #pragma unroll
-      for (int t = 0; t < kRouterTok; ++t) {
-        if (t < nt) {
-          const float4 b = *reinterpret_cast<const float4*>(xn + (long)(t0 + t) * H + i);
-          acc[t] += (double)a.x * (double)b.x;
-          acc[t] += (double)a.y * (double)b.y;
-          acc[t] += (double)a.z * (double)b.z;
-          acc[t] += (double)a.w * (double)b.w;
+        for (int t = 0; t < kRouterTok; ++t) {
+          if (t < nt) {
+            const float4 b = *reinterpret_cast<const float4*>(xn + (long)(t0 + t) * H + i);
+            acc[t] += (double)a.x * (double)b.x;
+            acc[t] += (double)a.y * (double)b.y;
+            acc[t] += (double)a.z * (double)b.z;
+            acc[t] += (double)a.w * (double)b.w;
+          }
         }
       }
     }
@@ -247,17 +267,21 @@ __global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn,
       }
     }
     __syncthreads();
-    if (threadIdx.x < nt) {
-      const int t = threadIdx.x;
-      double v = part[0][t];
-      for (int w = 1; w < kW; ++w) v += part[w][t];
-      logits[(long)(t0 + t) * logits_stride + row] = (float)v;
+    if (threadIdx.x < kRouterRpb * nt) {
+      const int rr = threadIdx.x / nt, t = threadIdx.x - rr * nt;
+      const int r = blockIdx.x * kRouterRpb + rr;
+      if (r < nrows) {
+        double v = part[rr * kWpr][t];
+        for (int w2 = 1; w2 < kWpr; ++w2) v += part[rr * kWpr + w2][t];
+        logits[(long)(t0 + t) * logits_stride + r] = (float)v;
+      }
     }
   }
   __shared__ int is_last;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = __builtin_amdgcn_atomic_inc32(counters + tg, gridDim.x - 1, __ATOMIC_ACQ_REL, "agent");
+    const unsigned old = __builtin_amdgcn_atomic_inc32(counters + (long)tg * cstride, gridDim.x - 1, __ATOMIC_ACQ_REL,
+                                                       "agent");
     is_last = (old == gridDim.x - 1);
   }
   __syncthreads();
@@ -679,8 +703,11 @@ int launch_quantize(const float* x, int n, void* xq, hipStream_t st) {
 int launch_router(const float* xn, const float* W, const float* wsg, int n_tok, int H, int E, int k, float* logits,
                   float* user_logits, int32_t* ids, float* wts, float* sg, unsigned* counters, hipStream_t st) {
   const int nrows = E + (wsg ? 1 : 0);
-  hipLaunchKernelGGL(k_router_topk, dim3(nrows, (n_tok + kRouterTok - 1) / kRouterTok), dim3(kRouterThreads), 0, st, xn,
-                     W, wsg, n_tok, H, E, k, logits, user_logits, ids, wts, sg, counters);
+  const int ngroups = (n_tok + kRouterTok - 1) / kRouterTok;
+  // one counter per 128-byte line when the counter area has room for it
+  const int cstride = (ngroups * 32 <= kCounterSlots) ? 32 : 1;
+  hipLaunchKernelGGL(k_router_topk, dim3((nrows + kRouterRpb - 1) / kRouterRpb, ngroups), dim3(kRouterThreads), 0, st,
+                     xn, W, wsg, n_tok, H, E, k, logits, user_logits, ids, wts, sg, counters, cstride);
   return launch_ok();
 }
 
