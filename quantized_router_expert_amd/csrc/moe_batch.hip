@@ -32,17 +32,17 @@ constexpr int kBRowsPerBlock = kBRows * kBWaves;
 // ---------------------------------------------------------------- grouping
 // Exclusive prefix sum over the block (blockDim.x a multiple of 64): a
 // shuffle scan in each wave, then the wave totals; wsum holds one int per wave.
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
+__device__ __forceinline__ long long block_excl_scan(long long v, long long* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
+  long long x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
+    const long long y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  int pre = 0;
+  long long pre = 0;
   for (int w = 0; w < wave; ++w) pre += wsum[w];
   __syncthreads();
   return pre + x - v;
@@ -51,11 +51,11 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
 // ids [n][k] -> cnt[e] tokens per expert, moff[e] first member, members (p = t*k + s,
 // token order within an expert), dlist = the experts with cnt > 0 in increasing
 // order, nd[0] = their number, err[0] = 1 if an id is outside [0, E).
-__global__ __launch_bounds__(1024) void k_group(const int32_t* ids, int n, int k, int E, int* cnt, int* moff,
-                                                int* members, int* dlist, int* nd, int* err) {
+__global__ __launch_bounds__(1024) void k_group(const int32_t* ids, int n, int k, int E, int gmin, int* cnt, int* moff,
+                                                int* members, int* dlist, int* nd, int* blist, int* nb, int* err) {
   __shared__ int s_cnt[MOE_MAX_EXPERTS];
   __shared__ int s_off[MOE_MAX_EXPERTS];
-  __shared__ int tmp[1024];
+  __shared__ long long tmp[1024 / 64];
   __shared__ int s_ids[MOE_MAX_BATCH * MOE_MAX_TOPK];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
@@ -71,18 +71,23 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* ids, int n, int k
   }
   __syncthreads();
   const int c = (tid < E) ? s_cnt[tid] : 0;
-  // one scan of (count, count > 0) packed in 16-bit halves: each total is at
-  // most n*k <= MOE_MAX_BATCH * MOE_MAX_TOPK = 1024 and E <= 1024
+  // one scan of (count, count > 0, count >= gmin) packed in 16-bit fields:
+  // each total is at most n*k <= MOE_MAX_BATCH * MOE_MAX_TOPK = 1024 and E <= 1024
   static_assert(MOE_MAX_BATCH * MOE_MAX_TOPK < 65536 && MOE_MAX_EXPERTS <= 1024, "packed scan");
-  const int sc = block_excl_scan(c | ((c > 0 ? 1 : 0) << 16), tmp);
-  const int off = sc & 0xffff, pos = sc >> 16;
+  const long long sc = block_excl_scan((long long)c | ((long long)(c > 0 ? 1 : 0) << 16) |
+                                       ((long long)(c >= gmin ? 1 : 0) << 32), tmp);
+  const int off = (int)(sc & 0xffff), pos = (int)((sc >> 16) & 0xffff), bpos = (int)((sc >> 32) & 0xffff);
   if (tid < E) {
     s_off[tid] = off;
     cnt[tid] = c;
     moff[tid] = off;
     if (c > 0) dlist[pos] = tid;
+    if (c >= gmin) blist[bpos] = tid;
   }
-  if (tid == 1023) nd[0] = pos + (c > 0 ? 1 : 0);
+  if (tid == 1023) {
+    nd[0] = pos + (c > 0 ? 1 : 0);
+    nb[0] = bpos + (c >= gmin ? 1 : 0);
+  }
   __syncthreads();
   for (int p = tid; p < P; p += 1024) {
     const int e = s_ids[p];
@@ -288,6 +293,8 @@ struct BGroupArgs {
   const int* members;
   const int* dlist;
   const int* nd;
+  const int* blist;         // the experts with group_min or more tokens, increasing
+  const int* nb;
   const float* xn;          // [n][H]
   const uint8_t* xq;        // [n][H/32] Q8_1
   const uint8_t* gate;      // routed [E][F] rows
@@ -309,6 +316,8 @@ struct Group {
   bool shared;
   int e, ne, mbase;
 };
+// (COMPACT: blockIdx.x indexes the groups of group_min or more tokens only)
+template <bool COMPACT>
 __device__ __forceinline__ bool block_group(const BGroupArgs& a, Group& gp) {
   const int gi = blockIdx.x;
   gp.shared = a.has_sg && gi == (int)gridDim.x - 1;
@@ -318,8 +327,8 @@ __device__ __forceinline__ bool block_group(const BGroupArgs& a, Group& gp) {
     gp.mbase = 0;
     return true;
   }
-  if (gi >= a.nd[0]) return false;
-  gp.e = a.dlist[gi];
+  if (gi >= (COMPACT ? a.nb[0] : a.nd[0])) return false;
+  gp.e = COMPACT ? a.blist[gi] : a.dlist[gi];
   gp.ne = a.cnt[gp.e];
   gp.mbase = a.moff[gp.e];
   return true;
@@ -467,7 +476,7 @@ template <int ST, bool BIG>
 __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Group gp;
-  if (!block_group(a, gp)) return;
+  if (!block_group<false>(a, gp)) return;
   const int Fx = gp.shared ? a.Fs : a.F;
   const bool big = gp.ne >= a.gmin;
   if (big != BIG) return;
@@ -616,7 +625,7 @@ template <int DT, int ST, bool BIG>
 __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Group gp;
-  if (!block_group(a, gp)) return;
+  if (!block_group<BIG>(a, gp)) return;
   const int H = a.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool big = gp.ne >= a.gmin;
@@ -778,6 +787,8 @@ BatchWs batch_ws_layout(const moe_layer_desc* d, int n) {
   L.members = o; o += up256(sizeof(int) * (size_t)n * k);
   L.dlist = o; o += up256(sizeof(int) * E);
   L.nd = o; o += 256;
+  L.blist = o; o += up256(sizeof(int) * E);
+  L.nb = o; o += 256;
   L.err = o; o += 256;
   L.xn = o; o += up256(sizeof(float) * (size_t)n * H);
   L.xq = o; o += up256((size_t)n * (H / 32) * kQ81Bytes);
@@ -809,6 +820,8 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   a.members = reinterpret_cast<const int*>(ws + L.members);
   a.dlist = reinterpret_cast<const int*>(ws + L.dlist);
   a.nd = reinterpret_cast<const int*>(ws + L.nd);
+  a.blist = reinterpret_cast<const int*>(ws + L.blist);
+  a.nb = reinterpret_cast<const int*>(ws + L.nb);
   a.xn = xn;
   a.xq = static_cast<const uint8_t*>(xq);
   a.gate = static_cast<const uint8_t*>(w->gate);
@@ -832,13 +845,16 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   a.gmin = gmin;
   a.has_sg = has_sg;
   a.stage_gu = a.stage_dn = 0;
-  hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, st, ids, n, k, E, reinterpret_cast<int*>(ws + L.cnt),
+  hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, st, ids, n, k, E, gmin, reinterpret_cast<int*>(ws + L.cnt),
                      reinterpret_cast<int*>(ws + L.moff), reinterpret_cast<int*>(ws + L.members),
                      reinterpret_cast<int*>(ws + L.dlist), reinterpret_cast<int*>(ws + L.nd),
+                     reinterpret_cast<int*>(ws + L.blist), reinterpret_cast<int*>(ws + L.nb),
                      reinterpret_cast<int*>(ws + L.err));
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
   // groups: at most min(E, n*k) distinct experts, plus the shared group
   const int ngroups = min(E, n * k) + has_sg;
+  // groups of group_min or more tokens: at most n*k / group_min experts, plus the shared group
+  const int ngroups_big = min(E, n * k / gmin) + has_sg;
   const int small = gmin - 1;   // largest group on the integer path
   const int fmax = max(F, Fs);
   const dim3 ggu(ngroups, (fmax + kBSmallRows - 1) / kBSmallRows);
@@ -858,7 +874,10 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
       if (hipFuncSetAttribute(fs_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu) != hipSuccess) return MOE_ERR_HIP;
       if (hipLaunchKernel(fs_, ggu, dim3(kBThreads), args, lds_gu, st) != hipSuccess) return MOE_ERR_HIP;
     }
-    const dim3 ggu_big(ngroups, ggu.y, (n + 15) / 16);   // z: tiles of 16 tokens
+    // z: tiles of 16 tokens.  x spans every group: this instance runs one
+    // workgroup per CU, and the compact list of big groups (as for down)
+    // packed its few real workgroups together and measured slower
+    const dim3 ggu_big(ngroups, ggu.y, (n + 15) / 16);
     if (any_big) {
       if (hipFuncSetAttribute(fb_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu_big) != hipSuccess)
         return MOE_ERR_HIP;
@@ -892,7 +911,7 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   if (any_big) {
     if (hipFuncSetAttribute(fdb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn_big) != hipSuccess)
       return MOE_ERR_HIP;
-    const dim3 gdn_big(ngroups, gdn.y, (n + 15) / 16);   // z: tiles of 16 tokens
+    const dim3 gdn_big(ngroups_big, gdn.y, (n + 15) / 16);   // z: tiles of 16 tokens
     if (hipLaunchKernel(fdb, gdn_big, dim3(kBThreads), args, lds_dn_big, st) != hipSuccess) return MOE_ERR_HIP;
   }
   hipLaunchKernelGGL(k_bcombine, dim3(n, (H + 255) / 256), dim3(256), 0, st, a.y, a.ys, wts, sg,

@@ -41,7 +41,7 @@ int launch_fill(void* p, size_t n_u32, uint32_t v, hipStream_t st);
 
 // workspace of the grouped (batch > 1) path
 struct BatchWs {
-  size_t router, cnt, moff, members, dlist, nd, err, xn, xq, ids, wts, sg, h, hs, y, ys, total;
+  size_t router, cnt, moff, members, dlist, nd, blist, nb, err, xn, xq, ids, wts, sg, h, hs, y, ys, total;
 };
 BatchWs batch_ws_layout(const moe_layer_desc* d, int n_tok);
 int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const float* xn, const void* xq,
