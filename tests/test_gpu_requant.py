@@ -37,19 +37,24 @@ def _x(n_rows, K, seed):
     return torch.from_numpy(x.astype(np.float32).reshape(n_rows, K))
 
 
-def _run(q, src, src_type, n_rows, K):
-    dst = torch.zeros(n_rows * (K // 256) * 144, dtype=torch.uint8, device="cuda")
+def _run(q, src, src_type, n_rows, K, skew=0):
+    """skew: bytes past a 16-byte boundary for dst (2: the library's
+    superblock-per-wave kernel, which needs only 2-byte alignment; 0: the
+    sub-block-per-lane kernel)."""
+    n = n_rows * (K // 256) * 144
+    buf = torch.zeros(n + 16, dtype=torch.uint8, device="cuda")
+    dst = buf[skew:skew + n]
     q.moe_requant_q4k(src, src_type, n_rows, K, dst)
     torch.cuda.synchronize()
     return dst
 
 
 @pytest.mark.parametrize("src_type", [wl.Q8_0, wl.Q5_K, wl.Q4_K])
-@pytest.mark.parametrize("n_rows,K", [(1, 256), (37, 2048), (5, 768)])
-def test_requant_bit_exact(q, orc, src_type, n_rows, K):
-    gu.banner(f"requant to Q4_K from type {src_type}, {n_rows} x {K}")
+@pytest.mark.parametrize("n_rows,K,skew", [(1, 256, 0), (37, 2048, 0), (5, 768, 0), (37, 2048, 2), (3, 256, 2)])
+def test_requant_bit_exact(q, orc, src_type, n_rows, K, skew):
+    gu.banner(f"requant to Q4_K from type {src_type}, {n_rows} x {K}, dst skew {skew}")
     src = wl.quantize(_x(n_rows, K, 100 * src_type + K + n_rows), src_type).numpy()
-    got = gu.host(_run(q, gu.dev(src), src_type, n_rows, K))
+    got = gu.host(_run(q, gu.dev(src), src_type, n_rows, K, skew))
     ref = orc.requant_q4k(src, src_type, n_rows, K)
     bad = np.nonzero((got.reshape(-1, 144) != ref.reshape(-1, 144)).any(1))[0]
     assert bad.size == 0, f"{bad.size} superblocks differ, first {bad[:5]}"
