@@ -140,57 +140,63 @@ __device__ __forceinline__ uint2 q80_codes8(const uint8_t* row, int t, int q) {
   return make_uint2((uint32_t)c[0] | ((uint32_t)c[1] << 16), (uint32_t)c[2] | ((uint32_t)c[3] << 16));
 }
 
-// The fp64 value of task t of this lane's rows (4 rows: 4*(lane/16) + i of the
-// 16; rows past nr and tokens past the tile give unused values) against the
-// lane's token (column lane % 16), for NM matrices of TYPE.  codes8(blk, q)
-// -> the token's 8 codes 8q..8q+7 of its Q8_1 block blk (zero for a missing
-// token); ds(blk) -> its d and s.
+// The fp64 value of task t of this lane's row (row lane % 16 of the 16; a
+// row past nr gives an unused value) against the lane's 4 tokens (tile
+// tokens 4*(lane/16) + i), for NM matrices of TYPE.  The tokens' codes are
+// the MFMA's A operand and the weight codes its B operand, so each lane's
+// results share one weight row and its scales are decoded once per task.
+// codes8(blk, q) -> the codes 8q..8q+7 of Q8_1 block blk of tile token
+// lane % 16 (zero for a missing token); ds(tok, blk) -> d and s of tile token
+// tok's block blk (zero for a missing token).
 template <int TYPE, int NM, class Codes, class DS>
 __device__ __forceinline__ void i8_task(const uint8_t* const (&mats)[NM], long rb, int nr, int t, Codes codes8, DS ds,
                                         double (&v)[NM][4]) {
   const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
   const bool rv = r < nr;
+  const long ro = (long)(rv ? r : 0) * rb;
   if (TYPE == MOE_TYPE_Q8_0) {
-    const uint2 bq = codes8(t, q);
-    const float2 a = ds(t);
+    const uint2 aq = codes8(t, q);
+    float2 a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = ds(4 * q + i, t);
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi) {
-      uint2 aq = q80_codes8(mats[mi] + (long)(rv ? r : 0) * rb, t, q);
-      if (!rv) aq = make_uint2(0u, 0u);
-      const v4i D = mfma_i8(aq, bq);
+      uint2 wq = q80_codes8(mats[mi] + ro, t, q);
+      if (!rv) wq = make_uint2(0u, 0u);
+      const v4i D = mfma_i8(aq, wq);
+      const float dw = f16_to_f32(*reinterpret_cast<const uint16_t*>(mats[mi] + ro + 34L * t));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ri = 4 * q + i;
-        const float di = f16_to_f32(*reinterpret_cast<const uint16_t*>(mats[mi] + (long)(ri < nr ? ri : 0) * rb + 34L * t));
-        v[mi][i] = (double)di * (double)a.x * (double)D[i];
-      }
+      for (int i = 0; i < 4; ++i) v[mi][i] = (double)dw * (double)a[i].x * (double)D[i];
     }
     return;
   }
   const int b = t >> 2, g = t & 3;
   const int jlo = 8 * b + 2 * g;
-  const uint2 blo = codes8(jlo, q), bhi = codes8(jlo + 1, q);
-  const float2 alo = ds(jlo), ahi = ds(jlo + 1);
+  const uint2 alo = codes8(jlo, q), ahi = codes8(jlo + 1, q);
+  float2 slo[4], shi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    slo[i] = ds(4 * q + i, jlo);
+    shi[i] = ds(4 * q + i, jlo + 1);
+  }
 #pragma unroll
   for (int mi = 0; mi < NM; ++mi) {
-    const uint8_t* blkA = mats[mi] + (long)(rv ? r : 0) * rb + (long)b * block_bytes(TYPE);
-    uint2 wlo = kq_codes8<TYPE>(blkA, g, q, 0), whi = kq_codes8<TYPE>(blkA, g, q, 1);
+    const uint8_t* blk = mats[mi] + ro + (long)b * block_bytes(TYPE);
+    uint2 wlo = kq_codes8<TYPE>(blk, g, q, 0), whi = kq_codes8<TYPE>(blk, g, q, 1);
     if (!rv) wlo = whi = make_uint2(0u, 0u);
-    const v4i Dlo = mfma_i8(wlo, blo), Dhi = mfma_i8(whi, bhi);
+    const v4i Dlo = mfma_i8(alo, wlo), Dhi = mfma_i8(ahi, whi);
+    const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+    int sclo, mlo, schi, mhi;
+    kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g, sclo, mlo);
+    kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g + 1, schi, mhi);
+    const double d = (double)f16_to_f32(hdr.x);
+    const double dmin = (double)f16_to_f32(hdr.x >> 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ri = 4 * q + i;
-      const uint8_t* blk = mats[mi] + (long)(ri < nr ? ri : 0) * rb + (long)b * block_bytes(TYPE);
-      const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
-      int sclo, mlo, schi, mhi;
-      kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g, sclo, mlo);
-      kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g + 1, schi, mhi);
-      const double d = (double)f16_to_f32(hdr.x);
-      const double dmin = (double)f16_to_f32(hdr.x >> 16);
-      const double t1 = d * (double)sclo * (double)alo.x * (double)Dlo[i];
-      const double t2 = dmin * (double)mlo * (double)alo.y;
-      const double t3 = d * (double)schi * (double)ahi.x * (double)Dhi[i];
-      const double t4 = dmin * (double)mhi * (double)ahi.y;
+      const double t1 = d * (double)sclo * (double)slo[i].x * (double)Dlo[i];
+      const double t2 = dmin * (double)mlo * (double)slo[i].y;
+      const double t3 = d * (double)schi * (double)shi[i].x * (double)Dhi[i];
+      const double t4 = dmin * (double)mhi * (double)shi[i].y;
       v[mi][i] = ((t1 - t2) + t3) - t4;
     }
   }
@@ -198,7 +204,7 @@ __device__ __forceinline__ void i8_task(const uint8_t* const (&mats)[NM], long r
 
 // This wave's subtree: positions p0 .. p0+N-1 (N a power of two), each the sum
 // of tasks p, p+64, ... < T in order (0 past T), met pairwise in a balanced
-// tree.  out[mi][i] = the subtree's value for the lane's row i and token.
+// tree.  out[mi][i] = the subtree's value for the lane's row and token i.
 template <int TYPE, int NM, int N, class Codes, class DS>
 __device__ __forceinline__ void i8_subtree(const uint8_t* const (&mats)[NM], long rb, int nr, int T, int p0, Codes codes8,
                                            DS ds, double (&out)[NM][4]) {
@@ -503,12 +509,15 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
       const uint8_t* src1 = gp.shared ? a.sup + f0 * rbw : a.up + ((long)gp.e * a.F + f0) * rbw;
       const uint8_t* w0 = src0;
       const uint8_t* w1 = src1;
-      const uint8_t* xq0 = a.xq;   // token t's blocks at xq0 + t * nb * 36
-      const int m = 16 * j + (lane & 15);
-      const bool mv = m < gp.ne;
-      int t = 0, s = 0;
-      if (mv) member(a, gp, m, t, s);
-      long xq_stride = (long)t * nb * kQ81Bytes;
+      const int nm = min(16, gp.ne - 16 * j);   // tokens of this tile
+      __shared__ int s_tok[16];                  // token of tile position c
+      if ((int)threadIdx.x < nm) {
+        int tc, sc_;
+        member(a, gp, 16 * j + (int)threadIdx.x, tc, sc_);
+        s_tok[threadIdx.x] = tc;
+      }
+      const uint8_t* xq0 = a.xq;   // tile token c's blocks at xq0 + tokoff(c)
+      bool staged = false;
       if (a.stage_gu) {
         // one bulk load of the block's rows and the tile's activations, so
         // the task loop reads LDS instead of waiting on memory per task
@@ -516,27 +525,27 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
         uint8_t* xst = wst + 2L * kBRows * rbw;
         copy_to_lds(wst, src0, nr * rbw);
         copy_to_lds(wst + kBRows * rbw, src1, nr * rbw);
-        const int nm = min(16, gp.ne - 16 * j);
-        for (int c = 0; c < nm; ++c) {
-          int tc, sc_;
-          member(a, gp, 16 * j + c, tc, sc_);
-          copy_to_lds(xst + (long)c * nb * kQ81Bytes, a.xq + (long)tc * nb * kQ81Bytes, (long)nb * kQ81Bytes);
-        }
-        __syncthreads();
+        __syncthreads();   // s_tok
+        for (int c = 0; c < nm; ++c)
+          copy_to_lds(xst + (long)c * nb * kQ81Bytes, a.xq + (long)s_tok[c] * nb * kQ81Bytes, (long)nb * kQ81Bytes);
         w0 = wst;
         w1 = wst + kBRows * rbw;
         xq0 = xst;
-        xq_stride = (long)(lane & 15) * nb * kQ81Bytes;
+        staged = true;
       }
-      const uint8_t* xqt = xq0 + (mv ? xq_stride : 0);
+      __syncthreads();
+      auto tokoff = [&](int c) -> long { return (long)(staged ? c : s_tok[c]) * nb * kQ81Bytes; };
+      const int cl = lane & 15;
+      const bool mv = cl < nm;
+      const uint8_t* xqt = xq0 + (mv ? tokoff(cl) : 0);
       auto codes8 = [&](int blk, int q) -> uint2 {
         if (!mv) return make_uint2(0u, 0u);
         const uint32_t* c = reinterpret_cast<const uint32_t*>(xqt + (long)blk * kQ81Bytes + 4 + 8 * q);
         return make_uint2(c[0], c[1]);
       };
-      auto ds = [&](int blk) -> float2 {
-        if (!mv) return make_float2(0.f, 0.f);
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(xqt + (long)blk * kQ81Bytes);
+      auto ds = [&](int c, int blk) -> float2 {
+        if (c >= nm) return make_float2(0.f, 0.f);
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(xq0 + tokoff(c) + (long)blk * kQ81Bytes);
         return make_float2(f16_to_f32(w), f16_to_f32(w >> 16));
       };
       double gu[2][4];
@@ -544,11 +553,14 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
       const uint8_t* const mats[2] = {w0, w1};
       if (gp.shared) first = i8_rows<ST, 2>(mats, rbw, nr, tasks_per_row(ST, H), codes8, ds, buf, gu);
       else first = i8_rows<MOE_TYPE_Q4_K, 2>(mats, rbw, nr, tasks_per_row(MOE_TYPE_Q4_K, H), codes8, ds, buf, gu);
-      if (first && mv) {
+      const int rr = lane & 15;   // the lane's row
+      if (first && rr < nr) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rr = 4 * (lane >> 4) + i;
-          if (rr >= nr) continue;
+          const int c = 4 * (lane >> 4) + i;   // the lane's tokens
+          if (c >= nm) continue;
+          int t, s;
+          member(a, gp, 16 * j + c, t, s);
           const float g = (float)gu[0][i], u = (float)gu[1][i];
           const float hv = (float)(silu_f64((double)g) * (double)u);
           if (gp.shared) a.hs[(long)t * a.Fs + f0 + rr] = hv;
@@ -667,9 +679,9 @@ __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
         if (!mv) return make_uint2(0u, 0u);
         return *reinterpret_cast<const uint2*>(codes + (long)c * Kx + 32 * blk + 8 * q);
       };
-      auto ds = [&](int blk) -> float2 {
-        if (!mv) return make_float2(0.f, 0.f);
-        return make_float2(dq[c * nb + blk], sq[c * nb + blk]);
+      auto ds = [&](int c2, int blk) -> float2 {
+        if (c2 >= nm) return make_float2(0.f, 0.f);
+        return make_float2(dq[c2 * nb + blk], sq[c2 * nb + blk]);
       };
       double yv[1][4];
       bool first;
@@ -685,13 +697,14 @@ __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
       const uint8_t* const mats[1] = {w0};
       if (gp.shared) first = i8_rows<ST, 1>(mats, rb, nr, tasks_per_row(ST, Kx), codes8, ds, buf, yv);
       else first = i8_rows<DT, 1>(mats, rb, nr, tasks_per_row(DT, Kx), codes8, ds, buf, yv);
-      if (first && mv) {
-        int t, s;
-        member(a, gp, 16 * j + c, t, s);
+      const int rr = lane & 15;   // the lane's row
+      if (first && rr < nr) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rr = 4 * (lane >> 4) + i;
-          if (rr >= nr) continue;
+          const int c2 = 4 * (lane >> 4) + i;   // the lane's tokens
+          if (c2 >= nm) continue;
+          int t, s;
+          member(a, gp, 16 * j + c2, t, s);
           if (gp.shared) a.ys[(long)t * H + i0 + rr] = (float)yv[0][i];
           else a.y[((long)t * a.k + s) * H + i0 + rr] = (float)yv[0][i];
         }
