@@ -221,10 +221,7 @@ __device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* id
 // 128-byte line when the workspace has room, returns gridDim.x-1 to it and
 // leaves 0 behind) selects for the group's tokens, one token per wave at a
 // time.
-#ifndef MOE_ROUTER_RPB
-#define MOE_ROUTER_RPB 1
-#endif
-constexpr int kRouterRpb = MOE_ROUTER_RPB;
+constexpr int kRouterRpb = 1;   // router rows per workgroup
 __global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn, const float* W, const float* wsg,
                                                                  int n_tok, int H, int E, int k, float* logits,
                                                                  float* user_logits, int32_t* ids, float* wts,
