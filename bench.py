@@ -465,7 +465,8 @@ def main():
                "sample": f"{c['tokens']} whole tokens through the {cfg.layers}-layer stack (same weights and inputs)",
                "single_thread": {"value": c["us_per_token_1t"], "unit": "us/token", "cores": 1,
                                  "sample": f"{c['tokens_1t']} whole tokens"},
-               "cpu_model": cpu_model()}
+               "cpu_model": cpu_model(),
+               "achieved_GBs": res["alg_bytes_per_token"] / (c["us_per_token"] * 1e-6) / 1e9}
     kernel = "moe_stack_persistent" if res["mode"] == "persistent" else "per-token graph of per-layer kernels"
     line = {
         "metric": "MoE decode stage latency (us/token, 40 layers) + achieved HBM GB/s vs peak",
@@ -480,6 +481,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": res["kernel_GBs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": res["kernel_GBs"] / HBM_PEAK_GBS,
                      "traffic": res["traffic_bytes_per_launch"],
+                     # measured HBM bytes (committed counter summary) over the same launch time
+                     "traffic_GBs": (res["traffic_bytes_per_launch"] / (res["launch_us"] * 1e-6) / 1e9
+                                     if res["traffic_bytes_per_launch"] else None),
                      "alg_bytes_per_launch": res["alg_bytes_per_token"], "launch_us": res["launch_us"],
                      "stream_read_GBs": stream_read_gbs(q)},
         "cpu_baseline": cpu,
