@@ -475,7 +475,7 @@ __device__ __forceinline__ void stage_xq(const uint8_t* xq_all, const int* toks,
   }
 }
 
-// gate/up + SwiGLU of one group, 64 rows per block
+// gate/up + SwiGLU of one group, kBSmallRows (16) rows per block
 // (BIG: the instance for groups of group_min or more tokens; the other
 // instance takes the smaller groups, so each keeps its own register budget)
 template <int ST, bool BIG>
@@ -632,7 +632,8 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
   }
 }
 
-// down rows of one group, 64 output rows per block
+// down rows of one group: 64 output rows per block for a small group, 16 for a
+// big one (blockIdx.y counts 16-row units)
 template <int DT, int ST, bool BIG>
 __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
