@@ -202,15 +202,32 @@ __device__ __forceinline__ void i8_task(const uint8_t* const (&mats)[NM], long r
   }
 }
 
-// This wave's subtree: positions p0 .. p0+N-1 (N a power of two), each the sum
-// of tasks p, p+64, ... < T in order (0 past T), met pairwise in a balanced
-// tree.  out[mi][i] = the subtree's value for the lane's row and token i.
-template <int TYPE, int NM, int N, class Codes, class DS>
-__device__ __forceinline__ void i8_subtree(const uint8_t* const (&mats)[NM], long rb, int nr, int T, int p0, Codes codes8,
-                                           DS ds, double (&out)[NM][4]) {
-  constexpr int L = (N == 1) ? 1 : (N == 2) ? 2 : (N == 4) ? 3 : (N == 8) ? 4 : 5;
-  double stk[L][NM][4];
+// This wave's subtree: positions p0 .. p0+N-1 (N a power of two <= 16), each
+// the sum of tasks p, p+64, ... < T in order (0 past T), met pairwise in a
+// balanced tree.  out[mi][i] = the subtree's value for the lane's row and
+// token i.  A runtime loop with the task inlined once (the unrolled form did
+// not fit the instruction cache): the partial sums of the tree live in five
+// named levels, position n merging the levels of its trailing one bits (left
+// operand first), as the unrolled tree does.
+template <int NM>
+__device__ __forceinline__ void tree_set(double (&d)[NM][4], const double (&s)[NM][4]) {
 #pragma unroll
+  for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[mi][i] = s[mi][i];
+}
+template <int NM>
+__device__ __forceinline__ void tree_merge(const double (&left)[NM][4], double (&v)[NM][4]) {
+#pragma unroll
+  for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[mi][i] = left[mi][i] + v[mi][i];
+}
+template <int TYPE, int NM, class Codes, class DS>
+__device__ __forceinline__ void i8_subtree(const uint8_t* const (&mats)[NM], long rb, int nr, int T, int p0, int N,
+                                           Codes codes8, DS ds, double (&out)[NM][4]) {
+  double s0[NM][4], s1[NM][4], s2[NM][4], s3[NM][4], s4[NM][4];
+#pragma unroll 1
   for (int n = 0; n < N; ++n) {
     const int p = p0 + n;
     double v[NM][4];
@@ -218,41 +235,39 @@ __device__ __forceinline__ void i8_subtree(const uint8_t* const (&mats)[NM], lon
     for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[mi][i] = 0.0;
-    if (p < T) {
-      i8_task<TYPE, NM>(mats, rb, nr, p, codes8, ds, v);
-      for (int t = p + 64; t < T; t += 64) {
-        double w[NM][4];
-        i8_task<TYPE, NM>(mats, rb, nr, t, codes8, ds, w);
+#pragma unroll 1
+    for (int t = p; t < T; t += 64) {
+      double w[NM][4];
+      i8_task<TYPE, NM>(mats, rb, nr, t, codes8, ds, w);
+      if (t == p) tree_set<NM>(v, w);
+      else {
 #pragma unroll
         for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[mi][i] += w[mi][i];
       }
     }
-    // merge with the completed left siblings (n's trailing one bits), then park
-    int lvl = 0;
-#pragma unroll
-    for (int k = 0; k < L - 1; ++k) {
-      if (((n >> k) & 1) == 0) break;
-#pragma unroll
-      for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[mi][i] = stk[k][mi][i] + v[mi][i];
-      lvl = k + 1;
+    const int tz = __builtin_ctz(~(unsigned)n);   // trailing one bits of n (wave-uniform)
+    if (tz >= 1) tree_merge<NM>(s0, v);
+    if (tz >= 2) tree_merge<NM>(s1, v);
+    if (tz >= 3) tree_merge<NM>(s2, v);
+    if (tz >= 4) tree_merge<NM>(s3, v);
+    switch (tz) {
+      case 0: tree_set<NM>(s0, v); break;
+      case 1: tree_set<NM>(s1, v); break;
+      case 2: tree_set<NM>(s2, v); break;
+      case 3: tree_set<NM>(s3, v); break;
+      default: tree_set<NM>(s4, v); break;
     }
-#pragma unroll
-    for (int k = 0; k < L; ++k)
-      if (k == lvl) {
-#pragma unroll
-        for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) stk[k][mi][i] = v[mi][i];
-      }
   }
-#pragma unroll
-  for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[mi][i] = stk[L - 1][mi][i];
+  // the root: the level of N's single bit
+  switch (N) {
+    case 1: tree_set<NM>(out, s0); break;
+    case 2: tree_set<NM>(out, s1); break;
+    case 4: tree_set<NM>(out, s2); break;
+    case 8: tree_set<NM>(out, s3); break;
+    default: tree_set<NM>(out, s4); break;
+  }
 }
 
 // The block's rows (nr <= 16) of NM matrices against one tile of tokens:
@@ -268,13 +283,7 @@ __device__ __forceinline__ bool i8_rows(const uint8_t* const (&mats)[NM], long r
   while (TP < T && TP < 64) TP <<= 1;
   const int N = TP / kBWaves, p0 = wave * N;
   double c[NM][4];
-  switch (N) {
-    case 1: i8_subtree<TYPE, NM, 1>(mats, rb, nr, T, p0, codes8, ds, c); break;
-    case 2: i8_subtree<TYPE, NM, 2>(mats, rb, nr, T, p0, codes8, ds, c); break;
-    case 4: i8_subtree<TYPE, NM, 4>(mats, rb, nr, T, p0, codes8, ds, c); break;
-    case 8: i8_subtree<TYPE, NM, 8>(mats, rb, nr, T, p0, codes8, ds, c); break;
-    default: i8_subtree<TYPE, NM, 16>(mats, rb, nr, T, p0, codes8, ds, c); break;
-  }
+  i8_subtree<TYPE, NM>(mats, rb, nr, T, p0, N, codes8, ds, c);
 #pragma unroll
   for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
