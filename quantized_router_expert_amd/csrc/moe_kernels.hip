@@ -217,15 +217,20 @@ __device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* id
 // e == E) for up to kRouterTok tokens, so a row is read once per token group;
 // the waves of a row take interleaved parts of it and their fp64 partial
 // sums are added in wave order.  The last workgroup of a token group to
-// finish (a wrapping atomic increment on the group's counter, one counter per
-// 128-byte line when the workspace has room, returns gridDim.x-1 to it and
-// leaves 0 behind) selects for the group's tokens, one token per wave at a
-// time.
+// finish selects for the group's tokens, one token per wave at a time.  It is
+// found with wrapping atomic increments (each returns limit-1 to its last
+// arrival and leaves 0 behind), one counter per 128-byte line when the
+// workspace has room.  With nsub > 0 (the group's counters are slot 0, the
+// top, and slots 1..nsub) workgroup x counts on sub-counter x % nsub and the
+// last arrival of each sub-counter on the top one, so no counter takes more
+// than about gridDim.x / nsub increments (increments of one address are
+// performed one after another); with nsub == 0 all count on slot 0.
 constexpr int kRouterRpb = 1;   // router rows per workgroup
 __global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn, const float* W, const float* wsg,
                                                                  int n_tok, int H, int E, int k, float* logits,
                                                                  float* user_logits, int32_t* ids, float* wts,
-                                                                 float* sg_out, unsigned* counters, int cstride) {
+                                                                 float* sg_out, unsigned* counters, int cstride,
+                                                                 int nsub) {
   constexpr int kW = kRouterThreads / 64;
   constexpr int kWpr = kW / kRouterRpb;   // waves per row
   __shared__ double part[kW][kRouterTok];
@@ -242,26 +247,33 @@ __global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn,
     for (int t = 0; t < kRouterTok; ++t) acc[t] = 0.0;
     if (row < nrows) {
       const float* wr = (row < E) ? W + (long)row * H : wsg;
+      // every load of a step goes out before the first product: token slots
+      // past nt read the last token again (their sums are never stored), so
+      // no branch separates the loads
       for (int i = (qw * 64 + lane) * 4; i < H; i += 256 * kWpr) {
         const float4 a = *reinterpret_cast<const float4*>(wr + i);
+        float4 b[kRouterTok];
+#pragma unroll
+        for (int t = 0; t < kRouterTok; ++t)
+          b[t] = *reinterpret_cast<const float4*>(xn + (long)(t0 + min(t, nt - 1)) * H + i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < kRouterTok; ++t) {
-          if (t < nt) {
-            const float4 b = *reinterpret_cast<const float4*>(xn + (long)(t0 + t) * H + i);
-            acc[t] += (double)a.x * (double)b.x;
-            acc[t] += (double)a.y * (double)b.y;
-            acc[t] += (double)a.z * (double)b.z;
-            acc[t] += (double)a.w * (double)b.w;
-          }
+          acc[t] += (double)a.x * (double)b[t].x;
+          acc[t] += (double)a.y * (double)b[t].y;
+          acc[t] += (double)a.z * (double)b[t].z;
+          acc[t] += (double)a.w * (double)b[t].w;
         }
       }
     }
+    // the kRouterTok reductions are independent chains
+    double red[kRouterTok];
 #pragma unroll
-    for (int t = 0; t < kRouterTok; ++t) {
-      if (t < nt) {
-        const double v = wave_sum_f64(acc[t]);
-        if (lane == 0) part[wave][t] = v;
-      }
+    for (int t = 0; t < kRouterTok; ++t) red[t] = wave_sum_f64(acc[t]);
+    if (lane == 0) {
+#pragma unroll
+      for (int t = 0; t < kRouterTok; ++t)
+        if (t < nt) part[wave][t] = red[t];
     }
     __syncthreads();
     if (threadIdx.x < kRouterRpb * nt) {
@@ -270,19 +282,38 @@ __global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn,
       if (r < nrows) {
         double v = part[rr * kWpr][t];
         for (int w2 = 1; w2 < kWpr; ++w2) v += part[rr * kWpr + w2][t];
-        logits[(long)(t0 + t) * logits_stride + r] = (float)v;
+        // agent-coherent store, complete before the counter moves: the
+        // workgroup that finishes last reads it after invalidating its own
+        // L2, so no workgroup has to write its L2 back (the release of an
+        // acq_rel counter increment would)
+        __hip_atomic_store(logits + (long)(t0 + t) * logits_stride + r, (float)v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
     }
   }
   __shared__ int is_last;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = __builtin_amdgcn_atomic_inc32(counters + (long)tg * cstride, gridDim.x - 1, __ATOMIC_ACQ_REL,
-                                                       "agent");
-    is_last = (old == gridDim.x - 1);
+    unsigned* const c0 = counters + (long)tg * (nsub + 1) * cstride;
+    if (nsub > 0) {
+      const unsigned j = blockIdx.x % (unsigned)nsub;
+      const unsigned nj = (gridDim.x - j + nsub - 1) / (unsigned)nsub;   // workgroups on sub-counter j
+      const unsigned o1 = __builtin_amdgcn_atomic_inc32(c0 + (1 + j) * cstride, nj - 1, __ATOMIC_RELAXED, "agent");
+      int last = 0;
+      if (o1 == nj - 1) {
+        const unsigned nz = min((unsigned)nsub, gridDim.x);   // sub-counters in use
+        last = __builtin_amdgcn_atomic_inc32(c0, nz - 1, __ATOMIC_RELAXED, "agent") == nz - 1;
+      }
+      is_last = last;
+    } else {
+      const unsigned old = __builtin_amdgcn_atomic_inc32(c0, gridDim.x - 1, __ATOMIC_RELAXED, "agent");
+      is_last = (old == gridDim.x - 1);
+    }
   }
   __syncthreads();
   if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   for (int t = wave; t < nt; t += kRouterThreads / 64) {
     const float* lg = logits + (long)(t0 + t) * logits_stride;
     wave_topk_softmax(lg, E, k, ids + (long)(t0 + t) * k, wts + (long)(t0 + t) * k);
@@ -701,10 +732,14 @@ int launch_router(const float* xn, const float* W, const float* wsg, int n_tok, 
                   float* user_logits, int32_t* ids, float* wts, float* sg, unsigned* counters, hipStream_t st) {
   const int nrows = E + (wsg ? 1 : 0);
   const int ngroups = (n_tok + kRouterTok - 1) / kRouterTok;
-  // one counter per 128-byte line when the counter area has room for it
-  const int cstride = (ngroups * 32 <= kCounterSlots) ? 32 : 1;
+  // one counter per 128-byte line when the counter area has room for it, and
+  // eight sub-counters per token group when it has room for those too
+  constexpr int kSub = 8;
+  const bool split = ngroups * (kSub + 1) * 32 <= kCounterSlots;
+  const int nsub = split ? kSub : 0;
+  const int cstride = (split || ngroups * 32 <= kCounterSlots) ? 32 : 1;
   hipLaunchKernelGGL(k_router_topk, dim3((nrows + kRouterRpb - 1) / kRouterRpb, ngroups), dim3(kRouterThreads), 0, st,
-                     xn, W, wsg, n_tok, H, E, k, logits, user_logits, ids, wts, sg, counters, cstride);
+                     xn, W, wsg, n_tok, H, E, k, logits, user_logits, ids, wts, sg, counters, cstride, nsub);
   return launch_ok();
 }
 
