@@ -413,24 +413,40 @@ __device__ __forceinline__ void topk_candidates(const float* lg, int E, int k, i
 }
 
 // wave 0, after a barrier: slot ids -> sel[0..k), their logits -> lgsel[0..k),
-// the shared-gate logit -> lgsel[k].  Lane kc*w + s holds candidate s of wave w
-// and counts the candidates above it over all 4*kc slots, read with unrolled
-// 16-byte loads (unused slots hold 0).  Returns true if an id is out of range.
+// the shared-gate logit -> lgsel[k].  Each candidate counts the candidates
+// above it over all 4*kc slots (unused slots hold 0, read with unrolled
+// 16-byte loads).  For kc == 8 (32 slots) lanes L and L+32 both hold slot L
+// and count half of the slots each; one cross-half lane swap adds the halves.
+// For kc == 16 lane L holds slot L and counts all 64.  Returns true unless
+// exactly k candidates rank below k (fewer than k valid experts).
 __device__ __forceinline__ bool rank_candidates(const float* lg, int E, int k, bool has_sg,
                                                 const unsigned long long* cand, uint32_t* sel, float* lgsel) {
   const int lane = threadIdx.x & 63;
   const int kc = cand_stride(k);
-  const unsigned long long c = (lane < 4 * kc && (lane & (kc - 1)) < k) ? cand[lane] : 0ull;
-  const int rank = (kc == 8) ? count_above<16>(reinterpret_cast<const ulonglong2*>(cand), c)
-                             : count_above<32>(reinterpret_cast<const ulonglong2*>(cand), c);
-  if (c != 0ull && rank < k) {
+  const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand);
+  unsigned long long c;
+  int rank;
+  bool mine;
+  if (kc == 8) {
+    const int slot = lane & 31;
+    c = ((slot & 7) < k) ? cand[slot] : 0ull;
+    const int part = count_above<8>(c2 + 8 * (lane >> 5), c);
+    const auto sw = __builtin_amdgcn_permlane32_swap(part, part, false, false);
+    rank = (int)sw[0] + (int)sw[1];
+    mine = lane < 32;
+  } else {
+    c = (lane < 4 * kc && (lane & (kc - 1)) < k) ? cand[lane] : 0ull;
+    rank = count_above<32>(c2, c);
+    mine = true;
+  }
+  const bool take = mine && c != 0ull && rank < k;
+  if (take) {
     const uint32_t id = ~(uint32_t)c;
     sel[rank] = id;
     lgsel[rank] = lg[id];
   }
   if (lane == 0) lgsel[k] = has_sg ? lg[E] : 0.0f;
-  const bool bad = (lane < k) && (sel[lane] >= (uint32_t)E);
-  return __any(bad);
+  return __popcll(__ballot(take)) != k;
 }
 
 // wave 0: routing weights sel[k..2k) and the shared gate sel[2k] from lgsel;
