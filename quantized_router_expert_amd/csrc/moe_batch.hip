@@ -324,6 +324,7 @@ struct BGroupArgs {
   float* ys;                // [n][H]
   int n, k, H, E, F, Fs, Kp, Kps, gmin, has_sg;
   int stage_gu, stage_dn;   // matrix-core groups: rows (and gate/up activations) staged in LDS
+  int stage_dma;            // gate/up rows streamed into LDS by buffer->LDS loads (whole KiB per block)
 };
 
 // the group of blockIdx.x: returns false if this block has no group
@@ -465,6 +466,36 @@ __device__ __forceinline__ void copy_to_lds(uint8_t* dst, const uint8_t* src, lo
   for (long i = threadIdx.x; i < (bytes >> 4); i += kBThreads) d4[i] = s4[i];
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// `bytes` from global src straight into LDS dst, 16 bytes per lane and 1 KiB
+// per wave instruction (buffer_load ... lds), the waves of the block taking
+// the KiB chunks in turn.  The loads hold no registers, so every chunk is in
+// flight at once; the loads are issued from inline asm, untracked by the
+// compiler, and the block waits for them with s_waitcnt vmcnt(0) and a
+// barrier.  The source descriptor is range-checked: lanes past `bytes` read
+// 0 and write it, so dst needs room up to the next KiB.
+__device__ __forceinline__ void dma_to_lds(uint8_t* dst, const uint8_t* src, uint32_t bytes) {
+  if (bytes == 0) return;
+  const unsigned long long ad = (unsigned long long)src;
+  typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+  v4u_t r;
+  r.x = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ad);
+  r.y = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(ad >> 32) & 0xffffu));
+  r.z = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000u;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)dst;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t nchunks = (bytes + 1023) >> 10;
+  for (uint32_t c = wave; c < nchunks; c += kBThreads / 64) {
+    const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (c << 10)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m), "v"((c << 10) + lane * 16), "s"(r)
+                 : "memory", "m0");
+  }
+}
+
 // Q8_1 activations of `nt` tokens unpacked into LDS (codes [nt][K], d/s [nt][K/32])
 __device__ __forceinline__ void stage_xq(const uint8_t* xq_all, const int* toks, int nt, int K, uint8_t* codes,
                                          float* dq, float* sq) {
@@ -532,11 +563,35 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
         // the task loop reads LDS instead of waiting on memory per task
         uint8_t* wst = smem + kI8Lds;
         uint8_t* xst = wst + 2L * kBRows * rbw;
-        copy_to_lds(wst, src0, nr * rbw);
-        copy_to_lds(wst + kBRows * rbw, src1, nr * rbw);
+        if (a.stage_dma) {
+          // the rows stream in while the threads copy the activations below
+          dma_to_lds(wst, src0, (uint32_t)(nr * rbw));
+          dma_to_lds(wst + kBRows * rbw, src1, (uint32_t)(nr * rbw));
+        } else {
+          copy_to_lds(wst, src0, nr * rbw);
+          copy_to_lds(wst + kBRows * rbw, src1, nr * rbw);
+        }
         __syncthreads();   // s_tok
-        for (int c = 0; c < nm; ++c)
-          copy_to_lds(xst + (long)c * nb * kQ81Bytes, a.xq + (long)s_tok[c] * nb * kQ81Bytes, (long)nb * kQ81Bytes);
+        // the tile's activations, token after token: four 16-byte words per
+        // thread in flight before any is stored
+        const int nx = (int)(((long)nb * kQ81Bytes) >> 4), nxt = nm * nx;
+        for (int base = 0; base < nxt; base += 4 * kBThreads) {
+          uint4 v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = base + u * kBThreads + (int)threadIdx.x;
+            if (i < nxt) {
+              const int c = i / nx;
+              v[u] = reinterpret_cast<const uint4*>(a.xq + (long)s_tok[c] * nb * kQ81Bytes)[i - c * nx];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = base + u * kBThreads + (int)threadIdx.x;
+            if (i < nxt) reinterpret_cast<uint4*>(xst)[i] = v[u];
+          }
+        }
+        if (a.stage_dma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         w0 = wst;
         w1 = wst + kBRows * rbw;
         xq0 = xst;
@@ -867,7 +922,7 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   a.Kps = has_sg ? pad_k(st_type, Fs) : 0;
   a.gmin = gmin;
   a.has_sg = has_sg;
-  a.stage_gu = a.stage_dn = 0;
+  a.stage_gu = a.stage_dn = a.stage_dma = 0;
   hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, st, ids, n, k, E, gmin, reinterpret_cast<int*>(ws + L.cnt),
                      reinterpret_cast<int*>(ws + L.moff), reinterpret_cast<int*>(ws + L.members),
                      reinterpret_cast<int*>(ws + L.dlist), reinterpret_cast<int*>(ws + L.nd),
@@ -888,6 +943,10 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   const size_t gu_stage = 2 * kBRows * (size_t)rbw_max + 16 * (size_t)(H / 32) * kQ81Bytes;
   a.stage_gu = kI8Lds + gu_stage <= kStageLdsMax && (reinterpret_cast<uintptr_t>(xq) & 15) == 0;
   const size_t lds_gu_big = kI8Lds + (a.stage_gu ? gu_stage : 0);
+  // streamed rows write whole KiB chunks: a block of kBRows rows must end on
+  // a KiB boundary so a short block's zero padding stays inside its own area
+  a.stage_dma = a.stage_gu && (kBRows * row_bytes(MOE_TYPE_Q4_K, H)) % 1024 == 0 &&
+                (!has_sg || (kBRows * row_bytes(st_type, H)) % 1024 == 0);
   void* args[] = {&a};
   {
     const bool q80 = st_type == MOE_TYPE_Q8_0;
