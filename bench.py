@@ -145,12 +145,15 @@ def time_steps(stack, steps, warmup, repeats):
     return per_token_us
 
 
-def batch_leg(q, sizes=(8, 32), group_min=4, iters=30):
+def batch_leg(q, sizes=(8, 32), group_min=9, iters=30):
     """The grouped batch path on one layer of the 40-layer shape: per batch
     size, microseconds per layer step (norm, router, grouped experts, combine)
     over `iters` steps on fresh seeded inputs, tokens/s, and GB/s over the
     bytes the step must read (router, shared expert, each distinct selected
-    expert once)."""
+    expert once).  group_min 9: groups of 9 or more tokens take the int8
+    matrix cores, whose tile is 16 tokens (a smaller group would leave more
+    than half of it empty); the measured best at batch 8 and 32 among 4, 6,
+    9, 12 and 16."""
     cfg = wl.CONFIGS["batch"]
     W = wl.layer_weights(cfg, 0, "cuda")
     H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
