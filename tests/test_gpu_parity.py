@@ -189,6 +189,36 @@ def test_topk_identical_logits_tie_heavy(q, orc, E, k):
     assert int(ws[:4 * n].view(torch.int32).abs().sum()) == 0
 
 
+@pytest.mark.parametrize("n", [1, 8, 112, 113, 1024, 1025])
+def test_router_counter_layouts(q, orc, n):
+    """The last-workgroup handshake in each of its counter layouts: eight
+    sub-counters and a top counter per token group (up to 14 groups of 8
+    tokens), one counter per 128-byte line (up to 128 groups), one per word
+    beyond.  Selection from identical logits (identity router) must match
+    the oracle on every token, twice in a row, and every counter word must be
+    back at zero after each launch."""
+    E, k, H = 256, 8, 256
+    gu.banner(f"router counter layouts n {n}")
+    rng = np.random.default_rng(n)
+    L = np.zeros((n, H), np.float32)
+    L[:, :E] = rng.standard_normal((n, E)).astype(np.float32)
+    L[::7, :E] = np.round(L[::7, :E])             # some tie-heavy tokens
+    W = _identity_router(E, H)
+    nb = q.router_ws_bytes(n, E)
+    ws = torch.zeros(nb + 256, dtype=torch.uint8, device="cuda")
+    ws = ws[(-ws.data_ptr()) % 256:][:nb]
+    q.moe_workspace_init(ws)
+    counter_bytes = 4 * 4096                      # the counter area ahead of the logits
+    ref = np.stack([orc.topk(L[t, :E], k) for t in range(n)])
+    for rep in range(2):
+        ids = torch.full((n, k), -1, dtype=torch.int32, device="cuda")
+        wts = torch.zeros(n, k, dtype=torch.float32, device="cuda")
+        q.router_topk(gu.dev(L), gu.dev(W), None, n, H, E, k, None, ids, wts, None, ws)
+        _sync()
+        assert np.array_equal(gu.host(ids), ref), rep
+        assert int(ws[:counter_bytes].view(torch.int32).abs().sum()) == 0, rep
+
+
 @pytest.mark.parametrize("cfg_name", ["tiny", "layer", "e128"])
 def test_router_topk_real(q, orc, cfg_name):
     cfg = wl.CONFIGS[cfg_name]
