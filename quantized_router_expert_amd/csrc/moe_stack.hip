@@ -352,11 +352,33 @@ __device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int kc,
   }
 }
 
+// Adds [k_i > c] to a_i for four keys.  The four compares write four
+// separate SGPR-pair masks and only then do the four carry-in adds read
+// them: the compiler's form puts every compare through VCC, each add waiting
+// on its own compare, a chain of one compare, two wait states and one add
+// per key.  Here each add reads a mask written three instructions earlier,
+// which covers the wait states a VALU-written mask needs before a VALU reads
+// it as a carry.
+__device__ __forceinline__ void count4_above(unsigned long long k0, unsigned long long k1, unsigned long long k2,
+                                             unsigned long long k3, unsigned long long c, int& a0, int& a1, int& a2,
+                                             int& a3) {
+  unsigned long long m0, m1, m2, m3;
+  asm volatile(
+      "v_cmp_gt_u64_e64 %4, %8, %12\n\t"
+      "v_cmp_gt_u64_e64 %5, %9, %12\n\t"
+      "v_cmp_gt_u64_e64 %6, %10, %12\n\t"
+      "v_cmp_gt_u64_e64 %7, %11, %12\n\t"
+      "v_addc_co_u32_e64 %0, %4, 0, %0, %4\n\t"
+      "v_addc_co_u32_e64 %1, %5, 0, %1, %5\n\t"
+      "v_addc_co_u32_e64 %2, %6, 0, %2, %6\n\t"
+      "v_addc_co_u32_e64 %3, %7, 0, %3, %7"
+      : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "=&s"(m0), "=&s"(m1), "=&s"(m2), "=&s"(m3)
+      : "v"(k0), "v"(k1), "v"(k2), "v"(k3), "v"(c));
+}
+
 // Count of the 2*NP keys at `k2` (NP pairs) that are above c.  The loads go
 // out in batches of 8 pairs, each batch before the compares of the previous
-// one, and the count is kept in four separate sums (the empty asm stops the
-// compiler from folding them back into one chain of dependent adds, which
-// would cost a full VALU latency per key).
+// one, and the count is kept in four separate sums.
 template <int NP>
 __device__ __forceinline__ int count_above(const ulonglong2* k2, unsigned long long c) {
   static_assert(NP % 8 == 0, "whole batches");
@@ -372,13 +394,7 @@ __device__ __forceinline__ int count_above(const ulonglong2* k2, unsigned long l
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      a0 += (v[j].x > c) ? 1 : 0;
-      a1 += (v[j].y > c) ? 1 : 0;
-      a2 += (v[j + 1].x > c) ? 1 : 0;
-      a3 += (v[j + 1].y > c) ? 1 : 0;
-      asm("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
-    }
+    for (int j = 0; j < 8; j += 2) count4_above(v[j].x, v[j].y, v[j + 1].x, v[j + 1].y, c, a0, a1, a2, a3);
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = nv[j];
   }
