@@ -53,10 +53,12 @@ __host__ __device__ constexpr inline int tasks_per_row(int type, int K) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 // round to nearest, ties to even; NaN stays NaN
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  // both results, then a select: a branch on NaN would cost an exec-mask
+  // region per conversion
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rn = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;   // round to nearest even
+  const uint32_t qn = (u >> 16) | 0x40u;                         // NaN stays a (quiet) NaN
+  return (uint16_t)((f != f) ? qn : rn);
 }
 // binary16 <-> fp32 through the hardware conversions (exact one way, round to
 // nearest even the other, subnormals kept).
