@@ -73,16 +73,14 @@ def _declare(L):
     L.orc_router_topk.argtypes = [P, P, P, P, P, P, P, P]; L.orc_router_topk.restype = None
     L.orc_expert_ffn.argtypes = [P, P, P, P, P, C.c_float, P]; L.orc_expert_ffn.restype = None
     L.orc_moe_layer.argtypes = [P, P, P, P, P, P, P]; L.orc_moe_layer.restype = C.c_int
+    L.orc_moe_layer_sel.argtypes = [P, P, P, P, P, P, P, P]; L.orc_moe_layer_sel.restype = C.c_int
     L.orc_moe_stack.argtypes = [P, P, C.c_int, P, P, P, P, P, P]; L.orc_moe_stack.restype = C.c_int
     L.orc_num_threads.argtypes = []; L.orc_num_threads.restype = C.c_int
     L.orc_quantize_q4k.argtypes = [P, P]; L.orc_quantize_q4k.restype = None
     L.orc_requant_q4k.argtypes = [P, C.c_int, C.c_int, C.c_int, P]; L.orc_requant_q4k.restype = C.c_int
     L.orc_set_threads.argtypes = [C.c_int]; L.orc_set_threads.restype = None
-    L.orc_moe_layer_batch.argtypes = [P, P, C.c_int, C.c_int, P, P, P, P, P]
+    L.orc_moe_layer_batch.argtypes = [P, P, C.c_int, P, P, P, P, P]
     L.orc_moe_layer_batch.restype = C.c_int
-    L.orc_row_dot_bf16.argtypes = [P, C.c_int, C.c_int, P, C.c_int]; L.orc_row_dot_bf16.restype = C.c_float
-    L.orc_rows_dot_bf16.argtypes = [P, C.c_int, C.c_int, C.c_int, P, C.c_int, C.c_int, P]
-    L.orc_rows_dot_bf16.restype = None
 
 
 def _p(a):
@@ -307,18 +305,24 @@ def _alloc_out(desc):
     }
 
 
-def moe_layer(desc, weights, residual=None, routed_prev=None, shared_prev=None, x=None):
-    """One layer for one token.  Returns a dict with every stored intermediate."""
+def moe_layer(desc, weights, residual=None, routed_prev=None, shared_prev=None, x=None, ids=None):
+    """One layer for one token.  Returns a dict with every stored intermediate.
+    ids (k experts in slot order) replaces the top-k selection (the near-tie
+    rule of chained comparisons); the routing weights are then the softmax
+    over those experts' logits."""
     L = lib()
     held = _Held()
     wst = make_weights(weights, held)
     out = _alloc_out(desc)
     lo = LayerOut(**{n: out[n].ctypes.data for n in _OUT_FIELDS})
-    rc = L.orc_moe_layer(C.byref(desc), C.byref(wst),
-                         held.hold(residual, np.uint16), held.hold(routed_prev, np.uint16),
-                         held.hold(shared_prev, np.uint16), held.hold(x, np.float32), C.byref(lo))
+    args = (C.byref(desc), C.byref(wst), held.hold(residual, np.uint16), held.hold(routed_prev, np.uint16),
+            held.hold(shared_prev, np.uint16), held.hold(x, np.float32))
+    if ids is None:
+        rc = L.orc_moe_layer(*args, C.byref(lo))
+    else:
+        rc = L.orc_moe_layer_sel(*args, held.hold(ids, np.int32), C.byref(lo))
     if rc != 0:
-        raise ValueError("oracle rejected the layer description")
+        raise ValueError("oracle rejected the layer description or the selection")
     out["ids"] = out["ids"].copy()
     out["h"] = out["h"].reshape(desc.k, desc.F)
     out["y"] = out["y"].reshape(desc.k, desc.H)
@@ -362,10 +366,10 @@ class BatchOut(C.Structure):
     _fields_ = [(n, P) for n in _BATCH_FIELDS]
 
 
-def moe_layer_batch(desc, weights, n_tok, threshold=4, residual=None, routed_prev=None, shared_prev=None, x=None):
-    """One layer for n_tok tokens at once, experts grouped (groups of at least
-    `threshold` tokens on the bf16 path).  Inputs are [n_tok][H] arrays;
-    returns a dict of [n_tok][...] arrays."""
+def moe_layer_batch(desc, weights, n_tok, residual=None, routed_prev=None, shared_prev=None, x=None):
+    """One layer for n_tok tokens at once, experts grouped by the tokens that
+    selected them; every group member gets the batch-1 integer path's result.
+    Inputs are [n_tok][H] arrays; returns a dict of [n_tok][...] arrays."""
     L = lib()
     held = _Held()
     wst = make_weights(weights, held)
@@ -382,29 +386,12 @@ def moe_layer_batch(desc, weights, n_tok, threshold=4, residual=None, routed_pre
         "shared_exact": np.zeros((n, H), np.float64),
     }
     bo = BatchOut(**{f: out[f].ctypes.data for f in _BATCH_FIELDS})
-    rc = L.orc_moe_layer_batch(C.byref(desc), C.byref(wst), n, threshold,
+    rc = L.orc_moe_layer_batch(C.byref(desc), C.byref(wst), n,
                                held.hold(residual, np.uint16), held.hold(routed_prev, np.uint16),
                                held.hold(shared_prev, np.uint16), held.hold(x, np.float32), C.byref(bo))
     if rc != 0:
         raise ValueError("oracle rejected the batch description")
     out["hs"] = out["hs"][:, :Fs]
-    return out
-
-
-def row_dot_bf16(row, typ, K, x, n=None):
-    """One weight row on the bf16 path: f32(sum bf16(f32(w_i)) * bf16(x_i)), i < n."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    row = _u8(row)
-    return float(lib().orc_row_dot_bf16(_p(row), typ, K, _p(x), len(x) if n is None else n))
-
-
-def rows_dot_bf16(rows, typ, K, n_rows, x):
-    """n_rows weight rows on the bf16 path against the vectors x [m][n] (n <= K;
-    elements past n are zero activations): returns fp32 [m][n_rows]."""
-    x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
-    rows = _u8(rows)
-    out = np.zeros((x.shape[0], n_rows), np.float32)
-    lib().orc_rows_dot_bf16(_p(rows), typ, K, n_rows, _p(x), x.shape[1], x.shape[0], _p(out))
     return out
 
 

@@ -12,6 +12,7 @@
 #include "moe_oracle.h"
 
 #include <math.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -95,6 +96,29 @@ static double rd_f16(const uint8_t* p) { return orc_f16_to_f64((uint16_t)(p[0] |
 /* Rounding to the fp32 storage type, then (where stated) to bf16. */
 static float st_f32(double v) { return (float)v; }
 static uint16_t st_bf16(double v) { return orc_f32_to_bf16((float)v); }
+
+/* Scratch allocation: the oracle has no way to continue without its
+ * buffers, so running out of memory ends the process with a message. */
+static void* must_alloc(size_t n)
+{
+    void* p = malloc(n ? n : 1);
+    if (!p) {
+        fputs("moe_oracle: out of memory\n", stderr);
+        abort();
+    }
+    return p;
+}
+
+static void* must_zalloc(size_t n, size_t size)
+{
+    void* p = calloc(n ? n : 1, size);
+    if (!p) {
+        fputs("moe_oracle: out of memory\n", stderr);
+        abort();
+    }
+    return p;
+}
+
 
 /* ------------------------------------------------------------------ */
 /* Block formats.  The pages name Q4_K, Q5_K, Q8_0 (34 bytes per block) */
@@ -445,7 +469,7 @@ void orc_add_rmsnorm(const uint16_t* residual, const uint16_t* routed, const uin
                      const float* w, int H, float eps,
                      uint16_t* out_sum, float* xn, uint8_t* xq)
 {
-    double* u = (double*)malloc(sizeof(double) * (size_t)H);
+    double* u = (double*)must_alloc(sizeof(double) * (size_t)H);
     for (int i = 0; i < H; ++i) {
         double t;
         if (routed && shared)
@@ -463,7 +487,7 @@ void orc_add_rmsnorm(const uint16_t* residual, const uint16_t* routed, const uin
     for (int i = 0; i < H; ++i)
         ss += u[i] * u[i];
     double r = 1.0 / sqrt(ss / (double)H + (double)eps);
-    float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+    float* xf = (float*)must_alloc(sizeof(float) * (size_t)H);
     for (int i = 0; i < H; ++i)
         xf[i] = st_f32((u[i] * r) * (double)w[i]);
     if (xn)
@@ -523,7 +547,7 @@ void orc_topk(const float* logits, int E, int k, int32_t* ids)
 void orc_softmax_selected(const float* logits, const int32_t* ids, int k, float* w)
 {
     double m = (double)logits[ids[0]];
-    double* p = (double*)malloc(sizeof(double) * (size_t)k);
+    double* p = (double*)must_alloc(sizeof(double) * (size_t)k);
     double s = 0.0;
     for (int j = 0; j < k; ++j) {
         p[j] = exp((double)logits[ids[j]] - m);
@@ -612,9 +636,9 @@ void orc_expert_ffn(const orc_desc* d, const orc_weights* w, const uint8_t* xq,
     int Kp = orc_pad_k(d->down_type, F);
     long gu_rb = orc_row_bytes(d->gate_up_type, H);
     long dn_rb = orc_row_bytes(d->down_type, Kp);
-    float* h = (float*)malloc(sizeof(float) * (size_t)k * F);
-    float* y = (float*)malloc(sizeof(float) * (size_t)k * H);
-    uint8_t* hq = (uint8_t*)malloc((size_t)(Kp / 32) * ORC_Q81_BYTES);
+    float* h = (float*)must_alloc(sizeof(float) * (size_t)k * F);
+    float* y = (float*)must_alloc(sizeof(float) * (size_t)k * H);
+    uint8_t* hq = (uint8_t*)must_alloc((size_t)(Kp / 32) * ORC_Q81_BYTES);
     for (int s = 0; s < k; ++s) {
         long e = ids[s];
         ffn_gate_up(w->gate + e * F * gu_rb, w->up + e * F * gu_rb, d->gate_up_type, H, F, xq, h + (long)s * F);
@@ -636,9 +660,9 @@ void orc_expert_ffn(const orc_desc* d, const orc_weights* w, const uint8_t* xq,
 
     if (Fs > 0) {
         int Kps = orc_pad_k(d->shared_type, Fs);
-        float* hs = (float*)malloc(sizeof(float) * (size_t)Fs);
-        float* ys = (float*)malloc(sizeof(float) * (size_t)H);
-        uint8_t* hqs = (uint8_t*)malloc((size_t)(Kps / 32) * ORC_Q81_BYTES);
+        float* hs = (float*)must_alloc(sizeof(float) * (size_t)Fs);
+        float* ys = (float*)must_alloc(sizeof(float) * (size_t)H);
+        uint8_t* hqs = (uint8_t*)must_alloc((size_t)(Kps / 32) * ORC_Q81_BYTES);
         ffn_gate_up(w->sgate, w->sup, d->shared_type, H, Fs, xq, hs);
         quantize_h_padded(hs, Fs, Kps, hqs);
         ffn_down(w->sdown, d->shared_type, H, Kps, hqs, ys);
@@ -677,18 +701,29 @@ static int desc_ok(const orc_desc* d)
     return 1;
 }
 
-int orc_moe_layer(const orc_desc* d, const orc_weights* w,
-                  const uint16_t* residual, const uint16_t* routed_prev, const uint16_t* shared_prev,
-                  const float* x, orc_layer_out* o)
+/* One layer; ids_in == NULL takes the selection from the top-k, otherwise
+ * ids_in[0..k) is the selection in slot order. */
+static int moe_layer_impl(const orc_desc* d, const orc_weights* w,
+                          const uint16_t* residual, const uint16_t* routed_prev, const uint16_t* shared_prev,
+                          const float* x, const int32_t* ids_in, orc_layer_out* o)
 {
     if (!desc_ok(d))
         return -1;
+    if (ids_in) {
+        for (int s = 0; s < d->k; ++s) {
+            if (ids_in[s] < 0 || ids_in[s] >= d->E)
+                return -1;
+            for (int t = 0; t < s; ++t)
+                if (ids_in[t] == ids_in[s])
+                    return -1;
+        }
+    }
     int H = d->H, E = d->E, k = d->k;
-    float* xn = (float*)malloc(sizeof(float) * (size_t)H);
-    uint8_t* xq = (uint8_t*)malloc((size_t)(H / 32) * ORC_Q81_BYTES);
-    float* logits = (float*)malloc(sizeof(float) * (size_t)E);
-    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
-    float* wts = (float*)malloc(sizeof(float) * (size_t)k);
+    float* xn = (float*)must_alloc(sizeof(float) * (size_t)H);
+    uint8_t* xq = (uint8_t*)must_alloc((size_t)(H / 32) * ORC_Q81_BYTES);
+    float* logits = (float*)must_alloc(sizeof(float) * (size_t)E);
+    int32_t* ids = (int32_t*)must_alloc(sizeof(int32_t) * (size_t)k);
+    float* wts = (float*)must_alloc(sizeof(float) * (size_t)k);
     float z = 0.0f, sg = 0.0f;
     if (d->norm) {
         orc_add_rmsnorm(residual, routed_prev, shared_prev, w->norm_w, H, d->eps, o->out_sum, xn, xq);
@@ -697,6 +732,11 @@ int orc_moe_layer(const orc_desc* d, const orc_weights* w,
         orc_quantize_q8_1(xn, H, xq);
     }
     orc_router_topk(d, w, xn, logits, &z, ids, wts, &sg);
+    if (ids_in) {
+        /* the given selection; its weights are the softmax over its logits */
+        memcpy(ids, ids_in, sizeof(int32_t) * (size_t)k);
+        orc_softmax_selected(logits, ids, k, wts);
+    }
     orc_expert_ffn(d, w, xq, ids, wts, sg, o);
     if (o->xn) memcpy(o->xn, xn, sizeof(float) * (size_t)H);
     if (o->xq) memcpy(o->xq, xq, (size_t)(H / 32) * ORC_Q81_BYTES);
@@ -713,123 +753,71 @@ int orc_moe_layer(const orc_desc* d, const orc_weights* w,
     return 0;
 }
 
+int orc_moe_layer(const orc_desc* d, const orc_weights* w,
+                  const uint16_t* residual, const uint16_t* routed_prev, const uint16_t* shared_prev,
+                  const float* x, orc_layer_out* o)
+{
+    return moe_layer_impl(d, w, residual, routed_prev, shared_prev, x, NULL, o);
+}
+
+/* Reading of the near-tie rule for chained comparisons: two implementations
+ * whose inputs to a layer differ by rounding may order two almost equal
+ * logits differently, and both selections are then correct.  The oracle can
+ * continue such a comparison with the other side's selection: the layer is
+ * computed as defined, except that the experts are the given ones (in the
+ * given slot order) and the routing weights the softmax over their logits. */
+int orc_moe_layer_sel(const orc_desc* d, const orc_weights* w,
+                      const uint16_t* residual, const uint16_t* routed_prev, const uint16_t* shared_prev,
+                      const float* x, const int32_t* ids_in, orc_layer_out* o)
+{
+    if (!ids_in)
+        return -1;
+    return moe_layer_impl(d, w, residual, routed_prev, shared_prev, x, ids_in, o);
+}
+
 
 /* ------------------------------------------------------------------ */
 /* a8: several tokens at once, grouped by expert.  The pages cover batch 1 */
-/* only; reading: the tokens whose top-k contains expert e form its group; */
-/* a group of at least `threshold` tokens runs on bf16 inputs -- weights   */
-/* f32(w_deq) then bf16, activations bf16(xn) and bf16(h), exact products, */
-/* the sum rounded once to fp32 -- and a smaller group runs the Q8_1       */
-/* integer path of a4/a5 for each of its tokens.  The shared expert is one */
-/* group of all tokens.  Norm, router, top-k, weights and the combine are  */
-/* the single-token steps applied to each token.                          */
+/* only; reading: the tokens whose top-k contains expert e form its group  */
+/* and the shared expert is one group of all tokens; every member of a     */
+/* group gets exactly what the batch-1 integer path (a4/a5) gives it, so   */
+/* the result does not depend on the batch it runs in.  Norm, router,      */
+/* top-k, weights and the combine are the single-token steps per token.    */
 /* ------------------------------------------------------------------ */
-
-/* bf16 of a value: first to fp32, then to bf16, both to nearest even. */
-static double bf16_of(double v) { return orc_bf16_to_f64(st_bf16(v)); }
-
-/* n_rows rows of K elements of `type`, decoded exactly and rounded as the
- * bf16 path feeds them: out[r*K + i] = bf16(f32(w)). */
-static void decode_rows_bf16(const uint8_t* rows, int type, int K, int n_rows, double* out)
-{
-    long rb = orc_row_bytes(type, K);
-    int per = (type == ORC_Q8_0) ? 32 : 256;
-    int r;
-#ifdef _OPENMP
-#pragma omp parallel for schedule(static)
-#endif
-    for (r = 0; r < n_rows; ++r) {
-        double blk[256];
-        for (int b = 0; b < K / per; ++b) {
-            const uint8_t* p = rows + rb * r + (long)b * (type == ORC_Q8_0 ? ORC_Q80_BYTES
-                                                       : (type == ORC_Q5_K ? ORC_Q5K_BYTES : ORC_Q4K_BYTES));
-            if (type == ORC_Q4_K) orc_decode_q4k(p, blk);
-            else if (type == ORC_Q5_K) orc_decode_q5k(p, blk);
-            else orc_decode_q8_0(p, blk);
-            for (int i = 0; i < per; ++i)
-                out[(long)r * K + (long)b * per + i] = bf16_of(blk[i]);
-        }
-    }
-}
-
-/* f32 of sum_{i<n} wb[i] * bf16(x[i]); wb already bf16 values, x fp32 */
-static float dot_bf16(const double* wb, const float* x, int n)
-{
-    double acc = 0.0;
-    for (int i = 0; i < n; ++i)
-        acc += wb[i] * bf16_of((double)x[i]);
-    return st_f32(acc);
-}
-
-/* Gate/up + SwiGLU and down of one expert on the bf16 path for the tokens
- * toks[0..nt): xn [n_tok][H] fp32; h_out [nt][F]; y_out [nt][H]. */
-static void expert_bf16(const uint8_t* gate, const uint8_t* up, int gu_type, const uint8_t* down, int dn_type,
-                        int H, int F, int Kp, const float* xn, const int* toks, int nt, float* h_out, float* y_out)
-{
-    double* G = (double*)malloc(sizeof(double) * (size_t)F * H);
-    double* U = (double*)malloc(sizeof(double) * (size_t)F * H);
-    double* D = (double*)malloc(sizeof(double) * (size_t)H * Kp);
-    decode_rows_bf16(gate, gu_type, H, F, G);
-    decode_rows_bf16(up, gu_type, H, F, U);
-    decode_rows_bf16(down, dn_type, Kp, H, D);
-    for (int j = 0; j < nt; ++j) {
-        const float* x = xn + (long)toks[j] * H;
-        float* h = h_out + (long)j * F;
-        float* y = y_out + (long)j * H;
-        int f, i;
-#ifdef _OPENMP
-#pragma omp parallel for schedule(static)
-#endif
-        for (f = 0; f < F; ++f) {
-            float g = dot_bf16(G + (long)f * H, x, H);
-            float u = dot_bf16(U + (long)f * H, x, H);
-            h[f] = st_f32(silu((double)g) * (double)u);
-        }
-        /* the padding past F holds zero activations (reading S14) */
-#ifdef _OPENMP
-#pragma omp parallel for schedule(static)
-#endif
-        for (i = 0; i < H; ++i)
-            y[i] = dot_bf16(D + (long)i * Kp, h, F);
-    }
-    free(D);
-    free(U);
-    free(G);
-}
 
 /* Q8_1 integer path of one expert for one token (a4/a5). */
 static void expert_int(const uint8_t* gate, const uint8_t* up, int gu_type, const uint8_t* down, int dn_type,
                        int H, int F, int Kp, const uint8_t* xq, float* h, float* y)
 {
-    uint8_t* hq = (uint8_t*)malloc((size_t)(Kp / 32) * ORC_Q81_BYTES);
+    uint8_t* hq = (uint8_t*)must_alloc((size_t)(Kp / 32) * ORC_Q81_BYTES);
     ffn_gate_up(gate, up, gu_type, H, F, xq, h);
     quantize_h_padded(h, F, Kp, hq);
     ffn_down(down, dn_type, H, Kp, hq, y);
     free(hq);
 }
 
-int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok, int threshold,
+int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok,
                         const uint16_t* residual, const uint16_t* routed_prev, const uint16_t* shared_prev,
                         const float* x, orc_batch_out* o)
 {
-    if (!desc_ok(d) || n_tok <= 0 || threshold < 1)
+    if (!desc_ok(d) || n_tok <= 0)
         return -1;
     int H = d->H, E = d->E, k = d->k, F = d->F, Fs = d->Fs;
     int Kp = orc_pad_k(d->down_type, F);
     int Kps = Fs > 0 ? orc_pad_k(d->shared_type, Fs) : 0;
     long gu_rb = orc_row_bytes(d->gate_up_type, H);
     long dn_rb = orc_row_bytes(d->down_type, Kp);
-    float* xn = (float*)malloc(sizeof(float) * (size_t)n_tok * H);
-    uint8_t* xq = (uint8_t*)malloc((size_t)n_tok * (H / 32) * ORC_Q81_BYTES);
-    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_tok * k);
-    float* wts = (float*)malloc(sizeof(float) * (size_t)n_tok * k);
-    float* sg = (float*)malloc(sizeof(float) * (size_t)n_tok);
-    float* logits = (float*)malloc(sizeof(float) * (size_t)E);
-    float* y = (float*)malloc(sizeof(float) * (size_t)n_tok * k * H);
-    float* ys = (float*)malloc(sizeof(float) * (size_t)n_tok * H);
-    int* cnt = (int*)calloc((size_t)E, sizeof(int));
-    int* toks = (int*)malloc(sizeof(int) * (size_t)n_tok);
-    int* slot_of = (int*)malloc(sizeof(int) * (size_t)n_tok);
+    float* xn = (float*)must_alloc(sizeof(float) * (size_t)n_tok * H);
+    uint8_t* xq = (uint8_t*)must_alloc((size_t)n_tok * (H / 32) * ORC_Q81_BYTES);
+    int32_t* ids = (int32_t*)must_alloc(sizeof(int32_t) * (size_t)n_tok * k);
+    float* wts = (float*)must_alloc(sizeof(float) * (size_t)n_tok * k);
+    float* sg = (float*)must_alloc(sizeof(float) * (size_t)n_tok);
+    float* logits = (float*)must_alloc(sizeof(float) * (size_t)E);
+    float* y = (float*)must_alloc(sizeof(float) * (size_t)n_tok * k * H);
+    float* ys = (float*)must_alloc(sizeof(float) * (size_t)n_tok * H);
+    int* cnt = (int*)must_zalloc((size_t)E, sizeof(int));
+    int* toks = (int*)must_alloc(sizeof(int) * (size_t)n_tok);
+    int* slot_of = (int*)must_alloc(sizeof(int) * (size_t)n_tok);
 
     /* a1..a3 per token */
     for (int t = 0; t < n_tok; ++t) {
@@ -860,15 +848,11 @@ int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok, int 
         const uint8_t* G = w->gate + (long)e * F * gu_rb;
         const uint8_t* U = w->up + (long)e * F * gu_rb;
         const uint8_t* D = w->down + (long)e * H * dn_rb;
-        float* h = (float*)malloc(sizeof(float) * (size_t)nt * F);
-        float* ye = (float*)malloc(sizeof(float) * (size_t)nt * H);
-        if (cnt[e] >= threshold) {
-            expert_bf16(G, U, d->gate_up_type, D, d->down_type, H, F, Kp, xn, toks, nt, h, ye);
-        } else {
-            for (int j = 0; j < nt; ++j)
-                expert_int(G, U, d->gate_up_type, D, d->down_type, H, F, Kp,
-                           xq + (long)toks[j] * (H / 32) * ORC_Q81_BYTES, h + (long)j * F, ye + (long)j * H);
-        }
+        float* h = (float*)must_alloc(sizeof(float) * (size_t)nt * F);
+        float* ye = (float*)must_alloc(sizeof(float) * (size_t)nt * H);
+        for (int j = 0; j < nt; ++j)
+            expert_int(G, U, d->gate_up_type, D, d->down_type, H, F, Kp,
+                       xq + (long)toks[j] * (H / 32) * ORC_Q81_BYTES, h + (long)j * F, ye + (long)j * H);
         for (int j = 0; j < nt; ++j) {
             memcpy(y + ((long)toks[j] * k + slot_of[j]) * H, ye + (long)j * H, sizeof(float) * (size_t)H);
             if (o->h) memcpy(o->h + ((long)toks[j] * k + slot_of[j]) * F, h + (long)j * F, sizeof(float) * (size_t)F);
@@ -878,15 +862,10 @@ int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok, int 
     }
     /* shared expert: one group of all tokens */
     if (Fs > 0) {
-        float* hs = (float*)malloc(sizeof(float) * (size_t)n_tok * Fs);
-        for (int t = 0; t < n_tok; ++t) toks[t] = t;
-        if (n_tok >= threshold) {
-            expert_bf16(w->sgate, w->sup, d->shared_type, w->sdown, d->shared_type, H, Fs, Kps, xn, toks, n_tok, hs, ys);
-        } else {
-            for (int t = 0; t < n_tok; ++t)
-                expert_int(w->sgate, w->sup, d->shared_type, w->sdown, d->shared_type, H, Fs, Kps,
-                           xq + (long)t * (H / 32) * ORC_Q81_BYTES, hs + (long)t * Fs, ys + (long)t * H);
-        }
+        float* hs = (float*)must_alloc(sizeof(float) * (size_t)n_tok * Fs);
+        for (int t = 0; t < n_tok; ++t)
+            expert_int(w->sgate, w->sup, d->shared_type, w->sdown, d->shared_type, H, Fs, Kps,
+                       xq + (long)t * (H / 32) * ORC_Q81_BYTES, hs + (long)t * Fs, ys + (long)t * H);
         if (o->hs) memcpy(o->hs, hs, sizeof(float) * (size_t)n_tok * Fs);
         free(hs);
     }
@@ -926,33 +905,6 @@ int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok, int 
     return 0;
 }
 
-/* Rows on the bf16 path against m vectors (test export):
- * out[j][r] = f32(sum_{i<n} bf16(f32(w_ri)) * bf16(x_j[i])), x [m][n]. */
-void orc_rows_dot_bf16(const uint8_t* rows, int type, int K, int n_rows, const float* x, int n, int m, float* out)
-{
-    double* wb = (double*)malloc(sizeof(double) * (size_t)K * n_rows);
-    decode_rows_bf16(rows, type, K, n_rows, wb);
-    for (int j = 0; j < m; ++j) {
-        int r;
-#ifdef _OPENMP
-#pragma omp parallel for schedule(static)
-#endif
-        for (r = 0; r < n_rows; ++r)
-            out[(long)j * n_rows + r] = dot_bf16(wb + (long)r * K, x + (long)j * n, n);
-    }
-    free(wb);
-}
-
-/* One row on the bf16 path (test export): f32(sum_{i<n} bf16(f32(w_i)) * bf16(x_i)). */
-float orc_row_dot_bf16(const uint8_t* row, int type, int K, const float* x, int n)
-{
-    double* wb = (double*)malloc(sizeof(double) * (size_t)K);
-    decode_rows_bf16(row, type, K, 1, wb);
-    float r = dot_bf16(wb, x, n);
-    free(wb);
-    return r;
-}
-
 /* Stack of L layers for one token.  Layer l reads the residual stream and
  * the previous layer's routed/shared outputs (zero before layer 0, so the
  * first norm sees the input itself); the stack output is the residual plus
@@ -966,10 +918,10 @@ int orc_moe_stack(const orc_desc* d, const orc_weights* layers, int L,
     if (!desc_ok(d) || !d->norm || L <= 0)
         return -1;
     int H = d->H;
-    uint16_t* res = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
-    uint16_t* routed = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
-    uint16_t* shared = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
-    uint16_t* nres = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+    uint16_t* res = (uint16_t*)must_alloc(sizeof(uint16_t) * (size_t)H);
+    uint16_t* routed = (uint16_t*)must_alloc(sizeof(uint16_t) * (size_t)H);
+    uint16_t* shared = (uint16_t*)must_alloc(sizeof(uint16_t) * (size_t)H);
+    uint16_t* nres = (uint16_t*)must_alloc(sizeof(uint16_t) * (size_t)H);
     memcpy(res, input, sizeof(uint16_t) * (size_t)H);
     memset(routed, 0, sizeof(uint16_t) * (size_t)H);
     memset(shared, 0, sizeof(uint16_t) * (size_t)H);
@@ -977,8 +929,8 @@ int orc_moe_stack(const orc_desc* d, const orc_weights* layers, int L,
     for (int l = 0; l < L && rc == 0; ++l) {
         orc_layer_out o;
         memset(&o, 0, sizeof(o));
-        uint16_t* nrouted = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
-        uint16_t* nshared = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+        uint16_t* nrouted = (uint16_t*)must_alloc(sizeof(uint16_t) * (size_t)H);
+        uint16_t* nshared = (uint16_t*)must_alloc(sizeof(uint16_t) * (size_t)H);
         o.out_sum = nres;
         o.routed = nrouted;
         o.shared = nshared;

@@ -157,6 +157,16 @@ int orc_moe_layer(const orc_desc* d, const orc_weights* w,
                   const uint16_t* residual, const uint16_t* routed_prev, const uint16_t* shared_prev,
                   const float* x, orc_layer_out* o);
 
+/* orc_moe_layer with the selection given: ids_in[0..k) (distinct, in
+ * [0, E)) are the experts in slot order and the routing weights are the
+ * softmax over their logits; everything else as defined.  For chained
+ * comparisons that hit a near tie (two logits closer than the other side's
+ * rounding can separate): the oracle continues with the other side's
+ * selection.  Returns -1 on an invalid selection. */
+int orc_moe_layer_sel(const orc_desc* d, const orc_weights* w,
+                      const uint16_t* residual, const uint16_t* routed_prev, const uint16_t* shared_prev,
+                      const float* x, const int32_t* ids_in, orc_layer_out* o);
+
 /* L-layer stack for one token: res_0 = input, previous outputs zero at layer 0;
  * layer l folds the previous layer's routed/shared into its norm; the result
  * is the fold a virtual layer L would do.  Per-layer outputs are optional
@@ -169,12 +179,11 @@ int orc_moe_stack(const orc_desc* d, const orc_weights* layers, int L,
                   uint16_t* resid_per_layer /* [L][H] or NULL: out_sum of each layer */);
 
 /* ---- several tokens at once, grouped by expert ----
- * Per token: a1..a3.  The tokens whose ids contain expert e form its group;
- * a group of >= threshold tokens runs on bf16 inputs (weights f32(w_deq) then
- * bf16, activations bf16(xn) and bf16(h), exact products, one fp32 rounding
- * of the sum), a smaller group runs the Q8_1 integer path per token.  The
- * shared expert is one group of all n_tok tokens.  Arrays are [n_tok][...]
- * versions of the single-token ones; every output pointer may be NULL. */
+ * Per token: a1..a3.  The tokens whose ids contain expert e form its group
+ * and the shared expert is one group of all n_tok tokens; each member of a
+ * group gets exactly the batch-1 integer path's result (a4..a6), so nothing
+ * depends on the batch.  Arrays are [n_tok][...] versions of the
+ * single-token ones; every output pointer may be NULL. */
 typedef struct {
     uint16_t* out_sum;       /* [n][H] */
     float* xn;               /* [n][H] */
@@ -193,16 +202,9 @@ typedef struct {
     double* shared_exact;    /* [n][H] */
 } orc_batch_out;
 
-int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok, int threshold,
+int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok,
                         const uint16_t* residual, const uint16_t* routed_prev, const uint16_t* shared_prev,
                         const float* x, orc_batch_out* o);
-
-/* One weight row on the bf16 path: f32(sum_{i<n} bf16(f32(w_i)) * bf16(x_i));
- * elements past n count as zero activations. */
-float orc_row_dot_bf16(const uint8_t* row, int type, int K, const float* x, int n);
-
-/* n_rows rows on the bf16 path against m vectors x [m][n]: out [m][n_rows]. */
-void orc_rows_dot_bf16(const uint8_t* rows, int type, int K, int n_rows, const float* x, int n, int m, float* out);
 
 /* Threads the OpenMP loops use (1 when built without OpenMP). */
 int orc_num_threads(void);

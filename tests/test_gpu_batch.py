@@ -5,9 +5,8 @@ Groups of group_min or more tokens run on the int8 matrix cores and give each
 token the value of the single-token integer path (the same integer sub-block
 dots, the same fp64 task expression, the same summation tree), smaller
 groups run that path member by member: the grouped path is batch-invariant.
-Its reference is the oracle's grouped definition with every group on the
-integer path (a threshold above the batch), which the oracle's own tests pin
-to its single-token path.
+Its reference is the oracle's grouped definition, which the oracle's own
+tests pin to its single-token path.
 
 Stage-isolated: the oracle's own xn, Q8_1 xq, ids, weights and gates go into
 expert_ffn_grouped; every h must match the oracle's fp32 value to one
@@ -38,7 +37,6 @@ def q():
 
 
 SMALL = wl.Config("small", H=512, E=16, k=4, F=128, Fs=256, router_dup=2, config_index=9)
-INTEGER_ONLY = 1 << 20   # an oracle threshold above any batch: every group on the integer path
 
 
 def _inputs(cfg, n):
@@ -88,7 +86,7 @@ def test_grouped_ffn_stage_isolated(q, orc, cfg_name, n, gmin, shared_type, down
     d_o = orc.make_desc(H, E, k, F, Fs, down_type=down_type, shared_type=shared_type, eps=cfg.eps)
     d_g = q.make_desc(H, E, k, F, Fs, down_type=down_type, shared_type=shared_type, eps=cfg.eps)
     inp = _inputs(cfg, n)
-    o = orc.moe_layer_batch(d_o, Wn, n, INTEGER_ONLY, **inp)
+    o = orc.moe_layer_batch(d_o, Wn, n, **inp)
     ws = q.alloc_batch_workspace(d_g, n)
     routed = torch.zeros(n, H, dtype=torch.bfloat16, device="cuda")
     shared = torch.zeros(n, H, dtype=torch.bfloat16, device="cuda")
@@ -124,7 +122,7 @@ def test_grouped_is_batch_invariant(q, orc, cfg_name, n, gmin, shared_type, down
     H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
     d_o = orc.make_desc(H, E, k, F, Fs, down_type=down_type, shared_type=shared_type, eps=cfg.eps)
     d_g = q.make_desc(H, E, k, F, Fs, down_type=down_type, shared_type=shared_type, eps=cfg.eps)
-    o = orc.moe_layer_batch(d_o, Wn, n, INTEGER_ONLY, **_inputs(cfg, n))
+    o = orc.moe_layer_batch(d_o, Wn, n, **_inputs(cfg, n))
     xq, ids, wts, sg = gu.dev(o["xq"]), gu.dev(o["ids"]), gu.dev(o["weights"]), gu.dev(o["shared_gate"])
     ws = q.alloc_batch_workspace(d_g, n)
     routed = torch.zeros(n, H, dtype=torch.bfloat16, device="cuda")
@@ -157,7 +155,7 @@ def test_decode_layer_batch_chained(q, orc, cfg_name, n, gmin):
     d_o = orc.make_desc(H, E, k, F, Fs, eps=cfg.eps)
     d_g = q.make_desc(H, E, k, F, Fs, eps=cfg.eps)
     inp = _inputs(cfg, n)
-    o = orc.moe_layer_batch(d_o, Wn, n, INTEGER_ONLY, **inp)
+    o = orc.moe_layer_batch(d_o, Wn, n, **inp)
     ws = q.alloc_batch_workspace(d_g, n)
     io = {"residual": gu.dev_u16(inp["residual"]), "routed_in": gu.dev_u16(inp["routed_prev"]),
           "shared_in": gu.dev_u16(inp["shared_prev"]),

@@ -166,3 +166,43 @@ def test_zero_token_stays_zero(orc):
     o = orc.moe_layer(desc, Ws[0], np.zeros(cfg.H, np.uint16), None, None)
     assert np.all(o["weights"] == np.float32(1.0 / cfg.k))
     assert np.array_equal(o["routed"], np.zeros(cfg.H, np.uint16))
+
+
+def test_layer_with_given_selection(orc):
+    """The near-tie continuation: a layer run with a given selection.  Given
+    the top-k it would pick itself, every output is bit-identical to the plain
+    layer; given another selection, the routed output is the dense-pinned
+    expert FFN of those experts weighted by the softmax over their own logits
+    (so the rank order of the weights follows the logits, not the slots), and
+    everything before the selection (norm, logits, shared gate) and the shared
+    output are unchanged.  Invalid selections are refused."""
+    cfg = wl.variant(wl.CONFIGS["layer"], E=32)
+    W = _np_weights(cfg)
+    ti, pv = wl.token_inputs(cfg, 1), wl.prev_outputs(cfg, 1)
+    res, rp, sp = wl.u16(ti["residual"]), wl.u16(pv["routed_prev"]), wl.u16(pv["shared_prev"])
+    desc = orc.make_desc(cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs)
+    o = orc.moe_layer(desc, W, res, rp, sp)
+    same = orc.moe_layer(desc, W, res, rp, sp, ids=o["ids"])
+    for key in ("out_sum", "xn", "xq", "logits", "ids", "weights", "shared_gate", "h", "y", "routed", "shared"):
+        assert np.array_equal(o[key], same[key]), key
+    # ranks k-1 and k swapped in, slot order reversed
+    order = np.lexsort((np.arange(cfg.E), -o["logits"].astype(np.float64)))
+    alt = np.concatenate([order[:cfg.k - 1], order[cfg.k:cfg.k + 1]])[::-1].astype(np.int32)
+    a = orc.moe_layer(desc, W, res, rp, sp, ids=alt)
+    assert np.array_equal(a["ids"], alt)
+    for key in ("out_sum", "xn", "xq", "logits", "shared_gate", "shared"):
+        assert np.array_equal(o[key], a[key]), key
+    lg = o["logits"].astype(np.float64)[alt]
+    p = np.exp(lg - lg[0])
+    assert np.allclose(a["weights"], p / p.sum(), rtol=2 ** -22, atol=0)
+    assert np.all(np.diff(a["weights"]) >= 0)          # slots go from the smallest logit up
+    f = orc.expert_ffn(desc, W, o["xq"], alt, a["weights"], float(o["shared_gate"][0]))
+    assert np.array_equal(a["routed"], f["routed"]) and np.array_equal(a["y"], f["y"])
+    # expert alt[s]'s rows land in slot s: its y is that of the same expert in the plain run
+    s_plain = {int(e): s for s, e in enumerate(o["ids"])}
+    for s, e in enumerate(alt):
+        if int(e) in s_plain:
+            assert np.array_equal(a["y"][s], o["y"][s_plain[int(e)]])
+    for bad in ([0] * cfg.k, list(range(cfg.k - 1)) + [cfg.E], list(range(cfg.k - 1)) + [-1]):
+        with pytest.raises(ValueError):
+            orc.moe_layer(desc, W, res, rp, sp, ids=np.array(bad, np.int32))
