@@ -9,7 +9,7 @@ before timing.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 128] [--warmup 8] [--mode auto|kernels|persistent]
                   [--variant after|before|both] [--no-cpu] [--no-batch] [--no-requant]
-                  [--no-e128] [--calib-copy] [--trace]
+                  [--no-e128] [--no-layer] [--calib-copy] [--trace]
 """
 import argparse
 import json
@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--no-batch", action="store_true", help="skip the grouped batch-path leg")
     p.add_argument("--no-requant", action="store_true", help="skip the load-time requantisation leg")
     p.add_argument("--no-e128", action="store_true", help="skip the 128-expert 48-layer stack leg")
+    p.add_argument("--no-layer", action="store_true", help="skip the single-layer moe_decode_layer leg")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--cpu-seconds-1t", type=float, default=6.0, help="single-thread oracle time")
     p.add_argument("--calib-copy", action="store_true",
@@ -145,6 +146,107 @@ def time_steps(stack, steps, warmup, repeats):
     return per_token_us
 
 
+def layer_leg(q, n_inputs=128, repeats=5):
+    """One Qwen3.6-shaped layer (H 2048, 256 experts top-8, F 512, shared 512,
+    Q4_K) through the per-layer entry point moe_decode_layer, batch 1, on
+    n_inputs fresh seeded inputs (residual, previous routed and shared
+    outputs ~N(0,1) bf16), each input's call captured in its own HIP graph and
+    the graphs replayed back to back: microseconds per layer call (median of
+    `repeats` passes), and GB/s over the bytes the layer must read (router,
+    norm weight, shared-gate row, the 8 selected experts, the shared expert).
+    The routed weights of the layer (453 MB) exceed the 256 MB last-level
+    cache, and each input selects other experts."""
+    cfg = wl.CONFIGS["layer"]
+    W = wl.layer_weights(cfg, 0, "cuda")
+    H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+    desc = q.make_desc(H, E, k, F, Fs, eps=cfg.eps)
+    lw = q.make_weights(W)
+    ws = q.alloc_workspace(desc)
+    ios = []
+    for t in range(n_inputs):
+        ti, pv = wl.token_inputs(cfg, t, "cuda"), wl.prev_outputs(cfg, t, "cuda")
+        ios.append({"residual": ti["residual"], "routed_in": pv["routed_prev"], "shared_in": pv["shared_prev"],
+                    "out_sum": torch.empty(H, dtype=torch.bfloat16, device="cuda"),
+                    "routed_out": torch.empty(H, dtype=torch.bfloat16, device="cuda"),
+                    "shared_out": torch.empty(H, dtype=torch.bfloat16, device="cuda")})
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q.moe_decode_layer(desc, lw, ios[0], ws)
+    s.synchronize()
+    graphs = []
+    for io in ios:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            q.moe_decode_layer(desc, lw, io, ws)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for g in graphs[:8]:
+        g.replay()
+    us = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for g in graphs:
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3 / n_inputs)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for io in ios:
+        q.moe_decode_layer(desc, lw, io, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager = e0.elapsed_time(e1) * 1e3 / n_inputs
+    med = float(np.median(us))
+    nbytes = algorithmic_bytes(cfg, wl.Q4_K, wl.Q4_K)
+    res = {"workload": f"one Qwen3.6-shaped layer through moe_decode_layer, batch 1, {n_inputs} fresh inputs, "
+                       "one HIP graph per input replayed back to back",
+           "us_per_layer": med, "us_p10": float(np.percentile(us, 10)), "us_p90": float(np.percentile(us, 90)),
+           "us_per_layer_eager": eager, "alg_bytes_per_layer": nbytes, "achieved_GBs": nbytes / (med * 1e-6) / 1e9}
+    res["frac_of_peak"] = res["achieved_GBs"] / HBM_PEAK_GBS
+    print(f"# layer (moe_decode_layer in graphs): {med:.1f} us per layer ({res['achieved_GBs']:.0f} GB/s); "
+          f"eager {eager:.1f} us", file=sys.stderr, flush=True)
+    del graphs, W
+    torch.cuda.empty_cache()
+    return res
+
+
+def check_against_kernels(q, stack, t=0):
+    """The timed path's output for token t against the per-layer kernel path
+    on the same input (another summation order, so rare last-bit
+    differences): fraction of equal bf16 outputs and relative L2 distance."""
+    if stack.mode != q.MOE_STACK_PERSISTENT:
+        return None
+    ws_k = q.alloc_workspace(stack.desc, stack.cfg.layers)
+    out_p = torch.zeros(stack.cfg.H, dtype=torch.bfloat16, device="cuda")
+    out_k = torch.zeros_like(out_p)
+    stack.q.moe_decode_stack(stack.desc, None, stack.inputs[t], out_p, None, None, q.MOE_STACK_PERSISTENT, stack.ws,
+                             layer_array=stack.arr)
+    stack.q.moe_decode_stack(stack.desc, None, stack.inputs[t], out_k, None, None, q.MOE_STACK_KERNELS, ws_k,
+                             layer_array=stack.arr)
+    torch.cuda.synchronize()
+    a, b = out_p.double(), out_k.double()
+    rel = float((a - b).norm() / b.norm())
+    del ws_k
+    return {"token": t, "bits_equal_frac": float((out_p.view(torch.int16) == out_k.view(torch.int16)).float().mean()),
+            "rel_l2": rel}
+
+
+def require_status_ok(q, stack, what):
+    """The persistent kernel's status word must be 0 after the timed launches
+    (1: a launch stopped at a bounded wait; 2: the bound table was not the
+    caller's); otherwise the run is invalid and the benchmark stops."""
+    if stack.mode != q.MOE_STACK_PERSISTENT:
+        return
+    st = q.stack_status(stack.desc, stack.cfg.layers, stack.ws)
+    if st != 0:
+        print(json.dumps({"error": f"{what}: persistent stack status word {st} after the timed launches"}))
+        sys.exit(1)
+
+
 def batch_leg(q, sizes=(8, 32), group_min=9, iters=30):
     """The grouped batch path on one layer of the 40-layer shape: per batch
     size, microseconds per layer step (norm, router, grouped experts, combine)
@@ -201,12 +303,14 @@ def e128_leg(q, steps, warmup, repeats):
     med = float(np.median(us))
     alg = algorithmic_bytes(cfg3, wl.Q4_K, wl.Q4_K)
     launch = launch_durations(stack, min(64, steps))
+    require_status_ok(q, stack, "e128")
+    check = check_against_kernels(q, stack)
     res = {"workload": f"128-expert variant: {cfg3.layers} layers, H 2048, 128 experts top-8, F 768, no shared "
                        f"expert, batch 1, {cfg3.tokens} sequential tokens",
            "us_per_token": med, "us_p10": float(np.percentile(us, 10)), "us_p90": float(np.percentile(us, 90)),
            "tokens_per_s": 1e6 / med, "alg_bytes_per_token": alg, "achieved_GBs": alg / (med * 1e-6) / 1e9,
            "us_per_layer": med / cfg3.layers, "launch_us": launch, "kernel_GBs": alg / (launch * 1e-6) / 1e9,
-           "mode": "persistent" if stack.mode == q.MOE_STACK_PERSISTENT else "kernels"}
+           "mode": "persistent" if stack.mode == q.MOE_STACK_PERSISTENT else "kernels", "output_check": check}
     res["frac_of_peak"] = res["kernel_GBs"] / HBM_PEAK_GBS
     res["traffic_bytes_per_launch"] = (measured_traffic("moe_stack_48L_e128_traffic")
                                        if res["mode"] == "persistent" else None)
@@ -280,11 +384,13 @@ def cpu_baseline(stack, seconds, seconds_1t):
                       shared_type=stack.shared_type, eps=cfg.eps)
     inputs = [wl.u16(stack.inputs[t]) for t in range(cfg.tokens)]
 
+    outs = {}
+
     def run(limit):
         n = 0
         t0 = time.time()
         while True:
-            orc.moe_stack(d, Wn, inputs[n % cfg.tokens])
+            outs[n % cfg.tokens] = orc.moe_stack(d, Wn, inputs[n % cfg.tokens])
             n += 1
             if time.time() - t0 >= limit or n >= cfg.tokens:
                 break
@@ -295,8 +401,24 @@ def cpu_baseline(stack, seconds, seconds_1t):
     orc.set_threads(1)
     us1, n1 = run(seconds_1t)
     orc.set_threads(threads)
+    # the timed path's outputs for the same tokens, computed again here (a short
+    # timed run need not have reached every token)
+    gout = torch.zeros(cfg.tokens, cfg.H, dtype=torch.bfloat16, device="cuda")
+    for t in outs:
+        stack.q.moe_decode_stack(stack.desc, None, stack.inputs[t], gout[t], None, None, stack.mode, stack.ws,
+                                 layer_array=stack.arr)
+    torch.cuda.synchronize()
+    g = gout.view(torch.int16).cpu().numpy().view(np.uint16)
+    eq, rels = [], []
+    for t, o in outs.items():
+        a = (g[t].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        b = (o.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        eq.append(float((g[t] == o).mean()))
+        rels.append(float(np.linalg.norm(a - b) / np.linalg.norm(b)))
+    check = {"tokens": len(outs), "bits_equal_frac_min": min(eq), "bits_equal_frac_mean": float(np.mean(eq)),
+             "rel_l2_max": max(rels)}
     return {"us_per_token": us, "tokens": n, "threads": threads, "copy_s": copy_s,
-            "us_per_token_1t": us1, "tokens_1t": n1}
+            "us_per_token_1t": us1, "tokens_1t": n1, "output_check": check}
 
 
 def stream_read_gbs(q, n_bytes=4 << 30, reps=10, blocks=512):
@@ -385,8 +507,6 @@ def cpu_model():
 
 def main():
     a = parse()
-    if a.trace:
-        os.environ["MOE_STACK_TRACE"] = "1"
     if a.gpus != 1:
         print(json.dumps({"error": f"--gpus {a.gpus}: this benchmark runs on one GPU only; the stage is a batch-1 "
                                    "decode step whose multi-GPU sharding is not built"}))
@@ -423,12 +543,18 @@ def main():
                "us_per_layer": med / cfg.layers, "mode": "persistent" if stack.mode == q.MOE_STACK_PERSISTENT else "kernels"}
         res["frac_of_peak"] = res["achieved_GBs"] / HBM_PEAK_GBS
         res["launch_us"] = launch_durations(stack, min(64, a.steps))
+        require_status_ok(q, stack, name)
+        res["output_check"] = check_against_kernels(q, stack)
         res["kernel_GBs"] = alg / (res["launch_us"] * 1e-6) / 1e9
         res["traffic_bytes_per_launch"] = (measured_traffic(f"moe_stack_40L_{name}_traffic")
                                            if res["mode"] == "persistent" else None)
         res["cold_us_per_token"] = cold_tokens(stack, 32)
         if a.trace and stack.mode == q.MOE_STACK_PERSISTENT:
-            stack.step(0)
+            # one more token with every workgroup stamping its events (the timed
+            # launches above ran without the per-workgroup stamps)
+            for t in range(3):
+                q.moe_decode_stack(stack.desc, None, stack.inputs[t], stack.out[t], None, None,
+                                   q.MOE_STACK_PERSISTENT, stack.ws, layer_array=stack.arr, trace=1)
             torch.cuda.synchronize()
             tr, mhz = q.stack_trace(stack.desc, cfg.layers, stack.ws)
             tr = tr[1:]   # layer 0 has no previous outputs to wait for
@@ -458,6 +584,7 @@ def main():
         results[name] = res
         print(f"# {name}: {med:.1f} us/token ({res['achieved_GBs']:.0f} GB/s)", file=sys.stderr, flush=True)
     stack, res = primary if primary else (None, results[order[0]])
+    layer = None if a.no_layer else layer_leg(q)
     e128 = None if a.no_e128 else e128_leg(q, a.steps, a.warmup, a.repeats)
     batch = None if a.no_batch else batch_leg(q)
     requant = None if a.no_requant else requant_leg(q)
@@ -469,7 +596,11 @@ def main():
                "single_thread": {"value": c["us_per_token_1t"], "unit": "us/token", "cores": 1,
                                  "sample": f"{c['tokens_1t']} whole tokens"},
                "cpu_model": cpu_model(),
-               "achieved_GBs": res["alg_bytes_per_token"] / (c["us_per_token"] * 1e-6) / 1e9}
+               "achieved_GBs": res["alg_bytes_per_token"] / (c["us_per_token"] * 1e-6) / 1e9,
+               "gpu_output_vs_oracle": c["output_check"]}
+        if c["output_check"]["rel_l2_max"] > 2e-3:
+            print(json.dumps({"error": "timed outputs differ from the oracle's", "check": c["output_check"]}))
+            sys.exit(1)
     kernel = "moe_stack_persistent" if res["mode"] == "persistent" else "per-token graph of per-layer kernels"
     line = {
         "metric": "MoE decode stage latency (us/token, 40 layers) + achieved HBM GB/s vs peak",
@@ -477,7 +608,8 @@ def main():
         "ms_per_step": res["us_per_token"] / 1e3, "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "q4_k x q8_1 (int8 dot), fp64 accumulate, bf16 out", "data": "synthetic",
         "config": {"workload": f"Qwen3.6-35B-A3B-shaped MoE stack: {cfg.layers} layers, H 2048, 256 experts top-8, "
-                               f"F 512, shared 512, batch 1, {cfg.tokens} sequential tokens",
+                               f"F 512, shared 512, batch 1; timed: {a.steps} sequential tokens per pass (inputs "
+                               f"cycling through {cfg.tokens} seeded N(0,1) tokens), {a.repeats} passes, median",
                    "variant": "shared Q4_K + routed down Q4_K", "parallelism": "none (1 GPU)"},
         "tokens_per_s": res["tokens_per_s"], "achieved_GBs": res["achieved_GBs"],
         "us_per_layer": res["us_per_layer"], "us_p10": res["us_p10"], "us_p90": res["us_p90"],
@@ -492,6 +624,7 @@ def main():
         "cpu_baseline": cpu,
         "variants": results,
         "e128": e128,
+        "layer": layer,
         "batch": batch,
         "requant": requant,
     }

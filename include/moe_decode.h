@@ -21,7 +21,8 @@
  *    read only during the call.
  *  - The caller allocates and owns every buffer, the workspace included.  The
  *    library keeps no mutable state between calls apart from what the caller's
- *    workspace holds; it never allocates device memory.
+ *    workspace holds and the host-side record of bound stacks (moe_stack_bind);
+ *    it never allocates device memory.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    null stream).  No call synchronises the host, reads device data back or
  *    issues a memset, so every call can be captured in a HIP graph.
@@ -253,34 +254,55 @@ int moe_decode_layer_batch(const moe_layer_desc* desc, const moe_layer_weights* 
  *   routed/shared outputs into its norm; output = bf16(res_L + t_L) with
  *   t_L = bf16(routed_{L-1} + shared_{L-1}) (the fold the next norm would do).
  * layers: host array of n_layers structs of device pointers.
+ *
  * mode MOE_STACK_KERNELS enqueues 4 kernels per layer plus the final fold on
- * `stream` (capture them in a HIP graph to remove launch overhead);
+ * `stream` (capture them in a HIP graph to remove launch overhead).
  * MOE_STACK_PERSISTENT runs every layer in one cooperative launch (one
- * workgroup per CU) and needs a prior moe_stack_bind of the same layers into
- * the same workspace (it copies the pointer table to the device, clears the
- * stack's exchange buffers and synchronises `stream` once; do not call it
- * during graph capture).  A launch checks on the device that the bound table
- * is the caller's; see moe_stack_status_offset for its status word.
- * MOE_STACK_AUTO uses the persistent kernel when the shape fits in LDS, else
- * the per-layer kernels.
- * ids_per_layer [L][k] int32 and resid_per_layer [L][H] bf16 (each layer's
- * out_sum) are optional device outputs.  desc->norm must be 1.
+ * workgroup per CU).  It needs a prior moe_stack_bind of the same layers into
+ * the same workspace, else it returns MOE_ERR_NOT_BOUND and enqueues nothing;
+ * bind copies the pointer table to the device, clears the stack's exchange
+ * buffers and synchronises `stream` once (do not call it during graph
+ * capture).  The library keeps a host-side record of the workspaces that
+ * hold a bound stack (workspace address, size, layer count and a hash of the
+ * whole pointer table), the only state it keeps outside the caller's
+ * buffers; moe_workspace_init of an overlapping range drops the record.  Each
+ * launch also checks on the device that the table bound in the workspace
+ * hashes to the caller's (see moe_stack_status_offset for the outcome).
+ * MOE_STACK_AUTO uses the persistent kernel when the layers are bound in this
+ * workspace and the shape fits in LDS, else the per-layer kernels.
+ * desc->norm must be 1.
  * ---------------------------------------------------------------------- */
 #define MOE_STACK_AUTO 0
 #define MOE_STACK_KERNELS 1
 #define MOE_STACK_PERSISTENT 2
+
+/* Device buffers of one moe_decode_stack call.  The per-layer outputs are
+ * optional (NULL = not written). */
+typedef struct moe_stack_io {
+    const uint16_t* input;   /* [H] bf16 token input (the residual of layer 0) */
+    uint16_t* output;        /* [H] bf16 stack output */
+    int32_t* ids;            /* [L][k] experts selected per layer, slot order */
+    uint16_t* resid;         /* [L][H] bf16 out_sum of each layer (the residual after its fold) */
+    uint16_t* routed;        /* [L][H] bf16 routed output of each layer */
+    uint16_t* shared;        /* [L][H] bf16 shared output of each layer (Fs > 0) */
+    int trace;               /* persistent mode: 1 = every workgroup stamps its phase events
+                                (moe_stack_trace_offset); 0 = only workgroup 0's phase table */
+} moe_stack_io;
+
 int moe_stack_bind(const moe_layer_desc* desc, const moe_layer_weights* layers, int n_layers,
                    void* ws, size_t ws_bytes, void* stream);
 int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers, int n_layers,
-                     const uint16_t* input, uint16_t* output, int32_t* ids_per_layer, uint16_t* resid_per_layer,
-                     int mode, void* ws, size_t ws_bytes, void* stream);
+                     const moe_stack_io* io, int mode, void* ws, size_t ws_bytes, void* stream);
 
 /* Byte offset, in a workspace sized for (desc, n_layers), of a uint32 status
- * word of the persistent stack: 0 while every launch completed, 1 after a
- * launch stopped at a bounded wait (its outputs are invalid), 2 after a launch
- * found no binding of the caller's layers (its output is set to NaN).  A
- * nonzero word stays until moe_stack_bind or moe_workspace_init clears the
- * workspace.  Returns 0 if the shape has no persistent stack. */
+ * word of the persistent stack: 0 while every launch completed; 1 after a
+ * launch stopped at a bounded wait; 2 after a launch found that the table
+ * bound in the workspace is not the caller's.  A launch that starts with a
+ * nonzero word does no work: it sets its output to NaN and leaves the word as
+ * it is.  So after a stopped or refused launch every later persistent launch
+ * on that workspace is refused too (their outputs are NaN), until
+ * moe_stack_bind (or moe_workspace_init) clears the word.  Returns 0 if the
+ * shape has no persistent stack. */
 size_t moe_stack_status_offset(const moe_layer_desc* desc, int n_layers);
 
 /* Byte offset, in the same workspace, of the persistent stack's phase
@@ -296,10 +318,8 @@ size_t moe_stack_status_offset(const moe_layer_desc* desc, int n_layers);
  * 4 shared h stored, 5 experts known, 6 routed gate/up rows landed, 7 routed h
  * stored, 8 down inputs quantised, 9 down rows landed, 10 layer outputs stored,
  * 11 input normalised, 12 input quantised, 13 logits received, 14 every h
- * received),
- * written only when the environment variable MOE_STACK_TRACE is "1" at the
- * library's first persistent launch.  Returns 0 if the shape has no
- * persistent stack. */
+ * received, 15 down rows queued), written only by launches with io->trace = 1.
+ * Returns 0 if the shape has no persistent stack. */
 size_t moe_stack_trace_offset(const moe_layer_desc* desc, int n_layers);
 
 /* ------------------------------------------------------------------------
@@ -354,6 +374,22 @@ int moe_stream_read(const void* p, size_t bytes, uint32_t* out, int blocks, void
  * Q8_1 blocks of 36 bytes (d, s, 32 codes).  All device.
  * ---------------------------------------------------------------------- */
 int moe_test_quantize_q81(const float* x, int n, void* xq, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Test export: the persistent stack kernel's own expert selection ([P273]
+ * Summary item 1: top-k by value with ties to the lower expert index, checked
+ * over tie-heavy cases), run on n_sets independent logit sets, one workgroup
+ * each, with the same device functions and barriers a layer uses.
+ * logits [n_sets][E+1] fp32 (element E of a set is the shared-gate logit,
+ * read when with_gate != 0); ids [n_sets][k] int32 (slot order; -1 for every
+ * slot of a set where fewer than k candidates ranked, which valid input never
+ * gives); weights [n_sets][k] fp32 = softmax over the selected logits;
+ * gate [n_sets] fp32 = sigmoid of the shared-gate logit (with_gate != 0).
+ * NaN ranks as -inf and -0 equals +0.  All device.  E 1..MOE_MAX_EXPERTS,
+ * k 1..min(E, MOE_MAX_TOPK), n_sets 1..65535.
+ * ---------------------------------------------------------------------- */
+int moe_test_stack_select(const float* logits, int n_sets, int n_experts, int top_k, int with_gate, int32_t* ids,
+                          float* weights, float* gate, void* stream);
 
 #ifdef __cplusplus
 }

@@ -48,6 +48,11 @@ class LayerWeights(C.Structure):
                                  "shared_gate", "shared_up", "shared_down")]
 
 
+class StackIO(C.Structure):
+    _fields_ = [("input", P), ("output", P), ("ids", P), ("resid", P), ("routed", P), ("shared", P),
+                ("trace", C.c_int)]
+
+
 class LayerIO(C.Structure):
     _fields_ = [(n, P) for n in ("residual", "routed_in", "shared_in", "x", "out_sum", "routed_out", "shared_out",
                                  "xn", "xq", "logits", "ids", "weights", "shared_gate", "h", "hs")]
@@ -71,8 +76,8 @@ _moe_decode_layer = _sig("moe_decode_layer", C.c_int, C.POINTER(LayerDesc), C.PO
                          C.POINTER(LayerIO), P, C.c_size_t, P)
 _moe_stack_bind = _sig("moe_stack_bind", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights), C.c_int, P,
                        C.c_size_t, P)
-_moe_decode_stack = _sig("moe_decode_stack", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights), C.c_int, P, P, P,
-                         P, C.c_int, P, C.c_size_t, P)
+_moe_decode_stack = _sig("moe_decode_stack", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights), C.c_int,
+                         C.POINTER(StackIO), C.c_int, P, C.c_size_t, P)
 _moe_batch_workspace_size = _sig("moe_batch_workspace_size", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
 _expert_ffn_grouped = _sig("expert_ffn_grouped", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights), P, P, P, P, P,
                            C.c_int, C.c_int, P, P, P, P, P, C.c_size_t, P)
@@ -83,12 +88,13 @@ _moe_stack_trace_offset = _sig("moe_stack_trace_offset", C.c_size_t, C.POINTER(L
 _moe_test_subblock_dots = _sig("moe_test_subblock_dots", C.c_int, P, C.c_int, C.c_int, C.c_int, P, P, P)
 _moe_test_quantize_q81 = _sig("moe_test_quantize_q81", C.c_int, P, C.c_int, P, P)
 _moe_stream_read = _sig("moe_stream_read", C.c_int, P, C.c_size_t, P, C.c_int, P)
+_moe_test_stack_select = _sig("moe_test_stack_select", C.c_int, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P)
 _moe_requant_q4k = _sig("moe_requant_q4k", C.c_int, P, C.c_int, C.c_int, C.c_int, P, P)
 
 EXPORTS = ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", "moe_stack_bind",
            "moe_decode_stack", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
            "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots", "moe_test_quantize_q81", "moe_stream_read", "moe_requant_q4k",
-           "moe_batch_workspace_size", "expert_ffn_grouped", "moe_decode_layer_batch")
+           "moe_batch_workspace_size", "expert_ffn_grouped", "moe_decode_layer_batch", "moe_test_stack_select")
 MAX_BATCH = 64
 MAX_GROUP_MIN = 16
 
@@ -240,11 +246,12 @@ def moe_stack_bind(desc, layers, ws, stream=None):
 
 
 def moe_decode_stack(desc, layers, inp, out, ids_per_layer=None, resid_per_layer=None, mode=MOE_STACK_AUTO, ws=None,
-                     stream=None, layer_array=None):
+                     stream=None, layer_array=None, routed_per_layer=None, shared_per_layer=None, trace=0):
     arr = layer_array if layer_array is not None else _layer_array(layers)
     n = len(arr)
-    return _check("moe_decode_stack", _moe_decode_stack(C.byref(desc), arr, n, ptr(inp), ptr(out), ptr(ids_per_layer),
-                                                        ptr(resid_per_layer), mode, ptr(ws),
+    io = StackIO(ptr(inp), ptr(out), ptr(ids_per_layer), ptr(resid_per_layer), ptr(routed_per_layer),
+                 ptr(shared_per_layer), int(trace))
+    return _check("moe_decode_stack", _moe_decode_stack(C.byref(desc), arr, n, C.byref(io), mode, ptr(ws),
                                                         ws.numel() * ws.element_size(), stream_handle(stream)))
 
 
@@ -286,13 +293,13 @@ TRACE_MAX_G = 256
 
 def stack_block_trace(desc, n_layers, ws):
     """Per-workgroup event times of the last persistent launch, in microseconds
-    of the device wall clock, as a [min(L, 64), 256, 16] float tensor (recorded
-    only when MOE_STACK_TRACE=1 was set before the library's first launch):
+    of the device wall clock, as a [min(L, 64), 256, 16] float tensor (written
+    only by launches made with trace=1):
     0 layer start, 1 previous outputs received, 2 fixed weights landed,
     3 router rows stored, 4 shared h stored, 5 experts known, 6 routed gate/up
     rows landed, 7 routed h stored, 8 down inputs quantised, 9 down rows landed,
     10 layer outputs stored, 11 input normalised, 12 input quantised, 13 logits
-    received, 14 every h received."""
+    received, 14 every h received, 15 down rows queued."""
     off = moe_stack_trace_offset(desc, n_layers)
     if off == 0:
         raise MoeError("moe_stack_trace_offset", -7)
@@ -317,6 +324,12 @@ def moe_stream_read(p, n_bytes, out, blocks, stream=None):
 
 def moe_test_quantize_q81(x, n, xq, stream=None):
     return _check("moe_test_quantize_q81", _moe_test_quantize_q81(ptr(x), n, ptr(xq), stream_handle(stream)))
+
+
+def moe_test_stack_select(logits, n_sets, n_experts, top_k, with_gate, ids, weights, gate=None, stream=None):
+    return _check("moe_test_stack_select", _moe_test_stack_select(ptr(logits), n_sets, n_experts, top_k, int(with_gate),
+                                                                  ptr(ids), ptr(weights), ptr(gate),
+                                                                  stream_handle(stream)))
 
 
 def moe_test_subblock_dots(rows, typ, K, n_rows, xq, out, stream=None):

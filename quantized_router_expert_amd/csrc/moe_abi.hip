@@ -3,6 +3,8 @@
 // passes validation.
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe_decode.h"
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -28,6 +30,41 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (!aligned(ws, 256)) return MOE_ERR_ALIGN;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   return MOE_OK;
+}
+
+// Host-side record of the workspaces that hold a bound stack: which layer
+// table (its length and hash) moe_stack_bind copied into which workspace.
+// moe_decode_stack consults it to refuse (PERSISTENT) or avoid (AUTO) the
+// persistent kernel on a workspace that does not hold the caller's layers.
+struct BindRecord {
+  uintptr_t ws;
+  size_t bytes;
+  int n_layers;
+  uint64_t hash;
+};
+constexpr int kBindRecords = 64;
+std::mutex g_bind_mu;
+BindRecord g_bind[kBindRecords];
+int g_bind_next = 0;
+
+void bind_forget(uintptr_t lo, size_t bytes) {
+  const uintptr_t hi = lo + bytes;
+  for (auto& r : g_bind)
+    if (r.ws && r.ws < hi && lo < r.ws + r.bytes) r = BindRecord{};
+}
+
+void bind_record(void* ws, size_t bytes, int n_layers, uint64_t hash) {
+  std::lock_guard<std::mutex> lock(g_bind_mu);
+  bind_forget((uintptr_t)ws, bytes);
+  g_bind[g_bind_next] = BindRecord{(uintptr_t)ws, bytes, n_layers, hash};
+  g_bind_next = (g_bind_next + 1) % kBindRecords;
+}
+
+bool bind_holds(void* ws, int n_layers, uint64_t hash) {
+  std::lock_guard<std::mutex> lock(g_bind_mu);
+  for (const auto& r : g_bind)
+    if (r.ws == (uintptr_t)ws && r.n_layers == n_layers && r.hash == hash) return true;
+  return false;
 }
 
 }  // namespace
@@ -58,6 +95,10 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (!ws) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_ALIGN;
   if (ws_bytes < 256) return MOE_ERR_WORKSPACE;
+  {
+    std::lock_guard<std::mutex> lock(g_bind_mu);
+    bind_forget((uintptr_t)ws, ws_bytes);
+  }
   return launch_fill(ws, ws_bytes / 4, 0u, as_stream(stream));
 }
 
@@ -248,61 +289,76 @@ int moe_stack_bind(const moe_layer_desc* desc, const moe_layer_weights* layers, 
   if (rc) return rc;
   hipStream_t st = as_stream(stream);
   if (L.stack == 0) return MOE_ERR_UNSUPPORTED;
+  {
+    // the record goes before the copies: if one of them fails, the workspace
+    // holds no complete table and must not count as bound
+    std::lock_guard<std::mutex> lock(g_bind_mu);
+    bind_forget((uintptr_t)ws, ws_bytes);
+  }
   if (hipMemcpyAsync(at<void>(ws, L.table), layers, sizeof(moe_layer_weights) * n_layers, hipMemcpyHostToDevice, st) !=
       hipSuccess)
     return MOE_ERR_HIP;
-  const int bound[4] = {(int)kBoundMagic, n_layers, 0, 0};
+  const uint64_t hash = layer_table_hash(layers, n_layers);
+  const uint32_t bound[4] = {kBoundMagic, (uint32_t)n_layers, (uint32_t)hash, (uint32_t)(hash >> 32)};
   if (hipMemcpyAsync(at<void>(ws, L.bound), bound, sizeof(bound), hipMemcpyHostToDevice, st) != hipSuccess)
     return MOE_ERR_HIP;
   // a fresh generation: control block and exchange words start from zero
   rc = launch_fill(at<void>(ws, L.stack), (L.total - L.stack) / 4, 0u, st);
   if (rc) return rc;
-  return hipStreamSynchronize(st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_ERR_HIP;
+  bind_record(ws, ws_bytes, n_layers, hash);
+  return MOE_OK;
 }
 
-int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers, int n_layers, const uint16_t* input,
-                     uint16_t* output, int32_t* ids_per_layer, uint16_t* resid_per_layer, int mode, void* ws,
-                     size_t ws_bytes, void* stream) {
+int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers, int n_layers, const moe_stack_io* io,
+                     int mode, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (!desc->norm) return MOE_ERR_UNSUPPORTED;
-  if (!layers || !input || !output) return MOE_ERR_NULL;
+  if (!layers || !io || !io->input || !io->output) return MOE_ERR_NULL;
   if (n_layers <= 0 || n_layers > MOE_MAX_LAYERS) return MOE_ERR_SHAPE;
   if (mode != MOE_STACK_AUTO && mode != MOE_STACK_KERNELS && mode != MOE_STACK_PERSISTENT) return MOE_ERR_SHAPE;
   for (int l = 0; l < n_layers; ++l)
     if ((rc = check_weights(desc, &layers[l]))) return rc;
-  if (!aligned(input, 2) || !aligned(output, 2) || (ids_per_layer && !aligned(ids_per_layer, 4)) ||
-      (resid_per_layer && !aligned(resid_per_layer, 2)))
+  if (!aligned(io->input, 2) || !aligned(io->output, 2) || (io->ids && !aligned(io->ids, 4)) ||
+      (io->resid && !aligned(io->resid, 2)) || (io->routed && !aligned(io->routed, 2)) ||
+      (io->shared && !aligned(io->shared, 2)))
     return MOE_ERR_ALIGN;
   const WsLayout L = ws_layout(desc, n_layers);
   rc = check_ws(ws, ws_bytes, L.total);
   if (rc) return rc;
   hipStream_t st = as_stream(stream);
   if (mode == MOE_STACK_PERSISTENT || mode == MOE_STACK_AUTO) {
+    const uint64_t hash = layer_table_hash(layers, n_layers);
+    const bool bound = bind_holds(ws, n_layers, hash);
+    if (mode == MOE_STACK_PERSISTENT && !bound) return MOE_ERR_NOT_BOUND;
     int G = 0;
     if ((rc = device_cu_count(&G))) return rc;
     StackGeom g;
     rc = (G >= 8 && G % 8 == 0 && L.stack) ? stack_geometry(desc, G, &g) : MOE_ERR_UNSUPPORTED;
     if (rc == MOE_OK && g.lds > kStackMaxLds) rc = MOE_ERR_UNSUPPORTED;
-    if (rc == MOE_OK) {
+    if (rc == MOE_OK && bound) {
       stack_ws_layout(&g, L.stack);
-      return launch_stack(desc, n_layers, at<moe_layer_weights>(ws, L.table), at<int>(ws, L.bound), layers[0],
-                          layers[n_layers - 1], input, output, ids_per_layer, resid_per_layer,
+      return launch_stack(desc, n_layers, at<moe_layer_weights>(ws, L.table), at<uint32_t>(ws, L.bound), hash, io,
                           static_cast<uint8_t*>(ws), g, st);
     }
     if (mode == MOE_STACK_PERSISTENT) return rc;
   }
   const int H = desc->hidden, E = desc->n_experts, k = desc->top_k;
   const bool has_shared = desc->shared_ffn > 0;
-  uint16_t* routed = at<uint16_t>(ws, L.routed);
-  uint16_t* shared = at<uint16_t>(ws, L.shared);
-  const uint16_t* res_in = input;
+  const uint16_t* res_in = io->input;
+  const uint16_t* prev_routed = nullptr;
+  const uint16_t* prev_shared = nullptr;
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer_weights* w = &layers[l];
-    uint16_t* res_out = resid_per_layer ? resid_per_layer + (size_t)l * H : at<uint16_t>(ws, L.res);
-    int32_t* ids = ids_per_layer ? ids_per_layer + (size_t)l * k : at<int32_t>(ws, L.ids);
-    rc = launch_norm(res_in, l ? routed : nullptr, (l && has_shared) ? shared : nullptr, w->norm_w, H, 1, desc->eps,
-                     res_out, at<float>(ws, L.xn), at<void>(ws, L.xq), 1, st);
+    uint16_t* res_out = io->resid ? io->resid + (size_t)l * H : at<uint16_t>(ws, L.res);
+    int32_t* ids = io->ids ? io->ids + (size_t)l * k : at<int32_t>(ws, L.ids);
+    // the layer's outputs may overwrite the previous layer's in the workspace:
+    // the norm that reads those runs first on the stream
+    uint16_t* routed = io->routed ? io->routed + (size_t)l * H : at<uint16_t>(ws, L.routed);
+    uint16_t* shared = has_shared ? (io->shared ? io->shared + (size_t)l * H : at<uint16_t>(ws, L.shared)) : nullptr;
+    rc = launch_norm(res_in, prev_routed, prev_shared, w->norm_w, H, 1, desc->eps, res_out, at<float>(ws, L.xn),
+                     at<void>(ws, L.xq), 1, st);
     if (rc) return rc;
     rc = launch_router(at<float>(ws, L.xn), w->router_w, has_shared ? w->shared_gate_w : nullptr, 1, H, E, k,
                        at<float>(ws, L.logits), nullptr, ids, at<float>(ws, L.wts), at<float>(ws, L.sg),
@@ -311,13 +367,14 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
     rc = launch_gate_up(desc, w, at<void>(ws, L.xq), ids, at<float>(ws, L.h), at<float>(ws, L.hs), st);
     if (rc) return rc;
     rc = launch_down(desc, w, at<float>(ws, L.h), at<float>(ws, L.hs), ids, at<float>(ws, L.wts), at<float>(ws, L.sg),
-                     routed, has_shared ? shared : nullptr, st);
+                     routed, shared, st);
     if (rc) return rc;
     res_in = res_out;
+    prev_routed = routed;
+    prev_shared = shared;
   }
   // the fold the next layer's norm would do: output = bf16(res_L + bf16(routed + shared))
-  return launch_norm(res_in, routed, has_shared ? shared : nullptr, nullptr, H, 1, desc->eps, output, nullptr, nullptr, 0,
-                     st);
+  return launch_norm(res_in, prev_routed, prev_shared, nullptr, H, 1, desc->eps, io->output, nullptr, nullptr, 0, st);
 }
 
 size_t moe_stack_status_offset(const moe_layer_desc* desc, int n_layers) {
@@ -368,6 +425,19 @@ int moe_test_quantize_q81(const float* x, int n, void* xq, void* stream) {
   if (n <= 0 || n % 32 || n > (1 << 26)) return MOE_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(xq, 2)) return MOE_ERR_ALIGN;
   return launch_test_q81_groups(x, n, xq, as_stream(stream));
+}
+
+int moe_test_stack_select(const float* logits, int n_sets, int n_experts, int top_k, int with_gate, int32_t* ids,
+                          float* weights, float* gate, void* stream) {
+  if (!logits || !ids || !weights) return MOE_ERR_NULL;
+  if (with_gate && !gate) return MOE_ERR_NULL;
+  if (n_sets <= 0 || n_sets > 65535 || n_experts <= 0 || n_experts > MOE_MAX_EXPERTS || top_k <= 0 ||
+      top_k > n_experts || top_k > MOE_MAX_TOPK)
+    return MOE_ERR_SHAPE;
+  if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4) || (gate && !aligned(gate, 4)))
+    return MOE_ERR_ALIGN;
+  return launch_test_stack_select(logits, n_sets, n_experts, top_k, with_gate, ids, weights, with_gate ? gate : nullptr,
+                                  as_stream(stream));
 }
 
 }  // extern "C"

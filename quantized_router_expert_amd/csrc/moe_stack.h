@@ -39,15 +39,22 @@ struct StackGeom {
 
 constexpr uint32_t kBoundMagic = 0x4d6f4553u;
 
+// 64-bit hash of a layer-pointer table (its bytes, 8 at a time): moe_stack_bind
+// stores it beside the device copy of the table, and every launch compares it
+// with the caller's.
+uint64_t layer_table_hash(const moe_layer_weights* layers, int n);
+
 struct StackArgs {
   StackGeom g;
   const moe_layer_weights* layers;   // device copy of the per-layer pointer table
-  const int* bound;                  // {magic, n_layers} written by moe_stack_bind
-  moe_layer_weights first, last;     // the caller's first and last layer, checked against the table
+  const uint32_t* bound;             // {magic, n_layers, hash lo, hash hi} written by moe_stack_bind
+  uint64_t table_hash;               // hash of the caller's table
   const uint16_t* input;
   uint16_t* output;
   int32_t* ids_out;
   uint16_t* resid_out;
+  uint16_t* routed_out;
+  uint16_t* shared_out;
   uint8_t* ws;
   int L, H, E, k, F, Fs;
   float eps;
@@ -56,10 +63,10 @@ struct StackArgs {
 
 int stack_geometry(const moe_layer_desc* d, int G, StackGeom* out);
 void stack_ws_layout(StackGeom* g, size_t base);
-int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_dev, const int* bound,
-                 const moe_layer_weights& first, const moe_layer_weights& last, const uint16_t* input,
-                 uint16_t* output, int32_t* ids_out, uint16_t* resid_out, uint8_t* ws, const StackGeom& g,
-                 hipStream_t st);
+int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_dev, const uint32_t* bound,
+                 uint64_t table_hash, const moe_stack_io* io, uint8_t* ws, const StackGeom& g, hipStream_t st);
 int device_cu_count(int* n);
+int launch_test_stack_select(const float* logits, int n_sets, int E, int k, int with_gate, int32_t* ids, float* wts,
+                             float* gate, hipStream_t st);
 
 }  // namespace moe

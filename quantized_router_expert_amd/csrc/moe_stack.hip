@@ -484,12 +484,6 @@ __device__ __forceinline__ void routing_weights(int k, bool has_sg, const float*
   else if (lane == k) sel[2 * k] = __float_as_uint(has_sg ? (float)(1.0 / (1.0 + ex)) : 0.0f);
 }
 
-__device__ __forceinline__ bool same_layer(const moe_layer_weights& p, const moe_layer_weights& q) {
-  return p.norm_w == q.norm_w && p.router_w == q.router_w && p.shared_gate_w == q.shared_gate_w && p.gate == q.gate &&
-         p.up == q.up && p.down == q.down && p.shared_gate == q.shared_gate && p.shared_up == q.shared_up &&
-         p.shared_down == q.shared_down;
-}
-
 // A layer's weight pointers, wave-uniform.  Read once per layer at a moment
 // when this wave has no row transfer in flight: a later read of the table
 // would make the wave wait (in order) for every transfer queued before it.
@@ -666,27 +660,30 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
 
   __shared__ uint32_t s_gen;
   __shared__ int s_fail;
-  {
-    // the bound pointer table must be the caller's stack
-    bool ok = a.bound[0] == (int)kBoundMagic && a.bound[1] == a.L;
-    if (ok) ok = same_layer(a.layers[0], a.first) && same_layer(a.layers[a.L - 1], a.last);
-    if (!ok) {
-      if (b == 0) {
-        for (int i = tid; i < H; i += kStackThreads) a.output[i] = 0x7fc0u;
-        if (tid == 0) __hip_atomic_store(reinterpret_cast<uint32_t*>(a.ws + a.g.w_ctrl) + kErrWord, 2u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-      }
-      return;
-    }
-  }
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(a.ws + a.g.w_ctrl);
   const __amdgpu_buffer_rsrc_t r_ctrl = make_rsrc(ctrl, kStackCtrlBytes);
   if (tid == 0) {
-    s_fail = 0;
+    // the table bound in the workspace must be the caller's (the whole table's
+    // hash), and no earlier launch may have stopped or been refused: a stopped
+    // launch leaves exchange words of its generation behind, which a launch
+    // of the same generation would take as current
+    const bool bound = a.bound[0] == kBoundMagic && a.bound[1] == (uint32_t)a.L &&
+                       a.bound[2] == (uint32_t)a.table_hash && a.bound[3] == (uint32_t)(a.table_hash >> 32);
+    const uint32_t err = __builtin_amdgcn_raw_buffer_load_b32(r_ctrl, kErrWord * 4, 0, kAuxSC1);
+    s_fail = !bound ? 2 : (err != 0u ? 3 : 0);
     v2u gv = __builtin_amdgcn_raw_buffer_load_b64(r_ctrl, 0, 0, kAuxSC1);
     s_gen = gv.x;
   }
   lds_barrier();
+  if (s_fail) {
+    // refused: workgroup 0 sets the output to NaN; an unbound table is
+    // recorded in the status word, an earlier failure stays as it is
+    if (b == 0) {
+      for (int i = tid; i < H; i += kStackThreads) a.output[i] = 0x7fc0u;
+      if (tid == 0 && s_fail == 2) __builtin_amdgcn_raw_buffer_store_b32(2u, r_ctrl, kErrWord * 4, 0, kAuxSC1);
+    }
+    return;
+  }
   const uint32_t base = s_gen * (uint32_t)(3 * a.L + 2) + 1u;
 
   // writers see every copy; this workgroup reads copy b % R
@@ -1008,9 +1005,11 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         if (sl == 0) {
           const uint16_t routed = f32_to_bf16((float)v);
           float t = bf16_to_f32(routed);
+          if (a.routed_out) a.routed_out[(long)l * H + row0 + r] = routed;
           if (has_sg) {
             const uint16_t shared = f32_to_bf16((float)((double)sgv * (double)(float)part[k * nrd + r]));
             t = bf16_to_f32(f32_to_bf16(bf16_to_f32(routed) + bf16_to_f32(shared)));
+            if (a.shared_out) a.shared_out[(long)l * H + row0 + r] = shared;
           }
           tb[r] = f32_to_bf16(t);
         }
@@ -1047,6 +1046,44 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- test export of the selection
+// One workgroup per logit set runs the stack kernel's selection exactly as a
+// layer does: topk_candidates on waves 0..3, rank_candidates and
+// routing_weights on wave 0, with the same LDS arrays and barriers.
+__global__ __launch_bounds__(kStackThreads) void k_test_stack_select(const float* lg_in, int E, int k, int with_gate,
+                                                                     int32_t* ids, float* wts, float* gate) {
+  __shared__ float lg[MOE_MAX_EXPERTS + 1];
+  __shared__ unsigned long long keys[256];
+  __shared__ unsigned long long cand[64];
+  __shared__ uint32_t sel[2 * MOE_MAX_TOPK + 2];
+  __shared__ float lgsel[MOE_MAX_TOPK + 1];
+  __shared__ int s_fail;
+  const int set = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  const bool has_sg = with_gate != 0;
+  const float* src = lg_in + (long)set * (E + 1);
+  for (int i = tid; i < E + 1; i += kStackThreads) lg[i] = src[i];
+  if (tid == 0) s_fail = 0;
+  lds_barrier();
+  topk_candidates(lg, E, k, wave, keys, cand);
+  lds_barrier();
+  if (wave == 0 && rank_candidates(lg, E, k, has_sg, cand, sel, lgsel)) s_fail = 1;
+  lds_barrier();
+  if (wave == 0) routing_weights(k, has_sg, lgsel, sel, reinterpret_cast<double*>(cand));
+  lds_barrier();
+  for (int s = tid; s < k; s += kStackThreads) {
+    ids[(long)set * k + s] = s_fail ? -1 : (int32_t)sel[s];
+    wts[(long)set * k + s] = __uint_as_float(sel[k + s]);
+  }
+  if (tid == 0 && gate) gate[set] = __uint_as_float(sel[2 * k]);
+}
+
+int launch_test_stack_select(const float* logits, int n_sets, int E, int k, int with_gate, int32_t* ids, float* wts,
+                             float* gate, hipStream_t st) {
+  hipLaunchKernelGGL(k_test_stack_select, dim3(n_sets), dim3(kStackThreads), 0, st, logits, E, k, with_gate, ids, wts,
+                     gate);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 // ---------------------------------------------------------------- host side
 int stack_geometry(const moe_layer_desc* d, int G, StackGeom* out) {
   const int st = d->shared_ffn > 0 ? d->shared_type : MOE_TYPE_Q4_K;
@@ -1071,20 +1108,32 @@ int device_cu_count(int* n) {
   return MOE_OK;
 }
 
-int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_dev, const int* bound,
-                 const moe_layer_weights& first, const moe_layer_weights& last, const uint16_t* input,
-                 uint16_t* output, int32_t* ids_out, uint16_t* resid_out, uint8_t* ws, const StackGeom& g,
-                 hipStream_t st) {
+uint64_t layer_table_hash(const moe_layer_weights* layers, int n) {
+  // FNV-1a over 8-byte words of the table
+  uint64_t h = 0xcbf29ce484222325ull;
+  const size_t words = sizeof(moe_layer_weights) * (size_t)n / 8;
+  for (size_t i = 0; i < words; ++i) {
+    uint64_t w;
+    memcpy(&w, reinterpret_cast<const uint8_t*>(layers) + 8 * i, 8);
+    h = (h ^ w) * 0x100000001b3ull;
+  }
+  return h;
+}
+
+int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_dev, const uint32_t* bound,
+                 uint64_t table_hash, const moe_stack_io* io, uint8_t* ws, const StackGeom& g, hipStream_t st) {
+  static_assert(sizeof(moe_layer_weights) % 8 == 0, "the table hashes in 8-byte words");
   StackArgs a;
   a.g = g;
   a.layers = table_dev;
   a.bound = bound;
-  a.first = first;
-  a.last = last;
-  a.input = input;
-  a.output = output;
-  a.ids_out = ids_out;
-  a.resid_out = resid_out;
+  a.table_hash = table_hash;
+  a.input = io->input;
+  a.output = io->output;
+  a.ids_out = io->ids;
+  a.resid_out = io->resid;
+  a.routed_out = io->routed;
+  a.shared_out = io->shared;
   a.ws = ws;
   a.L = L;
   a.H = d->hidden;
@@ -1093,11 +1142,7 @@ int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_
   a.F = d->ffn;
   a.Fs = d->shared_ffn;
   a.eps = d->eps;
-  static const int trace_blocks = [] {
-    const char* e = getenv("MOE_STACK_TRACE");
-    return (e && e[0] == '1') ? 1 : 0;
-  }();
-  a.trace_blocks = trace_blocks;
+  a.trace_blocks = io->trace ? 1 : 0;
   const void* fn;
   const int dt = d->down_type;
   const int stt = d->shared_ffn > 0 ? d->shared_type : MOE_TYPE_Q4_K;

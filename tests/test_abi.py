@@ -142,11 +142,21 @@ def test_layer_and_stack_validation(q):
     assert q._moe_decode_layer(C.byref(d), C.byref(w), C.byref(io2), FAKE, 1 << 24, None) == -1
     assert q._moe_decode_layer(C.byref(d), C.byref(w), C.byref(io), FAKE, 16, None) == -5
     arr = (q.LayerWeights * 2)(w, w)
-    assert q._moe_decode_stack(C.byref(d), arr, 0, FAKE, FAKE, None, None, 0, FAKE, 1 << 24, None) == -2
-    assert q._moe_decode_stack(C.byref(d), arr, 2, FAKE, FAKE, None, None, 9, FAKE, 1 << 24, None) == -2
-    assert q._moe_decode_stack(C.byref(d), arr, 2, None, FAKE, None, None, 0, FAKE, 1 << 24, None) == -1
+    sio = q.StackIO(input=FAKE, output=FAKE)
+    big = q.moe_workspace_size(d, 2)
+    ds = q._moe_decode_stack
+    assert ds(C.byref(d), arr, 0, C.byref(sio), 0, FAKE, big, None) == -2
+    assert ds(C.byref(d), arr, 2, C.byref(sio), 9, FAKE, big, None) == -2
+    assert ds(C.byref(d), arr, 2, None, 0, FAKE, big, None) == -1
+    assert ds(C.byref(d), arr, 2, C.byref(q.StackIO(input=None, output=FAKE)), 0, FAKE, big, None) == -1
+    assert ds(C.byref(d), arr, 2, C.byref(q.StackIO(input=FAKE, output=FAKE, routed=FAKE + 1)), 0, FAKE, big,
+              None) == -4
+    assert ds(C.byref(d), arr, 2, C.byref(sio), 0, FAKE, big - 1, None) == -5
     d0 = _desc(q, norm=0)
-    assert q._moe_decode_stack(C.byref(d0), arr, 2, FAKE, FAKE, None, None, 0, FAKE, 1 << 24, None) == -7
+    assert ds(C.byref(d0), arr, 2, C.byref(sio), 0, FAKE, big, None) == -7
+    # the persistent kernel on a workspace that holds no bound stack: refused
+    # on the host before anything is enqueued
+    assert ds(C.byref(d), arr, 2, C.byref(sio), q.MOE_STACK_PERSISTENT, FAKE, big, None) == -8
     assert q._moe_stack_bind(C.byref(d), arr, 2, FAKE, 1024, None) == -5
     assert q._moe_test_subblock_dots(FAKE, 9, 256, 1, FAKE, FAKE, None) == -3
     assert q._moe_test_subblock_dots(FAKE, 12, 100, 1, FAKE, FAKE, None) == -2
@@ -163,6 +173,14 @@ def test_layer_and_stack_validation(q):
     assert q._moe_stream_read(FAKE, 1000, FAKE, 8, None) == -2
     assert q._moe_stream_read(FAKE, 1024, FAKE, 0, None) == -2
     assert q._moe_stream_read(FAKE + 8, 1024, FAKE, 8, None) == -4
+    sel = q._moe_test_stack_select
+    assert sel(None, 1, 256, 8, 0, FAKE, FAKE, None, None) == -1
+    assert sel(FAKE, 1, 256, 8, 1, FAKE, FAKE, None, None) == -1    # the gate output is needed
+    assert sel(FAKE, 0, 256, 8, 0, FAKE, FAKE, None, None) == -2
+    assert sel(FAKE, 1, 4, 8, 0, FAKE, FAKE, None, None) == -2      # k > E
+    assert sel(FAKE, 1, 2048, 8, 0, FAKE, FAKE, None, None) == -2
+    assert sel(FAKE, 1, 256, 17, 0, FAKE, FAKE, None, None) == -2
+    assert sel(FAKE + 2, 1, 256, 8, 0, FAKE, FAKE, None, None) == -4
     assert q._moe_workspace_init(None, 1024, None) == -5
     assert q._moe_workspace_init(FAKE + 8, 1024, None) == -4
 

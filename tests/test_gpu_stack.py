@@ -1,11 +1,17 @@
 """Parity of the persistent L-layer stack (one cooperative launch per token)
-against the oracle's stack, token after token, and against the per-layer
-kernel path; plus its refusal to run on a workspace that was not bound."""
+against the oracle, at the depth the benchmark runs (40 layers of the
+Qwen3.6-shaped layer in both weight variants, 48 layers of the 128-expert
+shape, with an all-zero token) and on smaller shapes that reach the other code
+paths (E > 256 up to 1024, k > 8, few experts, no shared expert, the tiny
+shape), with the per-layer stage-isolated and chained checks of
+stack_check.py; plus the binding rules, refusals and many launches in a row.
+"""
 import numpy as np
 import pytest
 import torch
 
 import gpu_util as gu
+import stack_check as sc
 import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -22,104 +28,142 @@ def _status(q, desc, L, ws):
     return q.stack_status(desc, L, ws)
 
 
-STACK_CASES = [
-    ("stack", dict(layers=3), wl.Q4_K, wl.Q4_K, 3),
-    ("stack", dict(layers=2), wl.Q8_0, wl.Q5_K, 2),
-    ("e128", dict(layers=3), wl.Q4_K, wl.Q4_K, 3),
-    ("tiny", dict(layers=2, norm=True), wl.Q4_K, wl.Q4_K, 4),
-    ("stack", dict(layers=2, E=16), wl.Q4_K, wl.Q4_K, 2),
-    ("tiny", dict(layers=2, norm=True, E=320, router_dup=1), wl.Q4_K, wl.Q4_K, 3),   # E > 256: per-wave picks
-    ("tiny", dict(layers=2, norm=True, k=12), wl.Q4_K, wl.Q4_K, 3),                   # k > 8: 16 slots per wave
-    ("tiny", dict(layers=2, norm=True, E=320, k=16, router_dup=1), wl.Q4_K, wl.Q4_K, 2),
+FULL_CASES = [
+    ("stack", wl.Q4_K, wl.Q4_K, [0, 1, 2]),
+    ("stack", wl.Q8_0, wl.Q5_K, [0, 1, 2]),
+    ("e128", wl.Q4_K, wl.Q4_K, [0, 1, "zero"]),
 ]
 
 
-@pytest.mark.parametrize("cfg_name,kw,shared_type,down_type,ntok", STACK_CASES)
-def test_stack_persistent_vs_oracle(q, orc, cfg_name, kw, shared_type, down_type, ntok):
+@pytest.mark.parametrize("cfg_name,shared_type,down_type,tokens", FULL_CASES,
+                         ids=["stack40-q4k-q4k", "stack40-q8_0-q5k", "e128-48L"])
+def test_stack_full_depth_vs_oracle(q, orc, cfg_name, shared_type, down_type, tokens):
+    cfg = wl.CONFIGS[cfg_name]
+    gu.banner(f"persistent stack {cfg_name} {cfg.layers} layers shared {shared_type} down {down_type} tokens {tokens}")
+    sc.run_and_check(q, orc, cfg, shared_type, down_type, tokens, q.MOE_STACK_PERSISTENT)
+    torch.cuda.empty_cache()
+
+
+SMALL_CASES = [
+    ("stack", dict(layers=4, E=16), wl.Q4_K, wl.Q4_K, [0, 1]),
+    ("tiny", dict(layers=3, norm=True), wl.Q4_K, wl.Q4_K, [0, 1, 2]),
+    ("tiny", dict(layers=3, norm=True, E=320, router_dup=1), wl.Q4_K, wl.Q4_K, [0, 1]),    # E > 256: per-wave picks
+    ("tiny", dict(layers=3, norm=True, k=12), wl.Q4_K, wl.Q4_K, [0, 1]),                   # k > 8: 16 slots per wave
+    ("tiny", dict(layers=3, norm=True, E=320, k=16, router_dup=1), wl.Q4_K, wl.Q4_K, [0, 1]),
+    ("tiny", dict(layers=3, norm=True, E=1024, k=16, router_dup=1), wl.Q4_K, wl.Q4_K, [0]),
+    ("tiny", dict(layers=3, norm=True, Fs=0, three_input=False), wl.Q4_K, wl.Q4_K, [0, 1]),
+]
+
+
+@pytest.mark.parametrize("cfg_name,kw,shared_type,down_type,tokens", SMALL_CASES)
+def test_stack_small_shapes_vs_oracle(q, orc, cfg_name, kw, shared_type, down_type, tokens):
     cfg = wl.variant(wl.CONFIGS[cfg_name], **kw)
-    L, H, E, k = cfg.layers, cfg.H, cfg.E, cfg.k
-    gu.banner(f"persistent stack {cfg_name} {kw} shared {shared_type} down {down_type}")
-    Ws = [wl.layer_weights(cfg, l, "cuda", shared_type=shared_type, down_type=down_type) for l in range(L)]
-    Wn = [wl.to_numpy_weights(w) for w in Ws]
-    desc_g = q.make_desc(H, E, k, cfg.F, cfg.Fs, down_type=down_type, shared_type=shared_type, eps=cfg.eps)
-    desc_o = orc.make_desc(H, E, k, cfg.F, cfg.Fs, down_type=down_type, shared_type=shared_type, eps=cfg.eps)
-    ws = q.alloc_workspace(desc_g, L)
-    q.moe_stack_bind(desc_g, Ws, ws)
-    ws_k = q.alloc_workspace(desc_g, L)
-    arr = q.layer_array(Ws)
-    for t in range(ntok):
-        inp = wl.token_inputs(cfg, t, "cpu")["residual"]
-        if cfg.zero_token_frac and t == ntok - 1:
-            inp = torch.zeros_like(inp)
-        out = torch.zeros(H, dtype=torch.bfloat16, device="cuda")
-        ids = torch.full((L, k), -1, dtype=torch.int32, device="cuda")
-        res = torch.zeros(L, H, dtype=torch.bfloat16, device="cuda")
-        q.moe_decode_stack(desc_g, None, inp.cuda(), out, ids, res, q.MOE_STACK_PERSISTENT, ws, layer_array=arr)
-        torch.cuda.synchronize()
-        assert _status(q, desc_g, L, ws) == 0
-        # the per-layer kernel path on the same input
-        out_k = torch.zeros_like(out)
-        ids_k = torch.full_like(ids, -1)
-        q.moe_decode_stack(desc_g, None, inp.cuda(), out_k, ids_k, None, q.MOE_STACK_KERNELS, ws_k, layer_array=arr)
-        torch.cuda.synchronize()
-        o_out, per = orc.moe_stack(desc_o, Wn, wl.u16(inp), per_layer=True)
-        g_ids = gu.host(ids)
-        assert np.array_equal(g_ids, gu.host(ids_k)), "persistent and per-layer paths chose different experts"
-        same_bits = float((gu.u16_host(out) == gu.u16_host(out_k)).mean())
-        if np.array_equal(g_ids, per["ids"]):
-            for l in range(L):
-                ok, _ = gu.bf16_within(gu.u16_host(res)[l], gu.bf16_bits_to_f64(per["resid"][l]))
-                assert ok.mean() > 0.999, (l, ok.mean())
-            gu.assert_bf16_within(gu.u16_host(out), gu.bf16_bits_to_f64(o_out), "stack output")
-            print(f"  token {t}: ids match; out exact vs oracle "
-                  f"{float((gu.u16_host(out) == o_out).mean()):.5f}, vs per-layer path {same_bits:.5f}", flush=True)
-        else:
-            assert np.array_equal(g_ids[0], per["ids"][0])
-            print(f"  token {t}: a later layer selected differently (near tie)", flush=True)
-        assert same_bits > 0.999
+    gu.banner(f"persistent stack {cfg_name} {kw}")
+    Ws, desc, ws, arr = sc.run_and_check(q, orc, cfg, shared_type, down_type, tokens, q.MOE_STACK_PERSISTENT)
+    # the per-layer kernel path on the same input chooses the same experts
+    L, H, k = cfg.layers, cfg.H, cfg.k
+    ws_k = q.alloc_workspace(desc, L)
+    inp = wl.token_inputs(cfg, tokens[0], "cuda")["residual"]
+    ids_p = torch.full((L, k), -1, dtype=torch.int32, device="cuda")
+    ids_k = torch.full_like(ids_p, -1)
+    out_p = torch.zeros(H, dtype=torch.bfloat16, device="cuda")
+    out_k = torch.zeros_like(out_p)
+    q.moe_decode_stack(desc, None, inp, out_p, ids_p, None, q.MOE_STACK_PERSISTENT, ws, layer_array=arr)
+    q.moe_decode_stack(desc, None, inp, out_k, ids_k, None, q.MOE_STACK_KERNELS, ws_k, layer_array=arr)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_p, ids_k)
 
 
-def test_stack_refuses_unbound_workspace(q, orc):
+def test_stack_binding_and_refusals(q, orc):
+    """Unbound, bound to other layers, bound correctly; AUTO without a binding
+    takes the per-layer kernels; a launch that starts with a nonzero status
+    word does no work and leaves the word as it was."""
     cfg = wl.variant(wl.CONFIGS["stack"], layers=2, E=16)
-    gu.banner("persistent stack without binding")
+    gu.banner("persistent stack binding and refusals")
     Ws = [wl.layer_weights(cfg, l, "cuda") for l in range(2)]
     desc = q.make_desc(cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs)
     ws = q.alloc_workspace(desc, 2)
     out = torch.zeros(cfg.H, dtype=torch.bfloat16, device="cuda")
     inp = wl.token_inputs(cfg, 0, "cuda")["residual"]
-    q.moe_decode_stack(desc, Ws, inp, out, None, None, q.MOE_STACK_PERSISTENT, ws)
+    with pytest.raises(q.MoeError) as e:
+        q.moe_decode_stack(desc, Ws, inp, out, None, None, q.MOE_STACK_PERSISTENT, ws)
+    assert e.value.status == -8
+    # AUTO on the unbound workspace: the per-layer kernels, whose result is the reference
+    ref = torch.zeros_like(out)
+    ws_k = q.alloc_workspace(desc, 2)
+    q.moe_decode_stack(desc, Ws, inp, ref, None, None, q.MOE_STACK_KERNELS, ws_k)
+    q.moe_decode_stack(desc, Ws, inp, out, None, None, q.MOE_STACK_AUTO, ws)
     torch.cuda.synchronize()
-    assert _status(q, desc, 2, ws) == 2
-    assert torch.isnan(out.float()).all()
-    # bound to other layers: also refused
+    assert torch.equal(out, ref) and _status(q, desc, 2, ws) == 0
+    # bound to other layers: the caller's table is not the bound one
     Ws2 = [wl.layer_weights(cfg, l + 5, "cuda") for l in range(2)]
     q.moe_stack_bind(desc, Ws2, ws)
-    q.moe_decode_stack(desc, Ws, inp, out, None, None, q.MOE_STACK_PERSISTENT, ws)
+    with pytest.raises(q.MoeError) as e:
+        q.moe_decode_stack(desc, Ws, inp, out, None, None, q.MOE_STACK_PERSISTENT, ws)
+    assert e.value.status == -8
+    # a middle layer changed in the caller's table: not the bound stack
+    Ws3 = [wl.layer_weights(cfg, l, "cuda") for l in range(3)]
+    Ws3b = [Ws3[0], wl.layer_weights(cfg, 7, "cuda"), Ws3[2]]
+    ws3 = q.alloc_workspace(desc, 3)
+    q.moe_stack_bind(desc, Ws3, ws3)
+    with pytest.raises(q.MoeError) as e:
+        q.moe_decode_stack(desc, Ws3b, inp, out, None, None, q.MOE_STACK_PERSISTENT, ws3)
+    assert e.value.status == -8
+    ref3 = torch.zeros_like(out)
+    ws3k = q.alloc_workspace(desc, 3)
+    q.moe_decode_stack(desc, Ws3b, inp, ref3, None, None, q.MOE_STACK_KERNELS, ws3k)
+    q.moe_decode_stack(desc, Ws3b, inp, out, None, None, q.MOE_STACK_AUTO, ws3)
     torch.cuda.synchronize()
-    assert _status(q, desc, 2, ws) == 2
-    # bound correctly: runs, status clear
+    assert torch.equal(out, ref3)
+    # the workspace cleared behind the library's back (the host record still
+    # names it): the launch finds no bound table on the device and refuses
+    ws3.zero_()
+    q.moe_decode_stack(desc, Ws3, inp, out, None, None, q.MOE_STACK_PERSISTENT, ws3)
+    torch.cuda.synchronize()
+    assert _status(q, desc, 3, ws3) == 2 and torch.isnan(out.float()).all()
+    # bound correctly: runs, status clear, the same result as the per-layer path's ids
     q.moe_stack_bind(desc, Ws, ws)
     q.moe_decode_stack(desc, Ws, inp, out, None, None, q.MOE_STACK_PERSISTENT, ws)
     torch.cuda.synchronize()
-    assert _status(q, desc, 2, ws) == 0
-    assert not torch.isnan(out.float()).any()
+    assert _status(q, desc, 2, ws) == 0 and not torch.isnan(out.float()).any()
+    good = out.clone()
+    # a nonzero status word set from the host: refused, output NaN, word unchanged
+    off = q.moe_stack_status_offset(desc, 2)
+    ws[off:off + 4].view(torch.int32).fill_(1)
+    q.moe_decode_stack(desc, Ws, inp, out, None, None, q.MOE_STACK_PERSISTENT, ws)
+    torch.cuda.synchronize()
+    assert _status(q, desc, 2, ws) == 1 and torch.isnan(out.float()).all()
+    q.moe_decode_stack(desc, Ws, inp, out, None, None, q.MOE_STACK_PERSISTENT, ws)
+    torch.cuda.synchronize()
+    assert _status(q, desc, 2, ws) == 1 and torch.isnan(out.float()).all()
+    # re-binding clears it
+    q.moe_stack_bind(desc, Ws, ws)
+    q.moe_decode_stack(desc, Ws, inp, out, None, None, q.MOE_STACK_PERSISTENT, ws)
+    torch.cuda.synchronize()
+    assert _status(q, desc, 2, ws) == 0 and torch.equal(out, good)
+    # moe_workspace_init drops the host record
+    q.moe_workspace_init(ws)
+    with pytest.raises(q.MoeError) as e:
+        q.moe_decode_stack(desc, Ws, inp, out, None, None, q.MOE_STACK_PERSISTENT, ws)
+    assert e.value.status == -8
 
 
 def test_stack_many_tokens_deterministic(q):
-    """50 launches in a row on one workspace (the generation counter advances each
-    launch): the same input gives the same output every time."""
+    """200 launches in a row on one workspace (the generation counter advances
+    each launch): the same input gives the same output every time, and the
+    status word stays 0."""
     cfg = wl.variant(wl.CONFIGS["stack"], layers=4)
-    gu.banner("persistent stack: 50 launches")
+    gu.banner("persistent stack: 200 launches")
     Ws = [wl.layer_weights(cfg, l, "cuda") for l in range(4)]
     desc = q.make_desc(cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs)
     ws = q.alloc_workspace(desc, 4)
     q.moe_stack_bind(desc, Ws, ws)
     arr = q.layer_array(Ws)
     inps = [wl.token_inputs(cfg, t, "cuda")["residual"] for t in range(3)]
-    outs = torch.zeros(50, cfg.H, dtype=torch.bfloat16, device="cuda")
-    for i in range(50):
+    outs = torch.zeros(200, cfg.H, dtype=torch.bfloat16, device="cuda")
+    for i in range(200):
         q.moe_decode_stack(desc, None, inps[i % 3], outs[i], None, None, q.MOE_STACK_PERSISTENT, ws, layer_array=arr)
     torch.cuda.synchronize()
     assert _status(q, desc, 4, ws) == 0
-    for i in range(3, 50):
+    for i in range(3, 200):
         assert torch.equal(outs[i], outs[i % 3]), i
