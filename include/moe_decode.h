@@ -207,6 +207,24 @@ int moe_decode_layer(const moe_layer_desc* desc, const moe_layer_weights* w,
                      const moe_layer_io* io, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_decode_layer without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts that
+ * forbid allocation).  Same arguments, kernels and results as
+ * moe_decode_layer; the layer's intermediates (router counters, xn, xq,
+ * logits, ids, weights, gate, h, hs) live in a static device array of the
+ * library of 256 KiB, one per GPU, held until the process ends.  A shape whose
+ * intermediates need more returns MOE_ERR_WORKSPACE and enqueues nothing
+ * (every shape of up to 8 selected experts of FFN 2048 at hidden 8192 fits).
+ * No allocation happens: the first call on a device looks the array up and
+ * queues the clearing of its router counters on `stream`; every completed
+ * call leaves them at zero again.  All calls on one GPU share the array and
+ * see what the last call left there: calls that may overlap in time on one
+ * GPU (other streams, other threads) race and must be ordered by the caller.
+ * ---------------------------------------------------------------------- */
+int moe_decode_layer_noalloc(const moe_layer_desc* desc, const moe_layer_weights* w,
+                             const moe_layer_io* io, void* stream);
+
+/* ------------------------------------------------------------------------
  * a8: several tokens at once, experts grouped by the tokens that selected
  * them (the pages describe batch 1 only; this is the batch > 1 reading).
  * Per token the norm, router, top-k and weights are the batch-1 steps.  The

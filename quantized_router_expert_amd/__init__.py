@@ -78,6 +78,8 @@ _moe_stack_bind = _sig("moe_stack_bind", C.c_int, C.POINTER(LayerDesc), C.POINTE
                        C.c_size_t, P)
 _moe_decode_stack = _sig("moe_decode_stack", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights), C.c_int,
                          C.POINTER(StackIO), C.c_int, P, C.c_size_t, P)
+_moe_decode_layer_noalloc = _sig("moe_decode_layer_noalloc", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights),
+                                 C.POINTER(LayerIO), P)
 _moe_batch_workspace_size = _sig("moe_batch_workspace_size", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
 _expert_ffn_grouped = _sig("expert_ffn_grouped", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights), P, P, P, P, P,
                            C.c_int, C.c_int, P, P, P, P, P, C.c_size_t, P)
@@ -94,7 +96,8 @@ _moe_requant_q4k = _sig("moe_requant_q4k", C.c_int, P, C.c_int, C.c_int, C.c_int
 EXPORTS = ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", "moe_stack_bind",
            "moe_decode_stack", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
            "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots", "moe_test_quantize_q81", "moe_stream_read", "moe_requant_q4k",
-           "moe_batch_workspace_size", "expert_ffn_grouped", "moe_decode_layer_batch", "moe_test_stack_select")
+           "moe_batch_workspace_size", "expert_ffn_grouped", "moe_decode_layer_batch", "moe_test_stack_select",
+           "moe_decode_layer_noalloc")
 MAX_BATCH = 64
 MAX_GROUP_MIN = 16
 
@@ -195,6 +198,14 @@ def moe_decode_layer(desc, weights, io, ws, stream=None):
     lio = LayerIO(**{n: ptr(io.get(n)) for n, _ in LayerIO._fields_})
     return _check("moe_decode_layer", _moe_decode_layer(C.byref(desc), C.byref(lw), C.byref(lio), ptr(ws),
                                                         ws.numel() * ws.element_size(), stream_handle(stream)))
+
+
+def moe_decode_layer_noalloc(desc, weights, io, stream=None):
+    """moe_decode_layer with the library's static scratch array instead of a workspace."""
+    lw = weights if isinstance(weights, LayerWeights) else make_weights(weights)
+    lio = LayerIO(**{n: ptr(io.get(n)) for n, _ in LayerIO._fields_})
+    return _check("moe_decode_layer_noalloc", _moe_decode_layer_noalloc(C.byref(desc), C.byref(lw), C.byref(lio),
+                                                                        stream_handle(stream)))
 
 
 def moe_batch_workspace_size(desc, n_tok):

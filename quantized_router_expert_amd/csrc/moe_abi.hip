@@ -12,6 +12,13 @@
 
 using namespace moe;
 
+// The scratch array of moe_decode_layer_noalloc: one copy per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not the device array: kernels get the device address
+// that hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = 256 * 1024;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -65,6 +72,81 @@ bool bind_holds(void* ws, int n_layers, uint64_t hash) {
   for (const auto& r : g_bind)
     if (r.ws == (uintptr_t)ws && r.n_layers == n_layers && r.hash == hash) return true;
   return false;
+}
+
+// Argument checks of a single-layer call (everything but the workspace).
+int check_layer_call(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_layer_io* io) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  rc = check_weights(desc, w);
+  if (rc) return rc;
+  if (!io || !io->routed_out) return MOE_ERR_NULL;
+  if (desc->norm ? (!io->residual || !io->out_sum) : !io->x) return MOE_ERR_NULL;
+  if (desc->shared_ffn > 0 && !io->shared_out) return MOE_ERR_NULL;
+  if (io->shared_in && !io->routed_in) return MOE_ERR_NULL;
+  if ((io->x && !aligned(io->x, 16)) || (io->xn && !aligned(io->xn, 16)) || (io->xq && !aligned(io->xq, 4)) ||
+      (io->residual && !aligned(io->residual, 2)) || (io->out_sum && !aligned(io->out_sum, 2)) ||
+      !aligned(io->routed_out, 2) || (io->shared_out && !aligned(io->shared_out, 2)) ||
+      (io->logits && !aligned(io->logits, 4)) || (io->ids && !aligned(io->ids, 4)) ||
+      (io->weights && !aligned(io->weights, 4)) || (io->h && !aligned(io->h, 4)) || (io->hs && !aligned(io->hs, 4)))
+    return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+// a1..a6 for one token on the per-layer kernels; ws holds at least the
+// layer's intermediates (ws_layout(desc, 0) up to its pointer table) and its
+// router counters are zero.
+int decode_layer(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_layer_io* io, void* ws,
+                 hipStream_t st) {
+  int rc;
+  const WsLayout L = ws_layout(desc, 0);
+  const int H = desc->hidden, E = desc->n_experts, k = desc->top_k;
+  float* xn = io->xn ? io->xn : at<float>(ws, L.xn);
+  void* xq = io->xq ? io->xq : at<void>(ws, L.xq);
+  int32_t* ids = io->ids ? io->ids : at<int32_t>(ws, L.ids);
+  float* wts = io->weights ? io->weights : at<float>(ws, L.wts);
+  float* sg = io->shared_gate ? io->shared_gate : at<float>(ws, L.sg);
+  float* h = io->h ? io->h : at<float>(ws, L.h);
+  float* hs = io->hs ? io->hs : at<float>(ws, L.hs);
+  if (desc->norm) {
+    rc = launch_norm(io->residual, io->routed_in, io->shared_in, w->norm_w, H, 1, desc->eps, io->out_sum, xn, xq, 1, st);
+  } else {
+    if (io->xn) {
+      if (hipMemcpyAsync(xn, io->x, sizeof(float) * H, hipMemcpyDeviceToDevice, st) != hipSuccess) return MOE_ERR_HIP;
+    }
+    xn = io->xn ? io->xn : const_cast<float*>(io->x);
+    rc = launch_quantize(io->x, H, xq, st);
+  }
+  if (rc) return rc;
+  rc = launch_router(xn, w->router_w, desc->shared_ffn > 0 ? w->shared_gate_w : nullptr, 1, H, E, k,
+                     at<float>(ws, L.logits), io->logits, ids, wts, sg, at<unsigned>(ws, L.counters), st);
+  if (rc) return rc;
+  rc = launch_gate_up(desc, w, xq, ids, h, hs, st);
+  if (rc) return rc;
+  return launch_down(desc, w, h, hs, ids, wts, sg, io->routed_out, io->shared_out, st);
+}
+
+// ---- the scratch array of moe_decode_layer_noalloc (declared at file scope below)
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, looked up once per device; the first
+// call on a device also queues the clearing of the router counters (the only
+// part that must start at zero: every completed call returns them to zero).
+int scratch_for_current_device(void** out, hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    const int rc = launch_fill(p, sizeof(unsigned) * kCounterSlots / 4, 0u, st);
+    if (rc) return rc;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -157,48 +239,24 @@ int expert_ffn_q4k(const moe_layer_desc* desc, const moe_layer_weights* w, const
 
 int moe_decode_layer(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_layer_io* io, void* ws,
                      size_t ws_bytes, void* stream) {
-  int rc = check_desc(desc);
+  int rc = check_layer_call(desc, w, io);
   if (rc) return rc;
-  rc = check_weights(desc, w);
+  rc = check_ws(ws, ws_bytes, ws_layout(desc, 0).total);
   if (rc) return rc;
-  if (!io || !io->routed_out) return MOE_ERR_NULL;
-  if (desc->norm ? (!io->residual || !io->out_sum) : !io->x) return MOE_ERR_NULL;
-  if (desc->shared_ffn > 0 && !io->shared_out) return MOE_ERR_NULL;
-  if (io->shared_in && !io->routed_in) return MOE_ERR_NULL;
-  if ((io->x && !aligned(io->x, 16)) || (io->xn && !aligned(io->xn, 16)) || (io->xq && !aligned(io->xq, 4)) ||
-      (io->residual && !aligned(io->residual, 2)) || (io->out_sum && !aligned(io->out_sum, 2)) ||
-      !aligned(io->routed_out, 2) || (io->shared_out && !aligned(io->shared_out, 2)) ||
-      (io->logits && !aligned(io->logits, 4)) || (io->ids && !aligned(io->ids, 4)) ||
-      (io->weights && !aligned(io->weights, 4)) || (io->h && !aligned(io->h, 4)) || (io->hs && !aligned(io->hs, 4)))
-    return MOE_ERR_ALIGN;
-  const WsLayout L = ws_layout(desc, 0);
-  rc = check_ws(ws, ws_bytes, L.total);
+  return decode_layer(desc, w, io, ws, as_stream(stream));
+}
+
+int moe_decode_layer_noalloc(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_layer_io* io,
+                             void* stream) {
+  int rc = check_layer_call(desc, w, io);
   if (rc) return rc;
+  // the layer's intermediates end where the stack's pointer table would begin
+  if (ws_layout(desc, 0).table > kScratchBytes) return MOE_ERR_WORKSPACE;
+  void* sp = nullptr;
   hipStream_t st = as_stream(stream);
-  const int H = desc->hidden, E = desc->n_experts, k = desc->top_k;
-  float* xn = io->xn ? io->xn : at<float>(ws, L.xn);
-  void* xq = io->xq ? io->xq : at<void>(ws, L.xq);
-  int32_t* ids = io->ids ? io->ids : at<int32_t>(ws, L.ids);
-  float* wts = io->weights ? io->weights : at<float>(ws, L.wts);
-  float* sg = io->shared_gate ? io->shared_gate : at<float>(ws, L.sg);
-  float* h = io->h ? io->h : at<float>(ws, L.h);
-  float* hs = io->hs ? io->hs : at<float>(ws, L.hs);
-  if (desc->norm) {
-    rc = launch_norm(io->residual, io->routed_in, io->shared_in, w->norm_w, H, 1, desc->eps, io->out_sum, xn, xq, 1, st);
-  } else {
-    if (io->xn) {
-      if (hipMemcpyAsync(xn, io->x, sizeof(float) * H, hipMemcpyDeviceToDevice, st) != hipSuccess) return MOE_ERR_HIP;
-    }
-    xn = io->xn ? io->xn : const_cast<float*>(io->x);
-    rc = launch_quantize(io->x, H, xq, st);
-  }
+  rc = scratch_for_current_device(&sp, st);
   if (rc) return rc;
-  rc = launch_router(xn, w->router_w, desc->shared_ffn > 0 ? w->shared_gate_w : nullptr, 1, H, E, k,
-                     at<float>(ws, L.logits), io->logits, ids, wts, sg, at<unsigned>(ws, L.counters), st);
-  if (rc) return rc;
-  rc = launch_gate_up(desc, w, xq, ids, h, hs, st);
-  if (rc) return rc;
-  return launch_down(desc, w, h, hs, ids, wts, sg, io->routed_out, io->shared_out, st);
+  return decode_layer(desc, w, io, sp, st);
 }
 
 size_t moe_batch_workspace_size(const moe_layer_desc* desc, int n_tok) {

@@ -181,6 +181,11 @@ def test_layer_and_stack_validation(q):
     assert sel(FAKE, 1, 2048, 8, 0, FAKE, FAKE, None, None) == -2
     assert sel(FAKE, 1, 256, 17, 0, FAKE, FAKE, None, None) == -2
     assert sel(FAKE + 2, 1, 256, 8, 0, FAKE, FAKE, None, None) == -4
+    na = q._moe_decode_layer_noalloc
+    assert na(C.byref(d), C.byref(w), None, None) == -1
+    assert na(C.byref(d), C.byref(w), C.byref(io2), None) == -1
+    big = _desc(q, top_k=16, ffn=4096, shared_ffn=0)           # intermediates beyond the static array
+    assert na(C.byref(big), C.byref(w), C.byref(io), None) == -5
     assert q._moe_workspace_init(None, 1024, None) == -5
     assert q._moe_workspace_init(FAKE + 8, 1024, None) == -4
 
