@@ -636,6 +636,61 @@ __device__ __forceinline__ void rows_dot(int nrows, int T, RowFn rowfn, double* 
 }
 
 __device__ __forceinline__ double silu_f64(double x) { return x / (1.0 + exp(-x)); }
+
+// The value lane `src` (any lane of the wave) holds, as a double.
+__device__ __forceinline__ double lane_f64(double v, int src) {
+  const int lo = __builtin_amdgcn_ds_bpermute(src << 2, (int)lo32(v));
+  const int hi = __builtin_amdgcn_ds_bpermute(src << 2, (int)hi32(v));
+  return dbl((uint32_t)lo, (uint32_t)hi);
+}
+
+// SwiGLU outputs of npairs (gate row, up row) pairs: h_p = f32(silu(g_p) * u_p)
+// with g_p, u_p the fp32-rounded row values.  A pair takes 2*TP consecutive
+// lanes (TP = the next power of two >= min(T, 32)): the gate row's tasks in
+// the first TP, the up row's in the next TP (a lane takes tasks t, t+TP, ...);
+// each half is summed by a lane-group tree, the up sum travels to the gate
+// half's first lane, which calls store(p, h).  Waves [0, nw) (index `wave`)
+// take 32/TP pairs per pass, two passes' worth at a time (two independent
+// chains per lane).  pairfn(p) returns {gate row, up row, activations}.
+struct PairRef {
+  const uint8_t* gate;
+  const uint8_t* up;
+  ActLds act;
+};
+template <int TYPE, class PairFn, class Store>
+__device__ __forceinline__ void pair_h(int npairs, int T, PairFn pairfn, Store store, int wave, int nw) {
+  int TP = 1;
+  while (TP < T && TP < 32) TP <<= 1;
+  const int ppw = 32 / TP;
+  const int lane = threadIdx.x & 63;
+  const int ps = lane / (2 * TP), half = (lane / TP) & 1, t0 = lane & (TP - 1);
+  const int step = nw * ppw;
+  for (int p0 = wave * ppw; p0 < npairs; p0 += 2 * step) {
+    const int pa = p0 + ps, pb = p0 + step + ps;
+    const bool two = (p0 + step) < npairs;   // wave-uniform
+    const PairRef A = pairfn(pa < npairs ? pa : npairs - 1);
+    const uint8_t* ra = half ? A.up : A.gate;
+    double va = 0.0, vb = 0.0;
+    PairRef B = A;
+    const uint8_t* rb = ra;
+    if (two) {
+      B = pairfn(pb < npairs ? pb : npairs - 1);
+      rb = half ? B.up : B.gate;
+    }
+    for (int t = t0; t < T; t += TP) {
+      va += row_task<TYPE>(ra, t, A.act);
+      if (two) vb += row_task<TYPE>(rb, t, B.act);
+    }
+    va = group_sum_f64(va, TP);
+    const double ua = lane_f64(va, lane + TP < 64 ? lane + TP : lane);
+    if (two) vb = group_sum_f64(vb, TP);
+    const double ub = two ? lane_f64(vb, lane + TP < 64 ? lane + TP : lane) : 0.0;
+    if (t0 == 0 && half == 0) {
+      if (pa < npairs) store(pa, (float)(silu_f64((double)(float)va) * (double)(float)ua));
+      if (two && pb < npairs) store(pb, (float)(silu_f64((double)(float)vb) * (double)(float)ub));
+    }
+  }
+}
 __device__ __forceinline__ double sigmoid_f64(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 }  // namespace moe

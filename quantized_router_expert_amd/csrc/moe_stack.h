@@ -27,14 +27,14 @@ struct StackGeom {
   int G;
   int RR, SR, RD, RP;                 // per-workgroup rows: router, shared gate/up, down outputs, routed gate/up pairs
   int Kp, Kps;
-  int n_t, n_lg, n_h, n_sel;          // exchange sizes in 8-byte words (n_sel: selection words in LDS)
+  int n_t, n_lg, n_h, n_sel, n_y;     // exchange sizes in 8-byte words (n_sel: selection words in LDS)
   // LDS byte offsets
   int o_res, o_xn, o_xqc, o_xqd, o_xqs, o_nw, o_rrow, o_sgu, o_sdn, o_rgu, o_rdn, o_hqc, o_hqd, o_hqs, o_part, o_xbuf,
       o_sel, o_red, o_y, o_cand, o_keys, o_lgsel, o_hs;
   int sgu_half, rgu_half, rdn_slot;
   int lds;
   // workspace byte offsets
-  size_t w_ctrl, w_t, w_lg, w_h, w_trace, w_end;
+  size_t w_ctrl, w_t, w_lg, w_h, w_y, w_trace, w_end;
 };
 
 constexpr uint32_t kBoundMagic = 0x4d6f4553u;

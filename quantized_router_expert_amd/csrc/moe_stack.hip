@@ -52,6 +52,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+constexpr int kXcc = 8;   // accelerator complex dies (XCCs) of the MI355X, each with its own L2
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xfu;
+}
+
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -550,6 +557,7 @@ constexpr int stack_geometry_core(int H, int E, int k, int F, int Fs, int down_t
   g.n_lg = E + (has_sg ? 1 : 0);
   g.n_h = k * F + Fs;
   g.n_sel = 2 * k + 1;
+  g.n_y = k * H;
   const int nblk = k * (g.Kp / 32) + g.Kps / 32;
   // LDS
   long o = 0;
@@ -628,6 +636,10 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   // always come from the arguments
   constexpr bool FIX = S != 0;
   constexpr FixShape fs = kFixShapes[S];
+  // XCD slots: with 8 selected experts on 256 workgroups, slot s is taken by
+  // the 32 workgroups b with b % 8 == s, which the cooperative launch places
+  // on XCC s (checked below): their h exchange stays in that XCC's L2
+  constexpr bool XS = FIX && fs.k == kXcc && fs.G == 256;
   const StackGeom g = FIX ? kFixGeom<DT, ST, S> : a.g;
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   const int H = FIX ? fs.H : a.H, E = FIX ? fs.E : a.E, k = FIX ? fs.k : a.k, F = FIX ? fs.F : a.F,
@@ -671,6 +683,12 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
                        a.bound[2] == (uint32_t)a.table_hash && a.bound[3] == (uint32_t)(a.table_hash >> 32);
     const uint32_t err = __builtin_amdgcn_raw_buffer_load_b32(r_ctrl, kErrWord * 4, 0, kAuxSC1);
     s_fail = !bound ? 2 : (err != 0u ? 3 : 0);
+    // the XCD-slot exchanges need workgroup b on XCC b % 8; should a launch
+    // ever place it elsewhere, it stops here (status 1) instead of waiting
+    if (XS && s_fail == 0 && xcc_id() != (uint32_t)(b % kXcc)) {
+      __builtin_amdgcn_raw_buffer_store_b32(1u, r_ctrl, kErrWord * 4, 0, kAuxSC1);
+      s_fail = 3;
+    }
     v2u gv = __builtin_amdgcn_raw_buffer_load_b64(r_ctrl, 0, 0, kAuxSC1);
     s_gen = gv.x;
   }
@@ -693,7 +711,8 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   // scalar offset, which keeps one descriptor in scalar registers instead of
   // one per area and copy
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.ws + a.g.w_t, (uint32_t)(a.g.w_trace - a.g.w_t));
-  const uint32_t x_lg = (uint32_t)(a.g.w_lg - a.g.w_t), x_h = (uint32_t)(a.g.w_h - a.g.w_t);
+  const uint32_t x_lg = (uint32_t)(a.g.w_lg - a.g.w_t), x_h = (uint32_t)(a.g.w_h - a.g.w_t),
+                 x_y = (uint32_t)(a.g.w_y - a.g.w_t);
   const uint32_t rd_t = (b % kRepT) * rb_t, rd_lg = x_lg + (b % kRepLg) * rb_lg, rd_h = x_h + (b % kRepH) * rb_h;
 
   const long rb_gu = row_bytes(MOE_TYPE_Q4_K, H);
@@ -886,10 +905,14 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     stamp(l, 4);
     bstamp(l, 5);
     // ================= phase B: routed gate/up rows (this workgroup's slot and rows)
+    // XS: slot b % 8, h rows [f0, f0 + F/32) and down rows [dr0, dr0 + H/32)
+    // of that slot's expert; else consecutive workgroups share a slot
     const int p0 = b * g.RP;
-    const int slot = p0 / F;
-    const int f0 = p0 - slot * F;
-    const int nrp = (slot < k) ? min(g.RP, F - f0) : 0;
+    const int slot = XS ? (b % kXcc) : p0 / F;
+    const int f0 = XS ? (b / kXcc) * (F / (fs.G / kXcc)) : p0 - slot * F;
+    const int nrp = XS ? F / (fs.G / kXcc) : ((slot < k) ? min(g.RP, F - f0) : 0);
+    constexpr int RDX = XS ? fs.H / (fs.G / kXcc) : 0;
+    const int dr0 = (b / kXcc) * RDX;
     if (nrp > 0 && wave < kPollWaves) {
       const long e = sel[slot];
       stage_async(rgu, w.gate + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0, kPollWaves);
@@ -920,7 +943,12 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     // gate/up rows have landed, so they do not share the memory system with
     // them (requested together, the gate/up rows land later by more than the
     // request time saved)
-    if (nrd > 0 && wave >= kPollWaves) {
+    if (XS && wave >= kPollWaves) {
+      // this slot's down rows [dr0, dr0 + RDX): one contiguous stream
+      const long e = sel[slot];
+      stage_async(rdn, w.down + (e * H + dr0) * rb_dn, (uint32_t)(RDX * rb_dn), wave, kPollWaves,
+                  kStackWaves - kPollWaves);
+    } else if (nrd > 0 && wave >= kPollWaves) {
       // wave 4+j queues slots j, j+4, j+8, j+12: their ids are read first, so
       // the requests go out back to back instead of each after an LDS round trip
       const int j = wave - kPollWaves;
@@ -951,14 +979,25 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         const float gg = (float)part[tid];
         const float uu = (float)part[nrp + tid];
         const float hv = (float)(silu_f64((double)gg) * (double)uu);
-        ll_store_rep<kRepH>(rx, x_h, rb_h, slot * F + f0 + tid, __float_as_uint(hv), ep1);
+        if (XS) {   // this XCC's copy of the h area, word f; a plain store stays in the XCC's L2
+          const v2u v = {__float_as_uint(hv), ep1};
+          __builtin_amdgcn_raw_buffer_store_b64(v, rx, 8u * (f0 + tid), x_h + slot * rb_h, 0);
+        }
+        else
+          ll_store_rep<kRepH>(rx, x_h, rb_h, slot * F + f0 + tid, __float_as_uint(hv), ep1);
       }
     }
     // ================= R3: every routed h, read and quantised to Q8_1 by every workgroup
     // (the shared h was done in phase B)
     stamp(l, 6);
     bstamp(l, 7);
-    {
+    if constexpr (XS) {
+      // this slot's h only, from this XCC's copy of the h area (its L2)
+      if (!poll_quantize_h(rx, x_h + slot * rb_h, g.Kp / 32, g.Kp / 32, inv_nbr, F, (uint32_t)F, ep1, xbuf, hqc, hqd,
+                           hqs, wave, kStackWaves))
+        s_fail = 1;
+      bstamp(l, 14);
+    } else {
       // the down rows waves 4..7 requested in phase B have had the whole of
       // phase B to land, so every wave polls; each wave quantises its own
       // blocks as soon as they are current
@@ -975,7 +1014,61 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     if (s_fail) { fail_out(); return; }
     stamp(l, 8);
     bstamp(l, 9);
-    if (nrd > 0) {
+    if constexpr (XS) {
+      // this slot's down rows [dr0, dr0 + RDX) -> y (fp32 row values), and
+      // the shared expert's rows of the combine rows [row0, row0 + nrd)
+      const ActLds acts{hqc + (long)k * g.Kp, hqd + k * (g.Kp / 32), hqs + k * (g.Kp / 32)};
+      const ActLds actr{hqc, hqd, hqs};
+      rows_dot<DT>(RDX, tasks_per_row(DT, g.Kp), [&](int r) { return RowRef{rdn + (long)r * rb_dn, actr}; }, part,
+                   wave, kStackWaves);
+      if (has_sg)
+        rows_dot<ST>(nrd, tasks_per_row(ST, g.Kps), [&](int r) { return RowRef{sdn + (long)r * rb_sdn, acts}; },
+                     part + RDX, wave, kStackWaves);
+      lds_barrier();
+      // y of row i of slot s travels as word s*H + i (read by the one
+      // workgroup that combines row i)
+      if (tid < RDX) ll_store(rx, (x_y >> 3) + (uint32_t)(slot * H + dr0 + tid), __float_as_uint((float)part[tid]), ep1,
+                              kAuxSC1);
+      // the k slots' y of the combine rows: slot s's nrd words are pairs
+      // (s*H + row0)/2 + 0..nrd/2-1 (one cache line), polled by wave 0
+      if (wave == 0) {
+        const int lane = tid & 63;
+        constexpr int PPS = XS ? fs.H / fs.G / 2 : 1;   // word pairs per slot
+        const int ps = lane / PPS, q = lane - ps * PPS;
+        const int pair[1] = {ps < k ? (int)((x_y >> 4) + ((uint32_t)(ps * H + row0) >> 1) + q) : -1};
+        uint32_t lo[1] = {0u}, hi[1] = {0u};
+        if (!poll_lane_pairs<kAuxSC1, 1>(rx, 0u, pair, 0xffffffffu, ep1, lo, hi)) s_fail = 1;
+        if (ps < k) {
+          xbuf[ps * nrd + 2 * q] = lo[0];
+          xbuf[ps * nrd + 2 * q + 1] = hi[0];
+        }
+      }
+      lds_barrier();
+      if (s_fail) { fail_out(); return; }
+      // combine: one lane per (row, slot), the k slots of a row in k adjacent
+      // lanes summed by a DPP tree (fp64; y_s is the fp32 row value)
+      const float sgv = __uint_as_float(sel[2 * k]);
+      uint16_t* tb = reinterpret_cast<uint16_t*>(yv);
+      if (tid < nrd * kXcc) {
+        const int r = tid / kXcc, sl = tid - r * kXcc;
+        double v = (double)__uint_as_float(sel[k + sl]) * (double)__uint_as_float(xbuf[sl * nrd + r]);
+        v = group_sum_f64(v, kXcc);
+        if (sl == 0) {
+          const uint16_t routed = f32_to_bf16((float)v);
+          float t = bf16_to_f32(routed);
+          if (a.routed_out) a.routed_out[(long)l * H + row0 + r] = routed;
+          if (has_sg) {
+            const uint16_t shared = f32_to_bf16((float)((double)sgv * (double)(float)part[RDX + r]));
+            t = bf16_to_f32(f32_to_bf16(bf16_to_f32(routed) + bf16_to_f32(shared)));
+            if (a.shared_out) a.shared_out[(long)l * H + row0 + r] = shared;
+          }
+          tb[r] = f32_to_bf16(t);
+        }
+      }
+      lds_barrier();
+      for (int r2 = tid; 2 * r2 < nrd; r2 += kStackThreads)
+        ll_store_rep<kRepT>(rx, 0u, rb_t, (row0 >> 1) + r2, (uint32_t)tb[2 * r2] | ((uint32_t)tb[2 * r2 + 1] << 16), ep2);
+    } else if (nrd > 0) {
       // row r < k*nrd is row r % nrd of slot r / nrd (the quotient from a
       // float product, exact as for the h blocks above); with the shared
       // expert's rows of the same type, its nrd rows follow as one more slot
@@ -1097,6 +1190,7 @@ void stack_ws_layout(StackGeom* g, size_t base) {
   g->w_t = take((size_t)kRepT * rep_bytes(g->n_t));
   g->w_lg = take((size_t)kRepLg * rep_bytes(g->n_lg));
   g->w_h = take((size_t)kRepH * rep_bytes(g->n_h));
+  g->w_y = take(8u * (size_t)g->n_y);
   g->w_trace = take(8u * kTraceLayers * kTraceSlots + 8u * kTraceLayers * kTraceMaxG * kBlockEvents);
   g->w_end = o;
 }
