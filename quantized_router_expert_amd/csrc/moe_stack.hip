@@ -944,11 +944,13 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     // them (requested together, the gate/up rows land later by more than the
     // request time saved)
     if (XS && wave >= kPollWaves) {
-      // this slot's down rows [dr0, dr0 + RDX): one contiguous stream
+      // this slot's down rows [dr0, dr0 + RDX): one contiguous stream, queued
+      // once the gate/up rows have landed (queued beside them, they delay the
+      // gate/up rows by more than the down rows gain)
       const long e = sel[slot];
       stage_async(rdn, w.down + (e * H + dr0) * rb_dn, (uint32_t)(RDX * rb_dn), wave, kPollWaves,
                   kStackWaves - kPollWaves);
-    } else if (nrd > 0 && wave >= kPollWaves) {
+    } else if (!XS && nrd > 0 && wave >= kPollWaves) {
       // wave 4+j queues slots j, j+4, j+8, j+12: their ids are read first, so
       // the requests go out back to back instead of each after an LDS round trip
       const int j = wave - kPollWaves;
@@ -992,6 +994,13 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     stamp(l, 6);
     bstamp(l, 7);
     if constexpr (XS) {
+      // the shared expert's rows of the combine rows [row0, row0 + nrd): its
+      // h was quantised in phase B, so this runs while the slot's h travels
+      if (has_sg) {
+        const ActLds acts{hqc + (long)k * g.Kp, hqd + k * (g.Kp / 32), hqs + k * (g.Kp / 32)};
+        rows_dot<ST>(nrd, tasks_per_row(ST, g.Kps), [&](int r) { return RowRef{sdn + (long)r * rb_sdn, acts}; },
+                     part + RDX, wave, kStackWaves);
+      }
       // this slot's h only, from this XCC's copy of the h area (its L2)
       if (!poll_quantize_h(rx, x_h + slot * rb_h, g.Kp / 32, g.Kp / 32, inv_nbr, F, (uint32_t)F, ep1, xbuf, hqc, hqd,
                            hqs, wave, kStackWaves))
@@ -1017,13 +1026,9 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     if constexpr (XS) {
       // this slot's down rows [dr0, dr0 + RDX) -> y (fp32 row values), and
       // the shared expert's rows of the combine rows [row0, row0 + nrd)
-      const ActLds acts{hqc + (long)k * g.Kp, hqd + k * (g.Kp / 32), hqs + k * (g.Kp / 32)};
       const ActLds actr{hqc, hqd, hqs};
       rows_dot<DT>(RDX, tasks_per_row(DT, g.Kp), [&](int r) { return RowRef{rdn + (long)r * rb_dn, actr}; }, part,
                    wave, kStackWaves);
-      if (has_sg)
-        rows_dot<ST>(nrd, tasks_per_row(ST, g.Kps), [&](int r) { return RowRef{sdn + (long)r * rb_sdn, acts}; },
-                     part + RDX, wave, kStackWaves);
       lds_barrier();
       // y of row i of slot s travels as word s*H + i (read by the one
       // workgroup that combines row i)
