@@ -41,7 +41,10 @@ constexpr int kPollWaves = 4;   // waves 0..3 poll and load the routed gate/up r
 // few cache lines.  Eight copies shorten the logits and h exchanges (2 and 4
 // copies of h helped less, 16 did worse); for t the extra stores cost more
 // than they save.
-constexpr int kRepT = 1, kRepLg = 8, kRepH = 8;   // measured: t copies cost more than they save
+// t: eight copies in the workspace, one per XCC for the XCD-slot path (each
+// XCC builds all of t in its own copy); the other path writes and reads copy
+// 0 only (measured: more copies of t cost more stores than they save)
+constexpr int kRepT = 8, kRepLg = 8, kRepH = 8;
 constexpr uint32_t rep_bytes(int n_words) { return (8u * (uint32_t)n_words + 4095u) & ~4095u; }
 constexpr int kAuxSC1 = 16;     // agent-coherent (bypasses the XCD L2)
 constexpr uint32_t kSpinLimit = 1u << 22;
@@ -557,7 +560,7 @@ constexpr int stack_geometry_core(int H, int E, int k, int F, int Fs, int down_t
   g.n_lg = E + (has_sg ? 1 : 0);
   g.n_h = k * F + Fs;
   g.n_sel = 2 * k + 1;
-  g.n_y = k * H;
+  g.n_y = (k + 1) * H;   // the slots' down row values, then the shared expert's
   const int nblk = k * (g.Kp / 32) + g.Kps / 32;
   // LDS
   long o = 0;
@@ -571,6 +574,10 @@ constexpr int stack_geometry_core(int H, int E, int k, int F, int Fs, int down_t
   g.o_rrow = take((long)g.RR * up1k(4L * H));
   g.sgu_half = up1k(g.SR * rb_sgu);
   g.o_sgu = take(2L * g.sgu_half);
+  // the XCD-slot path (k = 8 on 256 workgroups) combines H/32 rows per
+  // workgroup: as many row values
+  const bool xs = (k == 8 && G == 256);
+  const int rdx = xs ? H / (G / 8) : 0;
   g.o_sdn = take(up1k(g.RD * rb_sdn));
   g.rgu_half = up1k(g.RP * rb_gu);
   g.o_rgu = take(2L * g.rgu_half);
@@ -582,6 +589,7 @@ constexpr int stack_geometry_core(int H, int E, int k, int F, int Fs, int down_t
   long np = 2L * g.RP;                               // fp64 row values of one phase
   np = np > 2L * g.SR ? np : 2L * g.SR;
   np = np > (long)(k + 1) * g.RD ? np : (long)(k + 1) * g.RD;
+  np = np > 2L * rdx ? np : 2L * rdx;
   g.o_part = take(8L * np);
   long xb = g.n_h;                                   // words landing from an exchange
   xb = xb > g.n_t ? xb : g.n_t;
@@ -713,7 +721,8 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.ws + a.g.w_t, (uint32_t)(a.g.w_trace - a.g.w_t));
   const uint32_t x_lg = (uint32_t)(a.g.w_lg - a.g.w_t), x_h = (uint32_t)(a.g.w_h - a.g.w_t),
                  x_y = (uint32_t)(a.g.w_y - a.g.w_t);
-  const uint32_t rd_t = (b % kRepT) * rb_t, rd_lg = x_lg + (b % kRepLg) * rb_lg, rd_h = x_h + (b % kRepH) * rb_h;
+  const uint32_t rd_t = XS ? (b % kXcc) * rb_t : 0u, rd_lg = x_lg + (b % kRepLg) * rb_lg,
+                 rd_h = x_h + (b % kRepH) * rb_h;
 
   const long rb_gu = row_bytes(MOE_TYPE_Q4_K, H);
   const long rb_sgu = has_sg ? row_bytes(ST, H) : 0;
@@ -727,6 +736,9 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   const int sf0 = b * g.SR;
   const int nsr = has_sg ? max(0, min(g.SR, Fs - sf0)) : 0;
 
+  // XS: this workgroup's down rows (and combine rows) [dr0, dr0 + RDX)
+  constexpr int RDX = XS ? fs.H / (fs.G / kXcc) : 0;
+  const int dr0 = (b / kXcc) * RDX;
   // weights that do not depend on the routing decision, for layer `w`
   auto prefetch_fixed = [&](const LayerPtrs& w) {
     stage_async(smem + g.o_nw, w.norm_w, (uint32_t)(H * 4), wave, kPollWaves, kStackWaves - kPollWaves);
@@ -911,8 +923,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     const int slot = XS ? (b % kXcc) : p0 / F;
     const int f0 = XS ? (b / kXcc) * (F / (fs.G / kXcc)) : p0 - slot * F;
     const int nrp = XS ? F / (fs.G / kXcc) : ((slot < k) ? min(g.RP, F - f0) : 0);
-    constexpr int RDX = XS ? fs.H / (fs.G / kXcc) : 0;
-    const int dr0 = (b / kXcc) * RDX;
+
     if (nrp > 0 && wave < kPollWaves) {
       const long e = sel[slot];
       stage_async(rgu, w.gate + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0, kPollWaves);
@@ -997,9 +1008,15 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       // the shared expert's rows of the combine rows [row0, row0 + nrd): its
       // h was quantised in phase B, so this runs while the slot's h travels
       if (has_sg) {
+        // computed once: rows [row0, row0 + nrd), sent as fp32 row values
+        // (words H*k + row0 + r of the y area) to the workgroups that combine them
         const ActLds acts{hqc + (long)k * g.Kp, hqd + k * (g.Kp / 32), hqs + k * (g.Kp / 32)};
         rows_dot<ST>(nrd, tasks_per_row(ST, g.Kps), [&](int r) { return RowRef{sdn + (long)r * rb_sdn, acts}; },
                      part + RDX, wave, kStackWaves);
+        lds_barrier();
+        if (tid < nrd)
+          ll_store(rx, (x_y >> 3) + (uint32_t)(k * H + row0 + tid), __float_as_uint((float)part[RDX + tid]), ep1,
+                   kAuxSC1);
       }
       // this slot's h only, from this XCC's copy of the h area (its L2)
       if (!poll_quantize_h(rx, x_h + slot * rb_h, g.Kp / 32, g.Kp / 32, inv_nbr, F, (uint32_t)F, ep1, xbuf, hqc, hqd,
@@ -1034,45 +1051,51 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       // workgroup that combines row i)
       if (tid < RDX) ll_store(rx, (x_y >> 3) + (uint32_t)(slot * H + dr0 + tid), __float_as_uint((float)part[tid]), ep1,
                               kAuxSC1);
-      // the k slots' y of the combine rows: slot s's nrd words are pairs
-      // (s*H + row0)/2 + 0..nrd/2-1 (one cache line), polled by wave 0
-      if (wave == 0) {
-        const int lane = tid & 63;
-        constexpr int PPS = XS ? fs.H / fs.G / 2 : 1;   // word pairs per slot
-        const int ps = lane / PPS, q = lane - ps * PPS;
-        const int pair[1] = {ps < k ? (int)((x_y >> 4) + ((uint32_t)(ps * H + row0) >> 1) + q) : -1};
+      // the k slots' y of this workgroup's rows [dr0, dr0 + RDX): slot s's
+      // words s*H + dr0 .. are RDX/2 pairs; waves 0..3 poll one pair per lane
+      // (and, on wave 4, the shared expert's row values of the same rows:
+      // words k*H + dr0 .., landed as "slot" k)
+      if (wave <= kPollWaves) {
+        constexpr int PPS = XS ? RDX / 2 : 1;   // word pairs per slot
+        const int ps = tid / PPS, q = tid - ps * PPS;
+        const bool live = ps < k || (ps == k && has_sg);
+        const int pair[1] = {live ? (int)((x_y >> 4) + ((uint32_t)(ps * H + dr0) >> 1) + q) : -1};
         uint32_t lo[1] = {0u}, hi[1] = {0u};
         if (!poll_lane_pairs<kAuxSC1, 1>(rx, 0u, pair, 0xffffffffu, ep1, lo, hi)) s_fail = 1;
-        if (ps < k) {
-          xbuf[ps * nrd + 2 * q] = lo[0];
-          xbuf[ps * nrd + 2 * q + 1] = hi[0];
+        if (live) {
+          xbuf[ps * RDX + 2 * q] = lo[0];
+          xbuf[ps * RDX + 2 * q + 1] = hi[0];
         }
       }
       lds_barrier();
       if (s_fail) { fail_out(); return; }
       // combine: one lane per (row, slot), the k slots of a row in k adjacent
-      // lanes summed by a DPP tree (fp64; y_s is the fp32 row value)
+      // lanes summed by a DPP tree (fp64; y_s is the fp32 row value); the
+      // per-layer outputs come from XCC 0's workgroups
       const float sgv = __uint_as_float(sel[2 * k]);
       uint16_t* tb = reinterpret_cast<uint16_t*>(yv);
-      if (tid < nrd * kXcc) {
-        const int r = tid / kXcc, sl = tid - r * kXcc;
-        double v = (double)__uint_as_float(sel[k + sl]) * (double)__uint_as_float(xbuf[sl * nrd + r]);
+      for (int i = tid; i < RDX * kXcc; i += kStackThreads) {
+        const int r = i / kXcc, sl = i - r * kXcc;
+        double v = (double)__uint_as_float(sel[k + sl]) * (double)__uint_as_float(xbuf[sl * RDX + r]);
         v = group_sum_f64(v, kXcc);
         if (sl == 0) {
           const uint16_t routed = f32_to_bf16((float)v);
           float t = bf16_to_f32(routed);
-          if (a.routed_out) a.routed_out[(long)l * H + row0 + r] = routed;
+          if (a.routed_out && slot == 0) a.routed_out[(long)l * H + dr0 + r] = routed;
           if (has_sg) {
-            const uint16_t shared = f32_to_bf16((float)((double)sgv * (double)(float)part[RDX + r]));
+            const uint16_t shared = f32_to_bf16((float)((double)sgv * (double)__uint_as_float(xbuf[k * RDX + r])));
             t = bf16_to_f32(f32_to_bf16(bf16_to_f32(routed) + bf16_to_f32(shared)));
-            if (a.shared_out) a.shared_out[(long)l * H + row0 + r] = shared;
+            if (a.shared_out && slot == 0) a.shared_out[(long)l * H + dr0 + r] = shared;
           }
           tb[r] = f32_to_bf16(t);
         }
       }
       lds_barrier();
-      for (int r2 = tid; 2 * r2 < nrd; r2 += kStackThreads)
-        ll_store_rep<kRepT>(rx, 0u, rb_t, (row0 >> 1) + r2, (uint32_t)tb[2 * r2] | ((uint32_t)tb[2 * r2 + 1] << 16), ep2);
+      // t rows [dr0, dr0 + RDX) into this XCC's copy of t: plain stores, its L2
+      for (int r2 = tid; 2 * r2 < RDX; r2 += kStackThreads) {
+        const v2u v = {(uint32_t)tb[2 * r2] | ((uint32_t)tb[2 * r2 + 1] << 16), ep2};
+        __builtin_amdgcn_raw_buffer_store_b64(v, rx, 8u * ((dr0 >> 1) + r2), rd_t, 0);
+      }
     } else if (nrd > 0) {
       // row r < k*nrd is row r % nrd of slot r / nrd (the quotient from a
       // float product, exact as for the h blocks above); with the shared
@@ -1114,7 +1137,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       }
       lds_barrier();
       for (int r2 = tid; 2 * r2 < nrd; r2 += kStackThreads)
-        ll_store_rep<kRepT>(rx, 0u, rb_t, (row0 >> 1) + r2, (uint32_t)tb[2 * r2] | ((uint32_t)tb[2 * r2 + 1] << 16), ep2);
+        ll_store_rep<1>(rx, 0u, rb_t, (row0 >> 1) + r2, (uint32_t)tb[2 * r2] | ((uint32_t)tb[2 * r2 + 1] << 16), ep2);
     }
     lds_barrier();
     stamp(l, 9);
