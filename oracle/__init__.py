@@ -74,7 +74,7 @@ def _declare(L):
     L.orc_expert_ffn.argtypes = [P, P, P, P, P, C.c_float, P]; L.orc_expert_ffn.restype = None
     L.orc_moe_layer.argtypes = [P, P, P, P, P, P, P]; L.orc_moe_layer.restype = C.c_int
     L.orc_moe_layer_sel.argtypes = [P, P, P, P, P, P, P, P]; L.orc_moe_layer_sel.restype = C.c_int
-    L.orc_moe_stack.argtypes = [P, P, C.c_int, P, P, P, P, P, P]; L.orc_moe_stack.restype = C.c_int
+    L.orc_moe_stack.argtypes = [P, P, C.c_int, P, P, P, P, P, P, P]; L.orc_moe_stack.restype = C.c_int
     L.orc_num_threads.argtypes = []; L.orc_num_threads.restype = C.c_int
     L.orc_quantize_q4k.argtypes = [P, P]; L.orc_quantize_q4k.restype = None
     L.orc_requant_q4k.argtypes = [P, C.c_int, C.c_int, C.c_int, P]; L.orc_requant_q4k.restype = C.c_int
@@ -395,8 +395,9 @@ def moe_layer_batch(desc, weights, n_tok, residual=None, routed_prev=None, share
     return out
 
 
-def moe_stack(desc, layers, inp, per_layer=False):
-    """L-layer stack for one token; layers is a list of weight dicts."""
+def moe_stack(desc, layers, inp, per_layer=False, attn=None):
+    """L-layer stack for one token; layers is a list of weight dicts; attn
+    ([L][H] bf16 bits or None) is each layer's attention-block output."""
     L = lib()
     held = _Held()
     nl = len(layers)
@@ -407,7 +408,8 @@ def moe_stack(desc, layers, inp, per_layer=False):
     rt = np.zeros((nl, desc.H), np.uint16) if per_layer else None
     sh = np.zeros((nl, desc.H), np.uint16) if per_layer else None
     rs = np.zeros((nl, desc.H), np.uint16) if per_layer else None
-    rc = L.orc_moe_stack(C.byref(desc), arr, nl, _p(inp), _p(out), _p(ids), _p(rt), _p(sh), _p(rs))
+    at = None if attn is None else np.ascontiguousarray(attn, dtype=np.uint16)
+    rc = L.orc_moe_stack(C.byref(desc), arr, nl, _p(inp), _p(at), _p(out), _p(ids), _p(rt), _p(sh), _p(rs))
     if rc != 0:
         raise ValueError("oracle rejected the stack description")
     if per_layer:

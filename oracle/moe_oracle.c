@@ -911,7 +911,7 @@ int orc_moe_layer_batch(const orc_desc* d, const orc_weights* w, int n_tok,
  * the last layer's routed+shared, folded the same way the next norm would.
  * Requires norm = 1. */
 int orc_moe_stack(const orc_desc* d, const orc_weights* layers, int L,
-                  const uint16_t* input, uint16_t* output,
+                  const uint16_t* input, const uint16_t* attn_per_layer, uint16_t* output,
                   int32_t* ids_per_layer, uint16_t* routed_per_layer,
                   uint16_t* shared_per_layer, uint16_t* resid_per_layer)
 {
@@ -935,7 +935,24 @@ int orc_moe_stack(const orc_desc* d, const orc_weights* layers, int L,
         o.routed = nrouted;
         o.shared = nshared;
         if (ids_per_layer) o.ids = ids_per_layer + (long)l * d->k;
-        rc = orc_moe_layer(d, &layers[l], res, routed, d->Fs > 0 ? shared : NULL, NULL, &o);
+        if (attn_per_layer) {
+            /* Reading of the layer behind an attention block: the fold of the
+             * previous outputs (the add that precedes the attention's input
+             * norm) gives u1; the attention block is outside this stage, its
+             * bf16 output is an input; the post-attention add-norm takes
+             * bf16(u1 + attn) as the residual it normalises for the experts
+             * ([P273] Relation to open PRs: add_rmsnorm2_q8 after the
+             * attention, add_rmsnorm3 folding the expert outputs). */
+            for (int i = 0; i < H; ++i) {
+                double t = d->Fs > 0
+                    ? orc_bf16_to_f64(st_bf16(orc_bf16_to_f64(routed[i]) + orc_bf16_to_f64(shared[i])))
+                    : orc_bf16_to_f64(routed[i]);
+                nres[i] = st_bf16(orc_bf16_to_f64(res[i]) + t);
+            }
+            rc = orc_moe_layer(d, &layers[l], nres, attn_per_layer + (long)l * H, NULL, NULL, &o);
+        } else {
+            rc = orc_moe_layer(d, &layers[l], res, routed, d->Fs > 0 ? shared : NULL, NULL, &o);
+        }
         memcpy(res, nres, sizeof(uint16_t) * (size_t)H);
         memcpy(routed, nrouted, sizeof(uint16_t) * (size_t)H);
         memcpy(shared, nshared, sizeof(uint16_t) * (size_t)H);

@@ -169,10 +169,13 @@ int orc_moe_layer_sel(const orc_desc* d, const orc_weights* w,
 
 /* L-layer stack for one token: res_0 = input, previous outputs zero at layer 0;
  * layer l folds the previous layer's routed/shared into its norm; the result
- * is the fold a virtual layer L would do.  Per-layer outputs are optional
- * (arrays of L entries each, or NULL). */
+ * is the fold a virtual layer L would do.  With attn_per_layer ([L][H] bf16,
+ * an attention block's output per layer) layer l first folds the previous
+ * outputs, u1 = bf16(res + bf16(routed + shared)), then normalises
+ * u2 = bf16(u1 + attn_l) (which becomes its out_sum).  Per-layer outputs are
+ * optional (arrays of L entries each, or NULL). */
 int orc_moe_stack(const orc_desc* d, const orc_weights* layers, int L,
-                  const uint16_t* input, uint16_t* output,
+                  const uint16_t* input, const uint16_t* attn_per_layer, uint16_t* output,
                   int32_t* ids_per_layer /* [L][k] or NULL */,
                   uint16_t* routed_per_layer /* [L][H] or NULL */,
                   uint16_t* shared_per_layer /* [L][H] or NULL */,

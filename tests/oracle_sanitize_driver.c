@@ -11,7 +11,8 @@
  *   gate.u8 up.u8 down.u8 sgate.u8 sup.u8 sdown.u8   (L layers back to back)
  *   input.u16     [H]              batch_res.u16 batch_rp.u16 batch_sp.u16 [n_tok][H]
  *   logits.f32    [n_sets][E]      q81_x.f32 [n] (n % 32 == 0)
- * Outputs: stack_out.u16 [H], stack_ids.i32 [L][k], batch_routed.u16
+ *   attn.u16      [L][H]           (an attention block's output per layer)
+ * Outputs: stack_out.u16 [H], stack_ids.i32 [L][k], stack_attn_out.u16 [H], batch_routed.u16
  * [n_tok][H], batch_shared.u16 [n_tok][H], topk.i32 [n_sets][k], q81.u8,
  * requant_down.u8, requant_sgate.u8.
  */
@@ -99,9 +100,14 @@ int main(int argc, char** argv)
     uint16_t* input = (uint16_t*)read_file("input.u16", NULL);
     uint16_t* out = (uint16_t*)calloc((size_t)H, sizeof(uint16_t));
     int32_t* ids = (int32_t*)calloc((size_t)L * k, sizeof(int32_t));
-    if (orc_moe_stack(&d, W, L, input, out, ids, NULL, NULL, NULL) != 0) return 3;
+    if (orc_moe_stack(&d, W, L, input, NULL, out, ids, NULL, NULL, NULL) != 0) return 3;
     write_file("stack_out.u16", out, sizeof(uint16_t) * (size_t)H);
     write_file("stack_ids.i32", ids, sizeof(int32_t) * (size_t)L * k);
+    /* the stack behind an attention block's outputs */
+    uint16_t* attn = (uint16_t*)read_file("attn.u16", NULL);
+    if (orc_moe_stack(&d, W, L, input, attn, out, ids, NULL, NULL, NULL) != 0) return 7;
+    write_file("stack_attn_out.u16", out, sizeof(uint16_t) * (size_t)H);
+    free(attn);
 
     /* the grouped batch on layer 0 */
     uint16_t* br = (uint16_t*)read_file("batch_res.u16", NULL);

@@ -206,3 +206,29 @@ def test_layer_with_given_selection(orc):
     for bad in ([0] * cfg.k, list(range(cfg.k - 1)) + [cfg.E], list(range(cfg.k - 1)) + [-1]):
         with pytest.raises(ValueError):
             orc.moe_layer(desc, W, res, rp, sp, ids=np.array(bad, np.int32))
+
+
+def test_stack_behind_attention_blocks(orc):
+    """The stack with an attention block's output per layer: each layer is
+    the fold of the previous outputs (u1) followed by the 2-input layer on
+    (u1, attn) -- checked against that composition built from the separately
+    pinned fold and layer; an all-zero attention output changes nothing
+    (bf16(u1 + 0) = u1), bit for bit; and a nonzero one changes the result."""
+    cfg = wl.variant(wl.CONFIGS["layer"], E=16, layers=3)
+    Ws = [_np_weights(cfg, l) for l in range(3)]
+    desc = orc.make_desc(cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs)
+    inp = wl.u16(wl.token_inputs(cfg, 0)["residual"])
+    attn = np.stack([wl.u16(wl.attention_output(cfg, 0, l)) for l in range(3)])
+    out, per = orc.moe_stack(desc, Ws, inp, per_layer=True, attn=attn)
+    res, rt, sh = inp, None, None
+    for l in range(3):
+        u1 = orc.add_rmsnorm(res, rt, sh, Ws[l]["norm_w"], cfg.eps)[0] if l else res
+        o = orc.moe_layer(desc, Ws[l], u1, attn[l], None)
+        assert np.array_equal(per["ids"][l], o["ids"]) and np.array_equal(per["resid"][l], o["out_sum"])
+        assert np.array_equal(per["routed"][l], o["routed"]) and np.array_equal(per["shared"][l], o["shared"])
+        res, rt, sh = o["out_sum"], o["routed"], o["shared"]
+    fin = orc.add_rmsnorm(res, rt, sh, Ws[0]["norm_w"], cfg.eps)[0]
+    assert np.array_equal(out, fin)
+    plain = orc.moe_stack(desc, Ws, inp)
+    assert np.array_equal(orc.moe_stack(desc, Ws, inp, attn=np.zeros_like(attn)), plain)
+    assert not np.array_equal(out, plain)

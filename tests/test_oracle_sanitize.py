@@ -54,6 +54,7 @@ def test_oracle_under_sanitizers(orc, sanitized, tmp_path):
         "sgw.f32": np.stack([w["shared_gate_w"] for w in Ws]),
         "input.u16": inp, "batch_res.u16": res, "batch_rp.u16": rp, "batch_sp.u16": sp,
         "logits.f32": lg, "q81_x.f32": q81_x,
+        "attn.u16": np.stack([wl.u16(wl.attention_output(cfg, 0, l)) for l in range(L)]),
     }
     for name in ("gate", "up", "down", "sgate", "sup", "sdown"):
         files[name + ".u8"] = np.concatenate([w[name].reshape(-1) for w in Ws])
@@ -72,6 +73,7 @@ def test_oracle_under_sanitizers(orc, sanitized, tmp_path):
     out, per = orc.moe_stack(do, Ws, inp, per_layer=True)
     assert np.array_equal(got("stack_out.u16", np.uint16), out)
     assert np.array_equal(got("stack_ids.i32", np.int32).reshape(L, k), per["ids"])
+    assert np.array_equal(got("stack_attn_out.u16", np.uint16), orc.moe_stack(do, Ws, inp, attn=files["attn.u16"]))
     ob = orc.moe_layer_batch(do, Ws[0], n_tok, residual=res, routed_prev=rp, shared_prev=sp)
     assert np.array_equal(got("batch_routed.u16", np.uint16).reshape(n_tok, H), ob["routed"])
     assert np.array_equal(got("batch_shared.u16", np.uint16).reshape(n_tok, H), ob["shared"])

@@ -80,7 +80,8 @@ def row_bytes(typ, K):
 
 # ------------------------------------------------------------------ seeds
 # Tensor ids for the seed spawn key.
-T_NORM, T_ROUTER, T_SGATE, T_GATE, T_UP, T_DOWN, T_SG, T_SU, T_SD, T_INPUT, T_RPREV, T_SPREV, T_ZERO, T_PAIR, T_STEER = range(15)
+T_NORM, T_ROUTER, T_SGATE, T_GATE, T_UP, T_DOWN, T_SG, T_SU, T_SD, T_INPUT, T_RPREV, T_SPREV, T_ZERO, T_PAIR, T_STEER, \
+    T_ATTN = range(16)
 
 
 def seed_for(cfg_index, layer, tensor, expert=0, base=0):
@@ -275,6 +276,13 @@ def token_inputs(cfg, token, device="cpu", layer=0):
         res = torch.zeros_like(res)
     out = {"residual": res.to(torch.bfloat16)}
     return out
+
+
+def attention_output(cfg, token, layer, device="cpu", std=1.0):
+    """The attention block's output of one layer for one token: bf16 [H] drawn
+    ~N(0, std) (a stand-in for the block the MoE stage follows; its own
+    arithmetic is outside the stage)."""
+    return randn((cfg.H,), seed_for(cfg.config_index, layer, T_ATTN, token), device, std).to(torch.bfloat16)
 
 
 def prev_outputs(cfg, token, device="cpu", layer=0):
