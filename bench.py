@@ -9,7 +9,7 @@ before timing.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 128] [--warmup 8] [--mode auto|kernels|persistent]
                   [--variant after|before|both] [--no-cpu] [--no-batch] [--no-requant]
-                  [--no-e128] [--no-layer] [--calib-copy] [--trace]
+                  [--no-e128] [--no-layer] [--no-attn] [--calib-copy] [--trace]
 """
 import argparse
 import json
@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--no-requant", action="store_true", help="skip the load-time requantisation leg")
     p.add_argument("--no-e128", action="store_true", help="skip the 128-expert 48-layer stack leg")
     p.add_argument("--no-layer", action="store_true", help="skip the single-layer moe_decode_layer leg")
+    p.add_argument("--no-attn", action="store_true", help="skip the stack-behind-attention leg")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--cpu-seconds-1t", type=float, default=6.0, help="single-thread oracle time")
     p.add_argument("--calib-copy", action="store_true",
@@ -65,9 +66,11 @@ def algorithmic_bytes(cfg, shared_type, down_type):
 
 
 class Stack:
-    """40 layers of weights on the GPU plus everything one token needs."""
+    """40 layers of weights on the GPU plus everything one token needs
+    (with_attn: a seeded attention-block output per token and layer, which
+    each layer adds to the folded residual before its norm)."""
 
-    def __init__(self, q, cfg, shared_type, down_type, mode):
+    def __init__(self, q, cfg, shared_type, down_type, mode, with_attn=False):
         self.q, self.cfg = q, cfg
         self.shared_type, self.down_type = shared_type, down_type
         t0 = time.time()
@@ -80,6 +83,10 @@ class Stack:
         self.arr = q.layer_array(self.layers)
         self.ws = q.alloc_workspace(self.desc, cfg.layers)
         self.inputs = torch.stack([wl.token_inputs(cfg, t, "cuda")["residual"] for t in range(cfg.tokens)])
+        self.attn = None
+        if with_attn:
+            self.attn = torch.stack([torch.stack([wl.attention_output(cfg, t, l, "cuda") for l in range(cfg.layers)])
+                                     for t in range(cfg.tokens)]).contiguous()
         self.out = torch.zeros(cfg.tokens, cfg.H, dtype=torch.bfloat16, device="cuda")
         self.ids = torch.zeros(cfg.layers, cfg.k, dtype=torch.int32, device="cuda")
         self.mode = self._pick_mode(mode)
@@ -103,7 +110,7 @@ class Stack:
 
     def run_eager(self, t, mode, ids=None):
         self.q.moe_decode_stack(self.desc, None, self.inputs[t], self.out[t], ids, None, mode, self.ws,
-                                layer_array=self.arr)
+                                layer_array=self.arr, attn=None if self.attn is None else self.attn[t])
 
     def _capture(self):
         """One HIP graph per token input (4 kernels per layer + the final fold)."""
@@ -291,6 +298,28 @@ def batch_leg(q, sizes=(8, 32), group_min=9, iters=30):
         print(f"# batch {n}: {us:.1f} us per layer step, {distinct} distinct experts, "
               f"{out[f'batch{n}']['achieved_GBs']:.0f} GB/s", file=sys.stderr, flush=True)
     return out
+
+
+def attn_leg(q, steps, warmup, repeats):
+    """The 40-layer stack (Q4_K shared and down) behind an attention block per
+    layer: each layer adds a seeded bf16 attention output to the folded
+    residual (the post-attention add-norm) before its norm.  Timed like the
+    primary stack."""
+    cfg = wl.CONFIGS["stack"]
+    stack = Stack(q, cfg, wl.Q4_K, wl.Q4_K, "auto", with_attn=True)
+    us = time_steps(stack, steps, warmup, repeats)
+    med = float(np.median(us))
+    alg = algorithmic_bytes(cfg, wl.Q4_K, wl.Q4_K)
+    require_status_ok(q, stack, "attn")
+    res = {"workload": f"{cfg.layers}-layer stack as the primary one, each layer behind an attention block's seeded "
+                       "bf16 output (post-attention add-norm before the MoE norm)",
+           "us_per_token": med, "us_p10": float(np.percentile(us, 10)), "us_p90": float(np.percentile(us, 90)),
+           "tokens_per_s": 1e6 / med, "achieved_GBs": alg / (med * 1e-6) / 1e9,
+           "mode": "persistent" if stack.mode == q.MOE_STACK_PERSISTENT else "kernels"}
+    print(f"# attn: {med:.1f} us/token", file=sys.stderr, flush=True)
+    del stack
+    torch.cuda.empty_cache()
+    return res
 
 
 def e128_leg(q, steps, warmup, repeats):
@@ -585,6 +614,7 @@ def main():
         print(f"# {name}: {med:.1f} us/token ({res['achieved_GBs']:.0f} GB/s)", file=sys.stderr, flush=True)
     stack, res = primary if primary else (None, results[order[0]])
     layer = None if a.no_layer else layer_leg(q)
+    attn = None if a.no_attn else attn_leg(q, a.steps, a.warmup, a.repeats)
     e128 = None if a.no_e128 else e128_leg(q, a.steps, a.warmup, a.repeats)
     batch = None if a.no_batch else batch_leg(q)
     requant = None if a.no_requant else requant_leg(q)
@@ -625,6 +655,7 @@ def main():
         "variants": results,
         "e128": e128,
         "layer": layer,
+        "attn": attn,
         "batch": batch,
         "requant": requant,
     }

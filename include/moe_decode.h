@@ -159,6 +159,16 @@ int add_rmsnorm3(const uint16_t* residual, const uint16_t* routed, const uint16_
                  uint16_t* out_sum, float* xn, void* xq, void* stream);
 
 /* ------------------------------------------------------------------------
+ * The post-attention add-norm ([P273] Relation to open PRs: add_rmsnorm2_q8,
+ * after the attention block; the 3-input fold precedes the attention):
+ *   u = bf16(residual + attn_out) -> out_sum; xn = u * (1/sqrt(mean(u^2) + eps))
+ *   * norm_w; xq = Q8_1(xn).  The 2-input form of add_rmsnorm3, with the same
+ * layouts, limits and error codes.
+ * ---------------------------------------------------------------------- */
+int add_rmsnorm2_q8(const uint16_t* residual, const uint16_t* attn_out, const float* norm_w, int hidden, int n_tok,
+                    float eps, uint16_t* out_sum, float* xn, void* xq, void* stream);
+
+/* ------------------------------------------------------------------------
  * a2 + a3: router GEMV + in-kernel top-k + routing weights ([P273] Summary
  * item 1: the split-K fp32 GEMV's logits and the top-k select in one kernel,
  * selection by value descending with ties to the lower expert index, the
@@ -303,6 +313,9 @@ typedef struct moe_stack_io {
     uint16_t* resid;         /* [L][H] bf16 out_sum of each layer (the residual after its fold) */
     uint16_t* routed;        /* [L][H] bf16 routed output of each layer */
     uint16_t* shared;        /* [L][H] bf16 shared output of each layer (Fs > 0) */
+    const uint16_t* attn;    /* [L][H] bf16 attention-block output per layer, or NULL: layer l then
+                                folds the previous outputs, u1 = bf16(res + t), and normalises
+                                u2 = bf16(u1 + attn_l), its out_sum (the add_rmsnorm2_q8 step) */
     int trace;               /* persistent mode: 1 = every workgroup stamps its phase events
                                 (moe_stack_trace_offset); 0 = only workgroup 0's phase table */
 } moe_stack_io;

@@ -50,7 +50,7 @@ class LayerWeights(C.Structure):
 
 class StackIO(C.Structure):
     _fields_ = [("input", P), ("output", P), ("ids", P), ("resid", P), ("routed", P), ("shared", P),
-                ("trace", C.c_int)]
+                ("attn", P), ("trace", C.c_int)]
 
 
 class LayerIO(C.Structure):
@@ -69,6 +69,7 @@ _moe_status_string = _sig("moe_status_string", C.c_char_p, C.c_int)
 _moe_workspace_size = _sig("moe_workspace_size", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
 _moe_workspace_init = _sig("moe_workspace_init", C.c_int, P, C.c_size_t, P)
 _add_rmsnorm3 = _sig("add_rmsnorm3", C.c_int, P, P, P, P, C.c_int, C.c_int, C.c_float, P, P, P, P)
+_add_rmsnorm2_q8 = _sig("add_rmsnorm2_q8", C.c_int, P, P, P, C.c_int, C.c_int, C.c_float, P, P, P, P)
 _router_topk = _sig("router_topk", C.c_int, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P, P, C.c_size_t, P)
 _expert_ffn_q4k = _sig("expert_ffn_q4k", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights), P, P, P, P, C.c_int,
                        P, P, P, P, P, C.c_size_t, P)
@@ -97,7 +98,7 @@ EXPORTS = ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", 
            "moe_decode_stack", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
            "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots", "moe_test_quantize_q81", "moe_stream_read", "moe_requant_q4k",
            "moe_batch_workspace_size", "expert_ffn_grouped", "moe_decode_layer_batch", "moe_test_stack_select",
-           "moe_decode_layer_noalloc")
+           "moe_decode_layer_noalloc", "add_rmsnorm2_q8")
 MAX_BATCH = 64
 MAX_GROUP_MIN = 16
 
@@ -171,6 +172,11 @@ def alloc_workspace(desc, n_layers=0, extra=0, device="cuda"):
 def add_rmsnorm3(residual, routed, shared, norm_w, hidden, n_tok, eps, out_sum, xn=None, xq=None, stream=None):
     return _check("add_rmsnorm3", _add_rmsnorm3(ptr(residual), ptr(routed), ptr(shared), ptr(norm_w), hidden, n_tok,
                                                 eps, ptr(out_sum), ptr(xn), ptr(xq), stream_handle(stream)))
+
+
+def add_rmsnorm2_q8(residual, attn_out, norm_w, hidden, n_tok, eps, out_sum, xn=None, xq=None, stream=None):
+    return _check("add_rmsnorm2_q8", _add_rmsnorm2_q8(ptr(residual), ptr(attn_out), ptr(norm_w), hidden, n_tok, eps,
+                                                      ptr(out_sum), ptr(xn), ptr(xq), stream_handle(stream)))
 
 
 def router_topk(xn, w_router, w_shared_gate, n_tok, hidden, n_experts, top_k, logits, ids, weights, shared_gate_out,
@@ -257,11 +263,11 @@ def moe_stack_bind(desc, layers, ws, stream=None):
 
 
 def moe_decode_stack(desc, layers, inp, out, ids_per_layer=None, resid_per_layer=None, mode=MOE_STACK_AUTO, ws=None,
-                     stream=None, layer_array=None, routed_per_layer=None, shared_per_layer=None, trace=0):
+                     stream=None, layer_array=None, routed_per_layer=None, shared_per_layer=None, trace=0, attn=None):
     arr = layer_array if layer_array is not None else _layer_array(layers)
     n = len(arr)
     io = StackIO(ptr(inp), ptr(out), ptr(ids_per_layer), ptr(resid_per_layer), ptr(routed_per_layer),
-                 ptr(shared_per_layer), int(trace))
+                 ptr(shared_per_layer), ptr(attn), int(trace))
     return _check("moe_decode_stack", _moe_decode_stack(C.byref(desc), arr, n, C.byref(io), mode, ptr(ws),
                                                         ws.numel() * ws.element_size(), stream_handle(stream)))
 

@@ -196,6 +196,12 @@ int add_rmsnorm3(const uint16_t* residual, const uint16_t* routed, const uint16_
   return launch_norm(residual, routed, shared, norm_w, hidden, n_tok, eps, out_sum, xn, xq, 1, as_stream(stream));
 }
 
+int add_rmsnorm2_q8(const uint16_t* residual, const uint16_t* attn_out, const float* norm_w, int hidden, int n_tok,
+                    float eps, uint16_t* out_sum, float* xn, void* xq, void* stream) {
+  if (!attn_out) return MOE_ERR_NULL;
+  return add_rmsnorm3(residual, attn_out, nullptr, norm_w, hidden, n_tok, eps, out_sum, xn, xq, stream);
+}
+
 int router_topk(const float* xn, const float* w_router, const float* w_shared_gate, int n_tok, int hidden,
                 int n_experts, int top_k, float* logits, int32_t* ids, float* weights, float* shared_gate_out,
                 void* ws, size_t ws_bytes, void* stream) {
@@ -380,7 +386,7 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
     if ((rc = check_weights(desc, &layers[l]))) return rc;
   if (!aligned(io->input, 2) || !aligned(io->output, 2) || (io->ids && !aligned(io->ids, 4)) ||
       (io->resid && !aligned(io->resid, 2)) || (io->routed && !aligned(io->routed, 2)) ||
-      (io->shared && !aligned(io->shared, 2)))
+      (io->shared && !aligned(io->shared, 2)) || (io->attn && !aligned(io->attn, 8)))
     return MOE_ERR_ALIGN;
   const WsLayout L = ws_layout(desc, n_layers);
   rc = check_ws(ws, ws_bytes, L.total);
@@ -415,8 +421,21 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
     // the norm that reads those runs first on the stream
     uint16_t* routed = io->routed ? io->routed + (size_t)l * H : at<uint16_t>(ws, L.routed);
     uint16_t* shared = has_shared ? (io->shared ? io->shared + (size_t)l * H : at<uint16_t>(ws, L.shared)) : nullptr;
-    rc = launch_norm(res_in, prev_routed, prev_shared, w->norm_w, H, 1, desc->eps, res_out, at<float>(ws, L.xn),
-                     at<void>(ws, L.xq), 1, st);
+    if (io->attn) {
+      // fold the previous outputs (u1), then the post-attention add-norm on (u1, attn_l)
+      const uint16_t* u1 = res_in;
+      if (l > 0) {
+        rc = launch_norm(res_in, prev_routed, prev_shared, nullptr, H, 1, desc->eps, at<uint16_t>(ws, L.u1), nullptr,
+                         nullptr, 0, st);
+        if (rc) return rc;
+        u1 = at<uint16_t>(ws, L.u1);
+      }
+      rc = launch_norm(u1, io->attn + (size_t)l * H, nullptr, w->norm_w, H, 1, desc->eps, res_out, at<float>(ws, L.xn),
+                       at<void>(ws, L.xq), 1, st);
+    } else {
+      rc = launch_norm(res_in, prev_routed, prev_shared, w->norm_w, H, 1, desc->eps, res_out, at<float>(ws, L.xn),
+                       at<void>(ws, L.xq), 1, st);
+    }
     if (rc) return rc;
     rc = launch_router(at<float>(ws, L.xn), w->router_w, has_shared ? w->shared_gate_w : nullptr, 1, H, E, k,
                        at<float>(ws, L.logits), nullptr, ids, at<float>(ws, L.wts), at<float>(ws, L.sg),

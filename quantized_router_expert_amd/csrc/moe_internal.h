@@ -21,7 +21,7 @@ constexpr size_t kLdsBudget = 64 * 1024;
 
 // Byte offsets of the workspace regions (all 256-byte aligned).
 struct WsLayout {
-  size_t counters, xn, xq, logits, ids, wts, sg, h, hs, res, routed, shared, table, bound, stack, total;
+  size_t counters, xn, xq, logits, ids, wts, sg, h, hs, res, routed, shared, u1, table, bound, stack, total;
 };
 WsLayout ws_layout(const moe_layer_desc* d, int n_layers);
 

@@ -699,6 +699,7 @@ WsLayout ws_layout(const moe_layer_desc* d, int n_layers) {
   L.res = o; o += up256(sizeof(uint16_t) * d->hidden);
   L.routed = o; o += up256(sizeof(uint16_t) * d->hidden);
   L.shared = o; o += up256(sizeof(uint16_t) * d->hidden);
+  L.u1 = o; o += up256(sizeof(uint16_t) * d->hidden);
   L.table = o; o += up256(sizeof(moe_layer_weights) * (size_t)(n_layers > 0 ? n_layers : 1));
   L.bound = o; o += up256(sizeof(int) * 4);
   // exchange buffers of the persistent stack (their sizes do not depend on the grid)

@@ -598,6 +598,7 @@ constexpr int stack_geometry_core(int H, int E, int k, int F, int Fs, int down_t
   // not in use (before they are staged, after they are consumed): share it
   if (4L * (xb + 2) <= 2L * g.rgu_half) g.o_xbuf = g.o_rgu;
   else g.o_xbuf = take(4L * (xb + 2));
+  g.o_attn = take(up1k(2L * H));   // an attention-block output (bf16) of the layer
   g.o_sel = take(4L * (g.n_sel + 1));
   g.o_red = take(8L * (kStackThreads / 64));
   g.o_y = take(4L * (k + 1) * g.RD);
@@ -785,6 +786,9 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     const uint32_t ep0 = base + 3u * l, ep1 = ep0 + 1u, ep2 = ep0 + 2u;
     stamp(l, 0);
     bstamp(l, 0);
+    // this layer's attention-block output, if any, streamed into LDS by the
+    // polling waves now, so that the t exchange hides the transfer
+    if (a.attn) stage_async(smem + g.o_attn, a.attn + (long)l * H, (uint32_t)(2 * H), wave, 0, kPollWaves);
     // ================= R1: t of the previous layer, read by every workgroup.
     // Word pair p holds t rows 4p..4p+3 (bf16 pairs); the polling lane adds
     // them to its residual float4 as soon as they are current and takes the
@@ -810,6 +814,24 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     stamp(l, 1);
     bstamp(l, 1);
     if (wave >= kPollWaves) wait_vmem();
+    if (a.attn) {
+      // the post-attention add: u2 = bf16(u1 + attn), once every t word and
+      // the attention output are in
+      if (wave < kPollWaves) wait_vmem();
+      lds_barrier();
+      ss = 0.0;
+      const uint2* av = reinterpret_cast<const uint2*>(smem + g.o_attn);
+      for (int c = tid; c < H / 4; c += kStackThreads) {
+        float4 r = res4[c];
+        const uint2 v = av[c];
+        r.x = bf16_to_f32(f32_to_bf16(r.x + bf16_to_f32((uint16_t)(v.x & 0xffffu))));
+        r.y = bf16_to_f32(f32_to_bf16(r.y + bf16_to_f32((uint16_t)(v.x >> 16))));
+        r.z = bf16_to_f32(f32_to_bf16(r.z + bf16_to_f32((uint16_t)(v.y & 0xffffu))));
+        r.w = bf16_to_f32(f32_to_bf16(r.w + bf16_to_f32((uint16_t)(v.y >> 16))));
+        res4[c] = r;
+        ss += sq4_f64(r);
+      }
+    }
     // the barrier inside also publishes s_fail and the new residual
     ss = block_sum_f64(ss, red);
     if (s_fail) { fail_out(); return; }
@@ -1256,6 +1278,7 @@ int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_
   a.resid_out = io->resid;
   a.routed_out = io->routed;
   a.shared_out = io->shared;
+  a.attn = io->attn;
   a.ws = ws;
   a.L = L;
   a.H = d->hidden;

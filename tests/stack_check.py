@@ -74,7 +74,10 @@ def _fold(res, rt, sh, has_shared):
     return b(_f64(res) + _f64(t))
 
 
-def run_and_check(q, orc, cfg, st, dt, tokens, mode):
+def run_and_check(q, orc, cfg, st, dt, tokens, mode, with_attn=False):
+    """with_attn: every layer runs behind a seeded attention-block output
+    (u1 = the fold of the previous outputs, then the 2-input add-norm of
+    (u1, attn_l)); the oracle's layer then takes (u1, attn_l) as its inputs."""
     L, H, E, k = cfg.layers, cfg.H, cfg.E, cfg.k
     has_sh = cfg.Fs > 0
     Ws = [wl.layer_weights(cfg, l, "cuda", shared_type=st, down_type=dt) for l in range(L)]
@@ -98,8 +101,19 @@ def run_and_check(q, orc, cfg, st, dt, tokens, mode):
         res = torch.zeros(L, H, dtype=torch.bfloat16, device="cuda")
         rts = torch.zeros(L, H, dtype=torch.bfloat16, device="cuda")
         shs = torch.zeros(L, H, dtype=torch.bfloat16, device="cuda") if has_sh else None
+        at_t = None
+        if with_attn:
+            at_t = torch.stack([wl.attention_output(cfg, 0 if t == "zero" else t, l) for l in range(L)])
         q.moe_decode_stack(desc_g, None, inp.cuda(), out, ids, res, mode, ws, layer_array=arr,
-                           routed_per_layer=rts, shared_per_layer=shs)
+                           routed_per_layer=rts, shared_per_layer=shs,
+                           attn=None if at_t is None else at_t.cuda().contiguous())
+        at_u = None if at_t is None else wl.u16(at_t)
+
+        def oracle_layer(l, r_in, rt_in, sh_in, ids=None):
+            if at_u is None:
+                return orc.moe_layer(desc_o, Wn[l], r_in, rt_in, sh_in, ids=ids)
+            u1 = r_in if rt_in is None else _fold(r_in, rt_in, sh_in, has_sh)
+            return orc.moe_layer(desc_o, Wn[l], u1, at_u[l], None, ids=ids)
         torch.cuda.synchronize()
         if persistent:
             assert q.stack_status(desc_g, L, ws) == 0
@@ -111,12 +125,12 @@ def run_and_check(q, orc, cfg, st, dt, tokens, mode):
             r_in = inp_u if l == 0 else g_res[l - 1]
             rt_in = None if l == 0 else g_rt[l - 1]
             sh_in = None if (l == 0 or not has_sh) else g_sh[l - 1]
-            o = orc.moe_layer(desc_o, Wn[l], r_in, rt_in, sh_in)
+            o = oracle_layer(l, r_in, rt_in, sh_in)
             if not np.array_equal(o["ids"], g_ids[l]):
                 d = _router_delta(Wn[l]["router_w"], o["xn"], H, 4.0)
                 assert _near_tie_ok(g_ids[l], o["logits"], d), (t, l, o["ids"], g_ids[l])
                 events["isolated last-bit ties"] += 1
-                o = orc.moe_layer(desc_o, Wn[l], r_in, rt_in, sh_in, ids=g_ids[l])
+                o = oracle_layer(l, r_in, rt_in, sh_in, ids=g_ids[l])
             assert np.array_equal(g_res[l], o["out_sum"]), (t, l, "out_sum")
             gu.assert_bf16_within(g_rt[l], o["routed_exact"], f"token {t} layer {l} routed")
             if has_sh:
@@ -125,12 +139,12 @@ def run_and_check(q, orc, cfg, st, dt, tokens, mode):
         r_o, rt_o, sh_o = inp_u, None, None
         identical = True
         for l in range(L):
-            o = orc.moe_layer(desc_o, Wn[l], r_o, rt_o, sh_o if has_sh else None)
+            o = oracle_layer(l, r_o, rt_o, sh_o if has_sh else None)
             if not np.array_equal(o["ids"], g_ids[l]):
                 d = _router_delta(Wn[l]["router_w"], o["xn"], H, float(H))
                 assert _near_tie_ok(g_ids[l], o["logits"], d), (t, l, o["ids"], g_ids[l])
                 events["chained near ties"] += 1
-                o = orc.moe_layer(desc_o, Wn[l], r_o, rt_o, sh_o if has_sh else None, ids=g_ids[l])
+                o = oracle_layer(l, r_o, rt_o, sh_o if has_sh else None, ids=g_ids[l])
             pairs = [("out_sum", g_res[l], _f64(o["out_sum"])), ("routed", g_rt[l], o["routed_exact"])]
             if has_sh:
                 pairs.append(("shared", g_sh[l], o["shared_exact"]))

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", "moe_decode_stack",
+    for n in ("add_rmsnorm3", "add_rmsnorm2_q8", "router_topk", "expert_ffn_q4k", "moe_decode_layer", "moe_decode_stack",
               "moe_stack_bind", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
               "moe_test_subblock_dots", "moe_test_quantize_q81"):
         assert n in names, n
@@ -84,6 +84,8 @@ def test_add_rmsnorm3_validation(q):
     assert call(eps=float("nan")) == -2
     assert call(res=ODD) == -4
     assert call(xq=FAKE + 2) == -4
+    assert q._add_rmsnorm2_q8(FAKE, None, FAKE, 2048, 1, 1e-6, FAKE, None, None, None) == -1
+    assert q._add_rmsnorm2_q8(FAKE, FAKE, FAKE, 100, 1, 1e-6, FAKE, None, None, None) == -2
 
 
 def test_router_topk_validation(q):

@@ -384,15 +384,19 @@ def test_decode_layer_chained(q, orc, cfg_name, shared_type, down_type, ntok):
 
 
 # ------------------------------------------------------------------ a7: stack, per-layer kernels
-@pytest.mark.parametrize("cfg_name,L,E,st,dt", [("stack", 40, 256, wl.Q4_K, wl.Q4_K), ("stack", 6, 256, wl.Q8_0, wl.Q5_K),
-                                               ("e128", 8, 128, wl.Q4_K, wl.Q4_K)])
-def test_stack_kernels_mode(q, orc, cfg_name, L, E, st, dt):
-    """The stack on the per-layer kernels (four launches per layer and the
-    final fold), with the per-layer stage-isolated and chained checks."""
+@pytest.mark.parametrize("cfg_name,L,E,st,dt,attn", [("stack", 40, 256, wl.Q4_K, wl.Q4_K, False),
+                                                    ("stack", 6, 256, wl.Q8_0, wl.Q5_K, False),
+                                                    ("e128", 8, 128, wl.Q4_K, wl.Q4_K, False),
+                                                    ("stack", 6, 256, wl.Q4_K, wl.Q4_K, True),
+                                                    ("e128", 4, 128, wl.Q4_K, wl.Q4_K, True)])
+def test_stack_kernels_mode(q, orc, cfg_name, L, E, st, dt, attn):
+    """The stack on the per-layer kernels (four launches per layer, one more
+    behind an attention block, and the final fold), with the per-layer
+    stage-isolated and chained checks."""
     import stack_check as sc
     cfg = wl.variant(wl.CONFIGS[cfg_name], layers=L, E=E)
-    gu.banner(f"moe_decode_stack kernels {cfg_name} L {L} shared {st} down {dt}")
-    sc.run_and_check(q, orc, cfg, st, dt, [0, 1], q.MOE_STACK_KERNELS)
+    gu.banner(f"moe_decode_stack kernels {cfg_name} L {L} shared {st} down {dt} attention {attn}")
+    sc.run_and_check(q, orc, cfg, st, dt, [0, 1], q.MOE_STACK_KERNELS, with_attn=attn)
     torch.cuda.empty_cache()
 
 
@@ -441,3 +445,27 @@ def test_layer_deterministic_and_1000_graph_replays(q, orc):
         if rep % 10 == 9:
             q.moe_decode_layer(desc_g, W, io, ws)      # eager work between replays
             torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n_tok", [1, 5])
+def test_add_rmsnorm2_q8(q, orc, n_tok):
+    """The post-attention add-norm: out_sum bit-exact, xn within one fp32 ulp,
+    Q8_1 bytes identical wherever the xn block is identical."""
+    cfg = wl.CONFIGS["layer"]
+    H = cfg.H
+    gu.banner(f"add_rmsnorm2_q8 n_tok {n_tok}")
+    w = wl.rand_uniform((H,), 5, 0.5, 1.5)
+    res = torch.stack([wl.token_inputs(cfg, t)["residual"] for t in range(n_tok)])
+    att = torch.stack([wl.attention_output(cfg, t, 0) for t in range(n_tok)])
+    out = torch.zeros(n_tok, H, dtype=torch.bfloat16, device="cuda")
+    xn = torch.zeros(n_tok, H, dtype=torch.float32, device="cuda")
+    xq = torch.zeros(n_tok, H // 32 * 36, dtype=torch.uint8, device="cuda")
+    q.add_rmsnorm2_q8(res.cuda(), att.cuda(), w.cuda(), H, n_tok, cfg.eps, out, xn, xq)
+    torch.cuda.synchronize()
+    for t in range(n_tok):
+        o_out, o_xn, o_xq = orc.add_rmsnorm(wl.u16(res[t]), wl.u16(att[t]), None, w.numpy(), cfg.eps)
+        assert np.array_equal(gu.u16_host(out)[t], o_out)
+        d = gu.ulp_diff_f32(gu.host(xn)[t], o_xn)
+        assert d.max() <= 1
+        same = (gu.host(xn)[t].reshape(-1, 32) == o_xn.reshape(-1, 32)).all(1)
+        assert np.array_equal(gu.host(xq)[t].reshape(-1, 36)[same], o_xq.reshape(-1, 36)[same])

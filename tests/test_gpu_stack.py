@@ -29,19 +29,30 @@ def _status(q, desc, L, ws):
 
 
 FULL_CASES = [
-    ("stack", wl.Q4_K, wl.Q4_K, [0, 1, 2]),
-    ("stack", wl.Q8_0, wl.Q5_K, [0, 1, 2]),
-    ("e128", wl.Q4_K, wl.Q4_K, [0, 1, "zero"]),
+    ("stack", wl.Q4_K, wl.Q4_K, [0, 1, 2], False),
+    ("stack", wl.Q8_0, wl.Q5_K, [0, 1, 2], False),
+    ("e128", wl.Q4_K, wl.Q4_K, [0, 1, "zero"], False),
+    ("stack", wl.Q4_K, wl.Q4_K, [0, 1], True),
 ]
 
 
-@pytest.mark.parametrize("cfg_name,shared_type,down_type,tokens", FULL_CASES,
-                         ids=["stack40-q4k-q4k", "stack40-q8_0-q5k", "e128-48L"])
-def test_stack_full_depth_vs_oracle(q, orc, cfg_name, shared_type, down_type, tokens):
+@pytest.mark.parametrize("cfg_name,shared_type,down_type,tokens,attn", FULL_CASES,
+                         ids=["stack40-q4k-q4k", "stack40-q8_0-q5k", "e128-48L", "stack40-q4k-q4k-attn"])
+def test_stack_full_depth_vs_oracle(q, orc, cfg_name, shared_type, down_type, tokens, attn):
     cfg = wl.CONFIGS[cfg_name]
-    gu.banner(f"persistent stack {cfg_name} {cfg.layers} layers shared {shared_type} down {down_type} tokens {tokens}")
-    sc.run_and_check(q, orc, cfg, shared_type, down_type, tokens, q.MOE_STACK_PERSISTENT)
+    gu.banner(f"persistent stack {cfg_name} {cfg.layers} layers shared {shared_type} down {down_type} tokens {tokens} "
+              f"attention {attn}")
+    sc.run_and_check(q, orc, cfg, shared_type, down_type, tokens, q.MOE_STACK_PERSISTENT, with_attn=attn)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kw", [dict(layers=4, E=16), dict(layers=3, E=16, Fs=0, three_input=False)])
+def test_stack_behind_attention_small(q, orc, kw):
+    """The attention path on the generic instance (every size at run time),
+    with and without a shared expert."""
+    cfg = wl.variant(wl.CONFIGS["stack"], **kw)
+    gu.banner(f"persistent stack behind attention {kw}")
+    sc.run_and_check(q, orc, cfg, wl.Q4_K, wl.Q4_K, [0, 1], q.MOE_STACK_PERSISTENT, with_attn=True)
 
 
 SMALL_CASES = [
