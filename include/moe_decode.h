@@ -336,6 +336,15 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
  * shape has no persistent stack. */
 size_t moe_stack_status_offset(const moe_layer_desc* desc, int n_layers);
 
+/* Which persistent-kernel instance the current device would run for desc:
+ * 0 = the instance that takes every size at run time, n >= 1 = a compile-time
+ * shape (hidden 2048 with 256 experts top-8, FFN 512, shared 512 = 1; with
+ * 128 experts top-8, FFN 768, no shared expert = 2), each for Q4_K or Q5_K
+ * down and Q4_K or Q8_0 shared matrices; -1 = no persistent kernel for desc
+ * (the per-layer kernels then run).  Queries the device's compute-unit
+ * count; enqueues nothing. */
+int moe_stack_kernel_shape(const moe_layer_desc* desc);
+
 /* Byte offset, in the same workspace, of the persistent stack's phase
  * timestamps: uint64 [64 layers][12 slots], written by the last launch for each
  * of its first 64 layers.  Slots 0..9: the 100 MHz device wall clock seen by

@@ -87,6 +87,7 @@ _expert_ffn_grouped = _sig("expert_ffn_grouped", C.c_int, C.POINTER(LayerDesc), 
 _moe_decode_layer_batch = _sig("moe_decode_layer_batch", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights),
                                C.POINTER(LayerIO), C.c_int, C.c_int, P, C.c_size_t, P)
 _moe_stack_status_offset = _sig("moe_stack_status_offset", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
+_moe_stack_kernel_shape = _sig("moe_stack_kernel_shape", C.c_int, C.POINTER(LayerDesc))
 _moe_stack_trace_offset = _sig("moe_stack_trace_offset", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
 _moe_test_subblock_dots = _sig("moe_test_subblock_dots", C.c_int, P, C.c_int, C.c_int, C.c_int, P, P, P)
 _moe_test_quantize_q81 = _sig("moe_test_quantize_q81", C.c_int, P, C.c_int, P, P)
@@ -98,7 +99,7 @@ EXPORTS = ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", 
            "moe_decode_stack", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
            "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots", "moe_test_quantize_q81", "moe_stream_read", "moe_requant_q4k",
            "moe_batch_workspace_size", "expert_ffn_grouped", "moe_decode_layer_batch", "moe_test_stack_select",
-           "moe_decode_layer_noalloc", "add_rmsnorm2_q8")
+           "moe_decode_layer_noalloc", "add_rmsnorm2_q8", "moe_stack_kernel_shape")
 MAX_BATCH = 64
 MAX_GROUP_MIN = 16
 
@@ -282,6 +283,11 @@ def stack_status(desc, n_layers, ws):
     if off == 0:
         raise MoeError("moe_stack_status_offset", -7)
     return int(ws[off:off + 4].view(torch.int32).item())
+
+
+def moe_stack_kernel_shape(desc):
+    """0 = generic persistent instance, n >= 1 = compile-time shape n, -1 = none."""
+    return _moe_stack_kernel_shape(C.byref(desc))
 
 
 def moe_stack_trace_offset(desc, n_layers):

@@ -464,6 +464,16 @@ size_t moe_stack_status_offset(const moe_layer_desc* desc, int n_layers) {
   return g.w_ctrl + 4 * kErrWord;
 }
 
+int moe_stack_kernel_shape(const moe_layer_desc* desc) {
+  if (check_desc(desc) != MOE_OK || !desc->norm) return -1;
+  int G = 0;
+  if (device_cu_count(&G) != MOE_OK) return -1;
+  StackGeom g;
+  if (G < 8 || G % 8 || stack_geometry(desc, G, &g) != MOE_OK || g.lds > kStackMaxLds) return -1;
+  int shape = -1;
+  return stack_kernel_for(desc, g, &shape) ? shape : -1;
+}
+
 size_t moe_stack_trace_offset(const moe_layer_desc* desc, int n_layers) {
   if (check_desc(desc) != MOE_OK || n_layers <= 0 || n_layers > MOE_MAX_LAYERS) return 0;
   const WsLayout L = ws_layout(desc, n_layers);

@@ -67,6 +67,9 @@ void stack_ws_layout(StackGeom* g, size_t base);
 int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_dev, const uint32_t* bound,
                  uint64_t table_hash, const moe_stack_io* io, uint8_t* ws, const StackGeom& g, hipStream_t st);
 int device_cu_count(int* n);
+// the persistent kernel instance for a description and its geometry; *shape
+// (if given) gets the compile-time shape index (0 = sizes at run time)
+const void* stack_kernel_for(const moe_layer_desc* d, const StackGeom& g, int* shape);
 int launch_test_stack_select(const float* logits, int n_sets, int E, int k, int with_gate, int32_t* ids, float* wts,
                              float* gate, hipStream_t st);
 

@@ -1264,6 +1264,45 @@ uint64_t layer_table_hash(const moe_layer_weights* layers, int n) {
   return h;
 }
 
+// The kernel instances: one per (down type, shared type) with every size from
+// the arguments, and the compile-time shapes of kFixShapes with each weight
+// variant the workloads use -- shape 1 (hidden 2048, 256 experts, top-8, FFN
+// 512, shared 512) with Q4_K or Q5_K down and Q4_K or Q8_0 shared, shape 2
+// (hidden 2048, 128 experts, top-8, FFN 768, no shared expert) with Q4_K or
+// Q5_K down.  A description takes a compile-time instance when its sizes and
+// its whole geometry are that instance's.
+struct StackInst {
+  int S, DT, ST;
+  const void* fn;
+  const StackGeom* geom;
+};
+#define MOE_STACK_INST(S, DT, ST) {S, DT, ST, (const void*)k_stack<DT, ST, S>, &kFixGeom<DT, ST, S>}
+static const StackInst kStackInst[] = {
+    MOE_STACK_INST(1, MOE_TYPE_Q4_K, MOE_TYPE_Q4_K), MOE_STACK_INST(1, MOE_TYPE_Q5_K, MOE_TYPE_Q8_0),
+    MOE_STACK_INST(1, MOE_TYPE_Q4_K, MOE_TYPE_Q8_0), MOE_STACK_INST(1, MOE_TYPE_Q5_K, MOE_TYPE_Q4_K),
+    MOE_STACK_INST(2, MOE_TYPE_Q4_K, MOE_TYPE_Q4_K), MOE_STACK_INST(2, MOE_TYPE_Q5_K, MOE_TYPE_Q4_K),
+    MOE_STACK_INST(0, MOE_TYPE_Q4_K, MOE_TYPE_Q4_K), MOE_STACK_INST(0, MOE_TYPE_Q5_K, MOE_TYPE_Q8_0),
+    MOE_STACK_INST(0, MOE_TYPE_Q4_K, MOE_TYPE_Q8_0), MOE_STACK_INST(0, MOE_TYPE_Q5_K, MOE_TYPE_Q4_K),
+};
+#undef MOE_STACK_INST
+
+const void* stack_kernel_for(const moe_layer_desc* d, const StackGeom& g, int* shape) {
+  const int dt = d->down_type;
+  const int st = d->shared_ffn > 0 ? d->shared_type : MOE_TYPE_Q4_K;
+  for (const StackInst& in : kStackInst) {
+    if (in.DT != dt || in.ST != st) continue;
+    if (in.S != 0) {
+      const FixShape& f = kFixShapes[in.S];
+      const bool sizes = d->hidden == f.H && d->n_experts == f.E && d->top_k == f.k && d->ffn == f.F &&
+                         d->shared_ffn == f.Fs;
+      if (!sizes || memcmp(&g, in.geom, offsetof(StackGeom, w_ctrl)) != 0) continue;
+    }
+    if (shape) *shape = in.S;
+    return in.fn;
+  }
+  return nullptr;
+}
+
 int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_dev, const uint32_t* bound,
                  uint64_t table_hash, const moe_stack_io* io, uint8_t* ws, const StackGeom& g, hipStream_t st) {
   static_assert(sizeof(moe_layer_weights) % 8 == 0, "the table hashes in 8-byte words");
@@ -1288,30 +1327,8 @@ int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_
   a.Fs = d->shared_ffn;
   a.eps = d->eps;
   a.trace_blocks = io->trace ? 1 : 0;
-  const void* fn;
-  const int dt = d->down_type;
-  const int stt = d->shared_ffn > 0 ? d->shared_type : MOE_TYPE_Q4_K;
-  // a compile-time shape when every size and the whole geometry match it
-  auto is_shape = [&](int S) {
-    const FixShape& f = kFixShapes[S];
-    return d->hidden == f.H && d->n_experts == f.E && d->top_k == f.k && d->ffn == f.F && d->shared_ffn == f.Fs;
-  };
-  const bool fix44 = is_shape(1) && dt == MOE_TYPE_Q4_K && stt == MOE_TYPE_Q4_K &&
-                     memcmp(&g, &kFixGeom<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, 1>, offsetof(StackGeom, w_ctrl)) == 0;
-  const bool fix58 = is_shape(1) && dt == MOE_TYPE_Q5_K && stt == MOE_TYPE_Q8_0 &&
-                     memcmp(&g, &kFixGeom<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, 1>, offsetof(StackGeom, w_ctrl)) == 0;
-  const bool fix2 = is_shape(2) && dt == MOE_TYPE_Q4_K && stt == MOE_TYPE_Q4_K &&
-                    memcmp(&g, &kFixGeom<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, 2>, offsetof(StackGeom, w_ctrl)) == 0;
-  if (dt == MOE_TYPE_Q5_K)
-    fn = (stt == MOE_TYPE_Q8_0) ? (fix58 ? (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, 1>
-                                         : (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0, 0>)
-                                : (const void*)k_stack<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K, 0>;
-  else if (stt == MOE_TYPE_Q8_0)
-    fn = (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0, 0>;
-  else
-    fn = fix44 ? (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, 1>
-               : fix2 ? (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, 2>
-                      : (const void*)k_stack<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, 0>;
+  const void* fn = stack_kernel_for(d, g, nullptr);
+  if (!fn) return MOE_ERR_UNSUPPORTED;
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds) != hipSuccess) return MOE_ERR_HIP;
   void* args[] = {&a};
   if (hipLaunchCooperativeKernel(fn, dim3(g.G), dim3(kStackThreads), args, g.lds, st) != hipSuccess) {

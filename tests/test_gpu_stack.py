@@ -33,11 +33,15 @@ FULL_CASES = [
     ("stack", wl.Q8_0, wl.Q5_K, [0, 1, 2], False),
     ("e128", wl.Q4_K, wl.Q4_K, [0, 1, "zero"], False),
     ("stack", wl.Q4_K, wl.Q4_K, [0, 1], True),
+    ("stack", wl.Q8_0, wl.Q4_K, [0, 1], False),
+    ("stack", wl.Q4_K, wl.Q5_K, [0, 1], False),
+    ("e128", wl.Q4_K, wl.Q5_K, [0, "zero"], False),
 ]
 
 
 @pytest.mark.parametrize("cfg_name,shared_type,down_type,tokens,attn", FULL_CASES,
-                         ids=["stack40-q4k-q4k", "stack40-q8_0-q5k", "e128-48L", "stack40-q4k-q4k-attn"])
+                         ids=["stack40-q4k-q4k", "stack40-q8_0-q5k", "e128-48L", "stack40-q4k-q4k-attn",
+                              "stack40-q8_0-q4k", "stack40-q4k-q5k", "e128-48L-q5k"])
 def test_stack_full_depth_vs_oracle(q, orc, cfg_name, shared_type, down_type, tokens, attn):
     cfg = wl.CONFIGS[cfg_name]
     gu.banner(f"persistent stack {cfg_name} {cfg.layers} layers shared {shared_type} down {down_type} tokens {tokens} "
@@ -53,6 +57,20 @@ def test_stack_behind_attention_small(q, orc, kw):
     cfg = wl.variant(wl.CONFIGS["stack"], **kw)
     gu.banner(f"persistent stack behind attention {kw}")
     sc.run_and_check(q, orc, cfg, wl.Q4_K, wl.Q4_K, [0, 1], q.MOE_STACK_PERSISTENT, with_attn=True)
+
+
+def test_every_benchmark_shape_has_a_compile_time_instance(q):
+    """The 40-layer shape in each of its four weight variants and the
+    128-expert shape in both of its down variants run compile-time
+    instances; a shape outside the table takes the run-time one."""
+    gu.banner("persistent instances of the benchmark shapes")
+    for st in (wl.Q4_K, wl.Q8_0):
+        for dt in (wl.Q4_K, wl.Q5_K):
+            assert q.moe_stack_kernel_shape(q.make_desc(2048, 256, 8, 512, 512, down_type=dt, shared_type=st)) == 1
+    for dt in (wl.Q4_K, wl.Q5_K):
+        assert q.moe_stack_kernel_shape(q.make_desc(2048, 128, 8, 768, 0, down_type=dt)) == 2
+    assert q.moe_stack_kernel_shape(q.make_desc(2048, 16, 8, 512, 512)) == 0
+    assert q.moe_stack_kernel_shape(q.make_desc(512, 32, 4, 128, 128, norm=0)) == -1
 
 
 SMALL_CASES = [
