@@ -113,7 +113,8 @@ typedef struct moe_layer_io {
     const uint16_t* routed_in;  /* [H] bf16 previous layer's routed output, or NULL (= 0) */
     const uint16_t* shared_in;  /* [H] bf16 previous layer's shared output, or NULL (2-input form) */
     const float* x;             /* [H] fp32 input (norm = 0) */
-    uint16_t* out_sum;          /* [H] bf16 new residual = bf16(residual + bf16(routed_in + shared_in)) (norm = 1) */
+    uint16_t* out_sum;          /* [H] bf16 new residual = bf16(residual + bf16(routed_in + shared_in)) (norm = 1);
+                                   may be the residual buffer itself (updated in place) */
     uint16_t* routed_out;       /* [H] bf16 */
     uint16_t* shared_out;       /* [H] bf16 (Fs > 0) */
     /* optional intermediates, NULL = not written */

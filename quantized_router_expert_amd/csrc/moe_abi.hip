@@ -93,34 +93,37 @@ int check_layer_call(const moe_layer_desc* desc, const moe_layer_weights* w, con
   return MOE_OK;
 }
 
-// a1..a6 for one token on the per-layer kernels; ws holds at least the
-// layer's intermediates (ws_layout(desc, 0) up to its pointer table) and its
-// router counters are zero.
+// a1..a6 for one token in one launch; ws holds at least the layer's
+// intermediates (ws_layout(desc, 0) up to its pointer table) and its counters
+// are zero.
 int decode_layer(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_layer_io* io, void* ws,
                  hipStream_t st) {
   int rc;
   const WsLayout L = ws_layout(desc, 0);
   const int H = desc->hidden, E = desc->n_experts, k = desc->top_k;
-  float* xn = io->xn ? io->xn : at<float>(ws, L.xn);
   void* xq = io->xq ? io->xq : at<void>(ws, L.xq);
   int32_t* ids = io->ids ? io->ids : at<int32_t>(ws, L.ids);
   float* wts = io->weights ? io->weights : at<float>(ws, L.wts);
   float* sg = io->shared_gate ? io->shared_gate : at<float>(ws, L.sg);
   float* h = io->h ? io->h : at<float>(ws, L.h);
   float* hs = io->hs ? io->hs : at<float>(ws, L.hs);
+  const float* wsg = desc->shared_ffn > 0 ? w->shared_gate_w : nullptr;
   if (desc->norm) {
-    rc = launch_norm(io->residual, io->routed_in, io->shared_in, w->norm_w, H, 1, desc->eps, io->out_sum, xn, xq, 1, st);
+    rc = launch_norm_router(io->residual, io->routed_in, io->shared_in, w->norm_w, w->router_w, wsg, H, E, k,
+                            desc->eps, io->out_sum, io->xn, xq, at<float>(ws, L.logits), io->logits, ids, wts, sg,
+                            at<unsigned>(ws, L.counters), st);
+    if (rc) return rc;
   } else {
     if (io->xn) {
-      if (hipMemcpyAsync(xn, io->x, sizeof(float) * H, hipMemcpyDeviceToDevice, st) != hipSuccess) return MOE_ERR_HIP;
+      if (hipMemcpyAsync(io->xn, io->x, sizeof(float) * H, hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return MOE_ERR_HIP;
     }
-    xn = io->xn ? io->xn : const_cast<float*>(io->x);
     rc = launch_quantize(io->x, H, xq, st);
+    if (rc) return rc;
+    rc = launch_router(io->x, w->router_w, wsg, 1, H, E, k, at<float>(ws, L.logits), io->logits, ids, wts, sg,
+                       at<unsigned>(ws, L.counters), st);
+    if (rc) return rc;
   }
-  if (rc) return rc;
-  rc = launch_router(xn, w->router_w, desc->shared_ffn > 0 ? w->shared_gate_w : nullptr, 1, H, E, k,
-                     at<float>(ws, L.logits), io->logits, ids, wts, sg, at<unsigned>(ws, L.counters), st);
-  if (rc) return rc;
   rc = launch_gate_up(desc, w, xq, ids, h, hs, st);
   if (rc) return rc;
   return launch_down(desc, w, h, hs, ids, wts, sg, io->routed_out, io->shared_out, st);
@@ -421,25 +424,24 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
     // the norm that reads those runs first on the stream
     uint16_t* routed = io->routed ? io->routed + (size_t)l * H : at<uint16_t>(ws, L.routed);
     uint16_t* shared = has_shared ? (io->shared ? io->shared + (size_t)l * H : at<uint16_t>(ws, L.shared)) : nullptr;
+    // the add-norm (after an attention block: the fold of the previous outputs
+    // into u1, then the add-norm on (u1, attn_l)) and the router in one launch
+    const uint16_t* nin = res_in;
+    const uint16_t* n1 = prev_routed;
+    const uint16_t* n2 = prev_shared;
     if (io->attn) {
-      // fold the previous outputs (u1), then the post-attention add-norm on (u1, attn_l)
-      const uint16_t* u1 = res_in;
       if (l > 0) {
         rc = launch_norm(res_in, prev_routed, prev_shared, nullptr, H, 1, desc->eps, at<uint16_t>(ws, L.u1), nullptr,
                          nullptr, 0, st);
         if (rc) return rc;
-        u1 = at<uint16_t>(ws, L.u1);
+        nin = at<uint16_t>(ws, L.u1);
       }
-      rc = launch_norm(u1, io->attn + (size_t)l * H, nullptr, w->norm_w, H, 1, desc->eps, res_out, at<float>(ws, L.xn),
-                       at<void>(ws, L.xq), 1, st);
-    } else {
-      rc = launch_norm(res_in, prev_routed, prev_shared, w->norm_w, H, 1, desc->eps, res_out, at<float>(ws, L.xn),
-                       at<void>(ws, L.xq), 1, st);
+      n1 = io->attn + (size_t)l * H;
+      n2 = nullptr;
     }
-    if (rc) return rc;
-    rc = launch_router(at<float>(ws, L.xn), w->router_w, has_shared ? w->shared_gate_w : nullptr, 1, H, E, k,
-                       at<float>(ws, L.logits), nullptr, ids, at<float>(ws, L.wts), at<float>(ws, L.sg),
-                       at<unsigned>(ws, L.counters), st);
+    rc = launch_norm_router(nin, n1, n2, w->norm_w, w->router_w, has_shared ? w->shared_gate_w : nullptr, H, E, k,
+                            desc->eps, res_out, nullptr, at<void>(ws, L.xq), at<float>(ws, L.logits), nullptr, ids,
+                            at<float>(ws, L.wts), at<float>(ws, L.sg), at<unsigned>(ws, L.counters), st);
     if (rc) return rc;
     rc = launch_gate_up(desc, w, at<void>(ws, L.xq), ids, at<float>(ws, L.h), at<float>(ws, L.hs), st);
     if (rc) return rc;

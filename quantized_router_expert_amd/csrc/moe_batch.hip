@@ -466,34 +466,10 @@ __device__ __forceinline__ void copy_to_lds(uint8_t* dst, const uint8_t* src, lo
   for (long i = threadIdx.x; i < (bytes >> 4); i += kBThreads) d4[i] = s4[i];
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// `bytes` from global src straight into LDS dst, 16 bytes per lane and 1 KiB
-// per wave instruction (buffer_load ... lds), the waves of the block taking
-// the KiB chunks in turn.  The loads hold no registers, so every chunk is in
-// flight at once; the loads are issued from inline asm, untracked by the
-// compiler, and the block waits for them with s_waitcnt vmcnt(0) and a
-// barrier.  The source descriptor is range-checked: lanes past `bytes` read
-// 0 and write it, so dst needs room up to the next KiB.
+// `bytes` from global src straight into LDS dst by all waves of the block (the
+// block waits with wait_vmem() and a barrier; dst needs room up to the next KiB)
 __device__ __forceinline__ void dma_to_lds(uint8_t* dst, const uint8_t* src, uint32_t bytes) {
-  if (bytes == 0) return;
-  const unsigned long long ad = (unsigned long long)src;
-  typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
-  v4u_t r;
-  r.x = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ad);
-  r.y = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(ad >> 32) & 0xffffu));
-  r.z = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
-  r.w = 0x00020000u;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)dst;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t nchunks = (bytes + 1023) >> 10;
-  for (uint32_t c = wave; c < nchunks; c += kBThreads / 64) {
-    const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (c << 10)));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(m), "v"((c << 10) + lane * 16), "s"(r)
-                 : "memory", "m0");
-  }
+  stage_async(dst, src, bytes, threadIdx.x >> 6, 0, kBThreads / 64);
 }
 
 // Q8_1 activations of `nt` tokens unpacked into LDS (codes [nt][K], d/s [nt][K/32])

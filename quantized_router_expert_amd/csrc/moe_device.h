@@ -33,6 +33,54 @@ constexpr int kQ5KBytes = 176;
 constexpr int kQ80Bytes = 34;
 constexpr int kQ81Bytes = 36;
 
+// ---------------------------------------------------------------- global -> LDS streaming
+typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Wait for every vector-memory load the wave has issued (the DMA loads below
+// are invisible to the compiler's own bookkeeping, so their consumers call this).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS (buffer_load ... lds):
+// the wave's 64 lanes fill the 1 KiB at LDS address `lds` (M0) from byte
+// offset `off` + 16 * lane of the buffer described by `rsrc`.  Issued from
+// inline asm so the compiler does not track it: it would otherwise wait for
+// every such load before any LDS read it cannot prove disjoint, which stalls
+// the waves that compute while their next rows stream in.  The consumer waits
+// explicitly (wait_vmem() in the issuing waves, then a barrier).
+__device__ __forceinline__ void lds_dma_1k(v4u rsrc, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(off), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Buffer descriptor with hardware range checking: loads past `bytes` read 0.
+__device__ __forceinline__ v4u raw_rsrc(const void* p, uint32_t bytes) {
+  const unsigned long long a = (unsigned long long)p;
+  v4u r;
+  r.x = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r.z = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000u;
+  return r;
+}
+
+// Stream `bytes` from src into LDS dst (1 KiB per wave instruction); waves
+// [w0, w0+nw) take chunks round-robin.  The loads hold no registers, so every
+// chunk is in flight at once.  dst must have room for the byte count rounded
+// up to 1 KiB: lanes past the source end read 0 (range-checked descriptor) and
+// write that 0 into the padding.
+__device__ __forceinline__ void stage_async(uint8_t* dst, const void* src, uint32_t bytes, int wave, int w0, int nw) {
+  if (wave < w0 || wave >= w0 + nw || bytes == 0) return;
+  const v4u r = raw_rsrc(src, bytes);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)dst;
+  const int lane = threadIdx.x & 63;
+  const uint32_t nchunks = (bytes + 1023) >> 10;
+  for (uint32_t c = wave - w0; c < nchunks; c += nw)
+    lds_dma_1k(r, (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (c << 10))), (c << 10) + lane * 16);
+}
+
 __host__ __device__ constexpr inline int block_bytes(int type) {
   return type == MOE_TYPE_Q4_K ? kQ4KBytes : type == MOE_TYPE_Q5_K ? kQ5KBytes : type == MOE_TYPE_Q8_0 ? kQ80Bytes : kQ81Bytes;
 }

@@ -33,6 +33,12 @@ int launch_norm(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, con
 int launch_quantize(const float* x, int n, void* xq, hipStream_t st);
 int launch_router(const float* xn, const float* W, const float* wsg, int n_tok, int H, int E, int k, float* logits,
                   float* user_logits, int32_t* ids, float* wts, float* sg, unsigned* counters, hipStream_t st);
+// a1 + a2 + a3 of one token in one launch (the residual fold and norm, the
+// router rows, the top-k); out_sum may alias res.
+int launch_norm_router(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, const float* norm_w, const float* W,
+                       const float* wsg, int H, int E, int k, float eps, uint16_t* out_sum, float* xn, void* xq,
+                       float* logits, float* user_logits, int32_t* ids, float* wts, float* sg, unsigned* counters,
+                       hipStream_t st);
 int launch_gate_up(const moe_layer_desc* d, const moe_layer_weights* w, const void* xq, const int32_t* ids, float* h,
                    float* hs, hipStream_t st);
 int launch_down(const moe_layer_desc* d, const moe_layer_weights* w, const float* h, const float* hs, const int32_t* ids,

@@ -17,6 +17,10 @@
 
 namespace moe {
 
+// Areas that the DMA into LDS fills start at a KiB boundary of their own: it
+// writes whole KiB chunks.
+__host__ __device__ constexpr inline long kib_up(long bytes) { return (bytes + 1023) & ~1023L; }
+
 // =====================================================================
 // a1: residual add folded into RMSNorm, Q8_1 of the normed vector
 // =====================================================================
@@ -34,13 +38,40 @@ __device__ __forceinline__ void unpack_bf16x8(uint4 v, float f[8]) {
     f[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
   }
 }
-__device__ void norm_token_block(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, const float* w,
-                                 int H, float eps, uint16_t* out_sum, float* xn_out, uint8_t* xq_out,
-                                 float* u_lds, double* red_lds, int do_norm) {
+// Q8_1 of the H values at xn_lds (LDS) into xq_out, four lanes per 32-block.
+__device__ void q81_from_lds(const float* xn_lds, int H, uint8_t* xq_out) {
+  // block j: lanes 4j .. 4j+3, values 8p .. 8p+7 each
+  for (int i0 = threadIdx.x; i0 < H / 8; i0 += kNormThreads) {
+    const int j = i0 >> 2, p = i0 & 3;
+    const float4 a = reinterpret_cast<const float4*>(xn_lds + 32 * j + 8 * p)[0];
+    const float4 b = reinterpret_cast<const float4*>(xn_lds + 32 * j + 8 * p)[1];
+    float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float amax = 0.0f;
+    bool nan = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      amax = fmaxf(amax, fabsf(x[i]));
+      nan |= (x[i] != x[i]);
+    }
+    amax = fmaxf(amax, __uint_as_float(partner_dpp<0>(__float_as_uint(amax))));
+    amax = fmaxf(amax, __uint_as_float(partner_dpp<1>(__float_as_uint(amax))));
+    const bool slow = nan || !(amax == 0.0f || (amax >= 0x1p-100f && amax <= 0x1p100f));
+    uint32_t q[2];
+    uint32_t ds;
+    if (__builtin_expect(__any(slow), 0)) ds = q81_group<4, true>(x, amax, q);
+    else ds = q81_group<4, false>(x, amax, q);
+    uint8_t* ob = xq_out + (long)j * kQ81Bytes;
+    reinterpret_cast<uint32_t*>(ob + 4 + 8 * p)[0] = q[0];
+    reinterpret_cast<uint32_t*>(ob + 4 + 8 * p)[1] = q[1];
+    if (p == 0) *reinterpret_cast<uint32_t*>(ob) = ds;
+  }
+}
+
+// The fold: u = bf16(res + t) into u_lds (and out_sum); returns this thread's
+// part of sum(u^2).  vec: 8 elements per thread with 16-byte accesses.
+__device__ double norm_fold(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, int H, uint16_t* out_sum,
+                            float* u_lds, bool vec) {
   const int tid = threadIdx.x;
-  const bool vec = ((reinterpret_cast<uintptr_t>(res) | reinterpret_cast<uintptr_t>(rt) |
-                     reinterpret_cast<uintptr_t>(sh) | reinterpret_cast<uintptr_t>(out_sum) |
-                     reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(xn_out)) & 15) == 0;
   double ss = 0.0;
   if (!vec) {
     for (int i = tid; i < H; i += kNormThreads) {
@@ -53,8 +84,9 @@ __device__ void norm_token_block(const uint16_t* res, const uint16_t* rt, const 
       u_lds[i] = u;
       ss += (double)u * (double)u;
     }
+    return ss;
   }
-  for (int c = tid; vec && c < H / 8; c += kNormThreads) {
+  for (int c = tid; c < H / 8; c += kNormThreads) {
     float r8[8], t8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     unpack_bf16x8(reinterpret_cast<const uint4*>(res)[c], r8);
     if (rt) {
@@ -80,7 +112,15 @@ __device__ void norm_token_block(const uint16_t* res, const uint16_t* rt, const 
     reinterpret_cast<float4*>(u_lds)[2 * c] = make_float4(u8[0], u8[1], u8[2], u8[3]);
     reinterpret_cast<float4*>(u_lds)[2 * c + 1] = make_float4(u8[4], u8[5], u8[6], u8[7]);
   }
-  if (!do_norm) return;
+  return ss;
+}
+
+// The norm: sum(u^2) over the workgroup in fp64 (waves in order), r =
+// 1/sqrt(mean + eps), xn = f32((u*r)*w) into xl (and xn_out).  w may be in
+// LDS or global memory; vec: 4 elements per thread with 16-byte accesses.
+__device__ void norm_scale(double ss, const float* w, int H, float eps, float* xn_out, const float* u_lds, float* xl,
+                           double* red_lds, bool vec) {
+  const int tid = threadIdx.x;
   ss = wave_sum_f64(ss);
   if ((tid & 63) == 0) red_lds[tid >> 6] = ss;
   __syncthreads();
@@ -92,10 +132,11 @@ __device__ void norm_token_block(const uint16_t* res, const uint16_t* rt, const 
     for (int i = tid; i < H; i += kNormThreads) {
       const float x = (float)(((double)u_lds[i] * r) * (double)w[i]);
       if (xn_out) xn_out[i] = x;
-      u_lds[i] = x;
+      xl[i] = x;
     }
+    return;
   }
-  for (int c = tid; vec && c < H / 4; c += kNormThreads) {
+  for (int c = tid; c < H / 4; c += kNormThreads) {
     const float4 u = reinterpret_cast<const float4*>(u_lds)[c];
     const float4 wv = reinterpret_cast<const float4*>(w)[c];
     float4 x;
@@ -104,35 +145,25 @@ __device__ void norm_token_block(const uint16_t* res, const uint16_t* rt, const 
     x.z = (float)(((double)u.z * r) * (double)wv.z);
     x.w = (float)(((double)u.w * r) * (double)wv.w);
     if (xn_out) reinterpret_cast<float4*>(xn_out)[c] = x;
-    reinterpret_cast<float4*>(u_lds)[c] = x;   // xn replaces u (each float4 is read and written by one thread)
+    reinterpret_cast<float4*>(xl)[c] = x;   // (each float4 is read and written by one thread)
   }
+}
+
+// Fold + norm + Q8_1 of one token by one workgroup.  xn goes to xn_lds when
+// given (u stays in u_lds), else it replaces u in u_lds.
+__device__ void norm_token_block(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, const float* w,
+                                 int H, float eps, uint16_t* out_sum, float* xn_out, uint8_t* xq_out,
+                                 float* u_lds, double* red_lds, int do_norm, float* xn_lds = nullptr) {
+  const bool vec = ((reinterpret_cast<uintptr_t>(res) | reinterpret_cast<uintptr_t>(rt) |
+                     reinterpret_cast<uintptr_t>(sh) | reinterpret_cast<uintptr_t>(out_sum) |
+                     reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(xn_out)) & 15) == 0;
+  const double ss = norm_fold(res, rt, sh, H, out_sum, u_lds, vec);
+  if (!do_norm) return;
+  float* const xl = xn_lds ? xn_lds : u_lds;
+  norm_scale(ss, w, H, eps, xn_out, u_lds, xl, red_lds, vec);
   if (!xq_out) return;
   __syncthreads();
-  // block j: lanes 4j .. 4j+3, values 8p .. 8p+7 each
-  for (int i0 = tid; i0 < H / 8; i0 += kNormThreads) {
-    const int j = i0 >> 2, p = i0 & 3;
-    const float4 a = reinterpret_cast<const float4*>(u_lds + 32 * j + 8 * p)[0];
-    const float4 b = reinterpret_cast<const float4*>(u_lds + 32 * j + 8 * p)[1];
-    float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    float amax = 0.0f;
-    bool nan = false;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      amax = fmaxf(amax, fabsf(x[i]));
-      nan |= (x[i] != x[i]);
-    }
-    amax = fmaxf(amax, __uint_as_float(partner_dpp<0>(__float_as_uint(amax))));
-    amax = fmaxf(amax, __uint_as_float(partner_dpp<1>(__float_as_uint(amax))));
-    const bool slow = nan || !(amax == 0.0f || (amax >= 0x1p-100f && amax <= 0x1p100f));
-    uint32_t q[2];
-    uint32_t ds;
-    if (__builtin_expect(__any(slow), 0)) ds = q81_group<4, true>(x, amax, q);
-    else ds = q81_group<4, false>(x, amax, q);
-    uint8_t* ob = xq_out + (long)j * kQ81Bytes;
-    reinterpret_cast<uint32_t*>(ob + 4 + 8 * p)[0] = q[0];
-    reinterpret_cast<uint32_t*>(ob + 4 + 8 * p)[1] = q[1];
-    if (p == 0) *reinterpret_cast<uint32_t*>(ob) = ds;
-  }
+  q81_from_lds(xl, H, xq_out);
 }
 
 __global__ __launch_bounds__(kNormThreads) void k_add_rmsnorm(const uint16_t* res, const uint16_t* rt, const uint16_t* sh,
@@ -210,6 +241,22 @@ __device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* id
   else if (E <= 256) wave_topk_softmax_n<4>(logits, E, k, ids_out, w_out);
   else if (E <= 512) wave_topk_softmax_n<8>(logits, E, k, ids_out, w_out);
   else wave_topk_softmax_n<16>(logits, E, k, ids_out, w_out);
+}
+
+// The workgroup's arrival on a grid-completion counter group at c0 (called by
+// one thread after the workgroup's results are stored): true for the last of
+// the gridDim.x workgroups to arrive.  The counters wrap back to zero.
+__device__ __forceinline__ bool arrive_last(unsigned* c0, int cstride, int nsub) {
+  if (nsub > 0) {
+    const unsigned j = blockIdx.x % (unsigned)nsub;
+    const unsigned nj = (gridDim.x - j + nsub - 1) / (unsigned)nsub;   // workgroups on sub-counter j
+    const unsigned o1 = __builtin_amdgcn_atomic_inc32(c0 + (1 + j) * cstride, nj - 1, __ATOMIC_RELAXED, "agent");
+    if (o1 != nj - 1) return false;
+    const unsigned nz = min((unsigned)nsub, gridDim.x);   // sub-counters in use
+    return __builtin_amdgcn_atomic_inc32(c0, nz - 1, __ATOMIC_RELAXED, "agent") == nz - 1;
+  }
+  const unsigned old = __builtin_amdgcn_atomic_inc32(c0, gridDim.x - 1, __ATOMIC_RELAXED, "agent");
+  return old == gridDim.x - 1;
 }
 
 // grid (ceil(nrows / kRouterRpb), ceil(n_tok / kRouterTok)): workgroup x
@@ -294,23 +341,7 @@ __global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn,
   }
   __shared__ int is_last;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned* const c0 = counters + (long)tg * (nsub + 1) * cstride;
-    if (nsub > 0) {
-      const unsigned j = blockIdx.x % (unsigned)nsub;
-      const unsigned nj = (gridDim.x - j + nsub - 1) / (unsigned)nsub;   // workgroups on sub-counter j
-      const unsigned o1 = __builtin_amdgcn_atomic_inc32(c0 + (1 + j) * cstride, nj - 1, __ATOMIC_RELAXED, "agent");
-      int last = 0;
-      if (o1 == nj - 1) {
-        const unsigned nz = min((unsigned)nsub, gridDim.x);   // sub-counters in use
-        last = __builtin_amdgcn_atomic_inc32(c0, nz - 1, __ATOMIC_RELAXED, "agent") == nz - 1;
-      }
-      is_last = last;
-    } else {
-      const unsigned old = __builtin_amdgcn_atomic_inc32(c0, gridDim.x - 1, __ATOMIC_RELAXED, "agent");
-      is_last = (old == gridDim.x - 1);
-    }
-  }
+  if (threadIdx.x == 0) is_last = arrive_last(counters + (long)tg * (nsub + 1) * cstride, cstride, nsub);
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -324,6 +355,95 @@ __global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn,
       const int t = i / E, e = i - t * E;
       user_logits[(long)(t0 + t) * E + e] = logits[(long)(t0 + t) * logits_stride + e];
     }
+}
+
+// a1 + a2 + a3 for one token in one launch ([P273] Summary items 1 and 2: the
+// residual fold and norm ahead of the router's GEMV, the top-k in the same
+// kernel).  Workgroup x (kNormThreads threads) owns router row x (the
+// shared-gate row when x == E): it streams the row and the norm weight into
+// LDS while it folds the token itself, normalises it (the same element
+// mapping and fp64 reduction order as k_add_rmsnorm, so the same u, r and xn)
+// and takes the row's fp64 dot with xn.  Workgroup 0 also writes xn and xq;
+// the last workgroup to arrive selects and writes out_sum, after every
+// workgroup has read the residual inputs, so out_sum may be one of them.
+struct NormRouterArgs {
+  const uint16_t* res;
+  const uint16_t* rt;
+  const uint16_t* sh;
+  const float* norm_w;
+  const float* W;          // [E][H]
+  const float* wsg;        // [H] or null
+  uint16_t* out_sum;
+  float* xn;               // or null
+  uint8_t* xq;
+  float* logits;           // [E + 1] workspace
+  float* user_logits;      // [E] or null
+  int32_t* ids;
+  float* wts;
+  float* sg;
+  unsigned* counters;
+  int H, E, k, cstride, nsub;
+  float eps;
+};
+
+__global__ __launch_bounds__(kNormThreads) void k_norm_router(NormRouterArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ double red[kNormThreads / 64];
+  __shared__ int is_last;
+  const int H = a.H, x = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long hb = kib_up(4L * H);
+  float* row = reinterpret_cast<float*>(smem);                 // H floats, padded to the next KiB
+  float* nw = reinterpret_cast<float*>(smem + hb);             // the norm weight, likewise
+  float* u = reinterpret_cast<float*>(smem + 2 * hb);          // H floats: the folded sum
+  float* xn = u + H;                                            // H floats
+  stage_async(reinterpret_cast<uint8_t*>(row), x < a.E ? a.W + (long)x * H : a.wsg, (uint32_t)(H * 4), wave, 0,
+              kNormThreads / 64);
+  stage_async(reinterpret_cast<uint8_t*>(nw), a.norm_w, (uint32_t)(H * 4), wave, 0, kNormThreads / 64);
+  // the fold's loads queue behind the streamed rows, so both have landed after it
+  const bool vec = ((reinterpret_cast<uintptr_t>(a.res) | reinterpret_cast<uintptr_t>(a.rt) |
+                     reinterpret_cast<uintptr_t>(a.sh)) & 15) == 0;
+  const double ss = norm_fold(a.res, a.rt, a.sh, H, nullptr, u, vec);
+  wait_vmem();
+  __syncthreads();
+  norm_scale(ss, nw, H, a.eps, nullptr, u, xn, red, vec);
+  __syncthreads();
+  double acc = 0.0;
+  for (int i = threadIdx.x * 4; i < H; i += kNormThreads * 4) {
+    const float4 w4 = *reinterpret_cast<const float4*>(row + i);
+    const float4 x4 = *reinterpret_cast<const float4*>(xn + i);
+    acc += (double)w4.x * (double)x4.x;
+    acc += (double)w4.y * (double)x4.y;
+    acc += (double)w4.z * (double)x4.z;
+    acc += (double)w4.w * (double)x4.w;
+  }
+  acc = wave_sum_f64(acc);
+  __syncthreads();                       // every wave is done with red (the norm's sums)
+  if (lane == 0) red[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double v = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < kNormThreads / 64; ++w2) v += red[w2];
+    // agent-coherent store, complete before the counter moves (as in k_router_topk)
+    __hip_atomic_store(a.logits + x, (float)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.user_logits && x < a.E) a.user_logits[x] = (float)v;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    is_last = arrive_last(a.counters, a.cstride, a.nsub);
+  }
+  __syncthreads();
+  if (x == 0) {
+    for (int i = threadIdx.x * 4; a.xn && i < H; i += kNormThreads * 4)
+      *reinterpret_cast<float4*>(a.xn + i) = *reinterpret_cast<const float4*>(xn + i);
+    q81_from_lds(xn, H, a.xq);
+  }
+  if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (wave == 0) {
+    wave_topk_softmax(a.logits, a.E, a.k, a.ids, a.wts);
+    if (lane == 0 && a.sg) a.sg[0] = a.wsg ? (float)sigmoid_f64((double)a.logits[a.E]) : 0.0f;
+  }
+  for (int i = threadIdx.x; i < H; i += kNormThreads) a.out_sum[i] = f32_to_bf16(u[i]);
 }
 
 // =====================================================================
@@ -390,16 +510,15 @@ struct GateUpArgs {
   int type, stype;
 };
 
+
 template <int TYPE>
-__device__ void gate_up_chunk(const uint8_t* gate_rows, const uint8_t* up_rows, int nr, int H, const ActLds& act,
-                              uint8_t* stage, double* partial, float* h_out) {
+__device__ void gate_up_chunk(const uint8_t* stage, long up_off, int nr, int H, const ActLds& act, double* partial,
+                              float* h_out) {
   const long rb = row_bytes(TYPE, H);
-  stage_to_lds(stage, gate_rows, nr * rb, blockDim.x);
-  stage_to_lds(stage + nr * rb, up_rows, nr * rb, blockDim.x);
-  __syncthreads();
-  rows_partials<TYPE>(stage, rb, 2 * nr, H, act, partial, blockDim.x);
-  __syncthreads();
   const int T = tasks_per_row(TYPE, H);
+  rows_partials<TYPE>(stage, rb, nr, H, act, partial, blockDim.x);
+  rows_partials<TYPE>(stage + up_off, rb, nr, H, act, partial + (long)nr * T, blockDim.x);
+  __syncthreads();
   for (int f = threadIdx.x; f < nr; f += blockDim.x) {
     const float g = (float)sum_partials(partial + (long)f * T, T);
     const float u = (float)sum_partials(partial + (long)(nr + f) * T, T);
@@ -407,42 +526,50 @@ __device__ void gate_up_chunk(const uint8_t* gate_rows, const uint8_t* up_rows, 
   }
 }
 
+// The gate and up rows are streamed straight into LDS (every KiB chunk in
+// flight at once) as soon as the expert id is known; the activations are read
+// behind them.
 __global__ __launch_bounds__(kFfnThreads) void k_gate_up(GateUpArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int H = a.H;
-  uint8_t* codes = smem;
-  float* dact = reinterpret_cast<float*>(smem + H);
-  float* sact = dact + H / 32;
-  uint8_t* stage = reinterpret_cast<uint8_t*>(sact + H / 32);
-  stage = reinterpret_cast<uint8_t*>(((uintptr_t)stage + 15) & ~(uintptr_t)15);
-  load_act_lds(a.xq, H, codes, dact, sact, blockDim.x);
-  __syncthreads();
-  ActLds act{codes, dact, sact};
+  const int wave = threadIdx.x >> 6;
   const int b = blockIdx.x;
-  if (b < a.k * a.cpe) {
+  const bool routed = b < a.k * a.cpe;
+  const int type = routed ? MOE_TYPE_Q4_K : a.stype;
+  const long rb = row_bytes(type, H);
+  const long up_off = kib_up((long)a.R * rb);
+  uint8_t* stage = smem;
+  double* partial = reinterpret_cast<double*>(stage + 2 * up_off);
+  uint8_t* codes = reinterpret_cast<uint8_t*>(partial + 2 * (long)a.R * tasks_per_row(type, H));
+  float* dact = reinterpret_cast<float*>(codes + H);
+  float* sact = dact + H / 32;
+  int nr, f0;
+  float* h_out;
+  if (routed) {
     const int slot = b / a.cpe;
-    const int f0 = (b % a.cpe) * a.R;
-    const int nr = min(a.R, a.F - f0);
+    f0 = (b % a.cpe) * a.R;
+    nr = min(a.R, a.F - f0);
     const long e = a.ids[slot];
     if (e < 0 || e >= a.E) {  // an id outside the experts reads nothing and yields NaN
       for (int f = threadIdx.x; f < nr; f += blockDim.x) a.h[(long)slot * a.F + f0 + f] = __builtin_nanf("");
       return;
     }
-    const long rb = row_bytes(MOE_TYPE_Q4_K, H);
-    const uint8_t* g = a.gate + (e * a.F + f0) * rb;
-    const uint8_t* u = a.up + (e * a.F + f0) * rb;
-    double* partial = reinterpret_cast<double*>(stage + 2 * (long)a.R * rb + 16);
-    gate_up_chunk<MOE_TYPE_Q4_K>(g, u, nr, H, act, stage, partial, a.h + (long)slot * a.F + f0);
+    stage_async(stage, a.gate + (e * a.F + f0) * rb, (uint32_t)(nr * rb), wave, 0, kFfnThreads / 64);
+    stage_async(stage + up_off, a.up + (e * a.F + f0) * rb, (uint32_t)(nr * rb), wave, 0, kFfnThreads / 64);
+    h_out = a.h + (long)slot * a.F + f0;
   } else {
-    const int f0 = (b - a.k * a.cpe) * a.R;
-    const int nr = min(a.R, a.Fs - f0);
-    const long rb = row_bytes(a.stype, H);
-    double* partial = reinterpret_cast<double*>(stage + 2 * (long)a.R * rb + 16);
-    if (a.stype == MOE_TYPE_Q8_0)
-      gate_up_chunk<MOE_TYPE_Q8_0>(a.sgate + f0 * rb, a.sup + f0 * rb, nr, H, act, stage, partial, a.hs + f0);
-    else
-      gate_up_chunk<MOE_TYPE_Q4_K>(a.sgate + f0 * rb, a.sup + f0 * rb, nr, H, act, stage, partial, a.hs + f0);
+    f0 = (b - a.k * a.cpe) * a.R;
+    nr = min(a.R, a.Fs - f0);
+    stage_async(stage, a.sgate + f0 * rb, (uint32_t)(nr * rb), wave, 0, kFfnThreads / 64);
+    stage_async(stage + up_off, a.sup + f0 * rb, (uint32_t)(nr * rb), wave, 0, kFfnThreads / 64);
+    h_out = a.hs + f0;
   }
+  load_act_lds(a.xq, H, codes, dact, sact, blockDim.x);
+  wait_vmem();
+  __syncthreads();
+  ActLds act{codes, dact, sact};
+  if (type == MOE_TYPE_Q8_0) gate_up_chunk<MOE_TYPE_Q8_0>(stage, up_off, nr, H, act, partial, h_out);
+  else gate_up_chunk<MOE_TYPE_Q4_K>(stage, up_off, nr, H, act, partial, h_out);
 }
 
 // =====================================================================
@@ -495,10 +622,12 @@ __device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
   uint8_t* stage = reinterpret_cast<uint8_t*>((((uintptr_t)(ssh + Kps / 32)) + 15) & ~(uintptr_t)15);
   const long rb = row_bytes(DT, Kp);
   const long rbs = a.Fs > 0 ? row_bytes(ST, Kps) : 0;
+  const long slot_bytes = kib_up((long)a.Ro * rb);   // each slot's rows start at a KiB boundary
   const int i0 = blockIdx.x * a.Ro;
   const int nr = min(a.Ro, a.H - i0);
-  uint8_t* stage_s = stage + (long)a.k * a.Ro * rb;
-  double* partial = reinterpret_cast<double*>(stage_s + (long)a.Ro * rbs + 16);
+  const int wave = threadIdx.x >> 6;
+  uint8_t* stage_s = stage + (long)a.k * slot_bytes;
+  double* partial = reinterpret_cast<double*>(stage_s + kib_up((long)a.Ro * rbs));
   const int T = tasks_per_row(DT, Kp);
   const int Ts = a.Fs > 0 ? tasks_per_row(ST, Kps) : 0;
   double* partial_s = partial + (long)a.k * a.Ro * T;
@@ -514,15 +643,36 @@ __device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
     return;
   }
 
-  // stage the weight rows first so their loads are in flight during the quantisation
+  // stream the weight rows into LDS first so they are in flight during the quantisation
   for (int s = 0; s < a.k; ++s) {
     const long e = a.ids[s];
-    stage_to_lds(stage + (long)s * a.Ro * rb, a.down + (e * a.H + i0) * rb, nr * rb, blockDim.x);
+    stage_async(stage + (long)s * slot_bytes, a.down + (e * a.H + i0) * rb, (uint32_t)(nr * rb), wave, 0,
+                kFfnThreads / 64);
   }
-  if (a.Fs > 0) stage_to_lds(stage_s, a.sdown + (long)i0 * rbs, nr * rbs, blockDim.x);
-  for (int s = 0; s < a.k; ++s)
-    quantize_to_lds(a.h + (long)s * a.F, a.F, Kp, codes + (long)s * Kp, dact + s * (Kp / 32), sact + s * (Kp / 32));
-  if (a.Fs > 0) quantize_to_lds(a.hs, a.Fs, Kps, codes_s, dsh, ssh);
+  if (a.Fs > 0) stage_async(stage_s, a.sdown + (long)i0 * rbs, (uint32_t)(nr * rbs), wave, 0, kFfnThreads / 64);
+  // Q8_1 of every h: with 16-byte aligned h, four lanes per block and two
+  // blocks in flight per lane (every load of a pass out before the first
+  // quantisation); otherwise one lane per element
+  const bool vec_h = (((uintptr_t)a.h | (uintptr_t)(a.Fs > 0 ? a.hs : nullptr)) & 15) == 0;
+  if (vec_h) {
+    const int nbk = Kp / 32, F = a.F, Fs = a.Fs;
+    quantize_q81_groups<4, 2>(
+        a.k * nbk, a.h,
+        [nbk, F](int j) {
+          const int s = j / nbk, jj = j - s * nbk;
+          return 32 * jj < F ? s * F + 32 * jj : -1;
+        },
+        [codes](int j) { return codes + 32 * j; }, dact, sact, threadIdx.x, kFfnThreads);
+    if (a.Fs > 0)
+      quantize_q81_groups<4, 2>(
+          Kps / 32, a.hs, [Fs](int j) { return 32 * j < Fs ? 32 * j : -1; },
+          [codes_s](int j) { return codes_s + 32 * j; }, dsh, ssh, threadIdx.x, kFfnThreads);
+  } else {
+    for (int s = 0; s < a.k; ++s)
+      quantize_to_lds(a.h + (long)s * a.F, a.F, Kp, codes + (long)s * Kp, dact + s * (Kp / 32), sact + s * (Kp / 32));
+    if (a.Fs > 0) quantize_to_lds(a.hs, a.Fs, Kps, codes_s, dsh, ssh);
+  }
+  wait_vmem();
   __syncthreads();
   // tasks of all routed rows
   const int total = a.k * nr * T;
@@ -531,7 +681,7 @@ __device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
     const int rem = i - s * nr * T;
     const int r = rem / T, t = rem - r * T;
     ActLds act{codes + (long)s * Kp, dact + s * (Kp / 32), sact + s * (Kp / 32)};
-    partial[((long)s * a.Ro + r) * T + t] = row_task<DT>(stage + ((long)s * a.Ro + r) * rb, t, act);
+    partial[((long)s * a.Ro + r) * T + t] = row_task<DT>(stage + (long)s * slot_bytes + (long)r * rb, t, act);
   }
   if (a.Fs > 0) {
     ActLds acts{codes_s, dsh, ssh};
@@ -744,12 +894,49 @@ int launch_router(const float* xn, const float* W, const float* wsg, int n_tok, 
   return launch_ok();
 }
 
+int launch_norm_router(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, const float* norm_w, const float* W,
+                       const float* wsg, int H, int E, int k, float eps, uint16_t* out_sum, float* xn, void* xq,
+                       float* logits, float* user_logits, int32_t* ids, float* wts, float* sg, unsigned* counters,
+                       hipStream_t st) {
+  NormRouterArgs a;
+  a.res = res;
+  a.rt = rt;
+  a.sh = sh;
+  a.norm_w = norm_w;
+  a.W = W;
+  a.wsg = wsg;
+  a.out_sum = out_sum;
+  a.xn = xn;
+  a.xq = (uint8_t*)xq;
+  a.logits = logits;
+  a.user_logits = user_logits;
+  a.ids = ids;
+  a.wts = wts;
+  a.sg = sg;
+  a.counters = counters;
+  a.H = H;
+  a.E = E;
+  a.k = k;
+  a.eps = eps;
+  // one token group: eight sub-counters, one counter per 128-byte line
+  a.nsub = 8;
+  a.cstride = 32;
+  static_assert(9 * 32 <= kCounterSlots, "counter area holds one split token group");
+  const int nrows = E + (wsg ? 1 : 0);
+  const size_t lds = 2 * (size_t)kib_up(4L * H) + 8 * (size_t)H;
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)k_norm_router, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return MOE_ERR_HIP;
+  hipLaunchKernelGGL(k_norm_router, dim3(nrows), dim3(kNormThreads), lds, st, a);
+  return launch_ok();
+}
+
 size_t gate_up_lds(int H, int R, int rtype) {
   const long rb = row_bytes(rtype, H);
-  size_t act = (size_t)H + 2 * sizeof(float) * (H / 32) + 16;
-  size_t stage = 2 * (size_t)R * rb + 16;
+  size_t act = (size_t)H + 2 * sizeof(float) * (H / 32);
+  size_t stage = 2 * (size_t)kib_up((long)R * rb);
   size_t part = sizeof(double) * 2 * (size_t)R * tasks_per_row(rtype, H);
-  return act + stage + part + 16;
+  return stage + part + act;
 }
 
 int pick_gate_up_rows(int H, int rtype) {
@@ -798,7 +985,7 @@ size_t down_lds(const moe_layer_desc* d, int Ro) {
   size_t acts = (size_t)k * Kp + Kps + 2 * sizeof(float) * ((size_t)k * (Kp / 32) + Kps / 32) + 16;
   const long rb = row_bytes(d->down_type, Kp);
   const long rbs = d->shared_ffn > 0 ? row_bytes(d->shared_type, Kps) : 0;
-  size_t stage = (size_t)k * Ro * rb + (size_t)Ro * rbs + 16;
+  size_t stage = (size_t)k * kib_up((long)Ro * rb) + (size_t)kib_up((long)Ro * rbs);
   size_t part = sizeof(double) * ((size_t)k * Ro * tasks_per_row(d->down_type, Kp) +
                                   (size_t)Ro * (d->shared_ffn > 0 ? tasks_per_row(d->shared_type, Kps) : 0));
   size_t y = sizeof(float) * (size_t)(k + 1) * Ro;

@@ -33,7 +33,6 @@
 
 namespace moe {
 
-typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kPollWaves = 4;   // waves 0..3 poll and load the routed gate/up rows
 // Copies of each exchange area: the producer of a word writes it into every
 // copy and workgroup b reads copy b % R, so the 256 readers of one word are
@@ -53,8 +52,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 constexpr int kXcc = 8;   // accelerator complex dies (XCCs) of the MI355X, each with its own L2
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t v;
@@ -63,8 +60,6 @@ __device__ __forceinline__ uint32_t xcc_id() {
 }
 
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
 // outstanding global load of the wave (its workgroup-scope fence covers global
@@ -76,45 +71,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// 16 bytes per lane from global memory straight into LDS (buffer_load ... lds):
-// the wave's 64 lanes fill the 1 KiB at LDS address `lds` (M0) from byte
-// offset `off` + 16 * lane of the buffer described by `rsrc`.  Issued from
-// inline asm so the compiler does not track it: it would otherwise wait for
-// every such load before any LDS read it cannot prove disjoint, which stalls
-// the waves that compute while their next rows stream in.  The consumer waits
-// explicitly (s_waitcnt vmcnt(0) in the issuing waves, then a barrier).
-__device__ __forceinline__ void lds_dma_1k(v4u rsrc, uint32_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(off), "s"(rsrc)
-               : "memory", "m0");
-}
-
-// Buffer descriptor with hardware range checking: loads past `bytes` read 0.
-__device__ __forceinline__ v4u raw_rsrc(const void* p, uint32_t bytes) {
-  const unsigned long long a = (unsigned long long)p;
-  v4u r;
-  r.x = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-  r.z = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
-  r.w = 0x00020000u;
-  return r;
-}
-
-// Stream `bytes` from src into LDS dst (1 KiB per wave instruction); waves
-// [w0, w0+nw) take chunks round-robin.  dst must have room for the byte count
-// rounded up to 1 KiB: lanes past the source end read 0 (range-checked
-// descriptor) and write that 0 into the padding.
-__device__ __forceinline__ void stage_async(uint8_t* dst, const void* src, uint32_t bytes, int wave, int w0, int nw) {
-  if (wave < w0 || wave >= w0 + nw || bytes == 0) return;
-  const v4u r = raw_rsrc(src, bytes);
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)dst;
-  const int lane = threadIdx.x & 63;
-  const uint32_t nchunks = (bytes + 1023) >> 10;
-  for (uint32_t c = wave - w0; c < nchunks; c += nw)
-    lds_dma_1k(r, (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (c << 10))), (c << 10) + lane * 16);
 }
 
 __device__ __forceinline__ void ll_store(const __amdgpu_buffer_rsrc_t& r, uint32_t word, uint32_t payload, uint32_t epoch,

@@ -355,7 +355,11 @@ def test_decode_layer_chained(q, orc, cfg_name, shared_type, down_type, ntok):
         _sync()
         if norm:
             assert np.array_equal(gu.u16_host(io["out_sum"]), o["out_sum"])
-        assert gu.ulp_diff_f32(gu.host(io["xn"]), o["xn"]).max() <= 1
+        g_xn = gu.host(io["xn"])
+        assert gu.ulp_diff_f32(g_xn, o["xn"]).max() <= 1
+        same_blocks = (g_xn.reshape(-1, 32) == o["xn"].reshape(-1, 32)).all(1)
+        gb, ob = gu.host(io["xq"]).reshape(-1, 36), o["xq"].reshape(-1, 36)
+        assert np.array_equal(gb[same_blocks], ob[same_blocks])  # identical inputs -> identical Q8_1 bytes
         assert gu.ulp_diff_f32(gu.host(io["logits"]), o["logits"]).max() <= 1
         same_logits = np.array_equal(gu.host(io["logits"]), o["logits"])
         g_ids = gu.host(io["ids"])
@@ -381,6 +385,19 @@ def test_decode_layer_chained(q, orc, cfg_name, shared_type, down_type, ntok):
             gu.assert_bf16_within(gu.u16_host(io["shared_out"]), o["shared_exact"], "shared")
         print(f"  token {t}: ids {g_ids.tolist()} routed exact "
               f"{float((gu.u16_host(io['routed_out']) == o['routed']).mean()):.5f}", flush=True)
+        if norm:
+            # the residual updated in place (out_sum is the residual buffer): same results
+            io2 = {n: (v.clone() if isinstance(v, torch.Tensor) else v) for n, v in io.items()}
+            io2["out_sum"] = io2["residual"]
+            for n in ("routed_out", "shared_out", "ids", "weights"):
+                if n in io2:
+                    io2[n].zero_()
+            q.moe_decode_layer(desc_g, W, io2, ws)
+            _sync()
+            assert np.array_equal(gu.u16_host(io2["residual"]), gu.u16_host(io["out_sum"]))
+            for n in ("routed_out", "shared_out", "ids", "weights"):
+                if n in io2:
+                    assert torch.equal(io2[n], io[n]), n
 
 
 # ------------------------------------------------------------------ a7: stack, per-layer kernels
