@@ -109,10 +109,16 @@ int decode_layer(const moe_layer_desc* desc, const moe_layer_weights* w, const m
   float* hs = io->hs ? io->hs : at<float>(ws, L.hs);
   const float* wsg = desc->shared_ffn > 0 ? w->shared_gate_w : nullptr;
   if (desc->norm) {
-    rc = launch_norm_router(io->residual, io->routed_in, io->shared_in, w->norm_w, w->router_w, wsg, H, E, k,
-                            desc->eps, io->out_sum, io->xn, xq, at<float>(ws, L.logits), io->logits, ids, wts, sg,
-                            at<unsigned>(ws, L.counters), st);
+    // the fold + norm + router rows, then gate/up selecting from their logits
+    // (and writing the folded residual sum), then down + combine
+    rc = launch_norm_router(io->residual, io->routed_in, io->shared_in, w->norm_w, w->router_w, wsg, H, E, desc->eps,
+                            io->xn, xq, at<float>(ws, L.logits), io->logits, st);
     if (rc) return rc;
+    const GateUpSelect sel{at<float>(ws, L.logits), ids, wts, sg, io->residual, io->routed_in, io->shared_in,
+                           io->out_sum};
+    rc = launch_gate_up(desc, w, xq, nullptr, h, hs, st, &sel);
+    if (rc) return rc;
+    return launch_down(desc, w, h, hs, ids, wts, sg, io->routed_out, io->shared_out, st);
   } else {
     if (io->xn) {
       if (hipMemcpyAsync(io->xn, io->x, sizeof(float) * H, hipMemcpyDeviceToDevice, st) != hipSuccess)
@@ -439,11 +445,12 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
       n1 = io->attn + (size_t)l * H;
       n2 = nullptr;
     }
-    rc = launch_norm_router(nin, n1, n2, w->norm_w, w->router_w, has_shared ? w->shared_gate_w : nullptr, H, E, k,
-                            desc->eps, res_out, nullptr, at<void>(ws, L.xq), at<float>(ws, L.logits), nullptr, ids,
-                            at<float>(ws, L.wts), at<float>(ws, L.sg), at<unsigned>(ws, L.counters), st);
+    rc = launch_norm_router(nin, n1, n2, w->norm_w, w->router_w, has_shared ? w->shared_gate_w : nullptr, H, E,
+                            desc->eps, nullptr, at<void>(ws, L.xq), at<float>(ws, L.logits), nullptr, st);
     if (rc) return rc;
-    rc = launch_gate_up(desc, w, at<void>(ws, L.xq), ids, at<float>(ws, L.h), at<float>(ws, L.hs), st);
+    const GateUpSelect sel{at<float>(ws, L.logits), ids, at<float>(ws, L.wts), at<float>(ws, L.sg), nin, n1, n2,
+                           res_out};
+    rc = launch_gate_up(desc, w, at<void>(ws, L.xq), nullptr, at<float>(ws, L.h), at<float>(ws, L.hs), st, &sel);
     if (rc) return rc;
     rc = launch_down(desc, w, at<float>(ws, L.h), at<float>(ws, L.hs), ids, at<float>(ws, L.wts), at<float>(ws, L.sg),
                      routed, shared, st);

@@ -33,14 +33,25 @@ int launch_norm(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, con
 int launch_quantize(const float* x, int n, void* xq, hipStream_t st);
 int launch_router(const float* xn, const float* W, const float* wsg, int n_tok, int H, int E, int k, float* logits,
                   float* user_logits, int32_t* ids, float* wts, float* sg, unsigned* counters, hipStream_t st);
-// a1 + a2 + a3 of one token in one launch (the residual fold and norm, the
-// router rows, the top-k); out_sum may alias res.
+// a1 + a2 of one token in one launch (the residual fold and norm, the router
+// rows): logits [E + 1], xq, and xn when given.
 int launch_norm_router(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, const float* norm_w, const float* W,
-                       const float* wsg, int H, int E, int k, float eps, uint16_t* out_sum, float* xn, void* xq,
-                       float* logits, float* user_logits, int32_t* ids, float* wts, float* sg, unsigned* counters,
-                       hipStream_t st);
+                       const float* wsg, int H, int E, float eps, float* xn, void* xq, float* logits,
+                       float* user_logits, hipStream_t st);
+// k_gate_up selecting its experts itself from the router launch's logits (a3)
+// and writing the folded residual sum (res, rt, sh -> out_sum, may alias).
+struct GateUpSelect {
+  const float* logits;
+  int32_t* ids;
+  float* wts;
+  float* sg;
+  const uint16_t* res;
+  const uint16_t* rt;
+  const uint16_t* sh;
+  uint16_t* out_sum;
+};
 int launch_gate_up(const moe_layer_desc* d, const moe_layer_weights* w, const void* xq, const int32_t* ids, float* h,
-                   float* hs, hipStream_t st);
+                   float* hs, hipStream_t st, const GateUpSelect* sel = nullptr);
 int launch_down(const moe_layer_desc* d, const moe_layer_weights* w, const float* h, const float* hs, const int32_t* ids,
                 const float* wts, const float* sg, uint16_t* routed, uint16_t* shared, hipStream_t st);
 int launch_fill(void* p, size_t n_u32, uint32_t v, hipStream_t st);

@@ -38,6 +38,15 @@ __device__ __forceinline__ void unpack_bf16x8(uint4 v, float f[8]) {
     f[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
   }
 }
+// One element of the fold: bf16(res + bf16(rt + sh)) (bf16(res + rt) without
+// sh, res alone without rt) -- the same operations as norm_fold.
+__device__ __forceinline__ uint16_t fold_elem(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, int i) {
+  float t = 0.0f;
+  if (rt && sh) t = bf16_to_f32(f32_to_bf16(bf16_to_f32(rt[i]) + bf16_to_f32(sh[i])));
+  else if (rt) t = bf16_to_f32(rt[i]);
+  return f32_to_bf16(bf16_to_f32(res[i]) + t);
+}
+
 // Q8_1 of the H values at xn_lds (LDS) into xq_out, four lanes per 32-block.
 __device__ void q81_from_lds(const float* xn_lds, int H, uint8_t* xq_out) {
   // block j: lanes 4j .. 4j+3, values 8p .. 8p+7 each
@@ -357,15 +366,15 @@ __global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn,
     }
 }
 
-// a1 + a2 + a3 for one token in one launch ([P273] Summary items 1 and 2: the
-// residual fold and norm ahead of the router's GEMV, the top-k in the same
-// kernel).  Workgroup x (kNormThreads threads) owns router row x (the
-// shared-gate row when x == E): it streams the row and the norm weight into
-// LDS while it folds the token itself, normalises it (the same element
-// mapping and fp64 reduction order as k_add_rmsnorm, so the same u, r and xn)
-// and takes the row's fp64 dot with xn.  Workgroup 0 also writes xn and xq;
-// the last workgroup to arrive selects and writes out_sum, after every
-// workgroup has read the residual inputs, so out_sum may be one of them.
+// a1 + a2 for one token in one launch ([P273] Summary item 2: the residual
+// fold and norm ahead of the router's GEMV).  Workgroup x (kNormThreads
+// threads) owns router row x (the shared-gate row when x == E): it streams the
+// row and the norm weight into LDS while it folds the token itself,
+// normalises it (the same element mapping and fp64 reduction order in every
+// workgroup, so the same xn everywhere) and stores the row's fp64 dot with xn.
+// Workgroup 0 also writes xn and xq.  The selection runs in the next launch
+// (k_gate_up), which also writes the folded sum: by then every read of the
+// residual inputs is done, so out_sum may be one of them.
 struct NormRouterArgs {
   const uint16_t* res;
   const uint16_t* rt;
@@ -373,23 +382,17 @@ struct NormRouterArgs {
   const float* norm_w;
   const float* W;          // [E][H]
   const float* wsg;        // [H] or null
-  uint16_t* out_sum;
   float* xn;               // or null
   uint8_t* xq;
   float* logits;           // [E + 1] workspace
   float* user_logits;      // [E] or null
-  int32_t* ids;
-  float* wts;
-  float* sg;
-  unsigned* counters;
-  int H, E, k, cstride, nsub;
+  int H, E;
   float eps;
 };
 
 __global__ __launch_bounds__(kNormThreads) void k_norm_router(NormRouterArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ double red[kNormThreads / 64];
-  __shared__ int is_last;
   const int H = a.H, x = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long hb = kib_up(4L * H);
@@ -425,25 +428,14 @@ __global__ __launch_bounds__(kNormThreads) void k_norm_router(NormRouterArgs a) 
     double v = 0.0;
 #pragma unroll
     for (int w2 = 0; w2 < kNormThreads / 64; ++w2) v += red[w2];
-    // agent-coherent store, complete before the counter moves (as in k_router_topk)
-    __hip_atomic_store(a.logits + x, (float)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.logits[x] = (float)v;
     if (a.user_logits && x < a.E) a.user_logits[x] = (float)v;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    is_last = arrive_last(a.counters, a.cstride, a.nsub);
   }
-  __syncthreads();
   if (x == 0) {
     for (int i = threadIdx.x * 4; a.xn && i < H; i += kNormThreads * 4)
       *reinterpret_cast<float4*>(a.xn + i) = *reinterpret_cast<const float4*>(xn + i);
     q81_from_lds(xn, H, a.xq);
   }
-  if (!is_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (wave == 0) {
-    wave_topk_softmax(a.logits, a.E, a.k, a.ids, a.wts);
-    if (lane == 0 && a.sg) a.sg[0] = a.wsg ? (float)sigmoid_f64((double)a.logits[a.E]) : 0.0f;
-  }
-  for (int i = threadIdx.x; i < H; i += kNormThreads) a.out_sum[i] = f32_to_bf16(u[i]);
 }
 
 // =====================================================================
@@ -499,7 +491,17 @@ __device__ __forceinline__ double sum_partials(const double* p, int T) {
 // in memory and staged into LDS with 16-byte loads.
 struct GateUpArgs {
   const uint8_t* xq;
-  const int32_t* ids;
+  const int32_t* ids;      // the selected experts, or null: select from `logits`
+  const float* logits;     // [E + 1] (selection; logit E is the shared gate's)
+  int32_t* ids_out;        // selection: ids, weights and shared gate written by workgroup 0
+  float* wts_out;
+  float* sg_out;           // or null
+  int has_sg;
+  // the residual fold u = bf16(res + bf16(rt + sh)) -> out_sum, a slice per workgroup (or null)
+  const uint16_t* res;
+  const uint16_t* rt;
+  const uint16_t* sh;
+  uint16_t* out_sum;
   const uint8_t* gate;
   const uint8_t* up;
   const uint8_t* sgate;
@@ -545,11 +547,32 @@ __global__ __launch_bounds__(kFfnThreads) void k_gate_up(GateUpArgs a) {
   float* sact = dact + H / 32;
   int nr, f0;
   float* h_out;
+  if (a.out_sum) {   // this workgroup's slice of the folded residual sum
+    const int cs = (H + gridDim.x - 1) / gridDim.x;
+    const int iend = min(H, (b + 1) * cs);
+    for (int i = b * cs + threadIdx.x; i < iend; i += blockDim.x) a.out_sum[i] = fold_elem(a.res, a.rt, a.sh, i);
+  }
   if (routed) {
     const int slot = b / a.cpe;
     f0 = (b % a.cpe) * a.R;
     nr = min(a.R, a.F - f0);
-    const long e = a.ids[slot];
+    __shared__ int32_t s_ids[MOE_MAX_TOPK];
+    __shared__ float s_wts[MOE_MAX_TOPK];
+    if (!a.ids) {   // the selection, from the logits of the router launch
+      if (wave == 0) {
+        wave_topk_softmax(a.logits, a.E, a.k, s_ids, s_wts);
+        if (b == 0) {
+          const int lane = threadIdx.x & 63;
+          if (lane < a.k) {
+            a.ids_out[lane] = s_ids[lane];
+            a.wts_out[lane] = s_wts[lane];
+          }
+          if (lane == 0 && a.sg_out) a.sg_out[0] = a.has_sg ? (float)sigmoid_f64((double)a.logits[a.E]) : 0.0f;
+        }
+      }
+      __syncthreads();
+    }
+    const long e = a.ids ? a.ids[slot] : s_ids[slot];
     if (e < 0 || e >= a.E) {  // an id outside the experts reads nothing and yields NaN
       for (int f = threadIdx.x; f < nr; f += blockDim.x) a.h[(long)slot * a.F + f0 + f] = __builtin_nanf("");
       return;
@@ -633,6 +656,10 @@ __device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
   double* partial_s = partial + (long)a.k * a.Ro * T;
   float* y = reinterpret_cast<float*>(partial_s + (long)a.Ro * Ts);
 
+  // the routing weights and the gate are read now (they are needed only at the end)
+  __shared__ float s_wts[MOE_MAX_TOPK], s_sg;
+  if (threadIdx.x < a.k) s_wts[threadIdx.x] = a.wts[threadIdx.x];
+  if (threadIdx.x == 0) s_sg = a.Fs > 0 ? a.sg[0] : 0.0f;
   bool bad_id = false;
   for (int s = 0; s < a.k; ++s) bad_id |= (a.ids[s] < 0 || a.ids[s] >= a.E);
   if (bad_id) {  // an id outside the experts reads nothing and yields NaN outputs
@@ -699,9 +726,9 @@ __device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
   __syncthreads();
   for (int r = threadIdx.x; r < nr; r += blockDim.x) {
     double acc = 0.0;
-    for (int s = 0; s < a.k; ++s) acc += (double)a.wts[s] * (double)y[s * a.Ro + r];
+    for (int s = 0; s < a.k; ++s) acc += (double)s_wts[s] * (double)y[s * a.Ro + r];
     a.routed[i0 + r] = f32_to_bf16((float)acc);
-    if (a.Fs > 0 && a.shared) a.shared[i0 + r] = f32_to_bf16((float)((double)a.sg[0] * (double)y[a.k * a.Ro + r]));
+    if (a.Fs > 0 && a.shared) a.shared[i0 + r] = f32_to_bf16((float)((double)s_sg * (double)y[a.k * a.Ro + r]));
   }
 }
 
@@ -895,9 +922,8 @@ int launch_router(const float* xn, const float* W, const float* wsg, int n_tok, 
 }
 
 int launch_norm_router(const uint16_t* res, const uint16_t* rt, const uint16_t* sh, const float* norm_w, const float* W,
-                       const float* wsg, int H, int E, int k, float eps, uint16_t* out_sum, float* xn, void* xq,
-                       float* logits, float* user_logits, int32_t* ids, float* wts, float* sg, unsigned* counters,
-                       hipStream_t st) {
+                       const float* wsg, int H, int E, float eps, float* xn, void* xq, float* logits,
+                       float* user_logits, hipStream_t st) {
   NormRouterArgs a;
   a.res = res;
   a.rt = rt;
@@ -905,23 +931,13 @@ int launch_norm_router(const uint16_t* res, const uint16_t* rt, const uint16_t* 
   a.norm_w = norm_w;
   a.W = W;
   a.wsg = wsg;
-  a.out_sum = out_sum;
   a.xn = xn;
   a.xq = (uint8_t*)xq;
   a.logits = logits;
   a.user_logits = user_logits;
-  a.ids = ids;
-  a.wts = wts;
-  a.sg = sg;
-  a.counters = counters;
   a.H = H;
   a.E = E;
-  a.k = k;
   a.eps = eps;
-  // one token group: eight sub-counters, one counter per 128-byte line
-  a.nsub = 8;
-  a.cstride = 32;
-  static_assert(9 * 32 <= kCounterSlots, "counter area holds one split token group");
   const int nrows = E + (wsg ? 1 : 0);
   const size_t lds = 2 * (size_t)kib_up(4L * H) + 8 * (size_t)H;
   if (lds > 64 * 1024 &&
@@ -946,10 +962,19 @@ int pick_gate_up_rows(int H, int rtype) {
 }
 
 int launch_gate_up(const moe_layer_desc* d, const moe_layer_weights* w, const void* xq, const int32_t* ids, float* h,
-                   float* hs, hipStream_t st) {
+                   float* hs, hipStream_t st, const GateUpSelect* sel) {
   GateUpArgs a;
   a.xq = (const uint8_t*)xq;
-  a.ids = ids;
+  a.ids = sel ? nullptr : ids;
+  a.logits = sel ? sel->logits : nullptr;
+  a.ids_out = sel ? sel->ids : nullptr;
+  a.wts_out = sel ? sel->wts : nullptr;
+  a.sg_out = sel ? sel->sg : nullptr;
+  a.has_sg = d->shared_ffn > 0;
+  a.res = sel ? sel->res : nullptr;
+  a.rt = sel ? sel->rt : nullptr;
+  a.sh = sel ? sel->sh : nullptr;
+  a.out_sum = sel ? sel->out_sum : nullptr;
   a.gate = (const uint8_t*)w->gate;
   a.up = (const uint8_t*)w->up;
   a.sgate = (const uint8_t*)w->shared_gate;
