@@ -263,12 +263,15 @@ def check_against_kernels(q, stack, t=0):
 def require_status_ok(q, stack, what):
     """The persistent kernel's status word must be 0 after the timed launches
     (1: a launch stopped at a bounded wait; 2: the bound table was not the
-    caller's); otherwise the run is invalid and the benchmark stops."""
+    caller's; 3: a die number outside 0..7); otherwise
+    the run is invalid and the benchmark stops."""
     if stack.mode != q.MOE_STACK_PERSISTENT:
         return
     st = q.stack_status(stack.desc, stack.cfg.layers, stack.ws)
     if st != 0:
-        print(json.dumps({"error": f"{what}: persistent stack status word {st} after the timed launches"}))
+        detail = q.stack_stop_detail(stack.desc, stack.cfg.layers, stack.ws) if st == 1 else None
+        print(json.dumps({"error": f"{what}: persistent stack status word {st} after the timed launches",
+                          "stop_layer_check": detail}))
         sys.exit(1)
 
 

@@ -328,8 +328,15 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
 
 /* Byte offset, in a workspace sized for (desc, n_layers), of a uint32 status
  * word of the persistent stack: 0 while every launch completed; 1 after a
- * launch stopped at a bounded wait; 2 after a launch found that the table
- * bound in the workspace is not the caller's.  A launch that starts with a
+ * launch stopped (a bounded wait ran out, or a selection came out
+ * incomplete); 2 after a launch found that the table
+ * bound in the workspace is not the caller's; 3 after a launch of an instance
+ * that pairs each workgroup with the accelerator die (XCC) it runs on read a
+ * die number outside 0..7 (it stops before any exchange).  After a stop (1)
+ * the next uint32 word holds (layer << 8) | check, the check being 1 the previous
+ * layer's outputs, 2 the logits, 3 an incomplete selection, 4 the shared
+ * expert's h, 5 the routed h, 6 the down rows' values, 7 the last layer's
+ * outputs for the final fold.  A launch that starts with a
  * nonzero word does no work: it sets its output to NaN and leaves the word as
  * it is.  So after a stopped or refused launch every later persistent launch
  * on that workspace is refused too (their outputs are NaN), until

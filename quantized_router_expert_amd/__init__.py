@@ -285,6 +285,15 @@ def stack_status(desc, n_layers, ws):
     return int(ws[off:off + 4].view(torch.int32).item())
 
 
+def stack_stop_detail(desc, n_layers, ws):
+    """After a stopped persistent launch (status 1): (layer, check) of the stop."""
+    off = moe_stack_status_offset(desc, n_layers)
+    if off == 0:
+        raise MoeError("moe_stack_status_offset", -7)
+    v = int(ws[off + 4:off + 8].view(torch.int32).item())
+    return v >> 8, v & 0xff
+
+
 def moe_stack_kernel_shape(desc):
     """0 = generic persistent instance, n >= 1 = compile-time shape n, -1 = none."""
     return _moe_stack_kernel_shape(C.byref(desc))

@@ -602,8 +602,8 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   constexpr bool FIX = S != 0;
   constexpr FixShape fs = kFixShapes[S];
   // XCD slots: with 8 selected experts on 256 workgroups, slot s is taken by
-  // the 32 workgroups b with b % 8 == s, which the cooperative launch places
-  // on XCC s (checked below): their h exchange stays in that XCC's L2
+  // the 32 workgroups that run on die (XCC) s: their h exchange stays in that
+  // die's L2
   constexpr bool XS = FIX && fs.k == kXcc && fs.G == 256;
   const StackGeom g = FIX ? kFixGeom<DT, ST, S> : a.g;
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
@@ -648,10 +648,9 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
                        a.bound[2] == (uint32_t)a.table_hash && a.bound[3] == (uint32_t)(a.table_hash >> 32);
     const uint32_t err = __builtin_amdgcn_raw_buffer_load_b32(r_ctrl, kErrWord * 4, 0, kAuxSC1);
     s_fail = !bound ? 2 : (err != 0u ? 3 : 0);
-    // the XCD-slot exchanges need workgroup b on XCC b % 8; should a launch
-    // ever place it elsewhere, it stops here (status 1) instead of waiting
-    if (XS && s_fail == 0 && xcc_id() != (uint32_t)(b % kXcc)) {
-      __builtin_amdgcn_raw_buffer_store_b32(1u, r_ctrl, kErrWord * 4, 0, kAuxSC1);
+    // the XCD-slot exchanges pair each workgroup with the die it runs on
+    if (XS && s_fail == 0 && xcc_id() >= (uint32_t)kXcc) {
+      __builtin_amdgcn_raw_buffer_store_b32(3u, r_ctrl, kErrWord * 4, 0, kAuxSC1);
       s_fail = 3;
     }
     v2u gv = __builtin_amdgcn_raw_buffer_load_b64(r_ctrl, 0, 0, kAuxSC1);
@@ -678,7 +677,14 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.ws + a.g.w_t, (uint32_t)(a.g.w_trace - a.g.w_t));
   const uint32_t x_lg = (uint32_t)(a.g.w_lg - a.g.w_t), x_h = (uint32_t)(a.g.w_h - a.g.w_t),
                  x_y = (uint32_t)(a.g.w_y - a.g.w_t);
-  const uint32_t rd_t = XS ? (b % kXcc) * rb_t : 0u, rd_lg = x_lg + (b % kRepLg) * rb_lg,
+  // XS: the die this workgroup runs on.  A launch spreads its workgroups over
+  // the 8 dies in rotation (workgroup b on die (b + r) % 8, r fixed for the
+  // launch but not always 0), so each die holds exactly one workgroup of
+  // every index j = b / 8: (die, j) names the workgroup's part of the XCD-slot
+  // phases.  (Were a launch ever placed otherwise, some part would go
+  // missing and the waits for it would stop the launch at their bound.)
+  const uint32_t xcc = XS ? xcc_id() : 0u;
+  const uint32_t rd_t = XS ? xcc * rb_t : 0u, rd_lg = x_lg + (b % kRepLg) * rb_lg,
                  rd_h = x_h + (b % kRepH) * rb_h;
 
   const long rb_gu = row_bytes(MOE_TYPE_Q4_K, H);
@@ -729,8 +735,16 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       btrace[((long)l * kTraceMaxG + b) * kBlockEvents + i] = wall_clock64();
   };
 
-  auto fail_out = [&]() {
-    if (tid == 0) __builtin_amdgcn_raw_buffer_store_b32(1u, r_ctrl, kErrWord * 4, 0, kAuxSC1);
+  // a stopped launch: status 1, and beside it the layer and the check that
+  // stopped it (s_fail: 1 the t words, 2 the logits, 3 an incomplete
+  // selection, 4 the shared h, 5 the routed h, 6 the down rows' values, 7 the
+  // last t for the output)
+  auto fail_out = [&](int l) {
+    if (tid == 0) {
+      __builtin_amdgcn_raw_buffer_store_b32(((uint32_t)l << 8) | (uint32_t)s_fail, r_ctrl, (kErrWord + 1) * 4, 0,
+                                            kAuxSC1);
+      __builtin_amdgcn_raw_buffer_store_b32(1u, r_ctrl, kErrWord * 4, 0, kAuxSC1);
+    }
   };
 
   // ---- layer-0 inputs: the token's residual, no previous outputs
@@ -790,7 +804,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     }
     // the barrier inside also publishes s_fail and the new residual
     ss = block_sum_f64(ss, red);
-    if (s_fail) { fail_out(); return; }
+    if (s_fail) { fail_out(l); return; }
     stamp(l, 2);
     bstamp(l, 2);
     if (b == 0 && a.resid_out)
@@ -863,7 +877,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
           const int p = 32 * wave + (lane & 31) + 128 * (lane >> 5);
           const int pair[1] = {(uint32_t)p < ((g.n_lg + 1u) >> 1) ? p : -1};
           uint32_t lo[1] = {0u}, hi[1] = {0u};
-          if (!poll_lane_pairs<kAuxSC1, 1>(rx, rd_lg, pair, g.n_lg, ep0, lo, hi)) s_fail = 1;
+          if (!poll_lane_pairs<kAuxSC1, 1>(rx, rd_lg, pair, g.n_lg, ep0, lo, hi)) s_fail = 2;
           if (pair[0] >= 0) {
             xbuf[2 * p] = lo[0];
             if (2 * p + 1 < g.n_lg) xbuf[2 * p + 1] = hi[0];
@@ -875,30 +889,30 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
           topk_candidates(reinterpret_cast<const float*>(xbuf), E, k, wave, keys, cand);
         }
         lds_barrier();
-        if (s_fail) { fail_out(); return; }
+        if (s_fail) { fail_out(l); return; }
       } else {
         const bool ok = poll_ll<kAuxSC1>(rx, rd_lg, g.n_lg, ep0, xbuf, kPollWaves);
-        if (!ok) s_fail = 1;
+        if (!ok) s_fail = 2;
         lds_barrier();
-        if (s_fail) { fail_out(); return; }
+        if (s_fail) { fail_out(l); return; }
         bstamp(l, 13);
         topk_candidates(reinterpret_cast<const float*>(xbuf), E, k, wave, keys, cand);
         lds_barrier();
       }
       if (wave == 0 && rank_candidates(reinterpret_cast<const float*>(xbuf), E, k, has_sg, cand, sel, lgsel))
-        s_fail = 1;
+        s_fail = 3;
       lds_barrier();
-      if (s_fail) { fail_out(); return; }
+      if (s_fail) { fail_out(l); return; }
       if (b == 0 && a.ids_out)
         for (int s = tid; s < k; s += kStackThreads) a.ids_out[(long)l * k + s] = (int32_t)sel[s];
     }
     stamp(l, 4);
     bstamp(l, 5);
     // ================= phase B: routed gate/up rows (this workgroup's slot and rows)
-    // XS: slot b % 8, h rows [f0, f0 + F/32) and down rows [dr0, dr0 + H/32)
+    // XS: slot = the die, h rows [f0, f0 + F/32) and down rows [dr0, dr0 + H/32)
     // of that slot's expert; else consecutive workgroups share a slot
     const int p0 = b * g.RP;
-    const int slot = XS ? (b % kXcc) : p0 / F;
+    const int slot = XS ? (int)xcc : p0 / F;
     const int f0 = XS ? (b / kXcc) * (F / (fs.G / kXcc)) : p0 - slot * F;
     const int nrp = XS ? F / (fs.G / kXcc) : ((slot < k) ? min(g.RP, F - f0) : 0);
 
@@ -914,7 +928,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     // and quantises it: h blocks k*nb_r .. k*nb_r + nb_s - 1
     if (has_sg && wave == kPollWaves) {
       // the shared h words follow the k*F routed words
-      if (!poll_ll<kAuxSC1>(rx, rd_h + 8u * k * F, Fs, ep1, reinterpret_cast<uint32_t*>(hsf), 1, kPollWaves)) s_fail = 1;
+      if (!poll_ll<kAuxSC1>(rx, rd_h + 8u * k * F, Fs, ep1, reinterpret_cast<uint32_t*>(hsf), 1, kPollWaves)) s_fail = 4;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
@@ -925,7 +939,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     }
     if (wave < kPollWaves) wait_vmem();
     lds_barrier();
-    if (s_fail) { fail_out(); return; }
+    if (s_fail) { fail_out(l); return; }
     stamp(l, 5);
     bstamp(l, 6);
     // the down rows are needed only after the h exchange: requested once the
@@ -999,7 +1013,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       // this slot's h only, from this XCC's copy of the h area (its L2)
       if (!poll_quantize_h(rx, x_h + slot * rb_h, g.Kp / 32, g.Kp / 32, inv_nbr, F, (uint32_t)F, ep1, xbuf, hqc, hqd,
                            hqs, wave, kStackWaves))
-        s_fail = 1;
+        s_fail = 5;
       bstamp(l, 14);
     } else {
       // the down rows waves 4..7 requested in phase B have had the whole of
@@ -1007,7 +1021,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       // blocks as soon as they are current
       if (!poll_quantize_h(rx, rd_h, k * (g.Kp / 32), g.Kp / 32, inv_nbr, F, (uint32_t)(k * F), ep1, xbuf, hqc, hqd,
                            hqs, wave, kStackWaves))
-        s_fail = 1;
+        s_fail = 5;
       bstamp(l, 14);
     }
     // ================= phase C: down rows of all slots + shared, combine
@@ -1015,7 +1029,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     bstamp(l, 8);
     if (wave >= kPollWaves) wait_vmem();
     lds_barrier();
-    if (s_fail) { fail_out(); return; }
+    if (s_fail) { fail_out(l); return; }
     stamp(l, 8);
     bstamp(l, 9);
     if constexpr (XS) {
@@ -1039,14 +1053,14 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         const bool live = ps < k || (ps == k && has_sg);
         const int pair[1] = {live ? (int)((x_y >> 4) + ((uint32_t)(ps * H + dr0) >> 1) + q) : -1};
         uint32_t lo[1] = {0u}, hi[1] = {0u};
-        if (!poll_lane_pairs<kAuxSC1, 1>(rx, 0u, pair, 0xffffffffu, ep1, lo, hi)) s_fail = 1;
+        if (!poll_lane_pairs<kAuxSC1, 1>(rx, 0u, pair, 0xffffffffu, ep1, lo, hi)) s_fail = 6;
         if (live) {
           xbuf[ps * RDX + 2 * q] = lo[0];
           xbuf[ps * RDX + 2 * q + 1] = hi[0];
         }
       }
       lds_barrier();
-      if (s_fail) { fail_out(); return; }
+      if (s_fail) { fail_out(l); return; }
       // combine: one lane per (row, slot), the k slots of a row in k adjacent
       // lanes summed by a DPP tree (fp64; y_s is the fp32 row value); the
       // per-layer outputs come from XCC 0's workgroups
@@ -1129,9 +1143,9 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   if (b == 0) {
     const uint32_t epl = base + 3u * (a.L - 1) + 2u;
     const bool ok = poll_ll<kAuxSC1>(rx, rd_t, g.n_t, epl, xbuf, kPollWaves);
-    if (!ok) s_fail = 1;
+    if (!ok) s_fail = 7;
     lds_barrier();
-    if (s_fail) { fail_out(); return; }
+    if (s_fail) { fail_out(a.L); return; }
     for (int i = tid; i < H; i += kStackThreads) {
       const uint32_t pr = xbuf[i >> 1];
       const float t = bf16_to_f32((uint16_t)((i & 1) ? (pr >> 16) : (pr & 0xffffu)));
