@@ -223,9 +223,12 @@ __device__ __forceinline__ void tree_merge(const double (&left)[NM][4], double (
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[mi][i] = left[mi][i] + v[mi][i];
 }
-template <int TYPE, int NM, class Codes, class DS>
+// LV: the number of tree levels held, log2(N) + 1 for the largest N the
+// instance serves (levels past it are never live, so they take no registers)
+template <int TYPE, int NM, int LV, class Codes, class DS>
 __device__ __forceinline__ void i8_subtree(const uint8_t* const (&mats)[NM], long rb, int nr, int T, int p0, int N,
                                            Codes codes8, DS ds, double (&out)[NM][4]) {
+  static_assert(LV >= 1 && LV <= 5, "up to 16 positions per wave");
   double s0[NM][4], s1[NM][4], s2[NM][4], s3[NM][4], s4[NM][4];
 #pragma unroll 1
   for (int n = 0; n < N; ++n) {
@@ -249,24 +252,24 @@ __device__ __forceinline__ void i8_subtree(const uint8_t* const (&mats)[NM], lon
     }
     const int tz = __builtin_ctz(~(unsigned)n);   // trailing one bits of n (wave-uniform)
     if (tz >= 1) tree_merge<NM>(s0, v);
-    if (tz >= 2) tree_merge<NM>(s1, v);
-    if (tz >= 3) tree_merge<NM>(s2, v);
-    if (tz >= 4) tree_merge<NM>(s3, v);
+    if constexpr (LV > 2) if (tz >= 2) tree_merge<NM>(s1, v);
+    if constexpr (LV > 3) if (tz >= 3) tree_merge<NM>(s2, v);
+    if constexpr (LV > 4) if (tz >= 4) tree_merge<NM>(s3, v);
     switch (tz) {
       case 0: tree_set<NM>(s0, v); break;
-      case 1: tree_set<NM>(s1, v); break;
-      case 2: tree_set<NM>(s2, v); break;
-      case 3: tree_set<NM>(s3, v); break;
-      default: tree_set<NM>(s4, v); break;
+      case 1: if constexpr (LV > 1) tree_set<NM>(s1, v); break;
+      case 2: if constexpr (LV > 2) tree_set<NM>(s2, v); break;
+      case 3: if constexpr (LV > 3) tree_set<NM>(s3, v); break;
+      default: if constexpr (LV > 4) tree_set<NM>(s4, v); break;
     }
   }
   // the root: the level of N's single bit
   switch (N) {
     case 1: tree_set<NM>(out, s0); break;
-    case 2: tree_set<NM>(out, s1); break;
-    case 4: tree_set<NM>(out, s2); break;
-    case 8: tree_set<NM>(out, s3); break;
-    default: tree_set<NM>(out, s4); break;
+    case 2: if constexpr (LV > 1) tree_set<NM>(out, s1); break;
+    case 4: if constexpr (LV > 2) tree_set<NM>(out, s2); break;
+    case 8: if constexpr (LV > 3) tree_set<NM>(out, s3); break;
+    default: if constexpr (LV > 4) tree_set<NM>(out, s4); break;
   }
 }
 
@@ -283,7 +286,10 @@ __device__ __forceinline__ bool i8_rows(const uint8_t* const (&mats)[NM], long r
   while (TP < T && TP < 64) TP <<= 1;
   const int N = TP / kBWaves, p0 = wave * N;
   double c[NM][4];
-  i8_subtree<TYPE, NM>(mats, rb, nr, T, p0, N, codes8, ds, c);
+  // up to 8 positions per wave (rows of up to 2048 K-quant elements) hold
+  // four tree levels; more take the fifth
+  if (N <= 8) i8_subtree<TYPE, NM, 4>(mats, rb, nr, T, p0, N, codes8, ds, c);
+  else i8_subtree<TYPE, NM, 5>(mats, rb, nr, T, p0, N, codes8, ds, c);
 #pragma unroll
   for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
@@ -516,6 +522,7 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
     const int f0 = fb;
     const int nr = min(kBRows, Fx - f0);
     const int nb = H / 32;
+    const long act_slot = (nb * kQ81Bytes + 1023) & ~1023L;   // a staged token's Q8_1 row, KiB-aligned
     double* buf = reinterpret_cast<double*>(smem);
     const int j = blockIdx.z;
     if (16 * j >= gp.ne) return;
@@ -540,7 +547,7 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
         uint8_t* wst = smem + kI8Lds;
         uint8_t* xst = wst + 2L * kBRows * rbw;
         if (a.stage_dma) {
-          // the rows stream in while the threads copy the activations below
+          // the rows stream in, the activations behind them
           dma_to_lds(wst, src0, (uint32_t)(nr * rbw));
           dma_to_lds(wst + kBRows * rbw, src1, (uint32_t)(nr * rbw));
         } else {
@@ -548,33 +555,18 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
           copy_to_lds(wst + kBRows * rbw, src1, nr * rbw);
         }
         __syncthreads();   // s_tok
-        // the tile's activations, token after token: four 16-byte words per
-        // thread in flight before any is stored
-        const int nx = (int)(((long)nb * kQ81Bytes) >> 4), nxt = nm * nx;
-        for (int base = 0; base < nxt; base += 4 * kBThreads) {
-          uint4 v[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = base + u * kBThreads + (int)threadIdx.x;
-            if (i < nxt) {
-              const int c = i / nx;
-              v[u] = reinterpret_cast<const uint4*>(a.xq + (long)s_tok[c] * nb * kQ81Bytes)[i - c * nx];
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = base + u * kBThreads + (int)threadIdx.x;
-            if (i < nxt) reinterpret_cast<uint4*>(xst)[i] = v[u];
-          }
-        }
-        if (a.stage_dma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // the tile's activations streamed the same way, token c's Q8_1 row
+        // into its own KiB-aligned slot (the DMA pads each row to whole KiB)
+        for (int c = 0; c < nm; ++c)
+          dma_to_lds(xst + (long)c * act_slot, a.xq + (long)s_tok[c] * nb * kQ81Bytes, (uint32_t)(nb * kQ81Bytes));
+        wait_vmem();
         w0 = wst;
         w1 = wst + kBRows * rbw;
         xq0 = xst;
         staged = true;
       }
       __syncthreads();
-      auto tokoff = [&](int c) -> long { return (long)(staged ? c : s_tok[c]) * nb * kQ81Bytes; };
+      auto tokoff = [&](int c) -> long { return staged ? (long)c * act_slot : (long)s_tok[c] * nb * kQ81Bytes; };
       const int cl = lane & 15;
       const bool mv = cl < nm;
       const uint8_t* xqt = xq0 + (mv ? tokoff(cl) : 0);
@@ -916,7 +908,7 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   const size_t lds_gu = small > 0 ? int_path_lds(small > n ? n : small, H) : 0;
   // matrix-core groups stage their rows (and gate/up activations) in LDS when they fit
   const long rbw_max = std::max(row_bytes(MOE_TYPE_Q4_K, H), has_sg ? row_bytes(st_type, H) : 0L);
-  const size_t gu_stage = 2 * kBRows * (size_t)rbw_max + 16 * (size_t)(H / 32) * kQ81Bytes;
+  const size_t gu_stage = 2 * kBRows * (size_t)rbw_max + 16 * (((size_t)(H / 32) * kQ81Bytes + 1023) & ~(size_t)1023);
   a.stage_gu = kI8Lds + gu_stage <= kStageLdsMax && (reinterpret_cast<uintptr_t>(xq) & 15) == 0;
   const size_t lds_gu_big = kI8Lds + (a.stage_gu ? gu_stage : 0);
   // streamed rows write whole KiB chunks: a block of kBRows rows must end on
