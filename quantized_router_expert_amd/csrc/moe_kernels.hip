@@ -450,17 +450,29 @@ __device__ __forceinline__ void stage_to_lds(uint8_t* dst, const uint8_t* src, l
 }
 
 // Q8_1 activations (global, 36-byte blocks) -> LDS codes/d/s.
-__device__ void load_act_lds(const uint8_t* xq, int K, uint8_t* codes, float* d, float* s, int nthreads) {
-  const int nb = K / 32;
-  for (int i = threadIdx.x; i < nb * 8; i += nthreads) {
-    const int b = i >> 3, t = i & 7;
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(xq + (long)b * kQ81Bytes + 4 + 4 * t);
-    reinterpret_cast<uint32_t*>(codes)[i] = v;
-  }
-  for (int b = threadIdx.x; b < nb; b += nthreads) {
-    const uint32_t ds = *reinterpret_cast<const uint32_t*>(xq + (long)b * kQ81Bytes);
-    d[b] = f16_to_f32(ds);
-    s[b] = f16_to_f32(ds >> 16);
+__device__ void load_act_lds(const uint8_t* xq, int K, uint8_t* codes, float* d, float* s, int t0, int nthreads) {
+  // the K/32 blocks are 9 dwords each (d|s, then 8 of codes): thread t0 + i
+  // takes dwords i, i + nthreads, ..., four loads in flight before any store
+  // (a dword past the end reads the last one again and is not stored)
+  const int nb = K / 32, ndw = nb * 9;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(xq);
+  for (int i0 = t0; i0 < ndw; i0 += 4 * nthreads) {
+    uint32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = src[min(i0 + u * nthreads, ndw - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * nthreads;
+      if (i < ndw) {
+        const int b = i / 9, o = i - 9 * b;
+        if (o == 0) {
+          d[b] = f16_to_f32(v[u]);
+          s[b] = f16_to_f32(v[u] >> 16);
+        } else {
+          reinterpret_cast<uint32_t*>(codes)[8 * b + o - 1] = v[u];
+        }
+      }
+    }
   }
 }
 
@@ -558,6 +570,8 @@ __global__ __launch_bounds__(kFfnThreads) void k_gate_up(GateUpArgs a) {
     nr = min(a.R, a.F - f0);
     __shared__ int32_t s_ids[MOE_MAX_TOPK];
     __shared__ float s_wts[MOE_MAX_TOPK];
+    // waves 1..3 read the activations while wave 0 selects
+    if (!a.ids && wave > 0) load_act_lds(a.xq, H, codes, dact, sact, threadIdx.x - 64, blockDim.x - 64);
     if (!a.ids) {   // the selection, from the logits of the router launch
       if (wave == 0) {
         wave_topk_softmax(a.logits, a.E, a.k, s_ids, s_wts);
@@ -587,7 +601,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_gate_up(GateUpArgs a) {
     stage_async(stage + up_off, a.sup + f0 * rb, (uint32_t)(nr * rb), wave, 0, kFfnThreads / 64);
     h_out = a.hs + f0;
   }
-  load_act_lds(a.xq, H, codes, dact, sact, blockDim.x);
+  if (!routed || a.ids) load_act_lds(a.xq, H, codes, dact, sact, threadIdx.x, blockDim.x);
   wait_vmem();
   __syncthreads();
   ActLds act{codes, dact, sact};
@@ -683,7 +697,7 @@ __device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
   const bool vec_h = (((uintptr_t)a.h | (uintptr_t)(a.Fs > 0 ? a.hs : nullptr)) & 15) == 0;
   if (vec_h) {
     const int nbk = Kp / 32, F = a.F, Fs = a.Fs;
-    quantize_q81_groups<4, 2>(
+    quantize_q81_groups<4, 3>(
         a.k * nbk, a.h,
         [nbk, F](int j) {
           const int s = j / nbk, jj = j - s * nbk;
@@ -783,7 +797,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_subblock_dots(const uint8_t* ro
   float* d = reinterpret_cast<float*>(smem + K);
   float* s = d + K / 32;
   uint8_t* stage = reinterpret_cast<uint8_t*>((((uintptr_t)(s + K / 32)) + 15) & ~(uintptr_t)15);
-  load_act_lds(xq, K, codes, d, s, blockDim.x);
+  load_act_lds(xq, K, codes, d, s, threadIdx.x, blockDim.x);
   const long rb = row_bytes(type, K);
   stage_to_lds(stage, rows + blockIdx.x * rb, rb, blockDim.x);
   __syncthreads();
