@@ -243,7 +243,7 @@ __device__ void wave_topk_softmax_n(const float* logits, int E, int k, int32_t* 
   }
 }
 // keys per lane from the expert count (the scan is the same, over fewer keys)
-__device__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* ids_out, float* w_out) {
+__device__ __forceinline__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* ids_out, float* w_out) {
   static_assert(kTopkPerLane == 16, "dispatch below covers up to 16 keys per lane");
   if (E <= 64) wave_topk_softmax_n<1>(logits, E, k, ids_out, w_out);
   else if (E <= 128) wave_topk_softmax_n<2>(logits, E, k, ids_out, w_out);
@@ -670,12 +670,19 @@ __device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
   double* partial_s = partial + (long)a.k * a.Ro * T;
   float* y = reinterpret_cast<float*>(partial_s + (long)a.Ro * Ts);
 
-  // the routing weights and the gate are read now (they are needed only at the end)
+  // the ids, the routing weights and the gate, read at once into LDS (the
+  // row requests below are asm the compiler cannot move loads across: read
+  // there, each id would be a round trip of its own)
   __shared__ float s_wts[MOE_MAX_TOPK], s_sg;
-  if (threadIdx.x < a.k) s_wts[threadIdx.x] = a.wts[threadIdx.x];
+  __shared__ int32_t s_ids[MOE_MAX_TOPK];
+  if (threadIdx.x < a.k) {
+    s_ids[threadIdx.x] = a.ids[threadIdx.x];
+    s_wts[threadIdx.x] = a.wts[threadIdx.x];
+  }
   if (threadIdx.x == 0) s_sg = a.Fs > 0 ? a.sg[0] : 0.0f;
+  __syncthreads();
   bool bad_id = false;
-  for (int s = 0; s < a.k; ++s) bad_id |= (a.ids[s] < 0 || a.ids[s] >= a.E);
+  for (int s = 0; s < a.k; ++s) bad_id |= (s_ids[s] < 0 || s_ids[s] >= a.E);
   if (bad_id) {  // an id outside the experts reads nothing and yields NaN outputs
     for (int r = threadIdx.x; r < nr; r += blockDim.x) {
       a.routed[i0 + r] = 0x7fc0u;
@@ -686,7 +693,7 @@ __device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
 
   // stream the weight rows into LDS first so they are in flight during the quantisation
   for (int s = 0; s < a.k; ++s) {
-    const long e = a.ids[s];
+    const long e = s_ids[s];
     stage_async(stage + (long)s * slot_bytes, a.down + (e * a.H + i0) * rb, (uint32_t)(nr * rb), wave, 0,
                 kFfnThreads / 64);
   }
