@@ -12,7 +12,7 @@ namespace moe {
 constexpr int kNormThreads = 256;
 constexpr int kRouterThreads = 512;
 constexpr int kRouterTok = 8;      // tokens per router workgroup (a row is read once for them)
-constexpr int kFfnThreads = 256;
+constexpr int kFfnThreads = 512;
 constexpr int kTopkPerLane = MOE_MAX_EXPERTS / 64;
 constexpr int kCounterSlots = 4096;
 constexpr int kGateUpRows = 16;
