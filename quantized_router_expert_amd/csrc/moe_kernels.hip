@@ -199,37 +199,44 @@ __global__ __launch_bounds__(kNormThreads) void k_quantize_q81(const float* x, i
 // =====================================================================
 // a2 + a3: router GEMV + last-workgroup top-k + routing weights
 // =====================================================================
-// Orderable 64-bit key: larger key = larger logit, ties broken toward the lower
-// index.  -0 is canonicalised to +0 (IEEE equality ties them) and NaN to -inf.
-__device__ __forceinline__ unsigned long long topk_key(float v, int e) {
+// Wave-level top-k over E <= 64*NPL logits held in memory.  Each lane keeps
+// its NPL 32-bit order keys (expert e = lane + 64j in slot j); a round takes
+// the wave-wide maximum key and, among the experts holding it, the lowest
+// index (the first slot j with a match, then its first lane), so slots come in
+// rank order with ties to the lower index.  A taken key becomes 0, below
+// every real key.  The order key: -0 counts as +0 (IEEE equality ties them)
+// and NaN as -inf.
+__device__ __forceinline__ uint32_t order_key(float v) {
   if (v != v) v = -__builtin_inff();
   if (v == 0.0f) v = 0.0f;
-  uint32_t b = __float_as_uint(v);
-  uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((unsigned long long)o << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);   // never 0 for a real value
 }
-
-// Wave-level top-k over E <= 64*NPL logits held in memory.  Each lane keeps
-// its NPL keys; k rounds of a wave-wide 64-bit max pick the slots in rank order.
 template <int NPL>
 __device__ void wave_topk_softmax_n(const float* logits, int E, int k, int32_t* ids_out, float* w_out) {
   const int lane = threadIdx.x & 63;
-  unsigned long long key[NPL];
+  uint32_t key[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int e = lane + 64 * j;
-    key[j] = (e < E) ? topk_key(logits[e], e) : 0ull;
+    key[j] = (e < E) ? order_key(logits[e]) : 0u;
   }
   int my_id = 0;   // lane s < k: the id of slot s
   for (int s = 0; s < k; ++s) {
-    unsigned long long best = 0ull;
+    uint32_t best = key[0];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) best = key[j] > best ? key[j] : best;
-    const unsigned long long wbest = wave_max_u64(best);
+    for (int j = 1; j < NPL; ++j) best = max(best, key[j]);
+    const uint32_t wbest = wave_max_u32(best);
+    int win = -1;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const unsigned long long m = __ballot(key[j] == wbest);
+      if (win < 0 && m != 0ull) win = 64 * j + __ffsll((long long)m) - 1;
+    }
 #pragma unroll
     for (int j = 0; j < NPL; ++j)
-      if (key[j] == wbest) key[j] = 0ull;
-    if (lane == s) my_id = (int32_t)(0xffffffffu - (uint32_t)(wbest & 0xffffffffull));
+      if (win == lane + 64 * j) key[j] = 0u;
+    if (lane == s) my_id = win;
   }
   // softmax over the selected logits, shifted by the largest (slot 0), fp64:
   // lane s takes slot s's exponential, every lane sums them in slot order
@@ -559,10 +566,12 @@ __global__ __launch_bounds__(kFfnThreads) void k_gate_up(GateUpArgs a) {
   float* sact = dact + H / 32;
   int nr, f0;
   float* h_out;
-  if (a.out_sum) {   // this workgroup's slice of the folded residual sum
+  constexpr int kLastWave = kFfnThreads / 64 - 1;
+  if (a.out_sum && wave == kLastWave) {   // this workgroup's slice of the folded residual sum (the last
+    // wave: wave 0's loads are the selection's)
     const int cs = (H + gridDim.x - 1) / gridDim.x;
     const int iend = min(H, (b + 1) * cs);
-    for (int i = b * cs + threadIdx.x; i < iend; i += blockDim.x) a.out_sum[i] = fold_elem(a.res, a.rt, a.sh, i);
+    for (int i = b * cs + (threadIdx.x & 63); i < iend; i += 64) a.out_sum[i] = fold_elem(a.res, a.rt, a.sh, i);
   }
   if (routed) {
     const int slot = b / a.cpe;
