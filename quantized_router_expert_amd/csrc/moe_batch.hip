@@ -374,7 +374,6 @@ constexpr int kBSmallPerWave = 4;                       // rows per wave, small 
 constexpr int kBSmallRows = kBSmallPerWave * kBWaves;   // rows per block, small groups (gate/up)
 static_assert(kBRows % kBSmallRows == 0, "a big group's block spans whole small-group blocks");
 constexpr int kBigSpan = kBRows / kBSmallRows;              // gate/up: small-group blocks per big-group block
-constexpr int kDnSpan = kBRowsPerBlock / kBRows;            // down: 16-row units per small-group block
 
 template <int TYPE>
 __device__ __forceinline__ void row_task_multi(const uint8_t* row, int t, const ActLds* acts, int ne, double v[kMulti]) {
@@ -504,7 +503,7 @@ template <int ST, bool BIG>
 __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Group gp;
-  if (!block_group<false>(a, gp)) return;
+  if (!block_group<BIG>(a, gp)) return;
   const int Fx = gp.shared ? a.Fs : a.F;
   const bool big = gp.ne >= a.gmin;
   if (big != BIG) return;
@@ -675,11 +674,9 @@ __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool big = gp.ne >= a.gmin;
   if (big != BIG) return;
-  // blockIdx.y counts kBRows-row chunks: a big group's block takes one (its
-  // waves split K), a small group's block kDnSpan of them, kBRows rows per
-  // wave (the other blocks of its span leave at once)
-  if (!big && (blockIdx.y % kDnSpan)) return;
-  const int i0 = big ? blockIdx.y * kBRows : (blockIdx.y / kDnSpan) * kBRowsPerBlock + wave * kBRows;
+  // blockIdx.y: a big group's block takes kBRows rows (its waves split K), a
+  // small group's block kBRowsPerBlock rows (kBRows per wave)
+  const int i0 = BIG ? blockIdx.y * kBRows : blockIdx.y * kBRowsPerBlock + wave * kBRows;
   if (big && i0 >= H) return;
   const int nr = max(0, min(kBRows, H - i0));
   const int Fx = gp.shared ? a.Fs : a.F;
@@ -924,10 +921,11 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
       if (hipFuncSetAttribute(fs_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu) != hipSuccess) return MOE_ERR_HIP;
       if (hipLaunchKernel(fs_, ggu, dim3(kBThreads), args, lds_gu, st) != hipSuccess) return MOE_ERR_HIP;
     }
-    // z: tiles of 16 tokens.  x spans every group: this instance runs one
-    // workgroup per CU, and the compact list of big groups (as for down)
-    // packed its few real workgroups together and measured slower
-    const dim3 ggu_big(ngroups, ggu.y, (n + 15) / 16);
+    // x: the groups of group_min or more tokens (the compact list, as for
+    // down), z: tiles of 16 tokens.  A grid over every group spent most of
+    // the kernel dispatching workgroups that leave at once, one per CU at
+    // this instance's LDS size
+    const dim3 ggu_big(ngroups_big, ggu.y, (n + 15) / 16);
     if (any_big) {
       if (hipFuncSetAttribute(fb_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu_big) != hipSuccess)
         return MOE_ERR_HIP;
@@ -956,7 +954,8 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   }
   if (small > 0) {
     if (hipFuncSetAttribute(fds, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn) != hipSuccess) return MOE_ERR_HIP;
-    if (hipLaunchKernel(fds, gdn, dim3(kBThreads), args, lds_dn, st) != hipSuccess) return MOE_ERR_HIP;
+    const dim3 gdn_small(ngroups, (H + kBRowsPerBlock - 1) / kBRowsPerBlock);
+    if (hipLaunchKernel(fds, gdn_small, dim3(kBThreads), args, lds_dn, st) != hipSuccess) return MOE_ERR_HIP;
   }
   if (any_big) {
     if (hipFuncSetAttribute(fdb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn_big) != hipSuccess)
