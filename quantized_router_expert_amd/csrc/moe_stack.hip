@@ -684,7 +684,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   // phases.  (Were a launch ever placed otherwise, some part would go
   // missing and the waits for it would stop the launch at their bound.)
   const uint32_t xcc = XS ? xcc_id() : 0u;
-  const uint32_t rd_t = XS ? xcc * rb_t : 0u, rd_lg = x_lg + (b % kRepLg) * rb_lg,
+  const uint32_t rd_t = XS ? xcc * rb_t : 0u,
                  rd_h = x_h + (b % kRepH) * rb_h;
 
   const long rb_gu = row_bytes(MOE_TYPE_Q4_K, H);
@@ -702,10 +702,37 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   // XS: this workgroup's down rows (and combine rows) [dr0, dr0 + RDX)
   constexpr int RDX = XS ? fs.H / (fs.G / kXcc) : 0;
   const int dr0 = (b / kXcc) * RDX;
+  // PD (XS with at most 4 router rows per workgroup): the router per die.
+  // The 32 workgroups of die x compute all E logits (workgroup (x, j) rows j,
+  // j + 32, ...; the shared-gate row too when j == 0) and exchange them within
+  // the die, in its copy of the logits area, instead of across the dies.  The
+  // rows stream into the router row area, then the routed gate/up and down
+  // areas, which are idle from the end of a layer to the next one's
+  // selection.  Each die then reads the whole router matrix: measured, this
+  // pays at 4 rows per workgroup (128 experts: 698 -> 666 us per 48-layer
+  // token) and not at 8 (256 experts: 525 -> 837 us per 40-layer token, the
+  // 18 MB of router rows per layer stalling the row streams).
+  constexpr int kRowsPD = XS ? fs.E / (fs.G / kXcc) : 0;
+  constexpr bool PD = XS && kRowsPD <= 4;
+  constexpr StackGeom gx = kFixGeom<DT, ST, S>;
+  constexpr int kRowB = PD ? fs.H * 4 : 1;
+  constexpr int kCapR = PD ? (gx.o_sgu - gx.o_rrow) / kRowB : 0, kCapG = PD ? (gx.o_rdn - gx.o_rgu) / kRowB : 0,
+                kCapD = PD ? (gx.o_hqc - gx.o_rdn) / kRowB : 0;
+  static_assert(!PD || (gx.o_sgu > gx.o_rrow && gx.o_rdn > gx.o_rgu && gx.o_hqc > gx.o_rdn), "router row areas");
+  static_assert(!PD || kCapR + kCapG + kCapD >= kRowsPD + 1, "the router rows of a die's workgroup fit");
+  static_assert(!PD || (fs.E % (fs.G / kXcc) == 0 && kRepLg == kXcc), "router per die");
+  const int jd = XS ? b / kXcc : 0;                          // the workgroup's index within its die
+  const int nrows_pd = PD ? kRowsPD + ((jd == 0 && has_sg) ? 1 : 0) : 0;
+  // the logits copy this workgroup reads: its die's (PD), else copy b % R
+  const uint32_t rd_lg = x_lg + (PD ? xcc : (uint32_t)(b % kRepLg)) * rb_lg;
+  auto router_slot = [&](int m) -> uint8_t* {
+    return m < kCapR ? rrow + (long)m * kRowB
+                     : (m < kCapR + kCapG ? rgu + (long)(m - kCapR) * kRowB : rdn + (long)(m - kCapR - kCapG) * kRowB);
+  };
   // weights that do not depend on the routing decision, for layer `w`
   auto prefetch_fixed = [&](const LayerPtrs& w) {
     stage_async(smem + g.o_nw, w.norm_w, (uint32_t)(H * 4), wave, kPollWaves, kStackWaves - kPollWaves);
-    for (int j = 0; j < g.RR; ++j) {
+    for (int j = 0; !PD && j < g.RR; ++j) {
       const int r = b + j * g.G;
       const float* src = (r < E) ? w.router_w + (long)r * H : ((r == E && has_sg) ? w.shared_gate_w : nullptr);
       if (src) stage_async(rrow + (long)j * H * 4, src, (uint32_t)(H * 4), wave, kPollWaves, kStackWaves - kPollWaves);
@@ -719,6 +746,11 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     if (has_sg && nrd > 0)
       stage_async(sdn, w.shared_down + row0 * rb_sdn, (uint32_t)(nrd * rb_sdn), wave, kPollWaves,
                   kStackWaves - kPollWaves);
+    // PD: the router rows last, so that the norm can wait for the rest alone
+    for (int m = 0; PD && m < nrows_pd; ++m) {
+      const float* src = (m < kRowsPD) ? w.router_w + (long)(jd + (fs.G / kXcc) * m) * H : w.shared_gate_w;
+      stage_async(router_slot(m), src, (uint32_t)(H * 4), wave, kPollWaves, kStackWaves - kPollWaves);
+    }
   };
 
   uint64_t* trace = reinterpret_cast<uint64_t*>(a.ws + a.g.w_trace);
@@ -783,7 +815,17 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     // ================= phase A: norm, router rows, shared gate/up rows
     stamp(l, 1);
     bstamp(l, 1);
-    if (wave >= kPollWaves) wait_vmem();
+    if (wave >= kPollWaves) {
+      if constexpr (PD) {
+        // everything but the router rows (the last requests: two KiB per row
+        // from each of the four issuing waves) has landed
+        static_assert(fs.H * 4 == 1024 * (kStackWaves - kPollWaves) * 2, "two KiB per router row and wave");
+        if (nrows_pd > kRowsPD) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (kRowsPD + 1)) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kRowsPD) : "memory");
+      } else {
+        wait_vmem();
+      }
+    }
     if (a.attn) {
       // the post-attention add: u2 = bf16(u1 + attn), once every t word and
       // the attention output are in
@@ -820,6 +862,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       o.w = (float)(((double)r.w * rinv) * (double)wv.w);
       reinterpret_cast<float4*>(xn)[c] = o;
     }
+    if (PD && wave >= kPollWaves) wait_vmem();   // the router rows
     lds_barrier();
     bstamp(l, 11);
     // xq on waves 0..3 while waves 4.. take the router rows, which need xn only
@@ -827,8 +870,29 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       quantize_q81_groups<4, 1>(H / 32, xn, [](int j) { return 32 * j; }, [&](int j) { return xqc + 32 * j; }, xqd,
                                 xqs, tid, 64 * kPollWaves);
     bstamp(l, 12);
+    // PD: this workgroup's router rows of its die (fp64 dot of fp32 products),
+    // one wave per row; the logits go to the die's copy with plain stores
+    for (int m = wave - kPollWaves; PD && m >= 0 && m < nrows_pd; m += kStackWaves - kPollWaves) {
+      const float* wr = reinterpret_cast<const float*>(router_slot(m));
+      double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+#pragma unroll 4
+      for (int i = (tid & 63) * 4; i < H; i += 256) {
+        const float4 wv = *reinterpret_cast<const float4*>(wr + i);
+        const float4 xv = *reinterpret_cast<const float4*>(xn + i);
+        a0 += (double)wv.x * (double)xv.x;
+        a1 += (double)wv.y * (double)xv.y;
+        a2 += (double)wv.z * (double)xv.z;
+        a3 += (double)wv.w * (double)xv.w;
+      }
+      const double acc = wave_sum_f64((a0 + a1) + (a2 + a3));
+      const int r = (m < kRowsPD) ? jd + (fs.G / kXcc) * m : E;
+      if ((tid & 63) == 0) {
+        const v2u v = {__float_as_uint((float)acc), ep0};
+        __builtin_amdgcn_raw_buffer_store_b64(v, rx, 8u * (uint32_t)r, x_lg + xcc * rb_lg, 0);
+      }
+    }
     // router rows (fp64 dot of fp32 products), one wave per row
-    for (int j = wave - kPollWaves; j >= 0 && j < g.RR; j += kStackWaves - kPollWaves) {
+    for (int j = wave - kPollWaves; !PD && j >= 0 && j < g.RR; j += kStackWaves - kPollWaves) {
       const int r = b + j * g.G;
       const bool real = (r < E) || (r == E && has_sg);
       if (!real) break;
