@@ -116,6 +116,7 @@ class Stack:
         """One HIP graph per token input (4 kernels per layer + the final fold)."""
         s = torch.cuda.Stream()
         self.stream = s
+        torch.cuda.synchronize()   # the inputs are made on the default stream
         with torch.cuda.stream(s):
             self.run_eager(0, self.q.MOE_STACK_KERNELS)
         s.synchronize()
@@ -177,6 +178,7 @@ def layer_leg(q, n_inputs=128, repeats=5):
                     "routed_out": torch.empty(H, dtype=torch.bfloat16, device="cuda"),
                     "shared_out": torch.empty(H, dtype=torch.bfloat16, device="cuda")})
     s = torch.cuda.Stream()
+    torch.cuda.synchronize()   # the inputs are made on the default stream
     with torch.cuda.stream(s):
         q.moe_decode_layer(desc, lw, ios[0], ws)
     s.synchronize()
@@ -275,49 +277,75 @@ def require_status_ok(q, stack, what):
         sys.exit(1)
 
 
-def batch_leg(q, sizes=(8, 32), group_min=9, iters=30):
-    """The grouped batch path on one layer of the 40-layer shape: per batch
-    size, microseconds per layer step (norm, router, grouped experts, combine)
-    over `iters` steps on fresh seeded inputs, tokens/s, and GB/s over the
-    bytes the step must read (router, shared expert, each distinct selected
-    expert once).  group_min 9: groups of 9 or more tokens take the int8
-    matrix cores, whose tile is 16 tokens (a smaller group would leave more
-    than half of it empty); the measured best at batch 8 and 32 among 4, 6,
-    9, 12 and 16."""
+def batch_leg(q, sizes=(8, 32), group_min=9, n_layers=6, rounds=5):
+    """The grouped batch path on layers of the 40-layer shape: per batch size,
+    microseconds per layer step (norm, router, grouped experts, combine), with
+    `n_layers` layers, each with its own weights and its own seeded batch
+    (inputs ~N(0,1), a quarter of the tokens steered to two experts of that
+    layer), one HIP graph per layer step, replayed in layer order `rounds`
+    times.  A layer's weights come back only after the other layers' steps
+    (at least 5 x 108 MB at batch 8), more than the 256 MB last-level cache
+    holds, as in a decode step where each layer's weights are read once.
+    Reports tokens/s and GB/s over the bytes a step must read (router, shared
+    expert, each distinct selected expert once; averaged over the layers).
+    group_min 9: groups of 9 or more tokens take the int8 matrix cores, whose
+    tile is 16 tokens (a smaller group would leave more than half of it
+    empty); the measured best at batch 8 and 32 among 4, 6, 9, 12 and 16."""
     cfg = wl.CONFIGS["batch"]
-    W = wl.layer_weights(cfg, 0, "cuda")
     H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
     desc = q.make_desc(H, E, k, F, Fs, eps=cfg.eps)
+    Ws = [wl.layer_weights(cfg, l, "cuda") for l in range(n_layers)]
+    lws = [q.make_weights(W) for W in Ws]
     per_expert = 2 * F * wl.row_bytes(wl.Q4_K, H) + H * wl.row_bytes(wl.Q4_K, wl.pad_k(wl.Q4_K, F))
     fixed = 4 * E * H + 4 * H + 4 * H + 2 * Fs * wl.row_bytes(wl.Q4_K, H) + H * wl.row_bytes(wl.Q4_K, Fs)
     out = {}
+    s = torch.cuda.Stream()
     for n in sizes:
         ws = q.alloc_batch_workspace(desc, n)
-        inp, _, _ = wl.batch_inputs(cfg, n, "cuda")
-        res = inp["residual"].contiguous()
-        io = {"residual": res, "routed_in": inp["routed_prev"].contiguous(),
-              "shared_in": inp["shared_prev"].contiguous(),
-              "out_sum": torch.empty(n, H, dtype=torch.bfloat16, device="cuda"),
-              "routed_out": torch.empty(n, H, dtype=torch.bfloat16, device="cuda"),
-              "shared_out": torch.empty(n, H, dtype=torch.bfloat16, device="cuda"),
-              "ids": torch.empty(n, k, dtype=torch.int32, device="cuda")}
-        q.moe_decode_layer_batch(desc, W, io, n, group_min, ws)
+        ios = []
+        for l in range(n_layers):
+            inp, _, _ = wl.batch_inputs(cfg, n, "cuda", layer=l)
+            ios.append({"residual": inp["residual"].contiguous(), "routed_in": inp["routed_prev"].contiguous(),
+                        "shared_in": inp["shared_prev"].contiguous(),
+                        "out_sum": torch.empty(n, H, dtype=torch.bfloat16, device="cuda"),
+                        "routed_out": torch.empty(n, H, dtype=torch.bfloat16, device="cuda"),
+                        "shared_out": torch.empty(n, H, dtype=torch.bfloat16, device="cuda"),
+                        "ids": torch.empty(n, k, dtype=torch.int32, device="cuda")})
+        torch.cuda.synchronize()   # the inputs are made on the default stream
+        with torch.cuda.stream(s):
+            for l in range(n_layers):
+                q.moe_decode_layer_batch(desc, lws[l], ios[l], n, group_min, ws)
+        s.synchronize()
+        graphs = []
+        for l in range(n_layers):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                q.moe_decode_layer_batch(desc, lws[l], ios[l], n, group_min, ws)
+            graphs.append(g)
         torch.cuda.synchronize()
-        distinct = len(set(io["ids"].flatten().tolist()))
+        for g in graphs:
+            g.replay()
         stream = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(iters):
-            q.moe_decode_layer_batch(desc, W, io, n, group_min, ws)
+        for _ in range(rounds):
+            for g in graphs:
+                g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / iters
-        nbytes = fixed + distinct * per_expert
+        us = e0.elapsed_time(e1) * 1e3 / (rounds * n_layers)
+        distinct = [len(set(io["ids"].flatten().tolist())) for io in ios]   # as the replays selected
+        nbytes = fixed + float(np.mean(distinct)) * per_expert
         out[f"batch{n}"] = {"us_per_layer_step": us, "tokens_per_s_per_layer": n * 1e6 / us,
-                            "distinct_experts": distinct, "bytes_per_step": nbytes,
-                            "achieved_GBs": nbytes / (us * 1e-6) / 1e9, "group_min": group_min}
-        print(f"# batch {n}: {us:.1f} us per layer step, {distinct} distinct experts, "
-              f"{out[f'batch{n}']['achieved_GBs']:.0f} GB/s", file=sys.stderr, flush=True)
+                            "distinct_experts_mean": float(np.mean(distinct)), "distinct_experts": distinct,
+                            "bytes_per_step": nbytes, "achieved_GBs": nbytes / (us * 1e-6) / 1e9,
+                            "group_min": group_min, "layers_rotated": n_layers}
+        print(f"# batch {n}: {us:.1f} us per layer step over {n_layers} layers, {np.mean(distinct):.1f} distinct "
+              f"experts per layer, {out[f'batch{n}']['achieved_GBs']:.0f} GB/s", file=sys.stderr, flush=True)
+        del graphs, ws
+    del Ws, lws
+    torch.cuda.empty_cache()
     return out
 
 

@@ -365,31 +365,31 @@ __device__ __forceinline__ void member(const BGroupArgs& a, const Group& gp, int
 
 // ---------------------------------------------------------------- integer rows for several tokens
 // A small group's members share the expert's rows: each task's weights are
-// read once and dotted with up to kMulti members' Q8_1 activations.  Each
-// member's value is the single-token row_task value, summed in the same
+// read and decoded once and dotted with every member's Q8_1 activations.
+// Each member's value is the single-token row_task value, summed in the same
 // order (task t, t+64, ..., then the lane-group tree), so it is bit-identical
 // to running the rows once per member.
-constexpr int kMulti = 4;
 constexpr int kBSmallPerWave = 4;                       // rows per wave, small groups
 constexpr int kBSmallRows = kBSmallPerWave * kBWaves;   // rows per block, small groups (gate/up)
 static_assert(kBRows % kBSmallRows == 0, "a big group's block spans whole small-group blocks");
 constexpr int kBigSpan = kBRows / kBSmallRows;              // gate/up: small-group blocks per big-group block
 
+// A task's weight side, decoded once for all the members that use it: the
+// int8 codes of its two sub-blocks (Q4_K nibbles; Q5_K with the fifth bit
+// added) or of its Q8_0 block, and the fp64 factors the single-token task
+// multiplies by (d*sc and dmin*m per sub-block; d for Q8_0).  task_member()
+// then gives exactly row_task()'s value for one member's activations.
 template <int TYPE>
-__device__ __forceinline__ void row_task_multi(const uint8_t* row, int t, const ActLds* acts, int ne, double v[kMulti]) {
+struct TaskW {
+  uint32_t lo[8], hi[8];
+  double s_lo, m_lo, s_hi, m_hi;
+};
+template <int TYPE>
+__device__ __forceinline__ void task_decode(const uint8_t* row, int t, TaskW<TYPE>& w) {
   if (TYPE == MOE_TYPE_Q8_0) {
     float d;
-    uint32_t w[8];
-    q80_load(row, t, d, w);
-#pragma unroll
-    for (int m = 0; m < kMulti; ++m) {
-      v[m] = 0.0;
-      if (m < ne) {
-        uint32_t av[8];
-        lds_load8(acts[m].codes + 32 * t, av);
-        v[m] = (double)d * (double)acts[m].d[t] * (double)q8_block_dot(w, av);
-      }
-    }
+    q80_load(row, t, d, w.lo);
+    w.s_lo = (double)d;
     return;
   }
   const int b = t >> 2, g = t & 3;
@@ -402,64 +402,88 @@ __device__ __forceinline__ void row_task_multi(const uint8_t* row, int t, const 
   } else {
     lds_load8(blk + 16 + 32 * g, qs);
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    w.lo[i] = qs[i] & 0x0f0f0f0fu;
+    w.hi[i] = (qs[i] >> 4) & 0x0f0f0f0fu;
+    if (TYPE == MOE_TYPE_Q5_K) {
+      w.lo[i] |= ((qh[i] >> (2 * g)) & 0x01010101u) << 4;
+      w.hi[i] |= ((qh[i] >> (2 * g + 1)) & 0x01010101u) << 4;
+    }
+  }
   int sclo, mlo, schi, mhi;
   kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g, sclo, mlo);
   kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g + 1, schi, mhi);
   const double d = (double)f16_to_f32(hdr.x);
   const double dmin = (double)f16_to_f32(hdr.x >> 16);
-  const int jlo = 8 * b + 2 * g;
-#pragma unroll
-  for (int m = 0; m < kMulti; ++m) {
-    v[m] = 0.0;
-    if (m < ne) {
-      uint32_t alo[8], ahi[8];
-      lds_load8(acts[m].codes + 32 * jlo, alo);
-      lds_load8(acts[m].codes + 32 * (jlo + 1), ahi);
-      int Dlo, Dhi;
-      kquant_group_dots<TYPE == MOE_TYPE_Q5_K>(qs, qh, g, alo, ahi, Dlo, Dhi);
-      const double t1 = d * (double)sclo * (double)acts[m].d[jlo] * (double)Dlo;
-      const double t2 = dmin * (double)mlo * (double)acts[m].s[jlo];
-      const double t3 = d * (double)schi * (double)acts[m].d[jlo + 1] * (double)Dhi;
-      const double t4 = dmin * (double)mhi * (double)acts[m].s[jlo + 1];
-      v[m] = ((t1 - t2) + t3) - t4;
-    }
+  w.s_lo = d * (double)sclo;
+  w.m_lo = dmin * (double)mlo;
+  w.s_hi = d * (double)schi;
+  w.m_hi = dmin * (double)mhi;
+}
+template <int TYPE>
+__device__ __forceinline__ double task_member(const TaskW<TYPE>& w, int t, const ActLds& act) {
+  if (TYPE == MOE_TYPE_Q8_0) {
+    uint32_t a[8];
+    lds_load8(act.codes + 32 * t, a);
+    return w.s_lo * (double)act.d[t] * (double)q8_block_dot(w.lo, a);
   }
+  const int jlo = 8 * (t >> 2) + 2 * (t & 3);
+  uint32_t alo[8], ahi[8];
+  lds_load8(act.codes + 32 * jlo, alo);
+  lds_load8(act.codes + 32 * (jlo + 1), ahi);
+  int lo[2] = {0, 0}, hi[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    lo[i & 1] = __builtin_amdgcn_sdot4((int)w.lo[i], (int)alo[i], lo[i & 1], false);
+    hi[i & 1] = __builtin_amdgcn_sdot4((int)w.hi[i], (int)ahi[i], hi[i & 1], false);
+  }
+  const double t1 = w.s_lo * (double)act.d[jlo] * (double)(lo[0] + lo[1]);
+  const double t2 = w.m_lo * (double)act.s[jlo];
+  const double t3 = w.s_hi * (double)act.d[jlo + 1] * (double)(hi[0] + hi[1]);
+  const double t4 = w.m_hi * (double)act.s[jlo + 1];
+  return ((t1 - t2) + t3) - t4;
 }
 
-// rows_dot for ne <= kMulti activation sets (ne wave-uniform): rowfn(r) gives
-// row r's bytes; out[r * kMulti + m] receives row r against set m.
+// Row values of nrows rows of one wave for each of ne members (lanes and
+// lane-group sums as in rows_dot: TP lanes per row, lane position p holding
+// tasks p, p+64, ...): out[r * ldo + m] = row r against member m.  The
+// members go one at a time (a run-time loop) over the task words decoded
+// once per row pass, so the registers do not grow with the group.  Member m's
+// Q8_1 codes are at codes + m*K, its block scales at dq/sq + m*(K/32).
 template <int TYPE, class RowFn>
-__device__ __forceinline__ void rows_dot_multi(int nrows, int T, RowFn rowfn, const ActLds* acts, int ne, double* out,
-                                               int wave, int nw) {
+__device__ __forceinline__ void rows_dot_members(int nrows, int T, RowFn rowfn, const uint8_t* codes, const float* dq,
+                                                 const float* sq, int K, int ne, double* out, int ldo) {
   int TP = 1;
   while (TP < T && TP < 64) TP <<= 1;
   const int rpi = 64 / TP;
   const int lane = threadIdx.x & 63;
   const int rl = lane / TP, t0 = lane - rl * TP;
-  const int step = nw * rpi;
   const int tt = (t0 < T) ? t0 : 0;
-  for (int r0 = wave * rpi; r0 < nrows; r0 += step) {
+  const int nbk = K / 32;
+  for (int r0 = 0; r0 < nrows; r0 += rpi) {
     const int ra = r0 + rl;
     const uint8_t* row = rowfn(ra < nrows ? ra : nrows - 1);
-    double v[kMulti];
-    row_task_multi<TYPE>(row, tt, acts, ne, v);
-    if (t0 >= T) {
-#pragma unroll
-      for (int m = 0; m < kMulti; ++m) v[m] = 0.0;
-    }
-    for (int t = t0 + 64; t < T; t += 64) {
-      double w[kMulti];
-      row_task_multi<TYPE>(row, t, acts, ne, w);
-#pragma unroll
-      for (int m = 0; m < kMulti; ++m) v[m] += w[m];
-    }
-#pragma unroll
-    for (int m = 0; m < kMulti; ++m)
-      if (m < ne) v[m] = group_sum_f64(v[m], TP);
-    if (t0 == 0 && ra < nrows) {
-#pragma unroll
-      for (int m = 0; m < kMulti; ++m)
-        if (m < ne) out[ra * kMulti + m] = v[m];
+    if (T <= 64) {   // one task per lane and row
+      TaskW<TYPE> w;
+      task_decode<TYPE>(row, tt, w);
+#pragma unroll 1
+      for (int m = 0; m < ne; ++m) {
+        const ActLds act{codes + (long)m * K, dq + m * nbk, sq + m * nbk};
+        double v = task_member<TYPE>(w, tt, act);
+        if (t0 >= T) v = 0.0;
+        v = group_sum_f64(v, TP);
+        if (t0 == 0 && ra < nrows) out[ra * ldo + m] = v;
+      }
+    } else {         // tasks t0, t0 + 64, ... summed in that order
+#pragma unroll 1
+      for (int m = 0; m < ne; ++m) {
+        const ActLds act{codes + (long)m * K, dq + m * nbk, sq + m * nbk};
+        double v = row_task<TYPE>(row, t0, act);
+        for (int t = t0 + 64; t < T; t += 64) v += row_task<TYPE>(row, t, act);
+        v = group_sum_f64(v, TP);
+        if (t0 == 0 && ra < nrows) out[ra * ldo + m] = v;
+      }
     }
   }
 }
@@ -621,45 +645,30 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
   __syncthreads();
   const int fs = fb + wave * kBSmallPerWave;
   const int ns = max(0, min(kBSmallPerWave, Fx - fs));
-  if (ns > 0) {
-    double* pw = part + wave * 2 * kBSmallPerWave * kMulti;
-    for (int m0 = 0; m0 < gp.ne; m0 += kMulti) {
-      const int nm = min(kMulti, gp.ne - m0);
-      ActLds acts[kMulti];
-#pragma unroll
-      for (int i = 0; i < kMulti; ++i) {
-        const int m = m0 + min(i, nm - 1);
-        acts[i] = ActLds{codes + (long)m * H, dq + m * (H / 32), sq + m * (H / 32)};
-      }
-      if (gp.shared) {
-        const long rb = row_bytes(ST, H);
-        rows_dot_multi<ST>(2 * ns, tasks_per_row(ST, H), [&](int r) {
-          return (r < ns) ? a.sgate + (fs + r) * rb : a.sup + (fs + r - ns) * rb;
-        }, acts, nm, pw, 0, 1);
-      } else {
-        const long rb = row_bytes(MOE_TYPE_Q4_K, H);
-        const long base = ((long)gp.e * a.F + fs) * rb;
-        rows_dot_multi<MOE_TYPE_Q4_K>(2 * ns, tasks_per_row(MOE_TYPE_Q4_K, H), [&](int r) {
-          return (r < ns) ? a.gate + base + r * rb : a.up + base + (r - ns) * rb;
-        }, acts, nm, pw, 0, 1);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-      if (lane < ns * kMulti) {
-        const int r = lane / kMulti, i = lane - r * kMulti;
-        if (i < nm) {
-          const float g = (float)pw[r * kMulti + i], u = (float)pw[(ns + r) * kMulti + i];
-          const float hv = (float)(silu_f64((double)g) * (double)u);
-          const int m = m0 + i;
-          if (gp.shared) a.hs[(long)toks[m] * a.Fs + fs + r] = hv;
-          else a.h[((long)toks[m] * a.k + slots[m]) * a.F + fs + r] = hv;
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    }
+  if (ns == 0) return;
+  const int ne = gp.ne;
+  double* pw = part + (long)wave * 2 * kBSmallPerWave * ne;   // [2 ns rows][ne]
+  if (gp.shared) {
+    const long rb = row_bytes(ST, H);
+    rows_dot_members<ST>(2 * ns, tasks_per_row(ST, H), [&](int r) {
+      return (r < ns) ? a.sgate + (fs + r) * rb : a.sup + (fs + r - ns) * rb;
+    }, codes, dq, sq, H, ne, pw, ne);
+  } else {
+    const long rb = row_bytes(MOE_TYPE_Q4_K, H);
+    const long base = ((long)gp.e * a.F + fs) * rb;
+    rows_dot_members<MOE_TYPE_Q4_K>(2 * ns, tasks_per_row(MOE_TYPE_Q4_K, H), [&](int r) {
+      return (r < ns) ? a.gate + base + r * rb : a.up + base + (r - ns) * rb;
+    }, codes, dq, sq, H, ne, pw, ne);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  for (int o = lane; o < ns * ne; o += 64) {
+    const int r = o / ne, m = o - r * ne;
+    const float g = (float)pw[r * ne + m], u = (float)pw[(ns + r) * ne + m];
+    const float hv = (float)(silu_f64((double)g) * (double)u);
+    if (gp.shared) a.hs[(long)toks[m] * a.Fs + fs + r] = hv;
+    else a.h[((long)toks[m] * a.k + slots[m]) * a.F + fs + r] = hv;
   }
 }
 
@@ -763,39 +772,27 @@ __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
     return (blk * 32 < Fx) ? hsrc(m) + 32 * blk : nullptr;
   }, [&](int j) { return codes + 32L * j; }, dq, sq, threadIdx.x, kBThreads);
   __syncthreads();
-  if (nr > 0) {
-    double* pw = part + wave * kBRows * kMulti;
-    for (int m0 = 0; m0 < gp.ne; m0 += kMulti) {
-      const int nm = min(kMulti, gp.ne - m0);
-      ActLds acts[kMulti];
-#pragma unroll
-      for (int i = 0; i < kMulti; ++i) {
-        const int m = m0 + min(i, nm - 1);
-        acts[i] = ActLds{codes + (long)m * Kx, dq + m * nb, sq + m * nb};
-      }
-      if (gp.shared) {
-        const long rb = row_bytes(ST, Kx);
-        rows_dot_multi<ST>(nr, tasks_per_row(ST, Kx), [&](int r) { return a.sdown + (i0 + r) * rb; }, acts, nm, pw, 0,
-                           1);
-      } else {
-        const long rb = row_bytes(DT, Kx);
-        const uint8_t* base = a.down + ((long)gp.e * H + i0) * rb;
-        rows_dot_multi<DT>(nr, tasks_per_row(DT, Kx), [&](int r) { return base + r * rb; }, acts, nm, pw, 0, 1);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-      for (int o = lane; o < nr * nm; o += 64) {
-        const int r = o / nm, i = o - r * nm;
-        const float yv = (float)pw[r * kMulti + i];
-        const int m = m0 + i;
-        if (gp.shared) a.ys[(long)toks[m] * H + i0 + r] = yv;
-        else a.y[((long)toks[m] * a.k + slots[m]) * H + i0 + r] = yv;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    }
+  if (nr == 0) return;
+  const int ne = gp.ne;
+  double* pw = part + (long)wave * kBRows * ne;   // [nr rows][ne]
+  if (gp.shared) {
+    const long rb = row_bytes(ST, Kx);
+    rows_dot_members<ST>(nr, tasks_per_row(ST, Kx), [&](int r) { return a.sdown + (i0 + r) * rb; }, codes, dq, sq,
+                         Kx, ne, pw, ne);
+  } else {
+    const long rb = row_bytes(DT, Kx);
+    const uint8_t* base = a.down + ((long)gp.e * H + i0) * rb;
+    rows_dot_members<DT>(nr, tasks_per_row(DT, Kx), [&](int r) { return base + r * rb; }, codes, dq, sq, Kx, ne, pw,
+                         ne);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  for (int o = lane; o < nr * ne; o += 64) {
+    const int r = o / ne, m = o - r * ne;
+    const float yv = (float)pw[r * ne + m];
+    if (gp.shared) a.ys[(long)toks[m] * H + i0 + r] = yv;
+    else a.y[((long)toks[m] * a.k + slots[m]) * H + i0 + r] = yv;
   }
 }
 
@@ -846,9 +843,11 @@ BatchWs batch_ws_layout(const moe_layer_desc* d, int n) {
   return L;
 }
 
+// toks/slots, the members' Q8_1 codes and block scales, and each wave's row
+// values of every member (kBRows rows: the down rows; gate/up use half)
 static size_t int_path_lds(int ne_max, int K) {
   return 2 * sizeof(int) * MOE_MAX_BATCH + (size_t)ne_max * K + 8 * (size_t)ne_max * (K / 32) + 16 +
-         sizeof(double) * kMulti * 2 * kBRows * kBWaves;
+         sizeof(double) * (size_t)ne_max * kBRows * kBWaves;
 }
 
 int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const float* xn, const void* xq,
