@@ -384,38 +384,62 @@ struct TaskW {
   uint32_t lo[8], hi[8];
   double s_lo, m_lo, s_hi, m_hi;
 };
+// a task's weight bytes as loaded: K-quant header (4 dwords) and 32 code
+// bytes (8), Q5_K also its 32 bytes of fifth bits (8); Q8_0 the 9 dwords
+// from the dword boundary at or below the block (the block sits at 34t)
 template <int TYPE>
-__device__ __forceinline__ void task_decode(const uint8_t* row, int t, TaskW<TYPE>& w) {
+struct TaskRaw {
+  uint32_t v[TYPE == MOE_TYPE_Q5_K ? 20 : (TYPE == MOE_TYPE_Q8_0 ? 9 : 12)];
+};
+template <int TYPE>
+__device__ __forceinline__ void task_raw(const uint8_t* row, int t, TaskRaw<TYPE>& r) {
   if (TYPE == MOE_TYPE_Q8_0) {
-    float d;
-    q80_load(row, t, d, w.lo);
-    w.s_lo = (double)d;
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(row + ((34 * t) & ~3));
+#pragma unroll
+    for (int i = 0; i < 9; ++i) r.v[i] = base[i];
     return;
   }
   const int b = t >> 2, g = t & 3;
   const uint8_t* blk = row + (long)b * block_bytes(TYPE);
-  const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
-  uint32_t qs[8], qh[8];
+  const uint4* q = reinterpret_cast<const uint4*>(blk + (TYPE == MOE_TYPE_Q5_K ? 48 : 16) + 32 * g);
+  const uint4 h = *reinterpret_cast<const uint4*>(blk), q0 = q[0], q1 = q[1];
+  r.v[0] = h.x; r.v[1] = h.y; r.v[2] = h.z; r.v[3] = h.w;
+  r.v[4] = q0.x; r.v[5] = q0.y; r.v[6] = q0.z; r.v[7] = q0.w;
+  r.v[8] = q1.x; r.v[9] = q1.y; r.v[10] = q1.z; r.v[11] = q1.w;
   if (TYPE == MOE_TYPE_Q5_K) {
-    lds_load8(blk + 16, qh);
-    lds_load8(blk + 48 + 32 * g, qs);
-  } else {
-    lds_load8(blk + 16 + 32 * g, qs);
+    const uint4* hq = reinterpret_cast<const uint4*>(blk + 16);
+    const uint4 h0 = hq[0], h1 = hq[1];
+    r.v[12] = h0.x; r.v[13] = h0.y; r.v[14] = h0.z; r.v[15] = h0.w;
+    r.v[16] = h1.x; r.v[17] = h1.y; r.v[18] = h1.z; r.v[19] = h1.w;
   }
+}
+template <int TYPE>
+__device__ __forceinline__ void task_decode(const TaskRaw<TYPE>& r, int t, TaskW<TYPE>& w) {
+  if (TYPE == MOE_TYPE_Q8_0) {
+    // d in the low or the high half of the first dword; the codes 2 bytes on
+    const bool sh = (34 * t) & 2;
+    w.s_lo = (double)f16_to_f32(sh ? (r.v[0] >> 16) : (r.v[0] & 0xffffu));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w.lo[i] = sh ? r.v[i + 1] : __builtin_amdgcn_alignbyte(r.v[i + 1], r.v[i], 2);
+    return;
+  }
+  const int g = t & 3;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    w.lo[i] = qs[i] & 0x0f0f0f0fu;
-    w.hi[i] = (qs[i] >> 4) & 0x0f0f0f0fu;
+    const uint32_t qs = r.v[4 + i];
+    w.lo[i] = qs & 0x0f0f0f0fu;
+    w.hi[i] = (qs >> 4) & 0x0f0f0f0fu;
     if (TYPE == MOE_TYPE_Q5_K) {
-      w.lo[i] |= ((qh[i] >> (2 * g)) & 0x01010101u) << 4;
-      w.hi[i] |= ((qh[i] >> (2 * g + 1)) & 0x01010101u) << 4;
+      const uint32_t qh = r.v[12 + i];
+      w.lo[i] |= ((qh >> (2 * g)) & 0x01010101u) << 4;
+      w.hi[i] |= ((qh >> (2 * g + 1)) & 0x01010101u) << 4;
     }
   }
   int sclo, mlo, schi, mhi;
-  kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g, sclo, mlo);
-  kquant_scale_min(hdr.y, hdr.z, hdr.w, 2 * g + 1, schi, mhi);
-  const double d = (double)f16_to_f32(hdr.x);
-  const double dmin = (double)f16_to_f32(hdr.x >> 16);
+  kquant_scale_min(r.v[1], r.v[2], r.v[3], 2 * g, sclo, mlo);
+  kquant_scale_min(r.v[1], r.v[2], r.v[3], 2 * g + 1, schi, mhi);
+  const double d = (double)f16_to_f32(r.v[0]);
+  const double dmin = (double)f16_to_f32(r.v[0] >> 16);
   w.s_lo = d * (double)sclo;
   w.m_lo = dmin * (double)mlo;
   w.s_hi = d * (double)schi;
@@ -461,12 +485,19 @@ __device__ __forceinline__ void rows_dot_members(int nrows, int T, RowFn rowfn, 
   const int rl = lane / TP, t0 = lane - rl * TP;
   const int tt = (t0 < T) ? t0 : 0;
   const int nbk = K / 32;
-  for (int r0 = 0; r0 < nrows; r0 += rpi) {
-    const int ra = r0 + rl;
-    const uint8_t* row = rowfn(ra < nrows ? ra : nrows - 1);
-    if (T <= 64) {   // one task per lane and row
+  if (T <= 64) {   // one task per lane and row; the next pass's words load while this one computes
+    auto row_of = [&](int r0) {
+      const int ra = r0 + rl;
+      return rowfn(ra < nrows ? ra : nrows - 1);
+    };
+    TaskRaw<TYPE> next;
+    task_raw<TYPE>(row_of(0), tt, next);
+    for (int r0 = 0; r0 < nrows; r0 += rpi) {
+      const int ra = r0 + rl;
+      const TaskRaw<TYPE> cur = next;
+      if (r0 + rpi < nrows) task_raw<TYPE>(row_of(r0 + rpi), tt, next);
       TaskW<TYPE> w;
-      task_decode<TYPE>(row, tt, w);
+      task_decode<TYPE>(cur, tt, w);
 #pragma unroll 1
       for (int m = 0; m < ne; ++m) {
         const ActLds act{codes + (long)m * K, dq + m * nbk, sq + m * nbk};
@@ -475,7 +506,13 @@ __device__ __forceinline__ void rows_dot_members(int nrows, int T, RowFn rowfn, 
         v = group_sum_f64(v, TP);
         if (t0 == 0 && ra < nrows) out[ra * ldo + m] = v;
       }
-    } else {         // tasks t0, t0 + 64, ... summed in that order
+    }
+    return;
+  }
+  for (int r0 = 0; r0 < nrows; r0 += rpi) {
+    const int ra = r0 + rl;
+    const uint8_t* row = rowfn(ra < nrows ? ra : nrows - 1);
+    {                // tasks t0, t0 + 64, ... summed in that order
 #pragma unroll 1
       for (int m = 0; m < ne; ++m) {
         const ActLds act{codes + (long)m * K, dq + m * nbk, sq + m * nbk};
