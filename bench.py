@@ -154,21 +154,28 @@ def time_steps(stack, steps, warmup, repeats):
     return per_token_us
 
 
-def layer_leg(q, n_inputs=128, repeats=5):
-    """One Qwen3.6-shaped layer (H 2048, 256 experts top-8, F 512, shared 512,
+def layer_leg(q, layers=None, n_inputs=128, repeats=5):
+    """Qwen3.6-shaped layers (H 2048, 256 experts top-8, F 512, shared 512,
     Q4_K) through the per-layer entry point moe_decode_layer, batch 1, on
     n_inputs fresh seeded inputs (residual, previous routed and shared
-    outputs ~N(0,1) bf16), each input's call captured in its own HIP graph and
-    the graphs replayed back to back: microseconds per layer call (median of
-    `repeats` passes), and GB/s over the bytes the layer must read (router,
-    norm weight, shared-gate row, the 8 selected experts, the shared expert).
-    The routed weights of the layer (453 MB) exceed the 256 MB last-level
-    cache, and each input selects other experts."""
+    outputs ~N(0,1) bf16), input i on layer i mod len(layers) (the stack's
+    layers when given, else one layer of its own), each input's call
+    captured in its own HIP graph and the graphs replayed back to back:
+    microseconds per layer call (median of `repeats` passes), and GB/s over
+    the bytes the layer must read (router, norm weight, shared-gate row, the
+    8 selected experts, the shared expert).  With the 40 layers of the stack,
+    a layer's router and shared expert come back after 39 other layers'
+    calls, as in a decode step; with one layer they stay in the last-level
+    cache between calls."""
     cfg = wl.CONFIGS["layer"]
-    W = wl.layer_weights(cfg, 0, "cuda")
     H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+    W = None
+    if not layers:
+        W = wl.layer_weights(cfg, 0, "cuda")
+        layers = [W]
     desc = q.make_desc(H, E, k, F, Fs, eps=cfg.eps)
-    lw = q.make_weights(W)
+    lws = [q.make_weights(L) for L in layers]
+    nl = len(lws)
     ws = q.alloc_workspace(desc)
     ios = []
     for t in range(n_inputs):
@@ -180,13 +187,13 @@ def layer_leg(q, n_inputs=128, repeats=5):
     s = torch.cuda.Stream()
     torch.cuda.synchronize()   # the inputs are made on the default stream
     with torch.cuda.stream(s):
-        q.moe_decode_layer(desc, lw, ios[0], ws)
+        q.moe_decode_layer(desc, lws[0], ios[0], ws)
     s.synchronize()
     graphs = []
-    for io in ios:
+    for i, io in enumerate(ios):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
-            q.moe_decode_layer(desc, lw, io, ws)
+            q.moe_decode_layer(desc, lws[i % nl], io, ws)
         graphs.append(g)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -204,16 +211,16 @@ def layer_leg(q, n_inputs=128, repeats=5):
         us.append(e0.elapsed_time(e1) * 1e3 / n_inputs)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for io in ios:
-        q.moe_decode_layer(desc, lw, io, ws)
+    for i, io in enumerate(ios):
+        q.moe_decode_layer(desc, lws[i % nl], io, ws)
     e1.record(stream)
     torch.cuda.synchronize()
     eager = e0.elapsed_time(e1) * 1e3 / n_inputs
     # all the calls in one graph, the way a decode step captures its layers
     g_all = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_all, stream=s):
-        for io in ios:
-            q.moe_decode_layer(desc, lw, io, ws)
+        for i, io in enumerate(ios):
+            q.moe_decode_layer(desc, lws[i % nl], io, ws)
     torch.cuda.synchronize()
     g_all.replay()
     us_one = []
@@ -228,13 +235,14 @@ def layer_leg(q, n_inputs=128, repeats=5):
     one = float(np.median(us_one))
     med = float(np.median(us))
     nbytes = algorithmic_bytes(cfg, wl.Q4_K, wl.Q4_K)
-    res = {"workload": f"one Qwen3.6-shaped layer through moe_decode_layer, batch 1, {n_inputs} fresh inputs, "
-                       "one HIP graph per input replayed back to back",
+    res = {"workload": f"Qwen3.6-shaped layers through moe_decode_layer, batch 1, {n_inputs} fresh inputs, input i "
+                       f"on layer i mod {nl}, one HIP graph per input replayed back to back", "layers_rotated": nl,
            "us_per_layer": med, "us_p10": float(np.percentile(us, 10)), "us_p90": float(np.percentile(us, 90)),
            "us_per_layer_eager": eager, "us_per_layer_one_graph": one,
            "alg_bytes_per_layer": nbytes, "achieved_GBs": nbytes / (med * 1e-6) / 1e9}
     res["frac_of_peak"] = res["achieved_GBs"] / HBM_PEAK_GBS
-    print(f"# layer (moe_decode_layer in graphs): {med:.1f} us per layer ({res['achieved_GBs']:.0f} GB/s); "
+    print(f"# layer (moe_decode_layer in graphs, {nl} layers rotated): {med:.1f} us per layer "
+          f"({res['achieved_GBs']:.0f} GB/s); "
           f"eager {eager:.1f} us; all {n_inputs} calls in one graph {one:.1f} us", file=sys.stderr, flush=True)
     del graphs, g_all, W
     torch.cuda.empty_cache()
@@ -662,7 +670,8 @@ def main():
         results[name] = res
         print(f"# {name}: {med:.1f} us/token ({res['achieved_GBs']:.0f} GB/s)", file=sys.stderr, flush=True)
     stack, res = primary if primary else (None, results[order[0]])
-    layer = None if a.no_layer else layer_leg(q)
+    same_shape = primary is not None and cfg.H == wl.CONFIGS["layer"].H and cfg.E == wl.CONFIGS["layer"].E
+    layer = None if a.no_layer else layer_leg(q, primary[0].layers if same_shape else None)
     attn = None if a.no_attn else attn_leg(q, a.steps, a.warmup, a.repeats)
     e128 = None if a.no_e128 else e128_leg(q, a.steps, a.warmup, a.repeats)
     batch = None if a.no_batch else batch_leg(q)
