@@ -605,6 +605,8 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   // the 32 workgroups that run on die (XCC) s: their h exchange stays in that
   // die's L2
   constexpr bool XS = FIX && fs.k == kXcc && fs.G == 256;
+  // router rows per workgroup of a fixed shape (E rows and the shared-gate row over G)
+  constexpr int kRRFix = FIX ? (fs.E + (fs.Fs > 0 ? 1 : 0) + fs.G - 1) / fs.G : 0;
   const StackGeom g = FIX ? kFixGeom<DT, ST, S> : a.g;
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   const int H = FIX ? fs.H : a.H, E = FIX ? fs.E : a.E, k = FIX ? fs.k : a.k, F = FIX ? fs.F : a.F,
@@ -714,6 +716,12 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   // 18 MB of router rows per layer stalling the row streams).
   constexpr int kRowsPD = XS ? fs.E / (fs.G / kXcc) : 0;
   constexpr bool PD = XS && kRowsPD <= 4;
+  // FR: router dots fused into the norm (every router row already landed when
+  // the norm runs, one float4 of xn per thread); kRRFused rows per workgroup
+  constexpr bool FR = FIX && !PD && fs.H == 4 * kStackThreads && kRRFix <= 2;
+  constexpr int kRRFused = FR ? kRRFix : 1;
+  static_assert(!FR || kRRFused * kStackWaves <= (fs.k + 1) * kFixGeom<DT, ST, S>.RD,
+                "the wave partials fit the row-value area (at least (k + 1) * RD doubles)");
   constexpr StackGeom gx = kFixGeom<DT, ST, S>;
   constexpr int kRowB = PD ? fs.H * 4 : 1;
   constexpr int kCapR = PD ? (gx.o_sgu - gx.o_rrow) / kRowB : 0, kCapG = PD ? (gx.o_rdn - gx.o_rgu) / kRowB : 0,
@@ -852,6 +860,11 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     if (b == 0 && a.resid_out)
       for (int i = tid; i < H; i += kStackThreads) a.resid_out[(long)l * H + i] = f32_to_bf16(res[i]);
     const double rinv = 1.0 / sqrt(ss / (double)H + (double)a.eps);
+    // FR (a fixed shape with one float4 of xn per thread and the router rows
+    // already landed): each thread also takes its four products with each of
+    // the workgroup's router rows, and the rows' sums travel through the
+    // barrier below instead of a pass over xn after it
+    double rp[kRRFused];
     for (int c = tid; c < H / 4; c += kStackThreads) {
       const float4 r = res4[c];
       const float4 wv = reinterpret_cast<const float4*>(nw)[c];
@@ -861,6 +874,21 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
       o.z = (float)(((double)r.z * rinv) * (double)wv.z);
       o.w = (float)(((double)r.w * rinv) * (double)wv.w);
       reinterpret_cast<float4*>(xn)[c] = o;
+      if constexpr (FR) {
+#pragma unroll
+        for (int j = 0; j < kRRFused; ++j) {
+          const float4 rw = reinterpret_cast<const float4*>(rrow + (long)j * H * 4)[c];
+          rp[j] = ((double)rw.x * (double)o.x + (double)rw.y * (double)o.y) +
+                  ((double)rw.z * (double)o.z + (double)rw.w * (double)o.w);
+        }
+      }
+    }
+    if constexpr (FR) {
+#pragma unroll
+      for (int j = 0; j < kRRFused; ++j) {
+        const double s = wave_sum_f64(rp[j]);
+        if ((tid & 63) == 0) part[j * kStackWaves + wave] = s;
+      }
     }
     if (PD && wave >= kPollWaves) wait_vmem();   // the router rows
     lds_barrier();
@@ -891,8 +919,22 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         __builtin_amdgcn_raw_buffer_store_b64(v, rx, 8u * (uint32_t)r, x_lg + xcc * rb_lg, 0);
       }
     }
+    // FR: the router rows' sums of the wave partials, in wave order, by the
+    // first lanes of wave kPollWaves
+    if constexpr (FR) {
+      const int j = tid - 64 * kPollWaves;
+      if (j >= 0 && j < kRRFused) {
+        const int r = b + j * g.G;
+        if ((r < E) || (r == E && has_sg)) {
+          double acc = 0.0;
+#pragma unroll
+          for (int w2 = 0; w2 < kStackWaves; ++w2) acc += part[j * kStackWaves + w2];
+          ll_store_rep<kRepLg>(rx, x_lg, rb_lg, r, __float_as_uint((float)acc), ep0);
+        }
+      }
+    }
     // router rows (fp64 dot of fp32 products), one wave per row
-    for (int j = wave - kPollWaves; !PD && j >= 0 && j < g.RR; j += kStackWaves - kPollWaves) {
+    for (int j = wave - kPollWaves; !PD && !FR && j >= 0 && j < g.RR; j += kStackWaves - kPollWaves) {
       const int r = b + j * g.G;
       const bool real = (r < E) || (r == E && has_sg);
       if (!real) break;
