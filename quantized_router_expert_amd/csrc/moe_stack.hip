@@ -738,8 +738,18 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
                      : (m < kCapR + kCapG ? rgu + (long)(m - kCapR) * kRowB : rdn + (long)(m - kCapR - kCapG) * kRowB);
   };
   // weights that do not depend on the routing decision, for layer `w`
-  auto prefetch_fixed = [&](const LayerPtrs& w) {
-    stage_async(smem + g.o_nw, w.norm_w, (uint32_t)(H * 4), wave, kPollWaves, kStackWaves - kPollWaves);
+  // The next layer's fixed weights, requested at the layer's end, except the
+  // norm weight of the per-die form, requested as soon as this layer has sent
+  // its shared h (it is not read again): there the norm waits on its router
+  // rows, and the norm weight landing early shortens that wait (the
+  // 128-expert stack: 666 -> 660 us per token).  In the 256-expert form any
+  // load issued then runs into the cross-die logits exchange: requesting the
+  // norm weight early cost 9 us per token, with the router rows 29 us.
+  auto prefetch_early = [&](const LayerPtrs& w) {
+    if (PD) stage_async(smem + g.o_nw, w.norm_w, (uint32_t)(H * 4), wave, kPollWaves, kStackWaves - kPollWaves);
+  };
+  auto prefetch_late = [&](const LayerPtrs& w) {
+    if (!PD) stage_async(smem + g.o_nw, w.norm_w, (uint32_t)(H * 4), wave, kPollWaves, kStackWaves - kPollWaves);
     for (int j = 0; !PD && j < g.RR; ++j) {
       const int r = b + j * g.G;
       const float* src = (r < E) ? w.router_w + (long)r * H : ((r == E && has_sg) ? w.shared_gate_w : nullptr);
@@ -790,7 +800,9 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   // ---- layer-0 inputs: the token's residual, no previous outputs
   for (int i = tid; i < H; i += kStackThreads) res[i] = bf16_to_f32(a.input[i]);
   LayerPtrs w = load_layer(a.layers, 0);
-  prefetch_fixed(w);
+  prefetch_early(w);
+  prefetch_late(w);
+  LayerPtrs w_next = w;
 
   for (int l = 0; l < a.L; ++l) {
     const uint32_t ep0 = base + 3u * l, ep1 = ep0 + 1u, ep2 = ep0 + 2u;
@@ -968,6 +980,13 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         const float uu = (float)part[nsr + tid];
         const float hv = (float)(silu_f64((double)gg) * (double)uu);
         ll_store_rep<kRepH>(rx, x_h, rb_h, k * F + sf0 + tid, __float_as_uint(hv), ep1);
+      }
+    }
+    // the next layer's early weights (per-die form): this layer has read its own
+    if constexpr (PD) {
+      if (l + 1 < a.L) {
+        w_next = load_layer(a.layers, l + 1);
+        prefetch_early(w_next);
       }
     }
     // ================= R2: logits -> selection, in every workgroup
@@ -1241,8 +1260,8 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     stamp(l, 9);
     bstamp(l, 10);
     if (l + 1 < a.L) {
-      w = load_layer(a.layers, l + 1);
-      prefetch_fixed(w);
+      w = PD ? w_next : load_layer(a.layers, l + 1);
+      prefetch_late(w);
     }
   }
   // ================= the fold a next layer would do: output = bf16(res + t)
