@@ -286,8 +286,15 @@ int moe_decode_layer_batch(const moe_layer_desc* desc, const moe_layer_weights* 
  *
  * mode MOE_STACK_KERNELS enqueues 4 kernels per layer plus the final fold on
  * `stream` (capture them in a HIP graph to remove launch overhead).
- * MOE_STACK_PERSISTENT runs every layer in one cooperative launch (one
- * workgroup per CU).  It needs a prior moe_stack_bind of the same layers into
+ * MOE_STACK_PERSISTENT runs every layer in one launch of one workgroup per
+ * CU, whose workgroups exchange data through bounded waits and so must all
+ * be resident at once.  It is a plain launch: on a device that runs nothing
+ * else, every CU takes one of its workgroups.  When other streams' kernels
+ * hold CUs, a workgroup may start only after others have waited past their
+ * bound, and the launch then stops with status 1 (moe_stack_status_offset).
+ * MOE_STACK_COOPERATIVE is the same kernel in a cooperative launch, for which
+ * the runtime places the whole grid at once (about 18 us more per token on
+ * one MI355X).  Both need a prior moe_stack_bind of the same layers into
  * the same workspace, else it returns MOE_ERR_NOT_BOUND and enqueues nothing;
  * bind copies the pointer table to the device, clears the stack's exchange
  * buffers and synchronises `stream` once (do not call it during graph
@@ -304,6 +311,7 @@ int moe_decode_layer_batch(const moe_layer_desc* desc, const moe_layer_weights* 
 #define MOE_STACK_AUTO 0
 #define MOE_STACK_KERNELS 1
 #define MOE_STACK_PERSISTENT 2
+#define MOE_STACK_COOPERATIVE 3
 
 /* Device buffers of one moe_decode_stack call.  The per-layer outputs are
  * optional (NULL = not written). */

@@ -23,7 +23,7 @@ _lib = C.CDLL(LIB_PATH)
 Q8_0, Q8_1, Q4_K, Q5_K = 8, 9, 12, 13
 BLOCK_BYTES = {Q4_K: 144, Q5_K: 176, Q8_0: 34, Q8_1: 36}
 BLOCK_ELEMS = {Q4_K: 256, Q5_K: 256, Q8_0: 32, Q8_1: 32}
-MOE_STACK_AUTO, MOE_STACK_KERNELS, MOE_STACK_PERSISTENT = 0, 1, 2
+MOE_STACK_AUTO, MOE_STACK_KERNELS, MOE_STACK_PERSISTENT, MOE_STACK_COOPERATIVE = 0, 1, 2, 3
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_TYPE", -4: "MOE_ERR_ALIGN",
           -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP", -7: "MOE_ERR_UNSUPPORTED", -8: "MOE_ERR_NOT_BOUND"}
 

@@ -390,7 +390,9 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
   if (!desc->norm) return MOE_ERR_UNSUPPORTED;
   if (!layers || !io || !io->input || !io->output) return MOE_ERR_NULL;
   if (n_layers <= 0 || n_layers > MOE_MAX_LAYERS) return MOE_ERR_SHAPE;
-  if (mode != MOE_STACK_AUTO && mode != MOE_STACK_KERNELS && mode != MOE_STACK_PERSISTENT) return MOE_ERR_SHAPE;
+  if (mode != MOE_STACK_AUTO && mode != MOE_STACK_KERNELS && mode != MOE_STACK_PERSISTENT &&
+      mode != MOE_STACK_COOPERATIVE)
+    return MOE_ERR_SHAPE;
   for (int l = 0; l < n_layers; ++l)
     if ((rc = check_weights(desc, &layers[l]))) return rc;
   if (!aligned(io->input, 2) || !aligned(io->output, 2) || (io->ids && !aligned(io->ids, 4)) ||
@@ -401,10 +403,11 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
   rc = check_ws(ws, ws_bytes, L.total);
   if (rc) return rc;
   hipStream_t st = as_stream(stream);
-  if (mode == MOE_STACK_PERSISTENT || mode == MOE_STACK_AUTO) {
+  if (mode == MOE_STACK_PERSISTENT || mode == MOE_STACK_COOPERATIVE || mode == MOE_STACK_AUTO) {
+    const bool explicit_persistent = mode == MOE_STACK_PERSISTENT || mode == MOE_STACK_COOPERATIVE;
     const uint64_t hash = layer_table_hash(layers, n_layers);
     const bool bound = bind_holds(ws, n_layers, hash);
-    if (mode == MOE_STACK_PERSISTENT && !bound) return MOE_ERR_NOT_BOUND;
+    if (explicit_persistent && !bound) return MOE_ERR_NOT_BOUND;
     int G = 0;
     if ((rc = device_cu_count(&G))) return rc;
     StackGeom g;
@@ -413,9 +416,9 @@ int moe_decode_stack(const moe_layer_desc* desc, const moe_layer_weights* layers
     if (rc == MOE_OK && bound) {
       stack_ws_layout(&g, L.stack);
       return launch_stack(desc, n_layers, at<moe_layer_weights>(ws, L.table), at<uint32_t>(ws, L.bound), hash, io,
-                          static_cast<uint8_t*>(ws), g, st);
+                          static_cast<uint8_t*>(ws), g, st, mode == MOE_STACK_COOPERATIVE);
     }
-    if (mode == MOE_STACK_PERSISTENT) return rc;
+    if (explicit_persistent) return rc;
   }
   const int H = desc->hidden, E = desc->n_experts, k = desc->top_k;
   const bool has_shared = desc->shared_ffn > 0;

@@ -64,8 +64,11 @@ struct StackArgs {
 
 int stack_geometry(const moe_layer_desc* d, int G, StackGeom* out);
 void stack_ws_layout(StackGeom* g, size_t base);
+// cooperative: a cooperative launch (the runtime places the whole grid at
+// once); else a plain one, resident as a whole when no other kernel holds CUs
 int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_dev, const uint32_t* bound,
-                 uint64_t table_hash, const moe_stack_io* io, uint8_t* ws, const StackGeom& g, hipStream_t st);
+                 uint64_t table_hash, const moe_stack_io* io, uint8_t* ws, const StackGeom& g, hipStream_t st,
+                 bool cooperative);
 int device_cu_count(int* n);
 // the persistent kernel instance for a description and its geometry; *shape
 // (if given) gets the compile-time shape index (0 = sizes at run time)

@@ -1,4 +1,4 @@
-// moe_stack.hip -- the whole L-layer MoE stack for one token in one cooperative launch.
+// moe_stack.hip -- the whole L-layer MoE stack for one token in one launch (every workgroup resident).
 //
 // [P239] Summary: decode is graph- and launch-bound, so removing per-layer
 // launches pays; [P273] Summary item 1: the top-k runs inside the router's
@@ -25,6 +25,7 @@
 // error word and the grid exits.
 #include <cstddef>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe_decode.h"
 #include "moe_device.h"
@@ -1398,8 +1399,31 @@ const void* stack_kernel_for(const moe_layer_desc* d, const StackGeom& g, int* s
   return nullptr;
 }
 
+// whether one workgroup of kernel fn with lds bytes fits a CU (the occupancy
+// query, remembered per kernel and size: the answer does not change)
+static bool fits_cu(const void* fn, size_t lds) {
+  struct Entry {
+    const void* fn;
+    size_t lds;
+    bool fits;
+  };
+  static std::mutex m;
+  static Entry seen[32];
+  static int n = 0;
+  std::lock_guard<std::mutex> lock(m);
+  for (int i = 0; i < n; ++i)
+    if (seen[i].fn == fn && seen[i].lds == lds) return seen[i].fits;
+  int per_cu = 0;
+  const bool fits = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStackThreads, lds) == hipSuccess &&
+                    per_cu >= 1;
+  if (!fits) (void)hipGetLastError();
+  if (n < 32) seen[n++] = Entry{fn, lds, fits};
+  return fits;
+}
+
 int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_dev, const uint32_t* bound,
-                 uint64_t table_hash, const moe_stack_io* io, uint8_t* ws, const StackGeom& g, hipStream_t st) {
+                 uint64_t table_hash, const moe_stack_io* io, uint8_t* ws, const StackGeom& g, hipStream_t st,
+                 bool cooperative) {
   static_assert(sizeof(moe_layer_weights) % 8 == 0, "the table hashes in 8-byte words");
   StackArgs a;
   a.g = g;
@@ -1426,7 +1450,15 @@ int launch_stack(const moe_layer_desc* d, int L, const moe_layer_weights* table_
   if (!fn) return MOE_ERR_UNSUPPORTED;
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, g.lds) != hipSuccess) return MOE_ERR_HIP;
   void* args[] = {&a};
-  if (hipLaunchCooperativeKernel(fn, dim3(g.G), dim3(kStackThreads), args, g.lds, st) != hipSuccess) {
+  // The grid is one workgroup per CU (g.G is the CU count).  A plain launch
+  // places all of them at once when the kernel fits a CU and no other kernel
+  // holds CUs; the cooperative launch has the runtime guarantee it, at about
+  // 18 us more per launch.  A plain launch is used only when the occupancy
+  // query confirms that a workgroup fits a CU.
+  if (!cooperative && !fits_cu(fn, g.lds)) cooperative = true;
+  const hipError_t e = cooperative ? hipLaunchCooperativeKernel(fn, dim3(g.G), dim3(kStackThreads), args, g.lds, st)
+                                   : hipLaunchKernel(fn, dim3(g.G), dim3(kStackThreads), args, g.lds, st);
+  if (e != hipSuccess) {
     (void)hipGetLastError();
     return MOE_ERR_HIP;
   }

@@ -159,6 +159,8 @@ def test_layer_and_stack_validation(q):
     # the persistent kernel on a workspace that holds no bound stack: refused
     # on the host before anything is enqueued
     assert ds(C.byref(d), arr, 2, C.byref(sio), q.MOE_STACK_PERSISTENT, FAKE, big, None) == -8
+    assert ds(C.byref(d), arr, 2, C.byref(sio), q.MOE_STACK_COOPERATIVE, FAKE, big, None) == -8
+    assert ds(C.byref(d), arr, 2, C.byref(sio), 4, FAKE, big, None) == -2
     assert q._moe_stack_bind(C.byref(d), arr, 2, FAKE, 1024, None) == -5
     assert q._moe_test_subblock_dots(FAKE, 9, 256, 1, FAKE, FAKE, None) == -3
     assert q._moe_test_subblock_dots(FAKE, 12, 100, 1, FAKE, FAKE, None) == -2

@@ -1,4 +1,4 @@
-"""Parity of the persistent L-layer stack (one cooperative launch per token)
+"""Parity of the persistent L-layer stack (one launch per token)
 against the oracle, at the depth the benchmark runs (40 layers of the
 Qwen3.6-shaped layer in both weight variants, 48 layers of the 128-expert
 shape, with an all-zero token) and on smaller shapes that reach the other code
@@ -47,6 +47,35 @@ def test_stack_full_depth_vs_oracle(q, orc, cfg_name, shared_type, down_type, to
     gu.banner(f"persistent stack {cfg_name} {cfg.layers} layers shared {shared_type} down {down_type} tokens {tokens} "
               f"attention {attn}")
     sc.run_and_check(q, orc, cfg, shared_type, down_type, tokens, q.MOE_STACK_PERSISTENT, with_attn=attn)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg_name,layers", [("stack", 40), ("e128", 48)])
+def test_stack_cooperative_launch_is_the_same(q, cfg_name, layers):
+    """MOE_STACK_COOPERATIVE runs the kernel of MOE_STACK_PERSISTENT in a
+    cooperative launch: the same bits, token after token, with either launch
+    following the other, and status 0."""
+    cfg = wl.variant(wl.CONFIGS[cfg_name], layers=layers)
+    gu.banner(f"cooperative and plain launches of the {cfg_name} stack, {layers} layers")
+    L, H, k = cfg.layers, cfg.H, cfg.k
+    Ws = [wl.layer_weights(cfg, l, "cuda") for l in range(L)]
+    desc = q.make_desc(H, cfg.E, k, cfg.F, cfg.Fs, eps=cfg.eps)
+    ws = q.alloc_workspace(desc, L)
+    q.moe_stack_bind(desc, Ws, ws)
+    arr = q.layer_array(Ws)
+    for t in range(4):
+        inp = wl.token_inputs(cfg, t, "cuda")["residual"]
+        outs = []
+        for mode in ((q.MOE_STACK_PERSISTENT, q.MOE_STACK_COOPERATIVE) if t % 2 == 0
+                     else (q.MOE_STACK_COOPERATIVE, q.MOE_STACK_PERSISTENT)):
+            out = torch.zeros(H, dtype=torch.bfloat16, device="cuda")
+            ids = torch.full((L, k), -1, dtype=torch.int32, device="cuda")
+            q.moe_decode_stack(desc, None, inp, out, ids, None, mode, ws, layer_array=arr)
+            outs.append((out, ids))
+        torch.cuda.synchronize()
+        assert _status(q, desc, L, ws) == 0
+        assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16)), t
+        assert torch.equal(outs[0][1], outs[1][1]), t
     torch.cuda.empty_cache()
 
 
