@@ -485,23 +485,6 @@ __device__ void load_act_lds(const uint8_t* xq, int K, uint8_t* codes, float* d,
 
 // All tasks of `nrows` rows of K elements staged back to back at `rows`:
 // partial[r*T + t] = fp64 contribution of task t of row r.
-template <int TYPE>
-__device__ void rows_partials(const uint8_t* rows, long rbytes, int nrows, int K, const ActLds& act, double* partial,
-                              int nthreads) {
-  const int T = tasks_per_row(TYPE, K);
-  const int total = nrows * T;
-  for (int i = threadIdx.x; i < total; i += nthreads) {
-    const int r = i / T, t = i - r * T;
-    partial[i] = row_task<TYPE>(rows + (long)r * rbytes, t, act);
-  }
-}
-
-__device__ __forceinline__ double sum_partials(const double* p, int T) {
-  double a = 0.0;
-  for (int t = 0; t < T; ++t) a += p[t];
-  return a;
-}
-
 // =====================================================================
 // a4 (+ a6 gate/up): gate/up rows + SwiGLU
 // =====================================================================
@@ -532,17 +515,20 @@ struct GateUpArgs {
 };
 
 
+// the nr gate rows and nr up rows of a chunk by rows_dot (a row's tasks on
+// lane groups, summed by the lane-group tree, two rows per lane in flight:
+// the persistent kernel's row values bit for bit), then SwiGLU
 template <int TYPE>
 __device__ void gate_up_chunk(const uint8_t* stage, long up_off, int nr, int H, const ActLds& act, double* partial,
                               float* h_out) {
   const long rb = row_bytes(TYPE, H);
-  const int T = tasks_per_row(TYPE, H);
-  rows_partials<TYPE>(stage, rb, nr, H, act, partial, blockDim.x);
-  rows_partials<TYPE>(stage + up_off, rb, nr, H, act, partial + (long)nr * T, blockDim.x);
+  rows_dot<TYPE>(2 * nr, tasks_per_row(TYPE, H), [&](int r) {
+    return RowRef{(r < nr) ? stage + (long)r * rb : stage + up_off + (long)(r - nr) * rb, act};
+  }, partial, (int)(threadIdx.x >> 6), (int)(blockDim.x >> 6));
   __syncthreads();
   for (int f = threadIdx.x; f < nr; f += blockDim.x) {
-    const float g = (float)sum_partials(partial + (long)f * T, T);
-    const float u = (float)sum_partials(partial + (long)(nr + f) * T, T);
+    const float g = (float)partial[f];
+    const float u = (float)partial[nr + f];
     h_out[f] = (float)(silu_f64((double)g) * (double)u);
   }
 }
@@ -731,27 +717,25 @@ __device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
   }
   wait_vmem();
   __syncthreads();
-  // tasks of all routed rows
-  const int total = a.k * nr * T;
-  for (int i = threadIdx.x; i < total; i += blockDim.x) {
-    const int s = i / (nr * T);
-    const int rem = i - s * nr * T;
-    const int r = rem / T, t = rem - r * T;
-    ActLds act{codes + (long)s * Kp, dact + s * (Kp / 32), sact + s * (Kp / 32)};
-    partial[((long)s * a.Ro + r) * T + t] = row_task<DT>(stage + (long)s * slot_bytes + (long)r * rb, t, act);
-  }
-  if (a.Fs > 0) {
-    ActLds acts{codes_s, dsh, ssh};
-    for (int i = threadIdx.x; i < nr * Ts; i += blockDim.x) {
-      const int r = i / Ts, t = i - r * Ts;
-      partial_s[(long)r * Ts + t] = row_task<ST>(stage_s + (long)r * rbs, t, acts);
-    }
-  }
+  // the slots' rows by rows_dot (row i = row i % nr of slot i / nr: the
+  // persistent kernel's row values bit for bit); the shared expert's rows as
+  // one more slot in the same pass when its type and length are the routed ones
+  const ActLds acts{codes_s, dsh, ssh};
+  const bool one_pass = a.Fs > 0 && DT == ST && Kps == Kp;
+  const int wave_n = (int)(blockDim.x >> 6);
+  rows_dot<DT>((a.k + (one_pass ? 1 : 0)) * nr, T, [&](int i) {
+    const int s = i / nr, r = i - s * nr;
+    if (s == a.k) return RowRef{stage_s + (long)r * rbs, acts};
+    return RowRef{stage + (long)s * slot_bytes + (long)r * rb,
+                  ActLds{codes + (long)s * Kp, dact + s * (Kp / 32), sact + s * (Kp / 32)}};
+  }, partial, wave, wave_n);
+  if (a.Fs > 0 && !one_pass)
+    rows_dot<ST>(nr, Ts, [&](int r) { return RowRef{stage_s + (long)r * rbs, acts}; }, partial + (long)a.k * nr, wave,
+                 wave_n);
   __syncthreads();
   for (int i = threadIdx.x; i < nm * nr; i += blockDim.x) {
     const int m = i / nr, r = i - m * nr;
-    const double v = (m < a.k) ? sum_partials(partial + ((long)m * a.Ro + r) * T, T) : sum_partials(partial_s + (long)r * Ts, Ts);
-    y[m * a.Ro + r] = (float)v;
+    y[m * a.Ro + r] = (float)partial[(long)m * nr + r];
   }
   __syncthreads();
   for (int r = threadIdx.x; r < nr; r += blockDim.x) {
@@ -762,15 +746,11 @@ __device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
   }
 }
 
+// one instance per (down, shared) type pair, each with its own register budget
+template <int DT, int ST>
 __global__ __launch_bounds__(kFfnThreads) void k_down_combine(DownArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  if (a.dtype == MOE_TYPE_Q5_K) {
-    if (a.stype == MOE_TYPE_Q8_0) down_combine_body<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0>(a, smem);
-    else down_combine_body<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K>(a, smem);
-  } else {
-    if (a.stype == MOE_TYPE_Q8_0) down_combine_body<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0>(a, smem);
-    else down_combine_body<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K>(a, smem);
-  }
+  down_combine_body<DT, ST>(a, smem);
 }
 
 // =====================================================================
@@ -1077,7 +1057,10 @@ int launch_down(const moe_layer_desc* d, const moe_layer_weights* w, const float
   a.Ro = pick_down_rows(d);
   if (down_lds(d, a.Ro) > kLdsBudget) return MOE_ERR_UNSUPPORTED;
   const int nblk = (a.H + a.Ro - 1) / a.Ro;
-  hipLaunchKernelGGL(k_down_combine, dim3(nblk), dim3(kFfnThreads), down_lds(d, a.Ro), st, a);
+  const bool q5 = a.dtype == MOE_TYPE_Q5_K, s8 = a.stype == MOE_TYPE_Q8_0;
+  auto fn = q5 ? (s8 ? k_down_combine<MOE_TYPE_Q5_K, MOE_TYPE_Q8_0> : k_down_combine<MOE_TYPE_Q5_K, MOE_TYPE_Q4_K>)
+               : (s8 ? k_down_combine<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0> : k_down_combine<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K>);
+  hipLaunchKernelGGL(fn, dim3(nblk), dim3(kFfnThreads), down_lds(d, a.Ro), st, a);
   return launch_ok();
 }
 
