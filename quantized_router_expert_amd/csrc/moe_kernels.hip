@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kRouterThreads) void k_router_topk(const float* xn,
         if (t < nt) part[wave][t] = red[t];
     }
     __syncthreads();
-    if (threadIdx.x < kRouterRpb * nt) {
+    if ((int)threadIdx.x < kRouterRpb * nt) {
       const int rr = threadIdx.x / nt, t = threadIdx.x - rr * nt;
       const int r = blockIdx.x * kRouterRpb + rr;
       if (r < nrows) {
@@ -670,7 +670,7 @@ __device__ void down_combine_body(const DownArgs& a, uint8_t* smem) {
   // there, each id would be a round trip of its own)
   __shared__ float s_wts[MOE_MAX_TOPK], s_sg;
   __shared__ int32_t s_ids[MOE_MAX_TOPK];
-  if (threadIdx.x < a.k) {
+  if ((int)threadIdx.x < a.k) {
     s_ids[threadIdx.x] = a.ids[threadIdx.x];
     s_wts[threadIdx.x] = a.wts[threadIdx.x];
   }
