@@ -17,6 +17,7 @@
 // of A and column l%16 of B at k = 8*(l/16) .. +7, and rows 4*(l/16) .. +3 of
 // column l%16 of D.
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moe_decode.h"
 #include "moe_device.h"
@@ -887,6 +888,60 @@ static size_t int_path_lds(int ne_max, int K) {
          sizeof(double) * (size_t)ne_max * kBRows * kBWaves;
 }
 
+// The matrix-core groups and the integer-path groups write disjoint rows of
+// h, hs, y and ys, so their kernels can run side by side: the matrix-core
+// chain (gate/up, then down) goes to a second stream of the device, forked
+// from the caller's stream after the grouping and joined before the combine.
+// One such stream and its two events per device, made on the first call that
+// is not being captured into a graph (a captured call before that runs both
+// chains on the caller's stream).  The fork and join of one call happen under
+// a lock, so that calls from several host threads cannot interleave the
+// events' records and waits; their matrix-core chains then queue on the one
+// side stream in call order.
+namespace {
+constexpr int kMaxDevices = 64;
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// the device's side stream, or null (caller holds g_side_mu)
+SideStream* side_stream(hipStream_t st) {
+  int dev = -1;
+  if (st ? hipStreamGetDevice(st, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (ss.s) return &ss;
+  if (ss.failed) return nullptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  hipStream_t s = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  const bool ok = hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess &&
+                  hipEventCreateWithFlags(&e0, hipEventDisableTiming) == hipSuccess &&
+                  hipEventCreateWithFlags(&e1, hipEventDisableTiming) == hipSuccess;
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (!ok) {
+    if (e1) (void)hipEventDestroy(e1);
+    if (e0) (void)hipEventDestroy(e0);
+    if (s) (void)hipStreamDestroy(s);
+    ss.failed = true;
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  ss.s = s;
+  ss.fork = e0;
+  ss.join = e1;
+  return &ss;
+}
+}  // namespace
+
 int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, const float* xn, const void* xq,
                        const int32_t* ids, const float* wts, const float* sg, int n, int gmin, uint16_t* routed,
                        uint16_t* shared, float* h, float* hs, uint8_t* ws, const BatchWs& L, hipStream_t st) {
@@ -949,25 +1004,14 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   a.stage_dma = a.stage_gu && (kBRows * row_bytes(MOE_TYPE_Q4_K, H)) % 1024 == 0 &&
                 (!has_sg || (kBRows * row_bytes(st_type, H)) % 1024 == 0);
   void* args[] = {&a};
-  {
-    const bool q80 = st_type == MOE_TYPE_Q8_0;
-    const void* fs_ = q80 ? (const void*)k_bgu<MOE_TYPE_Q8_0, false> : (const void*)k_bgu<MOE_TYPE_Q4_K, false>;
-    const void* fb_ = q80 ? (const void*)k_bgu<MOE_TYPE_Q8_0, true> : (const void*)k_bgu<MOE_TYPE_Q4_K, true>;
-    if (small > 0) {
-      if (hipFuncSetAttribute(fs_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu) != hipSuccess) return MOE_ERR_HIP;
-      if (hipLaunchKernel(fs_, ggu, dim3(kBThreads), args, lds_gu, st) != hipSuccess) return MOE_ERR_HIP;
-    }
-    // x: the groups of group_min or more tokens (the compact list, as for
-    // down), z: tiles of 16 tokens.  A grid over every group spent most of
-    // the kernel dispatching workgroups that leave at once, one per CU at
-    // this instance's LDS size
-    const dim3 ggu_big(ngroups_big, ggu.y, (n + 15) / 16);
-    if (any_big) {
-      if (hipFuncSetAttribute(fb_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu_big) != hipSuccess)
-        return MOE_ERR_HIP;
-      if (hipLaunchKernel(fb_, ggu_big, dim3(kBThreads), args, lds_gu_big, st) != hipSuccess) return MOE_ERR_HIP;
-    }
-  }
+  const bool q80 = st_type == MOE_TYPE_Q8_0;
+  const void* fgs = q80 ? (const void*)k_bgu<MOE_TYPE_Q8_0, false> : (const void*)k_bgu<MOE_TYPE_Q4_K, false>;
+  const void* fgb = q80 ? (const void*)k_bgu<MOE_TYPE_Q8_0, true> : (const void*)k_bgu<MOE_TYPE_Q4_K, true>;
+  // x: the groups of group_min or more tokens (the compact list, as for
+  // down), z: tiles of 16 tokens.  A grid over every group spent most of
+  // the kernel dispatching workgroups that leave at once, one per CU at
+  // this instance's LDS size
+  const dim3 ggu_big(ngroups_big, ggu.y, (n + 15) / 16);
   const int kmax = max(a.Kp, a.Kps);
   const dim3 gdn(ngroups, (H + kBRows - 1) / kBRows);
   const size_t lds_dn = small > 0 ? int_path_lds(small > n ? n : small, kmax) : 0;
@@ -988,16 +1032,40 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
     fdb = (st_type == MOE_TYPE_Q8_0) ? (const void*)k_bdn<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0, true>
                                      : (const void*)k_bdn<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, true>;
   }
-  if (small > 0) {
-    if (hipFuncSetAttribute(fds, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn) != hipSuccess) return MOE_ERR_HIP;
-    const dim3 gdn_small(ngroups, (H + kBRowsPerBlock - 1) / kBRowsPerBlock);
-    if (hipLaunchKernel(fds, gdn_small, dim3(kBThreads), args, lds_dn, st) != hipSuccess) return MOE_ERR_HIP;
-  }
-  if (any_big) {
-    if (hipFuncSetAttribute(fdb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn_big) != hipSuccess)
-      return MOE_ERR_HIP;
-    const dim3 gdn_big(ngroups_big, gdn.y, (n + 15) / 16);   // z: tiles of 16 tokens
-    if (hipLaunchKernel(fdb, gdn_big, dim3(kBThreads), args, lds_dn_big, st) != hipSuccess) return MOE_ERR_HIP;
+  const dim3 gdn_small(ngroups, (H + kBRowsPerBlock - 1) / kBRowsPerBlock);
+  const dim3 gdn_big(ngroups_big, gdn.y, (n + 15) / 16);   // z: tiles of 16 tokens
+  if ((small > 0 && (hipFuncSetAttribute(fgs, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu) != hipSuccess ||
+                     hipFuncSetAttribute(fds, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn) != hipSuccess)) ||
+      (any_big && (hipFuncSetAttribute(fgb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu_big) != hipSuccess ||
+                   hipFuncSetAttribute(fdb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn_big) != hipSuccess)))
+    return MOE_ERR_HIP;
+  {
+    std::unique_lock<std::mutex> lock(g_side_mu, std::defer_lock);
+    SideStream* side = nullptr;
+    if (small > 0 && any_big) {
+      lock.lock();
+      side = side_stream(st);
+      if (!side) lock.unlock();
+    }
+    hipStream_t sb = st;   // the matrix-core chain's stream
+    if (side) {
+      if (hipEventRecord(side->fork, st) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+        return MOE_ERR_HIP;
+      sb = side->s;
+    }
+    // the matrix-core chain first: its workgroups run longest
+    int rc = MOE_OK;
+    if (any_big && (hipLaunchKernel(fgb, ggu_big, dim3(kBThreads), args, lds_gu_big, sb) != hipSuccess ||
+                    hipLaunchKernel(fdb, gdn_big, dim3(kBThreads), args, lds_dn_big, sb) != hipSuccess))
+      rc = MOE_ERR_HIP;
+    if (rc == MOE_OK && small > 0 &&
+        (hipLaunchKernel(fgs, ggu, dim3(kBThreads), args, lds_gu, st) != hipSuccess ||
+         hipLaunchKernel(fds, gdn_small, dim3(kBThreads), args, lds_dn, st) != hipSuccess))
+      rc = MOE_ERR_HIP;
+    // joined even after a failed launch, so that a capture is not left forked
+    if (side && (hipEventRecord(side->join, sb) != hipSuccess || hipStreamWaitEvent(st, side->join, 0) != hipSuccess))
+      rc = MOE_ERR_HIP;
+    if (rc) return rc;
   }
   hipLaunchKernelGGL(k_bcombine, dim3(n, (H + 255) / 256), dim3(256), 0, st, a.y, a.ys, wts, sg,
                      reinterpret_cast<const int*>(ws + L.err), k, H, has_sg, routed, shared);

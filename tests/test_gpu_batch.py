@@ -201,3 +201,53 @@ def test_grouped_ffn_bad_ids_give_nan(q, orc):
     q.expert_ffn_grouped(d_g, W, xn, xq, ids, wts, sg, n, 2, routed, shared, None, None, ws)
     torch.cuda.synchronize()
     assert torch.isnan(routed.float()).all() and torch.isnan(shared.float()).all()
+
+
+def test_decode_layer_batch_graph_replays(q, orc):
+    """The matrix-core groups run on a second stream forked from the caller's
+    and joined before the combine: a call captured into a HIP graph (after an
+    eager call, so the fork is in the graph) must give the eager call's
+    outputs bit for bit on every replay, with other work between replays."""
+    cfg = wl.CONFIGS["batch"]
+    n, gmin = 32, 4
+    gu.banner(f"decode_layer_batch in a graph: batch {n} group_min {gmin}, 5 replays")
+    W, _ = _weights(cfg, wl.Q4_K, wl.Q4_K)
+    H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+    d_g = q.make_desc(H, E, k, F, Fs, eps=cfg.eps)
+    inp = _inputs(cfg, n)
+    ws = q.alloc_batch_workspace(d_g, n)
+
+    def io_new():
+        return {"residual": gu.dev_u16(inp["residual"]), "routed_in": gu.dev_u16(inp["routed_prev"]),
+                "shared_in": gu.dev_u16(inp["shared_prev"]),
+                "out_sum": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda"),
+                "routed_out": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda"),
+                "shared_out": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda"),
+                "ids": torch.zeros(n, k, dtype=torch.int32, device="cuda")}
+
+    ref = io_new()
+    q.moe_decode_layer_batch(d_g, W, ref, n, gmin, ws)
+    torch.cuda.synchronize()
+    io = io_new()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        q.moe_decode_layer_batch(d_g, W, io, n, gmin, ws)
+    torch.cuda.synchronize()
+    for r in range(5):
+        for key in ("out_sum", "routed_out", "shared_out"):
+            io[key].fill_(float("nan"))
+        io["ids"].fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key in ("out_sum", "routed_out", "shared_out"):
+            assert torch.equal(io[key].view(torch.int16), ref[key].view(torch.int16)), (r, key)
+        assert torch.equal(io["ids"], ref["ids"]), r
+        # eager work between replays: the same call on other buffers
+        other = io_new()
+        q.moe_decode_layer_batch(d_g, W, other, n, gmin, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(other["routed_out"].view(torch.int16), ref["routed_out"].view(torch.int16)), r
+    print("  5 replays bit-identical to the eager call", flush=True)
