@@ -334,24 +334,33 @@ struct BGroupArgs {
   int stage_dma;            // gate/up rows streamed into LDS by buffer->LDS loads (whole KiB per block)
 };
 
-// the group of blockIdx.x: returns false if this block has no group
+// The group of a block, and the block's chunk of that group's rows.  The
+// big-group grids are (group, chunk, tile of 16 tokens); the small-group
+// grids are (chunk, group), so that a group's chunks are dispatched one after
+// another.  Either way group 0 is the shared expert's (when there is one):
+// its workgroups, the heaviest, start first instead of being dispatched last
+// and finishing after everything else.  block_group() returns false if the
+// block has no group.
 struct Group {
   bool shared;
   int e, ne, mbase;
 };
-// (COMPACT: blockIdx.x indexes the groups of group_min or more tokens only)
-template <bool COMPACT>
+template <bool BIG>
+__device__ __forceinline__ int block_chunk() { return BIG ? (int)blockIdx.y : (int)blockIdx.x; }
+// (BIG: the groups of group_min or more tokens only, the compact list)
+template <bool BIG>
 __device__ __forceinline__ bool block_group(const BGroupArgs& a, Group& gp) {
-  const int gi = blockIdx.x;
-  gp.shared = a.has_sg && gi == (int)gridDim.x - 1;
+  const int gi = BIG ? (int)blockIdx.x : (int)blockIdx.y;
+  gp.shared = a.has_sg && gi == 0;
   if (gp.shared) {
     gp.e = -1;
     gp.ne = a.n;
     gp.mbase = 0;
     return true;
   }
-  if (gi >= (COMPACT ? a.nb[0] : a.nd[0])) return false;
-  gp.e = COMPACT ? a.blist[gi] : a.dlist[gi];
+  const int li = gi - a.has_sg;   // index into the expert list
+  if (li >= (BIG ? a.nb[0] : a.nd[0])) return false;
+  gp.e = BIG ? a.blist[li] : a.dlist[li];
   gp.ne = a.cnt[gp.e];
   gp.mbase = a.moff[gp.e];
   return true;
@@ -569,12 +578,12 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
   const int Fx = gp.shared ? a.Fs : a.F;
   const bool big = gp.ne >= a.gmin;
   if (big != BIG) return;
-  // blockIdx.y counts kBSmallRows-row chunks: a small group's block takes
+  // the chunk counts kBSmallRows-row chunks: a small group's block takes
   // one (kBSmallPerWave rows per wave); a big group's block takes kBigSpan
   // of them, kBRows rows whose K its waves split (the other blocks of its
   // span leave at once)
-  if (big && (blockIdx.y % kBigSpan)) return;
-  const int fb = blockIdx.y * kBSmallRows;
+  if (big && (block_chunk<BIG>() % kBigSpan)) return;
+  const int fb = block_chunk<BIG>() * kBSmallRows;
   if (fb >= Fx) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H = a.H;
@@ -711,7 +720,7 @@ __global__ __launch_bounds__(kBThreads) void k_bgu(BGroupArgs a) {
 }
 
 // down rows of one group: 64 output rows per block for a small group, 16 for a
-// big one (blockIdx.y counts 16-row units)
+// big one (the chunk counts 16-row units)
 template <int DT, int ST, bool BIG>
 __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -721,9 +730,9 @@ __global__ __launch_bounds__(kBThreads) void k_bdn(BGroupArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool big = gp.ne >= a.gmin;
   if (big != BIG) return;
-  // blockIdx.y: a big group's block takes kBRows rows (its waves split K), a
+  // the chunk: a big group's block takes kBRows rows (its waves split K), a
   // small group's block kBRowsPerBlock rows (kBRows per wave)
-  const int i0 = BIG ? blockIdx.y * kBRows : blockIdx.y * kBRowsPerBlock + wave * kBRows;
+  const int i0 = BIG ? block_chunk<BIG>() * kBRows : block_chunk<BIG>() * kBRowsPerBlock + wave * kBRows;
   if (big && i0 >= H) return;
   const int nr = max(0, min(kBRows, H - i0));
   const int Fx = gp.shared ? a.Fs : a.F;
@@ -991,7 +1000,8 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   const int ngroups_big = min(E, n * k / gmin) + has_sg;
   const int small = gmin - 1;   // largest group on the integer path
   const int fmax = max(F, Fs);
-  const dim3 ggu(ngroups, (fmax + kBSmallRows - 1) / kBSmallRows);
+  const int ggu_chunks = (fmax + kBSmallRows - 1) / kBSmallRows;
+  const dim3 ggu(ggu_chunks, ngroups);   // small groups: (chunk, group)
   const bool any_big = gmin <= n;   // a group (at least the shared one when n >= gmin) can reach group_min
   const size_t lds_gu = small > 0 ? int_path_lds(small > n ? n : small, H) : 0;
   // matrix-core groups stage their rows (and gate/up activations) in LDS when they fit
@@ -1011,7 +1021,7 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
   // down), z: tiles of 16 tokens.  A grid over every group spent most of
   // the kernel dispatching workgroups that leave at once, one per CU at
   // this instance's LDS size
-  const dim3 ggu_big(ngroups_big, ggu.y, (n + 15) / 16);
+  const dim3 ggu_big(ngroups_big, ggu_chunks, (n + 15) / 16);
   const int kmax = max(a.Kp, a.Kps);
   const dim3 gdn(ngroups, (H + kBRows - 1) / kBRows);
   const size_t lds_dn = small > 0 ? int_path_lds(small > n ? n : small, kmax) : 0;
@@ -1032,7 +1042,7 @@ int launch_grouped_ffn(const moe_layer_desc* d, const moe_layer_weights* w, cons
     fdb = (st_type == MOE_TYPE_Q8_0) ? (const void*)k_bdn<MOE_TYPE_Q4_K, MOE_TYPE_Q8_0, true>
                                      : (const void*)k_bdn<MOE_TYPE_Q4_K, MOE_TYPE_Q4_K, true>;
   }
-  const dim3 gdn_small(ngroups, (H + kBRowsPerBlock - 1) / kBRowsPerBlock);
+  const dim3 gdn_small((H + kBRowsPerBlock - 1) / kBRowsPerBlock, ngroups);   // (chunk, group)
   const dim3 gdn_big(ngroups_big, gdn.y, (n + 15) / 16);   // z: tiles of 16 tokens
   if ((small > 0 && (hipFuncSetAttribute(fgs, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_gu) != hipSuccess ||
                      hipFuncSetAttribute(fds, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dn) != hipSuccess)) ||
