@@ -251,7 +251,13 @@ int moe_decode_layer_noalloc(const moe_layer_desc* desc, const moe_layer_weights
  * tokens, so a group of fewer than 9 leaves most of it empty: on one layer
  * of the 40-layer shape group_min 9 was the fastest at batch 8 and 32.  The shared expert is one group of
  * all n_tok tokens.  routed_out[t] = bf16(sum_s weights[t][s] * y[t][s]) in
- * slot order; shared_out[t] = bf16(shared_gate[t] * ys[t]).
+ * slot order; shared_out[t] = bf16(shared_gate[t] * ys[t]).  When a call has
+ * groups of both kinds, the matrix-core groups run on a second stream of the
+ * device (made by the first such call that is not under graph capture; a
+ * captured call before then keeps to `stream`), forked from `stream` after
+ * the grouping and joined back before the combine, so every kernel of the
+ * call is ordered before later work on `stream`.  Calls from several host
+ * threads share that stream and serialise the fork and join under a lock.
  *
  * moe_batch_workspace_size: bytes of workspace for n_tok tokens (0 on a bad
  * description or n_tok outside 1..MOE_MAX_BATCH).
