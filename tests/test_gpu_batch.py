@@ -251,3 +251,59 @@ def test_decode_layer_batch_graph_replays(q, orc):
         torch.cuda.synchronize()
         assert torch.equal(other["routed_out"].view(torch.int16), ref["routed_out"].view(torch.int16)), r
     print("  5 replays bit-identical to the eager call", flush=True)
+
+
+def test_decode_layer_batch_two_threads(q, orc):
+    """Two host threads, each on its own stream and workspace, calling the
+    batch path at once (both with matrix-core and integer-path groups, so both
+    fork onto the device's shared second stream): every call's outputs equal
+    a single-threaded call's bit for bit."""
+    import threading
+    cfg = wl.CONFIGS["batch"]
+    n, gmin = 32, 4
+    gu.banner(f"decode_layer_batch from two host threads: batch {n} group_min {gmin}, 10 calls each")
+    W, _ = _weights(cfg, wl.Q4_K, wl.Q4_K)
+    H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+    d_g = q.make_desc(H, E, k, F, Fs, eps=cfg.eps)
+    inp = _inputs(cfg, n)
+
+    def io_new():
+        return {"residual": gu.dev_u16(inp["residual"]), "routed_in": gu.dev_u16(inp["routed_prev"]),
+                "shared_in": gu.dev_u16(inp["shared_prev"]),
+                "out_sum": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda"),
+                "routed_out": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda"),
+                "shared_out": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda"),
+                "ids": torch.zeros(n, k, dtype=torch.int32, device="cuda")}
+
+    ref = io_new()
+    q.moe_decode_layer_batch(d_g, W, ref, n, gmin, q.alloc_batch_workspace(d_g, n))
+    torch.cuda.synchronize()
+    outs = [[io_new() for _ in range(10)] for _ in range(2)]
+    wss = [q.alloc_batch_workspace(d_g, n) for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for io in outs[i]:
+                    q.moe_decode_layer_batch(d_g, W, io, n, gmin, wss[i])
+            streams[i].synchronize()
+        except Exception as exc:   # reported by the main thread
+            errors.append(exc)
+
+    th = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in th)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i in range(2):
+        for c, io in enumerate(outs[i]):
+            for key in ("out_sum", "routed_out", "shared_out"):
+                assert torch.equal(io[key].view(torch.int16), ref[key].view(torch.int16)), (i, c, key)
+            assert torch.equal(io["ids"], ref["ids"]), (i, c)
+    print("  20 calls from two threads bit-identical to the single call", flush=True)
