@@ -422,7 +422,7 @@ def launch_durations(stack, n):
 
 
 KERNEL_SOURCES = ["quantized_router_expert_amd/csrc/moe_stack.hip", "quantized_router_expert_amd/csrc/moe_stack.h",
-                  "quantized_router_expert_amd/csrc/moe_device.h"]
+                  "quantized_router_expert_amd/csrc/moe_device.h", "quantized_router_expert_amd/csrc/moe_select.h"]
 
 
 def kernel_source_hash():

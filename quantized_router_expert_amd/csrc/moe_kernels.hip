@@ -11,6 +11,7 @@
 #include "../../include/moe_decode.h"
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_select.h"
 #include "moe_stack.h"
 
 #include <string.h>
@@ -199,66 +200,6 @@ __global__ __launch_bounds__(kNormThreads) void k_quantize_q81(const float* x, i
 // =====================================================================
 // a2 + a3: router GEMV + last-workgroup top-k + routing weights
 // =====================================================================
-// Wave-level top-k over E <= 64*NPL logits held in memory.  Each lane keeps
-// its NPL 32-bit order keys (expert e = lane + 64j in slot j); a round takes
-// the wave-wide maximum key and, among the experts holding it, the lowest
-// index (the first slot j with a match, then its first lane), so slots come in
-// rank order with ties to the lower index.  A taken key becomes 0, below
-// every real key.  The order key: -0 counts as +0 (IEEE equality ties them)
-// and NaN as -inf.
-__device__ __forceinline__ uint32_t order_key(float v) {
-  if (v != v) v = -__builtin_inff();
-  if (v == 0.0f) v = 0.0f;
-  const uint32_t b = __float_as_uint(v);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);   // never 0 for a real value
-}
-template <int NPL>
-__device__ void wave_topk_softmax_n(const float* logits, int E, int k, int32_t* ids_out, float* w_out) {
-  const int lane = threadIdx.x & 63;
-  uint32_t key[NPL];
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = (e < E) ? order_key(logits[e]) : 0u;
-  }
-  int my_id = 0;   // lane s < k: the id of slot s
-  for (int s = 0; s < k; ++s) {
-    uint32_t best = key[0];
-#pragma unroll
-    for (int j = 1; j < NPL; ++j) best = max(best, key[j]);
-    const uint32_t wbest = wave_max_u32(best);
-    int win = -1;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const unsigned long long m = __ballot(key[j] == wbest);
-      if (win < 0 && m != 0ull) win = 64 * j + __ffsll((long long)m) - 1;
-    }
-#pragma unroll
-    for (int j = 0; j < NPL; ++j)
-      if (win == lane + 64 * j) key[j] = 0u;
-    if (lane == s) my_id = win;
-  }
-  // softmax over the selected logits, shifted by the largest (slot 0), fp64:
-  // lane s takes slot s's exponential, every lane sums them in slot order
-  const double m = (double)logits[__shfl(my_id, 0)];
-  const double ex = (lane < k) ? exp((double)logits[my_id] - m) : 0.0;
-  double sum = 0.0;
-  for (int s = 0; s < k; ++s) sum += __shfl(ex, s);
-  if (lane < k) {
-    ids_out[lane] = my_id;
-    w_out[lane] = (float)(ex / sum);
-  }
-}
-// keys per lane from the expert count (the scan is the same, over fewer keys)
-__device__ __forceinline__ void wave_topk_softmax(const float* logits, int E, int k, int32_t* ids_out, float* w_out) {
-  static_assert(kTopkPerLane == 16, "dispatch below covers up to 16 keys per lane");
-  if (E <= 64) wave_topk_softmax_n<1>(logits, E, k, ids_out, w_out);
-  else if (E <= 128) wave_topk_softmax_n<2>(logits, E, k, ids_out, w_out);
-  else if (E <= 256) wave_topk_softmax_n<4>(logits, E, k, ids_out, w_out);
-  else if (E <= 512) wave_topk_softmax_n<8>(logits, E, k, ids_out, w_out);
-  else wave_topk_softmax_n<16>(logits, E, k, ids_out, w_out);
-}
-
 // The workgroup's arrival on a grid-completion counter group at c0 (called by
 // one thread after the workgroup's results are stored): true for the last of
 // the gridDim.x workgroups to arrive.  The counters wrap back to zero.
@@ -563,25 +504,33 @@ __global__ __launch_bounds__(kFfnThreads) void k_gate_up(GateUpArgs a) {
     const int slot = b / a.cpe;
     f0 = (b % a.cpe) * a.R;
     nr = min(a.R, a.F - f0);
-    __shared__ int32_t s_ids[MOE_MAX_TOPK];
-    __shared__ float s_wts[MOE_MAX_TOPK];
-    // waves 1..3 read the activations while wave 0 selects
-    if (!a.ids && wave > 0) load_act_lds(a.xq, H, codes, dact, sact, threadIdx.x - 64, blockDim.x - 64);
-    if (!a.ids) {   // the selection, from the logits of the router launch
-      if (wave == 0) {
-        wave_topk_softmax(a.logits, a.E, a.k, s_ids, s_wts);
-        if (b == 0) {
-          const int lane = threadIdx.x & 63;
-          if (lane < a.k) {
-            a.ids_out[lane] = s_ids[lane];
-            a.wts_out[lane] = s_wts[lane];
-          }
-          if (lane == 0 && a.sg_out) a.sg_out[0] = a.has_sg ? (float)sigmoid_f64((double)a.logits[a.E]) : 0.0f;
-        }
+    // the selection from the router launch's logits, as the persistent kernel
+    // makes it: waves 0..3 land the logits in LDS and rank them (candidates),
+    // wave 0 merges the candidates; waves 4..7 read the activations meanwhile
+    __shared__ float s_lg[MOE_MAX_EXPERTS + 1];
+    __shared__ unsigned long long s_keys[256], s_cand[4 * 16];
+    __shared__ uint32_t s_sel[2 * MOE_MAX_TOPK + 1];
+    __shared__ float s_lgsel[MOE_MAX_TOPK + 1];
+    constexpr int kSelWaves = 4;
+    static_assert(kFfnThreads / 64 > kSelWaves, "waves past the selecting ones read the activations");
+    if (!a.ids && wave >= kSelWaves)
+      load_act_lds(a.xq, H, codes, dact, sact, threadIdx.x - 64 * kSelWaves, blockDim.x - 64 * kSelWaves);
+    if (!a.ids) {
+      if (wave < kSelWaves) {
+        // wave w lands the logits it ranks: experts 64w + lane + 256j
+        const int lane = threadIdx.x & 63;
+        for (int e = 64 * wave + lane; e < a.E; e += 64 * kSelWaves) s_lg[e] = a.logits[e];
+        if (wave == 0 && lane == 0) s_lg[a.E] = a.has_sg ? a.logits[a.E] : 0.0f;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        topk_candidates(s_lg, a.E, a.k, wave, s_keys, s_cand);
       }
       __syncthreads();
+      if (wave == 0) rank_candidates(s_lg, a.E, a.k, a.has_sg, s_cand, s_sel, s_lgsel);
+      __syncthreads();
     }
-    const long e = a.ids ? a.ids[slot] : s_ids[slot];
+    const long e = a.ids ? a.ids[slot] : (long)s_sel[slot];
     if (e < 0 || e >= a.E) {  // an id outside the experts reads nothing and yields NaN
       for (int f = threadIdx.x; f < nr; f += blockDim.x) a.h[(long)slot * a.F + f0 + f] = __builtin_nanf("");
       return;
@@ -589,6 +538,15 @@ __global__ __launch_bounds__(kFfnThreads) void k_gate_up(GateUpArgs a) {
     stage_async(stage, a.gate + (e * a.F + f0) * rb, (uint32_t)(nr * rb), wave, 0, kFfnThreads / 64);
     stage_async(stage + up_off, a.up + (e * a.F + f0) * rb, (uint32_t)(nr * rb), wave, 0, kFfnThreads / 64);
     h_out = a.h + (long)slot * a.F + f0;
+    if (!a.ids && b == 0 && wave == 0) {   // ids, routing weights and gate, while the rows land
+      routing_weights(a.k, a.has_sg, s_lgsel, s_sel, reinterpret_cast<double*>(s_cand));
+      const int lane = threadIdx.x & 63;
+      if (lane < a.k) {
+        a.ids_out[lane] = (int32_t)s_sel[lane];
+        a.wts_out[lane] = __uint_as_float(s_sel[a.k + lane]);
+      }
+      if (lane == 0 && a.sg_out) a.sg_out[0] = __uint_as_float(s_sel[2 * a.k]);
+    }
   } else {
     f0 = (b - a.k * a.cpe) * a.R;
     nr = min(a.R, a.Fs - f0);
@@ -965,9 +923,12 @@ size_t gate_up_lds(int H, int R, int rtype) {
   return stage + part + act;
 }
 
+// the kernel's static LDS (the selection's logits, keys and candidates) comes
+// on top of the dynamic part
+constexpr size_t kGateUpStaticLds = 8 * 1024;
 int pick_gate_up_rows(int H, int rtype) {
   int R = kGateUpRows;
-  while (R > 1 && gate_up_lds(H, R, rtype) > kLdsBudget) R >>= 1;
+  while (R > 1 && gate_up_lds(H, R, rtype) > kLdsBudget - kGateUpStaticLds) R >>= 1;
   return R;
 }
 

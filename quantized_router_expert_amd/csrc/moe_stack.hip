@@ -30,6 +30,7 @@
 #include "../../include/moe_decode.h"
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_select.h"
 #include "moe_stack.h"
 
 namespace moe {
@@ -256,199 +257,6 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 
 __device__ __forceinline__ double sq4_f64(float4 r) {
   return ((double)r.x * (double)r.x + (double)r.y * (double)r.y) + ((double)r.z * (double)r.z + (double)r.w * (double)r.w);
-}
-
-// Order-preserving 32-bit key of a logit (a larger float gives a larger key);
-// NaN counts as -inf and -0 as +0.  Never 0, which marks an empty or taken slot.
-__device__ __forceinline__ uint32_t logit_key(float v) {
-  if (v != v) v = -__builtin_inff();
-  if (v == 0.0f) v = 0.0f;
-  const uint32_t b = __float_as_uint(v);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// Expert selection ([P273] Summary item 1: the top-k runs inside the router's
-// kernel), larger logit first and the lower expert id first among equal
-// logits, in three steps:
-//  1. waves 0..3 each take the experts e = 64w + lane + 256j and find their own
-//     k best (by ranking within the wave for E <= 256, else by k wave-wide
-//     picks), as 64-bit candidates key << 32 | ~id (0 where a wave has fewer
-//     than k experts);
-//  2. wave 0 ranks the 4k candidates against each other (all distinct), and
-//     the candidate of rank r < k is slot r; the selected logits (and the
-//     shared-gate logit) are copied out, as the logits' landing area is reused
-//     for the routed rows right after;
-//  3. later, off the critical path, wave 0 turns the copied logits into the
-//     softmax weights (fp64, shifted by the largest, summed in slot order) and
-//     the shared expert's sigmoid gate.
-// Candidate slots per wave: wave w's candidates sit at kc*w + 0..k-1 (the rest
-// of its kc slots hold 0), so 4*kc slots in all.
-__device__ __forceinline__ int cand_stride(int k) { return k <= 8 ? 8 : 16; }
-
-template <int NPL>
-__device__ __forceinline__ void wave_topk(const float* lg, int E, int k, int kc, int w, unsigned long long* cand) {
-  const int lane = threadIdx.x & 63;
-  uint32_t key[NPL];
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const int e = 64 * w + lane + 256 * j;
-    key[j] = (e < E) ? logit_key(lg[e]) : 0u;
-  }
-  if (lane >= k && lane < kc) cand[kc * w + lane] = 0ull;   // slots past k never rank
-  for (int s = 0; s < k; ++s) {
-    uint32_t hv = key[0], hid = (uint32_t)(64 * w + lane);
-#pragma unroll
-    for (int j = 1; j < NPL; ++j)
-      if (key[j] > hv) { hv = key[j]; hid = (uint32_t)(64 * w + lane + 256 * j); }
-    const uint32_t m = wave_max_u32(hv);
-    const unsigned long long tied = __ballot(hv == m);
-    // usually one lane holds the maximum: it takes its own key out and writes
-    // the candidate; on a tie the lowest id among the tied lanes goes first
-    uint32_t id = hid;
-    bool win = (hv == m);
-    if (__popcll(tied) != 1) {
-      id = wave_min_u32(hv == m ? hid : 0xffffffffu);
-      win = (hid == id);
-    }
-    if (win) {
-#pragma unroll
-      for (int j = 0; j < NPL; ++j)
-        if ((uint32_t)(64 * w + lane + 256 * j) == id) key[j] = 0u;
-      cand[kc * w + s] = m ? (((unsigned long long)m << 32) | (uint32_t)~id) : 0ull;
-    }
-  }
-}
-
-// Adds [k_i > c] to a_i for four keys.  The four compares write four
-// separate SGPR-pair masks and only then do the four carry-in adds read
-// them: the compiler's form puts every compare through VCC, each add waiting
-// on its own compare, a chain of one compare, two wait states and one add
-// per key.  Here each add reads a mask written three instructions earlier,
-// which covers the wait states a VALU-written mask needs before a VALU reads
-// it as a carry.
-__device__ __forceinline__ void count4_above(unsigned long long k0, unsigned long long k1, unsigned long long k2,
-                                             unsigned long long k3, unsigned long long c, int& a0, int& a1, int& a2,
-                                             int& a3) {
-  unsigned long long m0, m1, m2, m3;
-  asm volatile(
-      "v_cmp_gt_u64_e64 %4, %8, %12\n\t"
-      "v_cmp_gt_u64_e64 %5, %9, %12\n\t"
-      "v_cmp_gt_u64_e64 %6, %10, %12\n\t"
-      "v_cmp_gt_u64_e64 %7, %11, %12\n\t"
-      "v_addc_co_u32_e64 %0, %4, 0, %0, %4\n\t"
-      "v_addc_co_u32_e64 %1, %5, 0, %1, %5\n\t"
-      "v_addc_co_u32_e64 %2, %6, 0, %2, %6\n\t"
-      "v_addc_co_u32_e64 %3, %7, 0, %3, %7"
-      : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "=&s"(m0), "=&s"(m1), "=&s"(m2), "=&s"(m3)
-      : "v"(k0), "v"(k1), "v"(k2), "v"(k3), "v"(c));
-}
-
-// Count of the 2*NP keys at `k2` (NP pairs) that are above c.  The loads go
-// out in batches of 8 pairs, each batch before the compares of the previous
-// one, and the count is kept in four separate sums.
-template <int NP>
-__device__ __forceinline__ int count_above(const ulonglong2* k2, unsigned long long c) {
-  static_assert(NP % 8 == 0, "whole batches");
-  int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-  ulonglong2 v[8], nv[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = k2[j];
-#pragma unroll
-  for (int b = 0; b < NP; b += 8) {
-    if (b + 8 < NP) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) nv[j] = k2[b + 8 + j];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 8; j += 2) count4_above(v[j].x, v[j].y, v[j + 1].x, v[j + 1].y, c, a0, a1, a2, a3);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = nv[j];
-  }
-  return (a0 + a1) + (a2 + a3);
-}
-
-// E <= 256: wave w ranks its 64 experts against each other in parallel
-// (one key per lane; 32 broadcast 16-byte LDS loads and 64 independent
-// compares per lane, no dependent chain); the lanes ranked below k are the
-// wave's candidates, already in order.  keys: 256 u64 of LDS.
-__device__ __forceinline__ void wave_rank_topk(const float* lg, int E, int k, int kc, int w,
-                                               unsigned long long* keys, unsigned long long* cand) {
-  const int lane = threadIdx.x & 63;
-  const int e = 64 * w + lane;
-  const unsigned long long c = (e < E) ? (((unsigned long long)logit_key(lg[e]) << 32) | (uint32_t)~e) : 0ull;
-  keys[e] = c;
-  if (lane < kc) cand[kc * w + lane] = 0ull;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  const int rank = count_above<32>(reinterpret_cast<const ulonglong2*>(keys + 64 * w), c);
-  if (rank < k && c != 0ull) cand[kc * w + rank] = c;
-}
-
-__device__ __forceinline__ void topk_candidates(const float* lg, int E, int k, int wave, unsigned long long* keys,
-                                                unsigned long long* cand) {
-  if (wave >= 4) return;
-  const int kc = cand_stride(k);
-  if (E <= 256) wave_rank_topk(lg, E, k, kc, wave, keys, cand);
-  else if (E <= 512) wave_topk<2>(lg, E, k, kc, wave, cand);
-  else wave_topk<4>(lg, E, k, kc, wave, cand);
-}
-
-// wave 0, after a barrier: slot ids -> sel[0..k), their logits -> lgsel[0..k),
-// the shared-gate logit -> lgsel[k].  Each candidate counts the candidates
-// above it over all 4*kc slots (unused slots hold 0, read with unrolled
-// 16-byte loads).  For kc == 8 (32 slots) lanes L and L+32 both hold slot L
-// and count half of the slots each; one cross-half lane swap adds the halves.
-// For kc == 16 lane L holds slot L and counts all 64.  Returns true unless
-// exactly k candidates rank below k (fewer than k valid experts).
-__device__ __forceinline__ bool rank_candidates(const float* lg, int E, int k, bool has_sg,
-                                                const unsigned long long* cand, uint32_t* sel, float* lgsel) {
-  const int lane = threadIdx.x & 63;
-  const int kc = cand_stride(k);
-  const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand);
-  unsigned long long c;
-  int rank;
-  bool mine;
-  if (kc == 8) {
-    const int slot = lane & 31;
-    c = ((slot & 7) < k) ? cand[slot] : 0ull;
-    const int part = count_above<8>(c2 + 8 * (lane >> 5), c);
-    const auto sw = __builtin_amdgcn_permlane32_swap(part, part, false, false);
-    rank = (int)sw[0] + (int)sw[1];
-    mine = lane < 32;
-  } else {
-    c = (lane < 4 * kc && (lane & (kc - 1)) < k) ? cand[lane] : 0ull;
-    rank = count_above<32>(c2, c);
-    mine = true;
-  }
-  const bool take = mine && c != 0ull && rank < k;
-  if (take) {
-    const uint32_t id = ~(uint32_t)c;
-    sel[rank] = id;
-    lgsel[rank] = lg[id];
-  }
-  if (lane == 0) lgsel[k] = has_sg ? lg[E] : 0.0f;
-  return __popcll(__ballot(take)) != k;
-}
-
-// wave 0: routing weights sel[k..2k) and the shared gate sel[2k] from lgsel;
-// scr: k doubles of LDS
-__device__ __forceinline__ void routing_weights(int k, bool has_sg, const float* lgsel, uint32_t* sel, double* scr) {
-  const int lane = threadIdx.x & 63;
-  const double lmax = (double)lgsel[0];
-  double arg = 0.0;
-  if (lane < k) arg = (double)lgsel[lane] - lmax;
-  else if (lane == k && has_sg) arg = -(double)lgsel[k];
-  const double ex = exp(arg);
-  if (lane < k) scr[lane] = ex;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  double sum = 0.0;
-  for (int s = 0; s < k; ++s) sum += scr[s];   // slot order
-  if (lane < k) sel[k + lane] = __float_as_uint((float)(ex / sum));
-  else if (lane == k) sel[2 * k] = __float_as_uint(has_sg ? (float)(1.0 / (1.0 + ex)) : 0.0f);
 }
 
 // A layer's weight pointers, wave-uniform.  Read once per layer at a moment
