@@ -917,19 +917,26 @@ struct SideStream {
 std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
 
-// the device's side stream, or null (caller holds g_side_mu)
+// the device's side stream, or null (caller holds g_side_mu).  A failed query
+// here only means the call keeps to one stream: its error is cleared, so that
+// the launch path's own error check does not report it.
 SideStream* side_stream(hipStream_t st) {
+  auto none = []() -> SideStream* {
+    (void)hipGetLastError();
+    return nullptr;
+  };
   int dev = -1;
-  if (st ? hipStreamGetDevice(st, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess) return nullptr;
+  if (st ? hipStreamGetDevice(st, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess) return none();
   if (dev < 0 || dev >= kMaxDevices) return nullptr;
   SideStream& ss = g_side[dev];
   if (ss.s) return &ss;
   if (ss.failed) return nullptr;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return none();
+  if (cs != hipStreamCaptureStatusNone) return nullptr;
   int cur = -1;
-  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
-  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  if (hipGetDevice(&cur) != hipSuccess) return none();
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return none();
   hipStream_t s = nullptr;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   const bool ok = hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess &&
