@@ -285,7 +285,7 @@ def require_status_ok(q, stack, what):
         sys.exit(1)
 
 
-def batch_leg(q, sizes=(8, 32), group_min=9, n_layers=6, rounds=5):
+def batch_leg(q, sizes=(8, 32), group_min=9, n_layers=6, rounds=5, tune=(6, 9, 12)):
     """The grouped batch path on layers of the 40-layer shape: per batch size,
     microseconds per layer step (norm, router, grouped experts, combine), with
     `n_layers` layers, each with its own weights and its own seeded batch
@@ -296,9 +296,10 @@ def batch_leg(q, sizes=(8, 32), group_min=9, n_layers=6, rounds=5):
     holds, as in a decode step where each layer's weights are read once.
     Reports tokens/s and GB/s over the bytes a step must read (router, shared
     expert, each distinct selected expert once; averaged over the layers).
-    group_min 9: groups of 9 or more tokens take the int8 matrix cores, whose
-    tile is 16 tokens (a smaller group would leave more than half of it
-    empty); the measured best at batch 8 and 32 among 4, 6, 9, 12 and 16."""
+    group_min: groups of that many tokens or more take the int8 matrix cores,
+    whose tile is 16 tokens.  With `tune`, moe_tune_group_min picks it among
+    those candidates on this device (9 has been the measured best at batch 8
+    and 32 among 4, 6, 9, 12 and 16); group_min changes no output bit."""
     cfg = wl.CONFIGS["batch"]
     H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
     desc = q.make_desc(H, E, k, F, Fs, eps=cfg.eps)
@@ -320,15 +321,20 @@ def batch_leg(q, sizes=(8, 32), group_min=9, n_layers=6, rounds=5):
                         "shared_out": torch.empty(n, H, dtype=torch.bfloat16, device="cuda"),
                         "ids": torch.empty(n, k, dtype=torch.int32, device="cuda")})
         torch.cuda.synchronize()   # the inputs are made on the default stream
+        gmin = group_min
+        if tune:   # measured choice on this device (outputs do not depend on it)
+            with torch.cuda.stream(s):
+                gmin, _ = q.tune_group_min(desc, lws[0], ios[0], n, ws, candidates=tune, reps=5)
+            s.synchronize()
         with torch.cuda.stream(s):
             for l in range(n_layers):
-                q.moe_decode_layer_batch(desc, lws[l], ios[l], n, group_min, ws)
+                q.moe_decode_layer_batch(desc, lws[l], ios[l], n, gmin, ws)
         s.synchronize()
         graphs = []
         for l in range(n_layers):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
-                q.moe_decode_layer_batch(desc, lws[l], ios[l], n, group_min, ws)
+                q.moe_decode_layer_batch(desc, lws[l], ios[l], n, gmin, ws)
             graphs.append(g)
         torch.cuda.synchronize()
         for g in graphs:
@@ -348,9 +354,11 @@ def batch_leg(q, sizes=(8, 32), group_min=9, n_layers=6, rounds=5):
         out[f"batch{n}"] = {"us_per_layer_step": us, "tokens_per_s_per_layer": n * 1e6 / us,
                             "distinct_experts_mean": float(np.mean(distinct)), "distinct_experts": distinct,
                             "bytes_per_step": nbytes, "achieved_GBs": nbytes / (us * 1e-6) / 1e9,
-                            "group_min": group_min, "layers_rotated": n_layers}
+                            "group_min": gmin, "group_min_candidates": list(tune) if tune else None,
+                            "layers_rotated": n_layers}
         print(f"# batch {n}: {us:.1f} us per layer step over {n_layers} layers, {np.mean(distinct):.1f} distinct "
-              f"experts per layer, {out[f'batch{n}']['achieved_GBs']:.0f} GB/s", file=sys.stderr, flush=True)
+              f"experts per layer, {out[f'batch{n}']['achieved_GBs']:.0f} GB/s (group_min {gmin})", file=sys.stderr,
+              flush=True)
         del graphs, ws
     del Ws, lws
     torch.cuda.empty_cache()

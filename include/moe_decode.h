@@ -282,6 +282,23 @@ int expert_ffn_grouped(const moe_layer_desc* desc, const moe_layer_weights* w, c
 int moe_decode_layer_batch(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_layer_io* io,
                            int n_tok, int group_min, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_tune_group_min: the group_min for this description, batch size and
+ * device, chosen by measurement ([P273] "Relation to open PRs": the router's
+ * split factor and the F = 512 dispatch were retuned per shape by measuring
+ * them; here the threshold between the two grouped code paths is).  Each of
+ * the n_candidates values (each 1..MOE_MAX_GROUP_MIN) runs
+ * moe_decode_layer_batch on `io` once to warm up and then `reps` times
+ * (1..100), timed with events on `stream`; *best receives the candidate with
+ * the lowest mean time, *best_us that mean (may be NULL).  group_min changes
+ * no bit of any output, so the choice is a speed setting only.  io's outputs
+ * are overwritten.  The call synchronises `stream`: it returns
+ * MOE_ERR_UNSUPPORTED under graph capture and enqueues nothing then.  Other
+ * errors as for moe_decode_layer_batch; candidates and best are host memory.
+ */
+int moe_tune_group_min(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_layer_io* io, int n_tok,
+                       const int* candidates, int n_candidates, int reps, void* ws, size_t ws_bytes, void* stream,
+                       int* best, float* best_us);
+
 /* ------------------------------------------------------------------------
  * a7: the L-layer stack for one token ([P239] Summary: decode is graph- and
  * launch-bound; [P273] Summary item 2: one graph node per layer matters).

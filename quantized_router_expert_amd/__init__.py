@@ -86,6 +86,9 @@ _expert_ffn_grouped = _sig("expert_ffn_grouped", C.c_int, C.POINTER(LayerDesc), 
                            C.c_int, C.c_int, P, P, P, P, P, C.c_size_t, P)
 _moe_decode_layer_batch = _sig("moe_decode_layer_batch", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights),
                                C.POINTER(LayerIO), C.c_int, C.c_int, P, C.c_size_t, P)
+_moe_tune_group_min = _sig("moe_tune_group_min", C.c_int, C.POINTER(LayerDesc), C.POINTER(LayerWeights),
+                           C.POINTER(LayerIO), C.c_int, C.POINTER(C.c_int), C.c_int, C.c_int, P, C.c_size_t, P,
+                           C.POINTER(C.c_int), C.POINTER(C.c_float))
 _moe_stack_status_offset = _sig("moe_stack_status_offset", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
 _moe_stack_kernel_shape = _sig("moe_stack_kernel_shape", C.c_int, C.POINTER(LayerDesc))
 _moe_stack_trace_offset = _sig("moe_stack_trace_offset", C.c_size_t, C.POINTER(LayerDesc), C.c_int)
@@ -99,7 +102,7 @@ EXPORTS = ("add_rmsnorm3", "router_topk", "expert_ffn_q4k", "moe_decode_layer", 
            "moe_decode_stack", "moe_workspace_size", "moe_workspace_init", "moe_status_string",
            "moe_stack_status_offset", "moe_stack_trace_offset", "moe_test_subblock_dots", "moe_test_quantize_q81", "moe_stream_read", "moe_requant_q4k",
            "moe_batch_workspace_size", "expert_ffn_grouped", "moe_decode_layer_batch", "moe_test_stack_select",
-           "moe_decode_layer_noalloc", "add_rmsnorm2_q8", "moe_stack_kernel_shape")
+           "moe_decode_layer_noalloc", "add_rmsnorm2_q8", "moe_stack_kernel_shape", "moe_tune_group_min")
 MAX_BATCH = 64
 MAX_GROUP_MIN = 16
 
@@ -248,6 +251,18 @@ def moe_decode_layer_batch(desc, weights, io, n_tok, group_min, ws, stream=None)
     return _check("moe_decode_layer_batch", _moe_decode_layer_batch(C.byref(desc), C.byref(lw), C.byref(lio), n_tok,
                                                                     group_min, ptr(ws), ws.numel() * ws.element_size(),
                                                                     stream_handle(stream)))
+
+
+def tune_group_min(desc, weights, io, n_tok, ws, candidates=(4, 6, 9, 12, 16), reps=5, stream=None):
+    """(best group_min, its mean us per call) measured on this device; io's outputs are overwritten."""
+    lw = weights if isinstance(weights, LayerWeights) else make_weights(weights)
+    lio = LayerIO(**{n: ptr(io.get(n)) for n, _ in LayerIO._fields_})
+    cand = (C.c_int * len(candidates))(*candidates)
+    best, us = C.c_int(0), C.c_float(0.0)
+    _check("moe_tune_group_min", _moe_tune_group_min(C.byref(desc), C.byref(lw), C.byref(lio), n_tok, cand,
+                                                     len(candidates), reps, ptr(ws), ws.numel() * ws.element_size(),
+                                                     stream_handle(stream), C.byref(best), C.byref(us)))
+    return best.value, us.value
 
 
 def _layer_array(layers):

@@ -348,6 +348,48 @@ int moe_decode_layer_batch(const moe_layer_desc* desc, const moe_layer_weights* 
                             static_cast<uint8_t*>(ws), L, st);
 }
 
+int moe_tune_group_min(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_layer_io* io, int n_tok,
+                       const int* candidates, int n_candidates, int reps, void* ws, size_t ws_bytes, void* stream,
+                       int* best, float* best_us) {
+  if (!candidates || !best) return MOE_ERR_NULL;
+  if (n_candidates < 1 || n_candidates > MOE_MAX_GROUP_MIN || reps < 1 || reps > 100) return MOE_ERR_SHAPE;
+  for (int i = 0; i < n_candidates; ++i)
+    if (candidates[i] < 1 || candidates[i] > MOE_MAX_GROUP_MIN) return MOE_ERR_SHAPE;
+  hipStream_t st = as_stream(stream);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return MOE_ERR_HIP;
+  if (cs != hipStreamCaptureStatusNone) return MOE_ERR_UNSUPPORTED;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess) return MOE_ERR_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return MOE_ERR_HIP;
+  }
+  int rc = MOE_OK, pick = candidates[0];
+  float pick_us = 0.0f;
+  for (int i = 0; i < n_candidates && rc == MOE_OK; ++i) {
+    const int g = candidates[i];
+    rc = moe_decode_layer_batch(desc, w, io, n_tok, g, ws, ws_bytes, stream);   // warm-up
+    if (rc == MOE_OK && hipEventRecord(e0, st) != hipSuccess) rc = MOE_ERR_HIP;
+    for (int r = 0; r < reps && rc == MOE_OK; ++r) rc = moe_decode_layer_batch(desc, w, io, n_tok, g, ws, ws_bytes, stream);
+    float ms = 0.0f;
+    if (rc == MOE_OK && (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                         hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+      rc = MOE_ERR_HIP;
+    const float us = 1000.0f * ms / (float)reps;
+    if (rc == MOE_OK && (i == 0 || us < pick_us)) {
+      pick = g;
+      pick_us = us;
+    }
+  }
+  (void)hipEventDestroy(e1);
+  (void)hipEventDestroy(e0);
+  if (rc) return rc;
+  *best = pick;
+  if (best_us) *best_us = pick_us;
+  return MOE_OK;
+}
+
 int moe_stack_bind(const moe_layer_desc* desc, const moe_layer_weights* layers, int n_layers, void* ws,
                    size_t ws_bytes, void* stream) {
   int rc = check_desc(desc);

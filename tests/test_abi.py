@@ -223,3 +223,23 @@ def test_grouped_path_validation(q):
     assert g(C.byref(d), C.byref(w), C.byref(io), 8, 99, FAKE, need, None) == -2
     io2 = q.LayerIO(residual=FAKE, out_sum=FAKE, routed_out=FAKE, shared_out=None)
     assert g(C.byref(d), C.byref(w), C.byref(io2), 8, 4, FAKE, need, None) == -1
+
+
+def test_tune_group_min_rejects_bad_arguments():
+    """The group_min tuner validates its host arguments before any device call."""
+    import quantized_router_expert_amd as q
+    lib = C.CDLL(q.LIB_PATH)
+    f = lib.moe_tune_group_min
+    f.restype = C.c_int
+    f.argtypes = [C.c_void_p] * 3 + [C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p,
+                                     C.c_void_p, C.c_void_p]
+    best = C.c_int(-1)
+    cand = (C.c_int * 3)(4, 9, 16)
+    assert f(None, None, None, 8, None, 3, 5, None, 0, None, C.byref(best), None) == -1
+    assert f(None, None, None, 8, cand, 3, 5, None, 0, None, None, None) == -1
+    assert f(None, None, None, 8, cand, 0, 5, None, 0, None, C.byref(best), None) == -2
+    assert f(None, None, None, 8, cand, 3, 0, None, 0, None, C.byref(best), None) == -2
+    assert f(None, None, None, 8, cand, 3, 101, None, 0, None, C.byref(best), None) == -2
+    bad = (C.c_int * 2)(4, q.MAX_GROUP_MIN + 1)
+    assert f(None, None, None, 8, bad, 2, 5, None, 0, None, C.byref(best), None) == -2
+    assert best.value == -1

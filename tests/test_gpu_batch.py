@@ -307,3 +307,38 @@ def test_decode_layer_batch_two_threads(q, orc):
                 assert torch.equal(io[key].view(torch.int16), ref[key].view(torch.int16)), (i, c, key)
             assert torch.equal(io["ids"], ref["ids"]), (i, c)
     print("  20 calls from two threads bit-identical to the single call", flush=True)
+
+
+def test_tune_group_min_picks_a_candidate(q, orc):
+    """The measured group_min choice: one of the candidates, a positive time,
+    and outputs afterwards identical to a plain call's with that choice (and
+    so with any other: group_min moves work between bit-identical paths)."""
+    cfg = wl.CONFIGS["batch"]
+    n = 32
+    gu.banner(f"group_min tuner: batch {n}, candidates 4 9 16")
+    W, _ = _weights(cfg, wl.Q4_K, wl.Q4_K)
+    H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+    d_g = q.make_desc(H, E, k, F, Fs, eps=cfg.eps)
+    inp = _inputs(cfg, n)
+
+    def io_new():
+        return {"residual": gu.dev_u16(inp["residual"]), "routed_in": gu.dev_u16(inp["routed_prev"]),
+                "shared_in": gu.dev_u16(inp["shared_prev"]),
+                "out_sum": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda"),
+                "routed_out": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda"),
+                "shared_out": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda"),
+                "ids": torch.zeros(n, k, dtype=torch.int32, device="cuda")}
+
+    io = io_new()
+    ws = q.alloc_batch_workspace(d_g, n)
+    torch.cuda.synchronize()
+    best, us = q.tune_group_min(d_g, W, io, n, ws, candidates=(4, 9, 16), reps=3)
+    torch.cuda.synchronize()
+    assert best in (4, 9, 16) and us > 0.0, (best, us)
+    for g in (best, 1 if best != 1 else 16):
+        ref = io_new()
+        q.moe_decode_layer_batch(d_g, W, ref, n, g, q.alloc_batch_workspace(d_g, n))
+        torch.cuda.synchronize()
+        for key in ("out_sum", "routed_out", "shared_out"):
+            assert torch.equal(io[key].view(torch.int16), ref[key].view(torch.int16)), (g, key)
+    print(f"  picked group_min {best} at {us:.1f} us per call", flush=True)
