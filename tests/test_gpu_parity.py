@@ -310,13 +310,19 @@ def test_expert_ffn_stage_isolated(q, orc, cfg_name, shared_type, down_type):
 
 
 # ------------------------------------------------------------------ a1..a6: whole layer, chained
+# wide expert sets for the gate/up kernel's selection: more than 256 experts
+# (picks by wave-wide maxima in the four selecting waves) and top-k above 8
+# (16 candidate slots per wave), with duplicated router rows for ties
+WIDE = {"wide320": wl.Config("wide320", H=512, E=320, k=12, F=128, Fs=128, router_dup=2, config_index=11),
+        "wide1024": wl.Config("wide1024", H=512, E=1024, k=16, F=128, Fs=0, three_input=False, router_dup=4,
+                              config_index=12)}
 LAYER_CASES = [("tiny", wl.Q4_K, wl.Q4_K, 8), ("layer", wl.Q4_K, wl.Q4_K, 4), ("layer", wl.Q8_0, wl.Q5_K, 2),
-               ("e128", wl.Q4_K, wl.Q4_K, 3)]
+               ("e128", wl.Q4_K, wl.Q4_K, 3), ("wide320", wl.Q4_K, wl.Q4_K, 3), ("wide1024", wl.Q4_K, wl.Q4_K, 2)]
 
 
 @pytest.mark.parametrize("cfg_name,shared_type,down_type,ntok", LAYER_CASES)
 def test_decode_layer_chained(q, orc, cfg_name, shared_type, down_type, ntok):
-    cfg = wl.CONFIGS[cfg_name]
+    cfg = WIDE.get(cfg_name) or wl.CONFIGS[cfg_name]
     gu.banner(f"moe_decode_layer {cfg_name} shared {shared_type} down {down_type}")
     W, Wn = _gpu_weights(cfg, 0, shared_type, down_type)
     H, F, Fs, k, E = cfg.H, cfg.F, cfg.Fs, cfg.k, cfg.E
