@@ -37,6 +37,9 @@ def q():
 
 
 SMALL = wl.Config("small", H=512, E=16, k=4, F=128, Fs=256, router_dup=2, config_index=9)
+# more than 256 experts and top-12: the router's one-wave selection with eight
+# keys per lane, and groups built from twelve slots per token
+WIDE = wl.Config("wide", H=512, E=320, k=12, F=128, Fs=128, router_dup=2, config_index=13)
 
 
 def _inputs(cfg, n):
@@ -74,7 +77,7 @@ CASES = [
 
 
 def _cfg(name):
-    return SMALL if name == "small" else wl.CONFIGS[name]
+    return {"small": SMALL, "wide": WIDE}.get(name) or wl.CONFIGS[name]
 
 
 @pytest.mark.parametrize("cfg_name,n,gmin,shared_type,down_type", CASES)
@@ -146,7 +149,7 @@ def test_grouped_is_batch_invariant(q, orc, cfg_name, n, gmin, shared_type, down
     print(f"  {int(big.sum())} of {big.size} slots on the matrix cores; all outputs bit-identical", flush=True)
 
 
-@pytest.mark.parametrize("cfg_name,n,gmin", [("batch", 8, 4), ("batch", 32, 4), ("small", 12, 3)])
+@pytest.mark.parametrize("cfg_name,n,gmin", [("batch", 8, 4), ("batch", 32, 4), ("small", 12, 3), ("wide", 24, 3)])
 def test_decode_layer_batch_chained(q, orc, cfg_name, n, gmin):
     cfg = _cfg(cfg_name)
     gu.banner(f"decode_layer_batch {cfg_name} n {n} group_min {gmin}")
