@@ -127,9 +127,11 @@ __device__ __forceinline__ int count_above(const ulonglong2* k2, unsigned long l
 // E <= 256: wave w ranks its 64 experts against each other in parallel
 // (one key per lane; 32 broadcast 16-byte LDS loads and 64 independent
 // compares per lane, no dependent chain); the lanes ranked below k are the
-// wave's candidates, already in order.  keys: 256 u64 of LDS.
+// wave's candidates, already in order.  keys: 256 u64 of LDS.  cand_lg (or
+// null) receives each candidate's logit beside it.
 __device__ __forceinline__ void wave_rank_topk(const float* lg, int E, int k, int kc, int w,
-                                               unsigned long long* keys, unsigned long long* cand) {
+                                               unsigned long long* keys, unsigned long long* cand,
+                                               float* cand_lg = nullptr) {
   const int lane = threadIdx.x & 63;
   const int e = 64 * w + lane;
   const unsigned long long c = (e < E) ? (((unsigned long long)logit_key(lg[e]) << 32) | (uint32_t)~e) : 0ull;
@@ -139,14 +141,18 @@ __device__ __forceinline__ void wave_rank_topk(const float* lg, int E, int k, in
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   const int rank = count_above<32>(reinterpret_cast<const ulonglong2*>(keys + 64 * w), c);
-  if (rank < k && c != 0ull) cand[kc * w + rank] = c;
+  if (rank < k && c != 0ull) {
+    cand[kc * w + rank] = c;
+    if (cand_lg) cand_lg[kc * w + rank] = lg[e];
+  }
 }
 
+// (cand_lg: E <= 256 only)
 __device__ __forceinline__ void topk_candidates(const float* lg, int E, int k, int wave, unsigned long long* keys,
-                                                unsigned long long* cand) {
+                                                unsigned long long* cand, float* cand_lg = nullptr) {
   if (wave >= 4) return;
   const int kc = cand_stride(k);
-  if (E <= 256) wave_rank_topk(lg, E, k, kc, wave, keys, cand);
+  if (E <= 256) wave_rank_topk(lg, E, k, kc, wave, keys, cand, cand_lg);
   else if (E <= 512) wave_topk<2>(lg, E, k, kc, wave, cand);
   else wave_topk<4>(lg, E, k, kc, wave, cand);
 }
@@ -157,23 +163,28 @@ __device__ __forceinline__ void topk_candidates(const float* lg, int E, int k, i
 // 16-byte loads).  For kc == 8 (32 slots) lanes L and L+32 both hold slot L
 // and count half of the slots each; one cross-half lane swap adds the halves.
 // For kc == 16 lane L holds slot L and counts all 64.  Returns true unless
-// exactly k candidates rank below k (fewer than k valid experts).
+// exactly k candidates rank below k (fewer than k valid experts).  With
+// cand_lg (the candidates' logits, and at cand_lg[64] the shared-gate logit)
+// the logits are not read again.
 __device__ __forceinline__ bool rank_candidates(const float* lg, int E, int k, bool has_sg,
-                                                const unsigned long long* cand, uint32_t* sel, float* lgsel) {
+                                                const unsigned long long* cand, uint32_t* sel, float* lgsel,
+                                                const float* cand_lg = nullptr) {
   const int lane = threadIdx.x & 63;
   const int kc = cand_stride(k);
   const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand);
   unsigned long long c;
-  int rank;
+  int rank, ci;
   bool mine;
   if (kc == 8) {
     const int slot = lane & 31;
+    ci = slot;
     c = ((slot & 7) < k) ? cand[slot] : 0ull;
     const int part = count_above<8>(c2 + 8 * (lane >> 5), c);
     const auto sw = __builtin_amdgcn_permlane32_swap(part, part, false, false);
     rank = (int)sw[0] + (int)sw[1];
     mine = lane < 32;
   } else {
+    ci = lane;
     c = (lane < 4 * kc && (lane & (kc - 1)) < k) ? cand[lane] : 0ull;
     rank = count_above<32>(c2, c);
     mine = true;
@@ -182,10 +193,28 @@ __device__ __forceinline__ bool rank_candidates(const float* lg, int E, int k, b
   if (take) {
     const uint32_t id = ~(uint32_t)c;
     sel[rank] = id;
-    lgsel[rank] = lg[id];
+    lgsel[rank] = cand_lg ? cand_lg[ci] : lg[id];
   }
-  if (lane == 0) lgsel[k] = has_sg ? lg[E] : 0.0f;
+  if (lane == 0) lgsel[k] = has_sg ? (cand_lg ? cand_lg[64] : lg[E]) : 0.0f;
   return __popcll(__ballot(take)) != k;
+}
+
+// The id of the candidate of rank r (0 <= r < k), found by every lane of the
+// calling wave with rank_candidates' counting for kc == 8 (k <= 8); ok is
+// false unless exactly k candidates rank below k and one of them has rank r.
+__device__ __forceinline__ uint32_t candidate_of_rank(const unsigned long long* cand, int k, int r, bool& ok) {
+  const int lane = threadIdx.x & 63;
+  const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand);
+  const int slot = lane & 31;
+  const unsigned long long c = ((slot & 7) < k) ? cand[slot] : 0ull;
+  const int part = count_above<8>(c2 + 8 * (lane >> 5), c);
+  const auto sw = __builtin_amdgcn_permlane32_swap(part, part, false, false);
+  const int rank = (int)sw[0] + (int)sw[1];
+  const bool take = lane < 32 && c != 0ull && rank < k;
+  const unsigned long long m = __ballot(take && rank == r);
+  ok = __popcll(__ballot(take)) == k && m != 0ull;
+  const int src = m ? __ffsll((long long)m) - 1 : 0;
+  return (uint32_t)__builtin_amdgcn_readlane((int)~(uint32_t)c, src);
 }
 
 // wave 0: routing weights sel[k..2k) and the shared gate sel[2k] from lgsel;

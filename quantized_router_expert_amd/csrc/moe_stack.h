@@ -30,7 +30,7 @@ struct StackGeom {
   int n_t, n_lg, n_h, n_sel, n_y;     // exchange sizes in 8-byte words (n_sel: selection words in LDS)
   // LDS byte offsets
   int o_res, o_xn, o_xqc, o_xqd, o_xqs, o_nw, o_rrow, o_sgu, o_sdn, o_rgu, o_rdn, o_hqc, o_hqd, o_hqs, o_part, o_xbuf,
-      o_sel, o_red, o_y, o_cand, o_keys, o_lgsel, o_hs, o_attn;
+      o_sel, o_red, o_y, o_cand, o_keys, o_lgsel, o_hs, o_attn, o_candlg;
   int sgu_half, rgu_half, rdn_slot;
   int lds;
   // workspace byte offsets

@@ -370,6 +370,7 @@ constexpr int stack_geometry_core(int H, int E, int k, int F, int Fs, int down_t
   g.o_cand = take(8L * 64);
   g.o_keys = take(8L * 256);
   g.o_lgsel = take(4L * (MOE_MAX_TOPK + 1));
+  g.o_candlg = take(4L * 65);   // the candidates' logits and the shared-gate logit
   g.o_hs = take(4L * (g.Kps > 0 ? g.Kps : 1));
   g.lds = (int)o;
   if (g.lds < kStackMinLds) g.lds = kStackMinLds;   // keeps one workgroup per CU
@@ -414,6 +415,11 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   // the 32 workgroups that run on die (XCC) s: their h exchange stays in that
   // die's L2
   constexpr bool XS = FIX && fs.k == kXcc && fs.G == 256;
+  // XCD slots with the one-barrier selection (each polling wave finds its
+  // slot's expert itself): measured faster for the Q5_K/Q8_0 stack (518.2 ->
+  // 509.7 us per token) and slower for the Q4_K/Q4_K one (497.4 -> 501.2), so
+  // that instance keeps the barrier
+  constexpr bool OB = XS && !(DT == MOE_TYPE_Q4_K && ST == MOE_TYPE_Q4_K && S == 1);
   // router rows per workgroup of a fixed shape (E rows and the shared-gate row over G)
   constexpr int kRRFix = FIX ? (fs.E + (fs.Fs > 0 ? 1 : 0) + fs.G - 1) / fs.G : 0;
   const StackGeom g = FIX ? kFixGeom<DT, ST, S> : a.g;
@@ -444,6 +450,7 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(smem + g.o_cand);
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(smem + g.o_keys);
   float* lgsel = reinterpret_cast<float*>(smem + g.o_lgsel);
+  float* cand_lg = reinterpret_cast<float*>(smem + g.o_candlg);
   float* hsf = reinterpret_cast<float*>(smem + g.o_hs);   // the shared h, landed in phase B
 
   __shared__ uint32_t s_gen;
@@ -801,6 +808,8 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     // ================= R2: logits -> selection, in every workgroup
     stamp(l, 3);
     bstamp(l, 4);
+    uint32_t e_slot = 0;   // OB: this slot's expert, found by each polling wave
+    bool sel_ok = true;
     {
       if (E <= 256) {
         // wave w < 4 polls the logits of its own 64 experts (word pairs
@@ -820,7 +829,11 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
           bstamp(l, 13);
-          topk_candidates(reinterpret_cast<const float*>(xbuf), E, k, wave, keys, cand);
+          // OB: the candidates' logits (and the shared-gate logit, landed by
+          // wave 0) are copied beside them, as the landing area takes the
+          // routed rows once the selection is known
+          if (OB && wave == 0 && lane == 0) cand_lg[64] = has_sg ? reinterpret_cast<const float*>(xbuf)[E] : 0.0f;
+          topk_candidates(reinterpret_cast<const float*>(xbuf), E, k, wave, keys, cand, OB ? cand_lg : nullptr);
         }
         lds_barrier();
         if (s_fail) { fail_out(l); return; }
@@ -833,12 +846,35 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
         topk_candidates(reinterpret_cast<const float*>(xbuf), E, k, wave, keys, cand);
         lds_barrier();
       }
-      if (wave == 0 && rank_candidates(reinterpret_cast<const float*>(xbuf), E, k, has_sg, cand, sel, lgsel))
-        s_fail = 3;
-      lds_barrier();
-      if (s_fail) { fail_out(l); return; }
-      if (b == 0 && a.ids_out)
-        for (int s = tid; s < k; s += kStackThreads) a.ids_out[(long)l * k + s] = (int32_t)sel[s];
+      if constexpr (OB) {
+        // no second barrier: each polling wave finds its slot's expert in
+        // the candidates itself, and wave 0 writes the selection for the
+        // combine from the candidates and their copied logits (a later
+        // barrier publishes it; a failed selection stops the layer there)
+        if (wave < kPollWaves) {
+          bool ok = true;
+          e_slot = candidate_of_rank(cand, k, (int)xcc, ok);
+          sel_ok = ok;
+          if (!ok) s_fail = 3;
+        }
+        if (wave == 0) {
+          if (rank_candidates(reinterpret_cast<const float*>(xbuf), E, k, has_sg, cand, sel, lgsel, cand_lg))
+            s_fail = 3;
+          if (b == 0 && a.ids_out) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+            if (tid < k) a.ids_out[(long)l * k + tid] = (int32_t)sel[tid];
+          }
+        }
+      } else {
+        if (wave == 0 && rank_candidates(reinterpret_cast<const float*>(xbuf), E, k, has_sg, cand, sel, lgsel))
+          s_fail = 3;
+        lds_barrier();
+        if (s_fail) { fail_out(l); return; }
+        if (b == 0 && a.ids_out)
+          for (int s = tid; s < k; s += kStackThreads) a.ids_out[(long)l * k + s] = (int32_t)sel[s];
+      }
     }
     stamp(l, 4);
     bstamp(l, 5);
@@ -850,14 +886,15 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
     const int f0 = XS ? (b / kXcc) * (F / (fs.G / kXcc)) : p0 - slot * F;
     const int nrp = XS ? F / (fs.G / kXcc) : ((slot < k) ? min(g.RP, F - f0) : 0);
 
-    if (nrp > 0 && wave < kPollWaves) {
-      const long e = sel[slot];
+    if (nrp > 0 && wave < kPollWaves && sel_ok) {
+      const long e = OB ? (long)e_slot : (long)sel[slot];
       stage_async(rgu, w.gate + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0, kPollWaves);
       stage_async(rgu + g.rgu_half, w.up + (e * F + f0) * rb_gu, (uint32_t)(nrp * rb_gu), wave, 0,
                   kPollWaves);
     }
     // the routing weights are first needed by the combine: computed while the rows land
-    if (wave == 0) routing_weights(k, has_sg, lgsel, sel, reinterpret_cast<double*>(cand));
+    // (OB: scratch in the keys, as slower polling waves may still read the candidates)
+    if (wave == 0) routing_weights(k, has_sg, lgsel, sel, reinterpret_cast<double*>(OB ? keys : cand));
     // meanwhile wave 4 reads the shared h (sent in phase A, so long arrived)
     // and quantises it: h blocks k*nb_r .. k*nb_r + nb_s - 1
     if (has_sg && wave == kPollWaves) {
