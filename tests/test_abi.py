@@ -243,3 +243,17 @@ def test_tune_group_min_rejects_bad_arguments():
     bad = (C.c_int * 2)(4, q.MAX_GROUP_MIN + 1)
     assert f(None, None, None, 8, bad, 2, 5, None, 0, None, C.byref(best), None) == -2
     assert best.value == -1
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    """The boundary is a C ABI: the public header compiles as C99 with warnings as errors."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use_header.c"
+    src.write_text(f'#include "{HEADER}"\nint main(void) {{ return moe_status_string(0) == 0; }}\n')
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-c", str(src), "-o",
+                        str(tmp_path / "use_header.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
