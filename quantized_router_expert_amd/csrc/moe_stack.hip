@@ -1133,7 +1133,10 @@ __global__ __launch_bounds__(kStackThreads) void k_stack(StackArgs a) {
 // ---------------------------------------------------------------- test export of the selection
 // One workgroup per logit set runs the stack kernel's selection exactly as a
 // layer does: topk_candidates on waves 0..3, rank_candidates and
-// routing_weights on wave 0, with the same LDS arrays and barriers.
+// routing_weights on wave 0, with the same LDS arrays and barriers.  For
+// E <= 256 and k <= 8 it also runs the one-barrier form (candidate_of_rank
+// on waves 0..3, the merge from the copied candidate logits on wave 1) and
+// reports ids of -1 unless both forms agree bit for bit.
 __global__ __launch_bounds__(kStackThreads) void k_test_stack_select(const float* lg_in, int E, int k, int with_gate,
                                                                      int32_t* ids, float* wts, float* gate) {
   __shared__ float lg[MOE_MAX_EXPERTS + 1];
@@ -1141,6 +1144,9 @@ __global__ __launch_bounds__(kStackThreads) void k_test_stack_select(const float
   __shared__ unsigned long long cand[64];
   __shared__ uint32_t sel[2 * MOE_MAX_TOPK + 2];
   __shared__ float lgsel[MOE_MAX_TOPK + 1];
+  __shared__ float cand_lg[65];
+  __shared__ float lgsel2[MOE_MAX_TOPK + 1];
+  __shared__ uint32_t sel2[MOE_MAX_TOPK], sel3[MOE_MAX_TOPK];
   __shared__ int s_fail;
   const int set = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   const bool has_sg = with_gate != 0;
@@ -1148,9 +1154,28 @@ __global__ __launch_bounds__(kStackThreads) void k_test_stack_select(const float
   for (int i = tid; i < E + 1; i += kStackThreads) lg[i] = src[i];
   if (tid == 0) s_fail = 0;
   lds_barrier();
-  topk_candidates(lg, E, k, wave, keys, cand);
+  // the one-barrier form's inputs beside the candidates (E <= 256, k <= 8):
+  // the candidates' logits, and the shared-gate logit
+  const bool ob = E <= 256 && k <= 8;
+  if (ob && tid == 0) cand_lg[64] = has_sg ? lg[E] : 0.0f;
+  topk_candidates(lg, E, k, wave, keys, cand, ob ? cand_lg : nullptr);
   lds_barrier();
   if (wave == 0 && rank_candidates(lg, E, k, has_sg, cand, sel, lgsel)) s_fail = 1;
+  if (ob && wave == 1) rank_candidates(lg, E, k, has_sg, cand, sel2, lgsel2, cand_lg);
+  if (ob && wave < 4) {   // each of these waves finds the experts of ranks wave, wave + 4, ...
+    for (int r = wave; r < k; r += 4) {
+      bool ok = true;
+      const uint32_t id = candidate_of_rank(cand, k, r, ok);
+      if (ok && (tid & 63) == 0) sel3[r] = id;
+      if (!ok) s_fail = 2;
+    }
+  }
+  lds_barrier();
+  // the one-barrier form must agree with the two-barrier one bit for bit
+  if (ob && tid < k + 1 && !s_fail) {
+    if (tid < k && (sel2[tid] != sel[tid] || sel3[tid] != sel[tid])) s_fail = 3;
+    if (__float_as_uint(lgsel2[tid]) != __float_as_uint(lgsel[tid])) s_fail = 3;
+  }
   lds_barrier();
   if (wave == 0) routing_weights(k, has_sg, lgsel, sel, reinterpret_cast<double*>(cand));
   lds_barrier();

@@ -7,7 +7,10 @@ include all-equal sets, duplicated pairs, +0/-0 mixes, NaN (ranked as -inf),
 -inf and +inf.  The ids must equal the oracle's top-k bit for bit; the
 weights (softmax over the selected logits) and the shared-expert gate
 (sigmoid of logit E) must be within 2e-3 of the oracle's wherever the
-oracle's are finite."""
+oracle's are finite.  For E <= 256 and k <= 8 the export also runs the
+one-barrier form of the merge (each wave finding the expert of a rank from
+the candidates, and the candidates' copied logits) and reports ids of -1 if
+it disagrees with the two-barrier form in any id or selected logit bit."""
 import numpy as np
 import pytest
 import torch
