@@ -345,3 +345,34 @@ def test_tune_group_min_picks_a_candidate(q, orc):
         for key in ("out_sum", "routed_out", "shared_out"):
             assert torch.equal(io[key].view(torch.int16), ref[key].view(torch.int16)), (g, key)
     print(f"  picked group_min {best} at {us:.1f} us per call", flush=True)
+
+
+def test_tune_group_min_refuses_graph_capture(q, orc):
+    """The tuner synchronises its stream, so under graph capture it returns
+    MOE_ERR_UNSUPPORTED before enqueueing anything."""
+    cfg = SMALL
+    gu.banner("group_min tuner under graph capture")
+    W, _ = _weights(cfg, wl.Q4_K, wl.Q4_K)
+    H, E, k, F, Fs = cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+    d_g = q.make_desc(H, E, k, F, Fs, eps=cfg.eps)
+    n = 4
+    inp = _inputs(cfg, n)
+    io = {"residual": gu.dev_u16(inp["residual"]), "routed_in": gu.dev_u16(inp["routed_prev"]),
+          "shared_in": gu.dev_u16(inp["shared_prev"]),
+          "out_sum": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda"),
+          "routed_out": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda"),
+          "shared_out": torch.zeros(n, H, dtype=torch.bfloat16, device="cuda")}
+    ws = q.alloc_batch_workspace(d_g, n)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(q.MoeError) as err:
+        with torch.cuda.graph(g, stream=s):
+            io["out_sum"].zero_()   # one node, so the capture is not empty
+            q.tune_group_min(d_g, W, io, n, ws, candidates=(2, 3), reps=1)
+    assert err.value.status == -7, err.value
+    torch.cuda.synchronize()
+    # the device still works: a plain call afterwards
+    q.moe_decode_layer_batch(d_g, W, io, n, 2, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(io["routed_out"].float()).all()
